@@ -1,0 +1,110 @@
+"""Prefill side: write the compressed cache from exact keys and values (oracle).
+
+The steps the LowRAM pages give for compression, as plain definitions:
+
+  project     C = X B^T, the cross-layer low-rank coefficients of a
+              layer-group's pre-RoPE keys [review/keys; explainer/how
+              "Low-rank keys"].  Fitting the basis is out of scope: B is a
+              seeded orthonormal basis.
+  landmarks   per chunk of S prefix tokens, the mean of the exact post-RoPE
+              keys [review/keys: mean keys as landmarks].
+  values      the synthetic exact values V = MLP(X) + Laplace noise + spikes
+              (workload recipe, not the method).
+  residuals   R = V - MLP(K_pre) against the key decode rebuilds; keep the
+              floor(rho P) tokens with the largest ||R||_2, ties to the lower
+              index, stored in ascending token order [review/values;
+              explainer/how "Residuals for difficult tokens"; abstract].
+  window      the last W tokens exact: post-RoPE keys and values.
+  eviction    survivors of a per-head mask; landmarks compacted to them
+              (LowRAM-E / -EQ compositions of the review's tables).
+
+``exact=True`` keeps every stored array in fp64 (the invariant tests); the
+default stores bf16, or int4 group-32 codes for coefficients and residuals.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import codecs
+from .steps import reconstruct, rope, value_mlp
+
+
+def project(x_group: np.ndarray, basis: np.ndarray) -> np.ndarray:
+    """C = X B^T (fp64)."""
+    return np.asarray(x_group, np.float64) @ np.asarray(basis, np.float64).T
+
+
+def basis_block(basis: np.ndarray, cols: slice) -> np.ndarray:
+    """The (layer, head) block of B, transposed: [d][r], blk[i, m] = B[m, col(i)]."""
+    return np.ascontiguousarray(np.asarray(basis)[:, cols].T)
+
+
+def landmarks(x_pre: np.ndarray, prefix: int, chunk: int, theta: float) -> np.ndarray:
+    """Mean post-RoPE key of each chunk of the prefix, [P/S][d]."""
+    pos = np.arange(prefix)
+    k_post = rope(np.asarray(x_pre[:prefix], np.float64), pos, theta)
+    return k_post.reshape(prefix // chunk, chunk, -1).mean(axis=1)
+
+
+def exact_values(x: np.ndarray, w1, b1, w2, b2, noise, spike_pos, spike_vals) -> np.ndarray:
+    v = value_mlp(np.asarray(x, np.float64), w1, b1, w2, b2) + np.asarray(noise, np.float64)
+    v[spike_pos] += spike_vals
+    return v
+
+
+def residual_select(v_prefix: np.ndarray, k_pre_prefix: np.ndarray, w1, b1, w2, b2, n_resid: int):
+    """Indices (ascending) and rows of the n_resid worst-predicted prefix tokens."""
+    r = np.asarray(v_prefix, np.float64) - value_mlp(k_pre_prefix, w1, b1, w2, b2)
+    err = np.sqrt(np.sum(r * r, axis=1))
+    order = np.lexsort((np.arange(len(err)), -err))   # by -err, then index
+    idx = np.sort(order[:n_resid])
+    return idx.astype(np.int32), r[idx]
+
+
+def chunk_offsets(idx: np.ndarray, n_chunks: int, chunk: int) -> np.ndarray:
+    """off[c] = number of residual tokens below c * S, c = 0..nC (CSR over chunks)."""
+    bounds = np.arange(n_chunks + 1, dtype=np.int64) * chunk
+    return np.searchsorted(np.asarray(idx, np.int64), bounds, side="left").astype(np.int32)
+
+
+def _store(x, exact: bool):
+    return np.asarray(x, np.float64) if exact else codecs.bf16_encode(x)
+
+
+def compress_head(cfg, x_head: np.ndarray, coeff_stored, blk_stored, mlp, noise, spikes,
+                  exact: bool = False):
+    """Everything one (sequence, layer, KV head) stores, from its exact keys.
+
+    x_head: exact pre-RoPE keys [T][d]; coeff_stored: the group's stored
+    coefficients of the prefix tokens (as stored: bf16 bits, int4, or fp64);
+    blk_stored: stored basis block [d][r]; mlp = (w1, b1, w2, b2) as stored.
+    """
+    P, S, W = cfg.prefix, cfg.chunk, cfg.window
+    w = [np.asarray(a, np.float64) if exact else codecs.bf16_decode(a) for a in mlp]
+    v = exact_values(x_head, *w, noise, *spikes)
+
+    # the keys decode rebuilds: stored coefficients x stored basis
+    if cfg.int4 and not exact:
+        c_dec = codecs.int4_decode(*coeff_stored)
+    else:
+        c_dec = np.asarray(coeff_stored, np.float64) if exact else codecs.bf16_decode(coeff_stored)
+    blk = np.asarray(blk_stored, np.float64) if exact else codecs.bf16_decode(blk_stored)
+    k_pre = reconstruct(c_dec, blk)
+    idx, rows = residual_select(v[:P], k_pre, *w, cfg.n_resid)
+
+    out = dict(
+        landmark=_store(landmarks(x_head, P, S, cfg.rope_theta), exact),
+        res_idx=idx,
+        res_chunk_off=chunk_offsets(idx, cfg.n_chunks, S),
+        win_k=_store(rope(x_head[P:], np.arange(P, P + W), cfg.rope_theta), exact),
+        win_v=_store(v[P:], exact),
+    )
+    if cfg.int4 and not exact:
+        out["res_val"], out["res_scale"] = codecs.int4_encode(rows)
+    else:
+        out["res_val"] = _store(rows, exact)
+    return out
+
+
+def compact_landmarks(lm: np.ndarray, survivors: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(lm)[np.asarray(survivors)])

@@ -1,0 +1,124 @@
+"""Assemble the compressed cache of one layer from the seeded draws (test infrastructure).
+
+Draws come from ``synth`` (random numbers and the synthetic exact keys only);
+every arithmetic step of compression is the oracle's own (``compress``).
+Arrays come out in the layout the GPU library takes, batch major:
+
+  coeff        [NB][P][r] bf16, or [NB][P][r/2] int4 + coeff_scale [NB][P][r/32] fp16
+  basis        [NB][Hkv][d][r] bf16  (this layer's blocks of the group basis, transposed)
+  landmark     [NB][Hkv][nCand][d] bf16
+  cand_ids     [NB][Hkv][nCand] int32 (eviction only)
+  w1 [NB][Hkv][H][d], b1 [NB][Hkv][H], w2 [NB][Hkv][d][H], b2 [NB][Hkv][d] bf16
+  res_idx      [NB][Hkv][nR] int32 ascending
+  res_val      [NB][Hkv][nR][d] bf16, or [..][nR][d/2] int4 + res_scale [..][nR][d/32]
+  res_chunk_off [NB][Hkv][nC+1] int32
+  win_k, win_v [NB][Hkv][W][d] bf16
+  q            [NB][Hq][d] bf16
+"""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+
+import synth
+from . import codecs
+from .compress import basis_block, compact_landmarks, compress_head, project
+
+
+def _key_dtype(cfg):
+    return np.float64 if cfg.ctx <= 8192 else np.float32
+
+
+@functools.lru_cache(maxsize=2)
+def _group_state(cfg, b: int, grp: int, exact: bool):
+    """Exact keys, basis and stored coefficients of one (sequence, group)."""
+    x = synth.exact_keys(cfg, b, grp, dtype=_key_dtype(cfg))
+    B = synth.basis(cfg, b, grp)
+    c = project(x[: cfg.prefix], B)
+    if exact:
+        c_st = c
+    elif cfg.int4:
+        c_st = codecs.int4_encode(c)
+    else:
+        c_st = codecs.bf16_encode(c)
+    return x, B, c_st
+
+
+def build_layer(cfg, layer: int, batch=None, exact: bool = False):
+    """Compressed cache + queries of ``layer`` for the batch elements ``batch``."""
+    batch = list(range(cfg.batch)) if batch is None else list(batch)
+    G, Hkv = cfg.group_layers, cfg.n_heads_kv
+    grp = layer // G
+    per_b = []
+    for b in batch:
+        x, B, c_st = _group_state(cfg, b, grp, exact)
+        heads = []
+        for h in range(Hkv):
+            cols = synth.layer_cols(cfg, layer, h)
+            blk = basis_block(B, cols)
+            blk_st = blk if exact else codecs.bf16_encode(blk)
+            mlp = synth.mlp_weights(cfg, b, layer, h)
+            mlp_st = tuple(np.asarray(a, np.float64) if exact else codecs.bf16_encode(a) for a in mlp)
+            noise = synth.value_noise(cfg, b, layer, h)
+            spikes = synth.value_spikes(cfg, b, layer, h)
+            hd = compress_head(cfg, np.asarray(x[:, cols], np.float64), c_st, blk_st, mlp_st,
+                               noise, spikes, exact=exact)
+            hd["basis"] = blk_st
+            hd["w1"], hd["b1"], hd["w2"], hd["b2"] = mlp_st
+            if cfg.evict:
+                surv = synth.survivors(cfg, b, layer, h)
+                hd["landmark"] = compact_landmarks(hd["landmark"], surv)
+                hd["cand_ids"] = surv
+            heads.append(hd)
+        q = synth.queries(cfg, b, layer)
+        if cfg.needle:
+            cs = synth.needle_chunks(cfg, b, layer)
+            rows = np.stack([codecs.bf16_decode(heads[h]["landmark"][cs[h]]) if not exact
+                             else heads[h]["landmark"][cs[h]] for h in range(Hkv)])
+            q = synth.plant_needle(q, cfg.gqa, rows)
+        per_b.append((c_st, heads, q if exact else codecs.bf16_encode(q)))
+
+    cache = {}
+    if cfg.int4 and not exact:
+        cache["coeff"] = np.stack([p[0][0] for p in per_b])
+        cache["coeff_scale"] = np.stack([p[0][1] for p in per_b])
+    else:
+        cache["coeff"] = np.stack([p[0] for p in per_b])
+    keys = ["basis", "landmark", "w1", "b1", "w2", "b2", "res_idx", "res_val",
+            "res_chunk_off", "win_k", "win_v"]
+    if cfg.int4 and not exact:
+        keys.append("res_scale")
+    if cfg.evict:
+        keys.append("cand_ids")
+    for k in keys:
+        cache[k] = np.ascontiguousarray(np.stack([np.stack([hd[k] for hd in p[1]]) for p in per_b]))
+    cache["q"] = np.stack([p[2] for p in per_b])
+    if cfg.needle:
+        cache["needle"] = np.stack([synth.needle_chunks(cfg, b, layer) for b in batch])
+    return cache
+
+
+def dense_layer(cfg, layer: int, batch=None):
+    """Exact bf16 dense cache K (post-RoPE), V [NB][Hkv][T][d] and q (baseline).
+
+    The same synthetic model state the compressed cache is built from.
+    """
+    from .compress import exact_values
+    from .steps import rope
+    batch = list(range(cfg.batch)) if batch is None else list(batch)
+    grp = layer // cfg.group_layers
+    ks, vs, qs = [], [], []
+    for b in batch:
+        x = synth.exact_keys(cfg, b, grp, dtype=_key_dtype(cfg))
+        kh, vh = [], []
+        for h in range(cfg.n_heads_kv):
+            xh = np.asarray(x[:, synth.layer_cols(cfg, layer, h)], np.float64)
+            kh.append(codecs.bf16_encode(rope(xh, np.arange(cfg.ctx), cfg.rope_theta)))
+            w = [codecs.bf16_round(a) for a in synth.mlp_weights(cfg, b, layer, h)]
+            v = exact_values(xh, *w, synth.value_noise(cfg, b, layer, h), *synth.value_spikes(cfg, b, layer, h))
+            vh.append(codecs.bf16_encode(v))
+        ks.append(np.stack(kh))
+        vs.append(np.stack(vh))
+        qs.append(codecs.bf16_encode(synth.queries(cfg, b, layer)))
+    return np.stack(ks), np.stack(vs), np.stack(qs)

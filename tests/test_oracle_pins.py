@@ -1,0 +1,335 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Every pin uses an independent formulation: a library routine (torch SDPA,
+torch GELU, numpy lstsq, numpy stable argsort), a closed form (complex
+rotation), a brute force on tiny inputs, or a whole-step invariant of the
+method (full rank + all chunks + all residuals == dense attention).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings
+from hypothesis import strategies as st
+
+import synth
+from oracle import codecs, compress, decode, fixture, steps
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------ codecs --
+def test_bf16_golden():
+    g = json.load(open(os.path.join(GOLDEN, "codecs.json")))
+    for e in g["bf16"]:
+        assert codecs.bf16_encode(np.array([e["x"]]))[0] == int(e["bits"], 16), e
+
+
+def test_bf16_matches_torch_rne():
+    x = np.random.default_rng(0).standard_normal(100000) * np.exp(np.random.default_rng(1).uniform(-20, 20, 100000))
+    ours = codecs.bf16_encode(x)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(codecs.bf16_decode(ours), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
+
+
+def test_int4_golden():
+    g = json.load(open(os.path.join(GOLDEN, "codecs.json")))["int4"]
+    packed, sc = codecs.int4_encode(np.array(g["x"])[None, :])
+    assert sc[0, 0] == int(g["scale_bits"], 16)
+    assert [f"{b:02x}" for b in packed[0, :4]] == g["packed_first4"]
+    assert list(codecs.int4_codes(packed)[0, :8]) == g["codes"]
+    z, zs = codecs.int4_encode(np.zeros((1, 32)))
+    assert zs[0, 0] == 0 and not z.any()
+
+
+def test_int4_roundtrip_bound():
+    x = np.random.default_rng(2).standard_normal((64, 256)) * 3
+    p, s = codecs.int4_encode(x)
+    y = codecs.int4_decode(p, s)
+    scale = np.repeat(codecs.fp16_decode(s), 32, axis=-1)
+    absmax = np.repeat(np.abs(x).reshape(64, 8, 32).max(-1), 32, axis=-1)
+    assert np.all(np.abs(y - x) <= scale / 2 + absmax * 2.0 ** -10 + 1e-12)
+    assert np.all(np.abs(codecs.int4_codes(p)) <= 7)
+
+
+# -------------------------------------------------------------- RoPE --
+def complex_rope(x, pos, theta):
+    """RoPE as multiplication of z = x[:h] + i x[h:] by exp(i pos f)."""
+    d = x.shape[1]
+    h = d // 2
+    f = np.exp(-(2.0 * np.arange(h) / d) * math.log(theta))
+    z = (x[:, :h] + 1j * x[:, h:]) * np.exp(1j * np.outer(pos, f))
+    return np.concatenate([z.real, z.imag], axis=1)
+
+
+@pytest.mark.parametrize("theta", [1e4, 5e5, 1e6])
+def test_rope_complex_form(theta):
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((50, 128))
+    pos = rng.integers(0, 262144, 50)
+    assert np.allclose(steps.rope(x, pos, theta), complex_rope(x, pos, theta), atol=1e-9)
+
+
+def test_rope_identity_norm_relative():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((20, 128))
+    assert np.allclose(steps.rope(x, np.zeros(20), 5e5), x)
+    y = steps.rope(x, rng.integers(0, 10 ** 5, 20), 5e5)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1))
+    q, k = rng.standard_normal((1, 128)), rng.standard_normal((1, 128))
+    for m, n in [(7, 3), (1000, 10), (262143, 100000)]:
+        a = steps.rope(q, [m], 5e5) @ steps.rope(k, [n], 5e5).T
+        b = steps.rope(q, [m - n], 5e5) @ k.T
+        assert np.allclose(a, b, atol=1e-9)
+
+
+def test_rope_angle_by_atan2():
+    d, theta, t = 128, 1e4, 37
+    x = np.zeros((d // 2, d))
+    x[np.arange(d // 2), np.arange(d // 2)] = 1.0
+    y = steps.rope(x, np.full(d // 2, t), theta)
+    ang = np.arctan2(y[np.arange(d // 2), np.arange(d // 2) + d // 2], y[np.arange(d // 2), np.arange(d // 2)])
+    want = np.mod(t * theta ** (-np.arange(0, d, 2) / d) + np.pi, 2 * np.pi) - np.pi
+    assert np.allclose(ang, want, atol=1e-12)
+
+
+# ------------------------------------------------------- GELU / MLP --
+def test_gelu_against_math_erf_and_torch():
+    xs = np.linspace(-9, 9, 2001)
+    want = np.array([0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in xs])
+    assert np.allclose(steps.gelu(xs), want, atol=1e-15, rtol=1e-14)
+    t = torch.nn.functional.gelu(torch.from_numpy(xs), approximate="none").numpy()
+    assert np.allclose(steps.gelu(xs), t, atol=1e-15, rtol=1e-14)
+
+
+def test_value_mlp_against_torch_layers():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((33, 128))
+    w1, b1, w2, b2 = rng.standard_normal((256, 128)) * .1, rng.standard_normal(256), rng.standard_normal((128, 256)) * .1, rng.standard_normal(128)
+    l1, l2 = torch.nn.Linear(128, 256).double(), torch.nn.Linear(256, 128).double()
+    with torch.no_grad():
+        l1.weight[:], l1.bias[:], l2.weight[:], l2.bias[:] = map(torch.from_numpy, (w1, b1, w2, b2))
+        ref = l2(torch.nn.GELU()(l1(torch.from_numpy(x)))).numpy()
+    assert np.allclose(steps.value_mlp(x, w1, b1, w2, b2), ref, atol=1e-12)
+
+
+# --------------------------------------------------------- attention --
+def test_attend_against_torch_sdpa_gqa():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((8, 128))
+    k = rng.standard_normal((2, 300, 128))
+    v = rng.standard_normal((2, 300, 128))
+    ours = np.stack([steps.attend(q[j], k[j // 4], v[j // 4], 1 / math.sqrt(128)) for j in range(8)])
+    kk = torch.from_numpy(k).repeat_interleave(4, dim=0)
+    vv = torch.from_numpy(v).repeat_interleave(4, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q)[:, None, :], kk, vv)[:, 0].numpy()
+    assert np.allclose(ours, ref, atol=1e-12)
+
+
+def test_attend_special_cases():
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((1, 16))
+    assert np.allclose(steps.attend(rng.standard_normal(16), rng.standard_normal((1, 16)), v, 1.0), v[0])
+    vv = rng.standard_normal((9, 16))
+    assert np.allclose(steps.attend(np.zeros(16), rng.standard_normal((9, 16)), vv, 1.0), vv.mean(0))
+
+
+def test_dense_step_against_sdpa():
+    rng = np.random.default_rng(8)
+    k = rng.standard_normal((2, 2, 100, 128))
+    v = rng.standard_normal((2, 2, 100, 128))
+    q = rng.standard_normal((2, 8, 128))
+    ours = decode.dense_step(k, v, q, n_heads_kv=2)
+    kk = torch.from_numpy(k).repeat_interleave(4, dim=1)
+    vv = torch.from_numpy(v).repeat_interleave(4, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q)[:, :, None, :], kk, vv)[:, :, 0].numpy()
+    assert np.allclose(ours, ref, atol=1e-12)
+
+
+# ---------------------------------------------------- landmark / topk --
+def test_landmark_scores_max_over_group():
+    rng = np.random.default_rng(9)
+    q, lm = rng.standard_normal((4, 128)), rng.standard_normal((50, 128))
+    s = steps.landmark_scores(q, lm)
+    for c in range(50):
+        assert math.isclose(s[c], max(float(np.dot(q[j], lm[c])) for j in range(4)), rel_tol=1e-12, abs_tol=1e-12)
+
+
+def topk_by_threshold(s, k):
+    """Independent form: all scores above the k-th largest value, then the
+    lowest-index ties at that value."""
+    n = len(s)
+    if k >= n:
+        return np.arange(n)
+    kth = np.sort(s)[::-1][k - 1]
+    above = np.nonzero(s > kth)[0]
+    ties = np.nonzero(s == kth)[0][: k - len(above)]
+    return np.sort(np.concatenate([above, ties]))
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.lists(st.integers(-5, 5), min_size=1, max_size=60), st.integers(1, 70))
+def test_topk_with_ties_against_threshold_form(vals, k):
+    s = np.array(vals, dtype=np.float64)
+    got = steps.select_topk(s, k)
+    assert np.array_equal(got, topk_by_threshold(s, k))
+    order = np.argsort(-s, kind="stable")[: min(k, len(s))]
+    assert np.array_equal(got, np.sort(order))
+
+
+def test_topk_candidates_map_ids():
+    s = np.array([3.0, 1.0, 3.0, 2.0])
+    ids = np.array([4, 9, 11, 20])
+    assert list(steps.select_topk(s, 2, ids)) == [4, 11]
+    assert list(steps.select_topk(s, 9, ids)) == [4, 9, 11, 20]
+
+
+# ------------------------------------------------ reconstruction etc. --
+def test_reconstruct_is_orthogonal_projection():
+    cfg = synth.C0
+    B = synth.basis(cfg, 0, 0)
+    assert np.allclose(B @ B.T, np.eye(cfg.rank), atol=1e-12)
+    x = synth.exact_keys(cfg, 0, 0, 0, 300)
+    c = compress.project(x, B)
+    cols = synth.layer_cols(cfg, 1, 1)
+    got = steps.reconstruct(c, compress.basis_block(B, cols))
+    a, *_ = np.linalg.lstsq(B.T, x.T, rcond=None)
+    want = (B.T @ a).T[:, cols]
+    assert np.allclose(got, want, atol=1e-10)
+    # the keys live in the latent subspace: projection leaves only the noise out
+    err = np.linalg.norm(got - x[:, cols]) / np.linalg.norm(x[:, cols])
+    assert err < 0.1
+
+
+def test_landmarks_are_chunk_means_of_rotated_keys():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((64, 128))
+    lm = compress.landmarks(x, 64, 8, 1e4)
+    ref = complex_rope(x, np.arange(64), 1e4)
+    for c in range(8):
+        assert np.allclose(lm[c], sum(ref[8 * c + i] for i in range(8)) / 8, atol=1e-12)
+
+
+def test_residual_select_brute_force_and_offsets():
+    rng = np.random.default_rng(11)
+    cfg = synth.C0
+    w = synth.mlp_weights(cfg, 0, 0, 0)
+    kp = rng.standard_normal((40, 128))
+    v = rng.standard_normal((40, 128))
+    v[[3, 17]] = steps.value_mlp(kp[[3, 17]], *w) + 5.0   # two tokens far off, equal error
+    idx, rows = compress.residual_select(v, kp, *w, 5)
+    errs = [float(np.linalg.norm(v[t] - steps.value_mlp(kp[t:t + 1], *w)[0])) for t in range(40)]
+    brute = sorted(sorted(range(40), key=lambda t: (-errs[t], t))[:5])
+    assert list(idx) == brute and 3 in idx and 17 in idx
+    off = compress.chunk_offsets(idx, 5, 8)
+    assert [sum(1 for t in idx if t < 8 * c) for c in range(6)] == list(off)
+
+
+# ------------------------------------------------ whole-step invariants --
+def full_cfg():
+    """Tiny workload where rank = G*Hkv*d, k = nC and every token has a residual."""
+    return synth.C0.with_(name="ns1", ctx=512, window=32, rank=512, topk=10 ** 6, resid_frac=1.0,
+                          bias_std=0.1)
+
+
+def dense_reference(cfg, layer, exact=True):
+    """Exact post-RoPE keys (complex form) and exact values of every token.
+
+    The synthetic values come from the predictor's weights as stored (bf16
+    unless exact), like the cache they are compared with.
+    """
+    ks, vs = [], []
+    x = synth.exact_keys(cfg, 0, layer // cfg.group_layers)
+    for h in range(cfg.n_heads_kv):
+        xh = x[:, synth.layer_cols(cfg, layer, h)]
+        ks.append(complex_rope(xh, np.arange(cfg.ctx), cfg.rope_theta))
+        w = synth.mlp_weights(cfg, 0, layer, h)
+        w = w if exact else [codecs.bf16_round(a) for a in w]
+        vs.append(compress.exact_values(xh, *w, synth.value_noise(cfg, 0, layer, h), *synth.value_spikes(cfg, 0, layer, h)))
+    return np.stack(ks)[None], np.stack(vs)[None]
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_ns1_full_rank_all_chunks_all_residuals_equals_dense(layer):
+    cfg = full_cfg()
+    cache = fixture.build_layer(cfg, layer, exact=True)
+    out, st_ = decode.decode_step(cfg, cache, cache["q"])
+    k, v = dense_reference(cfg, layer)
+    kk = torch.from_numpy(k).repeat_interleave(cfg.gqa, dim=1)
+    vv = torch.from_numpy(v).repeat_interleave(cfg.gqa, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(cache["q"])[:, :, None, :], kk, vv)[:, :, 0].numpy()
+    assert np.max(np.abs(out - ref)) < 1e-10
+    assert len(st_[(0, 0)]["sel"]) == cfg.n_chunks
+
+
+def test_ns1_in_bf16_storage_within_rounding():
+    cfg = full_cfg()
+    cache = fixture.build_layer(cfg, 0)
+    out, _ = decode.decode_step(cfg, cache, cache["q"])
+    k, v = dense_reference(cfg, 0, exact=False)
+    q = codecs.bf16_decode(cache["q"])
+    ref = decode.dense_step(k, v, q, cfg.n_heads_kv)
+    rel = np.linalg.norm(out - ref) / np.linalg.norm(ref)
+    assert rel < 1e-2, rel
+
+
+def test_ns3_mlp_plus_residual_reproduces_values():
+    cfg = full_cfg().with_(resid_frac=0.25)
+    for exact in (True, False):
+        cache = fixture.build_layer(cfg, 0, exact=exact)
+        _, st_ = decode.decode_step(cfg, cache, cache["q"])
+        _, v = dense_reference(cfg, 0, exact)
+        for h in range(cfg.n_heads_kv):
+            s = st_[(0, h)]
+            ridx = cache["res_idx"][0, h]
+            pos = np.nonzero(np.isin(s["tokens"], ridx))[0]
+            assert len(pos) == len(ridx)
+            got, want = s["v_hat"][pos], v[0, h][s["tokens"][pos]]
+            if exact:
+                assert np.max(np.abs(got - want)) < 1e-10
+            else:
+                r = want - steps.value_mlp(s["k_pre"][pos], *[codecs.bf16_decode(cache[n][0, h]) for n in ("w1", "b1", "w2", "b2")])
+                assert np.all(np.abs(got - want) <= np.abs(r) * 2.0 ** -8 + 1e-12)
+
+
+def test_eviction_that_evicts_nothing_is_the_plain_path():
+    cfg = synth.C0
+    cache = fixture.build_layer(cfg, 0)
+    out0, _ = decode.decode_step(cfg, cache, cache["q"])
+    c2 = dict(cache)
+    c2["cand_ids"] = np.broadcast_to(np.arange(cfg.n_chunks, dtype=np.int32), (1, cfg.n_heads_kv, cfg.n_chunks)).copy()
+    out1, _ = decode.decode_step(cfg, c2, cache["q"])
+    assert np.array_equal(out0, out1)
+
+
+def test_selection_override_matches_own_selection():
+    cfg = synth.C0
+    cache = fixture.build_layer(cfg, 1)
+    out0, st_ = decode.decode_step(cfg, cache, cache["q"])
+    sel = [[st_[(0, h)]["sel"] for h in range(cfg.n_heads_kv)]]
+    out1, _ = decode.decode_step(cfg, cache, cache["q"], sel_override=sel)
+    assert np.array_equal(out0, out1)
+
+
+def test_needle_chunk_is_selected():
+    cfg = synth.C2.with_(name="needle_small", batch=1, ctx=8192, window=128, n_layers=4, rank=128, topk=16)
+    cache = fixture.build_layer(cfg, 1)
+    _, st_ = decode.decode_step(cfg, cache, cache["q"])
+    for h in range(cfg.n_heads_kv):
+        assert cache["needle"][0, h] in st_[(0, h)]["sel"]
+
+
+def test_int4_eviction_cache_decodes():
+    cfg = synth.C4.with_(name="c4_small", batch=1, ctx=4096, window=64, n_layers=4, topk=32)
+    cache = fixture.build_layer(cfg, 2)
+    assert cache["coeff"].dtype == np.uint8 and cache["coeff"].shape == (1, cfg.prefix, cfg.rank // 2)
+    assert cache["landmark"].shape[2] == cfg.n_cand == cfg.n_chunks - cfg.n_chunks // 2
+    assert np.all(cache["cand_ids"][0, :, :4] == np.arange(4))
+    out, st_ = decode.decode_step(cfg, cache, cache["q"])
+    assert np.all(np.isfinite(out))
+    for h in range(cfg.n_heads_kv):
+        assert np.all(np.isin(st_[(0, h)]["sel"], cache["cand_ids"][0, h]))
