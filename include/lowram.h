@@ -1,0 +1,176 @@
+/*
+ * lowram.h — C ABI of the LowRAM decode-step library (gfx950 / MI355X).
+ *
+ * One call runs the decode-time attention of one layer for a batch of
+ * sequences against their compressed KV cache, as the LowRAM pages describe
+ * it: the prefix is cut into chunks of S tokens whose mean post-RoPE key is a
+ * landmark; each step scores the current query against the landmarks, keeps
+ * the top-k chunks per KV head, rebuilds only those chunks' keys from
+ * cross-layer low-rank coefficients times the layer-group basis and rotates
+ * them at their token positions, predicts their values with the per-head
+ * key-to-value MLP plus the stored residuals of the worst-predicted tokens,
+ * and attends over them and the exact recent window.
+ *   - LowRAM review (agihunt.info), key paragraph: xKV shared basis, RoPE
+ *     undone before compression, chunked prefix, mean-key landmarks, top-k
+ *     chunks rebuilt per query.
+ *   - LowRAM explainer (cctest.ai), "How the method works": low-rank keys,
+ *     amortised values, residuals for difficult tokens, selective
+ *     reconstruction.
+ *   - LowRAM abstract: a selected subset of KV pairs rebuilt per step.
+ *
+ * Conventions for every entry point
+ *   - Array arguments are DEVICE pointers; the caller owns them.  The library
+ *     never allocates, frees or synchronises: all work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the null stream) and returns at once.
+ *   - bf16 and fp16 values travel as uint16_t bit patterns.
+ *   - Arrays are dense, row-major, batch-major, in the layouts stated below,
+ *     sliced to ONE layer by the caller.
+ *   - Bulk arrays must be 16-byte aligned; int32/fp16 side arrays 4-byte.
+ *   - Status: 0 on success, a negative LOWRAM_ERR_* otherwise.  Argument
+ *     errors (NULL, SHAPE, UNSUPPORTED, WORKSPACE, ALIGN) are detected before
+ *     any HIP call; LOWRAM_ERR_HIP reports a failed launch.
+ *   - Calls are re-entrant for distinct workspaces; two calls that share a
+ *     workspace must be ordered on one stream.
+ */
+#ifndef LOWRAM_H
+#define LOWRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOWRAM_ABI_VERSION 1
+
+enum {
+  LOWRAM_OK = 0,
+  LOWRAM_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  LOWRAM_ERR_SHAPE = -2,       /* inconsistent sizes (e.g. Hq % Hkv, P % S, k < 1)   */
+  LOWRAM_ERR_UNSUPPORTED = -3, /* valid but not built (d != 128, S != 8, H != 256...) */
+  LOWRAM_ERR_WORKSPACE = -4,   /* workspace smaller than *_workspace_bytes reports    */
+  LOWRAM_ERR_ALIGN = -5,       /* misaligned pointer                                 */
+  LOWRAM_ERR_HIP = -6          /* a HIP launch failed                                */
+};
+
+/* Storage format of the coefficients C and of the residual values. */
+enum {
+  LOWRAM_FMT_BF16 = 0,
+  /* int4 symmetric per group of 32 along the last axis: codes in [-7, 7],
+     two per byte (even element in the low nibble, two's complement), one
+     fp16 scale per group; value = float(code) * float(scale).  This is the
+     quantised composition (LowRAM-Q / -EQ) of the LowRAM review's tables. */
+  LOWRAM_FMT_INT4_G32 = 1
+};
+
+/* Sizes of one layer's decode step. */
+typedef struct lowram_shape {
+  int32_t batch;         /* NB >= 1 sequences                                        */
+  int32_t prefix_len;    /* P >= 0 compressed tokens, a multiple of chunk            */
+  int32_t window;        /* W >= 0 exact recent tokens at positions P .. P+W-1       */
+  int32_t chunk;         /* S, tokens per chunk; this build supports 8               */
+  int32_t n_heads_q;     /* Hq, a multiple of n_heads_kv, Hq/Hkv <= 16               */
+  int32_t n_heads_kv;    /* Hkv >= 1                                                 */
+  int32_t head_dim;      /* d; this build supports 128                               */
+  int32_t rank;          /* r, coefficients per token; 64, 128, 256 or 512           */
+  int32_t mlp_hidden;    /* H, value-MLP width; this build supports 256              */
+  int32_t topk;          /* k >= 1 chunks kept per KV head (all if fewer candidates) */
+  int32_t n_resid;       /* nR >= 0 stored residual rows per (sequence, KV head)     */
+  int32_t n_cand;        /* candidates per (sequence, KV head): P/S without eviction,
+                            the survivor count with cand_ids                          */
+  int32_t coeff_fmt;     /* LOWRAM_FMT_* of coeff                                    */
+  int32_t resid_fmt;     /* LOWRAM_FMT_* of res_val                                  */
+  float rope_theta;      /* RoPE base; rotate-half pairing (i, i + d/2),
+                            angle = position * theta^(-2i/d)                          */
+  float softmax_scale;   /* logit scale, usually 1/sqrt(d)                           */
+} lowram_shape;
+
+/* One layer's compressed cache (all device pointers). */
+typedef struct lowram_layer_cache {
+  const void* coeff;            /* bf16: [NB][P][r];  int4: [NB][P][r/2] bytes                */
+  const uint16_t* coeff_scale;  /* int4 only: [NB][P][r/32] fp16; NULL for bf16               */
+  const uint16_t* basis;        /* [NB][Hkv][d][r] bf16: this layer's block of the group
+                                   basis, transposed (basis[i][m] = B[m][col(layer,head,i)])  */
+  const uint16_t* landmark;     /* [NB][Hkv][n_cand][d] bf16, mean post-RoPE key per chunk     */
+  const int32_t* cand_ids;      /* [NB][Hkv][n_cand] ascending chunk ids of the candidates
+                                   (eviction survivors), or NULL = every chunk 0..P/S-1       */
+  const uint16_t* w1;           /* [NB][Hkv][H][d] bf16 value-MLP layer 1 weight              */
+  const uint16_t* b1;           /* [NB][Hkv][H]    bf16                                        */
+  const uint16_t* w2;           /* [NB][Hkv][d][H] bf16 layer 2 weight                        */
+  const uint16_t* b2;           /* [NB][Hkv][d]    bf16                                        */
+  const int32_t* res_idx;       /* [NB][Hkv][nR] ascending token ids (< P) with a residual    */
+  const void* res_val;          /* bf16: [NB][Hkv][nR][d];  int4: [NB][Hkv][nR][d/2] bytes    */
+  const uint16_t* res_scale;    /* int4 only: [NB][Hkv][nR][d/32] fp16; NULL for bf16         */
+  const int32_t* res_chunk_off; /* [NB][Hkv][P/S + 1]: res_idx rows of chunk c are
+                                   [off[c], off[c+1]) (see lowram_resid_chunk_offsets)        */
+  const uint16_t* win_k;        /* [NB][Hkv][W][d] bf16 post-RoPE keys of the window          */
+  const uint16_t* win_v;        /* [NB][Hkv][W][d] bf16 values of the window                  */
+} lowram_layer_cache;
+
+int lowram_abi_version(void);
+const char* lowram_strerror(int status);
+
+/* Bytes of device workspace lowram_decode_step needs for `shape` (a pure
+   function of the shape; no HIP call). */
+int lowram_workspace_bytes(const lowram_shape* shape, size_t* bytes);
+
+/*
+ * One decode step of one layer.
+ *   q        [NB][Hq][d] bf16 post-RoPE queries; query head j uses KV head
+ *            j / (Hq/Hkv) (GQA, LowRAM review, motivation paragraph).
+ *   out      [NB][Hq][d] bf16 attention output (written).
+ *   sel_out  optional [NB][Hkv][k] int32: the selected chunk ids, ascending,
+ *            padded with -1 when fewer than k candidates exist; may be NULL.
+ *   workspace / ws_bytes: device scratch of at least lowram_workspace_bytes.
+ * Score of a candidate chunk c for KV head h: max over h's query heads j of
+ * q_j . landmark[c] (raw dot product); the k largest are kept, exact ties
+ * going to the lower chunk id.
+ */
+int lowram_decode_step(const lowram_shape* shape, const lowram_layer_cache* cache,
+                       const uint16_t* q, uint16_t* out, int32_t* sel_out,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * lowram_decode_step that also writes its intermediate stages (for stage
+ * parity checks).  Every stage pointer may be NULL.
+ *   scores_out [NB][Hkv][n_cand] fp32 landmark scores
+ *   kpre_out, kpost_out, vhat_out [NB][Hkv][k*S][d] fp32: rebuilt pre-RoPE
+ *            keys, rotated keys, predicted values + residuals, rows in the
+ *            order of sel_out's chunks (ascending), S rows per chunk.
+ */
+int lowram_decode_stages(const lowram_shape* shape, const lowram_layer_cache* cache,
+                         const uint16_t* q, uint16_t* out, int32_t* sel_out,
+                         float* scores_out, float* kpre_out, float* kpost_out,
+                         float* vhat_out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Dense GQA decode over the full bf16 cache: the uncompressed baseline the
+   LowRAM pages compare against (review, results paragraph). */
+typedef struct dense_shape {
+  int32_t batch, ctx_len, n_heads_q, n_heads_kv, head_dim;
+  float softmax_scale;
+} dense_shape;
+
+typedef struct dense_layer_cache {
+  const uint16_t* k;  /* [NB][Hkv][T][d] bf16 post-RoPE keys */
+  const uint16_t* v;  /* [NB][Hkv][T][d] bf16 values         */
+} dense_layer_cache;
+
+int dense_workspace_bytes(const dense_shape* shape, size_t* bytes);
+int dense_decode_step(const dense_shape* shape, const dense_layer_cache* cache,
+                      const uint16_t* q, uint16_t* out, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/*
+ * Cache-layout helper: chunk_off[l][c] = number of entries of res_idx[l]
+ * below c*chunk, c = 0..n_chunks, for n_lists ascending lists of n_resid
+ * token ids each (res_idx [n_lists][n_resid], chunk_off [n_lists][n_chunks+1]).
+ */
+int lowram_resid_chunk_offsets(const int32_t* res_idx, int32_t n_lists, int32_t n_resid,
+                               int32_t n_chunks, int32_t chunk, int32_t* chunk_off,
+                               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LOWRAM_H */

@@ -1,0 +1,241 @@
+// C ABI of the LowRAM decode-step library: argument checks (before any HIP
+// call), workspace carving, and the launch sequence
+//   score (landmark GEMV) -> select (exact top-k) -> attend (fused rebuild +
+//   split-K attention, window included) -> merge (log-sum-exp of the splits).
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/lowram.h"
+#include "common.h"
+#include "internal.h"
+
+namespace {
+
+using namespace lowram;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+struct Plan {
+  int g, n_chunks, n_cand, k_eff, n_sel_tiles, n_win_tiles, n_split;
+  size_t off_keys, off_sel, off_part, total;
+};
+
+int check_shape(const lowram_shape* s) {
+  if (!s) return LOWRAM_ERR_NULL;
+  if (s->batch < 1 || s->prefix_len < 0 || s->window < 0 || s->n_heads_q < 1 ||
+      s->n_heads_kv < 1 || s->topk < 1 || s->n_resid < 0 || s->chunk < 1 || s->head_dim < 1 ||
+      s->rank < 1 || s->mlp_hidden < 1)
+    return LOWRAM_ERR_SHAPE;
+  if (s->n_heads_q % s->n_heads_kv) return LOWRAM_ERR_SHAPE;
+  if (s->prefix_len % s->chunk) return LOWRAM_ERR_SHAPE;
+  if (s->prefix_len + s->window < 1) return LOWRAM_ERR_SHAPE;
+  if (s->n_resid > s->prefix_len) return LOWRAM_ERR_SHAPE;
+  if (s->coeff_fmt != LOWRAM_FMT_BF16 && s->coeff_fmt != LOWRAM_FMT_INT4_G32) return LOWRAM_ERR_SHAPE;
+  if (s->resid_fmt != LOWRAM_FMT_BF16 && s->resid_fmt != LOWRAM_FMT_INT4_G32) return LOWRAM_ERR_SHAPE;
+  if (!(s->rope_theta > 0.f) || !std::isfinite(s->rope_theta)) return LOWRAM_ERR_SHAPE;
+  if (!std::isfinite(s->softmax_scale)) return LOWRAM_ERR_SHAPE;
+  const int n_chunks = s->prefix_len / s->chunk;
+  if (s->n_cand < 0 || s->n_cand > n_chunks) return LOWRAM_ERR_SHAPE;
+  if (s->chunk != kChunk || s->head_dim != kHeadDim || s->mlp_hidden != kHidden)
+    return LOWRAM_ERR_UNSUPPORTED;
+  if (s->n_heads_q / s->n_heads_kv > 16) return LOWRAM_ERR_UNSUPPORTED;
+  if (s->rank != 64 && s->rank != 128 && s->rank != 256 && s->rank != 512) return LOWRAM_ERR_UNSUPPORTED;
+  if (s->coeff_fmt == LOWRAM_FMT_INT4_G32 && s->rank % 128) return LOWRAM_ERR_UNSUPPORTED;
+  // 32-bit index arithmetic inside the kernels
+  if ((int64_t)s->batch * s->prefix_len >= (int64_t)1 << 31) return LOWRAM_ERR_UNSUPPORTED;
+  return LOWRAM_OK;
+}
+
+Plan make_plan(const lowram_shape* s) {
+  Plan p{};
+  p.g = s->n_heads_q / s->n_heads_kv;
+  p.n_chunks = s->prefix_len / s->chunk;
+  p.n_cand = s->n_cand;
+  p.k_eff = p.n_cand < s->topk ? p.n_cand : s->topk;
+  p.n_sel_tiles = (p.k_eff + kAttChunksWG - 1) / kAttChunksWG;
+  p.n_win_tiles = (s->window + kAttTokWG - 1) / kAttTokWG;
+  p.n_split = p.n_sel_tiles + p.n_win_tiles;
+  const size_t heads = (size_t)s->batch * s->n_heads_kv;
+  p.off_keys = 0;
+  p.off_sel = align_up(heads * (size_t)p.n_cand * 4);
+  p.off_part = p.off_sel + align_up(heads * (size_t)p.k_eff * 4);
+  p.total = p.off_part + align_up(heads * (size_t)p.n_split * p.g * kPartStride * 4);
+  return p;
+}
+
+int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t* q, uint16_t* out,
+             int32_t* sel_out, float* scores_out, float* kpre_out, float* kpost_out,
+             float* vhat_out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (!c || !q || !out || !ws) return LOWRAM_ERR_NULL;
+  const Plan p = make_plan(s);
+  const bool has_prefix = s->prefix_len > 0 && p.n_cand > 0;
+  const bool ci4 = s->coeff_fmt == LOWRAM_FMT_INT4_G32, ri4 = s->resid_fmt == LOWRAM_FMT_INT4_G32;
+  if (has_prefix) {
+    if (!c->coeff || !c->basis || !c->landmark || !c->w1 || !c->b1 || !c->w2 || !c->b2 ||
+        !c->res_chunk_off)
+      return LOWRAM_ERR_NULL;
+    if (s->n_resid > 0 && (!c->res_idx || !c->res_val)) return LOWRAM_ERR_NULL;
+    if (ci4 && !c->coeff_scale) return LOWRAM_ERR_NULL;
+    if (ri4 && s->n_resid > 0 && !c->res_scale) return LOWRAM_ERR_NULL;
+    if (!c->cand_ids && p.n_cand != p.n_chunks) return LOWRAM_ERR_SHAPE;
+  }
+  if (s->window > 0 && (!c->win_k || !c->win_v)) return LOWRAM_ERR_NULL;
+  const void* bulk[] = {q, out, ws, c->coeff, c->basis, c->landmark, c->w1, c->w2, c->res_val,
+                        c->win_k, c->win_v};
+  for (const void* ptr : bulk)
+    if (ptr && misaligned(ptr, 16)) return LOWRAM_ERR_ALIGN;
+  const void* small[] = {c->coeff_scale, c->cand_ids, c->b1, c->b2, c->res_idx, c->res_scale,
+                         c->res_chunk_off, sel_out, scores_out, kpre_out, kpost_out, vhat_out};
+  for (const void* ptr : small)
+    if (ptr && misaligned(ptr, 4)) return LOWRAM_ERR_ALIGN;
+  if (kpre_out && misaligned(kpre_out, 16)) return LOWRAM_ERR_ALIGN;
+  if (kpost_out && misaligned(kpost_out, 16)) return LOWRAM_ERR_ALIGN;
+  if (ws_bytes < p.total) return LOWRAM_ERR_WORKSPACE;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(w + p.off_keys);
+  int32_t* sel = reinterpret_cast<int32_t*>(w + p.off_sel);
+  float* part = reinterpret_cast<float*>(w + p.off_part);
+
+  if (has_prefix) {
+    if (launch_score(q, c->landmark, keys, scores_out, s->batch, p.n_cand, s->n_heads_q,
+                     s->n_heads_kv, hs) != hipSuccess)
+      return LOWRAM_ERR_HIP;
+  }
+  if (has_prefix || sel_out) {
+    if (launch_select(keys, c->cand_ids, sel, sel_out, s->batch, p.n_cand, s->topk, s->n_heads_kv,
+                      hs) != hipSuccess)
+      return LOWRAM_ERR_HIP;
+  }
+  AttendArgs a{};
+  a.coeff = c->coeff; a.coeff_scale = c->coeff_scale; a.basis = c->basis;
+  a.w1 = c->w1; a.b1 = c->b1; a.w2 = c->w2; a.b2 = c->b2;
+  a.res_idx = c->res_idx; a.res_val = c->res_val; a.res_scale = c->res_scale;
+  a.res_off = c->res_chunk_off; a.win_k = c->win_k; a.win_v = c->win_v;
+  a.q = q; a.sel = sel; a.part = part;
+  a.kpre_out = kpre_out; a.kpost_out = kpost_out; a.vhat_out = vhat_out;
+  a.nb = s->batch; a.hq = s->n_heads_q; a.hkv = s->n_heads_kv; a.g = p.g;
+  a.prefix = s->prefix_len; a.window = s->window; a.n_chunks = p.n_chunks; a.k_eff = p.k_eff;
+  a.n_resid = s->n_resid;
+  a.n_sel_tiles = has_prefix ? p.n_sel_tiles : 0;
+  a.n_win_tiles = p.n_win_tiles;
+  a.n_split = p.n_split;
+  a.total = s->batch * s->n_heads_kv * p.n_split;
+  a.padded_total = (a.total + 7) & ~7;
+  a.scale_log2 = s->softmax_scale * 1.4426950408889634f;
+  for (int i = 0; i < 64; ++i)
+    a.inv_freq[i] = std::pow((double)s->rope_theta, -2.0 * i / (double)kHeadDim);
+  if (launch_attend(a, s->rank, ci4, ri4, hs) != hipSuccess) return LOWRAM_ERR_HIP;
+  if (launch_merge(part, out, s->batch, s->n_heads_kv, p.g, p.n_split, hs) != hipSuccess)
+    return LOWRAM_ERR_HIP;
+  return LOWRAM_OK;
+}
+
+int check_dense(const dense_shape* s) {
+  if (!s) return LOWRAM_ERR_NULL;
+  if (s->batch < 1 || s->ctx_len < 1 || s->n_heads_q < 1 || s->n_heads_kv < 1 || s->head_dim < 1)
+    return LOWRAM_ERR_SHAPE;
+  if (s->n_heads_q % s->n_heads_kv) return LOWRAM_ERR_SHAPE;
+  if (!std::isfinite(s->softmax_scale)) return LOWRAM_ERR_SHAPE;
+  if (s->head_dim != kHeadDim || s->n_heads_q / s->n_heads_kv > 16) return LOWRAM_ERR_UNSUPPORTED;
+  return LOWRAM_OK;
+}
+
+constexpr int kDenseTokPerSplit = 2048;
+
+int dense_splits(const dense_shape* s) { return (s->ctx_len + kDenseTokPerSplit - 1) / kDenseTokPerSplit; }
+
+}  // namespace
+
+extern "C" {
+
+int lowram_abi_version(void) { return LOWRAM_ABI_VERSION; }
+
+const char* lowram_strerror(int status) {
+  switch (status) {
+    case LOWRAM_OK: return "ok";
+    case LOWRAM_ERR_NULL: return "a required pointer is NULL";
+    case LOWRAM_ERR_SHAPE: return "inconsistent shape";
+    case LOWRAM_ERR_UNSUPPORTED: return "shape not supported by this build";
+    case LOWRAM_ERR_WORKSPACE: return "workspace too small";
+    case LOWRAM_ERR_ALIGN: return "misaligned pointer";
+    case LOWRAM_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int lowram_workspace_bytes(const lowram_shape* shape, size_t* bytes) {
+  if (!bytes) return LOWRAM_ERR_NULL;
+  const int st = check_shape(shape);
+  if (st) return st;
+  *bytes = make_plan(shape).total;
+  return LOWRAM_OK;
+}
+
+int lowram_decode_step(const lowram_shape* shape, const lowram_layer_cache* cache,
+                       const uint16_t* q, uint16_t* out, int32_t* sel_out, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  return run_step(shape, cache, q, out, sel_out, nullptr, nullptr, nullptr, nullptr, workspace,
+                  ws_bytes, stream);
+}
+
+int lowram_decode_stages(const lowram_shape* shape, const lowram_layer_cache* cache,
+                         const uint16_t* q, uint16_t* out, int32_t* sel_out, float* scores_out,
+                         float* kpre_out, float* kpost_out, float* vhat_out, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  return run_step(shape, cache, q, out, sel_out, scores_out, kpre_out, kpost_out, vhat_out,
+                  workspace, ws_bytes, stream);
+}
+
+int dense_workspace_bytes(const dense_shape* shape, size_t* bytes) {
+  if (!bytes) return LOWRAM_ERR_NULL;
+  const int st = check_dense(shape);
+  if (st) return st;
+  *bytes = align_up((size_t)shape->batch * shape->n_heads_q * dense_splits(shape) * kPartStride * 4);
+  return LOWRAM_OK;
+}
+
+int dense_decode_step(const dense_shape* shape, const dense_layer_cache* cache, const uint16_t* q,
+                      uint16_t* out, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_dense(shape);
+  if (st) return st;
+  if (!cache || !cache->k || !cache->v || !q || !out || !workspace) return LOWRAM_ERR_NULL;
+  const void* bulk[] = {cache->k, cache->v, q, out, workspace};
+  for (const void* ptr : bulk)
+    if (misaligned(ptr, 16)) return LOWRAM_ERR_ALIGN;
+  size_t need = 0;
+  dense_workspace_bytes(shape, &need);
+  if (ws_bytes < need) return LOWRAM_ERR_WORKSPACE;
+  const int n_split = dense_splits(shape);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  float* part = static_cast<float*>(workspace);
+  if (launch_dense(cache->k, cache->v, q, part, shape->batch, shape->ctx_len, shape->n_heads_q,
+                   shape->n_heads_kv, n_split, kDenseTokPerSplit,
+                   shape->softmax_scale * 1.4426950408889634f, hs) != hipSuccess)
+    return LOWRAM_ERR_HIP;
+  if (launch_merge(part, out, shape->batch, shape->n_heads_kv, shape->n_heads_q / shape->n_heads_kv,
+                   n_split, hs) != hipSuccess)
+    return LOWRAM_ERR_HIP;
+  return LOWRAM_OK;
+}
+
+int lowram_resid_chunk_offsets(const int32_t* res_idx, int32_t n_lists, int32_t n_resid,
+                               int32_t n_chunks, int32_t chunk, int32_t* chunk_off, void* stream) {
+  if (!chunk_off || (n_resid > 0 && !res_idx)) return LOWRAM_ERR_NULL;
+  if (n_lists < 0 || n_resid < 0 || n_chunks < 0 || chunk < 1) return LOWRAM_ERR_SHAPE;
+  if (misaligned(chunk_off, 4) || (res_idx && misaligned(res_idx, 4))) return LOWRAM_ERR_ALIGN;
+  if (n_lists == 0) return LOWRAM_OK;
+  if (launch_chunk_offsets(res_idx, n_lists, n_resid, n_chunks, chunk, chunk_off,
+                           static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LOWRAM_ERR_HIP;
+  return LOWRAM_OK;
+}
+
+}  // extern "C"

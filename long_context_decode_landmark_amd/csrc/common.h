@@ -1,0 +1,86 @@
+// Internal helpers shared by the gfx950 kernels of the LowRAM decode library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lowram {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kHeadDim = 128;
+constexpr int kChunk = 8;
+constexpr int kHidden = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// v_mfma_f32_16x16x32_bf16.  Lane l supplies A[l%16][8*(l/16)+e] and
+// B[8*(l/16)+e][l%16] (e = 0..7); it receives D[4*(l/16)+e][l%16] (e = 0..3).
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t u) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, u));
+}
+
+// Eight floats -> bf16x8 (round to nearest even).
+__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
+  bf16x8 r;
+  r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];
+  r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
+  return r;
+}
+
+// Residual of the bf16 rounding of pack8, as a second bf16x8 (hi + lo split).
+__device__ __forceinline__ bf16x8 pack8_lo(f32x4 lo, f32x4 hi, bf16x8 h) {
+  bf16x8 r;
+  r[0] = (__bf16)(lo[0] - (float)h[0]); r[1] = (__bf16)(lo[1] - (float)h[1]);
+  r[2] = (__bf16)(lo[2] - (float)h[2]); r[3] = (__bf16)(lo[3] - (float)h[3]);
+  r[4] = (__bf16)(hi[0] - (float)h[4]); r[5] = (__bf16)(hi[1] - (float)h[5]);
+  r[6] = (__bf16)(hi[2] - (float)h[6]); r[7] = (__bf16)(hi[3] - (float)h[7]);
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+}
+
+// Two 4-element (8-byte) pieces -> one MFMA operand.
+__device__ __forceinline__ bf16x8 load_bf16x4x2(const uint16_t* p0, const uint16_t* p1) {
+  u32x2 a = *reinterpret_cast<const u32x2*>(p0);
+  u32x2 b = *reinterpret_cast<const u32x2*>(p1);
+  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+
+// Order-preserving map fp32 -> uint32 (larger float -> larger key); -0 == +0.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Map a 1-D grid onto logical work items so that each of the 8 XCDs (which
+// receive workgroups round-robin) gets one contiguous range of items:
+// neighbouring items share their per-head weights in that XCD's L2.
+__device__ __forceinline__ int xcd_logical_block(int lin, int padded_total) {
+  const int per = padded_total >> 3;
+  return (lin & 7) * per + (lin >> 3);
+}
+
+}  // namespace lowram

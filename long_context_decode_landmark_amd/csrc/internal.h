@@ -1,0 +1,56 @@
+// Launchers shared between the kernel translation units and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lowram {
+
+// Selected-chunk attention: one workgroup = 8 waves x 32 tokens = 32 chunks.
+constexpr int kAttWaves = 8;
+constexpr int kAttTokWave = 32;
+constexpr int kAttChunksWG = kAttWaves * kAttTokWave / 8;  // 32
+constexpr int kAttTokWG = kAttWaves * kAttTokWave;         // 256
+constexpr int kPartStride = 2 + 128;                       // m, l, o[128] per query head
+
+struct AttendArgs {
+  const void* coeff;
+  const uint16_t* coeff_scale;
+  const uint16_t* basis;
+  const uint16_t* w1;
+  const uint16_t* b1;
+  const uint16_t* w2;
+  const uint16_t* b2;
+  const int32_t* res_idx;
+  const void* res_val;
+  const uint16_t* res_scale;
+  const int32_t* res_off;
+  const uint16_t* win_k;
+  const uint16_t* win_v;
+  const uint16_t* q;
+  const int32_t* sel;
+  float* part;
+  float* kpre_out;
+  float* kpost_out;
+  float* vhat_out;
+  int nb, hq, hkv, g, prefix, window, n_chunks, k_eff, n_resid;
+  int n_sel_tiles, n_win_tiles, n_split, total, padded_total;
+  float scale_log2;
+  double inv_freq[64];
+};
+
+hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* keys,
+                        float* scores_out, int nb, int n_cand, int hq, int hkv, hipStream_t st);
+hipError_t launch_select(const uint32_t* keys, const int32_t* cand_ids, int32_t* sel,
+                         int32_t* sel_out, int nb, int n_cand, int k, int hkv, hipStream_t st);
+hipError_t launch_attend(const AttendArgs& a, int rank, bool coeff_int4, bool resid_int4,
+                         hipStream_t st);
+hipError_t launch_merge(const float* part, uint16_t* out, int nb, int hkv, int g, int n_split,
+                        hipStream_t st);
+hipError_t launch_dense(const uint16_t* k, const uint16_t* v, const uint16_t* q, float* part,
+                        int nb, int ctx, int hq, int hkv, int n_split, int tok_per_split,
+                        float scale_log2, hipStream_t st);
+hipError_t launch_chunk_offsets(const int32_t* res_idx, int n_lists, int n_resid, int n_chunks,
+                                int chunk, int32_t* off, hipStream_t st);
+
+}  // namespace lowram

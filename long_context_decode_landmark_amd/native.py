@@ -1,0 +1,188 @@
+"""ctypes binding of liblowram.so (argument marshalling only).
+
+Every function here takes torch tensors already resident on the GPU, passes
+their device pointers and the current HIP stream to the C ABI declared in
+include/lowram.h, and raises LowramError on a non-zero status.  No step of the
+decode computation runs in Python: if the library is not built, calls fail.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblowram.so")
+
+FMT_BF16 = 0
+FMT_INT4_G32 = 1
+
+# every entry point include/lowram.h declares
+SYMBOLS = (
+    "lowram_abi_version",
+    "lowram_strerror",
+    "lowram_workspace_bytes",
+    "lowram_decode_step",
+    "lowram_decode_stages",
+    "dense_workspace_bytes",
+    "dense_decode_step",
+    "lowram_resid_chunk_offsets",
+)
+
+ERRORS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "UNSUPPORTED", -4: "WORKSPACE", -5: "ALIGN", -6: "HIP"}
+
+
+class LowramShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "prefix_len", "window", "chunk", "n_heads_q", "n_heads_kv", "head_dim", "rank",
+        "mlp_hidden", "topk", "n_resid", "n_cand", "coeff_fmt", "resid_fmt")] + [
+        ("rope_theta", ctypes.c_float), ("softmax_scale", ctypes.c_float)]
+
+
+CACHE_FIELDS = ("coeff", "coeff_scale", "basis", "landmark", "cand_ids", "w1", "b1", "w2", "b2",
+                "res_idx", "res_val", "res_scale", "res_chunk_off", "win_k", "win_v")
+
+
+class LowramLayerCache(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in CACHE_FIELDS]
+
+
+class DenseShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("batch", "ctx_len", "n_heads_q", "n_heads_kv", "head_dim")] + [
+        ("softmax_scale", ctypes.c_float)]
+
+
+class DenseLayerCache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p)]
+
+
+class LowramError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({ERRORS.get(status, '?')}): {strerror(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "(or python -m long_context_decode_landmark_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        L.lowram_abi_version.restype = ctypes.c_int
+        L.lowram_strerror.restype = ctypes.c_char_p
+        L.lowram_strerror.argtypes = [ctypes.c_int]
+        L.lowram_workspace_bytes.argtypes = [ctypes.POINTER(LowramShape), ctypes.POINTER(sz)]
+        L.lowram_decode_step.argtypes = [ctypes.POINTER(LowramShape), ctypes.POINTER(LowramLayerCache),
+                                         vp, vp, vp, vp, sz, vp]
+        L.lowram_decode_stages.argtypes = [ctypes.POINTER(LowramShape), ctypes.POINTER(LowramLayerCache),
+                                           vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.dense_workspace_bytes.argtypes = [ctypes.POINTER(DenseShape), ctypes.POINTER(sz)]
+        L.dense_decode_step.argtypes = [ctypes.POINTER(DenseShape), ctypes.POINTER(DenseLayerCache),
+                                        vp, vp, vp, sz, vp]
+        L.lowram_resid_chunk_offsets.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_int32, vp, vp]
+        for name in SYMBOLS:
+            getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
+        L.lowram_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    try:
+        return lib().lowram_strerror(status).decode()
+    except RuntimeError:
+        return ERRORS.get(status, "?")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise LowramError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+# ------------------------------------------------------------------ shapes --
+def make_shape(cfg, batch: int | None = None, **over) -> LowramShape:
+    """lowram_shape of one layer of a workload (synth.Config-like object)."""
+    f = dict(batch=cfg.batch if batch is None else batch, prefix_len=cfg.prefix, window=cfg.window,
+             chunk=cfg.chunk, n_heads_q=cfg.n_heads_q, n_heads_kv=cfg.n_heads_kv,
+             head_dim=cfg.head_dim, rank=cfg.rank, mlp_hidden=cfg.mlp_hidden, topk=cfg.topk,
+             n_resid=cfg.n_resid, n_cand=cfg.n_cand,
+             coeff_fmt=FMT_INT4_G32 if cfg.int4 else FMT_BF16,
+             resid_fmt=FMT_INT4_G32 if cfg.int4 else FMT_BF16,
+             rope_theta=cfg.rope_theta, softmax_scale=cfg.head_dim ** -0.5)
+    f.update(over)
+    return LowramShape(**f)
+
+
+def make_cache(tensors: dict) -> LowramLayerCache:
+    return LowramLayerCache(**{n: (tensors[n].data_ptr() if tensors.get(n) is not None else None)
+                               for n in CACHE_FIELDS})
+
+
+# ------------------------------------------------------------- entry points --
+def abi_version() -> int:
+    return lib().lowram_abi_version()
+
+
+def workspace_bytes(shape: LowramShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().lowram_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)), "lowram_workspace_bytes")
+    return n.value
+
+
+def decode_step(shape, cache, q, out, workspace, sel_out=None, stream=None) -> None:
+    """lowram_decode_step on device tensors (cache: LowramLayerCache or dict)."""
+    c = cache if isinstance(cache, LowramLayerCache) else make_cache(cache)
+    _check(lib().lowram_decode_step(ctypes.byref(shape), ctypes.byref(c), _ptr(q), _ptr(out),
+                                    _ptr(sel_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)), "lowram_decode_step")
+
+
+def decode_stages(shape, cache, q, out, workspace, sel_out=None, scores=None, kpre=None, kpost=None,
+                  vhat=None, stream=None) -> None:
+    c = cache if isinstance(cache, LowramLayerCache) else make_cache(cache)
+    _check(lib().lowram_decode_stages(ctypes.byref(shape), ctypes.byref(c), _ptr(q), _ptr(out),
+                                      _ptr(sel_out), _ptr(scores), _ptr(kpre), _ptr(kpost), _ptr(vhat),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)), "lowram_decode_stages")
+
+
+def dense_shape(batch, ctx_len, n_heads_q, n_heads_kv, head_dim=128, softmax_scale=None) -> DenseShape:
+    return DenseShape(batch=batch, ctx_len=ctx_len, n_heads_q=n_heads_q, n_heads_kv=n_heads_kv,
+                      head_dim=head_dim, softmax_scale=head_dim ** -0.5 if softmax_scale is None else softmax_scale)
+
+
+def dense_workspace_bytes(shape: DenseShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().dense_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)), "dense_workspace_bytes")
+    return n.value
+
+
+def dense_decode_step(shape, k, v, q, out, workspace, stream=None) -> None:
+    c = DenseLayerCache(k=k.data_ptr(), v=v.data_ptr())
+    _check(lib().dense_decode_step(ctypes.byref(shape), ctypes.byref(c), _ptr(q), _ptr(out), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "dense_decode_step")
+
+
+def resid_chunk_offsets(res_idx, n_lists: int, n_resid: int, n_chunks: int, chunk: int, out,
+                        stream=None) -> None:
+    """res_idx [n_lists][n_resid] int32 (ascending rows) -> out [n_lists][n_chunks+1] int32."""
+    _check(lib().lowram_resid_chunk_offsets(_ptr(res_idx), n_lists, n_resid, n_chunks, chunk, _ptr(out),
+                                            _stream(stream)), "lowram_resid_chunk_offsets")

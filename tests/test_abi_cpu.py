@@ -1,0 +1,152 @@
+"""The C ABI library without a GPU: it loads, exports every declared entry
+point, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_decode_landmark_amd import native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lowram.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(native.SYMBOLS)
+
+
+def test_library_loads_and_exports_every_symbol():
+    L = native.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert native.abi_version() == 1
+    assert native.strerror(-4) == "workspace too small"
+
+
+def shape(**kw):
+    import synth
+    return native.make_shape(synth.C0, **kw)
+
+
+def ws_bytes(**kw):
+    return native.workspace_bytes(shape(**kw))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_heads_q=7), -2),            # Hq % Hkv
+    (dict(prefix_len=4031), -2),        # P % S
+    (dict(topk=0), -2),
+    (dict(prefix_len=0, window=0), -2),
+    (dict(n_resid=5000), -2),           # more residuals than prefix tokens
+    (dict(coeff_fmt=3), -2),
+    (dict(n_cand=600), -2),             # more candidates than chunks
+    (dict(rope_theta=-1.0), -2),
+    (dict(head_dim=64), -3),
+    (dict(chunk=16, prefix_len=4032, n_cand=252), -3),
+    (dict(mlp_hidden=128), -3),
+    (dict(rank=96), -3),
+    (dict(n_heads_q=64, n_heads_kv=2), -3),   # GQA group above 16
+    (dict(coeff_fmt=1), -3),            # int4 needs rank % 128 == 0 (rank 64 here)
+])
+def test_workspace_bytes_rejects_shapes(kw, code):
+    with pytest.raises(native.LowramError) as e:
+        ws_bytes(**kw)
+    assert e.value.status == code
+
+
+def test_workspace_bytes_formula():
+    import synth
+    cfg = synth.C3
+    s = native.make_shape(cfg, batch=28)
+    heads = 28 * 8
+    keff = min(cfg.topk, cfg.n_cand)
+    n_split = -(-keff // 32) + -(-cfg.window // 256)
+    al = lambda x: (x + 255) // 256 * 256
+    want = al(heads * cfg.n_cand * 4) + al(heads * keff * 4) + al(heads * n_split * 4 * 130 * 4)
+    assert native.workspace_bytes(s) == want
+
+
+class FakeTensor:
+    """A stand-in with a device address that is never dereferenced: every
+    call below fails argument checks before the library touches HIP."""
+
+    def __init__(self, addr, n=1 << 30):
+        self.addr, self.n = addr, n
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return 1
+
+
+def fake_cache(base=0x10000000):
+    return {n: FakeTensor(base + 0x1000000 * i) for i, n in enumerate(native.CACHE_FIELDS)
+            if n not in ("cand_ids", "coeff_scale", "res_scale")}
+
+
+def call_step(s, cache, q=FakeTensor(0x7000000000), out=FakeTensor(0x7100000000), ws=None):
+    ws = ws or FakeTensor(0x7200000000, n=native.workspace_bytes(s) if s.topk > 0 else 1)
+    with pytest.raises(native.LowramError) as e:
+        native.decode_step(s, cache, q, out, ws, stream=0)
+    return e.value.status
+
+
+def test_step_rejects_null_pointers():
+    s = shape()
+    for n in ("coeff", "basis", "landmark", "w1", "res_chunk_off", "win_k", "win_v"):
+        c = fake_cache()
+        c[n] = None
+        assert call_step(s, c) == -1, n
+    assert call_step(s, fake_cache(), q=None) == -1
+
+
+def test_step_rejects_short_workspace():
+    s = shape()
+    need = native.workspace_bytes(s)
+    assert call_step(s, fake_cache(), ws=FakeTensor(0x7200000000, n=need - 1)) == -4
+
+
+def test_step_rejects_misalignment():
+    s = shape()
+    c = fake_cache()
+    c["landmark"] = FakeTensor(0x10000008)
+    assert call_step(s, c) == -5
+    c = fake_cache()
+    c["res_idx"] = FakeTensor(0x10000002)
+    assert call_step(s, c) == -5
+
+
+def test_step_requires_int4_scales_and_candidates():
+    s = shape(rank=128, coeff_fmt=1)
+    assert call_step(s, fake_cache()) == -1          # coeff_scale missing
+    s = shape(n_cand=200)
+    assert call_step(s, fake_cache()) == -2          # fewer candidates but no cand_ids
+
+
+def test_dense_rejects():
+    with pytest.raises(native.LowramError) as e:
+        native.dense_workspace_bytes(native.dense_shape(1, 100, 7, 2))
+    assert e.value.status == -2
+    s = native.dense_shape(1, 100, 8, 2)
+    need = native.dense_workspace_bytes(s)
+    with pytest.raises(native.LowramError) as e:
+        native.dense_decode_step(s, FakeTensor(0x1000), FakeTensor(0x2000), FakeTensor(0x3000),
+                                 FakeTensor(0x4000), FakeTensor(0x5000, n=need - 1), stream=0)
+    assert e.value.status == -4
+
+
+def test_chunk_offsets_rejects():
+    with pytest.raises(native.LowramError) as e:
+        native.resid_chunk_offsets(FakeTensor(0x1002), 4, 16, 10, 8, FakeTensor(0x2000), stream=0)
+    assert e.value.status in (-5,)
