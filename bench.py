@@ -1,0 +1,327 @@
+"""Decode-throughput benchmark of the LowRAM decode step on one MI355X.
+
+A step is one decode step of every layer (32 calls of lowram_decode_step,
+one per layer, each for the whole batch) against a compressed cache resident
+in HBM; tokens/s = batch / step time.  Default workload: 262144-token
+context, batch 28, Llama-3-8B shape (32 layers, 32 query / 8 KV heads, head
+dim 128), top-1024 chunks of 8, window 256, rank 512, value MLP 128-256-128,
+12.5% residuals.  Every (sequence, layer) owns distinct device buffers.
+
+Prints one JSON line with the step time, the per-kernel HIP-event timings of
+the timed region, the roofline of the dominant kernel, the dense bf16
+baseline and the CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+KERNELS = ("score", "select", "attend", "merge")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c3_llama8b_262k")
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=None, help="fewer layers (debug only)")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--dense-batch", type=int, default=8)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-slices", type=int, default=10)
+    ap.add_argument("--graph", action="store_true", help="also time a hipGraph replay of the step")
+    ap.add_argument("--seed", type=int, default=1234)
+    return ap.parse_args()
+
+
+def algorithmic(cfg, nb):
+    """Algorithmic HBM bytes and MFMA flops of one layer for `nb` sequences.
+
+    Per (sequence, layer): landmarks read once; coefficients of the k*S
+    selected tokens per KV head; this layer's basis blocks and MLP weights;
+    residual rows (and indices, chunk offsets) of the selected tokens at the
+    stored density; the exact window; q in, out.  Flops: landmark scores,
+    reconstruction, the two MLP layers, attention.
+    """
+    Hkv, Hq, d, H, r, S = cfg.n_heads_kv, cfg.n_heads_q, cfg.head_dim, cfg.mlp_hidden, cfg.rank, cfg.chunk
+    k = min(cfg.topk, cfg.n_cand)
+    kS = k * S
+    rho = cfg.n_resid / cfg.prefix
+    s_c = 0.5 + 2.0 / 32 if cfg.int4 else 2.0          # bytes per coefficient (+fp16 scale / 32)
+    s_r = d * (0.5 + 2.0 / 32) if cfg.int4 else d * 2.0  # bytes per residual row
+    b = {}
+    b["score"] = cfg.n_cand * Hkv * d * 2 + (cfg.n_cand * Hkv * 4 if cfg.evict else 0) + Hq * d * 2
+    b["attend"] = (Hkv * kS * r * s_c + Hkv * r * d * 2 + Hkv * (2 * d * H + H + d) * 2
+                   + Hkv * kS * rho * (s_r + 4) + Hkv * k * 8 + 2 * Hkv * cfg.window * d * 2 + Hq * d * 2)
+    b["merge"] = Hq * d * 2
+    b["select"] = 0.0
+    f = {
+        "score": 2.0 * Hq * cfg.n_cand * d,
+        "attend": 2.0 * Hkv * kS * r * d + 4.0 * Hkv * kS * d * H + 4.0 * Hq * (kS + cfg.window) * d,
+        "select": 0.0, "merge": 0.0,
+    }
+    return {kk: v * nb for kk, v in b.items()}, {kk: v * nb for kk, v in f.items()}
+
+
+def build_device_cache(cfg, nb, n_layers, seed, dev):
+    """Distinct device buffers for every (sequence, layer); one drawn slice replicated."""
+    import torch
+
+    from long_context_decode_landmark_amd import native
+    from synth import device as sd
+
+    def rep(t):
+        return t.unsqueeze(0).expand((nb,) + tuple(t.shape)).contiguous()
+
+    base = sd.draw_layer(cfg, seed, dev)
+    off = torch.empty((cfg.n_heads_kv, cfg.n_chunks + 1), dtype=torch.int32, device=dev)
+    native.resid_chunk_offsets(base["res_idx"], cfg.n_heads_kv, cfg.n_resid, cfg.n_chunks, cfg.chunk, off)
+    base["res_chunk_off"] = off
+    coeff = sd.draw_coeff(cfg, seed + 1, dev)
+    groups = []
+    for _ in range((n_layers + cfg.group_layers - 1) // cfg.group_layers):
+        if cfg.int4:
+            groups.append({"coeff": rep(coeff[0]), "coeff_scale": rep(coeff[1])})
+        else:
+            groups.append({"coeff": rep(coeff)})
+    layers, qs = [], []
+    for li in range(n_layers):
+        t = {kk: rep(v) for kk, v in base.items()}
+        t.update(groups[li // cfg.group_layers])
+        layers.append(t)
+        qs.append(sd.draw_queries(cfg, nb, seed + 100 + li, dev))
+    torch.cuda.synchronize()
+    return layers, qs
+
+
+def time_lowram(cfg, nb, n_layers, steps, warmup, seed, graph):
+    import torch
+
+    from long_context_decode_landmark_amd import native
+
+    dev = torch.device("cuda:0")
+    layers, qs = build_device_cache(cfg, nb, n_layers, seed, dev)
+    shape = native.make_shape(cfg, batch=nb)
+    ws = torch.empty(native.workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(qs[0])
+    caches = [native.make_cache(t) for t in layers]
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for li in range(n_layers):
+            if events is None:
+                native.decode_step(shape, caches[li], qs[li], out, ws)
+            else:
+                native.decode_step_events(shape, caches[li], qs[li], out, ws, events[li])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: per-kernel events on the launch stream, step events around
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_layers)]
+           for _ in range(steps)]
+    for s in evs:
+        for lay in s:
+            for e in lay:
+                e.record(stream)  # creates the underlying hipEvent
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for s in range(steps):
+        step(evs[s])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    kern = {k: 0.0 for k in KERNELS}
+    for s in evs:
+        for lay in s:
+            for i, k in enumerate(KERNELS):
+                kern[k] += lay[i].elapsed_time(lay[i + 1])
+    kern = {k: v / (steps * n_layers) for k, v in kern.items()}  # ms per launch
+
+    graph_ms = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(stream)
+        with torch.cuda.stream(s2):
+            step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        graph_ms = a.elapsed_time(b) / steps
+
+    # one slice back to the host for the CPU baseline
+    host = {kk: v[0].cpu() for kk, v in layers[0].items()}
+    q0 = qs[0][:1].cpu()
+    del layers, qs, caches, ws, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return step_ms, kern, graph_ms, host, q0
+
+
+def time_dense(cfg, nb, n_layers, steps, warmup, seed):
+    """Dense bf16 GQA decode over the full cache; 2 distinct layer buffers
+    (each far larger than the 256 MB Infinity Cache) cycled over the layers."""
+    import torch
+
+    from long_context_decode_landmark_amd import native
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    shp = (nb, cfg.n_heads_kv, cfg.ctx, cfg.head_dim)
+    bufs = [(torch.randn(shp, generator=g, device=dev, dtype=torch.bfloat16),
+             torch.randn(shp, generator=g, device=dev, dtype=torch.bfloat16)) for _ in range(2)]
+    q = torch.randn((nb, cfg.n_heads_q, cfg.head_dim), generator=g, device=dev, dtype=torch.bfloat16)
+    out = torch.empty_like(q)
+    ds = native.dense_shape(nb, cfg.ctx, cfg.n_heads_q, cfg.n_heads_kv, cfg.head_dim)
+    ws = torch.empty(native.dense_workspace_bytes(ds), dtype=torch.uint8, device=dev)
+
+    def step():
+        for li in range(n_layers):
+            k, v = bufs[li % 2]
+            native.dense_decode_step(ds, k, v, q, out, ws)
+
+    for _ in range(warmup):
+        step()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    bytes_layer = 2.0 * nb * cfg.n_heads_kv * cfg.ctx * cfg.head_dim * 2
+    del bufs
+    torch.cuda.empty_cache()
+    return ms, bytes_layer * n_layers / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(cfg, host, q0, n_slices):
+    """The oracle on `n_slices` (sequence, layer) slices of the same workload."""
+    import numpy as np
+    import torch
+
+    from oracle import decode
+
+    def np_(t):
+        if t.dtype in (torch.bfloat16, torch.int16):
+            return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+        return t.contiguous().numpy()
+
+    cache = {k: np_(v)[None] for k, v in host.items()}
+    q = np_(q0)
+    rng = np.random.default_rng(0)
+    t0 = time.time()
+    for i in range(n_slices):
+        qi = q if i == 0 else np_(torch.randn((1, cfg.n_heads_q, cfg.head_dim)).to(torch.bfloat16))
+        decode.decode_step(cfg, cache, qi)
+    dt = (time.time() - t0) / n_slices
+    del rng
+    cores = len(os.sched_getaffinity(0))
+    try:  # the BLAS pool the oracle's matmuls actually ran on
+        from threadpoolctl import threadpool_info
+        blas = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        if blas:
+            cores = max(blas)
+    except Exception:
+        pass
+    return {"value": 1.0 / (dt * cfg.n_layers), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_slices} (sequence, layer) slices of the same workload (all {cfg.n_heads_kv} KV heads), "
+                      f"{dt:.2f} s each, extrapolated x{cfg.n_layers} layers per token"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode step shards by "
+              "sequence with no exchange, so N GPUs would each run this single-GPU workload.", file=sys.stderr)
+        sys.exit(2)
+    import synth
+    cfg = synth.CONFIGS[args.config]
+    nb = args.batch or cfg.batch
+    n_layers = args.layers or cfg.n_layers
+
+    step_ms, kern, graph_ms, host, q0 = time_lowram(cfg, nb, n_layers, args.steps, args.warmup, args.seed,
+                                                    args.graph)
+    byts, flops = algorithmic(cfg, nb)
+    dom = max(KERNELS, key=lambda k: kern[k])
+    t_dom = kern[dom] * 1e-3
+    inten = flops[dom] / max(byts[dom], 1.0)
+    bound = "hbm" if inten < MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+    if bound == "hbm":
+        ach, peak, unit = byts[dom] / t_dom / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        ach, peak, unit = flops[dom] / t_dom / 1e12, MFMA_BF16_PEAK_TFS, "TFLOP/s"
+    step_bytes = sum(byts.values()) * n_layers
+    step_flops = sum(flops.values()) * n_layers
+    t_roof = max(step_bytes / (HBM_PEAK_GBS * 1e9), step_flops / (MFMA_BF16_PEAK_TFS * 1e12))
+    per_kernel = {k: {"ms": round(kern[k], 5),
+                      "GB/s": round(byts[k] / (kern[k] * 1e-3) / 1e9, 1) if kern[k] > 0 else None,
+                      "TFLOP/s": round(flops[k] / (kern[k] * 1e-3) / 1e12, 2) if kern[k] > 0 else None}
+                  for k in KERNELS}
+
+    res = {
+        "metric": "decode tokens/sec at 262K ctx, batch 28; HBM GB/s & MFMA util vs peak",
+        "value": round(nb / (step_ms * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if not cfg.int4 else "bf16+int4",
+        "data": "synthetic (seeded device draws, distinct buffers per sequence and layer)",
+        "config": {"workload": cfg.name, "batch": nb, "ctx": cfg.ctx, "layers": n_layers,
+                   "heads_q": cfg.n_heads_q, "heads_kv": cfg.n_heads_kv, "topk": cfg.topk, "chunk": cfg.chunk,
+                   "window": cfg.window, "rank": cfg.rank, "resid_frac": cfg.resid_frac,
+                   "int4": cfg.int4, "evict": cfg.evict},
+        "roofline": {"bound": bound, "kernel": dom, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                     "frac": round(ach / peak, 4), "traffic": None},
+        "step_roofline": {"alg_bytes_GB": round(step_bytes / 1e9, 3), "alg_TFLOP": round(step_flops / 1e12, 3),
+                          "t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof / (step_ms * 1e-3), 4),
+                          "hbm_GB/s": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+                          "mfma_util": round(step_flops / (step_ms * 1e-3) / (MFMA_BF16_PEAK_TFS * 1e12), 4)},
+        "kernels": per_kernel,
+    }
+    if graph_ms is not None:
+        res["graph_ms_per_step"] = round(graph_ms, 4)
+    if not args.no_dense:
+        dnb = min(args.dense_batch, nb)
+        dms, dgbs = time_dense(cfg, dnb, n_layers, max(3, args.steps // 4), 1, args.seed)
+        res["dense_baseline"] = {"batch": dnb, "ms_per_step": round(dms, 3),
+                                 "tokens/s": round(dnb / (dms * 1e-3), 2), "hbm_GB/s": round(dgbs, 1),
+                                 "note": "dense bf16 cache needs 32 GiB per sequence at 262K: batch 8 is "
+                                         "the largest that fits 288 GB"}
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(cfg, host, q0, args.cpu_slices)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

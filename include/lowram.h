@@ -144,6 +144,19 @@ int lowram_decode_stages(const lowram_shape* shape, const lowram_layer_cache* ca
                          float* scores_out, float* kpre_out, float* kpost_out,
                          float* vhat_out, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * lowram_decode_step that also records five caller-created hipEvent_t
+ * (passed as void*) on `stream` around its kernels, for measurement:
+ *   events[0] before the landmark scoring, [1] after it, [2] after the top-k
+ *   selection, [3] after the fused rebuild + attention, [4] after the merge.
+ * `events` may be NULL (then it is lowram_decode_step).  The events are only
+ * recorded, never waited on.
+ */
+int lowram_decode_step_events(const lowram_shape* shape, const lowram_layer_cache* cache,
+                              const uint16_t* q, uint16_t* out, int32_t* sel_out,
+                              void* workspace, size_t ws_bytes, void* stream,
+                              void* const* events);
+
 /* Dense GQA decode over the full bf16 cache: the uncompressed baseline the
    LowRAM pages compare against (review, results paragraph). */
 typedef struct dense_shape {

@@ -69,7 +69,8 @@ Plan make_plan(const lowram_shape* s) {
 
 int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t* q, uint16_t* out,
              int32_t* sel_out, float* scores_out, float* kpre_out, float* kpost_out,
-             float* vhat_out, void* ws, size_t ws_bytes, void* stream) {
+             float* vhat_out, void* ws, size_t ws_bytes, void* stream,
+             void* const* events = nullptr) {
   int st = check_shape(s);
   if (st) return st;
   if (!c || !q || !out || !ws) return LOWRAM_ERR_NULL;
@@ -96,6 +97,7 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
     if (ptr && misaligned(ptr, 4)) return LOWRAM_ERR_ALIGN;
   if (kpre_out && misaligned(kpre_out, 16)) return LOWRAM_ERR_ALIGN;
   if (kpost_out && misaligned(kpost_out, 16)) return LOWRAM_ERR_ALIGN;
+  if ((long long)p.n_split * (p.g < 16 ? p.g : 16) > kMergeMaxWeights) return LOWRAM_ERR_UNSUPPORTED;
   if (ws_bytes < p.total) return LOWRAM_ERR_WORKSPACE;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -103,17 +105,23 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   uint32_t* keys = reinterpret_cast<uint32_t*>(w + p.off_keys);
   int32_t* sel = reinterpret_cast<int32_t*>(w + p.off_sel);
   float* part = reinterpret_cast<float*>(w + p.off_part);
+  auto mark = [&](int i) {
+    return !events || hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) == hipSuccess;
+  };
 
+  if (!mark(0)) return LOWRAM_ERR_HIP;
   if (has_prefix) {
     if (launch_score(q, c->landmark, keys, scores_out, s->batch, p.n_cand, s->n_heads_q,
                      s->n_heads_kv, hs) != hipSuccess)
       return LOWRAM_ERR_HIP;
   }
+  if (!mark(1)) return LOWRAM_ERR_HIP;
   if (has_prefix || sel_out) {
     if (launch_select(keys, c->cand_ids, sel, sel_out, s->batch, p.n_cand, s->topk, s->n_heads_kv,
                       hs) != hipSuccess)
       return LOWRAM_ERR_HIP;
   }
+  if (!mark(2)) return LOWRAM_ERR_HIP;
   AttendArgs a{};
   a.coeff = c->coeff; a.coeff_scale = c->coeff_scale; a.basis = c->basis;
   a.w1 = c->w1; a.b1 = c->b1; a.w2 = c->w2; a.b2 = c->b2;
@@ -133,8 +141,10 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   for (int i = 0; i < 64; ++i)
     a.inv_freq[i] = std::pow((double)s->rope_theta, -2.0 * i / (double)kHeadDim);
   if (launch_attend(a, s->rank, ci4, ri4, hs) != hipSuccess) return LOWRAM_ERR_HIP;
+  if (!mark(3)) return LOWRAM_ERR_HIP;
   if (launch_merge(part, out, s->batch, s->n_heads_kv, p.g, p.n_split, hs) != hipSuccess)
     return LOWRAM_ERR_HIP;
+  if (!mark(4)) return LOWRAM_ERR_HIP;
   return LOWRAM_OK;
 }
 
@@ -186,6 +196,13 @@ int lowram_decode_step(const lowram_shape* shape, const lowram_layer_cache* cach
                   ws_bytes, stream);
 }
 
+int lowram_decode_step_events(const lowram_shape* shape, const lowram_layer_cache* cache,
+                              const uint16_t* q, uint16_t* out, int32_t* sel_out, void* workspace,
+                              size_t ws_bytes, void* stream, void* const* events) {
+  return run_step(shape, cache, q, out, sel_out, nullptr, nullptr, nullptr, nullptr, workspace,
+                  ws_bytes, stream, events);
+}
+
 int lowram_decode_stages(const lowram_shape* shape, const lowram_layer_cache* cache,
                          const uint16_t* q, uint16_t* out, int32_t* sel_out, float* scores_out,
                          float* kpre_out, float* kpost_out, float* vhat_out, void* workspace,
@@ -212,6 +229,8 @@ int dense_decode_step(const dense_shape* shape, const dense_layer_cache* cache, 
     if (misaligned(ptr, 16)) return LOWRAM_ERR_ALIGN;
   size_t need = 0;
   dense_workspace_bytes(shape, &need);
+  if ((long long)dense_splits(shape) * (shape->n_heads_q / shape->n_heads_kv < 16 ? shape->n_heads_q / shape->n_heads_kv : 16) > kMergeMaxWeights)
+    return LOWRAM_ERR_UNSUPPORTED;
   if (ws_bytes < need) return LOWRAM_ERR_WORKSPACE;
   const int n_split = dense_splits(shape);
   hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -12,9 +12,10 @@
 //                               tokens (review, value paragraph; explainer
 //                               "Amortised values", "Residuals")
 //   partial softmax state (m, l, o) of the GQA query heads over the tokens
-// The exact recent window is attended by extra workgroups of the same grid.
+// The exact recent window is attended by extra workgroups of the same grid;
+// a separate merge kernel combines the partial states of each head.
 //
-// Layout of the work.  A workgroup is 8 waves; each wave owns 32 tokens
+// Layout of the work.  A workgroup is 4 waves; each wave owns 32 tokens
 // (4 chunks) and runs every stage on them with v_mfma_f32_16x16x32_bf16.
 // Tokens are the MFMA N dimension throughout, so each stage's accumulator
 // layout is the next stage's operand layout (up to a fixed permutation of
@@ -25,8 +26,10 @@
 //   MLP1    D[h][t]  = W1[h][d] (LDS)        x K_pre[t][d] (VGPR)
 //   MLP2    D[t][d]  = hid[t][h] (VGPR)      x W2[d][h] (LDS)
 //   PV      D[j][d]  = p[j][t] (VGPR)        x V[t][d] (VGPR, hi+lo bf16)
-// The shared operands (basis block, then W1/W2) are staged in LDS once per
-// workgroup and read by all 8 waves.
+// The operands shared by the 4 waves pass through one 64 KiB LDS buffer in
+// four stages (basis r < 256, basis r >= 256, W1, W2), so a workgroup needs
+// under 80 KiB and two workgroups share a CU: one stages or waits on the
+// coefficient gather while the other runs MFMA.
 #include "common.h"
 #include "internal.h"
 
@@ -65,23 +68,20 @@ __device__ __forceinline__ float2 rot_of(double angle) {
   return make_float2(c, s);
 }
 
-template <int RANK>
+constexpr int kBuf = 65536;  // bytes of the staged operand buffer
+
 struct AttLds {
-  static constexpr int BS = RANK + 8;         // basis^T row stride (elements)
-  static constexpr int W1S = kHeadDim + 8;    // W1 row stride
-  static constexpr int W2S = kHidden + 8;     // W2 row stride
-  static constexpr int W1_BYTES = kHidden * W1S * 2;
-  static constexpr int W_BYTES = W1_BYTES + kHeadDim * W2S * 2;
-  static constexpr int B_BYTES = kHeadDim * BS * 2;
-  static constexpr int M_BYTES = (kAttWaves * 16 * kHeadDim + 2 * kAttWaves * 16) * 4;
-  static constexpr int U_BYTES = (W_BYTES > B_BYTES ? (W_BYTES > M_BYTES ? W_BYTES : M_BYTES)
-                                                   : (B_BYTES > M_BYTES ? B_BYTES : M_BYTES));
-  alignas(16) unsigned char u[U_BYTES];
+  alignas(16) unsigned char buf[kBuf];
   float2 rope_off[kChunk][64];
   float2 rope_base[kAttChunksWG][64];
   float b1f[kHidden];
   float b2f[kHeadDim];
 };
+
+// Staged matrices keep dense rows; the 16-byte piece p of row r is stored at
+// piece p ^ (r & 7) so the 16 rows one MFMA operand read touches fall on
+// different LDS banks.
+__device__ __forceinline__ int swz(int row, int piece) { return piece ^ (row & 7); }
 
 // Column permutation of W1 (over d) and W2 (over h) inside each block of 32:
 // the MFMA slot 8*G + e of a k-step holds index 4*G + e (e < 4) or
@@ -89,19 +89,41 @@ struct AttLds {
 // rows sit in the lane.  Source 4-element group og -> slot group:
 __device__ __forceinline__ int perm_group(int og) { return og < 4 ? 2 * og : 2 * (og - 4) + 1; }
 
-// Stage a [rows][cols] bf16 matrix (global, dense) into LDS rows of stride
-// `ld`, permuting 4-element groups inside every 32-column block.
-__device__ __forceinline__ void stage_permuted(uint16_t* dst, int ld, const uint16_t* src,
-                                               int rows, int cols, int tid) {
+// Stage columns [c0, c0 + cols) of src[rows][ld] (global) into dst (rows of
+// `cols` elements), permuting 4-element groups inside every 32-column block,
+// then swizzling.
+__device__ __forceinline__ void stage_permuted(uint16_t* dst, const uint16_t* src, int rows, int ld,
+                                               int c0, int cols, int tid) {
   const int per_row = cols / 8;  // 16-byte pieces per row
+#pragma unroll 4
   for (int i = tid; i < rows * per_row; i += kAttWaves * 64) {
     const int r = i / per_row, p = i % per_row;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)r * cols + 8 * p);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)r * ld + c0 + 8 * p);
     const int blk = p >> 2, og0 = (p & 3) * 2;
-    uint16_t* row = dst + r * ld + 32 * blk;
-    *reinterpret_cast<u32x2*>(row + 4 * perm_group(og0)) = u32x2{v[0], v[1]};
-    *reinterpret_cast<u32x2*>(row + 4 * perm_group(og0 + 1)) = u32x2{v[2], v[3]};
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      const int sg = perm_group(og0 + hlf);            // slot group 0..7 in the block
+      const int piece = 4 * blk + (sg >> 1);
+      uint16_t* at = dst + r * cols + 8 * swz(r, piece) + 4 * (sg & 1);
+      *reinterpret_cast<u32x2*>(at) = hlf ? u32x2{v[2], v[3]} : u32x2{v[0], v[1]};
+    }
   }
+}
+
+// Stage columns [c0, c0 + width) of src[rows][ld] into dst (rows of `width`).
+__device__ __forceinline__ void stage_cols(uint16_t* dst, const uint16_t* src, int rows, int ld, int c0,
+                                           int width, int tid) {
+  const int per_row = width / 8;
+#pragma unroll 4
+  for (int i = tid; i < rows * per_row; i += kAttWaves * 64) {
+    const int r = i / per_row, p = i % per_row;
+    *reinterpret_cast<u32x4*>(dst + r * width + 8 * swz(r, p)) =
+        *reinterpret_cast<const u32x4*>(src + (size_t)r * ld + c0 + 8 * p);
+  }
+}
+
+__device__ __forceinline__ bf16x8 lds_piece(const uint16_t* m, int width, int row, int piece) {
+  return load_bf16x8(m + row * width + 8 * swz(row, piece));
 }
 
 // int4 x 8 (one 32-bit word, element e in bits 4e..4e+3) times scale -> bf16x8
@@ -116,11 +138,13 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float scale) {
 }
 
 template <int RANK, bool CI4, bool RI4>
-__global__ __launch_bounds__(kAttWaves * 64) void attend_kernel(const AttendArgs a) {
-  __shared__ AttLds<RANK> L;
-  using Lds = AttLds<RANK>;
-  constexpr int NKS = RANK / 32;   // k-steps of the reconstruction
-  constexpr int NKB = RANK / 128;  // int4 k-blocks (4 k-steps, 16 B per lane)
+__global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendArgs a) {
+  __shared__ AttLds L;
+  constexpr int NKS = RANK / 32;         // k-steps of the reconstruction
+  constexpr int NKB = RANK / 128;        // int4 k-blocks (4 k-steps, 16 B per lane)
+  constexpr int RB = RANK < 256 ? RANK : 256;  // basis columns per staged half
+  constexpr int NHALF = RANK / RB;
+  constexpr int KS_HALF = RB / 32;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, col = lane & 15;
@@ -131,6 +155,7 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend_kernel(const AttendArgs
   const int g = a.g;
   const size_t head = (size_t)b * a.hkv + h;
   const uint16_t* qh = a.q + ((size_t)b * a.hq + (size_t)h * g) * kHeadDim;
+  uint16_t* buf = reinterpret_cast<uint16_t*>(L.buf);
 
   f32x4 zacc[2];
   bf16x8 vb_hi[8], vb_lo[8];
@@ -148,47 +173,49 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend_kernel(const AttendArgs
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) tok[nt] = chunk_of(4 * wave + 2 * nt + (col >> 3)) * kChunk + (col & 7);
 
-    // ---- issue the coefficient gather first (HBM), then stage LDS
+    // ---- the coefficient gather goes out first (HBM), one basis half at a
+    //      time: half hb+1 is in flight while half hb is multiplied
     bf16x8 cv[CI4 ? 1 : NKS][2];
     u32x4 cq[CI4 ? NKB : 1][2];
     float csc[CI4 ? NKB : 1][2];
-    if constexpr (!CI4) {
-      const uint16_t* cb = static_cast<const uint16_t*>(a.coeff) + (size_t)b * a.prefix * RANK;
+    auto gather_half = [&](int hb) {
+      if constexpr (!CI4) {
+        const uint16_t* cb = static_cast<const uint16_t*>(a.coeff) + (size_t)b * a.prefix * RANK;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
+        for (int kl = 0; kl < KS_HALF; ++kl)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          cv[ks][nt] = load_bf16x8(cb + (size_t)tok[nt] * RANK + 32 * ks + 8 * grp);
-    } else {
-      const uint8_t* cb = static_cast<const uint8_t*>(a.coeff) + (size_t)b * a.prefix * (RANK / 2);
-      const uint16_t* sb = a.coeff_scale + (size_t)b * a.prefix * (RANK / 32);
+          for (int nt = 0; nt < 2; ++nt) {
+            const int ks = hb * KS_HALF + kl;
+            cv[ks][nt] = load_bf16x8(cb + (size_t)tok[nt] * RANK + 32 * ks + 8 * grp);
+          }
+      } else {
+        const uint8_t* cb = static_cast<const uint8_t*>(a.coeff) + (size_t)b * a.prefix * (RANK / 2);
+        const uint16_t* sb = a.coeff_scale + (size_t)b * a.prefix * (RANK / 32);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kl = 0; kl < NKB / NHALF; ++kl)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          cq[kb][nt] = *reinterpret_cast<const u32x4*>(cb + (size_t)tok[nt] * (RANK / 2) + 64 * kb + 16 * grp);
-          csc[kb][nt] = f16_to_f32(sb[(size_t)tok[nt] * (RANK / 32) + 4 * kb + grp]);
-        }
+          for (int nt = 0; nt < 2; ++nt) {
+            const int kb = hb * (NKB / NHALF) + kl;
+            cq[kb][nt] = *reinterpret_cast<const u32x4*>(cb + (size_t)tok[nt] * (RANK / 2) + 64 * kb + 16 * grp);
+            csc[kb][nt] = f16_to_f32(sb[(size_t)tok[nt] * (RANK / 32) + 4 * kb + grp]);
+          }
+      }
+    };
+    gather_half(0);
+    // ---- residual lookup of token `lane` (< 32): its row in res_idx or -1
+    int rn = -1;
+    if (lane < nvalid) {
+      const int cid = chunk_of(4 * wave + (lane >> 3));
+      const int token = cid * kChunk + (lane & 7);
+      const int32_t* off = a.res_off + head * (size_t)(a.n_chunks + 1);
+      const int32_t* ridx = a.res_idx + head * (size_t)a.n_resid;
+      const int o1 = min(off[cid + 1], a.n_resid);
+      for (int i = max(off[cid], 0); i < o1; ++i)
+        if (ridx[i] == token) rn = i;
     }
 
-    uint16_t* basisT = reinterpret_cast<uint16_t*>(L.u);
-    {
-      const uint16_t* src = a.basis + head * (size_t)kHeadDim * RANK;
-      constexpr int per_row = RANK / 8;
-      for (int i = tid; i < kHeadDim * per_row; i += kAttWaves * 64) {
-        const int r = i / per_row, p = i % per_row;
-        *reinterpret_cast<u32x4*>(basisT + r * Lds::BS + 8 * p) =
-            *reinterpret_cast<const u32x4*>(src + (size_t)r * RANK + 8 * p);
-      }
-    }
-    {  // RoPE rotations: base angle of every chunk start, offsets 0..7
-      const int cs = tid >> 4, p0 = (tid & 15) * 4;
-      const double pos = (double)chunk_of(cs) * kChunk;
-#pragma unroll
-      for (int p = p0; p < p0 + 4; ++p) L.rope_base[cs][p] = rot_of(pos * a.inv_freq[p]);
-      const int i = tid >> 6, p = tid & 63;
-      L.rope_off[i][p] = rot_of((double)i * a.inv_freq[p]);
-    }
+    const uint16_t* basis = a.basis + head * (size_t)kHeadDim * RANK;
+    stage_cols(buf, basis, kHeadDim, RANK, 0, RB, tid);
     __syncthreads();
 
     // ---- reconstruction: acc[nt][mt] = K_pre^T rows d = 16 mt + 4 grp + e
@@ -198,24 +225,34 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend_kernel(const AttendArgs
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 bop[2];
-      int r0;
-      if constexpr (!CI4) {
-        bop[0] = cv[ks][0];
-        bop[1] = cv[ks][1];
-        r0 = 32 * ks + 8 * grp;
-      } else {
-        const int kb = ks >> 2, kw = ks & 3;
-        bop[0] = dequant8(cq[kb][0][kw], csc[kb][0]);
-        bop[1] = dequant8(cq[kb][1][kw], csc[kb][1]);
-        r0 = 128 * kb + 32 * grp + 8 * kw;
+    for (int hb = 0; hb < NHALF; ++hb) {
+      if (hb > 0) {
+        __syncthreads();
+        stage_cols(buf, basis, kHeadDim, RANK, RB * hb, RB, tid);
+        __syncthreads();
       }
+      if (hb + 1 < NHALF) gather_half(hb + 1);
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const bf16x8 aop = load_bf16x8(basisT + (16 * mt + col) * Lds::BS + r0);
-        acc[0][mt] = mfma16(aop, bop[0], acc[0][mt]);
-        acc[1][mt] = mfma16(aop, bop[1], acc[1][mt]);
+      for (int kl = 0; kl < KS_HALF; ++kl) {
+        const int ks = hb * KS_HALF + kl;
+        bf16x8 bop[2];
+        int piece;
+        if constexpr (!CI4) {
+          bop[0] = cv[ks][0];
+          bop[1] = cv[ks][1];
+          piece = 4 * kl + grp;
+        } else {
+          const int kb = ks >> 2, kw = ks & 3;
+          bop[0] = dequant8(cq[kb][0][kw], csc[kb][0]);
+          bop[1] = dequant8(cq[kb][1][kw], csc[kb][1]);
+          piece = 16 * (kb & 1) + 4 * grp + kw;
+        }
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const bf16x8 aop = lds_piece(buf, RB, 16 * mt + col, piece);
+          acc[0][mt] = mfma16(aop, bop[0], acc[0][mt]);
+          acc[1][mt] = mfma16(aop, bop[1], acc[1][mt]);
+        }
       }
     }
     const size_t row0 = head * (size_t)a.k_eff * kChunk + (size_t)(chunk0 + 4 * wave) * kChunk;
@@ -228,12 +265,34 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend_kernel(const AttendArgs
             *reinterpret_cast<f32x4*>(a.kpre_out + (row0 + 16 * nt + col) * kHeadDim + 16 * mt + 4 * grp) = acc[nt][mt];
     }
 
-    // ---- K_pre as the MLP1 operand (bf16), then RoPE in place
+    // ---- K_pre as the MLP1 operand (bf16)
     bf16x8 kpre_b[2][4];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int s = 0; s < 4; ++s) kpre_b[nt][s] = pack8(acc[nt][2 * s], acc[nt][2 * s + 1]);
+
+    // ---- RoPE rotations of this workgroup's tokens: base angle of every
+    //      chunk start (fp64-reduced) and the offsets 0..7 inside a chunk.
+    //      The basis is no longer read: W1 / biases go to LDS meanwhile.
+    {
+      const int cs = tid >> 4, p0 = (tid & 15) * 4;
+      const double pos = (double)chunk_of(cs) * kChunk;
+#pragma unroll
+      for (int p = p0; p < p0 + 4; ++p) L.rope_base[cs][p] = rot_of(pos * a.inv_freq[p]);
+      const int i = tid >> 5, q0 = (tid & 31) * 2;
+#pragma unroll
+      for (int p = q0; p < q0 + 2; ++p) L.rope_off[i][p] = rot_of((double)i * a.inv_freq[p]);
+    }
+    __syncthreads();
+    const uint16_t* w1h = a.w1 + head * (size_t)kHidden * kHeadDim;
+    const uint16_t* w2h = a.w2 + head * (size_t)kHeadDim * kHidden;
+    uint16_t* w1s = buf;                            // [128 h][128 d]
+    uint16_t* w2s = buf + (kHidden / 2) * kHeadDim;  // [128 d][128 h]
+    stage_permuted(w1s, w1h, kHidden / 2, kHeadDim, 0, kHeadDim, tid);
+    stage_permuted(w2s, w2h, kHeadDim, kHidden, 0, kHidden / 2, tid);
+    L.b1f[tid] = bf16_to_f32(a.b1[head * kHidden + tid]);
+    if (tid < kHeadDim) L.b2f[tid] = bf16_to_f32(a.b2[head * kHeadDim + tid]);
 
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -283,99 +342,85 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend_kernel(const AttendArgs
       }
     }
 
-    // ---- swap the LDS contents: basis out, W1 / W2 / biases in
+    // ---- value MLP, 32 hidden units at a time: MLP1 chunk (b1 as the
+    //      accumulator's initial value) -> GELU -> bf16 -> MLP2 accumulate.
+    //      Hidden units [0, 128) use the W1/W2 halves staged above, then the
+    //      buffer is refilled with the halves of units [128, 256).
     __syncthreads();
-    uint16_t* w1s = reinterpret_cast<uint16_t*>(L.u);
-    uint16_t* w2s = reinterpret_cast<uint16_t*>(L.u + Lds::W1_BYTES);
-    stage_permuted(w1s, Lds::W1S, a.w1 + head * (size_t)kHidden * kHeadDim, kHidden, kHeadDim, tid);
-    stage_permuted(w2s, Lds::W2S, a.w2 + head * (size_t)kHeadDim * kHidden, kHeadDim, kHidden, tid);
-    if (tid < kHidden) L.b1f[tid] = bf16_to_f32(a.b1[head * kHidden + tid]);
-    if (tid < kHeadDim) L.b2f[tid] = bf16_to_f32(a.b2[head * kHeadDim + tid]);
-    __syncthreads();
-
-    // ---- value MLP, 32 hidden units at a time; hid never leaves the VGPRs
     f32x4 vacc[2][8];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) vacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int hc = 0; hc < kHidden / 32; ++hc) {
-      f32x4 hacc[2][2];
-#pragma unroll
-      for (int hm = 0; hm < 2; ++hm)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) hacc[hm][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int hm = 0; hm < 2; ++hm) {
-          const bf16x8 aop = load_bf16x8(w1s + (32 * hc + 16 * hm + col) * Lds::W1S + 32 * s + 8 * grp);
-          hacc[hm][0] = mfma16(aop, kpre_b[0][s], hacc[hm][0]);
-          hacc[hm][1] = mfma16(aop, kpre_b[1][s], hacc[hm][1]);
-        }
-      }
-#pragma unroll
-      for (int hm = 0; hm < 2; ++hm)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float bias = L.b1f[32 * hc + 16 * hm + 4 * grp + e];
-          hacc[hm][0][e] = gelu_fast(hacc[hm][0][e] + bias);
-          hacc[hm][1][e] = gelu_fast(hacc[hm][1][e] + bias);
-        }
-      const bf16x8 ha0 = pack8(hacc[0][0], hacc[1][0]);
-      const bf16x8 ha1 = pack8(hacc[0][1], hacc[1][1]);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const bf16x8 bop = load_bf16x8(w2s + (16 * nt + col) * Lds::W2S + 32 * hc + 8 * grp);
-        vacc[0][nt] = mfma16(ha0, bop, vacc[0][nt]);
-        vacc[1][nt] = mfma16(ha1, bop, vacc[1][nt]);
-      }
-    }
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       const float bias = L.b2f[16 * nt + col];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vacc[mt][nt][e] += bias;
+      vacc[0][nt] = f32x4{bias, bias, bias, bias};
+      vacc[1][nt] = vacc[0][nt];
     }
-
-    // ---- residual scatter-add: lane t (< 32) finds token t's stored row
-    {
-      int rn = -1;
-      if (lane < nvalid) {
-        const int cid = chunk_of(4 * wave + (lane >> 3));
-        const int token = cid * kChunk + (lane & 7);
-        const int32_t* off = a.res_off + head * (size_t)(a.n_chunks + 1);
-        const int32_t* ridx = a.res_idx + head * (size_t)a.n_resid;
-        const int o1 = min(off[cid + 1], a.n_resid);
-        for (int i = max(off[cid], 0); i < o1; ++i)
-          if (ridx[i] == token) rn = i;
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp) {
+      if (hp > 0) {
+        __syncthreads();
+        stage_permuted(w1s, w1h + (kHidden / 2) * kHeadDim, kHidden / 2, kHeadDim, 0, kHeadDim, tid);
+        stage_permuted(w2s, w2h, kHeadDim, kHidden, kHidden / 2, kHidden / 2, tid);
+        __syncthreads();
       }
+#pragma unroll 1
+      for (int hl = 0; hl < 4; ++hl) {
+        const int hc = 4 * hp + hl;
+        f32x4 hacc[2][2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int hm = 0; hm < 2; ++hm) {
+          const f32x4 bias = *reinterpret_cast<const f32x4*>(&L.b1f[32 * hc + 16 * hm + 4 * grp]);
+          hacc[hm][0] = bias;
+          hacc[hm][1] = bias;
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int nn = __shfl(rn, 16 * mt + 4 * grp + e);
-          if (nn >= 0) {
-            const size_t rrow = head * (size_t)a.n_resid + nn;
+        for (int s = 0; s < 4; ++s) {
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-              const int d = 16 * nt + col;
-              float r;
-              if constexpr (!RI4) {
-                r = bf16_to_f32(static_cast<const uint16_t*>(a.res_val)[rrow * kHeadDim + d]);
-              } else {
-                const uint32_t byte = static_cast<const uint8_t*>(a.res_val)[rrow * (kHeadDim / 2) + (d >> 1)];
-                const int code = static_cast<int>(((byte >> (4 * (d & 1))) & 0xFu) ^ 8u) - 8;
-                r = static_cast<float>(code) * f16_to_f32(a.res_scale[rrow * (kHeadDim / 32) + (d >> 5)]);
-              }
-              vacc[mt][nt][e] += r;
-            }
+          for (int hm = 0; hm < 2; ++hm) {
+            const bf16x8 aop = lds_piece(w1s, kHeadDim, 32 * hl + 16 * hm + col, 4 * s + grp);
+            hacc[hm][0] = mfma16(aop, kpre_b[0][s], hacc[hm][0]);
+            hacc[hm][1] = mfma16(aop, kpre_b[1][s], hacc[hm][1]);
           }
         }
+#pragma unroll
+        for (int hm = 0; hm < 2; ++hm)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hacc[hm][nt][e] = gelu_fast(hacc[hm][nt][e]);
+        const bf16x8 ha0 = pack8(hacc[0][0], hacc[1][0]);
+        const bf16x8 ha1 = pack8(hacc[0][1], hacc[1][1]);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const bf16x8 bop = lds_piece(w2s, kHidden / 2, 16 * nt + col, 4 * hl + grp);
+          vacc[0][nt] = mfma16(ha0, bop, vacc[0][nt]);
+          vacc[1][nt] = mfma16(ha1, bop, vacc[1][nt]);
+        }
+      }
     }
+
+    // ---- residual scatter-add (rows found at the start)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int nn = __shfl(rn, 16 * mt + 4 * grp + e);
+        if (nn >= 0) {
+          const size_t rrow = head * (size_t)a.n_resid + nn;
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) {
+            const int d = 16 * nt + col;
+            float r;
+            if constexpr (!RI4) {
+              r = bf16_to_f32(static_cast<const uint16_t*>(a.res_val)[rrow * kHeadDim + d]);
+            } else {
+              const uint32_t byte = static_cast<const uint8_t*>(a.res_val)[rrow * (kHeadDim / 2) + (d >> 1)];
+              const int code = static_cast<int>(((byte >> (4 * (d & 1))) & 0xFu) ^ 8u) - 8;
+              r = static_cast<float>(code) * f16_to_f32(a.res_scale[rrow * (kHeadDim / 32) + (d >> 5)]);
+            }
+            vacc[mt][nt][e] += r;
+          }
+        }
+      }
     if (a.vhat_out) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -458,9 +503,9 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend_kernel(const AttendArgs
     oacc[nt] = o;
   }
 
-  // ======================================== merge the 8 waves, write partial
+  // ======================================== merge the 4 waves, write partial
   __syncthreads();
-  float* mo = reinterpret_cast<float*>(L.u);
+  float* mo = reinterpret_cast<float*>(L.buf);
   float* ml = mo + kAttWaves * 16 * kHeadDim;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt)
@@ -471,7 +516,7 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend_kernel(const AttendArgs
     ml[kAttWaves * 16 + wave * 16 + col] = lsum;
   }
   __syncthreads();
-  float* part = a.part + ((head * a.n_split + split) * (size_t)g) * kPartStride;
+  float* part = a.part + (head * (size_t)a.n_split + split) * g * kPartStride;
   for (int idx = tid; idx < g * kHeadDim; idx += kAttWaves * 64) {
     const int j = idx / kHeadDim, d = idx % kHeadDim;
     float M = -__builtin_huge_valf();
@@ -491,6 +536,7 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend_kernel(const AttendArgs
     }
     part[j * kPartStride + 2 + d] = o;
   }
+
 }
 
 template <int RANK>
@@ -520,34 +566,67 @@ hipError_t launch_attend(const AttendArgs& a, int rank, bool ci4, bool ri4, hipS
 }
 
 // ---------------------------------------------------------------------------
-// Split merge: log-sum-exp combination of the per-workgroup partial states
-// (m in log2 units, l, o) of each query head, written as bf16.
+// Split merge: one workgroup per (sequence, KV head).  The per-split weights
+// w[s][j] = exp2(m_sj - M_j) / L_j go to LDS first, then every thread sums
+// its (j, d) outputs over the splits with independent loads.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part,
-                                                    uint16_t* __restrict__ out, int hkv, int g,
-                                                    int n_split) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const size_t head = (size_t)b * hkv + h;
-  for (int j = 0; j < g; ++j) {
-    const float* p = part + (head * n_split * (size_t)g + j) * kPartStride;
-    const size_t st = (size_t)g * kPartStride;
-    float M = -__builtin_huge_valf();
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, p[s * st]);
-    float lt = 0.f, o = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const float ms = p[s * st];
-      const float sc = ms == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-      lt += p[s * st + 1] * sc;
-      o += p[s * st + 2 + d] * sc;
+constexpr int kMergeThreads = 512;
+constexpr int kMergeMaxSplit = 1024;
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part,
+                                                              uint16_t* __restrict__ out, int hkv,
+                                                              int g, int n_split) {
+  __shared__ float wgt[kMergeMaxSplit * 4];
+  __shared__ float inv_l[16];
+  const int tid = threadIdx.x;
+  const size_t head = (size_t)blockIdx.y * hkv + blockIdx.x;
+  const float* ph = part + head * (size_t)n_split * g * kPartStride;
+  const size_t st = (size_t)g * kPartStride;
+  uint16_t* oh = out + head * (size_t)g * kHeadDim;
+  const int ns = n_split;  // n_split * min(g, 16) <= 4096 is checked at launch
+  for (int j0 = 0; j0 < g; j0 += 16) {
+    const int gj = min(16, g - j0);
+    // M_j: one wave per query head
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int j = wave; j < gj; j += kMergeThreads / 64) {
+      float m = -__builtin_huge_valf();
+      for (int s = lane; s < ns; s += 64) m = fmaxf(m, ph[s * st + (j0 + j) * kPartStride]);
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      float l = 0.f;
+      for (int s = lane; s < ns; s += 64) {
+        const float ms = ph[s * st + (j0 + j) * kPartStride];
+        const float w = ms == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(ms - m);
+        wgt[s * gj + j] = w;
+        l += w * ph[s * st + (j0 + j) * kPartStride + 1];
+      }
+      for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+      if (lane == 0) inv_l[j] = 1.f / l;
     }
-    const __bf16 r = (__bf16)(o / lt);
-    out[(head * g + j) * kHeadDim + d] = __builtin_bit_cast(uint16_t, r);
+    __syncthreads();
+    for (int idx = tid; idx < gj * kHeadDim; idx += kMergeThreads) {
+      const int j = idx / kHeadDim, d = idx % kHeadDim;
+      const float* p = ph + (j0 + j) * kPartStride + 2 + d;
+      float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+      int s = 0;
+      for (; s + 4 <= ns; s += 4) {
+        const float a0 = p[s * st], a1 = p[(s + 1) * st], a2 = p[(s + 2) * st], a3 = p[(s + 3) * st];
+        o0 += a0 * wgt[s * gj + j];
+        o1 += a1 * wgt[(s + 1) * gj + j];
+        o2 += a2 * wgt[(s + 2) * gj + j];
+        o3 += a3 * wgt[(s + 3) * gj + j];
+      }
+      for (; s < ns; ++s) o0 += p[s * st] * wgt[s * gj + j];
+      const __bf16 r = (__bf16)(((o0 + o1) + (o2 + o3)) * inv_l[j]);
+      oh[(j0 + j) * kHeadDim + d] = __builtin_bit_cast(uint16_t, r);
+    }
+    __syncthreads();
   }
 }
 
 hipError_t launch_merge(const float* part, uint16_t* out, int nb, int hkv, int g, int n_split,
                         hipStream_t st) {
-  hipLaunchKernelGGL(merge_kernel, dim3(hkv, nb), dim3(kHeadDim), 0, st, part, out, hkv, g, n_split);
+  if ((long long)n_split * (g < 16 ? g : 16) > kMergeMaxSplit * 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_kernel, dim3(hkv, nb), dim3(kMergeThreads), 0, st, part, out, hkv, g, n_split);
   return hipGetLastError();
 }
 

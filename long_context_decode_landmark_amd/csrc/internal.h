@@ -6,12 +6,13 @@
 
 namespace lowram {
 
-// Selected-chunk attention: one workgroup = 8 waves x 32 tokens = 32 chunks.
-constexpr int kAttWaves = 8;
+// Selected-chunk attention: one workgroup = 4 waves x 32 tokens = 16 chunks.
+constexpr int kAttWaves = 4;
 constexpr int kAttTokWave = 32;
-constexpr int kAttChunksWG = kAttWaves * kAttTokWave / 8;  // 32
-constexpr int kAttTokWG = kAttWaves * kAttTokWave;         // 256
+constexpr int kAttChunksWG = kAttWaves * kAttTokWave / 8;  // 16
+constexpr int kAttTokWG = kAttWaves * kAttTokWave;         // 128
 constexpr int kPartStride = 2 + 128;                       // m, l, o[128] per query head
+constexpr int kMergeMaxWeights = 4096;                     // n_split * min(g, 16) limit of the merge
 
 struct AttendArgs {
   const void* coeff;

@@ -23,6 +23,7 @@ SYMBOLS = (
     "lowram_workspace_bytes",
     "lowram_decode_step",
     "lowram_decode_stages",
+    "lowram_decode_step_events",
     "dense_workspace_bytes",
     "dense_decode_step",
     "lowram_resid_chunk_offsets",
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
                                          vp, vp, vp, vp, sz, vp]
         L.lowram_decode_stages.argtypes = [ctypes.POINTER(LowramShape), ctypes.POINTER(LowramLayerCache),
                                            vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.lowram_decode_step_events.argtypes = [ctypes.POINTER(LowramShape), ctypes.POINTER(LowramLayerCache),
+                                                vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_void_p)]
         L.dense_workspace_bytes.argtypes = [ctypes.POINTER(DenseShape), ctypes.POINTER(sz)]
         L.dense_decode_step.argtypes = [ctypes.POINTER(DenseShape), ctypes.POINTER(DenseLayerCache),
                                         vp, vp, vp, sz, vp]
@@ -152,6 +155,16 @@ def decode_step(shape, cache, q, out, workspace, sel_out=None, stream=None) -> N
     _check(lib().lowram_decode_step(ctypes.byref(shape), ctypes.byref(c), _ptr(q), _ptr(out),
                                     _ptr(sel_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)), "lowram_decode_step")
+
+
+def decode_step_events(shape, cache, q, out, workspace, events, sel_out=None, stream=None) -> None:
+    """lowram_decode_step recording 5 torch.cuda.Event (enable_timing) around its kernels."""
+    c = cache if isinstance(cache, LowramLayerCache) else make_cache(cache)
+    arr = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    _check(lib().lowram_decode_step_events(ctypes.byref(shape), ctypes.byref(c), _ptr(q), _ptr(out),
+                                           _ptr(sel_out), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(stream), arr),
+           "lowram_decode_step_events")
 
 
 def decode_stages(shape, cache, q, out, workspace, sel_out=None, scores=None, kpre=None, kpost=None,

@@ -67,7 +67,7 @@ def test_workspace_bytes_formula():
     s = native.make_shape(cfg, batch=28)
     heads = 28 * 8
     keff = min(cfg.topk, cfg.n_cand)
-    n_split = -(-keff // 32) + -(-cfg.window // 256)
+    n_split = -(-keff // 16) + -(-cfg.window // 128)
     al = lambda x: (x + 255) // 256 * 256
     want = al(heads * cfg.n_cand * 4) + al(heads * keff * 4) + al(heads * n_split * 4 * 130 * 4)
     assert native.workspace_bytes(s) == want
