@@ -22,10 +22,10 @@
 // the contraction index, applied to the other operand instead):
 //   recon   D[d][t]  = basis^T[d][r] (LDS)   x C[t][r] (global -> VGPR)
 //   RoPE    lane-local: pair (i, i+64) sits in m-tiles mt and mt+4
-//   QK      D[t][j]  = K_post[t][d] (VGPR, hi+lo bf16) x q[j][d]
+//   QK      D[t][j]  = K_post[t][d] (VGPR, bf16)  x q[j][d]
 //   MLP1    D[h][t]  = W1[h][d] (LDS)        x K_pre[t][d] (VGPR)
 //   MLP2    D[t][d]  = hid[t][h] (VGPR)      x W2[d][h] (LDS)
-//   PV      D[j][d]  = p[j][t] (VGPR)        x V[t][d] (VGPR, hi+lo bf16)
+//   PV      D[j][d]  = p[j][t] (VGPR)        x V[t][d] (VGPR, bf16)
 // The operands shared by the 4 waves pass through one 64 KiB LDS buffer in
 // four stages (basis r < 256, basis r >= 256, W1, W2), so a workgroup needs
 // under 80 KiB and two workgroups share a CU: one stages or waits on the
@@ -78,52 +78,58 @@ struct AttLds {
   float b2f[kHeadDim];
 };
 
-// Staged matrices keep dense rows; the 16-byte piece p of row r is stored at
-// piece p ^ (r & 7) so the 16 rows one MFMA operand read touches fall on
-// different LDS banks.
-__device__ __forceinline__ int swz(int row, int piece) { return piece ^ (row & 7); }
+// Staged matrices keep dense rows of NP 16-byte pieces; piece p of row r
+// sits at p ^ (r & mask) with mask = 15 (7 for 8-piece rows), so the 16
+// rows one MFMA operand read touches fall on different LDS banks.
+template <int NP>
+__device__ __forceinline__ constexpr int swz(int row, int piece) {
+  return piece ^ (row & (NP >= 16 ? 15 : 7));
+}
 
 // Column permutation of W1 (over d) and W2 (over h) inside each block of 32:
 // the MFMA slot 8*G + e of a k-step holds index 4*G + e (e < 4) or
 // 16 + 4*G + (e - 4) (e >= 4), which is how the previous stage's accumulator
 // rows sit in the lane.  Source 4-element group og -> slot group:
-__device__ __forceinline__ int perm_group(int og) { return og < 4 ? 2 * og : 2 * (og - 4) + 1; }
+__device__ __forceinline__ constexpr int perm_group(int og) { return og < 4 ? 2 * og : 2 * (og - 4) + 1; }
 
-// Stage columns [c0, c0 + cols) of src[rows][ld] (global) into dst (rows of
-// `cols` elements), permuting 4-element groups inside every 32-column block,
-// then swizzling.
-__device__ __forceinline__ void stage_permuted(uint16_t* dst, const uint16_t* src, int rows, int ld,
-                                               int c0, int cols, int tid) {
-  const int per_row = cols / 8;  // 16-byte pieces per row
-#pragma unroll 4
-  for (int i = tid; i < rows * per_row; i += kAttWaves * 64) {
-    const int r = i / per_row, p = i % per_row;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)r * ld + c0 + 8 * p);
-    const int blk = p >> 2, og0 = (p & 3) * 2;
+// Stage columns [c0, c0 + 8*NP) of the matrix behind `src` (row stride LD
+// elements) into dst (ROWS rows of NP pieces).  Thread t copies piece t % NP
+// of rows t / NP + u * (256 / NP): a buffer load (one lane offset, the pass
+// as SGPR offset) and an LDS store at a lane base plus an immediate.
+template <int ROWS, int NP, int LD>
+__device__ __forceinline__ void stage_plain(unsigned char* dst, __amdgpu_buffer_rsrc_t src, int c0, int tid) {
+  constexpr int RSTEP = kAttWaves * 64 / NP;
+  const int r0 = tid / NP, p = tid % NP;
+  const uint32_t goff = (uint32_t)(r0 * LD + c0 + 8 * p) * 2;
 #pragma unroll
-    for (int hlf = 0; hlf < 2; ++hlf) {
-      const int sg = perm_group(og0 + hlf);            // slot group 0..7 in the block
-      const int piece = 4 * blk + (sg >> 1);
-      uint16_t* at = dst + r * cols + 8 * swz(r, piece) + 4 * (sg & 1);
-      *reinterpret_cast<u32x2*>(at) = hlf ? u32x2{v[2], v[3]} : u32x2{v[0], v[1]};
-    }
+  for (int u = 0; u < ROWS / RSTEP; ++u) {
+    const int r = r0 + u * RSTEP;
+    const u32x4 v = buffer_ld16(src, goff, u * RSTEP * LD * 2);
+    *reinterpret_cast<u32x4*>(dst + (r * NP + swz<NP>(r, p)) * 16) = v;
   }
 }
 
-// Stage columns [c0, c0 + width) of src[rows][ld] into dst (rows of `width`).
-__device__ __forceinline__ void stage_cols(uint16_t* dst, const uint16_t* src, int rows, int ld, int c0,
-                                           int width, int tid) {
-  const int per_row = width / 8;
-#pragma unroll 4
-  for (int i = tid; i < rows * per_row; i += kAttWaves * 64) {
-    const int r = i / per_row, p = i % per_row;
-    *reinterpret_cast<u32x4*>(dst + r * width + 8 * swz(r, p)) =
-        *reinterpret_cast<const u32x4*>(src + (size_t)r * ld + c0 + 8 * p);
+// As stage_plain for 16-piece rows, with the 4-element group permutation
+// inside every 32-column block (W1 over d, W2 over h).
+template <int ROWS, int LD>
+__device__ __forceinline__ void stage_perm16(unsigned char* dst, __amdgpu_buffer_rsrc_t src, int c0, int tid) {
+  constexpr int NP = 16, RSTEP = kAttWaves * 64 / NP;  // 16 rows per pass keep r & 15
+  const int r0 = tid / NP, p = tid % NP;
+  const int blk = p >> 2, og0 = (p & 3) * 2;
+  const int sg0 = perm_group(og0), sg1 = perm_group(og0 + 1);
+  const int o0 = (r0 * NP + ((4 * blk + (sg0 >> 1)) ^ r0)) * 16 + 8 * (sg0 & 1);
+  const int o1 = (r0 * NP + ((4 * blk + (sg1 >> 1)) ^ r0)) * 16 + 8 * (sg1 & 1);
+  const uint32_t goff = (uint32_t)(r0 * LD + c0 + 8 * p) * 2;
+#pragma unroll
+  for (int u = 0; u < ROWS / RSTEP; ++u) {
+    const u32x4 v = buffer_ld16(src, goff, u * RSTEP * LD * 2);
+    *reinterpret_cast<u32x2*>(dst + o0 + u * RSTEP * NP * 16) = u32x2{v[0], v[1]};
+    *reinterpret_cast<u32x2*>(dst + o1 + u * RSTEP * NP * 16) = u32x2{v[2], v[3]};
   }
 }
 
-__device__ __forceinline__ bf16x8 lds_piece(const uint16_t* m, int width, int row, int piece) {
-  return load_bf16x8(m + row * width + 8 * swz(row, piece));
+__device__ __forceinline__ bf16x8 lds16(const unsigned char* base, int off) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + off));
 }
 
 // int4 x 8 (one 32-bit word, element e in bits 4e..4e+3) times scale -> bf16x8
@@ -145,6 +151,8 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
   constexpr int RB = RANK < 256 ? RANK : 256;  // basis columns per staged half
   constexpr int NHALF = RANK / RB;
   constexpr int KS_HALF = RB / 32;
+  constexpr int NPB = RB / 8;                  // 16-byte pieces per staged basis row
+  constexpr int W2OFF = (kHidden / 2) * kHeadDim * 2;  // byte offset of the W2 half in buf
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, col = lane & 15;
@@ -155,10 +163,10 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
   const int g = a.g;
   const size_t head = (size_t)b * a.hkv + h;
   const uint16_t* qh = a.q + ((size_t)b * a.hq + (size_t)h * g) * kHeadDim;
-  uint16_t* buf = reinterpret_cast<uint16_t*>(L.buf);
+  unsigned char* buf = L.buf;
 
   f32x4 zacc[2];
-  bf16x8 vb_hi[8], vb_lo[8];
+  bf16x8 vb[8];
   int nvalid;
 
   if (split < a.n_sel_tiles) {
@@ -172,6 +180,17 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
     int tok[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) tok[nt] = chunk_of(4 * wave + 2 * nt + (col >> 3)) * kChunk + (col & 7);
+
+    // Per-lane byte offsets of the swizzled operand reads.  A read of row
+    // 16*m + col, piece 4*k + grp lands at piece (4*k + grp) ^ (col & mask)
+    // = 4*(k ^ (col >> 2)) + (grp ^ (col & 3)) of that row (mask 15); the
+    // int4 basis read of piece 4*grp + k lands at 4*(grp ^ (col >> 2)) +
+    // (k ^ (col & 3)).  Row and 16-piece-block terms are immediates.
+    const int chi = col >> 2, clo = col & 3;
+    const int chib = NPB >= 16 ? chi : (chi & 1);
+    auto pbw = [&](int k) { return col * 256 + 16 * (4 * (k ^ chi) + (grp ^ clo)); };
+    auto pbb = [&](int k) { return col * (NPB * 16) + 16 * (4 * (k ^ chib) + (grp ^ clo)); };
+    auto pbi = [&](int k) { return col * (NPB * 16) + 16 * (4 * (grp ^ chib) + (k ^ clo)); };
 
     // ---- the coefficient gather goes out first (HBM), one basis half at a
     //      time: half hb+1 is in flight while half hb is multiplied
@@ -214,8 +233,8 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
         if (ridx[i] == token) rn = i;
     }
 
-    const uint16_t* basis = a.basis + head * (size_t)kHeadDim * RANK;
-    stage_cols(buf, basis, kHeadDim, RANK, 0, RB, tid);
+    const __amdgpu_buffer_rsrc_t basis = buffer_rsrc(a.basis + head * (size_t)kHeadDim * RANK, kHeadDim * RANK * 2);
+    stage_plain<kHeadDim, NPB, RANK>(buf, basis, 0, tid);
     __syncthreads();
 
     // ---- reconstruction: acc[nt][mt] = K_pre^T rows d = 16 mt + 4 grp + e
@@ -228,7 +247,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
     for (int hb = 0; hb < NHALF; ++hb) {
       if (hb > 0) {
         __syncthreads();
-        stage_cols(buf, basis, kHeadDim, RANK, RB * hb, RB, tid);
+        stage_plain<kHeadDim, NPB, RANK>(buf, basis, RB * hb, tid);
         __syncthreads();
       }
       if (hb + 1 < NHALF) gather_half(hb + 1);
@@ -236,20 +255,20 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
       for (int kl = 0; kl < KS_HALF; ++kl) {
         const int ks = hb * KS_HALF + kl;
         bf16x8 bop[2];
-        int piece;
+        int off;
         if constexpr (!CI4) {
           bop[0] = cv[ks][0];
           bop[1] = cv[ks][1];
-          piece = 4 * kl + grp;
+          off = pbb(kl & 3) + 256 * (kl >> 2);  // piece 4*kl + grp of the half
         } else {
           const int kb = ks >> 2, kw = ks & 3;
           bop[0] = dequant8(cq[kb][0][kw], csc[kb][0]);
           bop[1] = dequant8(cq[kb][1][kw], csc[kb][1]);
-          piece = 16 * (kb & 1) + 4 * grp + kw;
+          off = pbi(kw) + 256 * (kb & 1);       // piece 16*(kb&1) + 4*grp + kw
         }
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-          const bf16x8 aop = lds_piece(buf, RB, 16 * mt + col, piece);
+          const bf16x8 aop = lds16(buf, off + mt * 16 * NPB * 16);
           acc[0][mt] = mfma16(aop, bop[0], acc[0][mt]);
           acc[1][mt] = mfma16(aop, bop[1], acc[1][mt]);
         }
@@ -285,12 +304,10 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
       for (int p = q0; p < q0 + 2; ++p) L.rope_off[i][p] = rot_of((double)i * a.inv_freq[p]);
     }
     __syncthreads();
-    const uint16_t* w1h = a.w1 + head * (size_t)kHidden * kHeadDim;
-    const uint16_t* w2h = a.w2 + head * (size_t)kHeadDim * kHidden;
-    uint16_t* w1s = buf;                            // [128 h][128 d]
-    uint16_t* w2s = buf + (kHidden / 2) * kHeadDim;  // [128 d][128 h]
-    stage_permuted(w1s, w1h, kHidden / 2, kHeadDim, 0, kHeadDim, tid);
-    stage_permuted(w2s, w2h, kHeadDim, kHidden, 0, kHidden / 2, tid);
+    const __amdgpu_buffer_rsrc_t w1h = buffer_rsrc(a.w1 + head * (size_t)kHidden * kHeadDim, kHidden * kHeadDim * 2);
+    const __amdgpu_buffer_rsrc_t w2h = buffer_rsrc(a.w2 + head * (size_t)kHeadDim * kHidden, kHeadDim * kHidden * 2);
+    stage_perm16<kHidden / 2, kHeadDim>(buf, w1h, 0, tid);             // W1 rows h < 128
+    stage_perm16<kHeadDim, kHidden>(buf + W2OFF, w2h, 0, tid);         // W2 columns h < 128
     L.b1f[tid] = bf16_to_f32(a.b1[head * kHidden + tid]);
     if (tid < kHeadDim) L.b2f[tid] = bf16_to_f32(a.b2[head * kHeadDim + tid]);
 
@@ -320,7 +337,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
             *reinterpret_cast<f32x4*>(a.kpost_out + (row0 + 16 * nt + col) * kHeadDim + 16 * mt + 4 * grp) = acc[nt][mt];
     }
 
-    // ---- QK: z[t][j], K_post split hi + lo so the logits keep fp32 accuracy
+    // ---- QK: z[t][j] with K_post rounded to bf16 (2^-9 relative per entry)
     {
       bf16x8 qp[4];
 #pragma unroll
@@ -332,12 +349,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
       for (int nt = 0; nt < 2; ++nt) {
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 hi = pack8(acc[nt][2 * s], acc[nt][2 * s + 1]);
-          const bf16x8 lo = pack8_lo(acc[nt][2 * s], acc[nt][2 * s + 1], hi);
-          z = mfma16(hi, qp[s], z);
-          z = mfma16(lo, qp[s], z);
-        }
+        for (int s = 0; s < 4; ++s) z = mfma16(pack8(acc[nt][2 * s], acc[nt][2 * s + 1]), qp[s], z);
         zacc[nt] = z;
       }
     }
@@ -358,8 +370,8 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
     for (int hp = 0; hp < 2; ++hp) {
       if (hp > 0) {
         __syncthreads();
-        stage_permuted(w1s, w1h + (kHidden / 2) * kHeadDim, kHidden / 2, kHeadDim, 0, kHeadDim, tid);
-        stage_permuted(w2s, w2h, kHeadDim, kHidden, kHidden / 2, kHidden / 2, tid);
+        stage_perm16<kHidden / 2, kHeadDim>(buf, w1h, (kHidden / 2) * kHeadDim, tid);
+        stage_perm16<kHeadDim, kHidden>(buf + W2OFF, w2h, kHidden / 2, tid);
         __syncthreads();
       }
 #pragma unroll 1
@@ -376,7 +388,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
           for (int hm = 0; hm < 2; ++hm) {
-            const bf16x8 aop = lds_piece(w1s, kHeadDim, 32 * hl + 16 * hm + col, 4 * s + grp);
+            const bf16x8 aop = lds16(buf, pbw(s) + (32 * hl + 16 * hm) * 256);
             hacc[hm][0] = mfma16(aop, kpre_b[0][s], hacc[hm][0]);
             hacc[hm][1] = mfma16(aop, kpre_b[1][s], hacc[hm][1]);
           }
@@ -391,7 +403,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
         const bf16x8 ha1 = pack8(hacc[0][1], hacc[1][1]);
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
-          const bf16x8 bop = lds_piece(w2s, kHidden / 2, 16 * nt + col, 4 * hl + grp);
+          const bf16x8 bop = lds16(buf, W2OFF + pbw(hl) + 16 * nt * 256);
           vacc[0][nt] = mfma16(ha0, bop, vacc[0][nt]);
           vacc[1][nt] = mfma16(ha1, bop, vacc[1][nt]);
         }
@@ -434,8 +446,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
     }
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      vb_hi[nt] = pack8(vacc[0][nt], vacc[1][nt]);
-      vb_lo[nt] = pack8_lo(vacc[0][nt], vacc[1][nt], vb_hi[nt]);
+      vb[nt] = pack8(vacc[0][nt], vacc[1][nt]);
     }
   } else {
     // ========================================================= exact window
@@ -463,8 +474,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
         const int t = min(w0 + 16 * (e >> 2) + 4 * grp + (e & 3), a.window - 1);
         v[e] = __builtin_bit_cast(__bf16, vw[(size_t)t * kHeadDim + 16 * nt + col]);
       }
-      vb_hi[nt] = v;
-      vb_lo[nt] = zero_bf16x8();
+      vb[nt] = v;
     }
   }
 
@@ -498,8 +508,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    o = mfma16(pa, vb_hi[nt], o);
-    o = mfma16(pa, vb_lo[nt], o);
+    o = mfma16(pa, vb[nt], o);
     oacc[nt] = o;
   }
 

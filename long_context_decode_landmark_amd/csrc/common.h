@@ -63,6 +63,17 @@ __device__ __forceinline__ bf16x8 load_bf16x4x2(const uint16_t* p0, const uint16
   return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (reads past the end
+// return 0).  Loads through it take a 32-bit lane offset plus a wave-uniform
+// SGPR offset, so no 64-bit address is kept per load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+}
+
 // Order-preserving map fp32 -> uint32 (larger float -> larger key); -0 == +0.
 __device__ __forceinline__ uint32_t score_key(float s) {
   uint32_t u = __float_as_uint(s);
