@@ -84,9 +84,9 @@ def build_device_cache(cfg, nb, n_layers, seed, dev):
         return t.unsqueeze(0).expand((nb,) + tuple(t.shape)).contiguous()
 
     base = sd.draw_layer(cfg, seed, dev)
-    off = torch.empty((cfg.n_heads_kv, cfg.n_chunks + 1), dtype=torch.int32, device=dev)
-    native.resid_chunk_offsets(base["res_idx"], cfg.n_heads_kv, cfg.n_resid, cfg.n_chunks, cfg.chunk, off)
-    base["res_chunk_off"] = off
+    desc = torch.empty((cfg.n_heads_kv, cfg.n_chunks), dtype=torch.int32, device=dev)
+    native.resid_chunk_desc(base["res_idx"], cfg.n_heads_kv, cfg.n_resid, cfg.n_chunks, cfg.chunk, desc)
+    base["res_chunk_desc"] = desc
     coeff = sd.draw_coeff(cfg, seed + 1, dev)
     groups = []
     for _ in range((n_layers + cfg.group_layers - 1) // cfg.group_layers):

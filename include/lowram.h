@@ -102,8 +102,10 @@ typedef struct lowram_layer_cache {
   const int32_t* res_idx;       /* [NB][Hkv][nR] ascending token ids (< P) with a residual    */
   const void* res_val;          /* bf16: [NB][Hkv][nR][d];  int4: [NB][Hkv][nR][d/2] bytes    */
   const uint16_t* res_scale;    /* int4 only: [NB][Hkv][nR][d/32] fp16; NULL for bf16         */
-  const int32_t* res_chunk_off; /* [NB][Hkv][P/S + 1]: res_idx rows of chunk c are
-                                   [off[c], off[c+1]) (see lowram_resid_chunk_offsets)        */
+  const uint32_t* res_chunk_desc; /* [NB][Hkv][P/S] residual descriptor of chunk c: bits
+                                   8..31 = row of res_idx holding the chunk's first residual
+                                   token, bit i (< 8) set iff token c*S + i has a residual
+                                   (see lowram_resid_chunk_desc)                              */
   const uint16_t* win_k;        /* [NB][Hkv][W][d] bf16 post-RoPE keys of the window          */
   const uint16_t* win_v;        /* [NB][Hkv][W][d] bf16 values of the window                  */
 } lowram_layer_cache;
@@ -175,13 +177,14 @@ int dense_decode_step(const dense_shape* shape, const dense_layer_cache* cache,
                       void* stream);
 
 /*
- * Cache-layout helper: chunk_off[l][c] = number of entries of res_idx[l]
- * below c*chunk, c = 0..n_chunks, for n_lists ascending lists of n_resid
- * token ids each (res_idx [n_lists][n_resid], chunk_off [n_lists][n_chunks+1]).
+ * Cache-layout helper: the residual descriptors of n_lists ascending lists of
+ * n_resid token ids each (res_idx [n_lists][n_resid], desc [n_lists][n_chunks]):
+ * desc[l][c] = (number of entries of res_idx[l] below c*chunk) << 8
+ *            | bitmask of the tokens c*chunk + i (i < chunk) present in res_idx[l].
+ * Requires chunk <= 8 and n_resid < 2^24.
  */
-int lowram_resid_chunk_offsets(const int32_t* res_idx, int32_t n_lists, int32_t n_resid,
-                               int32_t n_chunks, int32_t chunk, int32_t* chunk_off,
-                               void* stream);
+int lowram_resid_chunk_desc(const int32_t* res_idx, int32_t n_lists, int32_t n_resid,
+                            int32_t n_chunks, int32_t chunk, uint32_t* desc, void* stream);
 
 #ifdef __cplusplus
 }

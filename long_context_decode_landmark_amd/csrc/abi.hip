@@ -34,6 +34,7 @@ int check_shape(const lowram_shape* s) {
   if (s->prefix_len % s->chunk) return LOWRAM_ERR_SHAPE;
   if (s->prefix_len + s->window < 1) return LOWRAM_ERR_SHAPE;
   if (s->n_resid > s->prefix_len) return LOWRAM_ERR_SHAPE;
+  if (s->n_resid >= (1 << 24)) return LOWRAM_ERR_UNSUPPORTED;  // 24-bit row field of the descriptor
   if (s->coeff_fmt != LOWRAM_FMT_BF16 && s->coeff_fmt != LOWRAM_FMT_INT4_G32) return LOWRAM_ERR_SHAPE;
   if (s->resid_fmt != LOWRAM_FMT_BF16 && s->resid_fmt != LOWRAM_FMT_INT4_G32) return LOWRAM_ERR_SHAPE;
   if (!(s->rope_theta > 0.f) || !std::isfinite(s->rope_theta)) return LOWRAM_ERR_SHAPE;
@@ -79,7 +80,7 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   const bool ci4 = s->coeff_fmt == LOWRAM_FMT_INT4_G32, ri4 = s->resid_fmt == LOWRAM_FMT_INT4_G32;
   if (has_prefix) {
     if (!c->coeff || !c->basis || !c->landmark || !c->w1 || !c->b1 || !c->w2 || !c->b2 ||
-        !c->res_chunk_off)
+        !c->res_chunk_desc)
       return LOWRAM_ERR_NULL;
     if (s->n_resid > 0 && (!c->res_idx || !c->res_val)) return LOWRAM_ERR_NULL;
     if (ci4 && !c->coeff_scale) return LOWRAM_ERR_NULL;
@@ -92,7 +93,7 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   for (const void* ptr : bulk)
     if (ptr && misaligned(ptr, 16)) return LOWRAM_ERR_ALIGN;
   const void* small[] = {c->coeff_scale, c->cand_ids, c->b1, c->b2, c->res_idx, c->res_scale,
-                         c->res_chunk_off, sel_out, scores_out, kpre_out, kpost_out, vhat_out};
+                         c->res_chunk_desc, sel_out, scores_out, kpre_out, kpost_out, vhat_out};
   for (const void* ptr : small)
     if (ptr && misaligned(ptr, 4)) return LOWRAM_ERR_ALIGN;
   if (kpre_out && misaligned(kpre_out, 16)) return LOWRAM_ERR_ALIGN;
@@ -126,7 +127,7 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   a.coeff = c->coeff; a.coeff_scale = c->coeff_scale; a.basis = c->basis;
   a.w1 = c->w1; a.b1 = c->b1; a.w2 = c->w2; a.b2 = c->b2;
   a.res_idx = c->res_idx; a.res_val = c->res_val; a.res_scale = c->res_scale;
-  a.res_off = c->res_chunk_off; a.win_k = c->win_k; a.win_v = c->win_v;
+  a.res_desc = c->res_chunk_desc; a.win_k = c->win_k; a.win_v = c->win_v;
   a.q = q; a.sel = sel; a.part = part;
   a.kpre_out = kpre_out; a.kpost_out = kpost_out; a.vhat_out = vhat_out;
   a.nb = s->batch; a.hq = s->n_heads_q; a.hkv = s->n_heads_kv; a.g = p.g;
@@ -245,14 +246,15 @@ int dense_decode_step(const dense_shape* shape, const dense_layer_cache* cache, 
   return LOWRAM_OK;
 }
 
-int lowram_resid_chunk_offsets(const int32_t* res_idx, int32_t n_lists, int32_t n_resid,
-                               int32_t n_chunks, int32_t chunk, int32_t* chunk_off, void* stream) {
-  if (!chunk_off || (n_resid > 0 && !res_idx)) return LOWRAM_ERR_NULL;
+int lowram_resid_chunk_desc(const int32_t* res_idx, int32_t n_lists, int32_t n_resid,
+                            int32_t n_chunks, int32_t chunk, uint32_t* desc, void* stream) {
+  if (!desc || (n_resid > 0 && !res_idx)) return LOWRAM_ERR_NULL;
   if (n_lists < 0 || n_resid < 0 || n_chunks < 0 || chunk < 1) return LOWRAM_ERR_SHAPE;
-  if (misaligned(chunk_off, 4) || (res_idx && misaligned(res_idx, 4))) return LOWRAM_ERR_ALIGN;
-  if (n_lists == 0) return LOWRAM_OK;
-  if (launch_chunk_offsets(res_idx, n_lists, n_resid, n_chunks, chunk, chunk_off,
-                           static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (chunk > 8 || n_resid >= (1 << 24)) return LOWRAM_ERR_UNSUPPORTED;
+  if (misaligned(desc, 4) || (res_idx && misaligned(res_idx, 4))) return LOWRAM_ERR_ALIGN;
+  if (n_lists == 0 || n_chunks == 0) return LOWRAM_OK;
+  if (launch_chunk_desc(res_idx, n_lists, n_resid, n_chunks, chunk, desc,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
     return LOWRAM_ERR_HIP;
   return LOWRAM_OK;
 }

@@ -221,17 +221,10 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
       }
     };
     gather_half(0);
-    // ---- residual lookup of token `lane` (< 32): its row in res_idx or -1
-    int rn = -1;
-    if (lane < nvalid) {
-      const int cid = chunk_of(4 * wave + (lane >> 3));
-      const int token = cid * kChunk + (lane & 7);
-      const int32_t* off = a.res_off + head * (size_t)(a.n_chunks + 1);
-      const int32_t* ridx = a.res_idx + head * (size_t)a.n_resid;
-      const int o1 = min(off[cid + 1], a.n_resid);
-      for (int i = max(off[cid], 0); i < o1; ++i)
-        if (ridx[i] == token) rn = i;
-    }
+    // ---- residual descriptor of token `lane` (< 32)'s chunk: one load,
+    //      consumed only after the MLP
+    uint32_t rdesc = 0;
+    if (lane < nvalid) rdesc = a.res_desc[head * (size_t)a.n_chunks + chunk_of(4 * wave + (lane >> 3))];
 
     const __amdgpu_buffer_rsrc_t basis = buffer_rsrc(a.basis + head * (size_t)kHeadDim * RANK, kHeadDim * RANK * 2);
     stage_plain<kHeadDim, NPB, RANK>(buf, basis, 0, tid);
@@ -410,7 +403,16 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
       }
     }
 
-    // ---- residual scatter-add (rows found at the start)
+    // ---- residual scatter-add: token `lane` has a stored row iff its bit is
+    //      set; the row is the chunk's first row plus the set bits below it
+    int rn = -1;
+    {
+      const int i = lane & 7;
+      if ((rdesc >> i) & 1u) {
+        rn = (int)(rdesc >> 8) + __popc(rdesc & ((1u << i) - 1u) & 0xFFu);
+        rn = min(rn, a.n_resid - 1);
+      }
+    }
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll

@@ -1,6 +1,6 @@
 // Dense GQA flash-decode over the full bf16 KV cache (the uncompressed
 // baseline of the LowRAM review's results paragraph), gfx950, and the
-// residual chunk-offset helper of the compressed cache layout.
+// residual chunk-descriptor helper of the compressed cache layout.
 //
 // One workgroup = 8 waves covers a split of the context; each wave walks
 // 32-token blocks with an online softmax.  QK on MFMA (K rows straight from
@@ -142,13 +142,14 @@ hipError_t launch_dense(const uint16_t* k, const uint16_t* v, const uint16_t* q,
   return hipGetLastError();
 }
 
-// chunk_off[l][c] = lower bound of c*chunk in the ascending list res_idx[l]
-__global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t* __restrict__ idx,
-                                                            int n_resid, int n_chunks, int chunk,
-                                                            int32_t* __restrict__ off) {
+// desc[l][c] = (lower bound of c*chunk in res_idx[l]) << 8 | bitmask of the
+// chunk's tokens present in res_idx[l]
+__global__ __launch_bounds__(256) void chunk_desc_kernel(const int32_t* __restrict__ idx, int n_resid,
+                                                         int n_chunks, int chunk,
+                                                         uint32_t* __restrict__ desc) {
   const int l = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c > n_chunks) return;
+  if (c >= n_chunks) return;
   const int32_t* r = idx + (size_t)l * n_resid;
   const int key = c * chunk;
   int lo = 0, hi = n_resid;
@@ -157,14 +158,15 @@ __global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t* __res
     if (r[mid] < key) lo = mid + 1;
     else hi = mid;
   }
-  off[(size_t)l * (n_chunks + 1) + c] = lo;
+  uint32_t mask = 0;
+  for (int i = lo; i < n_resid && r[i] < key + chunk; ++i) mask |= 1u << (r[i] - key);
+  desc[(size_t)l * n_chunks + c] = ((uint32_t)lo << 8) | mask;
 }
 
-hipError_t launch_chunk_offsets(const int32_t* res_idx, int n_lists, int n_resid, int n_chunks,
-                                int chunk, int32_t* off, hipStream_t st) {
-  const dim3 grid((n_chunks + 1 + 255) / 256, n_lists);
-  hipLaunchKernelGGL(chunk_offsets_kernel, grid, dim3(256), 0, st, res_idx, n_resid, n_chunks,
-                     chunk, off);
+hipError_t launch_chunk_desc(const int32_t* res_idx, int n_lists, int n_resid, int n_chunks, int chunk,
+                             uint32_t* desc, hipStream_t st) {
+  const dim3 grid((n_chunks + 255) / 256, n_lists);
+  hipLaunchKernelGGL(chunk_desc_kernel, grid, dim3(256), 0, st, res_idx, n_resid, n_chunks, chunk, desc);
   return hipGetLastError();
 }
 

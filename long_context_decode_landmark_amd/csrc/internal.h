@@ -25,7 +25,7 @@ struct AttendArgs {
   const int32_t* res_idx;
   const void* res_val;
   const uint16_t* res_scale;
-  const int32_t* res_off;
+  const uint32_t* res_desc;
   const uint16_t* win_k;
   const uint16_t* win_v;
   const uint16_t* q;
@@ -51,7 +51,7 @@ hipError_t launch_merge(const float* part, uint16_t* out, int nb, int hkv, int g
 hipError_t launch_dense(const uint16_t* k, const uint16_t* v, const uint16_t* q, float* part,
                         int nb, int ctx, int hq, int hkv, int n_split, int tok_per_split,
                         float scale_log2, hipStream_t st);
-hipError_t launch_chunk_offsets(const int32_t* res_idx, int n_lists, int n_resid, int n_chunks,
-                                int chunk, int32_t* off, hipStream_t st);
+hipError_t launch_chunk_desc(const int32_t* res_idx, int n_lists, int n_resid, int n_chunks,
+                             int chunk, uint32_t* desc, hipStream_t st);
 
 }  // namespace lowram

@@ -42,8 +42,9 @@ __global__ __launch_bounds__(256) void score_kernel(
   const int c_begin = blockIdx.x * chunks_per_wg;
   const int c_end = min(n_cand, c_begin + chunks_per_wg);
 
-  for (int c0 = c_begin + wave * 64; c0 < c_end; c0 += 256) {
-    bf16x8 lv[4][4];
+  // software pipeline: the next 64 landmarks of this wave are in flight
+  // while the current 64 are multiplied
+  auto load_group = [&](int c0, bf16x8 (&lv)[4][4]) {
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
       const int cc = min(c0 + 16 * gi + col, n_cand - 1);
@@ -51,11 +52,17 @@ __global__ __launch_bounds__(256) void score_kernel(
       for (int ks = 0; ks < 4; ++ks)
         lv[gi][ks] = load_bf16x8(lm + (size_t)cc * kHeadDim + 32 * ks + 8 * grp);
     }
+  };
+  bf16x8 cur[4][4], nxt[4][4];
+  int c0 = c_begin + wave * 64;
+  if (c0 < c_end) load_group(c0, cur);
+  for (; c0 < c_end; c0 += 256) {
+    if (c0 + 256 < c_end) load_group(c0 + 256, nxt);
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma16(qa[ks], lv[gi][ks], acc);
+      for (int ks = 0; ks < 4; ++ks) acc = mfma16(qa[ks], cur[gi][ks], acc);
       float s = -__builtin_huge_valf();
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -68,40 +75,64 @@ __global__ __launch_bounds__(256) void score_kernel(
         if (sout) sout[c] = s;
       }
     }
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) cur[gi][ks] = nxt[gi][ks];
   }
 }
 
 // ---------------------------------------------------------------------------
-// Exact top-k by radix select on the order-preserving keys: four 8-bit
-// passes find the k-th largest key T and how many keys equal to T are still
-// needed; a final ordered compaction keeps every key > T and the first
-// `need` keys == T in candidate order.  Candidates are in ascending chunk
-// order, so the output is ascending.  One workgroup per (sequence, KV head);
-// keys are read from L2 (the whole score vector of a head is <= 128 KiB).
+// Exact top-k by radix select on the order-preserving keys.  Three passes on
+// the key bits [31:20], [19:8], [7:0] find the k-th largest key T and how many
+// keys equal to T are still needed; an ordered compaction then keeps every
+// key > T and the first `need` keys == T in candidate order.  Candidates are
+// in ascending chunk order, so the output is ascending.  One workgroup of
+// 1024 threads per (sequence, KV head).  The keys of the head are staged in
+// LDS once (up to kSelLdsKeys of them; longer lists are re-read from L2 in
+// every pass).  12-bit first digits spread the fp32 exponent over 4096 bins
+// so few lanes of an LDS atomic hit the same bin; the digit search and the
+// compaction offsets use wave-shuffle scans with one LDS exchange.
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelBins = 4096;
+constexpr int kSelLdsKeys = 32768;
 
+struct SelLds {  // the key array comes last: the L2-reading variant omits it
+  uint32_t hist[kSelBins];
+  uint32_t wsum[2][kSelWaves];
+  uint32_t found[2];
+  uint32_t keys[kSelLdsKeys];
+};
+
+// inclusive scan of x over the 64 lanes of a wave, from the highest lane down
+__device__ __forceinline__ uint32_t wave_scan_down(uint32_t x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_down(x, o);
+    if (lane + o < 64) x += y;
+  }
+  return x;
+}
+
+template <bool kLds>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint32_t* __restrict__ keys, const int32_t* __restrict__ cand_ids,
     int32_t* __restrict__ sel, int32_t* __restrict__ sel_out, int n_cand, int k, int n_heads_kv) {
+  extern __shared__ unsigned char sel_smem[];
+  SelLds& S = *reinterpret_cast<SelLds*>(sel_smem);
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t head = (size_t)b * n_heads_kv + h;
-  const uint32_t* kv = keys + head * (size_t)n_cand;
+  const uint32_t* kg = keys + head * (size_t)n_cand;
   const int32_t* ids = cand_ids ? cand_ids + head * (size_t)n_cand : nullptr;
   const int k_eff = min(k, n_cand);
   int32_t* so = sel + head * (size_t)k_eff;
   int32_t* so2 = sel_out ? sel_out + head * (size_t)k : nullptr;
 
-  __shared__ uint32_t hist[kSelWaves][256];
-  __shared__ uint32_t suffix[257];
-  __shared__ uint32_t found[2];
-  __shared__ uint32_t scan_gt[kSelThreads], scan_eq[kSelThreads];
-
   if (so2)
     for (int i = k_eff + tid; i < k; i += kSelThreads) so2[i] = -1;
-
   if (n_cand <= k) {  // every candidate is selected
     for (int i = tid; i < n_cand; i += kSelThreads) {
       const int32_t c = ids ? ids[i] : i;
@@ -110,80 +141,96 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
     return;
   }
+  if constexpr (kLds) {
+    for (int i = tid; i < n_cand; i += kSelThreads) S.keys[i] = kg[i];
+  }
+  const uint32_t* kv = kLds ? S.keys : kg;
 
   uint32_t prefix = 0, pmask = 0, kk = (uint32_t)k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0;
+  constexpr int kShift[3] = {20, 8, 0};
+  constexpr int kBits[3] = {12, 12, 8};
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = kShift[pass], nbins = 1 << kBits[pass];
+    const uint32_t dmask = (uint32_t)nbins - 1;
+    for (int i = tid; i < nbins; i += kSelThreads) S.hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < n_cand; i += kSelThreads) {
       const uint32_t key = kv[i];
-      if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
+      if ((key & pmask) == prefix) atomicAdd(&S.hist[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
-    if (tid < 256) {
-      uint32_t s = 0;
-#pragma unroll
-      for (int w = 0; w < kSelWaves; ++w) s += hist[w][tid];
-      suffix[tid] = s;
-    }
-    if (tid == 256) suffix[256] = 0;
+    // thread t owns bins [bpt*t, bpt*t + bpt); the digit D is the bin where
+    // the count of keys in higher bins first reaches kk
+    const int bpt = nbins >= kSelThreads ? nbins / kSelThreads : 1;
+    const bool owner = tid * bpt < nbins;
+    uint32_t mine = 0;
+    if (owner)
+      for (int j = 0; j < bpt; ++j) mine += S.hist[tid * bpt + j];
+    const uint32_t incl = wave_scan_down(mine, lane);  // this lane and above, in the wave
+    if (lane == 0) S.wsum[0][wave] = incl;
     __syncthreads();
-    // inclusive suffix sums over the 256 digit counts (Hillis-Steele)
-    for (int off = 1; off < 256; off <<= 1) {
-      uint32_t v = 0;
-      if (tid < 256 && tid + off < 256) v = suffix[tid + off];
-      __syncthreads();
-      if (tid < 256) suffix[tid] += v;
-      __syncthreads();
-    }
-    if (tid < 256) {
-      const uint32_t above = suffix[tid + 1], incl = suffix[tid];
-      if (above < kk && kk <= incl) { found[0] = tid; found[1] = above; }
+    uint32_t above = incl - mine;
+    for (int w = wave + 1; w < kSelWaves; ++w) above += S.wsum[0][w];
+    if (owner) {
+      for (int j = bpt - 1; j >= 0; --j) {
+        const uint32_t c = S.hist[tid * bpt + j];
+        if (above < kk && kk <= above + c) {
+          S.found[0] = tid * bpt + j;
+          S.found[1] = above;
+        }
+        above += c;
+      }
     }
     __syncthreads();
-    const uint32_t digit = found[0], above = found[1];
-    kk -= above;
+    const uint32_t digit = S.found[0];
+    kk -= S.found[1];
     prefix |= digit << shift;
-    pmask |= 0xFFu << shift;
-    __syncthreads();
+    pmask |= dmask << shift;
+    __syncthreads();  // hist is cleared by the next pass
   }
   const uint32_t T = prefix, need = kk;
 
-  // ordered compaction: thread tid owns candidates [tid*per, tid*per + per)
-  const int per = (n_cand + kSelThreads - 1) / kSelThreads;
-  const int i0 = min(n_cand, tid * per), i1 = min(n_cand, i0 + per);
+  // ordered compaction: wave w owns candidates [w*per, w*per + per) and walks
+  // them 64 at a time (lane-strided, conflict-free LDS reads); ballots give
+  // each key its rank among the wave's earlier > T / == T keys.
+  const int per = (n_cand + kSelWaves - 1) / kSelWaves;
+  const int w0 = min(n_cand, wave * per), w1 = min(n_cand, w0 + per);
+  const uint64_t below = (1ull << lane) - 1;  // lanes under this one
   uint32_t ngt = 0, neq = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = kv[i];
-    ngt += key > T;
-    neq += key == T;
+  for (int i = w0 + lane; i < w1 + 63; i += 64) {
+    const uint32_t key = i < w1 ? kv[i] : 0u;
+    ngt += __popcll(__ballot(i < w1 && key > T));
+    neq += __popcll(__ballot(i < w1 && key == T));
   }
-  scan_gt[tid] = ngt;
-  scan_eq[tid] = neq;
+  if (lane == 0) {
+    S.wsum[0][wave] = ngt;
+    S.wsum[1][wave] = neq;
+  }
   __syncthreads();
-  for (int off = 1; off < kSelThreads; off <<= 1) {
-    uint32_t a = 0, c = 0;
-    if (tid >= off) { a = scan_gt[tid - off]; c = scan_eq[tid - off]; }
-    __syncthreads();
-    scan_gt[tid] += a;
-    scan_eq[tid] += c;
-    __syncthreads();
+  uint32_t gt_run = 0, eq_run = 0;
+  for (int w = 0; w < wave; ++w) {
+    gt_run += S.wsum[0][w];
+    eq_run += S.wsum[1][w];
   }
-  uint32_t eq_before = scan_eq[tid] - neq;
-  uint32_t pos = (scan_gt[tid] - ngt) + min(eq_before, need);
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = kv[i];
-    bool take = key > T;
-    if (key == T) { take = eq_before < need; ++eq_before; }
-    if (take && pos < (uint32_t)k_eff) {
-      const int32_t c = ids ? ids[i] : i;
-      so[pos] = c;
-      if (so2) so2[pos] = c;
-      ++pos;
+  for (int i = w0 + lane; i < w1 + 63; i += 64) {
+    const bool in = i < w1;
+    const uint32_t key = in ? kv[i] : 0u;
+    const bool gt = in && key > T, eq = in && key == T;
+    const uint64_t mg = __ballot(gt), me = __ballot(eq);
+    const uint32_t gt_before = gt_run + __popcll(mg & below);
+    const uint32_t eq_before = eq_run + __popcll(me & below);
+    if (gt || (eq && eq_before < need)) {
+      const uint32_t pos = gt_before + min(eq_before, need);
+      if (pos < (uint32_t)k_eff) {
+        const int32_t c = ids ? ids[i] : i;
+        so[pos] = c;
+        if (so2) so2[pos] = c;
+      }
     }
+    gt_run += __popcll(mg);
+    eq_run += __popcll(me);
   }
-  (void)lane;
 }
 
 hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* keys,
@@ -202,8 +249,21 @@ hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* k
 hipError_t launch_select(const uint32_t* keys, const int32_t* cand_ids, int32_t* sel,
                          int32_t* sel_out, int nb, int n_cand, int k, int hkv, hipStream_t st) {
   if (n_cand <= 0 && !sel_out) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3(hkv, nb), dim3(kSelThreads), 0, st, keys, cand_ids, sel,
-                     sel_out, n_cand, k, hkv);
+  const dim3 grid(hkv, nb), block(kSelThreads);
+  static bool attr_set = false;  // dynamic LDS above 64 KiB must be allowed once
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(select_kernel<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SelLds)) != hipSuccess)
+      return hipErrorInvalidValue;
+    attr_set = true;
+  }
+  if (n_cand <= kSelLdsKeys) {
+    hipLaunchKernelGGL(select_kernel<true>, grid, block, sizeof(SelLds), st, keys, cand_ids, sel, sel_out,
+                       n_cand, k, hkv);
+  } else {
+    hipLaunchKernelGGL(select_kernel<false>, grid, block, sizeof(SelLds) - kSelLdsKeys * 4, st, keys,
+                       cand_ids, sel, sel_out, n_cand, k, hkv);
+  }
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ SYMBOLS = (
     "lowram_decode_step_events",
     "dense_workspace_bytes",
     "dense_decode_step",
-    "lowram_resid_chunk_offsets",
+    "lowram_resid_chunk_desc",
 )
 
 ERRORS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "UNSUPPORTED", -4: "WORKSPACE", -5: "ALIGN", -6: "HIP"}
@@ -40,7 +40,7 @@ class LowramShape(ctypes.Structure):
 
 
 CACHE_FIELDS = ("coeff", "coeff_scale", "basis", "landmark", "cand_ids", "w1", "b1", "w2", "b2",
-                "res_idx", "res_val", "res_scale", "res_chunk_off", "win_k", "win_v")
+                "res_idx", "res_val", "res_scale", "res_chunk_desc", "win_k", "win_v")
 
 
 class LowramLayerCache(ctypes.Structure):
@@ -87,7 +87,7 @@ def lib() -> ctypes.CDLL:
         L.dense_workspace_bytes.argtypes = [ctypes.POINTER(DenseShape), ctypes.POINTER(sz)]
         L.dense_decode_step.argtypes = [ctypes.POINTER(DenseShape), ctypes.POINTER(DenseLayerCache),
                                         vp, vp, vp, sz, vp]
-        L.lowram_resid_chunk_offsets.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        L.lowram_resid_chunk_desc.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.c_int32, vp, vp]
         for name in SYMBOLS:
             getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
@@ -194,8 +194,8 @@ def dense_decode_step(shape, k, v, q, out, workspace, stream=None) -> None:
            "dense_decode_step")
 
 
-def resid_chunk_offsets(res_idx, n_lists: int, n_resid: int, n_chunks: int, chunk: int, out,
-                        stream=None) -> None:
-    """res_idx [n_lists][n_resid] int32 (ascending rows) -> out [n_lists][n_chunks+1] int32."""
-    _check(lib().lowram_resid_chunk_offsets(_ptr(res_idx), n_lists, n_resid, n_chunks, chunk, _ptr(out),
-                                            _stream(stream)), "lowram_resid_chunk_offsets")
+def resid_chunk_desc(res_idx, n_lists: int, n_resid: int, n_chunks: int, chunk: int, out,
+                     stream=None) -> None:
+    """res_idx [n_lists][n_resid] int32 (ascending rows) -> out [n_lists][n_chunks] uint32 (int32 tensor)."""
+    _check(lib().lowram_resid_chunk_desc(_ptr(res_idx), n_lists, n_resid, n_chunks, chunk, _ptr(out),
+                                         _stream(stream)), "lowram_resid_chunk_desc")

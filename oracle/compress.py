@@ -61,10 +61,18 @@ def residual_select(v_prefix: np.ndarray, k_pre_prefix: np.ndarray, w1, b1, w2, 
     return idx.astype(np.int32), r[idx]
 
 
-def chunk_offsets(idx: np.ndarray, n_chunks: int, chunk: int) -> np.ndarray:
-    """off[c] = number of residual tokens below c * S, c = 0..nC (CSR over chunks)."""
-    bounds = np.arange(n_chunks + 1, dtype=np.int64) * chunk
-    return np.searchsorted(np.asarray(idx, np.int64), bounds, side="left").astype(np.int32)
+def chunk_descriptors(idx: np.ndarray, n_chunks: int, chunk: int) -> np.ndarray:
+    """Residual descriptor per chunk (cache layout, no method arithmetic).
+
+    desc[c] = (number of residual tokens below c*S) << 8 | bitmask of the
+    chunk's tokens c*S + i that have a residual (S <= 8).
+    """
+    idx = np.asarray(idx, np.int64)
+    bounds = np.arange(n_chunks, dtype=np.int64) * chunk
+    first = np.searchsorted(idx, bounds, side="left")
+    mask = np.zeros(n_chunks, dtype=np.uint64)
+    np.bitwise_or.at(mask, idx // chunk, np.left_shift(np.uint64(1), (idx % chunk).astype(np.uint64)))
+    return ((first.astype(np.uint64) << np.uint64(8)) | mask).astype(np.uint32)
 
 
 def _store(x, exact: bool):
@@ -95,7 +103,7 @@ def compress_head(cfg, x_head: np.ndarray, coeff_stored, blk_stored, mlp, noise,
     out = dict(
         landmark=_store(landmarks(x_head, P, S, cfg.rope_theta), exact),
         res_idx=idx,
-        res_chunk_off=chunk_offsets(idx, cfg.n_chunks, S),
+        res_chunk_desc=chunk_descriptors(idx, cfg.n_chunks, S),
         win_k=_store(rope(x_head[P:], np.arange(P, P + W), cfg.rope_theta), exact),
         win_v=_store(v[P:], exact),
     )

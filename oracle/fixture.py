@@ -11,7 +11,7 @@ Arrays come out in the layout the GPU library takes, batch major:
   w1 [NB][Hkv][H][d], b1 [NB][Hkv][H], w2 [NB][Hkv][d][H], b2 [NB][Hkv][d] bf16
   res_idx      [NB][Hkv][nR] int32 ascending
   res_val      [NB][Hkv][nR][d] bf16, or [..][nR][d/2] int4 + res_scale [..][nR][d/32]
-  res_chunk_off [NB][Hkv][nC+1] int32
+  res_chunk_desc [NB][Hkv][nC] uint32 (first residual row << 8 | token bitmask)
   win_k, win_v [NB][Hkv][W][d] bf16
   q            [NB][Hq][d] bf16
 """
@@ -86,7 +86,7 @@ def build_layer(cfg, layer: int, batch=None, exact: bool = False):
     else:
         cache["coeff"] = np.stack([p[0] for p in per_b])
     keys = ["basis", "landmark", "w1", "b1", "w2", "b2", "res_idx", "res_val",
-            "res_chunk_off", "win_k", "win_v"]
+            "res_chunk_desc", "win_k", "win_v"]
     if cfg.int4 and not exact:
         keys.append("res_scale")
     if cfg.evict:

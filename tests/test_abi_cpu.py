@@ -104,7 +104,7 @@ def call_step(s, cache, q=FakeTensor(0x7000000000), out=FakeTensor(0x7100000000)
 
 def test_step_rejects_null_pointers():
     s = shape()
-    for n in ("coeff", "basis", "landmark", "w1", "res_chunk_off", "win_k", "win_v"):
+    for n in ("coeff", "basis", "landmark", "w1", "res_chunk_desc", "win_k", "win_v"):
         c = fake_cache()
         c[n] = None
         assert call_step(s, c) == -1, n
@@ -146,7 +146,10 @@ def test_dense_rejects():
     assert e.value.status == -4
 
 
-def test_chunk_offsets_rejects():
+def test_chunk_desc_rejects():
     with pytest.raises(native.LowramError) as e:
-        native.resid_chunk_offsets(FakeTensor(0x1002), 4, 16, 10, 8, FakeTensor(0x2000), stream=0)
-    assert e.value.status in (-5,)
+        native.resid_chunk_desc(FakeTensor(0x1002), 4, 16, 10, 8, FakeTensor(0x2000), stream=0)
+    assert e.value.status == -5
+    with pytest.raises(native.LowramError) as e:
+        native.resid_chunk_desc(FakeTensor(0x1000), 4, 16, 10, 16, FakeTensor(0x2000), stream=0)
+    assert e.value.status == -3

@@ -225,8 +225,11 @@ def test_residual_select_brute_force_and_offsets():
     errs = [float(np.linalg.norm(v[t] - steps.value_mlp(kp[t:t + 1], *w)[0])) for t in range(40)]
     brute = sorted(sorted(range(40), key=lambda t: (-errs[t], t))[:5])
     assert list(idx) == brute and 3 in idx and 17 in idx
-    off = compress.chunk_offsets(idx, 5, 8)
-    assert [sum(1 for t in idx if t < 8 * c) for c in range(6)] == list(off)
+    desc = compress.chunk_descriptors(idx, 5, 8)
+    for c in range(5):
+        first = sum(1 for t in idx if t < 8 * c)
+        bits = sum(1 << (t - 8 * c) for t in idx if 8 * c <= t < 8 * c + 8)
+        assert int(desc[c]) == (first << 8) | bits
 
 
 # ------------------------------------------------ whole-step invariants --
