@@ -41,7 +41,55 @@ def parse():
     ap.add_argument("--cpu-slices", type=int, default=10)
     ap.add_argument("--graph", action="store_true", help="also time a hipGraph replay of the step")
     ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first copy a buffer of this size 3 times (HBM counter calibration)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c3_262k_b28_hbm_traffic.txt")
+KERNEL_SOURCES = {
+    "attend": ("attend.hip", "common.h", "internal.h"),
+    "score": ("score_select.hip", "common.h", "internal.h"),
+    "select": ("score_select.hip", "common.h", "internal.h"),
+    "merge": ("attend.hip", "common.h", "internal.h"),
+}
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "long_context_decode_landmark_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload, nb):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size), or None when
+    the summary is for another workload or the kernel's sources changed since."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        f = ln.split()
+        if len(f) == 6 and f[0] == "traffic" and f[1] == kernel and f[2] == workload and int(f[3]) == nb:
+            return float(f[5]) if f[4] == source_hash(kernel) else None
+    return None
+
+
+def copy_probe(mib):
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    print(f"copy probe: 3 copies of {n} bytes", file=sys.stderr)
 
 
 def algorithmic(cfg, nb):
@@ -265,6 +313,8 @@ def main():
     nb = args.batch or cfg.batch
     n_layers = args.layers or cfg.n_layers
 
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
     step_ms, kern, graph_ms, host, q0 = time_lowram(cfg, nb, n_layers, args.steps, args.warmup, args.seed,
                                                     args.graph)
     byts, flops = algorithmic(cfg, nb)
@@ -302,7 +352,7 @@ def main():
                    "window": cfg.window, "rank": cfg.rank, "resid_frac": cfg.resid_frac,
                    "int4": cfg.int4, "evict": cfg.evict},
         "roofline": {"bound": bound, "kernel": dom, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-                     "frac": round(ach / peak, 4), "traffic": None},
+                     "frac": round(ach / peak, 4), "traffic": measured_traffic(dom, cfg.name, nb)},
         "step_roofline": {"alg_bytes_GB": round(step_bytes / 1e9, 3), "alg_TFLOP": round(step_flops / 1e12, 3),
                           "t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof / (step_ms * 1e-3), 4),
                           "hbm_GB/s": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
