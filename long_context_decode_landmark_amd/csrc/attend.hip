@@ -18,18 +18,28 @@
 // Layout of the work.  A workgroup is 4 waves; each wave owns 32 tokens
 // (4 chunks) and runs every stage on them with v_mfma_f32_16x16x32_bf16.
 // Tokens are the MFMA N dimension throughout, so each stage's accumulator
-// layout is the next stage's operand layout (up to a fixed permutation of
-// the contraction index, applied to the other operand instead):
+// is the next stage's operand without any data movement:
 //   recon   D[d][t]  = basis^T[d][r] (LDS)   x C[t][r] (global -> VGPR)
 //   RoPE    lane-local: pair (i, i+64) sits in m-tiles mt and mt+4
 //   QK      D[t][j]  = K_post[t][d] (VGPR, bf16)  x q[j][d]
 //   MLP1    D[h][t]  = W1[h][d] (LDS)        x K_pre[t][d] (VGPR)
 //   MLP2    D[t][d]  = hid[t][h] (VGPR)      x W2[d][h] (LDS)
 //   PV      D[j][d]  = p[j][t] (VGPR)        x V[t][d] (VGPR, bf16)
-// The operands shared by the 4 waves pass through one 64 KiB LDS buffer in
-// four stages (basis r < 256, basis r >= 256, W1, W2), so a workgroup needs
-// under 80 KiB and two workgroups share a CU: one stages or waits on the
-// coefficient gather while the other runs MFMA.
+// An accumulator tile holds rows 4*(lane/16) + e (e < 4) of each 16-row
+// m-tile, while the next product's operand wants 8 consecutive k per lane.
+// Staging the basis (and W1) rows in the order pi(16 m + 4 g + e) =
+// 32 (m / 2) + 8 g + 4 (m % 2) + e makes the two m-tiles 2s and 2s + 1 of
+// a lane hold exactly k = 32 s + 8 g .. 32 s + 8 g + 7, in natural order.
+//
+// Pipeline.  The shared operands (basis in r-slices of 64, then W1/W2 in
+// slices of 32 hidden units) stream through two 16 KiB LDS buffers, one
+// stage per step, 16 steps at rank 512.  Every load is an ordinary vector
+// load: a stage is loaded into registers two steps before it is needed and
+// written to LDS at the end of the previous step, and each wave's
+// coefficient gather runs three steps ahead.  Loads are issued in the order
+// they are consumed, so the in-order vmcnt waits never hold a step on data
+// it does not need.  The selected tokens' residual rows go to LDS as one
+// dense tile (zero rows where a token has none) after the last stage.
 #include "common.h"
 #include "internal.h"
 
@@ -68,69 +78,18 @@ __device__ __forceinline__ float2 rot_of(double angle) {
   return make_float2(c, s);
 }
 
-constexpr int kBuf = 65536;  // bytes of the staged operand buffer
+constexpr int kStage = 16384;  // bytes of one staged operand slice
+constexpr int kStageLd = 4;    // 16-byte loads per thread per stage (256 threads)
 
 struct AttLds {
-  alignas(16) unsigned char buf[kBuf];
+  alignas(16) unsigned char buf[2][kStage];  // stage ring; residual tile; wave merge
   float2 rope_off[kChunk][64];
   float2 rope_base[kAttChunksWG][64];
   float b1f[kHidden];
   float b2f[kHeadDim];
+  float ml[2 * kAttWaves * 16];
+  uint32_t rdesc[kAttChunksWG];
 };
-
-// Staged matrices keep dense rows of NP 16-byte pieces; piece p of row r
-// sits at p ^ (r & mask) with mask = 15 (7 for 8-piece rows), so the 16
-// rows one MFMA operand read touches fall on different LDS banks.
-template <int NP>
-__device__ __forceinline__ constexpr int swz(int row, int piece) {
-  return piece ^ (row & (NP >= 16 ? 15 : 7));
-}
-
-// Column permutation of W1 (over d) and W2 (over h) inside each block of 32:
-// the MFMA slot 8*G + e of a k-step holds index 4*G + e (e < 4) or
-// 16 + 4*G + (e - 4) (e >= 4), which is how the previous stage's accumulator
-// rows sit in the lane.  Source 4-element group og -> slot group:
-__device__ __forceinline__ constexpr int perm_group(int og) { return og < 4 ? 2 * og : 2 * (og - 4) + 1; }
-
-// Stage columns [c0, c0 + 8*NP) of the matrix behind `src` (row stride LD
-// elements) into dst (ROWS rows of NP pieces).  Thread t copies piece t % NP
-// of rows t / NP + u * (256 / NP): a buffer load (one lane offset, the pass
-// as SGPR offset) and an LDS store at a lane base plus an immediate.
-template <int ROWS, int NP, int LD>
-__device__ __forceinline__ void stage_plain(unsigned char* dst, __amdgpu_buffer_rsrc_t src, int c0, int tid) {
-  constexpr int RSTEP = kAttWaves * 64 / NP;
-  const int r0 = tid / NP, p = tid % NP;
-  const uint32_t goff = (uint32_t)(r0 * LD + c0 + 8 * p) * 2;
-#pragma unroll
-  for (int u = 0; u < ROWS / RSTEP; ++u) {
-    const int r = r0 + u * RSTEP;
-    const u32x4 v = buffer_ld16(src, goff, u * RSTEP * LD * 2);
-    *reinterpret_cast<u32x4*>(dst + (r * NP + swz<NP>(r, p)) * 16) = v;
-  }
-}
-
-// As stage_plain for 16-piece rows, with the 4-element group permutation
-// inside every 32-column block (W1 over d, W2 over h).
-template <int ROWS, int LD>
-__device__ __forceinline__ void stage_perm16(unsigned char* dst, __amdgpu_buffer_rsrc_t src, int c0, int tid) {
-  constexpr int NP = 16, RSTEP = kAttWaves * 64 / NP;  // 16 rows per pass keep r & 15
-  const int r0 = tid / NP, p = tid % NP;
-  const int blk = p >> 2, og0 = (p & 3) * 2;
-  const int sg0 = perm_group(og0), sg1 = perm_group(og0 + 1);
-  const int o0 = (r0 * NP + ((4 * blk + (sg0 >> 1)) ^ r0)) * 16 + 8 * (sg0 & 1);
-  const int o1 = (r0 * NP + ((4 * blk + (sg1 >> 1)) ^ r0)) * 16 + 8 * (sg1 & 1);
-  const uint32_t goff = (uint32_t)(r0 * LD + c0 + 8 * p) * 2;
-#pragma unroll
-  for (int u = 0; u < ROWS / RSTEP; ++u) {
-    const u32x4 v = buffer_ld16(src, goff, u * RSTEP * LD * 2);
-    *reinterpret_cast<u32x2*>(dst + o0 + u * RSTEP * NP * 16) = u32x2{v[0], v[1]};
-    *reinterpret_cast<u32x2*>(dst + o1 + u * RSTEP * NP * 16) = u32x2{v[2], v[3]};
-  }
-}
-
-__device__ __forceinline__ bf16x8 lds16(const unsigned char* base, int off) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + off));
-}
 
 // int4 x 8 (one 32-bit word, element e in bits 4e..4e+3) times scale -> bf16x8
 __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float scale) {
@@ -143,16 +102,23 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float scale) {
   return r;
 }
 
+__device__ __forceinline__ bf16x8 lds16(const unsigned char* base, int off) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + off));
+}
+
+// Row order of a staged 32-row block: position 16 m + 4 g + e holds row
+// 8 g + 4 m + e (m < 2), see the file comment.
+__device__ __forceinline__ constexpr int row_perm32(int pos) {
+  return 8 * ((pos >> 2) & 3) + 4 * (pos >> 4) + (pos & 3);
+}
+
 template <int RANK, bool CI4, bool RI4>
 __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendArgs a) {
   __shared__ AttLds L;
-  constexpr int NKS = RANK / 32;         // k-steps of the reconstruction
-  constexpr int NKB = RANK / 128;        // int4 k-blocks (4 k-steps, 16 B per lane)
-  constexpr int RB = RANK < 256 ? RANK : 256;  // basis columns per staged half
-  constexpr int NHALF = RANK / RB;
-  constexpr int KS_HALF = RB / 32;
-  constexpr int NPB = RB / 8;                  // 16-byte pieces per staged basis row
-  constexpr int W2OFF = (kHidden / 2) * kHeadDim * 2;  // byte offset of the W2 half in buf
+  constexpr int NR = RANK / 64;          // basis stages (64 columns of r each)
+  constexpr int NM = kHidden / 32;       // MLP stages (32 hidden units each)
+  constexpr int NS = NR + NM;
+  constexpr int LG = 3;                  // gather lookahead, in stages
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, col = lane & 15;
@@ -163,7 +129,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
   const int g = a.g;
   const size_t head = (size_t)b * a.hkv + h;
   const uint16_t* qh = a.q + ((size_t)b * a.hq + (size_t)h * g) * kHeadDim;
-  unsigned char* buf = L.buf;
+  unsigned char* buf = &L.buf[0][0];
 
   f32x4 zacc[2];
   bf16x8 vb[8];
@@ -180,210 +146,303 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
     int tok[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) tok[nt] = chunk_of(4 * wave + 2 * nt + (col >> 3)) * kChunk + (col & 7);
+    const int rope_chunk = chunk_of(tid >> 4);  // chunk whose RoPE base row this thread fills
 
-    // Per-lane byte offsets of the swizzled operand reads.  A read of row
-    // 16*m + col, piece 4*k + grp lands at piece (4*k + grp) ^ (col & mask)
-    // = 4*(k ^ (col >> 2)) + (grp ^ (col & 3)) of that row (mask 15); the
-    // int4 basis read of piece 4*grp + k lands at 4*(grp ^ (col >> 2)) +
-    // (k ^ (col & 3)).  Row and 16-piece-block terms are immediates.
-    const int chi = col >> 2, clo = col & 3;
-    const int chib = NPB >= 16 ? chi : (chi & 1);
-    auto pbw = [&](int k) { return col * 256 + 16 * (4 * (k ^ chi) + (grp ^ clo)); };
-    auto pbb = [&](int k) { return col * (NPB * 16) + 16 * (4 * (k ^ chib) + (grp ^ clo)); };
-    auto pbi = [&](int k) { return col * (NPB * 16) + 16 * (4 * (grp ^ chib) + (k ^ clo)); };
+    // ---- small loads first, and waited for before the operand stream is
+    //      issued, so that no later wait on them holds the stream's loads
+    uint32_t rd = 0;
+    if (tid < kAttChunksWG) rd = a.res_desc[head * (size_t)a.n_chunks + chunk_of(tid)];
+    const uint16_t b1v = a.b1[head * kHidden + tid];
+    const uint16_t b2v = tid < kHeadDim ? a.b2[head * kHeadDim + tid] : 0;
+    const int rp0 = (tid & 15) * 4, rq0 = (tid & 31) * 2;
+    double fb[4], fo[2];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) fb[p] = a.inv_freq[rp0 + p];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) fo[p] = a.inv_freq[rq0 + p];
+    asm volatile("" ::"v"(rd), "v"(b1v), "v"(b2v), "v"(rope_chunk), "v"(fb[0]), "v"(fb[1]), "v"(fb[2]),
+                 "v"(fb[3]), "v"(fo[0]), "v"(fo[1]), "v"(tok[0]), "v"(tok[1])
+                 : "memory");
 
-    // ---- the coefficient gather goes out first (HBM), one basis half at a
-    //      time: half hb+1 is in flight while half hb is multiplied
-    bf16x8 cv[CI4 ? 1 : NKS][2];
-    u32x4 cq[CI4 ? NKB : 1][2];
-    float csc[CI4 ? NKB : 1][2];
-    auto gather_half = [&](int hb) {
+    // ---- operand stream: stage s < NR is basis columns [64 s, 64 s + 64)
+    //      (128 rows in pi order, two rows per 256-byte line); stage NR + m
+    //      is W1 rows [32 m, 32 m + 32) (pi order, 8 KiB) then W2 columns
+    //      [32 m, 32 m + 32) (natural, four rows per line, 8 KiB).  Pieces
+    //      are XOR-swizzled inside each 256-byte line by the line index.
+    const __amdgpu_buffer_rsrc_t bas = buffer_rsrc(a.basis + head * (size_t)kHeadDim * RANK, kHeadDim * RANK * 2);
+    const __amdgpu_buffer_rsrc_t w1r = buffer_rsrc(a.w1 + head * (size_t)kHidden * kHeadDim, kHidden * kHeadDim * 2);
+    const __amdgpu_buffer_rsrc_t w2r = buffer_rsrc(a.w2 + head * (size_t)kHeadDim * kHidden, kHeadDim * kHidden * 2);
+    // basis: load u covers rows 32 u + r0 (r0 = tid / 8), piece tid % 8
+    const int r0 = tid >> 3, pb = tid & 7;
+    const uint32_t bas_goff = (uint32_t)((row_perm32(r0) * RANK + 8 * pb) * 2);
+    const int bas_loff = (r0 >> 1) * 256 + ((((r0 & 1) << 3) | pb) ^ ((r0 >> 1) & 15)) * 16;
+    // W1: load u < 2 covers pi rows 16 u + tid / 16, piece tid % 16
+    const int w1row = tid >> 4, w1p = tid & 15;
+    const uint32_t w1_goff = (uint32_t)(((8 * ((w1row >> 2) & 3) + (w1row & 3)) * kHeadDim + 8 * w1p) * 2);
+    const int w1_loff = w1row * 256 + (w1p ^ (w1row & 15)) * 16;
+    // W2: load u in {2, 3} covers rows 64 (u - 2) + tid / 4, piece tid % 4
+    const uint32_t w2_goff = (uint32_t)(((tid >> 2) * kHidden + 8 * (tid & 3)) * 2);
+    const int w2_loff = 8192 + (tid >> 4) * 256 + ((tid & 15) ^ ((tid >> 4) & 15)) * 16;
+
+    auto stage_load = [&](int s, u32x4 (&r)[kStageLd]) {
+      if (s < NR) {
+#pragma unroll
+        for (int u = 0; u < kStageLd; ++u) r[u] = buffer_ld16(bas, bas_goff, (32 * u * RANK + 64 * s) * 2);
+      } else {
+        const int m = s - NR;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) r[u] = buffer_ld16(w1r, w1_goff, (32 * m + 4 * u) * kHeadDim * 2);
+#pragma unroll
+        for (int u = 2; u < 4; ++u) r[u] = buffer_ld16(w2r, w2_goff, ((u - 2) * 64 * kHidden + 32 * m) * 2);
+      }
+    };
+    auto stage_store = [&](int s, const u32x4 (&r)[kStageLd]) {
+      unsigned char* dst = L.buf[s & 1];
+      if (s < NR) {
+#pragma unroll
+        for (int u = 0; u < kStageLd; ++u) *reinterpret_cast<u32x4*>(dst + bas_loff + 4096 * u) = r[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(dst + w1_loff + 4096 * u) = r[u];
+#pragma unroll
+        for (int u = 2; u < 4; ++u) *reinterpret_cast<u32x4*>(dst + w2_loff + 4096 * (u - 2)) = r[u];
+      }
+    };
+
+    // ---- coefficient gather of stage s (< NR): k-steps 2 s, 2 s + 1
+    bf16x8 cv[CI4 ? 1 : NR][2][2];
+    u32x2 cq[CI4 ? NR : 1][2];
+    float csc[CI4 ? NR : 1][2];
+    auto gather = [&](int s) {
       if constexpr (!CI4) {
         const uint16_t* cb = static_cast<const uint16_t*>(a.coeff) + (size_t)b * a.prefix * RANK;
 #pragma unroll
-        for (int kl = 0; kl < KS_HALF; ++kl)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const int ks = hb * KS_HALF + kl;
-            cv[ks][nt] = load_bf16x8(cb + (size_t)tok[nt] * RANK + 32 * ks + 8 * grp);
-          }
+          for (int nt = 0; nt < 2; ++nt)
+            cv[s][ks][nt] = load_bf16x8(cb + (size_t)tok[nt] * RANK + 64 * s + 32 * ks + 8 * grp);
       } else {
+        // 16 codes r = 64 s + 16 grp .. + 15 and their group scale
         const uint8_t* cb = static_cast<const uint8_t*>(a.coeff) + (size_t)b * a.prefix * (RANK / 2);
         const uint16_t* sb = a.coeff_scale + (size_t)b * a.prefix * (RANK / 32);
 #pragma unroll
-        for (int kl = 0; kl < NKB / NHALF; ++kl)
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const int kb = hb * (NKB / NHALF) + kl;
-            cq[kb][nt] = *reinterpret_cast<const u32x4*>(cb + (size_t)tok[nt] * (RANK / 2) + 64 * kb + 16 * grp);
-            csc[kb][nt] = f16_to_f32(sb[(size_t)tok[nt] * (RANK / 32) + 4 * kb + grp]);
-          }
+        for (int nt = 0; nt < 2; ++nt) {
+          cq[s][nt] = *reinterpret_cast<const u32x2*>(cb + (size_t)tok[nt] * (RANK / 2) + 32 * s + 8 * grp);
+          csc[s][nt] = f16_to_f32(sb[(size_t)tok[nt] * (RANK / 32) + 2 * s + (grp >> 1)]);
+        }
       }
     };
-    gather_half(0);
-    // ---- residual descriptor of token `lane` (< 32)'s chunk: one load,
-    //      consumed only after the MLP
-    uint32_t rdesc = 0;
-    if (lane < nvalid) rdesc = a.res_desc[head * (size_t)a.n_chunks + chunk_of(4 * wave + (lane >> 3))];
 
-    const __amdgpu_buffer_rsrc_t basis = buffer_rsrc(a.basis + head * (size_t)kHeadDim * RANK, kHeadDim * RANK * 2);
-    stage_plain<kHeadDim, NPB, RANK>(buf, basis, 0, tid);
+    // ---- prologue: stages 0 and 1 in flight, then the first gathers
+    u32x4 sreg[NS + 2][kStageLd];
+    stage_load(0, sreg[0]);
+    if (NS > 1) stage_load(1, sreg[1]);
+#pragma unroll
+    for (int s = 0; s < LG && s < NR; ++s) gather(s);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // RoPE rotations of this workgroup's tokens (VALU work while the loads
+    // fly): base angle of every chunk start, reduced in fp64, and the
+    // offsets 0..7 inside a chunk
+    {
+      const int cs = tid >> 4;
+      const double pos = (double)rope_chunk * kChunk;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) L.rope_base[cs][rp0 + p] = rot_of(pos * fb[p]);
+      const int i = tid >> 5;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) L.rope_off[i][rq0 + p] = rot_of((double)i * fo[p]);
+    }
+    if (tid < kAttChunksWG) L.rdesc[tid] = rd;
+    L.b1f[tid] = bf16_to_f32(b1v);
+    if (tid < kHeadDim) L.b2f[tid] = bf16_to_f32(b2v);
+    stage_store(0, sreg[0]);
     __syncthreads();
 
-    // ---- reconstruction: acc[nt][mt] = K_pre^T rows d = 16 mt + 4 grp + e
+    // ---- per-lane LDS read offsets
+    // recon A (basis), k-step ks of a stage, m-tile parity q: row 16 mt + col
+    // is line 8 mt + col/2, half col%2; the lane's piece is 4 ks + grp (bf16)
+    // or 2 grp + ks (int4: the lane holds r = 16 grp + 8 ks + e of the slice)
+    int ra[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int p = CI4 ? 2 * grp + ks : 4 * ks + grp;
+        ra[ks][q] = (col >> 1) * 256 + ((((col & 1) ^ q) << 3) | (p ^ (col >> 1))) * 16;
+      }
+    // MLP1 A (W1 pi rows 16 hm + col, piece 4 s + grp) and MLP2 B (W2 row
+    // 16 nd + col, piece grp; line 4 nd + col/4)
+    int rw1[4], rw2[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) rw1[s] = col * 256 + ((4 * s + grp) ^ col) * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      rw2[q] = 8192 + (col >> 2) * 256 + ((((col & 3) ^ q) << 2) | (grp ^ (col >> 2))) * 16;
+
     f32x4 acc[2][8];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int hb = 0; hb < NHALF; ++hb) {
-      if (hb > 0) {
-        __syncthreads();
-        stage_plain<kHeadDim, NPB, RANK>(buf, basis, RB * hb, tid);
-        __syncthreads();
-      }
-      if (hb + 1 < NHALF) gather_half(hb + 1);
-#pragma unroll
-      for (int kl = 0; kl < KS_HALF; ++kl) {
-        const int ks = hb * KS_HALF + kl;
-        bf16x8 bop[2];
-        int off;
-        if constexpr (!CI4) {
-          bop[0] = cv[ks][0];
-          bop[1] = cv[ks][1];
-          off = pbb(kl & 3) + 256 * (kl >> 2);  // piece 4*kl + grp of the half
-        } else {
-          const int kb = ks >> 2, kw = ks & 3;
-          bop[0] = dequant8(cq[kb][0][kw], csc[kb][0]);
-          bop[1] = dequant8(cq[kb][1][kw], csc[kb][1]);
-          off = pbi(kw) + 256 * (kb & 1);       // piece 16*(kb&1) + 4*grp + kw
-        }
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-          const bf16x8 aop = lds16(buf, off + mt * 16 * NPB * 16);
-          acc[0][mt] = mfma16(aop, bop[0], acc[0][mt]);
-          acc[1][mt] = mfma16(aop, bop[1], acc[1][mt]);
-        }
-      }
-    }
-    const size_t row0 = head * (size_t)a.k_eff * kChunk + (size_t)(chunk0 + 4 * wave) * kChunk;
-    if (a.kpre_out) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        if (16 * nt + col < nvalid)
-#pragma unroll
-          for (int mt = 0; mt < 8; ++mt)
-            *reinterpret_cast<f32x4*>(a.kpre_out + (row0 + 16 * nt + col) * kHeadDim + 16 * mt + 4 * grp) = acc[nt][mt];
-    }
-
-    // ---- K_pre as the MLP1 operand (bf16)
     bf16x8 kpre_b[2][4];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) kpre_b[nt][s] = pack8(acc[nt][2 * s], acc[nt][2 * s + 1]);
+    f32x4 vacc[2][8];
+    u32x4 rres[RI4 ? 3 : 8];  // residual tile pieces of this thread
 
-    // ---- RoPE rotations of this workgroup's tokens: base angle of every
-    //      chunk start (fp64-reduced) and the offsets 0..7 inside a chunk.
-    //      The basis is no longer read: W1 / biases go to LDS meanwhile.
-    {
-      const int cs = tid >> 4, p0 = (tid & 15) * 4;
-      const double pos = (double)chunk_of(cs) * kChunk;
-#pragma unroll
-      for (int p = p0; p < p0 + 4; ++p) L.rope_base[cs][p] = rot_of(pos * a.inv_freq[p]);
-      const int i = tid >> 5, q0 = (tid & 31) * 2;
-#pragma unroll
-      for (int p = q0; p < q0 + 2; ++p) L.rope_off[i][p] = rot_of((double)i * a.inv_freq[p]);
-    }
-    __syncthreads();
-    const __amdgpu_buffer_rsrc_t w1h = buffer_rsrc(a.w1 + head * (size_t)kHidden * kHeadDim, kHidden * kHeadDim * 2);
-    const __amdgpu_buffer_rsrc_t w2h = buffer_rsrc(a.w2 + head * (size_t)kHeadDim * kHidden, kHeadDim * kHidden * 2);
-    stage_perm16<kHidden / 2, kHeadDim>(buf, w1h, 0, tid);             // W1 rows h < 128
-    stage_perm16<kHeadDim, kHidden>(buf + W2OFF, w2h, 0, tid);         // W2 columns h < 128
-    L.b1f[tid] = bf16_to_f32(a.b1[head * kHidden + tid]);
-    if (tid < kHeadDim) L.b2f[tid] = bf16_to_f32(a.b2[head * kHeadDim + tid]);
+    const size_t row0 = head * (size_t)a.k_eff * kChunk + (size_t)(chunk0 + 4 * wave) * kChunk;
+    // residual row of workgroup token tl (< 128), or -1
+    auto resid_row = [&](int tl) -> int {
+      const uint32_t dsc = L.rdesc[tl >> 3];
+      const int i = tl & 7;
+      if (!((dsc >> i) & 1u)) return -1;
+      return (int)(dsc >> 8) + __popc(dsc & ((1u << i) - 1u) & 0xFFu);
+    };
 
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int cs = 4 * wave + 2 * nt + (col >> 3), i = col & 7;
+    for (int s = 0; s < NS; ++s) {
+      // loads for later stages: the stage two ahead, the gather LG ahead,
+      // and (two stages before the end) the residual tile
+      if (s + 2 < NS) stage_load(s + 2, sreg[s + 2]);
+      if (s + LG < NR) gather(s + LG);
+      if (s == NS - 2) {
+        if constexpr (!RI4) {
+          // 128 tokens x 16 pieces; a token without a residual reads past
+          // the end of the buffer, which returns zeros
+          const uint32_t nbytes = (uint32_t)a.n_resid * kHeadDim * 2;
+          const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(
+              static_cast<const uint16_t*>(a.res_val) + head * (size_t)a.n_resid * kHeadDim, nbytes);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+          for (int u = 0; u < 8; ++u) {
+            const int tl = 16 * u + (tid >> 4);
+            const int rn = resid_row(tl);
+            rres[u] = buffer_ld16(rv, rn >= 0 ? (uint32_t)rn * 256 + (tid & 15) * 16 : nbytes, 0);
+          }
+        } else {
+          // int4 rows: 64 bytes of codes (4 pieces) + 8 bytes of scales
+          const uint32_t nbytes = (uint32_t)a.n_resid * (kHeadDim / 2);
+          const uint32_t sbytes = (uint32_t)a.n_resid * (kHeadDim / 32) * 2;
+          const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(
+              static_cast<const uint8_t*>(a.res_val) + head * (size_t)a.n_resid * (kHeadDim / 2), nbytes);
+          const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
+              a.res_scale + head * (size_t)a.n_resid * (kHeadDim / 32), sbytes);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int p = 16 * mt + 4 * grp + e;
-          const float2 bs = L.rope_base[cs][p], of = L.rope_off[i][p];
-          const float c = bs.x * of.x - bs.y * of.y;
-          const float s = bs.y * of.x + bs.x * of.y;
-          const float x1 = acc[nt][mt][e], x2 = acc[nt][mt + 4][e];
-          acc[nt][mt][e] = x1 * c - x2 * s;
-          acc[nt][mt + 4][e] = x2 * c + x1 * s;
+          for (int u = 0; u < 2; ++u) {
+            const int tl = 64 * u + (tid >> 2);
+            const int rn = resid_row(tl);
+            rres[u] = buffer_ld16(rv, rn >= 0 ? (uint32_t)rn * 64 + (tid & 3) * 16 : nbytes, 0);
+          }
+          {
+            const int tl = tid >> 1;
+            const int rn = resid_row(tl);
+            const u32x2 sc = __builtin_amdgcn_raw_buffer_load_b64(rs, rn >= 0 ? (uint32_t)rn * 8 : sbytes, 0, 0);
+            rres[2] = u32x4{sc[0], sc[1], 0u, 0u};
+          }
         }
       }
-    }
-    if (a.kpost_out) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        if (16 * nt + col < nvalid)
-#pragma unroll
-          for (int mt = 0; mt < 8; ++mt)
-            *reinterpret_cast<f32x4*>(a.kpost_out + (row0 + 16 * nt + col) * kHeadDim + 16 * mt + 4 * grp) = acc[nt][mt];
-    }
 
-    // ---- QK: z[t][j] with K_post rounded to bf16 (2^-9 relative per entry)
-    {
-      bf16x8 qp[4];
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads above at the top of the step
+      const unsigned char* sb = L.buf[s & 1];
+      if (s < NR) {
+        // ---------------- reconstruction, basis columns [64 s, 64 s + 64)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        qp[s] = col < g ? load_bf16x4x2(qh + col * kHeadDim + 32 * s + 4 * grp,
-                                        qh + col * kHeadDim + 32 * s + 16 + 4 * grp)
-                        : zero_bf16x8();
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 bop[2];
+          if constexpr (!CI4) {
+            bop[0] = cv[s][ks][0];
+            bop[1] = cv[s][ks][1];
+          } else {
+            bop[0] = dequant8(cq[s][0][ks], csc[s][0]);
+            bop[1] = dequant8(cq[s][1][ks], csc[s][1]);
+          }
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          for (int mt = 0; mt < 8; ++mt) {
+            const bf16x8 aop = lds16(sb, ra[ks][mt & 1] + 2048 * mt);
+            acc[0][mt] = mfma16(aop, bop[0], acc[0][mt]);
+            acc[1][mt] = mfma16(aop, bop[1], acc[1][mt]);
+          }
+        }
+        if (s == NR - 1) {
+          // -------- K_pre done: acc[nt][mt][e] = K_pre[t][d], t = 16 nt + col,
+          //          d = 32 (mt / 2) + 8 grp + 4 (mt % 2) + e
+          if (a.kpre_out) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) z = mfma16(pack8(acc[nt][2 * s], acc[nt][2 * s + 1]), qp[s], z);
-        zacc[nt] = z;
-      }
-    }
-
-    // ---- value MLP, 32 hidden units at a time: MLP1 chunk (b1 as the
-    //      accumulator's initial value) -> GELU -> bf16 -> MLP2 accumulate.
-    //      Hidden units [0, 128) use the W1/W2 halves staged above, then the
-    //      buffer is refilled with the halves of units [128, 256).
-    __syncthreads();
-    f32x4 vacc[2][8];
+            for (int nt = 0; nt < 2; ++nt)
+              if (16 * nt + col < nvalid)
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const float bias = L.b2f[16 * nt + col];
-      vacc[0][nt] = f32x4{bias, bias, bias, bias};
-      vacc[1][nt] = vacc[0][nt];
-    }
+                for (int mt = 0; mt < 8; ++mt)
+                  *reinterpret_cast<f32x4*>(a.kpre_out + (row0 + 16 * nt + col) * kHeadDim + 32 * (mt >> 1) +
+                                            8 * grp + 4 * (mt & 1)) = acc[nt][mt];
+            }
 #pragma unroll
-    for (int hp = 0; hp < 2; ++hp) {
-      if (hp > 0) {
-        __syncthreads();
-        stage_perm16<kHidden / 2, kHeadDim>(buf, w1h, (kHidden / 2) * kHeadDim, tid);
-        stage_perm16<kHeadDim, kHidden>(buf + W2OFF, w2h, kHidden / 2, tid);
-        __syncthreads();
-      }
-#pragma unroll 1
-      for (int hl = 0; hl < 4; ++hl) {
-        const int hc = 4 * hp + hl;
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) kpre_b[nt][ks] = pack8(acc[nt][2 * ks], acc[nt][2 * ks + 1]);
+          // RoPE: pair (d, d + 64) = m-tiles (mt, mt + 4) of the same lane
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const int cs = 4 * wave + 2 * nt + (col >> 3), i = col & 7;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int p = 32 * (mt >> 1) + 8 * grp + 4 * (mt & 1) + e;
+                const float2 bs = L.rope_base[cs][p], of = L.rope_off[i][p];
+                const float c = bs.x * of.x - bs.y * of.y;
+                const float sn = bs.y * of.x + bs.x * of.y;
+                const float x1 = acc[nt][mt][e], x2 = acc[nt][mt + 4][e];
+                acc[nt][mt][e] = x1 * c - x2 * sn;
+                acc[nt][mt + 4][e] = x2 * c + x1 * sn;
+              }
+            }
+          }
+          if (a.kpost_out) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+              if (16 * nt + col < nvalid)
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt)
+                  *reinterpret_cast<f32x4*>(a.kpost_out + (row0 + 16 * nt + col) * kHeadDim + 32 * (mt >> 1) +
+                                            8 * grp + 4 * (mt & 1)) = acc[nt][mt];
+          }
+          // QK with K_post rounded to bf16 (2^-9 relative per entry)
+          {
+            bf16x8 qp[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+              qp[ks] = col < g ? load_bf16x8(qh + col * kHeadDim + 32 * ks + 8 * grp) : zero_bf16x8();
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+              f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int ks = 0; ks < 4; ++ks) z = mfma16(pack8(acc[nt][2 * ks], acc[nt][2 * ks + 1]), qp[ks], z);
+              zacc[nt] = z;
+            }
+          }
+#pragma unroll
+          for (int nd = 0; nd < 8; ++nd) {
+            const float bias = L.b2f[16 * nd + col];
+            vacc[0][nd] = f32x4{bias, bias, bias, bias};
+            vacc[1][nd] = vacc[0][nd];
+          }
+        }
+      } else {
+        // ---------------- value MLP, hidden units [32 m, 32 m + 32):
+        //                  MLP1 (b1 as the initial value) -> GELU -> bf16 -> MLP2
+        const int m = s - NR;
         f32x4 hacc[2][2];
 #pragma unroll
         for (int hm = 0; hm < 2; ++hm) {
-          const f32x4 bias = *reinterpret_cast<const f32x4*>(&L.b1f[32 * hc + 16 * hm + 4 * grp]);
+          const f32x4 bias = *reinterpret_cast<const f32x4*>(&L.b1f[32 * m + 8 * grp + 4 * hm]);
           hacc[hm][0] = bias;
           hacc[hm][1] = bias;
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
           for (int hm = 0; hm < 2; ++hm) {
-            const bf16x8 aop = lds16(buf, pbw(s) + (32 * hl + 16 * hm) * 256);
-            hacc[hm][0] = mfma16(aop, kpre_b[0][s], hacc[hm][0]);
-            hacc[hm][1] = mfma16(aop, kpre_b[1][s], hacc[hm][1]);
+            const bf16x8 aop = lds16(sb, rw1[ks] + 4096 * hm);
+            hacc[hm][0] = mfma16(aop, kpre_b[0][ks], hacc[hm][0]);
+            hacc[hm][1] = mfma16(aop, kpre_b[1][ks], hacc[hm][1]);
           }
         }
 #pragma unroll
@@ -395,61 +454,73 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
         const bf16x8 ha0 = pack8(hacc[0][0], hacc[1][0]);
         const bf16x8 ha1 = pack8(hacc[0][1], hacc[1][1]);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          const bf16x8 bop = lds16(buf, W2OFF + pbw(hl) + 16 * nt * 256);
-          vacc[0][nt] = mfma16(ha0, bop, vacc[0][nt]);
-          vacc[1][nt] = mfma16(ha1, bop, vacc[1][nt]);
+        for (int nd = 0; nd < 8; ++nd) {
+          const bf16x8 bop = lds16(sb, rw2[nd & 3] + 1024 * nd);
+          vacc[0][nd] = mfma16(ha0, bop, vacc[0][nd]);
+          vacc[1][nd] = mfma16(ha1, bop, vacc[1][nd]);
         }
+      }
+      if (s + 1 < NS) {
+        stage_store(s + 1, sreg[s + 1]);  // into the buffer step s - 1 read
+        __syncthreads();
       }
     }
 
-    // ---- residual scatter-add: token `lane` has a stored row iff its bit is
-    //      set; the row is the chunk's first row plus the set bits below it
-    int rn = -1;
-    {
-      const int i = lane & 7;
-      if ((rdesc >> i) & 1u) {
-        rn = (int)(rdesc >> 8) + __popc(rdesc & ((1u << i) - 1u) & 0xFFu);
-        rn = min(rn, a.n_resid - 1);
-      }
-    }
+    // ---- residual tile -> LDS (both buffers), then add to the values
+    __syncthreads();
+    if constexpr (!RI4) {
+      // row tl at tl * 256, piece p at p ^ ((tl / 4) % 16)
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int u = 0; u < 8; ++u) {
+        const int tl = 16 * u + (tid >> 4);
+        *reinterpret_cast<u32x4*>(buf + tl * 256 + (((tid & 15) ^ ((tl >> 2) & 15)) * 16)) = rres[u];
+      }
+    } else {
+      // codes: row tl at tl * 64, piece p at p ^ ((tl / 4) % 4); scales at 8192 + tl * 8
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int tl = 64 * u + (tid >> 2);
+        *reinterpret_cast<u32x4*>(buf + tl * 64 + (((tid & 3) ^ ((tl >> 2) & 3)) * 16)) = rres[u];
+      }
+      if ((tid & 1) == 0)
+        *reinterpret_cast<u32x2*>(buf + 8192 + (tid >> 1) * 8) = u32x2{rres[2][0], rres[2][1]};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int nn = __shfl(rn, 16 * mt + 4 * grp + e);
-        if (nn >= 0) {
-          const size_t rrow = head * (size_t)a.n_resid + nn;
+        const int tl = 32 * wave + 16 * tt + 4 * grp + e;
 #pragma unroll
-          for (int nt = 0; nt < 8; ++nt) {
-            const int d = 16 * nt + col;
-            float r;
-            if constexpr (!RI4) {
-              r = bf16_to_f32(static_cast<const uint16_t*>(a.res_val)[rrow * kHeadDim + d]);
-            } else {
-              const uint32_t byte = static_cast<const uint8_t*>(a.res_val)[rrow * (kHeadDim / 2) + (d >> 1)];
-              const int code = static_cast<int>(((byte >> (4 * (d & 1))) & 0xFu) ^ 8u) - 8;
-              r = static_cast<float>(code) * f16_to_f32(a.res_scale[rrow * (kHeadDim / 32) + (d >> 5)]);
-            }
-            vacc[mt][nt][e] += r;
+        for (int nd = 0; nd < 8; ++nd) {
+          const int d = 16 * nd + col;
+          float r;
+          if constexpr (!RI4) {
+            const int off = tl * 256 + (((d >> 3) ^ ((tl >> 2) & 15)) * 16) + (d & 7) * 2;
+            r = bf16_to_f32(*reinterpret_cast<const uint16_t*>(buf + off));
+          } else {
+            const int off = tl * 64 + ((((d >> 1) >> 4) ^ ((tl >> 2) & 3)) * 16) + ((d >> 1) & 15);
+            const uint32_t byte = buf[off];
+            const int code = static_cast<int>(((byte >> (4 * (d & 1))) & 0xFu) ^ 8u) - 8;
+            const uint16_t sc = *reinterpret_cast<const uint16_t*>(buf + 8192 + tl * 8 + (d >> 5) * 2);
+            r = static_cast<float>(code) * f16_to_f32(sc);
           }
+          vacc[tt][nd][e] += r;
         }
       }
     if (a.vhat_out) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int t = 16 * mt + 4 * grp + e;
+          const int t = 16 * tt + 4 * grp + e;
           if (t < nvalid)
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) a.vhat_out[(row0 + t) * kHeadDim + 16 * nt + col] = vacc[mt][nt][e];
+            for (int nd = 0; nd < 8; ++nd) a.vhat_out[(row0 + t) * kHeadDim + 16 * nd + col] = vacc[tt][nd][e];
         }
     }
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      vb[nt] = pack8(vacc[0][nt], vacc[1][nt]);
-    }
+    for (int nd = 0; nd < 8; ++nd) vb[nd] = pack8(vacc[0][nd], vacc[1][nd]);
   } else {
     // ========================================================= exact window
     const int w0 = (split - a.n_sel_tiles) * kAttTokWG + wave * kAttTokWave;
@@ -516,8 +587,8 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
 
   // ======================================== merge the 4 waves, write partial
   __syncthreads();
-  float* mo = reinterpret_cast<float*>(L.buf);
-  float* ml = mo + kAttWaves * 16 * kHeadDim;
+  float* mo = reinterpret_cast<float*>(buf);  // 32 KiB: 4 waves x 16 heads x 128
+  float* ml = L.ml;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt)
 #pragma unroll

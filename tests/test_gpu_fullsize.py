@@ -1,0 +1,96 @@
+"""GPU parity at the full 262K sizes, in the launch configuration the benchmark times.
+
+The whole batch (28 sequences at 262144 tokens, or 16 with int4 + eviction)
+runs through lowram_decode_step in one call, as the benchmark runs it; each
+sequence has its own seeded device-drawn cache.  The oracle then recomputes
+sampled (sequence, KV head) slices one by one from the same arrays copied to
+the host: selection within the tie band, that head's output within the
+decode tolerance against the oracle re-run on the GPU's selection.  Every
+output of the batch must be finite, and every selection ascending and full.
+"""
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gpu_util import DEV, check_output, check_selection, down_bf16  # noqa: E402
+from long_context_decode_landmark_amd import native  # noqa: E402
+from oracle import decode  # noqa: E402
+from synth import device as sd  # noqa: E402
+
+
+def host(t):
+    t = t.contiguous().cpu()
+    if t.dtype in (torch.bfloat16, torch.int16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def draw_batch(cfg, nb, seed):
+    """Distinct device caches for nb sequences (stacked on a batch axis)."""
+    per = [sd.draw_layer(cfg, seed + b, DEV) for b in range(nb)]
+    cache = {k: torch.stack([p[k] for p in per]) for k in per[0]}
+    del per
+    coeffs = [sd.draw_coeff(cfg, seed + 1000 + b, DEV) for b in range(nb)]
+    if cfg.int4:
+        cache["coeff"] = torch.stack([c[0] for c in coeffs])
+        cache["coeff_scale"] = torch.stack([c[1] for c in coeffs])
+    else:
+        cache["coeff"] = torch.stack(coeffs)
+    del coeffs
+    desc = torch.empty((nb, cfg.n_heads_kv, cfg.n_chunks), dtype=torch.int32, device=DEV)
+    native.resid_chunk_desc(cache["res_idx"], nb * cfg.n_heads_kv, cfg.n_resid, cfg.n_chunks, cfg.chunk, desc)
+    cache["res_chunk_desc"] = desc
+    return cache
+
+
+def head_slice(cfg, cache, b, h):
+    """Host copy of what the oracle reads for (sequence b, KV head h), as a 1 x 1 cache."""
+    out = {}
+    for k, v in cache.items():
+        if k in ("coeff", "coeff_scale"):
+            out[k] = host(v[b:b + 1])
+        elif k != "res_chunk_desc":
+            out[k] = host(v[b:b + 1, h:h + 1])
+    return out
+
+
+@pytest.mark.parametrize("name,nb", [("c3_llama8b_262k", 28), ("c4_eq_int4_evict_262k", 16)])
+def test_full_size_sampled_heads(name, nb):
+    cfg = synth.CONFIGS[name]
+    g, keff = cfg.gqa, min(cfg.topk, cfg.n_cand)
+    print(f"\n{name} batch {nb}: drawing caches", flush=True)
+    cache = draw_batch(cfg, nb, seed=4242)
+    q = sd.draw_queries(cfg, nb, 99, DEV)
+    out = torch.empty_like(q)
+    shape = native.make_shape(cfg, batch=nb)
+    ws = torch.empty(native.workspace_bytes(shape), dtype=torch.uint8, device=DEV)
+    sel = torch.full((nb, cfg.n_heads_kv, cfg.topk), -7, dtype=torch.int32, device=DEV)
+    native.decode_step(shape, native.make_cache(cache), q, out, ws, sel_out=sel)
+    torch.cuda.synchronize()
+    got = down_bf16(out)
+    sel_h = sel.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert np.all(np.diff(sel_h[..., :keff], axis=-1) > 0)
+    assert np.all(sel_h[..., keff:] == -1)
+    print(f"{name}: step done, checking sampled heads", flush=True)
+
+    q_h = host(q)
+    samples = [(0, 0), (nb // 2, 3), (nb - 1, cfg.n_heads_kv - 1)]
+    for b, h in samples:
+        sl = head_slice(cfg, cache, b, h)
+        qs = decode.widen(q_h[b, h * g:(h + 1) * g])
+        _, st = decode.decode_head(cfg, sl, qs, 0, 0)
+        if "cand_ids" in sl:
+            st["cand"] = sl["cand_ids"][0, 0]
+        fake_sel = sel_h[b:b + 1, h:h + 1]
+        nflip = check_selection(cfg, {(0, 0): st}, fake_sel, 0, 0)
+        ref, _ = decode.decode_head(cfg, sl, qs, 0, 0, sel_override=sel_h[b, h])
+        rel, mx = check_output(got[b, h * g:(h + 1) * g], ref, f"{name} b{b} h{h}")
+        print(f"{name} b{b} h{h}: rel {rel:.2e} max {mx:.2e} flips {nflip}", flush=True)

@@ -92,3 +92,19 @@ def test_deterministic_bitwise():
     a, sa, _ = run_gpu(cfg, cache)
     b, sb, _ = run_gpu(cfg, cache)
     assert np.array_equal(a, b) and np.array_equal(sa, sb)
+
+
+def test_c1_llama8b_32k_layer():
+    """C1 at its real shape: 32768 tokens, rank 512, top-256, window 128, one layer in the second group."""
+    res = run_case(synth.C1, layer=5)
+    print(f"c1 layer 5: rel {res['rel']:.2e} max {res['max_abs']:.2e} flips {res['flips']}")
+
+
+def test_c2_needle_is_selected():
+    """C2 at its real shape (131072 tokens, top-512) for one sequence: the planted chunk of every head is selected."""
+    cfg = synth.CONFIGS["c2_mistral7b_128k_needle"]
+    cache = fixture.build_layer(cfg, 9, batch=[0])
+    res = full_parity(cfg, cache, stages=False)
+    for h in range(cfg.n_heads_kv):
+        assert int(cache["needle"][0][h]) in set(res["sel"][0, h].tolist()), h
+    print(f"c2 layer 9: rel {res['rel']:.2e} max {res['max_abs']:.2e} flips {res['flips']}")
