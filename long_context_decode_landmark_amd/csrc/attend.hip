@@ -45,23 +45,24 @@
 
 namespace lowram {
 
-// Sigmoid-form GELU: Phi(x) = sigmoid(logit Phi(x)) with logit Phi(x) fitted
-// by the odd polynomial x * P(x^2), P of degree 4 (weighted least squares of
-// the GELU error over |x| <= 5, x^2 clamped at 25 inside P so the sigmoid
-// saturates correctly beyond).  This is the sigmoid/tanh approximation form
-// of Hendrycks & Gimpel's GELU paper with a refitted polynomial; its maximum
-// absolute deviation from the exact erf form is 3.1e-6 on the real line.
-constexpr float kGeluP0 = 1.595655155f;
-constexpr float kGeluP1 = 0.07293980766f;
-constexpr float kGeluP2 = -0.0002509101281f;
-constexpr float kGeluP3 = -6.094355622e-05f;
-constexpr float kGeluP4 = 2.225823705e-06f;
+// GELU without transcendental instructions (v_exp / v_rcp issue at a
+// quarter of the FMA rate): Phi(x) = 0.5 + x Q(x^2) for |x| <= 4.5, with Q of
+// degree 8 fitted by linear-programming minimax of the GELU error x (Phi~ - Phi)
+// under the constraint Phi~(4.5) = 1, and x clamped to +-4.5 (so Phi~ is 1 or
+// about 0 beyond).  Largest deviation from x Phi(x) (erf form) in fp32:
+// 5.2e-5 for |x| <= 10, growing as 4.4e-6 |x| below -4.5.
+constexpr float kGeluClamp = 4.5f;
+constexpr float kGeluQ[9] = {3.987086713e-01f, -6.597738713e-02f, 9.580709971e-03f,
+                             -1.036266563e-03f, 8.121141582e-05f, -4.431812613e-06f,
+                             1.580313267e-07f, -3.284044814e-09f, 3.000137985e-11f};
 
 __device__ __forceinline__ float gelu_fast(float x) {
-  const float u = fminf(x * x, 25.0f);
-  const float p = fmaf(fmaf(fmaf(fmaf(kGeluP4, u, kGeluP3), u, kGeluP2), u, kGeluP1), u, kGeluP0);
-  const float t = __builtin_amdgcn_exp2f(-kLog2e * x * p);
-  return x * __builtin_amdgcn_rcpf(1.0f + t);
+  const float xc = __builtin_amdgcn_fmed3f(x, -kGeluClamp, kGeluClamp);
+  const float u = xc * xc;
+  float q = kGeluQ[8];
+#pragma unroll
+  for (int k = 7; k >= 0; --k) q = fmaf(q, u, kGeluQ[k]);
+  return x * fmaf(xc, q, 0.5f);
 }
 
 // 2*pi split for the Cody-Waite reduction of large RoPE angles in fp64.
@@ -81,9 +82,13 @@ __device__ __forceinline__ float2 rot_of(double angle) {
 constexpr int kStage = 16384;  // bytes of one staged operand slice
 constexpr int kStageLd = 4;    // 16-byte loads per thread per stage (256 threads)
 
+constexpr int kResRow = 272;   // LDS stride of a bf16 residual row (256 + 16: rows on different banks)
+constexpr int kResRow4 = 80;   // int4 residual row: 64 bytes of codes, 8 of scales, 8 unused
+
 struct AttLds {
-  alignas(16) unsigned char buf[2][kStage];  // stage ring; residual tile; wave merge
-  float2 rope_off[kChunk][64];
+  // stage ring; then the residual tile (128 rows of kResRow); then the wave merge
+  alignas(16) unsigned char buf[2 * kStage > 128 * kResRow ? 2 * kStage : 128 * kResRow];
+  float2 rope_off[kChunk][65];  // padded: the 8 offsets of one frequency fall on distinct banks
   float2 rope_base[kAttChunksWG][64];
   float b1f[kHidden];
   float b2f[kHeadDim];
@@ -112,13 +117,26 @@ __device__ __forceinline__ constexpr int row_perm32(int pos) {
   return 8 * ((pos >> 2) & 3) + 4 * (pos >> 4) + (pos & 3);
 }
 
+// Workgroups per CU the register budget is sized for, and how many stages
+// ahead each wave's coefficient gather runs (compile-time tunables).
+#ifndef LOWRAM_ATT_WG_PER_CU
+#define LOWRAM_ATT_WG_PER_CU 2
+#endif
+#ifndef LOWRAM_ATT_GATHER_AHEAD
+#define LOWRAM_ATT_GATHER_AHEAD 3
+#endif
+#ifndef LOWRAM_ATT_STAGE_AHEAD
+#define LOWRAM_ATT_STAGE_AHEAD 2
+#endif
+
 template <int RANK, bool CI4, bool RI4>
-__global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendArgs a) {
+__global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_kernel(const AttendArgs a) {
   __shared__ AttLds L;
   constexpr int NR = RANK / 64;          // basis stages (64 columns of r each)
   constexpr int NM = kHidden / 32;       // MLP stages (32 hidden units each)
   constexpr int NS = NR + NM;
-  constexpr int LG = 3;                  // gather lookahead, in stages
+  constexpr int LG = LOWRAM_ATT_GATHER_AHEAD;
+  constexpr int SL = LOWRAM_ATT_STAGE_AHEAD;  // >= 2: stage s + SL is loaded at the top of step s
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, col = lane & 15;
@@ -129,7 +147,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
   const int g = a.g;
   const size_t head = (size_t)b * a.hkv + h;
   const uint16_t* qh = a.q + ((size_t)b * a.hq + (size_t)h * g) * kHeadDim;
-  unsigned char* buf = &L.buf[0][0];
+  unsigned char* buf = L.buf;
 
   f32x4 zacc[2];
   bf16x8 vb[8];
@@ -197,7 +215,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
       }
     };
     auto stage_store = [&](int s, const u32x4 (&r)[kStageLd]) {
-      unsigned char* dst = L.buf[s & 1];
+      unsigned char* dst = L.buf + (s & 1) * kStage;
       if (s < NR) {
 #pragma unroll
         for (int u = 0; u < kStageLd; ++u) *reinterpret_cast<u32x4*>(dst + bas_loff + 4096 * u) = r[u];
@@ -234,9 +252,9 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
     };
 
     // ---- prologue: stages 0 and 1 in flight, then the first gathers
-    u32x4 sreg[NS + 2][kStageLd];
-    stage_load(0, sreg[0]);
-    if (NS > 1) stage_load(1, sreg[1]);
+    u32x4 sreg[NS + SL][kStageLd];
+#pragma unroll
+    for (int s = 0; s < SL && s < NS; ++s) stage_load(s, sreg[s]);
 #pragma unroll
     for (int s = 0; s < LG && s < NR; ++s) gather(s);
     __builtin_amdgcn_sched_barrier(0);
@@ -302,7 +320,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
     for (int s = 0; s < NS; ++s) {
       // loads for later stages: the stage two ahead, the gather LG ahead,
       // and (two stages before the end) the residual tile
-      if (s + 2 < NS) stage_load(s + 2, sreg[s + 2]);
+      if (s + SL < NS) stage_load(s + SL, sreg[s + SL]);
       if (s + LG < NR) gather(s + LG);
       if (s == NS - 2) {
         if constexpr (!RI4) {
@@ -341,7 +359,7 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
       }
 
       __builtin_amdgcn_sched_barrier(0);  // keep the loads above at the top of the step
-      const unsigned char* sb = L.buf[s & 1];
+      const unsigned char* sb = L.buf + (s & 1) * kStage;
       if (s < NR) {
         // ---------------- reconstruction, basis columns [64 s, 64 s + 64)
 #pragma unroll
@@ -469,21 +487,19 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
     // ---- residual tile -> LDS (both buffers), then add to the values
     __syncthreads();
     if constexpr (!RI4) {
-      // row tl at tl * 256, piece p at p ^ ((tl / 4) % 16)
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int tl = 16 * u + (tid >> 4);
-        *reinterpret_cast<u32x4*>(buf + tl * 256 + (((tid & 15) ^ ((tl >> 2) & 15)) * 16)) = rres[u];
+        *reinterpret_cast<u32x4*>(buf + tl * kResRow + (tid & 15) * 16) = rres[u];
       }
     } else {
-      // codes: row tl at tl * 64, piece p at p ^ ((tl / 4) % 4); scales at 8192 + tl * 8
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int tl = 64 * u + (tid >> 2);
-        *reinterpret_cast<u32x4*>(buf + tl * 64 + (((tid & 3) ^ ((tl >> 2) & 3)) * 16)) = rres[u];
+        *reinterpret_cast<u32x4*>(buf + tl * kResRow4 + (tid & 3) * 16) = rres[u];
       }
       if ((tid & 1) == 0)
-        *reinterpret_cast<u32x2*>(buf + 8192 + (tid >> 1) * 8) = u32x2{rres[2][0], rres[2][1]};
+        *reinterpret_cast<u32x2*>(buf + (tid >> 1) * kResRow4 + 64) = u32x2{rres[2][0], rres[2][1]};
     }
     __syncthreads();
 #pragma unroll
@@ -496,13 +512,11 @@ __global__ __launch_bounds__(kAttWaves * 64, 2) void attend_kernel(const AttendA
           const int d = 16 * nd + col;
           float r;
           if constexpr (!RI4) {
-            const int off = tl * 256 + (((d >> 3) ^ ((tl >> 2) & 15)) * 16) + (d & 7) * 2;
-            r = bf16_to_f32(*reinterpret_cast<const uint16_t*>(buf + off));
+            r = bf16_to_f32(*reinterpret_cast<const uint16_t*>(buf + tl * kResRow + d * 2));
           } else {
-            const int off = tl * 64 + ((((d >> 1) >> 4) ^ ((tl >> 2) & 3)) * 16) + ((d >> 1) & 15);
-            const uint32_t byte = buf[off];
+            const uint32_t byte = buf[tl * kResRow4 + (d >> 1)];
             const int code = static_cast<int>(((byte >> (4 * (d & 1))) & 0xFu) ^ 8u) - 8;
-            const uint16_t sc = *reinterpret_cast<const uint16_t*>(buf + 8192 + tl * 8 + (d >> 5) * 2);
+            const uint16_t sc = *reinterpret_cast<const uint16_t*>(buf + tl * kResRow4 + 64 + (d >> 5) * 2);
             r = static_cast<float>(code) * f16_to_f32(sc);
           }
           vacc[tt][nd][e] += r;

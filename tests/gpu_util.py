@@ -21,6 +21,9 @@ def up(a):
 
 
 def down_bf16(t):
+    """bf16 bits (int16 or bfloat16 tensor) -> fp64 numpy."""
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
     return codecs.bf16_decode(t.cpu().numpy().view(np.uint16))
 
 
