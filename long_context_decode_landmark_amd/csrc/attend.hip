@@ -117,26 +117,61 @@ __device__ __forceinline__ constexpr int row_perm32(int pos) {
   return 8 * ((pos >> 2) & 3) + 4 * (pos >> 4) + (pos & 3);
 }
 
+// Softmax state of one wave's 32 tokens for query head j = col: the logits
+// z[t][j] sit in rows t = 16 nt + 4 grp + e of zacc[nt]; returns the
+// unnormalised weights as the MFMA operand whose k slot 8 grp + e' is token
+// 4 grp + e' (e' < 4) or 16 + 4 grp + e' - 4, and the wave's max and sum.
+__device__ __forceinline__ bf16x8 wave_softmax(const f32x4 (&zacc)[2], int nvalid, float scale_log2, int grp,
+                                               float& m, float& lsum) {
+  float p[2][4];
+  m = -__builtin_huge_valf();
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * nt + 4 * grp + e;
+      p[nt][e] = t < nvalid ? zacc[nt][e] * scale_log2 : -__builtin_huge_valf();
+      m = fmaxf(m, p[nt][e]);
+    }
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  const float msafe = m == -__builtin_huge_valf() ? 0.f : m;
+  lsum = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[nt][e] = __builtin_amdgcn_exp2f(p[nt][e] - msafe);
+      lsum += p[nt][e];
+    }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  return pack8(f32x4{p[0][0], p[0][1], p[0][2], p[0][3]}, f32x4{p[1][0], p[1][1], p[1][2], p[1][3]});
+}
+
 // Workgroups per CU the register budget is sized for, and how many stages
 // ahead each wave's coefficient gather runs (compile-time tunables).
 #ifndef LOWRAM_ATT_WG_PER_CU
 #define LOWRAM_ATT_WG_PER_CU 2
 #endif
 #ifndef LOWRAM_ATT_GATHER_AHEAD
-#define LOWRAM_ATT_GATHER_AHEAD 3
+#define LOWRAM_ATT_GATHER_AHEAD 2
 #endif
 #ifndef LOWRAM_ATT_STAGE_AHEAD
 #define LOWRAM_ATT_STAGE_AHEAD 2
 #endif
 
-template <int RANK, bool CI4, bool RI4>
+// STAGES: also write the rebuilt keys and the per-token values (for stage
+// parity checks).  The per-token values need the value MLP's second layer
+// per token, which the output path never forms (see the value section).
+template <int RANK, bool CI4, bool RI4, bool STAGES>
 __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_kernel(const AttendArgs a) {
   __shared__ AttLds L;
   constexpr int NR = RANK / 64;          // basis stages (64 columns of r each)
   constexpr int NM = kHidden / 32;       // MLP stages (32 hidden units each)
   constexpr int NS = NR + NM;
   constexpr int LG = LOWRAM_ATT_GATHER_AHEAD;
-  constexpr int SL = LOWRAM_ATT_STAGE_AHEAD;  // >= 2: stage s + SL is loaded at the top of step s
+  constexpr int SL = LOWRAM_ATT_STAGE_AHEAD;  // stage s + SL is loaded at the top of step s
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, col = lane & 15;
@@ -149,16 +184,17 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
   const uint16_t* qh = a.q + ((size_t)b * a.hq + (size_t)h * g) * kHeadDim;
   unsigned char* buf = L.buf;
 
-  f32x4 zacc[2];
-  bf16x8 vb[8];
-  int nvalid;
+  // every role ends with this wave's softmax state of query head j = col and
+  // o^T[d][j] in rows d = 16 nd + 4 grp + e of oacc[nd]
+  f32x4 oacc[8];
+  float wm, wl;
 
   if (split < a.n_sel_tiles) {
     // ===================================================== selected chunks
     const int chunk0 = split * kAttChunksWG;
     const int nch = min(kAttChunksWG, a.k_eff - chunk0);
     const int32_t* selh = a.sel + head * (size_t)a.k_eff;
-    nvalid = max(0, min(kAttTokWave, (nch - 4 * wave) * kChunk));
+    const int nvalid = max(0, min(kAttTokWave, (nch - 4 * wave) * kChunk));
     // chunk id of selection slot i of this workgroup (clamped into the prefix)
     auto chunk_of = [&](int i) { return min(max(selh[chunk0 + min(i, nch - 1)], 0), a.n_chunks - 1); };
     int tok[2];
@@ -170,7 +206,8 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     //      issued, so that no later wait on them holds the stream's loads
     uint32_t rd = 0;
     if (tid < kAttChunksWG) rd = a.res_desc[head * (size_t)a.n_chunks + chunk_of(tid)];
-    const uint16_t b1v = a.b1[head * kHidden + tid];
+    // b1 in the order the value section reads it: unit 32 c + row_perm32(p) at 32 c + p
+    const uint16_t b1v = a.b1[head * kHidden + (tid & ~31) + row_perm32(tid & 31)];
     const uint16_t b2v = tid < kHeadDim ? a.b2[head * kHeadDim + tid] : 0;
     const int rp0 = (tid & 15) * 4, rq0 = (tid & 31) * 2;
     double fb[4], fo[2];
@@ -183,9 +220,9 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
                  : "memory");
 
     // ---- operand stream: stage s < NR is basis columns [64 s, 64 s + 64)
-    //      (128 rows in pi order, two rows per 256-byte line); stage NR + m
-    //      is W1 rows [32 m, 32 m + 32) (pi order, 8 KiB) then W2 columns
-    //      [32 m, 32 m + 32) (natural, four rows per line, 8 KiB).  Pieces
+    //      (128 rows in pi order, two rows per 256-byte line); stage NR + c
+    //      is W1 rows [32 c, 32 c + 32) (pi order, 8 KiB) then W2 columns
+    //      [32 c, 32 c + 32) (natural, four rows per line, 8 KiB).  Pieces
     //      are XOR-swizzled inside each 256-byte line by the line index.
     const __amdgpu_buffer_rsrc_t bas = buffer_rsrc(a.basis + head * (size_t)kHeadDim * RANK, kHeadDim * RANK * 2);
     const __amdgpu_buffer_rsrc_t w1r = buffer_rsrc(a.w1 + head * (size_t)kHidden * kHeadDim, kHidden * kHeadDim * 2);
@@ -207,11 +244,11 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
 #pragma unroll
         for (int u = 0; u < kStageLd; ++u) r[u] = buffer_ld16(bas, bas_goff, (32 * u * RANK + 64 * s) * 2);
       } else {
-        const int m = s - NR;
+        const int c = s - NR;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) r[u] = buffer_ld16(w1r, w1_goff, (32 * m + 4 * u) * kHeadDim * 2);
+        for (int u = 0; u < 2; ++u) r[u] = buffer_ld16(w1r, w1_goff, (32 * c + 4 * u) * kHeadDim * 2);
 #pragma unroll
-        for (int u = 2; u < 4; ++u) r[u] = buffer_ld16(w2r, w2_goff, ((u - 2) * 64 * kHidden + 32 * m) * 2);
+        for (int u = 2; u < 4; ++u) r[u] = buffer_ld16(w2r, w2_goff, ((u - 2) * 64 * kHidden + 32 * c) * 2);
       }
     };
     auto stage_store = [&](int s, const u32x4 (&r)[kStageLd]) {
@@ -251,7 +288,7 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
       }
     };
 
-    // ---- prologue: stages 0 and 1 in flight, then the first gathers
+    // ---- prologue: the first stages and gathers in flight
     u32x4 sreg[NS + SL][kStageLd];
 #pragma unroll
     for (int s = 0; s < SL && s < NS; ++s) stage_load(s, sreg[s]);
@@ -289,8 +326,8 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
         const int p = CI4 ? 2 * grp + ks : 4 * ks + grp;
         ra[ks][q] = (col >> 1) * 256 + ((((col & 1) ^ q) << 3) | (p ^ (col >> 1))) * 16;
       }
-    // MLP1 A (W1 pi rows 16 hm + col, piece 4 s + grp) and MLP2 B (W2 row
-    // 16 nd + col, piece grp; line 4 nd + col/4)
+    // W1 position row 16 hn + col, piece 4 ks + grp; W2 row 16 nd + col,
+    // piece grp (line 4 nd + col/4)
     int rw1[4], rw2[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) rw1[s] = col * 256 + ((4 * s + grp) ^ col) * 16;
@@ -304,8 +341,9 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 kpre_b[2][4];
-    f32x4 vacc[2][8];
-    u32x4 rres[RI4 ? 3 : 8];  // residual tile pieces of this thread
+    bf16x8 pa;                              // softmax weights (B operand, token slots)
+    f32x4 vacc[STAGES ? 2 : 1][8];          // per-token values (stage output only)
+    u32x4 rres[RI4 ? 3 : 8];                // residual tile pieces of this thread
 
     const size_t row0 = head * (size_t)a.k_eff * kChunk + (size_t)(chunk0 + 4 * wave) * kChunk;
     // residual row of workgroup token tl (< 128), or -1
@@ -318,7 +356,7 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
 
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      // loads for later stages: the stage two ahead, the gather LG ahead,
+      // loads for later stages: the stage SL ahead, the gather LG ahead,
       // and (two stages before the end) the residual tile
       if (s + SL < NS) stage_load(s + SL, sreg[s + SL]);
       if (s + LG < NR) gather(s + LG);
@@ -357,8 +395,8 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
           }
         }
       }
-
       __builtin_amdgcn_sched_barrier(0);  // keep the loads above at the top of the step
+
       const unsigned char* sb = L.buf + (s & 1) * kStage;
       if (s < NR) {
         // ---------------- reconstruction, basis columns [64 s, 64 s + 64)
@@ -382,15 +420,17 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
         if (s == NR - 1) {
           // -------- K_pre done: acc[nt][mt][e] = K_pre[t][d], t = 16 nt + col,
           //          d = 32 (mt / 2) + 8 grp + 4 (mt % 2) + e
-          if (a.kpre_out) {
+          if constexpr (STAGES) {
+            if (a.kpre_out) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-              if (16 * nt + col < nvalid)
+              for (int nt = 0; nt < 2; ++nt)
+                if (16 * nt + col < nvalid)
 #pragma unroll
-                for (int mt = 0; mt < 8; ++mt)
-                  *reinterpret_cast<f32x4*>(a.kpre_out + (row0 + 16 * nt + col) * kHeadDim + 32 * (mt >> 1) +
-                                            8 * grp + 4 * (mt & 1)) = acc[nt][mt];
+                  for (int mt = 0; mt < 8; ++mt)
+                    *reinterpret_cast<f32x4*>(a.kpre_out + (row0 + 16 * nt + col) * kHeadDim + 32 * (mt >> 1) +
+                                              8 * grp + 4 * (mt & 1)) = acc[nt][mt];
             }
+          }
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -413,16 +453,20 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
               }
             }
           }
-          if (a.kpost_out) {
+          if constexpr (STAGES) {
+            if (a.kpost_out) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-              if (16 * nt + col < nvalid)
+              for (int nt = 0; nt < 2; ++nt)
+                if (16 * nt + col < nvalid)
 #pragma unroll
-                for (int mt = 0; mt < 8; ++mt)
-                  *reinterpret_cast<f32x4*>(a.kpost_out + (row0 + 16 * nt + col) * kHeadDim + 32 * (mt >> 1) +
-                                            8 * grp + 4 * (mt & 1)) = acc[nt][mt];
+                  for (int mt = 0; mt < 8; ++mt)
+                    *reinterpret_cast<f32x4*>(a.kpost_out + (row0 + 16 * nt + col) * kHeadDim + 32 * (mt >> 1) +
+                                              8 * grp + 4 * (mt & 1)) = acc[nt][mt];
+            }
           }
-          // QK with K_post rounded to bf16 (2^-9 relative per entry)
+          // QK with K_post rounded to bf16 (2^-9 relative per entry), then
+          // this wave's softmax weights: the value section needs them
+          f32x4 zacc[2];
           {
             bf16x8 qp[4];
 #pragma unroll
@@ -436,46 +480,90 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
               zacc[nt] = z;
             }
           }
+          pa = wave_softmax(zacc, nvalid, a.scale_log2, grp, wm, wl);
 #pragma unroll
-          for (int nd = 0; nd < 8; ++nd) {
-            const float bias = L.b2f[16 * nd + col];
-            vacc[0][nd] = f32x4{bias, bias, bias, bias};
-            vacc[1][nd] = vacc[0][nd];
+          for (int nd = 0; nd < 8; ++nd) oacc[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (STAGES) {
+#pragma unroll
+            for (int nd = 0; nd < 8; ++nd) {
+              const float bias = L.b2f[16 * nd + col];
+              vacc[0][nd] = f32x4{bias, bias, bias, bias};
+              vacc[1][nd] = vacc[0][nd];
+            }
           }
         }
       } else {
-        // ---------------- value MLP, hidden units [32 m, 32 m + 32):
-        //                  MLP1 (b1 as the initial value) -> GELU -> bf16 -> MLP2
-        const int m = s - NR;
-        f32x4 hacc[2][2];
+        // ---------------- values, hidden units [32 c, 32 c + 32).  With p the
+        // softmax weights, sum_t p_t V_t = W2 (sum_t p_t gelu(W1 K_t + b1))
+        // + b2 sum_t p_t + sum_t p_t R_t: the hidden activations are
+        // contracted over this wave's tokens first, so W2 is applied to
+        // one row per query head instead of one per token.
+        //   MLP1  D[t][h] = K_pre[t][d] x W1^T[d][h]   (b1 initial value)
+        //   PH    D[h][j] = gelu(hid)^T[h][t] x p^T[t][j]
+        //   OUT   D[d][j] += W2[d][h] x PH[h][j]
+        const int c = s - NR;
+        f32x4 hacc[2][2];  // [token tile][hidden tile]
 #pragma unroll
-        for (int hm = 0; hm < 2; ++hm) {
-          const f32x4 bias = *reinterpret_cast<const f32x4*>(&L.b1f[32 * m + 8 * grp + 4 * hm]);
-          hacc[hm][0] = bias;
-          hacc[hm][1] = bias;
+        for (int hn = 0; hn < 2; ++hn) {
+          const float bias = L.b1f[32 * c + 16 * hn + col];
+          hacc[0][hn] = f32x4{bias, bias, bias, bias};
+          hacc[1][hn] = hacc[0][hn];
         }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-          for (int hm = 0; hm < 2; ++hm) {
-            const bf16x8 aop = lds16(sb, rw1[ks] + 4096 * hm);
-            hacc[hm][0] = mfma16(aop, kpre_b[0][ks], hacc[hm][0]);
-            hacc[hm][1] = mfma16(aop, kpre_b[1][ks], hacc[hm][1]);
+          for (int hn = 0; hn < 2; ++hn) {
+            const bf16x8 bop = lds16(sb, rw1[ks] + 4096 * hn);
+            hacc[0][hn] = mfma16(kpre_b[0][ks], bop, hacc[0][hn]);
+            hacc[1][hn] = mfma16(kpre_b[1][ks], bop, hacc[1][hn]);
           }
         }
 #pragma unroll
-        for (int hm = 0; hm < 2; ++hm)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+          for (int hn = 0; hn < 2; ++hn)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hacc[hm][nt][e] = gelu_fast(hacc[hm][nt][e]);
-        const bf16x8 ha0 = pack8(hacc[0][0], hacc[1][0]);
-        const bf16x8 ha1 = pack8(hacc[0][1], hacc[1][1]);
+            for (int e = 0; e < 4; ++e) hacc[tt][hn][e] = gelu_fast(hacc[tt][hn][e]);
+        f32x4 pht[2];
 #pragma unroll
-        for (int nd = 0; nd < 8; ++nd) {
-          const bf16x8 bop = lds16(sb, rw2[nd & 3] + 1024 * nd);
-          vacc[0][nd] = mfma16(ha0, bop, vacc[0][nd]);
-          vacc[1][nd] = mfma16(ha1, bop, vacc[1][nd]);
+        for (int hn = 0; hn < 2; ++hn)
+          pht[hn] = mfma16(pack8(hacc[0][hn], hacc[1][hn]), pa, f32x4{0.f, 0.f, 0.f, 0.f});
+        const bf16x8 hb = pack8(pht[0], pht[1]);
+#pragma unroll
+        for (int nd = 0; nd < 8; ++nd) oacc[nd] = mfma16(lds16(sb, rw2[nd & 3] + 1024 * nd), hb, oacc[nd]);
+
+        if constexpr (STAGES) {
+          // per-token values for the stage output: MLP1 again as D[h][t]
+          // (W1 as the A operand), GELU, then D[t][d] = hid x W2^T
+          f32x4 hq[2][2];  // [hidden tile][token tile]
+#pragma unroll
+          for (int hm = 0; hm < 2; ++hm) {
+            const f32x4 bias = *reinterpret_cast<const f32x4*>(&L.b1f[32 * c + 16 * hm + 4 * grp]);
+            hq[hm][0] = bias;
+            hq[hm][1] = bias;
+          }
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int hm = 0; hm < 2; ++hm) {
+              const bf16x8 aop = lds16(sb, rw1[ks] + 4096 * hm);
+              hq[hm][0] = mfma16(aop, kpre_b[0][ks], hq[hm][0]);
+              hq[hm][1] = mfma16(aop, kpre_b[1][ks], hq[hm][1]);
+            }
+#pragma unroll
+          for (int hm = 0; hm < 2; ++hm)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) hq[hm][nt][e] = gelu_fast(hq[hm][nt][e]);
+          const bf16x8 ha0 = pack8(hq[0][0], hq[1][0]);
+          const bf16x8 ha1 = pack8(hq[0][1], hq[1][1]);
+#pragma unroll
+          for (int nd = 0; nd < 8; ++nd) {
+            const bf16x8 bop = lds16(sb, rw2[nd & 3] + 1024 * nd);
+            vacc[0][nd] = mfma16(ha0, bop, vacc[0][nd]);
+            vacc[1][nd] = mfma16(ha1, bop, vacc[1][nd]);
+          }
         }
       }
       if (s + 1 < NS) {
@@ -484,7 +572,7 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
       }
     }
 
-    // ---- residual tile -> LDS (both buffers), then add to the values
+    // ---- residual tile -> LDS (rows of kResRow / kResRow4 bytes)
     __syncthreads();
     if constexpr (!RI4) {
 #pragma unroll
@@ -502,49 +590,57 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
         *reinterpret_cast<u32x2*>(buf + (tid >> 1) * kResRow4 + 64) = u32x2{rres[2][0], rres[2][1]};
     }
     __syncthreads();
+    // residual of wave token t (< 32) at dimension d, as a float
+    auto resid_at = [&](int t, int d) -> float {
+      const int tl = 32 * wave + t;
+      if constexpr (!RI4) {
+        return bf16_to_f32(*reinterpret_cast<const uint16_t*>(buf + tl * kResRow + d * 2));
+      } else {
+        const uint32_t byte = buf[tl * kResRow4 + (d >> 1)];
+        const int code = static_cast<int>(((byte >> (4 * (d & 1))) & 0xFu) ^ 8u) - 8;
+        const uint16_t sc = *reinterpret_cast<const uint16_t*>(buf + tl * kResRow4 + 64 + (d >> 5) * 2);
+        return static_cast<float>(code) * f16_to_f32(sc);
+      }
+    };
+    // OUT += R^T[d][t] x p^T[t][j] (token slots as in the softmax operand)
+    // and b2[d] * sum_t p_t
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int nd = 0; nd < 8; ++nd) {
+      f32x4 lo, hi;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int tl = 32 * wave + 16 * tt + 4 * grp + e;
-#pragma unroll
-        for (int nd = 0; nd < 8; ++nd) {
-          const int d = 16 * nd + col;
-          float r;
-          if constexpr (!RI4) {
-            r = bf16_to_f32(*reinterpret_cast<const uint16_t*>(buf + tl * kResRow + d * 2));
-          } else {
-            const uint32_t byte = buf[tl * kResRow4 + (d >> 1)];
-            const int code = static_cast<int>(((byte >> (4 * (d & 1))) & 0xFu) ^ 8u) - 8;
-            const uint16_t sc = *reinterpret_cast<const uint16_t*>(buf + tl * kResRow4 + 64 + (d >> 5) * 2);
-            r = static_cast<float>(code) * f16_to_f32(sc);
-          }
-          vacc[tt][nd][e] += r;
-        }
+        lo[e] = resid_at(4 * grp + e, 16 * nd + col);
+        hi[e] = resid_at(16 + 4 * grp + e, 16 * nd + col);
       }
-    if (a.vhat_out) {
+      oacc[nd] = mfma16(pack8(lo, hi), pa, oacc[nd]);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * tt + 4 * grp + e;
-          if (t < nvalid)
-#pragma unroll
-            for (int nd = 0; nd < 8; ++nd) a.vhat_out[(row0 + t) * kHeadDim + 16 * nd + col] = vacc[tt][nd][e];
-        }
+      for (int e = 0; e < 4; ++e) oacc[nd][e] = fmaf(L.b2f[16 * nd + 4 * grp + e], wl, oacc[nd][e]);
     }
+    if constexpr (STAGES) {
+      if (a.vhat_out) {
 #pragma unroll
-    for (int nd = 0; nd < 8; ++nd) vb[nd] = pack8(vacc[0][nd], vacc[1][nd]);
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 16 * tt + 4 * grp + e;
+            if (t < nvalid)
+#pragma unroll
+              for (int nd = 0; nd < 8; ++nd)
+                a.vhat_out[(row0 + t) * kHeadDim + 16 * nd + col] = vacc[tt][nd][e] + resid_at(t, 16 * nd + col);
+          }
+      }
+    }
   } else {
     // ========================================================= exact window
     const int w0 = (split - a.n_sel_tiles) * kAttTokWG + wave * kAttTokWave;
-    nvalid = max(0, min(kAttTokWave, a.window - w0));
+    const int nvalid = max(0, min(kAttTokWave, a.window - w0));
     const uint16_t* kw = a.win_k + head * (size_t)a.window * kHeadDim;
     const uint16_t* vw = a.win_v + head * (size_t)a.window * kHeadDim;
     bf16x8 qn[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       qn[s] = col < g ? load_bf16x8(qh + col * kHeadDim + 32 * s + 8 * grp) : zero_bf16x8();
+    f32x4 zacc[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int t = min(w0 + 16 * nt + col, a.window - 1);
@@ -553,50 +649,19 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
       for (int s = 0; s < 4; ++s) z = mfma16(load_bf16x8(kw + (size_t)t * kHeadDim + 32 * s + 8 * grp), qn[s], z);
       zacc[nt] = z;
     }
+    // V^T[d][t] as the A operand: dimension d = 16 nd + col, token slots
+    bf16x8 vt[8];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      bf16x8 v;
+    for (int nd = 0; nd < 8; ++nd) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int t = min(w0 + 16 * (e >> 2) + 4 * grp + (e & 3), a.window - 1);
-        v[e] = __builtin_bit_cast(__bf16, vw[(size_t)t * kHeadDim + 16 * nt + col]);
+        vt[nd][e] = __builtin_bit_cast(__bf16, vw[(size_t)t * kHeadDim + 16 * nd + col]);
       }
-      vb[nt] = v;
     }
-  }
-
-  // ============================================= softmax + PV (both roles)
-  float p[2][4];
-  float m = -__builtin_huge_valf();
+    const bf16x8 pa = wave_softmax(zacc, nvalid, a.scale_log2, grp, wm, wl);
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 16 * nt + 4 * grp + e;
-      p[nt][e] = t < nvalid ? zacc[nt][e] * a.scale_log2 : -__builtin_huge_valf();
-      m = fmaxf(m, p[nt][e]);
-    }
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  const float msafe = m == -__builtin_huge_valf() ? 0.f : m;
-  float lsum = 0.f;
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      p[nt][e] = __builtin_amdgcn_exp2f(p[nt][e] - msafe);
-      lsum += p[nt][e];
-    }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  const bf16x8 pa = pack8(f32x4{p[0][0], p[0][1], p[0][2], p[0][3]},
-                          f32x4{p[1][0], p[1][1], p[1][2], p[1][3]});
-  f32x4 oacc[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    o = mfma16(pa, vb[nt], o);
-    oacc[nt] = o;
+    for (int nd = 0; nd < 8; ++nd) oacc[nd] = mfma16(vt[nd], pa, f32x4{0.f, 0.f, 0.f, 0.f});
   }
 
   // ======================================== merge the 4 waves, write partial
@@ -604,12 +669,11 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
   float* mo = reinterpret_cast<float*>(buf);  // 32 KiB: 4 waves x 16 heads x 128
   float* ml = L.ml;
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) mo[(wave * 16 + 4 * grp + e) * kHeadDim + 16 * nt + col] = oacc[nt][e];
+  for (int nd = 0; nd < 8; ++nd)
+    *reinterpret_cast<f32x4*>(&mo[(wave * 16 + col) * kHeadDim + 16 * nd + 4 * grp]) = oacc[nd];
   if (grp == 0) {
-    ml[wave * 16 + col] = m;
-    ml[kAttWaves * 16 + wave * 16 + col] = lsum;
+    ml[wave * 16 + col] = wm;
+    ml[kAttWaves * 16 + wave * 16 + col] = wl;
   }
   __syncthreads();
   float* part = a.part + (head * (size_t)a.n_split + split) * g * kPartStride;
@@ -632,33 +696,38 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     }
     part[j * kPartStride + 2 + d] = o;
   }
-
 }
 
-template <int RANK>
+template <int RANK, bool STAGES>
 static hipError_t launch_rank(const AttendArgs& a, bool ci4, bool ri4, hipStream_t st) {
   const dim3 grid(a.padded_total), block(kAttWaves * 64);
-  if (!ci4 && !ri4) hipLaunchKernelGGL((attend_kernel<RANK, false, false>), grid, block, 0, st, a);
-  else if (ci4 && ri4) hipLaunchKernelGGL((attend_kernel<RANK, true, true>), grid, block, 0, st, a);
-  else if (ci4) hipLaunchKernelGGL((attend_kernel<RANK, true, false>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((attend_kernel<RANK, false, true>), grid, block, 0, st, a);
+  if (!ci4 && !ri4) hipLaunchKernelGGL((attend_kernel<RANK, false, false, STAGES>), grid, block, 0, st, a);
+  else if (ci4 && ri4) hipLaunchKernelGGL((attend_kernel<RANK, true, true, STAGES>), grid, block, 0, st, a);
+  else if (ci4) hipLaunchKernelGGL((attend_kernel<RANK, true, false, STAGES>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((attend_kernel<RANK, false, true, STAGES>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attend(const AttendArgs& a, int rank, bool ci4, bool ri4, hipStream_t st) {
-  if (a.total == 0) return hipSuccess;
+template <bool STAGES>
+static hipError_t launch_attend_t(const AttendArgs& a, int rank, bool ci4, bool ri4, hipStream_t st) {
   switch (rank) {
-    case 128: return launch_rank<128>(a, ci4, ri4, st);
-    case 256: return launch_rank<256>(a, ci4, ri4, st);
-    case 512: return launch_rank<512>(a, ci4, ri4, st);
+    case 128: return launch_rank<128, STAGES>(a, ci4, ri4, st);
+    case 256: return launch_rank<256, STAGES>(a, ci4, ri4, st);
+    case 512: return launch_rank<512, STAGES>(a, ci4, ri4, st);
     default: break;
   }
   // rank 64: the int4 path needs rank % 128 == 0 and is not instantiated here
   if (ci4) return hipErrorInvalidValue;
   const dim3 grid(a.padded_total), block(kAttWaves * 64);
-  if (ri4) hipLaunchKernelGGL((attend_kernel<64, false, true>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((attend_kernel<64, false, false>), grid, block, 0, st, a);
+  if (ri4) hipLaunchKernelGGL((attend_kernel<64, false, true, STAGES>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((attend_kernel<64, false, false, STAGES>), grid, block, 0, st, a);
   return hipGetLastError();
+}
+
+hipError_t launch_attend(const AttendArgs& a, int rank, bool ci4, bool ri4, hipStream_t st) {
+  if (a.total == 0) return hipSuccess;
+  if (a.kpre_out || a.kpost_out || a.vhat_out) return launch_attend_t<true>(a, rank, ci4, ri4, st);
+  return launch_attend_t<false>(a, rank, ci4, ri4, st);
 }
 
 // ---------------------------------------------------------------------------
