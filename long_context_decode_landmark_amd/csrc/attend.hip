@@ -94,6 +94,7 @@ struct AttLds {
   float b2f[kHeadDim];
   float ml[2 * kAttWaves * 16];
   uint32_t rdesc[kAttChunksWG];
+  alignas(16) uint16_t qs[16][kHeadDim];  // this KV head's query rows
 };
 
 // int4 x 8 (one 32-bit word, element e in bits 4e..4e+3) times scale -> bf16x8
@@ -197,28 +198,6 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     const int nvalid = max(0, min(kAttTokWave, (nch - 4 * wave) * kChunk));
     // chunk id of selection slot i of this workgroup (clamped into the prefix)
     auto chunk_of = [&](int i) { return min(max(selh[chunk0 + min(i, nch - 1)], 0), a.n_chunks - 1); };
-    int tok[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) tok[nt] = chunk_of(4 * wave + 2 * nt + (col >> 3)) * kChunk + (col & 7);
-    const int rope_chunk = chunk_of(tid >> 4);  // chunk whose RoPE base row this thread fills
-
-    // ---- small loads first, and waited for before the operand stream is
-    //      issued, so that no later wait on them holds the stream's loads
-    uint32_t rd = 0;
-    if (tid < kAttChunksWG) rd = a.res_desc[head * (size_t)a.n_chunks + chunk_of(tid)];
-    // b1 in the order the value section reads it: unit 32 c + row_perm32(p) at 32 c + p
-    const uint16_t b1v = a.b1[head * kHidden + (tid & ~31) + row_perm32(tid & 31)];
-    const uint16_t b2v = tid < kHeadDim ? a.b2[head * kHeadDim + tid] : 0;
-    const int rp0 = (tid & 15) * 4, rq0 = (tid & 31) * 2;
-    double fb[4], fo[2];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) fb[p] = a.inv_freq[rp0 + p];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) fo[p] = a.inv_freq[rq0 + p];
-    asm volatile("" ::"v"(rd), "v"(b1v), "v"(b2v), "v"(rope_chunk), "v"(fb[0]), "v"(fb[1]), "v"(fb[2]),
-                 "v"(fb[3]), "v"(fo[0]), "v"(fo[1]), "v"(tok[0]), "v"(tok[1])
-                 : "memory");
-
     // ---- operand stream: stage s < NR is basis columns [64 s, 64 s + 64)
     //      (128 rows in pi order, two rows per 256-byte line); stage NR + c
     //      is W1 rows [32 c, 32 c + 32) (pi order, 8 KiB) then W2 columns
@@ -264,6 +243,8 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
       }
     };
 
+    int tok[2];  // this lane's token rows (set in the prologue)
+
     // ---- coefficient gather of stage s (< NR): k-steps 2 s, 2 s + 1
     bf16x8 cv[CI4 ? 1 : NR][2][2];
     u32x2 cq[CI4 ? NR : 1][2];
@@ -288,10 +269,33 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
       }
     };
 
-    // ---- prologue: the first stages and gathers in flight
+    // ---- prologue.  One memory round trip before the stream starts: the
+    //      first stages, biases, queries, RoPE frequencies and this
+    //      workgroup's chunk ids are loaded together and waited for at once;
+    //      then the gathers (which need the chunk ids) and the residual
+    //      descriptors go out.
     u32x4 sreg[NS + SL][kStageLd];
 #pragma unroll
     for (int s = 0; s < SL && s < NS; ++s) stage_load(s, sreg[s]);
+    // b1 in the order the value section reads it: unit 32 c + row_perm32(p) at 32 c + p
+    const uint16_t b1v = a.b1[head * kHidden + (tid & ~31) + row_perm32(tid & 31)];
+    const uint16_t b2v = tid < kHeadDim ? a.b2[head * kHeadDim + tid] : 0;
+    const u32x4 qv = tid < 16 * g ? *reinterpret_cast<const u32x4*>(qh + 8 * tid) : u32x4{0u, 0u, 0u, 0u};
+    const int rp0 = (tid & 15) * 4, rq0 = (tid & 31) * 2;
+    double fb[4], fo[2];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) fb[p] = a.inv_freq[rp0 + p];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) fo[p] = a.inv_freq[rq0 + p];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) tok[nt] = chunk_of(4 * wave + 2 * nt + (col >> 3)) * kChunk + (col & 7);
+    const int rope_chunk = chunk_of(tid >> 4);  // chunk whose RoPE base row this thread fills
+    const int rd_chunk = chunk_of(tid & (kAttChunksWG - 1));
+    asm volatile("" ::"v"(b1v), "v"(b2v), "v"(qv), "v"(rope_chunk), "v"(rd_chunk), "v"(fb[0]), "v"(fb[1]),
+                 "v"(fb[2]), "v"(fb[3]), "v"(fo[0]), "v"(fo[1]), "v"(tok[0]), "v"(tok[1])
+                 : "memory");
+    uint32_t rd = 0;
+    if (tid < kAttChunksWG) rd = a.res_desc[head * (size_t)a.n_chunks + rd_chunk];
 #pragma unroll
     for (int s = 0; s < LG && s < NR; ++s) gather(s);
     __builtin_amdgcn_sched_barrier(0);
@@ -308,9 +312,9 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
 #pragma unroll
       for (int p = 0; p < 2; ++p) L.rope_off[i][rq0 + p] = rot_of((double)i * fo[p]);
     }
-    if (tid < kAttChunksWG) L.rdesc[tid] = rd;
     L.b1f[tid] = bf16_to_f32(b1v);
     if (tid < kHeadDim) L.b2f[tid] = bf16_to_f32(b2v);
+    if (tid < 16 * g) *reinterpret_cast<u32x4*>(&L.qs[tid >> 4][8 * (tid & 15)]) = qv;
     stage_store(0, sreg[0]);
     __syncthreads();
 
@@ -471,7 +475,8 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
             bf16x8 qp[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-              qp[ks] = col < g ? load_bf16x8(qh + col * kHeadDim + 32 * ks + 8 * grp) : zero_bf16x8();
+              qp[ks] = col < g ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&L.qs[col][32 * ks + 8 * grp]))
+                               : zero_bf16x8();
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
               f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -566,6 +571,7 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
           }
         }
       }
+      if (s == 0 && tid < kAttChunksWG) L.rdesc[tid] = rd;  // first read at step NS - 2
       if (s + 1 < NS) {
         stage_store(s + 1, sreg[s + 1]);  // into the buffer step s - 1 read
         __syncthreads();
@@ -606,13 +612,23 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     // and b2[d] * sum_t p_t
 #pragma unroll
     for (int nd = 0; nd < 8; ++nd) {
-      f32x4 lo, hi;
+      bf16x8 rop;
+      if constexpr (!RI4) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo[e] = resid_at(4 * grp + e, 16 * nd + col);
-        hi[e] = resid_at(16 + 4 * grp + e, 16 * nd + col);
+        for (int e = 0; e < 8; ++e) {
+          const int tl = 32 * wave + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+          rop[e] = *reinterpret_cast<const __bf16*>(buf + tl * kResRow + (16 * nd + col) * 2);
+        }
+      } else {
+        f32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = resid_at(4 * grp + e, 16 * nd + col);
+          hi[e] = resid_at(16 + 4 * grp + e, 16 * nd + col);
+        }
+        rop = pack8(lo, hi);
       }
-      oacc[nd] = mfma16(pack8(lo, hi), pa, oacc[nd]);
+      oacc[nd] = mfma16(rop, pa, oacc[nd]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) oacc[nd][e] = fmaf(L.b2f[16 * nd + 4 * grp + e], wl, oacc[nd][e]);
     }
