@@ -101,8 +101,8 @@ constexpr int kResRow = 272;   // LDS stride of a bf16 residual row (256 + 16: r
 constexpr int kResRow4 = 80;   // int4 residual row: 64 bytes of codes, 8 of scales, 8 unused
 
 struct AttLds {
-  // stage ring; then the residual tile (128 rows of kResRow); then the wave merge
-  alignas(16) unsigned char buf[2 * kStage > 128 * kResRow ? 2 * kStage : 128 * kResRow];
+  // stage ring; then the residual tile (one row of kResRow per token); then the wave merge
+  alignas(16) unsigned char buf[2 * kStage > 8 * kAttChunksWG * kResRow ? 2 * kStage : 8 * kAttChunksWG * kResRow];
   float2 rope_off[kChunk][65];  // padded: the 8 offsets of one frequency fall on distinct banks
   float2 rope_base[kAttChunksWG][64];
   float b1f[kHidden];
@@ -133,16 +133,18 @@ __device__ __forceinline__ constexpr int row_perm32(int pos) {
   return 8 * ((pos >> 2) & 3) + 4 * (pos >> 4) + (pos & 3);
 }
 
-// Softmax state of one wave's 32 tokens for query head j = col: the logits
-// z[t][j] sit in rows t = 16 nt + 4 grp + e of zacc[nt]; returns the
-// unnormalised weights as the MFMA operand whose k slot 8 grp + e' is token
-// 4 grp + e' (e' < 4) or 16 + 4 grp + e' - 4, and the wave's max and sum.
-__device__ __forceinline__ bf16x8 wave_softmax(const f32x4 (&zacc)[2], int nvalid, float scale_log2, int grp,
-                                               float& m, float& lsum) {
-  float p[2][4];
+// Softmax state of one wave's 16 NT tokens for query head j = col: the logits
+// z[t][j] sit in rows t = 16 nt + 4 grp + e of zacc[nt].  Returns the wave's
+// max and sum and the unnormalised weights as NT / 2 MFMA operands; in
+// operand q, k slot 8 grp + e' is token 32 q + 4 grp + e' (e' < 4) or
+// 32 q + 16 + 4 grp + e' - 4.
+template <int NT>
+__device__ __forceinline__ void wave_softmax(const f32x4 (&zacc)[NT], int nvalid, float scale_log2, int grp,
+                                             float& m, float& lsum, bf16x8 (&pa)[NT / 2]) {
+  float p[NT][4];
   m = -__builtin_huge_valf();
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 16 * nt + 4 * grp + e;
@@ -154,7 +156,7 @@ __device__ __forceinline__ bf16x8 wave_softmax(const f32x4 (&zacc)[2], int nvali
   const float msafe = m == -__builtin_huge_valf() ? 0.f : m;
   lsum = 0.f;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       p[nt][e] = __builtin_amdgcn_exp2f(p[nt][e] - msafe);
@@ -162,13 +164,16 @@ __device__ __forceinline__ bf16x8 wave_softmax(const f32x4 (&zacc)[2], int nvali
     }
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  return pack8(f32x4{p[0][0], p[0][1], p[0][2], p[0][3]}, f32x4{p[1][0], p[1][1], p[1][2], p[1][3]});
+#pragma unroll
+  for (int q = 0; q < NT / 2; ++q)
+    pa[q] = pack8(f32x4{p[2 * q][0], p[2 * q][1], p[2 * q][2], p[2 * q][3]},
+                  f32x4{p[2 * q + 1][0], p[2 * q + 1][1], p[2 * q + 1][2], p[2 * q + 1][3]});
 }
 
 // Workgroups per CU the register budget is sized for, and how many stages
 // ahead each wave's coefficient gather runs (compile-time tunables).
 #ifndef LOWRAM_ATT_WG_PER_CU
-#define LOWRAM_ATT_WG_PER_CU 2
+#define LOWRAM_ATT_WG_PER_CU (kAttSelNT >= 4 ? 1 : 2)
 #endif
 #ifndef LOWRAM_ATT_GATHER_AHEAD
 #define LOWRAM_ATT_GATHER_AHEAD 2
@@ -188,6 +193,9 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
   constexpr int NS = NR + NM;
   constexpr int LG = LOWRAM_ATT_GATHER_AHEAD;
   constexpr int SL = LOWRAM_ATT_STAGE_AHEAD;  // stage s + SL is loaded at the top of step s
+  constexpr int NT = kAttSelNT;               // 16-token tiles per wave (selected chunks)
+  constexpr int TOKW = 16 * NT;               // tokens per wave
+  constexpr int CPW = TOKW / kChunk;          // chunks per wave
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, col = lane & 15;
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     const int chunk0 = split * kAttChunksWG;
     const int nch = min(kAttChunksWG, a.k_eff - chunk0);
     const int32_t* selh = a.sel + head * (size_t)a.k_eff;
-    const int nvalid = max(0, min(kAttTokWave, (nch - 4 * wave) * kChunk));
+    const int nvalid = max(0, min(TOKW, (nch - CPW * wave) * kChunk));
     // chunk id of selection slot i of this workgroup (clamped into the prefix)
     auto chunk_of = [&](int i) { return min(max(selh[chunk0 + min(i, nch - 1)], 0), a.n_chunks - 1); };
     // ---- operand stream: stage s < NR is basis columns [64 s, 64 s + 64)
@@ -258,26 +266,26 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
       }
     };
 
-    int tok[2];  // this lane's token rows (set in the prologue)
+    int tok[NT];  // this lane's token rows (set in the prologue)
 
     // ---- coefficient gather of stage s (< NR): k-steps 2 s, 2 s + 1
-    bf16x8 cv[CI4 ? 1 : NR][2][2];
-    u32x2 cq[CI4 ? NR : 1][2];
-    float csc[CI4 ? NR : 1][2];
+    bf16x8 cv[CI4 ? 1 : NR][2][NT];
+    u32x2 cq[CI4 ? NR : 1][NT];
+    float csc[CI4 ? NR : 1][NT];
     auto gather = [&](int s) {
       if constexpr (!CI4) {
         const uint16_t* cb = static_cast<const uint16_t*>(a.coeff) + (size_t)b * a.prefix * RANK;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+          for (int nt = 0; nt < NT; ++nt)
             cv[s][ks][nt] = load_bf16x8(cb + (size_t)tok[nt] * RANK + 64 * s + 32 * ks + 8 * grp);
       } else {
         // 16 codes r = 64 s + 16 grp .. + 15 and their group scale
         const uint8_t* cb = static_cast<const uint8_t*>(a.coeff) + (size_t)b * a.prefix * (RANK / 2);
         const uint16_t* sb = a.coeff_scale + (size_t)b * a.prefix * (RANK / 32);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
           cq[s][nt] = *reinterpret_cast<const u32x2*>(cb + (size_t)tok[nt] * (RANK / 2) + 32 * s + 8 * grp);
           csc[s][nt] = f16_to_f32(sb[(size_t)tok[nt] * (RANK / 32) + 2 * s + (grp >> 1)]);
         }
@@ -296,19 +304,23 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     const uint16_t b1v = a.b1[head * kHidden + (tid & ~31) + row_perm32(tid & 31)];
     const uint16_t b2v = tid < kHeadDim ? a.b2[head * kHeadDim + tid] : 0;
     const u32x4 qv = tid < 16 * g ? *reinterpret_cast<const u32x4*>(qh + 8 * tid) : u32x4{0u, 0u, 0u, 0u};
-    const int rp0 = (tid & 15) * 4, rq0 = (tid & 31) * 2;
-    double fb[4], fo[2];
+    constexpr int PPT = kAttChunksWG / 4;  // RoPE base entries per thread (chunks x 64 / 256)
+    const int rp0 = (tid % (64 / PPT)) * PPT, rq0 = (tid & 31) * 2;
+    double fb[PPT], fo[2];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) fb[p] = a.inv_freq[rp0 + p];
+    for (int p = 0; p < PPT; ++p) fb[p] = a.inv_freq[rp0 + p];
 #pragma unroll
     for (int p = 0; p < 2; ++p) fo[p] = a.inv_freq[rq0 + p];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) tok[nt] = chunk_of(4 * wave + 2 * nt + (col >> 3)) * kChunk + (col & 7);
-    const int rope_chunk = chunk_of(tid >> 4);  // chunk whose RoPE base row this thread fills
+    for (int nt = 0; nt < NT; ++nt) tok[nt] = chunk_of(CPW * wave + 2 * nt + (col >> 3)) * kChunk + (col & 7);
+    const int rope_chunk = chunk_of(tid / (64 / PPT));  // chunk whose RoPE base row this thread fills
     const int rd_chunk = chunk_of(tid & (kAttChunksWG - 1));
-    asm volatile("" ::"v"(b1v), "v"(b2v), "v"(qv), "v"(rope_chunk), "v"(rd_chunk), "v"(fb[0]), "v"(fb[1]),
-                 "v"(fb[2]), "v"(fb[3]), "v"(fo[0]), "v"(fo[1]), "v"(tok[0]), "v"(tok[1])
+    asm volatile("" ::"v"(b1v), "v"(b2v), "v"(qv), "v"(rope_chunk), "v"(rd_chunk), "v"(fo[0]), "v"(fo[1])
                  : "memory");
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) asm volatile("" ::"v"(fb[p]) : "memory");
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) asm volatile("" ::"v"(tok[nt]) : "memory");
     uint32_t rd = 0;
     if (tid < kAttChunksWG) rd = a.res_desc[head * (size_t)a.n_chunks + rd_chunk];
 #pragma unroll
@@ -319,10 +331,10 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     // fly): base angle of every chunk start, reduced in fp64, and the
     // offsets 0..7 inside a chunk
     {
-      const int cs = tid >> 4;
+      const int cs = tid / (64 / PPT);
       const double pos = (double)rope_chunk * kChunk;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) L.rope_base[cs][rp0 + p] = rot_of(pos * fb[p]);
+      for (int p = 0; p < PPT; ++p) L.rope_base[cs][rp0 + p] = rot_of(pos * fb[p]);
       const int i = tid >> 5;
 #pragma unroll
       for (int p = 0; p < 2; ++p) L.rope_off[i][rq0 + p] = rot_of((double)i * fo[p]);
@@ -354,17 +366,18 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     for (int q = 0; q < 4; ++q)
       rw2[q] = 8192 + (col >> 2) * 256 + ((((col & 3) ^ q) << 2) | (grp ^ (col >> 2))) * 16;
 
-    f32x4 acc[2][8];
+    f32x4 acc[NT][8];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 kpre_b[2][4];
-    bf16x8 pa;                              // softmax weights (B operand, token slots)
-    f32x4 vacc[STAGES ? 2 : 1][8];          // per-token values (stage output only)
-    u32x4 rres[RI4 ? 3 : 8];                // residual tile pieces of this thread
+    bf16x8 kpre_b[NT][4];
+    bf16x8 pa[NT / 2];                      // softmax weights (B operand, token slots)
+    f32x4 vacc[STAGES ? NT : 1][8];         // per-token values (stage output only)
+    constexpr int RL = RI4 ? kAttChunksWG / 8 : kAttChunksWG / 2;  // residual pieces per thread
+    u32x4 rres[RI4 ? RL + 1 : RL];
 
-    const size_t row0 = head * (size_t)a.k_eff * kChunk + (size_t)(chunk0 + 4 * wave) * kChunk;
+    const size_t row0 = head * (size_t)a.k_eff * kChunk + (size_t)(chunk0 + CPW * wave) * kChunk;
     // residual row of workgroup token tl (< 128), or -1
     auto resid_row = [&](int tl) -> int {
       const uint32_t dsc = L.rdesc[tl >> 3];
@@ -387,7 +400,7 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
           const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(
               static_cast<const uint16_t*>(a.res_val) + head * (size_t)a.n_resid * kHeadDim, nbytes);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
+          for (int u = 0; u < RL; ++u) {
             const int tl = 16 * u + (tid >> 4);
             const int rn = resid_row(tl);
             rres[u] = buffer_ld16(rv, rn >= 0 ? (uint32_t)rn * 256 + (tid & 15) * 16 : nbytes, 0);
@@ -401,16 +414,22 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
           const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
               a.res_scale + head * (size_t)a.n_resid * (kHeadDim / 32), sbytes);
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
+          for (int u = 0; u < RL; ++u) {
             const int tl = 64 * u + (tid >> 2);
             const int rn = resid_row(tl);
             rres[u] = buffer_ld16(rv, rn >= 0 ? (uint32_t)rn * 64 + (tid & 3) * 16 : nbytes, 0);
           }
           {
+            // scales: 8 bytes per token, threads 2 t and 2 t + 1 (and 2 t + 256...) share token t
             const int tl = tid >> 1;
             const int rn = resid_row(tl);
             const u32x2 sc = __builtin_amdgcn_raw_buffer_load_b64(rs, rn >= 0 ? (uint32_t)rn * 8 : sbytes, 0, 0);
-            rres[2] = u32x4{sc[0], sc[1], 0u, 0u};
+            u32x2 sc2 = {0u, 0u};
+            if constexpr (kAttChunksWG * 8 > 128) {
+              const int rn2 = resid_row(tl + 128);
+              sc2 = __builtin_amdgcn_raw_buffer_load_b64(rs, rn2 >= 0 ? (uint32_t)rn2 * 8 : sbytes, 0, 0);
+            }
+            rres[RL] = u32x4{sc[0], sc[1], sc2[0], sc2[1]};
           }
         }
       }
@@ -421,19 +440,17 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
         // ---------------- reconstruction, basis columns [64 s, 64 s + 64)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          bf16x8 bop[2];
-          if constexpr (!CI4) {
-            bop[0] = cv[s][ks][0];
-            bop[1] = cv[s][ks][1];
-          } else {
-            bop[0] = dequant8(cq[s][0][ks], csc[s][0]);
-            bop[1] = dequant8(cq[s][1][ks], csc[s][1]);
+          bf16x8 bop[NT];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            if constexpr (!CI4) bop[nt] = cv[s][ks][nt];
+            else bop[nt] = dequant8(cq[s][nt][ks], csc[s][nt]);
           }
 #pragma unroll
           for (int mt = 0; mt < 8; ++mt) {
             const bf16x8 aop = lds16(sb, ra[ks][mt & 1] + 2048 * mt);
-            acc[0][mt] = mfma16(aop, bop[0], acc[0][mt]);
-            acc[1][mt] = mfma16(aop, bop[1], acc[1][mt]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mfma16(aop, bop[nt], acc[nt][mt]);
           }
         }
         if (s == NR - 1) {
@@ -442,7 +459,7 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
           if constexpr (STAGES) {
             if (a.kpre_out) {
 #pragma unroll
-              for (int nt = 0; nt < 2; ++nt)
+              for (int nt = 0; nt < NT; ++nt)
                 if (16 * nt + col < nvalid)
 #pragma unroll
                   for (int mt = 0; mt < 8; ++mt)
@@ -451,13 +468,13 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
             }
           }
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+          for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) kpre_b[nt][ks] = pack8(acc[nt][2 * ks], acc[nt][2 * ks + 1]);
           // RoPE: pair (d, d + 64) = m-tiles (mt, mt + 4) of the same lane
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const int cs = 4 * wave + 2 * nt + (col >> 3), i = col & 7;
+          for (int nt = 0; nt < NT; ++nt) {
+            const int cs = CPW * wave + 2 * nt + (col >> 3), i = col & 7;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -475,7 +492,7 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
           if constexpr (STAGES) {
             if (a.kpost_out) {
 #pragma unroll
-              for (int nt = 0; nt < 2; ++nt)
+              for (int nt = 0; nt < NT; ++nt)
                 if (16 * nt + col < nvalid)
 #pragma unroll
                   for (int mt = 0; mt < 8; ++mt)
@@ -485,7 +502,7 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
           }
           // QK with K_post rounded to bf16 (2^-9 relative per entry), then
           // this wave's softmax weights: the value section needs them
-          f32x4 zacc[2];
+          f32x4 zacc[NT];
           {
             bf16x8 qp[4];
 #pragma unroll
@@ -493,22 +510,22 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
               qp[ks] = col < g ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&L.qs[col][32 * ks + 8 * grp]))
                                : zero_bf16x8();
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NT; ++nt) {
               f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
               for (int ks = 0; ks < 4; ++ks) z = mfma16(pack8(acc[nt][2 * ks], acc[nt][2 * ks + 1]), qp[ks], z);
               zacc[nt] = z;
             }
           }
-          pa = wave_softmax(zacc, nvalid, a.scale_log2, grp, wm, wl);
+          wave_softmax<NT>(zacc, nvalid, a.scale_log2, grp, wm, wl, pa);
 #pragma unroll
           for (int nd = 0; nd < 8; ++nd) oacc[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
           if constexpr (STAGES) {
 #pragma unroll
             for (int nd = 0; nd < 8; ++nd) {
               const float bias = L.b2f[16 * nd + col];
-              vacc[0][nd] = f32x4{bias, bias, bias, bias};
-              vacc[1][nd] = vacc[0][nd];
+#pragma unroll
+              for (int tt = 0; tt < NT; ++tt) vacc[tt][nd] = f32x4{bias, bias, bias, bias};
             }
           }
         }
@@ -522,32 +539,36 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
         //   PH    D[h][j] = gelu(hid)^T[h][t] x p^T[t][j]
         //   OUT   D[d][j] += W2[d][h] x PH[h][j]
         const int c = s - NR;
-        f32x4 hacc[2][2];  // [token tile][hidden tile]
+        f32x4 hacc[NT][2];  // [token tile][hidden tile]
 #pragma unroll
         for (int hn = 0; hn < 2; ++hn) {
           const float bias = L.b1f[32 * c + 16 * hn + col];
-          hacc[0][hn] = f32x4{bias, bias, bias, bias};
-          hacc[1][hn] = hacc[0][hn];
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) hacc[tt][hn] = f32x4{bias, bias, bias, bias};
         }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
           for (int hn = 0; hn < 2; ++hn) {
             const bf16x8 bop = lds16(sb, rw1[ks] + 4096 * hn);
-            hacc[0][hn] = mfma16(kpre_b[0][ks], bop, hacc[0][hn]);
-            hacc[1][hn] = mfma16(kpre_b[1][ks], bop, hacc[1][hn]);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) hacc[tt][hn] = mfma16(kpre_b[tt][ks], bop, hacc[tt][hn]);
           }
         }
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
           for (int hn = 0; hn < 2; ++hn)
 #pragma unroll
             for (int e = 0; e < 4; ++e) hacc[tt][hn][e] = gelu_fast(hacc[tt][hn][e]);
         f32x4 pht[2];
 #pragma unroll
-        for (int hn = 0; hn < 2; ++hn)
-          pht[hn] = mfma16(pack8(hacc[0][hn], hacc[1][hn]), pa, f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int hn = 0; hn < 2; ++hn) {
+          pht[hn] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int q = 0; q < NT / 2; ++q)
+            pht[hn] = mfma16(pack8(hacc[2 * q][hn], hacc[2 * q + 1][hn]), pa[q], pht[hn]);
+        }
         const bf16x8 hb = pack8(pht[0], pht[1]);
 #pragma unroll
         for (int nd = 0; nd < 8; ++nd) oacc[nd] = mfma16(lds16(sb, rw2[nd & 3] + 1024 * nd), hb, oacc[nd]);
@@ -555,34 +576,32 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
         if constexpr (STAGES) {
           // per-token values for the stage output: MLP1 again as D[h][t]
           // (W1 as the A operand), GELU, then D[t][d] = hid x W2^T
-          f32x4 hq[2][2];  // [hidden tile][token tile]
+          f32x4 hq[2][NT];  // [hidden tile][token tile]
 #pragma unroll
           for (int hm = 0; hm < 2; ++hm) {
             const f32x4 bias = *reinterpret_cast<const f32x4*>(&L.b1f[32 * c + 16 * hm + 4 * grp]);
-            hq[hm][0] = bias;
-            hq[hm][1] = bias;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) hq[hm][nt] = bias;
           }
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int hm = 0; hm < 2; ++hm) {
               const bf16x8 aop = lds16(sb, rw1[ks] + 4096 * hm);
-              hq[hm][0] = mfma16(aop, kpre_b[0][ks], hq[hm][0]);
-              hq[hm][1] = mfma16(aop, kpre_b[1][ks], hq[hm][1]);
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) hq[hm][nt] = mfma16(aop, kpre_b[nt][ks], hq[hm][nt]);
             }
 #pragma unroll
           for (int hm = 0; hm < 2; ++hm)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
               for (int e = 0; e < 4; ++e) hq[hm][nt][e] = gelu_fast(hq[hm][nt][e]);
-          const bf16x8 ha0 = pack8(hq[0][0], hq[1][0]);
-          const bf16x8 ha1 = pack8(hq[0][1], hq[1][1]);
 #pragma unroll
           for (int nd = 0; nd < 8; ++nd) {
             const bf16x8 bop = lds16(sb, rw2[nd & 3] + 1024 * nd);
-            vacc[0][nd] = mfma16(ha0, bop, vacc[0][nd]);
-            vacc[1][nd] = mfma16(ha1, bop, vacc[1][nd]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) vacc[nt][nd] = mfma16(pack8(hq[0][nt], hq[1][nt]), bop, vacc[nt][nd]);
           }
         }
       }
@@ -597,23 +616,26 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     __syncthreads();
     if constexpr (!RI4) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < RL; ++u) {
         const int tl = 16 * u + (tid >> 4);
         *reinterpret_cast<u32x4*>(buf + tl * kResRow + (tid & 15) * 16) = rres[u];
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < RL; ++u) {
         const int tl = 64 * u + (tid >> 2);
         *reinterpret_cast<u32x4*>(buf + tl * kResRow4 + (tid & 3) * 16) = rres[u];
       }
-      if ((tid & 1) == 0)
-        *reinterpret_cast<u32x2*>(buf + (tid >> 1) * kResRow4 + 64) = u32x2{rres[2][0], rres[2][1]};
+      if ((tid & 1) == 0) {
+        *reinterpret_cast<u32x2*>(buf + (tid >> 1) * kResRow4 + 64) = u32x2{rres[RL][0], rres[RL][1]};
+        if constexpr (kAttChunksWG * 8 > 128)
+          *reinterpret_cast<u32x2*>(buf + ((tid >> 1) + 128) * kResRow4 + 64) = u32x2{rres[RL][2], rres[RL][3]};
+      }
     }
     __syncthreads();
     // residual of wave token t (< 32) at dimension d, as a float
     auto resid_at = [&](int t, int d) -> float {
-      const int tl = 32 * wave + t;
+      const int tl = TOKW * wave + t;
       if constexpr (!RI4) {
         return bf16_to_f32(*reinterpret_cast<const uint16_t*>(buf + tl * kResRow + d * 2));
       } else {
@@ -627,30 +649,33 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     // and b2[d] * sum_t p_t
 #pragma unroll
     for (int nd = 0; nd < 8; ++nd) {
-      bf16x8 rop;
-      if constexpr (!RI4) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tl = 32 * wave + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
-          rop[e] = *reinterpret_cast<const __bf16*>(buf + tl * kResRow + (16 * nd + col) * 2);
-        }
-      } else {
-        f32x4 lo, hi;
+      for (int q = 0; q < NT / 2; ++q) {
+        bf16x8 rop;
+        if constexpr (!RI4) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lo[e] = resid_at(4 * grp + e, 16 * nd + col);
-          hi[e] = resid_at(16 + 4 * grp + e, 16 * nd + col);
+          for (int e = 0; e < 8; ++e) {
+            const int tl = TOKW * wave + 32 * q + (e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4);
+            rop[e] = *reinterpret_cast<const __bf16*>(buf + tl * kResRow + (16 * nd + col) * 2);
+          }
+        } else {
+          f32x4 lo, hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lo[e] = resid_at(32 * q + 4 * grp + e, 16 * nd + col);
+            hi[e] = resid_at(32 * q + 16 + 4 * grp + e, 16 * nd + col);
+          }
+          rop = pack8(lo, hi);
         }
-        rop = pack8(lo, hi);
+        oacc[nd] = mfma16(rop, pa[q], oacc[nd]);
       }
-      oacc[nd] = mfma16(rop, pa, oacc[nd]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) oacc[nd][e] = fmaf(L.b2f[16 * nd + 4 * grp + e], wl, oacc[nd][e]);
     }
     if constexpr (STAGES) {
       if (a.vhat_out) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int t = 16 * tt + 4 * grp + e;
@@ -690,9 +715,10 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
         vt[nd][e] = __builtin_bit_cast(__bf16, vw[(size_t)t * kHeadDim + 16 * nd + col]);
       }
     }
-    const bf16x8 pa = wave_softmax(zacc, nvalid, a.scale_log2, grp, wm, wl);
+    bf16x8 pa[1];
+    wave_softmax<2>(zacc, nvalid, a.scale_log2, grp, wm, wl, pa);
 #pragma unroll
-    for (int nd = 0; nd < 8; ++nd) oacc[nd] = mfma16(vt[nd], pa, f32x4{0.f, 0.f, 0.f, 0.f});
+    for (int nd = 0; nd < 8; ++nd) oacc[nd] = mfma16(vt[nd], pa[0], f32x4{0.f, 0.f, 0.f, 0.f});
   }
 
   // ======================================== merge the 4 waves, write partial

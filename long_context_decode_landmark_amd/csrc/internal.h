@@ -6,11 +6,16 @@
 
 namespace lowram {
 
-// Selected-chunk attention: one workgroup = 4 waves x 32 tokens = 16 chunks.
+// Attention workgroups are 4 waves.  Selected chunks: each wave owns
+// 16 * kAttSelNT tokens; the exact window: 32 tokens per wave.
+#ifndef LOWRAM_ATT_NT
+#define LOWRAM_ATT_NT 2
+#endif
 constexpr int kAttWaves = 4;
-constexpr int kAttTokWave = 32;
-constexpr int kAttChunksWG = kAttWaves * kAttTokWave / 8;  // 16
-constexpr int kAttTokWG = kAttWaves * kAttTokWave;         // 128
+constexpr int kAttSelNT = LOWRAM_ATT_NT;
+constexpr int kAttChunksWG = kAttWaves * 16 * kAttSelNT / 8;  // selected chunks per workgroup
+constexpr int kAttTokWave = 32;                              // window tokens per wave
+constexpr int kAttTokWG = kAttWaves * kAttTokWave;           // window tokens per workgroup
 constexpr int kPartStride = 2 + 128;                       // m, l, o[128] per query head
 constexpr int kMergeMaxWeights = 4096;                     // n_split * min(g, 16) limit of the merge
 

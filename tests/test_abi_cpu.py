@@ -67,6 +67,7 @@ def test_workspace_bytes_formula():
     s = native.make_shape(cfg, batch=28)
     heads = 28 * 8
     keff = min(cfg.topk, cfg.n_cand)
+    # selected-chunk workgroups cover 16 chunks (4 waves x 32 tokens), window ones 128 tokens
     n_split = -(-keff // 16) + -(-cfg.window // 128)
     al = lambda x: (x + 255) // 256 * 256
     want = al(heads * cfg.n_cand * 4) + al(heads * keff * 4) + al(heads * n_split * 4 * 130 * 4)
