@@ -8,6 +8,10 @@
 #include "common.h"
 #include "internal.h"
 
+#ifndef LOWRAM_SCORE_MAX_WG
+#define LOWRAM_SCORE_MAX_WG 8192
+#endif
+
 namespace lowram {
 
 // ---------------------------------------------------------------------------
@@ -20,7 +24,10 @@ namespace lowram {
 // 16-lane group) ends up owning chunk c0 + l%16 with rows j = 4*(l/16) + e.
 // Each wave keeps 4 groups of 16 landmarks (16 KiB) in flight per iteration.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void score_kernel(
+#ifndef LOWRAM_SCORE_WG_PER_CU
+#define LOWRAM_SCORE_WG_PER_CU 1
+#endif
+__global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ landmark,
     uint32_t* __restrict__ keys, float* __restrict__ scores_out, int n_cand, int n_heads_q,
     int n_heads_kv, int chunks_per_wg) {
@@ -236,10 +243,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* keys,
                         float* scores_out, int nb, int n_cand, int hq, int hkv, hipStream_t st) {
   if (n_cand <= 0) return hipSuccess;
-  // enough workgroups to cover the chip even at batch 1
+  // chunks per workgroup: the smallest power of two >= 256 that keeps the
+  // grid within LOWRAM_SCORE_MAX_WG workgroups
   const long long heads = (long long)nb * hkv;
   int cpw = 256;
-  while ((long long)((n_cand + cpw - 1) / cpw) * heads > 4096 && cpw < 4096) cpw *= 2;
+  while ((long long)((n_cand + cpw - 1) / cpw) * heads > LOWRAM_SCORE_MAX_WG && cpw < 4096) cpw *= 2;
   dim3 grid((n_cand + cpw - 1) / cpw, hkv, nb);
   hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, st, q, landmark, keys, scores_out,
                      n_cand, hq, hkv, cpw);
