@@ -43,13 +43,19 @@ def landmarks(x_pre: np.ndarray, prefix: int, chunk: int, theta: float) -> np.nd
     """Mean post-RoPE key of each chunk of the prefix, [P/S][d]."""
     pos = np.arange(prefix)
     k_post = rope(np.asarray(x_pre[:prefix], np.float64), pos, theta)
-    return k_post.reshape(prefix // chunk, chunk, -1).mean(axis=1)
+    return k_post.reshape(prefix // chunk, chunk, k_post.shape[-1]).mean(axis=1)
 
 
 def exact_values(x: np.ndarray, w1, b1, w2, b2, noise, spike_pos, spike_vals) -> np.ndarray:
     v = value_mlp(np.asarray(x, np.float64), w1, b1, w2, b2) + np.asarray(noise, np.float64)
     v[spike_pos] += spike_vals
     return v
+
+
+def residual_errors(v_prefix: np.ndarray, k_pre_prefix: np.ndarray, w1, b1, w2, b2) -> np.ndarray:
+    """||V_t - MLP(K_pre_t)||_2 of every prefix token."""
+    r = np.asarray(v_prefix, np.float64) - value_mlp(k_pre_prefix, w1, b1, w2, b2)
+    return np.sqrt(np.sum(r * r, axis=1))
 
 
 def residual_select(v_prefix: np.ndarray, k_pre_prefix: np.ndarray, w1, b1, w2, b2, n_resid: int):
@@ -79,23 +85,34 @@ def _store(x, exact: bool):
     return np.asarray(x, np.float64) if exact else codecs.bf16_encode(x)
 
 
-def compress_head(cfg, x_head: np.ndarray, coeff_stored, blk_stored, mlp, noise, spikes,
-                  exact: bool = False):
-    """Everything one (sequence, layer, KV head) stores, from its exact keys.
+def store_coeff(c, int4: bool, exact: bool = False):
+    """Coefficients as the cache stores them: fp64 (exact), int4 g32 (codes,
+    scales) or bf16 bits."""
+    if exact:
+        return np.asarray(c, np.float64)
+    return codecs.int4_encode(c) if int4 else codecs.bf16_encode(c)
 
-    x_head: exact pre-RoPE keys [T][d]; coeff_stored: the group's stored
-    coefficients of the prefix tokens (as stored: bf16 bits, int4, or fp64);
-    blk_stored: stored basis block [d][r]; mlp = (w1, b1, w2, b2) as stored.
+
+def decode_coeff(coeff_stored, int4: bool, exact: bool = False) -> np.ndarray:
+    if exact:
+        return np.asarray(coeff_stored, np.float64)
+    return codecs.int4_decode(*coeff_stored) if int4 else codecs.bf16_decode(coeff_stored)
+
+
+def compress_from_kv(cfg, x_head: np.ndarray, v_head: np.ndarray, coeff_stored, blk_stored, mlp,
+                     exact: bool = False):
+    """Everything one (sequence, layer, KV head) stores, from its exact keys and values.
+
+    x_head: exact pre-RoPE keys [T][d]; v_head: exact values [T][d];
+    coeff_stored: the group's stored coefficients of the prefix tokens (bf16
+    bits, int4 (codes, scales), or fp64 with exact=True); blk_stored: stored
+    basis block [d][r]; mlp = (w1, b1, w2, b2) as stored.  The residual test
+    runs against the keys decode rebuilds: stored coefficients x stored block.
     """
     P, S, W = cfg.prefix, cfg.chunk, cfg.window
     w = [np.asarray(a, np.float64) if exact else codecs.bf16_decode(a) for a in mlp]
-    v = exact_values(x_head, *w, noise, *spikes)
-
-    # the keys decode rebuilds: stored coefficients x stored basis
-    if cfg.int4 and not exact:
-        c_dec = codecs.int4_decode(*coeff_stored)
-    else:
-        c_dec = np.asarray(coeff_stored, np.float64) if exact else codecs.bf16_decode(coeff_stored)
+    v = np.asarray(v_head, np.float64)
+    c_dec = decode_coeff(coeff_stored, cfg.int4, exact)
     blk = np.asarray(blk_stored, np.float64) if exact else codecs.bf16_decode(blk_stored)
     k_pre = reconstruct(c_dec, blk)
     idx, rows = residual_select(v[:P], k_pre, *w, cfg.n_resid)
@@ -112,6 +129,14 @@ def compress_head(cfg, x_head: np.ndarray, coeff_stored, blk_stored, mlp, noise,
     else:
         out["res_val"] = _store(rows, exact)
     return out
+
+
+def compress_head(cfg, x_head: np.ndarray, coeff_stored, blk_stored, mlp, noise, spikes,
+                  exact: bool = False):
+    """compress_from_kv with the synthetic exact values V = MLP(X) + noise + spikes."""
+    w = [np.asarray(a, np.float64) if exact else codecs.bf16_decode(a) for a in mlp]
+    v = exact_values(x_head, *w, noise, *spikes)
+    return compress_from_kv(cfg, x_head, v, coeff_stored, blk_stored, mlp, exact=exact)
 
 
 def compact_landmarks(lm: np.ndarray, survivors: np.ndarray) -> np.ndarray:

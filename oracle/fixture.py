@@ -23,7 +23,7 @@ import numpy as np
 
 import synth
 from . import codecs
-from .compress import basis_block, compact_landmarks, compress_head, project
+from .compress import basis_block, compact_landmarks, compress_head, project, store_coeff
 
 
 def _key_dtype(cfg):
@@ -35,13 +35,7 @@ def _group_state(cfg, b: int, grp: int, exact: bool):
     """Exact keys, basis and stored coefficients of one (sequence, group)."""
     x = synth.exact_keys(cfg, b, grp, dtype=_key_dtype(cfg))
     B = synth.basis(cfg, b, grp)
-    c = project(x[: cfg.prefix], B)
-    if exact:
-        c_st = c
-    elif cfg.int4:
-        c_st = codecs.int4_encode(c)
-    else:
-        c_st = codecs.bf16_encode(c)
+    c_st = store_coeff(project(x[: cfg.prefix], B), cfg.int4, exact)
     return x, B, c_st
 
 
@@ -122,3 +116,64 @@ def dense_layer(cfg, layer: int, batch=None):
         vs.append(np.stack(vh))
         qs.append(codecs.bf16_encode(synth.queries(cfg, b, layer)))
     return np.stack(ks), np.stack(vs), np.stack(qs)
+
+
+def builder_io(cfg, layer: int, batch=None):
+    """Inputs of the cache builder for ``layer`` and the cache the oracle builds from them.
+
+    Inputs (bf16 bits, the layouts of lowram_build_coeff / lowram_build_layer):
+      keys [NB][T][D] exact pre-RoPE keys of the layer's group, group_basis
+      [NB][r][D], values [NB][Hkv][T][d] exact values of the layer, w1, b1, w2,
+      b2 as in the cache.
+    Expected: the oracle's compression (``compress``) run on exactly those
+    bf16 inputs: coeff (+ coeff_scale), basis, landmark, res_idx, res_val
+    (+ res_scale), res_chunk_desc, win_k, win_v, and ``errors`` [NB][Hkv][P],
+    the oracle's ||R_t|| of every prefix token (for the near-tie rule).
+    """
+    from .compress import compress_from_kv, decode_coeff, exact_values, residual_errors
+    from .steps import reconstruct
+    batch = list(range(cfg.batch)) if batch is None else list(batch)
+    grp = layer // cfg.group_layers
+    P = cfg.prefix
+    inp = {k: [] for k in ("keys", "group_basis", "values", "w1", "b1", "w2", "b2")}
+    exp = {k: [] for k in ("coeff", "coeff_scale", "basis", "landmark", "res_idx", "res_val", "res_scale",
+                           "res_chunk_desc", "win_k", "win_v", "errors")}
+    for b in batch:
+        x_bits = codecs.bf16_encode(synth.exact_keys(cfg, b, grp, dtype=_key_dtype(cfg)))
+        B_bits = codecs.bf16_encode(synth.basis(cfg, b, grp))
+        x, B = codecs.bf16_decode(x_bits), codecs.bf16_decode(B_bits)
+        c_st = store_coeff(project(x[:P], B), cfg.int4)
+        inp["keys"].append(x_bits)
+        inp["group_basis"].append(B_bits)
+        if cfg.int4:
+            exp["coeff"].append(c_st[0])
+            exp["coeff_scale"].append(c_st[1])
+        else:
+            exp["coeff"].append(c_st)
+        heads = {k: [] for k in inp if k not in ("keys", "group_basis")}
+        hexp = {k: [] for k in exp if k not in ("coeff", "coeff_scale")}
+        for h in range(cfg.n_heads_kv):
+            cols = synth.layer_cols(cfg, layer, h)
+            mlp_st = tuple(codecs.bf16_encode(a) for a in synth.mlp_weights(cfg, b, layer, h))
+            w = [codecs.bf16_decode(a) for a in mlp_st]
+            v_bits = codecs.bf16_encode(exact_values(np.asarray(x[:, cols]), *w, synth.value_noise(cfg, b, layer, h),
+                                                     *synth.value_spikes(cfg, b, layer, h)))
+            blk_st = basis_block(B_bits, cols)
+            hd = compress_from_kv(cfg, x[:, cols], codecs.bf16_decode(v_bits), c_st, blk_st, mlp_st)
+            hd["basis"] = blk_st
+            hd["errors"] = residual_errors(codecs.bf16_decode(v_bits)[:P],
+                                           reconstruct(decode_coeff(c_st, cfg.int4), codecs.bf16_decode(blk_st)), *w)
+            heads["values"].append(v_bits)
+            for k, a in zip(("w1", "b1", "w2", "b2"), mlp_st):
+                heads[k].append(a)
+            for k in hexp:
+                if k in hd:
+                    hexp[k].append(hd[k])
+        for k, v in heads.items():
+            inp[k].append(np.stack(v))
+        for k, v in hexp.items():
+            if v:
+                exp[k].append(np.stack(v))
+    inp = {k: np.ascontiguousarray(np.stack(v)) for k, v in inp.items()}
+    exp = {k: np.ascontiguousarray(np.stack(v)) for k, v in exp.items() if v}
+    return inp, exp

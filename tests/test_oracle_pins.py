@@ -232,6 +232,46 @@ def test_residual_select_brute_force_and_offsets():
         assert int(desc[c]) == (first << 8) | bits
 
 
+def test_compress_from_kv_planted_residuals():
+    """Values = torch MLP of the rebuilt keys + residuals planted on a known set.
+
+    The rebuilt keys come from the orthogonal projection x B^T B (not the
+    oracle's reconstruct); the MLP from torch layers; so the residual rows must
+    come back exactly as planted, on exactly the planted tokens, and the
+    landmarks / window from the complex-form rotation.
+    """
+    cfg = synth.C0.with_(name="planted", ctx=256, window=16, resid_frac=6 / 240)
+    P, W = cfg.prefix, cfg.window
+    assert cfg.n_resid == 6
+    rng = np.random.default_rng(12)
+    B = synth.basis(cfg, 0, 0)
+    x = rng.standard_normal((cfg.ctx, cfg.group_dim))
+    c = compress.project(x[:P], B)
+    layer, h = 1, 1
+    cols = synth.layer_cols(cfg, layer, h)
+    k_pre = (x[:P] @ B.T @ B)[:, cols]
+    w1, b1, w2, b2 = (np.asarray(a, np.float64) for a in synth.mlp_weights(cfg.with_(bias_std=0.2), 0, layer, h))
+    tt = torch.from_numpy
+    pred = torch.nn.functional.linear(torch.nn.functional.gelu(torch.nn.functional.linear(tt(k_pre), tt(w1), tt(b1))),
+                                      tt(w2), tt(b2)).numpy()
+    planted = np.array([3, 40, 41, 100, 177, 239])
+    e = np.zeros((cfg.ctx, cfg.head_dim))
+    e[planted] = rng.standard_normal((6, cfg.head_dim)) + 2.0
+    v = np.concatenate([pred, rng.standard_normal((W, cfg.head_dim))]) + e
+    out = compress.compress_from_kv(cfg, x[:, cols], v, c, compress.basis_block(B, cols), (w1, b1, w2, b2),
+                                    exact=True)
+    assert list(out["res_idx"]) == list(planted)
+    assert np.allclose(out["res_val"], e[planted], atol=1e-9)
+    rot = complex_rope(x[:, cols], np.arange(cfg.ctx), cfg.rope_theta)
+    assert np.allclose(out["landmark"], rot[:P].reshape(-1, 8, cfg.head_dim).mean(axis=1), atol=1e-12)
+    assert np.allclose(out["win_k"], rot[P:], atol=1e-12)
+    assert np.array_equal(out["win_v"], v[P:])
+    for ch in (0, 5, 12, 22, 29):
+        first = int(np.sum(planted < 8 * ch))
+        bits = sum(1 << int(t - 8 * ch) for t in planted if 8 * ch <= t < 8 * ch + 8)
+        assert int(out["res_chunk_desc"][ch]) == (first << 8) | bits
+
+
 # ------------------------------------------------ whole-step invariants --
 def full_cfg():
     """Tiny workload where rank = G*Hkv*d, k = nC and every token has a residual."""
