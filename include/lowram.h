@@ -186,6 +186,95 @@ int dense_decode_step(const dense_shape* shape, const dense_layer_cache* cache,
 int lowram_resid_chunk_desc(const int32_t* res_idx, int32_t n_lists, int32_t n_resid,
                             int32_t n_chunks, int32_t chunk, uint32_t* desc, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Cache builder (prefill side).  Writes the arrays lowram_decode_step reads,
+ * from a layer group's exact keys and each layer's exact values, as the
+ * LowRAM pages describe compression:
+ *   - review (agihunt.info), key paragraph: coefficients of the pre-RoPE keys
+ *     in the group's shared basis, chunked prefix, mean post-RoPE key per
+ *     chunk as its landmark;
+ *   - review, value paragraph, and explainer (cctest.ai), "How the method
+ *     works" / "Residuals for difficult tokens": values predicted from the
+ *     rebuilt keys by the per-head MLP, exact residuals kept for the tokens
+ *     it predicts worst.
+ * The basis and the MLP weights are inputs; fitting them is not done here.
+ * Conventions as above (device pointers, caller-owned, stream-ordered, no
+ * allocation, status codes).
+ * ------------------------------------------------------------------------- */
+typedef struct lowram_build_shape {
+  int32_t batch;         /* NB >= 1 sequences                                          */
+  int32_t ctx_len;       /* T >= 1 tokens of exact keys / values per sequence          */
+  int32_t window;        /* W, 0 <= W <= T: tokens P .. T-1 stay exact, P = T - W      */
+  int32_t chunk;         /* S; P must be a multiple of it; this build supports 8       */
+  int32_t n_heads_kv;    /* Hkv >= 1                                                   */
+  int32_t head_dim;      /* d; this build supports 128                                 */
+  int32_t rank;          /* r; 64, 128, 256 or 512 (int4 coefficients: 128 and up)     */
+  int32_t group_layers;  /* G >= 1 layers sharing one basis; key width D = G * Hkv * d */
+  int32_t mlp_hidden;    /* H; this build supports 256                                 */
+  int32_t n_resid;       /* nR, 0 <= nR <= P residual rows kept per (sequence, head)   */
+  int32_t coeff_fmt;     /* LOWRAM_FMT_* of the coefficients written                   */
+  int32_t resid_fmt;     /* LOWRAM_FMT_* of the residual rows written                  */
+  float rope_theta;      /* RoPE base, as in lowram_shape                              */
+} lowram_build_shape;
+
+/*
+ * Coefficients of one layer group: C[b][t][m] = sum_j X[b][t][j] B[b][m][j]
+ * for the prefix tokens t < P (fp32 accumulation of bf16 products), stored
+ * in shape->coeff_fmt.  Shared by the G layers of the group.
+ *   keys   [NB][T][D] bf16 exact pre-RoPE keys of the group; column
+ *          (l * Hkv + h) * d + i belongs to layer l of the group, KV head h
+ *   basis  [NB][r][D] bf16 the group's basis B (rows orthonormal)
+ *   coeff  out: bf16 [NB][P][r], or int4 [NB][P][r/2] bytes
+ *   coeff_scale  out: int4 only, [NB][P][r/32] fp16; may be NULL for bf16
+ * Needs no workspace.
+ */
+int lowram_build_coeff(const lowram_build_shape* shape, const uint16_t* keys,
+                       const uint16_t* basis, void* coeff, uint16_t* coeff_scale, void* stream);
+
+/* Inputs and outputs of one layer's build (all device pointers). */
+typedef struct lowram_layer_build {
+  const uint16_t* keys;         /* in:  [NB][T][D] bf16, as for lowram_build_coeff           */
+  const uint16_t* group_basis;  /* in:  [NB][r][D] bf16                                       */
+  const void* coeff;            /* in:  the group's coefficients from lowram_build_coeff      */
+  const uint16_t* coeff_scale;  /* in:  int4 only                                             */
+  const uint16_t* values;       /* in:  [NB][Hkv][T][d] bf16 exact values of this layer       */
+  const uint16_t* w1;           /* in:  value MLP, layouts of lowram_layer_cache              */
+  const uint16_t* b1;
+  const uint16_t* w2;
+  const uint16_t* b2;
+  uint16_t* basis;              /* out: [NB][Hkv][d][r] this layer's basis blocks, transposed */
+  uint16_t* landmark;           /* out: [NB][Hkv][P/S][d] bf16 mean post-RoPE key per chunk   */
+  int32_t* res_idx;             /* out: [NB][Hkv][nR] ascending token ids                     */
+  void* res_val;                /* out: bf16 [NB][Hkv][nR][d] or int4 [..][nR][d/2] bytes     */
+  uint16_t* res_scale;          /* out: int4 only, [NB][Hkv][nR][d/32] fp16                   */
+  uint32_t* res_chunk_desc;     /* out: [NB][Hkv][P/S] residual descriptors                   */
+  uint16_t* win_k;              /* out: [NB][Hkv][W][d] bf16 post-RoPE keys of the window     */
+  uint16_t* win_v;              /* out: [NB][Hkv][W][d] bf16 values of the window             */
+} lowram_layer_build;
+
+/* Workspace bytes lowram_build_layer needs (pure function of the shape):
+   NB * Hkv * P * (4 d + 4) bytes (rounded up), the fp32 residual of every
+   prefix token and its error key. */
+int lowram_build_layer_workspace_bytes(const lowram_build_shape* shape, size_t* bytes);
+
+/*
+ * One layer of the cache, layer_in_group in [0, G):
+ *   basis     the layer's columns of B, per KV head, transposed (exact copy)
+ *   landmark  per chunk c: mean over its S keys of RoPE(x_t, t), bf16
+ *   residuals R_t = v_t - MLP(K_pre_t), K_pre_t = C_t (as stored) x basis
+ *             block, MLP(k) = W2 gelu(W1 k + b1) + b2 with the erf GELU, all
+ *             evaluated to fp32 accuracy; the nR tokens of largest ||R_t||_2
+ *             (ties to the lower token), ascending, their R rows stored in
+ *             shape->resid_fmt, and the per-chunk descriptors of
+ *             lowram_resid_chunk_desc
+ *   window    RoPE(x_t, t) and v_t of t = P .. T-1
+ * Landmarks are written for all P/S chunks; eviction (cand_ids) is applied
+ * by the caller after the build.
+ */
+int lowram_build_layer(const lowram_build_shape* shape, int32_t layer_in_group,
+                       const lowram_layer_build* io, void* workspace, size_t ws_bytes,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

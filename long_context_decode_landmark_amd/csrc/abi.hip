@@ -159,6 +159,44 @@ int check_dense(const dense_shape* s) {
   return LOWRAM_OK;
 }
 
+int check_build_shape(const lowram_build_shape* s) {
+  if (!s) return LOWRAM_ERR_NULL;
+  if (s->batch < 1 || s->ctx_len < 1 || s->window < 0 || s->window > s->ctx_len || s->chunk < 1 ||
+      s->n_heads_kv < 1 || s->head_dim < 1 || s->rank < 1 || s->group_layers < 1 || s->mlp_hidden < 1 ||
+      s->n_resid < 0)
+    return LOWRAM_ERR_SHAPE;
+  const int P = s->ctx_len - s->window;
+  if (P % s->chunk) return LOWRAM_ERR_SHAPE;
+  if (s->n_resid > P) return LOWRAM_ERR_SHAPE;
+  if (s->coeff_fmt != LOWRAM_FMT_BF16 && s->coeff_fmt != LOWRAM_FMT_INT4_G32) return LOWRAM_ERR_SHAPE;
+  if (s->resid_fmt != LOWRAM_FMT_BF16 && s->resid_fmt != LOWRAM_FMT_INT4_G32) return LOWRAM_ERR_SHAPE;
+  if (!(s->rope_theta > 0.f) || !std::isfinite(s->rope_theta)) return LOWRAM_ERR_SHAPE;
+  if (s->chunk != kChunk || s->head_dim != kHeadDim || s->mlp_hidden != kHidden) return LOWRAM_ERR_UNSUPPORTED;
+  if (s->rank != 64 && s->rank != 128 && s->rank != 256 && s->rank != 512) return LOWRAM_ERR_UNSUPPORTED;
+  if (s->coeff_fmt == LOWRAM_FMT_INT4_G32 && s->rank % 128) return LOWRAM_ERR_UNSUPPORTED;
+  if (s->n_resid >= (1 << 24)) return LOWRAM_ERR_UNSUPPORTED;
+  // 32-bit token and element indices inside the kernels
+  if ((int64_t)s->batch * s->ctx_len >= (int64_t)1 << 31) return LOWRAM_ERR_UNSUPPORTED;
+  if ((int64_t)s->group_layers * s->n_heads_kv * kHeadDim >= (int64_t)1 << 20) return LOWRAM_ERR_UNSUPPORTED;
+  return LOWRAM_OK;
+}
+
+struct BuildPlan {
+  int P, n_chunks;
+  size_t off_r, off_keys, total;
+};
+
+BuildPlan make_build_plan(const lowram_build_shape* s) {
+  BuildPlan p{};
+  p.P = s->ctx_len - s->window;
+  p.n_chunks = p.P / s->chunk;
+  const size_t heads = (size_t)s->batch * s->n_heads_kv;
+  p.off_r = 0;                                                // fp32 residual rows [NB][Hkv][P][d]
+  p.off_keys = align_up(heads * (size_t)p.P * kHeadDim * 4);  // uint32 error keys [NB][Hkv][P]
+  p.total = p.off_keys + align_up(heads * (size_t)p.P * 4);
+  return p;
+}
+
 constexpr int kDenseTokPerSplit = 2048;
 
 int dense_splits(const dense_shape* s) { return (s->ctx_len + kDenseTokPerSplit - 1) / kDenseTokPerSplit; }
@@ -255,6 +293,90 @@ int lowram_resid_chunk_desc(const int32_t* res_idx, int32_t n_lists, int32_t n_r
   if (n_lists == 0 || n_chunks == 0) return LOWRAM_OK;
   if (launch_chunk_desc(res_idx, n_lists, n_resid, n_chunks, chunk, desc,
                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LOWRAM_ERR_HIP;
+  return LOWRAM_OK;
+}
+
+
+int lowram_build_coeff(const lowram_build_shape* shape, const uint16_t* keys, const uint16_t* basis,
+                       void* coeff, uint16_t* coeff_scale, void* stream) {
+  const int st = check_build_shape(shape);
+  if (st) return st;
+  const bool ci4 = shape->coeff_fmt == LOWRAM_FMT_INT4_G32;
+  const int P = shape->ctx_len - shape->window;
+  if (P == 0) return LOWRAM_OK;  // nothing to project
+  if (!keys || !basis || !coeff || (ci4 && !coeff_scale)) return LOWRAM_ERR_NULL;
+  if (misaligned(keys, 16) || misaligned(basis, 16) || misaligned(coeff, 16) ||
+      (coeff_scale && misaligned(coeff_scale, 4)))
+    return LOWRAM_ERR_ALIGN;
+  const int D = shape->group_layers * shape->n_heads_kv * kHeadDim;
+  if (launch_proj(keys, basis, coeff, coeff_scale, shape->batch, shape->ctx_len, P, D, shape->rank, ci4,
+                  static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LOWRAM_ERR_HIP;
+  return LOWRAM_OK;
+}
+
+int lowram_build_layer_workspace_bytes(const lowram_build_shape* shape, size_t* bytes) {
+  if (!bytes) return LOWRAM_ERR_NULL;
+  const int st = check_build_shape(shape);
+  if (st) return st;
+  *bytes = make_build_plan(shape).total;
+  return LOWRAM_OK;
+}
+
+int lowram_build_layer(const lowram_build_shape* s, int32_t layer_in_group, const lowram_layer_build* io,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_build_shape(s);
+  if (st) return st;
+  if (layer_in_group < 0 || layer_in_group >= s->group_layers) return LOWRAM_ERR_SHAPE;
+  const BuildPlan p = make_build_plan(s);
+  if (!io || (!workspace && p.total > 0)) return LOWRAM_ERR_NULL;  // no prefix: no workspace needed
+  const bool ci4 = s->coeff_fmt == LOWRAM_FMT_INT4_G32, ri4 = s->resid_fmt == LOWRAM_FMT_INT4_G32;
+  if (!io->keys || !io->group_basis || !io->basis) return LOWRAM_ERR_NULL;
+  if (p.P > 0) {
+    if (!io->coeff || !io->w1 || !io->b1 || !io->w2 || !io->b2 || !io->landmark || !io->res_chunk_desc)
+      return LOWRAM_ERR_NULL;
+    if (ci4 && !io->coeff_scale) return LOWRAM_ERR_NULL;
+    if (s->n_resid > 0 && (!io->res_idx || !io->res_val || (ri4 && !io->res_scale))) return LOWRAM_ERR_NULL;
+  }
+  if (s->window > 0 && (!io->values || !io->win_k || !io->win_v)) return LOWRAM_ERR_NULL;
+  if (p.P > 0 && s->n_resid > 0 && !io->values) return LOWRAM_ERR_NULL;
+  const void* bulk[] = {workspace, io->keys, io->group_basis, io->coeff, io->values, io->w1, io->w2,
+                        io->basis, io->landmark, io->res_val, io->win_k, io->win_v};
+  for (const void* ptr : bulk)
+    if (ptr && misaligned(ptr, 16)) return LOWRAM_ERR_ALIGN;
+  const void* small[] = {io->coeff_scale, io->b1, io->b2, io->res_idx, io->res_scale, io->res_chunk_desc};
+  for (const void* ptr : small)
+    if (ptr && misaligned(ptr, 4)) return LOWRAM_ERR_ALIGN;
+  if (ws_bytes < p.total) return LOWRAM_ERR_WORKSPACE;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  BuildGeo g{};
+  g.nb = s->batch; g.T = s->ctx_len; g.P = p.P; g.W = s->window;
+  g.D = s->group_layers * s->n_heads_kv * kHeadDim; g.r = s->rank; g.hkv = s->n_heads_kv;
+  g.layer_in_group = layer_in_group; g.n_chunks = p.n_chunks; g.n_resid = s->n_resid;
+  for (int i = 0; i < 64; ++i) g.inv_freq[i] = std::pow((double)s->rope_theta, -2.0 * i / (double)kHeadDim);
+  if (launch_build_layer_arrays(io->keys, io->values, io->group_basis, io->basis, io->landmark, io->win_k,
+                                io->win_v, g, hs) != hipSuccess)
+    return LOWRAM_ERR_HIP;
+  if (p.P == 0) return LOWRAM_OK;
+
+  unsigned char* w = static_cast<unsigned char*>(workspace);
+  float* r = reinterpret_cast<float*>(w + p.off_r);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(w + p.off_keys);
+  const size_t heads = (size_t)s->batch * s->n_heads_kv;
+  if (s->n_resid > 0) {
+    if (launch_predict_resid(io->coeff, io->coeff_scale, io->basis, io->w1, io->b1, io->w2, io->b2, io->values, r,
+                             keys, ci4, g, hs) != hipSuccess)
+      return LOWRAM_ERR_HIP;
+    if (launch_select(keys, nullptr, io->res_idx, nullptr, s->batch, p.P, s->n_resid, s->n_heads_kv, hs) !=
+        hipSuccess)
+      return LOWRAM_ERR_HIP;
+    if (launch_resid_store(r, io->res_idx, io->res_val, io->res_scale, g, ri4, hs) != hipSuccess)
+      return LOWRAM_ERR_HIP;
+  }
+  if (launch_chunk_desc(io->res_idx, (int)heads, s->n_resid, p.n_chunks, s->chunk, io->res_chunk_desc, hs) !=
+      hipSuccess)
     return LOWRAM_ERR_HIP;
   return LOWRAM_OK;
 }

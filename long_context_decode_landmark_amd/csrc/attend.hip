@@ -127,11 +127,6 @@ __device__ __forceinline__ bf16x8 lds16(const unsigned char* base, int off) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + off));
 }
 
-// Row order of a staged 32-row block: position 16 m + 4 g + e holds row
-// 8 g + 4 m + e (m < 2), see the file comment.
-__device__ __forceinline__ constexpr int row_perm32(int pos) {
-  return 8 * ((pos >> 2) & 3) + 4 * (pos >> 4) + (pos & 3);
-}
 
 // Softmax state of one wave's 16 NT tokens for query head j = col: the logits
 // z[t][j] sit in rows t = 16 nt + 4 grp + e of zacc[nt].  Returns the wave's

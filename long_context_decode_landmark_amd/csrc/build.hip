@@ -1,0 +1,541 @@
+// Cache builder (prefill side) of the LowRAM compressed cache, gfx950.
+//
+// From a layer group's exact pre-RoPE keys, its shared basis, each layer's
+// values and value MLP, it writes every array the decode step reads:
+//   coefficients  C = X B^T of the prefix tokens (LowRAM review, key
+//                 paragraph: cross-layer low-rank keys; LowRAM explainer,
+//                 "How the method works": low-rank keys), bf16 or int4 g32
+//   basis blocks  this layer's columns of B, transposed per KV head
+//   landmarks     the mean post-RoPE key of each chunk (review, key paragraph)
+//   residuals     R = V - MLP(K_pre) against the keys decode rebuilds from the
+//                 STORED coefficients; per KV head the n_resid prefix tokens
+//                 with the largest ||R||, ascending (review, value paragraph;
+//                 explainer, "Residuals for difficult tokens")
+//   window        the last W tokens exact: post-RoPE keys and values
+// The per-token predictions MLP(K_pre) are computed to fp32 accuracy (exact
+// three-piece bf16 operands on MFMA, erf GELU), so the residual ranking is the
+// exact one up to fp32 rounding; decode's own bf16 prediction differs from it
+// only by decode's rounding, which its output tolerance covers.
+#include <cmath>
+
+#include "common.h"
+#include "internal.h"
+
+namespace lowram {
+
+// ---------------------------------------------------------------------------
+// Projection C[t][m] = sum_j X[t][j] B[m][j] over the P prefix tokens, with
+// the storage encoding fused into the epilogue.
+//   workgroup tile  128 tokens x TN basis rows (TN = 128, or 64 at rank 64)
+//   waves           2 x 2; wave (wm, wn) owns 64 tokens x TN/2 rows
+//   k loop          64 columns per stage; X and B tiles go global -> VGPR ->
+//                   LDS (double buffered, rows of 128 B with the 16-byte
+//                   pieces XOR-swizzled by row & 7), one barrier per stage
+//   epilogue        fp32 tile to LDS, then one thread per group of 32 rows
+//                   writes bf16 or int4 codes + fp16 scale
+// ---------------------------------------------------------------------------
+constexpr int kProjTM = 128;
+constexpr int kProjBK = 64;
+
+template <int TN>
+struct ProjLds {
+  static constexpr int kStage = (kProjTM + TN) * kProjBK * 2;
+  static constexpr int kTileStride = TN + 4;  // padded fp32 row of the epilogue tile
+  static constexpr int kTile = kProjTM * kTileStride * 4;
+  static constexpr int kBytes = 2 * kStage > kTile ? 2 * kStage : kTile;
+};
+
+__device__ __forceinline__ int swz(int row, int piece) { return row * 128 + ((piece ^ (row & 7)) << 4); }
+
+// fp32 group of 32 -> bf16 (RNE) or int4 codes (symmetric, scale =
+// fp16(absmax / 7), code = clamp(rint(x / scale), -7, 7), even element in the
+// low nibble; an all-zero group stores scale 0 and zero codes).
+__device__ __forceinline__ void encode_group32(const float* __restrict__ x, bool int4,
+                                               uint16_t* __restrict__ bf, uint8_t* __restrict__ codes,
+                                               uint16_t* __restrict__ scale) {
+  if (!int4) {
+#pragma unroll
+    for (int i = 0; i < 32; i += 8) {
+      f32x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = x[i + e];
+        hi[e] = x[i + 4 + e];
+      }
+      *reinterpret_cast<bf16x8*>(bf + i) = pack8(lo, hi);
+    }
+    return;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const _Float16 sh = static_cast<_Float16>(amax / 7.0f);
+  const float s = static_cast<float>(sh);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (s > 0.f) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float q = fminf(fmaxf(rintf(x[i] / s), -7.f), 7.f);
+      w[i >> 3] |= (static_cast<uint32_t>(static_cast<int>(q)) & 0xFu) << (4 * (i & 7));
+    }
+  }
+  *reinterpret_cast<u32x4*>(codes) = u32x4{w[0], w[1], w[2], w[3]};
+  *scale = __builtin_bit_cast(uint16_t, sh);
+}
+
+struct ProjArgs {
+  const uint16_t* keys;   // [NB][T][D]
+  const uint16_t* basis;  // [NB][r][D]
+  void* coeff;            // bf16 [NB][P][r] or int4 [NB][P][r/2]
+  uint16_t* scale;        // int4: [NB][P][r/32]
+  int T, P, D, r, n_tb, n_rb, total, padded_total;
+  bool int4;
+};
+
+template <int TN>
+__global__ __launch_bounds__(256, 2) void proj_kernel(const ProjArgs a) {
+  using L = ProjLds<TN>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[L::kBytes];
+  constexpr int NTW = TN / 32;       // n-tiles per wave
+  constexpr int BPC = TN * 8 / 256;  // B pieces per thread per stage
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 4, col = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int logical = xcd_logical_block(blockIdx.x, a.padded_total);
+  if (logical >= a.total) return;
+  const int rb = logical % a.n_rb;
+  const int tb = (logical / a.n_rb) % a.n_tb;
+  const int b = logical / (a.n_rb * a.n_tb);
+  const int t0 = tb * kProjTM, m0 = rb * TN;
+  const uint16_t* xs = a.keys + (size_t)b * a.T * a.D;
+  const uint16_t* bs = a.basis + ((size_t)b * a.r + m0) * a.D;
+
+  // staging assignment: piece tid % 8 of rows tid / 8 + 32 u
+  const int srow = tid >> 3, spc = tid & 7;
+  u32x4 xa[4], xb[BPC];
+  auto load_stage = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = min(t0 + srow + 32 * u, a.P - 1);
+      xa[u] = *reinterpret_cast<const u32x4*>(xs + (size_t)t * a.D + k0 + 8 * spc);
+    }
+#pragma unroll
+    for (int u = 0; u < BPC; ++u)
+      xb[u] = *reinterpret_cast<const u32x4*>(bs + (size_t)(srow + 32 * u) * a.D + k0 + 8 * spc);
+  };
+  auto store_stage = [&](int buf) {
+    unsigned char* sa = lds + buf * L::kStage;
+    unsigned char* sb = sa + kProjTM * 128;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(sa + swz(srow + 32 * u, spc)) = xa[u];
+#pragma unroll
+    for (int u = 0; u < BPC; ++u) *reinterpret_cast<u32x4*>(sb + swz(srow + 32 * u, spc)) = xb[u];
+  };
+
+  f32x4 acc[4][NTW];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = a.D / kProjBK;
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int kb = 0; kb < nk; ++kb) {
+    const int cur = kb & 1;
+    if (kb + 1 < nk) load_stage((kb + 1) * kProjBK);
+    const unsigned char* sa = lds + cur * L::kStage;
+    const unsigned char* sb = sa + kProjTM * 128;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 av[4], bv[NTW];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        av[mt] = __builtin_bit_cast(bf16x8,
+                                    *reinterpret_cast<const u32x4*>(sa + swz(64 * wm + 16 * mt + col, 4 * ks + grp)));
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+        bv[nt] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(sb + swz((TN / 2) * wn + 16 * nt + col, 4 * ks + grp)));
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = mfma16(av[mt], bv[nt], acc[mt][nt]);
+    }
+    if (kb + 1 < nk) store_stage(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: D[token][row] -> LDS tile, then encode groups of 32 rows
+  float* tile = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        tile[(64 * wm + 16 * mt + 4 * grp + e) * L::kTileStride + (TN / 2) * wn + 16 * nt + col] = acc[mt][nt][e];
+  __syncthreads();
+  constexpr int GPT = TN / 32;  // groups per token row of the tile
+  for (int gi = tid; gi < kProjTM * GPT; gi += 256) {
+    const int tl = gi / GPT, j = gi % GPT;
+    const int t = t0 + tl;
+    if (t >= a.P) continue;
+    const size_t row = (size_t)b * a.P + t;
+    const int m = m0 + 32 * j;
+    if (a.int4)
+      encode_group32(tile + tl * L::kTileStride + 32 * j, true, nullptr,
+                     static_cast<uint8_t*>(a.coeff) + row * (a.r / 2) + m / 2, a.scale + row * (a.r / 32) + m / 32);
+    else
+      encode_group32(tile + tl * L::kTileStride + 32 * j, false, static_cast<uint16_t*>(a.coeff) + row * a.r + m,
+                     nullptr, nullptr);
+  }
+}
+
+hipError_t launch_proj(const uint16_t* keys, const uint16_t* basis, void* coeff, uint16_t* scale, int nb, int T,
+                       int P, int D, int r, bool int4, hipStream_t st) {
+  if (P == 0) return hipSuccess;
+  ProjArgs a{};
+  a.keys = keys; a.basis = basis; a.coeff = coeff; a.scale = scale;
+  a.T = T; a.P = P; a.D = D; a.r = r; a.int4 = int4;
+  const int tn = r >= 128 ? 128 : 64;
+  a.n_tb = (P + kProjTM - 1) / kProjTM;
+  a.n_rb = r / tn;
+  a.total = nb * a.n_tb * a.n_rb;
+  a.padded_total = (a.total + 7) & ~7;
+  if (tn == 128) hipLaunchKernelGGL(proj_kernel<128>, dim3(a.padded_total), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(proj_kernel<64>, dim3(a.padded_total), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-layer arrays that need no MLP: basis blocks, landmarks, window.
+// ---------------------------------------------------------------------------
+
+// RoPE rotation (cos, sin) of an angle: fp64 library sincos rounded to fp32
+// (one evaluation per key element; not a hot loop).
+__device__ __forceinline__ float2 build_rot(double angle) {
+  double s, c;
+  sincos(angle, &s, &c);
+  return make_float2(static_cast<float>(c), static_cast<float>(s));
+}
+
+// Basis blocks: blk[b][h][i][m] = B[b][m][col(layer, h, i)].
+// Grid (r / 64, Hkv, NB); LDS transpose of a 64 x 128 block.
+__global__ __launch_bounds__(256) void basis_block_kernel(const uint16_t* __restrict__ basis,
+                                                          uint16_t* __restrict__ blk, const BuildGeo g) {
+  __shared__ uint16_t tile[64][kHeadDim + 2];
+  const int m0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int col0 = (g.layer_in_group * g.hkv + h) * kHeadDim;
+  const uint16_t* bs = basis + (size_t)b * g.r * g.D;
+  for (int idx = tid; idx < 64 * kHeadDim; idx += 256) {
+    const int m = idx / kHeadDim, i = idx % kHeadDim;
+    tile[m][i] = bs[(size_t)(m0 + m) * g.D + col0 + i];
+  }
+  __syncthreads();
+  uint16_t* o = blk + ((size_t)b * g.hkv + h) * kHeadDim * g.r;
+  for (int idx = tid; idx < 64 * kHeadDim; idx += 256) {
+    const int i = idx / 64, m = idx % 64;
+    o[(size_t)i * g.r + m0 + m] = tile[m][i];
+  }
+}
+
+// Landmarks: one wave per (chunk, head), lane p owns the rotate-half pair
+// (p, p + 64); the chunk's S keys are rotated at their positions and averaged
+// in fp32.  Grid (ceil(nC / 4), Hkv, NB).
+__global__ __launch_bounds__(256) void landmark_kernel(const uint16_t* __restrict__ keys, uint16_t* __restrict__ lm,
+                                                       const BuildGeo g) {
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6), p = threadIdx.x & 63, h = blockIdx.y, b = blockIdx.z;
+  if (c >= g.n_chunks) return;
+  const uint16_t* xs = keys + (size_t)b * g.T * g.D + (g.layer_in_group * g.hkv + h) * kHeadDim;
+  float y1 = 0.f, y2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i) {
+    const int t = c * kChunk + i;
+    const float x1 = bf16_to_f32(xs[(size_t)t * g.D + p]);
+    const float x2 = bf16_to_f32(xs[(size_t)t * g.D + p + 64]);
+    const float2 cs = build_rot((double)t * g.inv_freq[p]);
+    y1 += x1 * cs.x - x2 * cs.y;
+    y2 += x2 * cs.x + x1 * cs.y;
+  }
+  uint16_t* o = lm + (((size_t)b * g.hkv + h) * g.n_chunks + c) * kHeadDim;
+  o[p] = __builtin_bit_cast(uint16_t, (__bf16)(y1 * (1.0f / kChunk)));
+  o[p + 64] = __builtin_bit_cast(uint16_t, (__bf16)(y2 * (1.0f / kChunk)));
+}
+
+// Window: rotated keys and the values of tokens P .. T-1.
+// Grid (ceil(W / 4), Hkv, NB), one wave per token.
+__global__ __launch_bounds__(256) void window_kernel(const uint16_t* __restrict__ keys,
+                                                     const uint16_t* __restrict__ values, uint16_t* __restrict__ wk,
+                                                     uint16_t* __restrict__ wv, const BuildGeo g) {
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6), p = threadIdx.x & 63, h = blockIdx.y, b = blockIdx.z;
+  if (w >= g.W) return;
+  const int t = g.P + w;
+  const size_t head = (size_t)b * g.hkv + h;
+  const uint16_t* xr = keys + ((size_t)b * g.T + t) * g.D + (g.layer_in_group * g.hkv + h) * kHeadDim;
+  const float x1 = bf16_to_f32(xr[p]);
+  const float x2 = bf16_to_f32(xr[p + 64]);
+  const float2 cs = build_rot((double)t * g.inv_freq[p]);
+  uint16_t* ko = wk + (head * g.W + w) * kHeadDim;
+  ko[p] = __builtin_bit_cast(uint16_t, (__bf16)(x1 * cs.x - x2 * cs.y));
+  ko[p + 64] = __builtin_bit_cast(uint16_t, (__bf16)(x2 * cs.x + x1 * cs.y));
+  const uint16_t* vi = values + (head * g.T + t) * kHeadDim;
+  uint16_t* vo = wv + (head * g.W + w) * kHeadDim;
+  vo[p] = vi[p];
+  vo[p + 64] = vi[p + 64];
+}
+
+// ---------------------------------------------------------------------------
+// Residual side.
+// ---------------------------------------------------------------------------
+
+// Three bf16 pieces whose sum is the fp32 value (8 + 8 + 8 significand bits
+// cover fp32's 24), for 8 floats: (lo4, hi4) = s0 + s1 + s2.  Products with a
+// bf16 weight are then exact in the MFMA and only its fp32 accumulation rounds.
+__device__ __forceinline__ void split3(f32x4 lo4, f32x4 hi4, bf16x8 (&s)[3]) {
+  s[0] = pack8(lo4, hi4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo4[e] -= (float)s[0][e];
+    hi4[e] -= (float)s[0][4 + e];
+  }
+  s[1] = pack8(lo4, hi4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo4[e] -= (float)s[1][e];
+    hi4[e] -= (float)s[1][4 + e];
+  }
+  s[2] = pack8(lo4, hi4);
+}
+
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+
+struct PredictArgs {
+  const void* coeff;            // bf16 [NB][P][r] or int4 [NB][P][r/2]
+  const uint16_t* coeff_scale;  // int4: [NB][P][r/32]
+  const uint16_t* blk;          // [NB][Hkv][d][r]
+  const uint16_t *w1, *b1, *w2, *b2;
+  const uint16_t* values;       // [NB][Hkv][T][d]
+  float* r;                     // out [NB][Hkv][P][d]
+  uint32_t* keys;               // out [NB][Hkv][P]
+  int T, P, hkv, n_tb, total, padded_total;
+};
+
+constexpr int kPredTokWG = 128;  // 4 waves x 32 tokens
+
+// Residuals of every prefix token of one KV head against an fp32-accurate
+// prediction: K^T = blk C^T (rebuilt pre-RoPE keys), Z^T = W1 K^T + b1,
+// V~^T = W2 gelu(Z)^T + b2, R = V - V~ and the selection key of ||R||.
+// Tokens are the MFMA column dimension (wave: 2 tiles of 16 tokens), so each
+// weight fragment loaded serves 2 (x 3 pieces) products; the A rows of blk
+// and W1 are taken in row_perm32 order so each product's accumulators are the
+// next one's B operand.  No LDS and no barriers: waves are independent.
+template <int RANK, bool CI4>
+__global__ __launch_bounds__(256) void predict_resid_kernel(const PredictArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 4, col = lane & 15;
+  const int logical = xcd_logical_block(blockIdx.x, a.padded_total);
+  if (logical >= a.total) return;
+  const int h = logical % a.hkv;
+  const int tb = (logical / a.hkv) % a.n_tb;
+  const int b = logical / (a.hkv * a.n_tb);
+  const size_t head = (size_t)b * a.hkv + h;
+  const int t0 = tb * kPredTokWG + 32 * wave;
+  if (t0 >= a.P) return;
+  int tok[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) tok[tt] = min(t0 + 16 * tt + col, a.P - 1);
+
+  // K^T[i][t] = sum_m blk[i][m] C[t][m]
+  const uint16_t* blk = a.blk + head * kHeadDim * RANK;
+  f32x4 kacc[8][2];
+#pragma unroll
+  for (int it = 0; it < 8; ++it)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) kacc[it][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int ks = 0; ks < RANK / 32; ++ks) {
+    bf16x8 cb[2][CI4 ? 2 : 1];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const size_t row = (size_t)b * a.P + tok[tt];
+      if constexpr (!CI4) {
+        cb[tt][0] = load_bf16x8(static_cast<const uint16_t*>(a.coeff) + row * RANK + 32 * ks + 8 * grp);
+      } else {
+        // code * scale has at most 15 significant bits: two bf16 pieces hold it exactly
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.coeff) +
+                                                              row * (RANK / 2) + 16 * ks + 4 * grp);
+        const float sc = f16_to_f32(a.coeff_scale[row * (RANK / 32) + ks]);
+        f32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = (float)(((int)(w << (28 - 4 * e))) >> 28) * sc;
+          hi[e] = (float)(((int)(w << (12 - 4 * e))) >> 28) * sc;
+        }
+        cb[tt][0] = pack8(lo, hi);
+        cb[tt][1] = pack8_lo(lo, hi, cb[tt][0]);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int irow = 32 * (it >> 1) + row_perm32(16 * (it & 1) + col);
+      const bf16x8 af = load_bf16x8(blk + irow * RANK + 32 * ks + 8 * grp);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int sp = 0; sp < (CI4 ? 2 : 1); ++sp) kacc[it][tt] = mfma16(af, cb[tt][sp], kacc[it][tt]);
+    }
+  }
+  // B operands of the next product: k-step s (i = 32 s + 8 g + 0..7) from tiles 2 s, 2 s + 1
+  bf16x8 kb[4][2][3];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) split3(kacc[2 * s][tt], kacc[2 * s + 1][tt], kb[s][tt]);
+
+  const uint16_t* w1 = a.w1 + head * kHidden * kHeadDim;
+  const uint16_t* b1 = a.b1 + head * kHidden;
+  const uint16_t* w2 = a.w2 + head * kHeadDim * kHidden;
+  f32x4 vacc[8][2];
+#pragma unroll
+  for (int nd = 0; nd < 8; ++nd)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) vacc[nd][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int jb = 0; jb < kHidden / 32; ++jb) {
+    // Z^T for hidden units 32 jb .. 32 jb + 31 (tiles jt = 0, 1)
+    f32x4 z[2][2];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      f32x4 bias;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bias[e] = bf16_to_f32(b1[32 * jb + 8 * grp + 4 * jt + e]);
+      z[jt][0] = bias;
+      z[jt][1] = bias;
+      const int jrow = 32 * jb + row_perm32(16 * jt + col);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 af = load_bf16x8(w1 + jrow * kHeadDim + 32 * s + 8 * grp);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int sp = 0; sp < 3; ++sp) z[jt][tt] = mfma16(af, kb[s][tt][sp], z[jt][tt]);
+      }
+    }
+    bf16x8 hb[2][3];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[jt][tt][e] = gelu_erf(z[jt][tt][e]);
+      split3(z[0][tt], z[1][tt], hb[tt]);
+    }
+#pragma unroll
+    for (int nd = 0; nd < 8; ++nd) {
+      const bf16x8 af = load_bf16x8(w2 + (16 * nd + col) * kHidden + 32 * jb + 8 * grp);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp) vacc[nd][tt] = mfma16(af, hb[tt][sp], vacc[nd][tt]);
+    }
+  }
+
+  // R = V - (V~ + b2) for d = 16 nd + 4 g + e, token column col
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = t0 + 16 * tt + col;
+    const bool valid = t < a.P;
+    const uint16_t* vr = a.values + (head * a.T + tok[tt]) * kHeadDim;
+    float* rr = a.r + (head * a.P + tok[tt]) * kHeadDim;
+    float ss = 0.f;
+#pragma unroll
+    for (int nd = 0; nd < 8; ++nd) {
+      const int d0 = 16 * nd + 4 * grp;
+      const u32x2 vv = *reinterpret_cast<const u32x2*>(vr + d0);
+      f32x4 res;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t vb = (uint16_t)(vv[e >> 1] >> (16 * (e & 1)));
+        res[e] = bf16_to_f32(vb) - (vacc[nd][tt][e] + bf16_to_f32(a.b2[head * kHeadDim + d0 + e]));
+        ss = fmaf(res[e], res[e], ss);
+      }
+      if (valid) *reinterpret_cast<f32x4*>(rr + d0) = res;
+    }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    if (valid && grp == 0) a.keys[head * a.P + t] = score_key(sqrtf(ss));
+  }
+}
+
+// Selected residual rows -> storage format; one thread per (row, group of 32).
+__global__ __launch_bounds__(256) void resid_store_kernel(const float* __restrict__ r, const int32_t* __restrict__ idx,
+                                                          void* __restrict__ res_val, uint16_t* __restrict__ res_scale,
+                                                          size_t n_rows, const BuildGeo g, bool int4) {
+  const size_t gi = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (gi >= n_rows * 4) return;
+  const size_t row = gi >> 2;  // (b * Hkv + h) * nR + i
+  const int j = (int)(gi & 3);
+  const size_t head = row / (size_t)g.n_resid;
+  const int t = idx[row];
+  const float* src = r + (head * g.P + t) * kHeadDim + 32 * j;
+  if (int4)
+    encode_group32(src, true, nullptr, static_cast<uint8_t*>(res_val) + row * (kHeadDim / 2) + 16 * j,
+                   res_scale + row * (kHeadDim / 32) + j);
+  else
+    encode_group32(src, false, static_cast<uint16_t*>(res_val) + row * kHeadDim + 32 * j, nullptr, nullptr);
+}
+
+hipError_t launch_build_layer_arrays(const uint16_t* keys, const uint16_t* values, const uint16_t* basis,
+                                     uint16_t* blk, uint16_t* lm, uint16_t* wk, uint16_t* wv, const BuildGeo& g,
+                                     hipStream_t st) {
+  hipLaunchKernelGGL(basis_block_kernel, dim3(g.r / 64, g.hkv, g.nb), dim3(256), 0, st, basis, blk, g);
+  if (g.n_chunks > 0)
+    hipLaunchKernelGGL(landmark_kernel, dim3((g.n_chunks + 3) / 4, g.hkv, g.nb), dim3(256), 0, st, keys, lm, g);
+  if (g.W > 0)
+    hipLaunchKernelGGL(window_kernel, dim3((g.W + 3) / 4, g.hkv, g.nb), dim3(256), 0, st, keys, values, wk, wv, g);
+  return hipGetLastError();
+}
+
+template <int RANK>
+static void launch_predict_rank(const PredictArgs& a, bool ci4, hipStream_t st) {
+  if (ci4) hipLaunchKernelGGL((predict_resid_kernel<RANK, true>), dim3(a.padded_total), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((predict_resid_kernel<RANK, false>), dim3(a.padded_total), dim3(256), 0, st, a);
+}
+
+hipError_t launch_predict_resid(const void* coeff, const uint16_t* coeff_scale, const uint16_t* blk,
+                                const uint16_t* w1, const uint16_t* b1, const uint16_t* w2, const uint16_t* b2,
+                                const uint16_t* values, float* r, uint32_t* keys, bool ci4, const BuildGeo& g,
+                                hipStream_t st) {
+  if (g.P == 0) return hipSuccess;
+  PredictArgs a{};
+  a.coeff = coeff; a.coeff_scale = coeff_scale; a.blk = blk;
+  a.w1 = w1; a.b1 = b1; a.w2 = w2; a.b2 = b2; a.values = values; a.r = r; a.keys = keys;
+  a.T = g.T; a.P = g.P; a.hkv = g.hkv;
+  a.n_tb = (g.P + kPredTokWG - 1) / kPredTokWG;
+  a.total = g.nb * g.hkv * a.n_tb;
+  a.padded_total = (a.total + 7) & ~7;
+  switch (g.r) {
+    case 64:
+      if (ci4) return hipErrorInvalidValue;  // int4 coefficients need rank % 128 == 0
+      launch_predict_rank<64>(a, false, st);
+      break;
+    case 128: launch_predict_rank<128>(a, ci4, st); break;
+    case 256: launch_predict_rank<256>(a, ci4, st); break;
+    case 512: launch_predict_rank<512>(a, ci4, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_store(const float* r, const int32_t* idx, void* res_val, uint16_t* res_scale,
+                              const BuildGeo& g, bool int4, hipStream_t st) {
+  const size_t n_rows = (size_t)g.nb * g.hkv * g.n_resid;
+  if (n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(resid_store_kernel, dim3((unsigned)((n_rows * 4 + 255) / 256)), dim3(256), 0, st, r, idx,
+                     res_val, res_scale, n_rows, g, int4);
+  return hipGetLastError();
+}
+
+}  // namespace lowram

@@ -22,6 +22,16 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Row order of a 32-row operand block: position 16 m + 4 g + e holds row
+// 8 g + 4 m + e (m, g, e: m < 2, g < 4, e < 4).  With the A rows of MFMA tiles
+// 2 s and 2 s + 1 taken in this order, the accumulators a lane (group g)
+// receives for one output column are rows 32 s + 8 g + 0..7 in natural order:
+// exactly the 8 consecutive k values that lane supplies as a B operand of a
+// following MFMA, so a chain of products needs no transpose.
+__device__ __forceinline__ constexpr int row_perm32(int pos) {
+  return 8 * ((pos >> 2) & 3) + 4 * (pos >> 4) + (pos & 3);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
   return __uint_as_float(static_cast<uint32_t>(u) << 16);
 }

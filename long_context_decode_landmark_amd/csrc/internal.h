@@ -59,4 +59,22 @@ hipError_t launch_dense(const uint16_t* k, const uint16_t* v, const uint16_t* q,
 hipError_t launch_chunk_desc(const int32_t* res_idx, int n_lists, int n_resid, int n_chunks,
                              int chunk, uint32_t* desc, hipStream_t st);
 
+// Cache builder.
+struct BuildGeo {
+  int nb, T, P, W, D, r, hkv, layer_in_group, n_chunks, n_resid;
+  double inv_freq[64];
+};
+
+hipError_t launch_proj(const uint16_t* keys, const uint16_t* basis, void* coeff, uint16_t* scale, int nb,
+                       int T, int P, int D, int r, bool int4, hipStream_t st);
+hipError_t launch_build_layer_arrays(const uint16_t* keys, const uint16_t* values, const uint16_t* basis,
+                                     uint16_t* blk, uint16_t* lm, uint16_t* wk, uint16_t* wv,
+                                     const BuildGeo& g, hipStream_t st);
+hipError_t launch_predict_resid(const void* coeff, const uint16_t* coeff_scale, const uint16_t* blk,
+                                const uint16_t* w1, const uint16_t* b1, const uint16_t* w2, const uint16_t* b2,
+                                const uint16_t* values, float* r, uint32_t* keys, bool ci4, const BuildGeo& g,
+                                hipStream_t st);
+hipError_t launch_resid_store(const float* r, const int32_t* idx, void* res_val, uint16_t* res_scale,
+                              const BuildGeo& g, bool int4, hipStream_t st);
+
 }  // namespace lowram

@@ -27,6 +27,9 @@ SYMBOLS = (
     "dense_workspace_bytes",
     "dense_decode_step",
     "lowram_resid_chunk_desc",
+    "lowram_build_coeff",
+    "lowram_build_layer_workspace_bytes",
+    "lowram_build_layer",
 )
 
 ERRORS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "UNSUPPORTED", -4: "WORKSPACE", -5: "ALIGN", -6: "HIP"}
@@ -45,6 +48,20 @@ CACHE_FIELDS = ("coeff", "coeff_scale", "basis", "landmark", "cand_ids", "w1", "
 
 class LowramLayerCache(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in CACHE_FIELDS]
+
+
+class LowramBuildShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "ctx_len", "window", "chunk", "n_heads_kv", "head_dim", "rank", "group_layers",
+        "mlp_hidden", "n_resid", "coeff_fmt", "resid_fmt")] + [("rope_theta", ctypes.c_float)]
+
+
+BUILD_FIELDS = ("keys", "group_basis", "coeff", "coeff_scale", "values", "w1", "b1", "w2", "b2",
+                "basis", "landmark", "res_idx", "res_val", "res_scale", "res_chunk_desc", "win_k", "win_v")
+
+
+class LowramLayerBuild(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BUILD_FIELDS]
 
 
 class DenseShape(ctypes.Structure):
@@ -89,6 +106,10 @@ def lib() -> ctypes.CDLL:
                                         vp, vp, vp, sz, vp]
         L.lowram_resid_chunk_desc.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.c_int32, vp, vp]
+        L.lowram_build_coeff.argtypes = [ctypes.POINTER(LowramBuildShape), vp, vp, vp, vp, vp]
+        L.lowram_build_layer_workspace_bytes.argtypes = [ctypes.POINTER(LowramBuildShape), ctypes.POINTER(sz)]
+        L.lowram_build_layer.argtypes = [ctypes.POINTER(LowramBuildShape), ctypes.c_int32,
+                                         ctypes.POINTER(LowramLayerBuild), vp, sz, vp]
         for name in SYMBOLS:
             getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
         L.lowram_strerror.restype = ctypes.c_char_p
@@ -199,3 +220,36 @@ def resid_chunk_desc(res_idx, n_lists: int, n_resid: int, n_chunks: int, chunk: 
     """res_idx [n_lists][n_resid] int32 (ascending rows) -> out [n_lists][n_chunks] uint32 (int32 tensor)."""
     _check(lib().lowram_resid_chunk_desc(_ptr(res_idx), n_lists, n_resid, n_chunks, chunk, _ptr(out),
                                          _stream(stream)), "lowram_resid_chunk_desc")
+
+
+# ------------------------------------------------------------ cache builder --
+def make_build_shape(cfg, batch: int | None = None, **over) -> LowramBuildShape:
+    """lowram_build_shape of a workload (synth.Config-like object)."""
+    f = dict(batch=cfg.batch if batch is None else batch, ctx_len=cfg.ctx, window=cfg.window,
+             chunk=cfg.chunk, n_heads_kv=cfg.n_heads_kv, head_dim=cfg.head_dim, rank=cfg.rank,
+             group_layers=cfg.group_layers, mlp_hidden=cfg.mlp_hidden, n_resid=cfg.n_resid,
+             coeff_fmt=FMT_INT4_G32 if cfg.int4 else FMT_BF16,
+             resid_fmt=FMT_INT4_G32 if cfg.int4 else FMT_BF16, rope_theta=cfg.rope_theta)
+    f.update(over)
+    return LowramBuildShape(**f)
+
+
+def build_coeff(shape, keys, basis, coeff, coeff_scale=None, stream=None) -> None:
+    """lowram_build_coeff: keys [NB][T][D], basis [NB][r][D] -> coeff (+ scales)."""
+    _check(lib().lowram_build_coeff(ctypes.byref(shape), _ptr(keys), _ptr(basis), _ptr(coeff), _ptr(coeff_scale),
+                                    _stream(stream)), "lowram_build_coeff")
+
+
+def build_layer_workspace_bytes(shape: LowramBuildShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().lowram_build_layer_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)),
+           "lowram_build_layer_workspace_bytes")
+    return n.value
+
+
+def build_layer(shape, layer_in_group: int, io: dict, workspace, stream=None) -> None:
+    """lowram_build_layer; io maps the lowram_layer_build field names to device tensors (or None)."""
+    b = LowramLayerBuild(**{n: (io[n].data_ptr() if io.get(n) is not None else None) for n in BUILD_FIELDS})
+    _check(lib().lowram_build_layer(ctypes.byref(shape), layer_in_group, ctypes.byref(b), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)),
+           "lowram_build_layer")

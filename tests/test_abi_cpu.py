@@ -154,3 +154,78 @@ def test_chunk_desc_rejects():
     with pytest.raises(native.LowramError) as e:
         native.resid_chunk_desc(FakeTensor(0x1000), 4, 16, 10, 16, FakeTensor(0x2000), stream=0)
     assert e.value.status == -3
+
+
+# ---------------------------------------------------------- cache builder --
+def bshape(**kw):
+    import synth
+    return native.make_build_shape(synth.C0, **kw)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=5000), -2),            # W > T
+    (dict(window=63), -2),              # P % S
+    (dict(n_resid=5000), -2),           # more residuals than prefix tokens
+    (dict(resid_fmt=2), -2),
+    (dict(rope_theta=0.0), -2),
+    (dict(group_layers=0), -2),
+    (dict(head_dim=64), -3),
+    (dict(chunk=16), -3),
+    (dict(rank=96), -3),
+    (dict(mlp_hidden=512), -3),
+    (dict(coeff_fmt=1), -3),            # int4 coefficients need rank % 128 == 0
+])
+def test_build_workspace_rejects_shapes(kw, code):
+    with pytest.raises(native.LowramError) as e:
+        native.build_layer_workspace_bytes(bshape(**kw))
+    assert e.value.status == code
+
+
+def test_build_workspace_formula():
+    import synth
+    cfg = synth.C3
+    s = native.make_build_shape(cfg, batch=2)
+    heads, P = 2 * cfg.n_heads_kv, cfg.prefix
+    r_bytes = -(-heads * P * 128 * 4 // 256) * 256
+    assert native.build_layer_workspace_bytes(s) == r_bytes + -(-heads * P * 4 // 256) * 256
+    assert native.build_layer_workspace_bytes(bshape(window=4096, n_resid=0)) == 0   # no prefix
+
+
+def build_io(**over):
+    io = {n: FakeTensor(0x7000000000 + 0x1000000 * i) for i, n in enumerate(native.BUILD_FIELDS)}
+    io.update(over)
+    return io
+
+
+def call_build(s, io, layer=0, ws=None):
+    ws = ws or FakeTensor(0x7f00000000, n=native.build_layer_workspace_bytes(s))
+    with pytest.raises(native.LowramError) as e:
+        native.build_layer(s, layer, io, ws, stream=0)
+    return e.value.status
+
+
+def test_build_layer_rejects():
+    s = bshape()
+    for n in ("keys", "group_basis", "basis", "coeff", "w1", "values", "landmark", "res_idx", "res_val",
+              "res_chunk_desc", "win_k"):
+        assert call_build(s, build_io(**{n: None})) == -1, n
+    assert call_build(s, build_io(), layer=2) == -2              # C0 has 2 layers per group
+    assert call_build(s, build_io(landmark=FakeTensor(0x10000008))) == -5
+    need = native.build_layer_workspace_bytes(s)
+    assert call_build(s, build_io(), ws=FakeTensor(0x7f00000000, n=need - 1)) == -4
+    s4 = bshape(rank=128, coeff_fmt=1, resid_fmt=1)
+    assert call_build(s4, build_io(coeff_scale=None)) == -1
+    assert call_build(s4, build_io(res_scale=None)) == -1
+
+
+def test_build_coeff_rejects():
+    with pytest.raises(native.LowramError) as e:
+        native.build_coeff(bshape(), FakeTensor(0x1000), None, FakeTensor(0x3000), stream=0)
+    assert e.value.status == -1
+    with pytest.raises(native.LowramError) as e:
+        native.build_coeff(bshape(), FakeTensor(0x1008), FakeTensor(0x2000), FakeTensor(0x3000), stream=0)
+    assert e.value.status == -5
+    with pytest.raises(native.LowramError) as e:
+        native.build_coeff(bshape(rank=128, coeff_fmt=1), FakeTensor(0x1000), FakeTensor(0x2000),
+                           FakeTensor(0x3000), stream=0)
+    assert e.value.status == -1                                   # int4 scales missing

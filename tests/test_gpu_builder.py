@@ -1,0 +1,292 @@
+"""GPU parity of the cache builder (lowram_build_coeff + lowram_build_layer).
+
+Both sides get the same bf16 inputs: the group's exact keys and basis, the
+layer's exact values and value MLP.  The oracle compresses them in fp64
+(``oracle.fixture.builder_io``); the GPU's arrays are compared with it:
+
+  basis blocks, window values      bit-exact (pure copies)
+  coefficients, landmarks,         within one bf16 step of the oracle's value
+  window keys, residual rows       (fp32 accumulation / rotation / prediction
+                                   against fp64) and mostly bit-identical;
+                                   int4: scales within one fp16 step, values
+                                   within one quantisation step, codes mostly
+                                   identical
+  residual selection               the GPU's set equals the oracle's except for
+                                   tokens whose oracle error lies within
+                                   SEL_BAND (relative) of the nR-th largest
+  descriptors                      bit-exact against the oracle's descriptors of
+                                   the GPU's own selection
+
+SEL_BAND: the GPU predicts values to fp32 accuracy (exact bf16 pieces on
+MFMA, fp32 accumulation over at most 512 terms, erf GELU): about 1e-6 of
+||V~|| ~ 7 per token, i.e. ~1e-5 of a typical error ||R|| ~ 0.5.  1e-4 leaves
+a factor of ten; a token can change sides only if both its error and the
+threshold move by that much.
+
+Coefficient roundings: the GPU's fp32-accumulated projection rounds a few
+coefficients (~4e-5 of them, already held to one step above) to the other
+neighbour of the fp64 value.  Each side then predicts the values of that
+token from its own stored coefficients.  For such a token t the prediction
+may move by at most L_h * sum_m |dC_tm| ||blk_h[:, m]||, with
+L_h = ||W2||_2 * max gelu' * ||W1||_2 (max gelu' < 1.13) the MLP's Lipschitz
+bound; its residual row and its error are held to that bound instead.
+"""
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+from gpu_util import DEV, up  # noqa: E402
+from long_context_decode_landmark_amd import native  # noqa: E402
+from oracle import codecs, compress, fixture  # noqa: E402
+
+SEL_BAND = 1e-4
+GELU_SLOPE = 1.13  # max over x of d/dx x Phi(x) = 1.1289...
+SENTINEL = 0x7FC1  # a bf16 NaN: any element left unwritten fails the comparisons
+
+
+def host(t):
+    t = t.contiguous().cpu()
+    if t.dtype == torch.int16:
+        return t.numpy().view(np.uint16)
+    if t.dtype == torch.int32:
+        return t.numpy()
+    return t.numpy()
+
+
+def run_builder(cfg, inp, layer, layer_coeff=None):
+    """Run lowram_build_coeff, then lowram_build_layer on ``layer_coeff`` (the
+    oracle's stored coefficients, so both sides predict from identical
+    coefficients) or, if None, on the GPU's own coefficients (chained)."""
+    nb = inp["keys"].shape[0]
+    P, W, r, hkv, d = cfg.prefix, cfg.window, cfg.rank, cfg.n_heads_kv, cfg.head_dim
+    nC, nR = cfg.n_chunks, cfg.n_resid
+    shape = native.make_build_shape(cfg, batch=nb)
+    t = {k: up(v) for k, v in inp.items()}
+
+    def bf(*s):
+        return torch.full(s, SENTINEL, dtype=torch.int16, device=DEV)
+
+    io = dict(t)
+    if cfg.int4:
+        io["coeff"] = torch.full((nb, P, r // 2), 0x88, dtype=torch.uint8, device=DEV)
+        io["coeff_scale"] = bf(nb, P, r // 32)
+        io["res_val"] = torch.full((nb, hkv, nR, d // 2), 0x88, dtype=torch.uint8, device=DEV)
+        io["res_scale"] = bf(nb, hkv, nR, d // 32)
+    else:
+        io["coeff"] = bf(nb, P, r)
+        io["res_val"] = bf(nb, hkv, nR, d)
+    io["basis"] = bf(nb, hkv, d, r)
+    io["landmark"] = bf(nb, hkv, nC, d)
+    io["res_idx"] = torch.full((nb, hkv, nR), -7, dtype=torch.int32, device=DEV)
+    io["res_chunk_desc"] = torch.full((nb, hkv, nC), -7, dtype=torch.int32, device=DEV)
+    io["win_k"] = bf(nb, hkv, W, d)
+    io["win_v"] = bf(nb, hkv, W, d)
+    native.build_coeff(shape, io["keys"], io["group_basis"], io["coeff"], io.get("coeff_scale"))
+    torch.cuda.synchronize()
+    out = {k: host(io[k]) for k in ("coeff", "coeff_scale") if k in io}
+    if layer_coeff is not None:
+        for k, v in layer_coeff.items():
+            io[k] = up(v)
+    out["coeff_used"] = host(io["coeff"])
+    if cfg.int4:
+        out["coeff_scale_used"] = host(io["coeff_scale"])
+    ws = torch.empty(native.build_layer_workspace_bytes(shape), dtype=torch.uint8, device=DEV)
+    native.build_layer(shape, layer % cfg.group_layers, io, ws)
+    torch.cuda.synchronize()
+    out.update({k: host(io[k]) for k in ("res_val", "res_scale", "basis", "landmark", "res_idx",
+                                         "res_chunk_desc", "win_k", "win_v") if k in io})
+    out["res_chunk_desc"] = out["res_chunk_desc"].view(np.uint32)
+    return out
+
+
+def close_bf16(got_bits, ref_bits, what, min_exact=0.99):
+    """Within one bf16 step of the reference (plus an absolute floor near 0)."""
+    g, r = codecs.bf16_decode(got_bits), codecs.bf16_decode(ref_bits)
+    assert g.shape == r.shape, what
+    assert np.all(np.isfinite(g)), what
+    if r.size == 0:
+        return 1.0
+    floor = 1e-5 * float(np.max(np.abs(r)))
+    assert np.all(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + floor), (what, float(np.max(np.abs(g - r))))
+    exact = float(np.mean(got_bits == ref_bits))
+    assert exact >= min_exact, (what, exact)
+    return exact
+
+
+def close_int4(codes_g, scale_g, codes_r, scale_r, what, min_exact=0.99):
+    sg, sr = codecs.fp16_decode(scale_g), codecs.fp16_decode(scale_r)
+    assert np.all(np.isfinite(sg)), what
+    assert np.all(np.abs(sg - sr) <= 2.0 ** -10 * sr + 1e-12), (what, float(np.max(np.abs(sg - sr))))
+    dg, dr = codecs.int4_decode(codes_g, scale_g), codecs.int4_decode(codes_r, scale_r)
+    step = np.repeat(sr, 32, axis=-1)
+    assert np.all(np.abs(dg - dr) <= step * 1.01 + 1e-12), (what, float(np.max(np.abs(dg - dr) - step)))
+    exact = float(np.mean(codecs.int4_codes(codes_g) == codecs.int4_codes(codes_r)))
+    assert exact >= min_exact, (what, exact)
+    return exact
+
+
+def check_layer(cfg, inp, exp, got):
+    nb, hkv, P = inp["keys"].shape[0], cfg.n_heads_kv, cfg.prefix
+    stats = {}
+    assert np.array_equal(got["basis"], exp["basis"]), "basis blocks"
+    assert np.array_equal(got["win_v"], exp["win_v"]), "window values"
+    stats["win_k"] = close_bf16(got["win_k"], exp["win_k"], "window keys")
+    stats["landmark"] = close_bf16(got["landmark"], exp["landmark"], "landmarks")
+    if cfg.int4:
+        stats["coeff"] = close_int4(got["coeff"], got["coeff_scale"], exp["coeff"], exp["coeff_scale"], "coeff")
+    else:
+        stats["coeff"] = close_bf16(got["coeff"], exp["coeff"], "coeff")
+    nR, flips, worst, n_moved = cfg.n_resid, 0, 0.0, 0
+    # coefficients the layer build consumed vs the oracle's (zero unless chained)
+    if cfg.int4:
+        dc = np.abs(codecs.int4_decode(got["coeff_used"], got["coeff_scale_used"]) -
+                    codecs.int4_decode(exp["coeff"], exp["coeff_scale"]))
+    else:
+        dc = np.abs(codecs.bf16_decode(got["coeff_used"]) - codecs.bf16_decode(exp["coeff"]))
+    gv, ov, gs, os_ = [], [], [], []
+    for b in range(nb):
+        for h in range(hkv):
+            # prediction bound of tokens whose stored coefficients differ
+            blk = codecs.bf16_decode(exp["basis"][b, h])
+            w1 = codecs.bf16_decode(inp["w1"][b, h])
+            w2 = codecs.bf16_decode(inp["w2"][b, h])
+            lip = np.linalg.norm(w2, 2) * GELU_SLOPE * np.linalg.norm(w1, 2)
+            bound = lip * (dc[b] @ np.linalg.norm(blk, axis=0))   # [P]
+            moved = bound > 0
+            n_moved += int(np.sum(moved))
+            gi = got["res_idx"][b, h]
+            assert len(gi) == nR
+            if nR:
+                assert np.all(np.diff(gi) > 0) and gi[0] >= 0 and gi[-1] < P, (b, h)
+            err = exp["errors"][b, h]
+            if 0 < nR < P:
+                thr = np.sort(err)[::-1][nR - 1]
+                near = np.abs(err - thr) <= SEL_BAND * thr + bound
+                shift = float(np.max(bound[near & moved], initial=0.0))
+                diff = set(gi.tolist()) ^ set(exp["res_idx"][b, h].tolist())
+                for t in diff:
+                    dist = abs(err[t] - thr)
+                    assert dist <= SEL_BAND * thr + bound[t] + shift, (b, h, t, err[t], thr, bound[t], shift)
+                    if not moved[t]:
+                        worst = max(worst, dist / thr)
+                flips += len(diff)
+            else:
+                assert np.array_equal(gi, exp["res_idx"][b, h])
+            # descriptors of the GPU's own selection
+            assert np.array_equal(got["res_chunk_desc"][b, h], compress.chunk_descriptors(gi, cfg.n_chunks, cfg.chunk))
+            # residual rows of the tokens both sides kept
+            common = np.intersect1d(gi, exp["res_idx"][b, h])
+            rg = np.searchsorted(gi, common)
+            ro = np.searchsorted(exp["res_idx"][b, h], common)
+            mv = moved[common]
+            if cfg.int4:
+                dg = codecs.int4_decode(got["res_val"][b, h, rg[mv]], got["res_scale"][b, h, rg[mv]])
+                do = codecs.int4_decode(exp["res_val"][b, h, ro[mv]], exp["res_scale"][b, h, ro[mv]])
+                store = np.linalg.norm(np.repeat(codecs.fp16_decode(exp["res_scale"][b, h, ro[mv]]), 32, axis=-1),
+                                       axis=-1)
+            else:
+                dg = codecs.bf16_decode(got["res_val"][b, h, rg[mv]])
+                do = codecs.bf16_decode(exp["res_val"][b, h, ro[mv]])
+                store = 2.0 ** -7 * np.linalg.norm(do, axis=-1)
+            e = np.linalg.norm(dg - do, axis=-1)
+            assert np.all(e <= bound[common[mv]] + store), (b, h, common[mv], e, bound[common[mv]])
+            gv.append(got["res_val"][b, h, rg[~mv]])
+            ov.append(exp["res_val"][b, h, ro[~mv]])
+            if cfg.int4:
+                gs.append(got["res_scale"][b, h, rg[~mv]])
+                os_.append(exp["res_scale"][b, h, ro[~mv]])
+    if nR:
+        if cfg.int4:
+            stats["res_val"] = close_int4(np.concatenate(gv), np.concatenate(gs), np.concatenate(ov),
+                                          np.concatenate(os_), "residual rows", min_exact=0.97)
+        else:
+            stats["res_val"] = close_bf16(np.concatenate(gv), np.concatenate(ov), "residual rows", min_exact=0.97)
+    stats["moved_tokens"] = n_moved
+    stats["worst_flip_rel"] = worst
+    stats["flips"] = flips
+    return stats
+
+
+CASES = {
+    "c0_layer0": (synth.C0, 0),
+    "c0_layer1": (synth.C0, 1),
+    "int4_r128": (synth.C0.with_(name="b_int4", rank=128, int4=True, resid_frac=0.25), 1),
+    "no_resid": (synth.C0.with_(name="b_nores", resid_frac=0.0, rank=128), 0),
+    "all_resid": (synth.C0.with_(name="b_allres", ctx=1024, resid_frac=1.0), 1),
+    "no_window": (synth.C0.with_(name="b_nowin", window=0, ctx=2048), 0),
+    "only_window": (synth.C0.with_(name="b_onlywin", ctx=64, window=64), 0),
+    "ragged_b2_r256": (synth.C0.with_(name="b_ragged", batch=2, ctx=4060, window=300, rank=256,
+                                      bias_std=0.1), 1),
+    "r512_g4": (synth.C0.with_(name="b_r512", ctx=2056, window=8, group_layers=2, n_heads_kv=4, rank=512,
+                               n_heads_q=8), 1),
+}
+
+
+def oracle_coeff(exp):
+    return {k: exp[k] for k in ("coeff", "coeff_scale") if k in exp}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_builder_matches_oracle(name):
+    cfg, layer = CASES[name]
+    print(f"\nbuilder {name}: P={cfg.prefix} W={cfg.window} r={cfg.rank} nR={cfg.n_resid} int4={cfg.int4}",
+          flush=True)
+    inp, exp = fixture.builder_io(cfg, layer)
+    got = run_builder(cfg, inp, layer, oracle_coeff(exp))
+    st = check_layer(cfg, inp, exp, got)
+    assert st["moved_tokens"] == 0
+    print(f"builder {name}: {st}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["c0_layer1", "int4_r128", "r512_g4"])
+def test_builder_chained(name):
+    """The layer build on the GPU's own coefficients (as a caller chains them)."""
+    cfg, layer = CASES[name]
+    inp, exp = fixture.builder_io(cfg, layer)
+    got = run_builder(cfg, inp, layer)
+    print(f"\nbuilder chained {name}: {check_layer(cfg, inp, exp, got)}", flush=True)
+
+
+def test_c1_size_layer():
+    """A 32K-token, rank-512, 8-head group (four layers share the basis)."""
+    cfg = synth.C1
+    print(f"\nbuilder c1: P={cfg.prefix} D={cfg.group_dim} r={cfg.rank}", flush=True)
+    inp, exp = fixture.builder_io(cfg, 6)
+    got = run_builder(cfg, inp, 6, oracle_coeff(exp))
+    st = check_layer(cfg, inp, exp, got)
+    assert st["moved_tokens"] == 0
+    print(f"builder c1: {st}", flush=True)
+
+
+def test_built_cache_decodes_like_oracle_cache():
+    """The builder's cache, fed to lowram_decode_step, gives the oracle's decode output."""
+    from gpu_util import check_output
+    from oracle import decode
+    cfg, layer = synth.C0.with_(name="b_decode", batch=2), 1
+    inp, exp = fixture.builder_io(cfg, layer)
+    got = run_builder(cfg, inp, layer)
+    cache = {k: got[k] for k in ("coeff", "basis", "landmark", "res_idx", "res_val", "res_chunk_desc", "win_k",
+                                 "win_v")}
+    for k in ("w1", "b1", "w2", "b2"):
+        cache[k] = inp[k]
+    cache["res_chunk_desc"] = cache["res_chunk_desc"].view(np.int32)
+    q = np.stack([codecs.bf16_encode(synth.queries(cfg, b, layer)) for b in range(cfg.batch)])
+    tc = {k: up(v) for k, v in cache.items()}
+    qd = up(q)
+    out = torch.empty_like(qd)
+    shape = native.make_shape(cfg)
+    ws = torch.empty(native.workspace_bytes(shape), dtype=torch.uint8, device=DEV)
+    sel = torch.empty((cfg.batch, cfg.n_heads_kv, cfg.topk), dtype=torch.int32, device=DEV)
+    native.decode_step(shape, tc, qd, out, ws, sel_out=sel)
+    torch.cuda.synchronize()
+    from gpu_util import down_bf16
+    ref, _ = decode.decode_step(cfg, cache, q, sel_override=sel.cpu().numpy())
+    rel, mx = check_output(down_bf16(out), ref, "built cache")
+    print(f"\nbuilt cache decode: rel {rel:.2e} max {mx:.2e}", flush=True)
