@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-slices", type=int, default=10)
     ap.add_argument("--graph", action="store_true", help="also time a hipGraph replay of the step")
     ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--build", action="store_true",
+                    help="time the cache builder (one layer group of one sequence) instead of the decode step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first copy a buffer of this size 3 times (HBM counter calibration)")
     return ap.parse_args()
@@ -302,12 +304,165 @@ def cpu_baseline(cfg, host, q0, n_slices):
                       f"{dt:.2f} s each, extrapolated x{cfg.n_layers} layers per token"}
 
 
+BUILD_KERNELS = ("proj", "arrays", "predict", "select", "store")
+
+
+def build_algorithmic(cfg, nb):
+    """Algorithmic MFMA flops and HBM bytes of the builder's kernels, per launch.
+
+    proj (one per group): C = X B^T over P tokens: 2 P D r flops; reads X (P x D
+    bf16), B; writes C.  predict (one per layer): per (token, KV head) the
+    rebuild 2 d r, the MLP 2 * 2 d H flops; reads C (once per head), this
+    layer's values, writes the fp32 residual rows and error keys.
+    """
+    P, D, r, Hkv, d, H = cfg.prefix, cfg.group_dim, cfg.rank, cfg.n_heads_kv, cfg.head_dim, cfg.mlp_hidden
+    s_c = 0.5 + 2.0 / 32 if cfg.int4 else 2.0
+    f = {"proj": 2.0 * P * D * r, "predict": Hkv * P * (2.0 * d * r + 4.0 * d * H)}
+    b = {"proj": P * D * 2.0 + r * D * 2.0 + P * r * s_c,
+         "predict": Hkv * P * (r * s_c + d * 2.0 + d * 4.0 + 4.0)}
+    return {k: v * nb for k, v in f.items()}, {k: v * nb for k, v in b.items()}
+
+
+def build_cpu_baseline(cfg, n_tok):
+    """The oracle's compression of the first n_tok prefix tokens of the group
+    (projection) and of one (layer, KV head), scaled to the whole group."""
+    import numpy as np
+    from oracle import codecs, compress
+    import synth
+    sub = cfg.with_(name=cfg.name + "_cpu", ctx=n_tok + cfg.window, resid_frac=cfg.resid_frac)
+    rng = np.random.default_rng(7)
+    x = codecs.bf16_round(synth.exact_keys(sub, 0, 0, 0, n_tok, dtype=np.float32))
+    B = codecs.bf16_round(synth.basis(cfg, 0, 0))
+    t0 = time.perf_counter()
+    c_st = compress.store_coeff(compress.project(x, B), cfg.int4)
+    t_proj = time.perf_counter() - t0
+    cols = synth.layer_cols(cfg, 0, 0)
+    xh = np.concatenate([x[:, cols], rng.standard_normal((cfg.window, cfg.head_dim))])
+    v = rng.standard_normal((n_tok + cfg.window, cfg.head_dim)) * 0.5
+    mlp = tuple(codecs.bf16_encode(a) for a in synth.mlp_weights(cfg, 0, 0, 0))
+    blk = codecs.bf16_encode(compress.basis_block(B, cols))
+    t0 = time.perf_counter()
+    compress.compress_from_kv(sub, xh, v, c_st, blk, mlp)
+    t_head = time.perf_counter() - t0
+    per_tok = (t_proj + cfg.group_layers * cfg.n_heads_kv * t_head) / n_tok
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": round(1.0 / per_tok, 1), "unit": "prefix tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"projection of {n_tok} tokens ({t_proj:.2f} s) and one (layer, KV head) compression of "
+                      f"them ({t_head:.2f} s), scaled x{cfg.group_layers * cfg.n_heads_kv} heads per group"}
+
+
+def bench_build(args):
+    import torch
+    import synth
+    from long_context_decode_landmark_amd import native
+    from synth import device as sd
+    cfg = synth.CONFIGS[args.config]
+    nb = args.batch or 1
+    dev = torch.device("cuda:0")
+    G, Hkv, d, r, P, W = cfg.group_layers, cfg.n_heads_kv, cfg.head_dim, cfg.rank, cfg.prefix, cfg.window
+    nC, nR = cfg.n_chunks, cfg.n_resid
+    inp = sd.draw_build_inputs(cfg, args.seed, dev, nb)
+    shape = native.make_build_shape(cfg, batch=nb)
+    bf = torch.bfloat16
+    if cfg.int4:
+        coeff = torch.empty((nb, P, r // 2), dtype=torch.uint8, device=dev)
+        cscale = torch.empty((nb, P, r // 32), dtype=torch.int16, device=dev)
+    else:
+        coeff, cscale = torch.empty((nb, P, r), dtype=bf, device=dev), None
+    ios = []
+    for li in range(G):
+        io = dict(keys=inp["keys"], group_basis=inp["group_basis"], coeff=coeff, coeff_scale=cscale,
+                  **inp["layers"][li])
+        io["basis"] = torch.empty((nb, Hkv, d, r), dtype=bf, device=dev)
+        io["landmark"] = torch.empty((nb, Hkv, nC, d), dtype=bf, device=dev)
+        io["res_idx"] = torch.empty((nb, Hkv, nR), dtype=torch.int32, device=dev)
+        if cfg.int4:
+            io["res_val"] = torch.empty((nb, Hkv, nR, d // 2), dtype=torch.uint8, device=dev)
+            io["res_scale"] = torch.empty((nb, Hkv, nR, d // 32), dtype=torch.int16, device=dev)
+        else:
+            io["res_val"] = torch.empty((nb, Hkv, nR, d), dtype=bf, device=dev)
+        io["res_chunk_desc"] = torch.empty((nb, Hkv, nC), dtype=torch.int32, device=dev)
+        io["win_k"] = torch.empty((nb, Hkv, W, d), dtype=bf, device=dev)
+        io["win_v"] = torch.empty((nb, Hkv, W, d), dtype=bf, device=dev)
+        ios.append(io)
+    ws = torch.empty(native.build_layer_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    acc = {k: 0.0 for k in BUILD_KERNELS}
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0][0].record()
+        native.build_coeff(shape, inp["keys"], inp["group_basis"], coeff, cscale)
+        if ev is not None:
+            ev[0][1].record()
+        for li in range(G):
+            native.build_layer(shape, li, ios[li], ws, events=ev[1 + li] if ev is not None else None)
+
+    for _ in range(args.warmup):
+        step()
+    # per-step events on the launch stream (recorded once here to create them)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)]] +
+           [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(G)] for _ in range(args.steps)]
+    for s_ in evs:
+        for grp_ in s_:
+            for e in grp_:
+                e.record()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s_ in range(args.steps):
+        step(evs[s_])
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / args.steps
+    for s_ in evs:
+        acc["proj"] += s_[0][0].elapsed_time(s_[0][1])
+        for li in range(G):
+            e = s_[1 + li]
+            for j, k in enumerate(BUILD_KERNELS[1:]):
+                acc[k] += e[j].elapsed_time(e[j + 1])
+    launches = {"proj": args.steps, **{k: args.steps * G for k in BUILD_KERNELS[1:]}}
+    per_launch = {k: acc[k] / launches[k] for k in BUILD_KERNELS}
+    flops, byts = build_algorithmic(cfg, nb)
+    share = {k: per_launch[k] * launches[k] for k in BUILD_KERNELS}
+    dom = max(("proj", "predict"), key=lambda k: share[k])
+    ach = flops[dom] / (per_launch[dom] * 1e-3) / 1e12
+    res = {
+        "metric": "cache build: prefix tokens compressed per second (all layers of one layer group)",
+        "value": round(nb * P / (step_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (fp32-accurate residual prediction)" if not cfg.int4 else "bf16+int4",
+        "data": "synthetic (seeded device draws: latent-structured keys, random values)",
+        "config": {"workload": cfg.name + "_build", "batch": nb, "ctx": cfg.ctx, "prefix": P,
+                   "group_layers": G, "heads_kv": Hkv, "rank": r, "resid_frac": cfg.resid_frac,
+                   "int4": cfg.int4},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": None},
+        "kernels": {k: {"ms_per_launch": round(per_launch[k], 5), "launches_per_step": launches[k] // args.steps,
+                        "TFLOP/s": round(flops[k] / (per_launch[k] * 1e-3) / 1e12, 2) if k in flops else None,
+                        "GB/s": round(byts[k] / (per_launch[k] * 1e-3) / 1e9, 1) if k in byts else None}
+                    for k in BUILD_KERNELS},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = build_cpu_baseline(cfg, 65536)
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode step shards by "
               "sequence with no exchange, so N GPUs would each run this single-GPU workload.", file=sys.stderr)
         sys.exit(2)
+    if args.build:
+        bench_build(args)
+        return
     import synth
     cfg = synth.CONFIGS[args.config]
     nb = args.batch or cfg.batch

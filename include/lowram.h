@@ -275,6 +275,18 @@ int lowram_build_layer(const lowram_build_shape* shape, int32_t layer_in_group,
                        const lowram_layer_build* io, void* workspace, size_t ws_bytes,
                        void* stream);
 
+/*
+ * lowram_build_layer that also records five caller-created hipEvent_t
+ * (passed as void*) on `stream`, for measurement: events[0] before its
+ * kernels, [1] after the basis blocks, landmarks and window, [2] after the
+ * residual prediction, [3] after the residual top-nR selection, [4] after the
+ * residual rows and descriptors are stored.  `events` may be NULL.  The events
+ * are only recorded, never waited on.
+ */
+int lowram_build_layer_events(const lowram_build_shape* shape, int32_t layer_in_group,
+                              const lowram_layer_build* io, void* workspace, size_t ws_bytes,
+                              void* stream, void* const* events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -324,8 +324,9 @@ int lowram_build_layer_workspace_bytes(const lowram_build_shape* shape, size_t* 
   return LOWRAM_OK;
 }
 
-int lowram_build_layer(const lowram_build_shape* s, int32_t layer_in_group, const lowram_layer_build* io,
-                       void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+int run_build_layer(const lowram_build_shape* s, int32_t layer_in_group, const lowram_layer_build* io,
+                    void* workspace, size_t ws_bytes, void* stream, void* const* events) {
   int st = check_build_shape(s);
   if (st) return st;
   if (layer_in_group < 0 || layer_in_group >= s->group_layers) return LOWRAM_ERR_SHAPE;
@@ -351,15 +352,20 @@ int lowram_build_layer(const lowram_build_shape* s, int32_t layer_in_group, cons
   if (ws_bytes < p.total) return LOWRAM_ERR_WORKSPACE;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) {
+    return !events || hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) == hipSuccess;
+  };
   BuildGeo g{};
   g.nb = s->batch; g.T = s->ctx_len; g.P = p.P; g.W = s->window;
   g.D = s->group_layers * s->n_heads_kv * kHeadDim; g.r = s->rank; g.hkv = s->n_heads_kv;
   g.layer_in_group = layer_in_group; g.n_chunks = p.n_chunks; g.n_resid = s->n_resid;
   for (int i = 0; i < 64; ++i) g.inv_freq[i] = std::pow((double)s->rope_theta, -2.0 * i / (double)kHeadDim);
+  if (!mark(0)) return LOWRAM_ERR_HIP;
   if (launch_build_layer_arrays(io->keys, io->values, io->group_basis, io->basis, io->landmark, io->win_k,
                                 io->win_v, g, hs) != hipSuccess)
     return LOWRAM_ERR_HIP;
-  if (p.P == 0) return LOWRAM_OK;
+  if (!mark(1)) return LOWRAM_ERR_HIP;
+  if (p.P == 0) return mark(2) && mark(3) && mark(4) ? LOWRAM_OK : LOWRAM_ERR_HIP;
 
   unsigned char* w = static_cast<unsigned char*>(workspace);
   float* r = reinterpret_cast<float*>(w + p.off_r);
@@ -369,16 +375,34 @@ int lowram_build_layer(const lowram_build_shape* s, int32_t layer_in_group, cons
     if (launch_predict_resid(io->coeff, io->coeff_scale, io->basis, io->w1, io->b1, io->w2, io->b2, io->values, r,
                              keys, ci4, g, hs) != hipSuccess)
       return LOWRAM_ERR_HIP;
+  }
+  if (!mark(2)) return LOWRAM_ERR_HIP;
+  if (s->n_resid > 0) {
     if (launch_select(keys, nullptr, io->res_idx, nullptr, s->batch, p.P, s->n_resid, s->n_heads_kv, hs) !=
         hipSuccess)
       return LOWRAM_ERR_HIP;
+  }
+  if (!mark(3)) return LOWRAM_ERR_HIP;
+  if (s->n_resid > 0) {
     if (launch_resid_store(r, io->res_idx, io->res_val, io->res_scale, g, ri4, hs) != hipSuccess)
       return LOWRAM_ERR_HIP;
   }
   if (launch_chunk_desc(io->res_idx, (int)heads, s->n_resid, p.n_chunks, s->chunk, io->res_chunk_desc, hs) !=
       hipSuccess)
     return LOWRAM_ERR_HIP;
+  if (!mark(4)) return LOWRAM_ERR_HIP;
   return LOWRAM_OK;
+}
+}  // namespace
+
+int lowram_build_layer(const lowram_build_shape* s, int32_t layer_in_group, const lowram_layer_build* io,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  return run_build_layer(s, layer_in_group, io, workspace, ws_bytes, stream, nullptr);
+}
+
+int lowram_build_layer_events(const lowram_build_shape* s, int32_t layer_in_group, const lowram_layer_build* io,
+                              void* workspace, size_t ws_bytes, void* stream, void* const* events) {
+  return run_build_layer(s, layer_in_group, io, workspace, ws_bytes, stream, events);
 }
 
 }  // extern "C"

@@ -323,88 +323,197 @@ struct PredictArgs {
   int T, P, hkv, n_tb, total, padded_total;
 };
 
-constexpr int kPredTokWG = 128;  // 4 waves x 32 tokens
+constexpr int kPredTokWG = 128;   // 4 waves x 32 tokens
+constexpr int kPredStage = 16384;  // bytes per LDS stage
+
+// LDS swizzles of the prediction kernel's stages (16-byte pieces); each makes
+// the 16 rows one MFMA operand read touches land on distinct banks.
+// blk stage: 128 rows x 128 B (64 basis columns)
+__device__ __forceinline__ int pred_blk_off(int row, int piece) {
+  return row * 128 + ((piece ^ (((row >> 1) & 1) | ((row >> 2) & 6))) << 4);
+}
+// W1 block: 32 rows x 256 B (one hidden unit per row, 128 inputs)
+__device__ __forceinline__ int pred_w1_off(int row, int piece) {
+  return row * 256 + ((piece ^ ((row & 3) | ((row >> 1) & 12))) << 4);
+}
+// W2 block: 128 rows x 64 B (one output per row, 32 hidden units)
+__device__ __forceinline__ int pred_w2_off(int row, int piece) {
+  return 8192 + row * 64 + ((piece ^ ((row >> 2) & 3)) << 4);
+}
 
 // Residuals of every prefix token of one KV head against an fp32-accurate
 // prediction: K^T = blk C^T (rebuilt pre-RoPE keys), Z^T = W1 K^T + b1,
 // V~^T = W2 gelu(Z)^T + b2, R = V - V~ and the selection key of ||R||.
-// Tokens are the MFMA column dimension (wave: 2 tiles of 16 tokens), so each
-// weight fragment loaded serves 2 (x 3 pieces) products; the A rows of blk
-// and W1 are taken in row_perm32 order so each product's accumulators are the
-// next one's B operand.  No LDS and no barriers: waves are independent.
+// Tokens are the MFMA column dimension (wave: 2 tiles of 16 tokens); the A
+// rows of blk and W1 are taken in row_perm32 order so each product's
+// accumulators are the next one's B operand.  The weights stream through LDS
+// in 16 KiB stages shared by the 4 waves: RANK/64 stages of blk columns, then
+// per block of 32 hidden units one stage of W1 rows + W2 columns.  A stage is
+// loaded one step ahead into registers and stored after the step's MFMAs,
+// with one barrier per step; the coefficient operands of the next blk stage
+// are loaded one step ahead too.
+#ifndef LOWRAM_PRED_WG_PER_CU
+#define LOWRAM_PRED_WG_PER_CU 2
+#endif
+
 template <int RANK, bool CI4>
-__global__ __launch_bounds__(256) void predict_resid_kernel(const PredictArgs a) {
+__global__ __launch_bounds__(256, LOWRAM_PRED_WG_PER_CU) void predict_resid_kernel(const PredictArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kPredStage];
+  constexpr int NS1 = RANK / 64;      // blk stages
+  constexpr int NS = NS1 + kHidden / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, col = lane & 15;
   const int logical = xcd_logical_block(blockIdx.x, a.padded_total);
-  if (logical >= a.total) return;
+  if (logical >= a.total) return;  // whole workgroup: before any barrier
   const int h = logical % a.hkv;
   const int tb = (logical / a.hkv) % a.n_tb;
   const int b = logical / (a.hkv * a.n_tb);
   const size_t head = (size_t)b * a.hkv + h;
   const int t0 = tb * kPredTokWG + 32 * wave;
-  if (t0 >= a.P) return;
   int tok[2];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) tok[tt] = min(t0 + 16 * tt + col, a.P - 1);
+  for (int tt = 0; tt < 2; ++tt) tok[tt] = min(t0 + 16 * tt + col, a.P - 1);  // waves past P repeat token P-1
 
-  // K^T[i][t] = sum_m blk[i][m] C[t][m]
   const uint16_t* blk = a.blk + head * kHeadDim * RANK;
-  f32x4 kacc[8][2];
-#pragma unroll
-  for (int it = 0; it < 8; ++it)
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) kacc[it][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int ks = 0; ks < RANK / 32; ++ks) {
-    bf16x8 cb[2][CI4 ? 2 : 1];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const size_t row = (size_t)b * a.P + tok[tt];
-      if constexpr (!CI4) {
-        cb[tt][0] = load_bf16x8(static_cast<const uint16_t*>(a.coeff) + row * RANK + 32 * ks + 8 * grp);
-      } else {
-        // code * scale has at most 15 significant bits: two bf16 pieces hold it exactly
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.coeff) +
-                                                              row * (RANK / 2) + 16 * ks + 4 * grp);
-        const float sc = f16_to_f32(a.coeff_scale[row * (RANK / 32) + ks]);
-        f32x4 lo, hi;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lo[e] = (float)(((int)(w << (28 - 4 * e))) >> 28) * sc;
-          hi[e] = (float)(((int)(w << (12 - 4 * e))) >> 28) * sc;
-        }
-        cb[tt][0] = pack8(lo, hi);
-        cb[tt][1] = pack8_lo(lo, hi, cb[tt][0]);
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int irow = 32 * (it >> 1) + row_perm32(16 * (it & 1) + col);
-      const bf16x8 af = load_bf16x8(blk + irow * RANK + 32 * ks + 8 * grp);
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int sp = 0; sp < (CI4 ? 2 : 1); ++sp) kacc[it][tt] = mfma16(af, cb[tt][sp], kacc[it][tt]);
-    }
-  }
-  // B operands of the next product: k-step s (i = 32 s + 8 g + 0..7) from tiles 2 s, 2 s + 1
-  bf16x8 kb[4][2][3];
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) split3(kacc[2 * s][tt], kacc[2 * s + 1][tt], kb[s][tt]);
-
   const uint16_t* w1 = a.w1 + head * kHidden * kHeadDim;
   const uint16_t* b1 = a.b1 + head * kHidden;
   const uint16_t* w2 = a.w2 + head * kHeadDim * kHidden;
+
+  // stage s -> 4 pieces of 16 B per thread
+  u32x4 sreg[4];
+  auto stage_load = [&](int s) {
+    if (s < NS1) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        sreg[u] = *reinterpret_cast<const u32x4*>(blk + (tid / 8 + 32 * u) * RANK + 64 * s + 8 * (tid % 8));
+    } else {
+      const int jb = s - NS1;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        sreg[u] = *reinterpret_cast<const u32x4*>(w1 + (32 * jb + tid / 16 + 16 * u) * kHeadDim + 8 * (tid % 16));
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        sreg[2 + u] = *reinterpret_cast<const u32x4*>(w2 + (tid / 4 + 64 * u) * kHidden + 32 * jb + 8 * (tid % 4));
+    }
+  };
+  auto stage_store = [&](int s, unsigned char* buf) {
+    if (s < NS1) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(buf + pred_blk_off(tid / 8 + 32 * u, tid % 8)) = sreg[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(buf + pred_w1_off(tid / 16 + 16 * u, tid % 16)) = sreg[u];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(buf + pred_w2_off(tid / 4 + 64 * u, tid % 4)) = sreg[2 + u];
+    }
+  };
+  // coefficient operands of blk stage s: k-steps 2 s, 2 s + 1, both token tiles
+  constexpr int CW = CI4 ? 1 : 4;  // 32-bit words per (k-step, token tile)
+  uint32_t creg[2][2][CW];
+  uint16_t csc[2][2];
+  auto coeff_load = [&](int s) {
+#pragma unroll
+    for (int kl = 0; kl < 2; ++kl)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const size_t row = (size_t)b * a.P + tok[tt];
+        const int ks = 2 * s + kl;
+        if constexpr (!CI4) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.coeff) + row * RANK +
+                                                          32 * ks + 8 * grp);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) creg[kl][tt][q] = v[q];
+        } else {
+          creg[kl][tt][0] = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.coeff) +
+                                                               row * (RANK / 2) + 16 * ks + 4 * grp);
+          csc[kl][tt] = a.coeff_scale[row * (RANK / 32) + ks];
+        }
+      }
+  };
+
+  stage_load(0);
+  coeff_load(0);
+  stage_store(0, lds);
+  __syncthreads();
+
+  // phase 1: K^T[i][t] = sum_m blk[i][m] C[t][m], 64 columns per stage
+  bf16x8 kb[4][2][3];
+  {
+    f32x4 kacc[8][2];
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) kacc[it][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int s = 0; s < NS1; ++s) {
+      const unsigned char* cur = lds + (s & 1) * kPredStage;
+      uint32_t cnow[2][2][CW];
+      uint16_t snow[2][2];
+#pragma unroll
+      for (int kl = 0; kl < 2; ++kl)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+          for (int q = 0; q < CW; ++q) cnow[kl][tt][q] = creg[kl][tt][q];
+          snow[kl][tt] = CI4 ? csc[kl][tt] : 0;
+        }
+      stage_load(s + 1);  // NS > NS1: the next stage always exists
+      if (s + 1 < NS1) coeff_load(s + 1);
+#pragma unroll
+      for (int kl = 0; kl < 2; ++kl) {
+        bf16x8 cb[2][CI4 ? 2 : 1];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          if constexpr (!CI4) {
+            cb[tt][0] = __builtin_bit_cast(bf16x8, u32x4{cnow[kl][tt][0], cnow[kl][tt][1], cnow[kl][tt][2],
+                                                         cnow[kl][tt][3]});
+          } else {
+            // code * scale has at most 15 significant bits: two bf16 pieces hold it exactly
+            const uint32_t w = cnow[kl][tt][0];
+            const float sc = f16_to_f32(snow[kl][tt]);
+            f32x4 lo, hi;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              lo[e] = (float)(((int)(w << (28 - 4 * e))) >> 28) * sc;
+              hi[e] = (float)(((int)(w << (12 - 4 * e))) >> 28) * sc;
+            }
+            cb[tt][0] = pack8(lo, hi);
+            cb[tt][1] = pack8_lo(lo, hi, cb[tt][0]);
+          }
+        }
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int irow = 32 * (it >> 1) + row_perm32(16 * (it & 1) + col);
+          const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                           cur + pred_blk_off(irow, 4 * kl + grp)));
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int sp = 0; sp < (CI4 ? 2 : 1); ++sp) kacc[it][tt] = mfma16(af, cb[tt][sp], kacc[it][tt]);
+        }
+      }
+      stage_store(s + 1, lds + ((s + 1) & 1) * kPredStage);
+      __syncthreads();
+    }
+    // B operands of the next product: k-step q (i = 32 q + 8 g + 0..7) from tiles 2 q, 2 q + 1
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) split3(kacc[2 * q][tt], kacc[2 * q + 1][tt], kb[q][tt]);
+  }
+
+  // phases 2 and 3, one block of 32 hidden units per stage:
+  // Z^T = W1 K^T + b1, h = gelu(Z), V~^T += W2[:, block] h^T
   f32x4 vacc[8][2];
 #pragma unroll
   for (int nd = 0; nd < 8; ++nd)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) vacc[nd][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int jb = 0; jb < kHidden / 32; ++jb) {
-    // Z^T for hidden units 32 jb .. 32 jb + 31 (tiles jt = 0, 1)
+#pragma unroll 1
+  for (int s = NS1; s < NS; ++s) {
+    const unsigned char* cur = lds + (s & 1) * kPredStage;
+    const int jb = s - NS1;
+    if (s + 1 < NS) stage_load(s + 1);
     f32x4 z[2][2];
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
@@ -413,14 +522,15 @@ __global__ __launch_bounds__(256) void predict_resid_kernel(const PredictArgs a)
       for (int e = 0; e < 4; ++e) bias[e] = bf16_to_f32(b1[32 * jb + 8 * grp + 4 * jt + e]);
       z[jt][0] = bias;
       z[jt][1] = bias;
-      const int jrow = 32 * jb + row_perm32(16 * jt + col);
+      const int jl = row_perm32(16 * jt + col);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 af = load_bf16x8(w1 + jrow * kHeadDim + 32 * s + 8 * grp);
+      for (int q = 0; q < 4; ++q) {
+        const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                         cur + pred_w1_off(jl, 4 * q + grp)));
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int sp = 0; sp < 3; ++sp) z[jt][tt] = mfma16(af, kb[s][tt][sp], z[jt][tt]);
+          for (int sp = 0; sp < 3; ++sp) z[jt][tt] = mfma16(af, kb[q][tt][sp], z[jt][tt]);
       }
     }
     bf16x8 hb[2][3];
@@ -434,12 +544,15 @@ __global__ __launch_bounds__(256) void predict_resid_kernel(const PredictArgs a)
     }
 #pragma unroll
     for (int nd = 0; nd < 8; ++nd) {
-      const bf16x8 af = load_bf16x8(w2 + (16 * nd + col) * kHidden + 32 * jb + 8 * grp);
+      const bf16x8 af = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                       cur + pred_w2_off(16 * nd + col, grp)));
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int sp = 0; sp < 3; ++sp) vacc[nd][tt] = mfma16(af, hb[tt][sp], vacc[nd][tt]);
     }
+    if (s + 1 < NS) stage_store(s + 1, lds + ((s + 1) & 1) * kPredStage);
+    __syncthreads();
   }
 
   // R = V - (V~ + b2) for d = 16 nd + 4 g + e, token column col

@@ -30,6 +30,7 @@ SYMBOLS = (
     "lowram_build_coeff",
     "lowram_build_layer_workspace_bytes",
     "lowram_build_layer",
+    "lowram_build_layer_events",
 )
 
 ERRORS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "UNSUPPORTED", -4: "WORKSPACE", -5: "ALIGN", -6: "HIP"}
@@ -110,6 +111,9 @@ def lib() -> ctypes.CDLL:
         L.lowram_build_layer_workspace_bytes.argtypes = [ctypes.POINTER(LowramBuildShape), ctypes.POINTER(sz)]
         L.lowram_build_layer.argtypes = [ctypes.POINTER(LowramBuildShape), ctypes.c_int32,
                                          ctypes.POINTER(LowramLayerBuild), vp, sz, vp]
+        L.lowram_build_layer_events.argtypes = [ctypes.POINTER(LowramBuildShape), ctypes.c_int32,
+                                                ctypes.POINTER(LowramLayerBuild), vp, sz, vp,
+                                                ctypes.POINTER(ctypes.c_void_p)]
         for name in SYMBOLS:
             getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
         L.lowram_strerror.restype = ctypes.c_char_p
@@ -247,9 +251,16 @@ def build_layer_workspace_bytes(shape: LowramBuildShape) -> int:
     return n.value
 
 
-def build_layer(shape, layer_in_group: int, io: dict, workspace, stream=None) -> None:
-    """lowram_build_layer; io maps the lowram_layer_build field names to device tensors (or None)."""
+def build_layer(shape, layer_in_group: int, io: dict, workspace, stream=None, events=None) -> None:
+    """lowram_build_layer (or _events with 5 torch.cuda.Event); io maps the
+    lowram_layer_build field names to device tensors (or None)."""
     b = LowramLayerBuild(**{n: (io[n].data_ptr() if io.get(n) is not None else None) for n in BUILD_FIELDS})
-    _check(lib().lowram_build_layer(ctypes.byref(shape), layer_in_group, ctypes.byref(b), _ptr(workspace),
-                                    workspace.numel() * workspace.element_size(), _stream(stream)),
-           "lowram_build_layer")
+    ws_ptr = _ptr(workspace)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if events is None:
+        _check(lib().lowram_build_layer(ctypes.byref(shape), layer_in_group, ctypes.byref(b), ws_ptr, ws_n,
+                                        _stream(stream)), "lowram_build_layer")
+        return
+    arr = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    _check(lib().lowram_build_layer_events(ctypes.byref(shape), layer_in_group, ctypes.byref(b), ws_ptr, ws_n,
+                                           _stream(stream), arr), "lowram_build_layer_events")

@@ -52,19 +52,23 @@ def exact_values(x: np.ndarray, w1, b1, w2, b2, noise, spike_pos, spike_vals) ->
     return v
 
 
-def residual_errors(v_prefix: np.ndarray, k_pre_prefix: np.ndarray, w1, b1, w2, b2) -> np.ndarray:
-    """||V_t - MLP(K_pre_t)||_2 of every prefix token."""
+def residuals(v_prefix: np.ndarray, k_pre_prefix: np.ndarray, w1, b1, w2, b2):
+    """R_t = V_t - MLP(K_pre_t) and ||R_t||_2 of every prefix token."""
     r = np.asarray(v_prefix, np.float64) - value_mlp(k_pre_prefix, w1, b1, w2, b2)
-    return np.sqrt(np.sum(r * r, axis=1))
+    return r, np.sqrt(np.sum(r * r, axis=1))
+
+
+def select_worst(err: np.ndarray, n_resid: int) -> np.ndarray:
+    """The n_resid largest errors, ties to the lower index, ascending."""
+    order = np.lexsort((np.arange(len(err)), -np.asarray(err)))   # by -err, then index
+    return np.sort(order[:n_resid]).astype(np.int32)
 
 
 def residual_select(v_prefix: np.ndarray, k_pre_prefix: np.ndarray, w1, b1, w2, b2, n_resid: int):
     """Indices (ascending) and rows of the n_resid worst-predicted prefix tokens."""
-    r = np.asarray(v_prefix, np.float64) - value_mlp(k_pre_prefix, w1, b1, w2, b2)
-    err = np.sqrt(np.sum(r * r, axis=1))
-    order = np.lexsort((np.arange(len(err)), -err))   # by -err, then index
-    idx = np.sort(order[:n_resid])
-    return idx.astype(np.int32), r[idx]
+    r, err = residuals(v_prefix, k_pre_prefix, w1, b1, w2, b2)
+    idx = select_worst(err, n_resid)
+    return idx, r[idx]
 
 
 def chunk_descriptors(idx: np.ndarray, n_chunks: int, chunk: int) -> np.ndarray:
@@ -115,7 +119,9 @@ def compress_from_kv(cfg, x_head: np.ndarray, v_head: np.ndarray, coeff_stored, 
     c_dec = decode_coeff(coeff_stored, cfg.int4, exact)
     blk = np.asarray(blk_stored, np.float64) if exact else codecs.bf16_decode(blk_stored)
     k_pre = reconstruct(c_dec, blk)
-    idx, rows = residual_select(v[:P], k_pre, *w, cfg.n_resid)
+    r, err = residuals(v[:P], k_pre, *w)
+    idx = select_worst(err, cfg.n_resid)
+    rows = r[idx]
 
     out = dict(
         landmark=_store(landmarks(x_head, P, S, cfg.rope_theta), exact),
@@ -123,6 +129,7 @@ def compress_from_kv(cfg, x_head: np.ndarray, v_head: np.ndarray, coeff_stored, 
         res_chunk_desc=chunk_descriptors(idx, cfg.n_chunks, S),
         win_k=_store(rope(x_head[P:], np.arange(P, P + W), cfg.rope_theta), exact),
         win_v=_store(v[P:], exact),
+        errors=err,   # not stored by the cache: every prefix token's ||R||, for near-tie checks
     )
     if cfg.int4 and not exact:
         out["res_val"], out["res_scale"] = codecs.int4_encode(rows)

@@ -118,6 +118,27 @@ def dense_layer(cfg, layer: int, batch=None):
     return np.stack(ks), np.stack(vs), np.stack(qs)
 
 
+def builder_expected(cfg, layer: int, x_bits, basis_bits, c_st, heads, values_bits, mlp_bits):
+    """The oracle's compression of one sequence's builder inputs (given as bf16 bits).
+
+    x_bits [T][D] group keys, basis_bits [r][D], c_st the stored coefficients
+    of the prefix, heads the KV heads to compress, values_bits [len(heads)][T][d]
+    and mlp_bits (per head: w1, b1, w2, b2) of those heads.  Arrays come out
+    with a head axis in the order of ``heads``.
+    """
+    from .compress import compress_from_kv
+    hexp = {}
+    for i, h in enumerate(heads):
+        cols = synth.layer_cols(cfg, layer, h)
+        blk_st = basis_block(basis_bits, cols)
+        hd = compress_from_kv(cfg, codecs.bf16_decode(x_bits[:, cols]), codecs.bf16_decode(values_bits[i]), c_st,
+                              blk_st, mlp_bits[i])
+        hd["basis"] = blk_st
+        for k, v in hd.items():
+            hexp.setdefault(k, []).append(v)
+    return {k: np.stack(v) for k, v in hexp.items()}
+
+
 def builder_io(cfg, layer: int, batch=None):
     """Inputs of the cache builder for ``layer`` and the cache the oracle builds from them.
 
@@ -130,50 +151,35 @@ def builder_io(cfg, layer: int, batch=None):
     (+ res_scale), res_chunk_desc, win_k, win_v, and ``errors`` [NB][Hkv][P],
     the oracle's ||R_t|| of every prefix token (for the near-tie rule).
     """
-    from .compress import compress_from_kv, decode_coeff, exact_values, residual_errors
-    from .steps import reconstruct
+    from .compress import exact_values
     batch = list(range(cfg.batch)) if batch is None else list(batch)
     grp = layer // cfg.group_layers
-    P = cfg.prefix
+    P, Hkv = cfg.prefix, cfg.n_heads_kv
     inp = {k: [] for k in ("keys", "group_basis", "values", "w1", "b1", "w2", "b2")}
-    exp = {k: [] for k in ("coeff", "coeff_scale", "basis", "landmark", "res_idx", "res_val", "res_scale",
-                           "res_chunk_desc", "win_k", "win_v", "errors")}
+    exp = {}
     for b in batch:
         x_bits = codecs.bf16_encode(synth.exact_keys(cfg, b, grp, dtype=_key_dtype(cfg)))
         B_bits = codecs.bf16_encode(synth.basis(cfg, b, grp))
-        x, B = codecs.bf16_decode(x_bits), codecs.bf16_decode(B_bits)
-        c_st = store_coeff(project(x[:P], B), cfg.int4)
+        x = codecs.bf16_decode(x_bits)
+        c_st = store_coeff(project(x[:P], codecs.bf16_decode(B_bits)), cfg.int4)
+        mlp_bits = [tuple(codecs.bf16_encode(a) for a in synth.mlp_weights(cfg, b, layer, h)) for h in range(Hkv)]
+        v_bits = np.stack([
+            codecs.bf16_encode(exact_values(np.asarray(x[:, synth.layer_cols(cfg, layer, h)]),
+                                            *[codecs.bf16_decode(a) for a in mlp_bits[h]],
+                                            synth.value_noise(cfg, b, layer, h), *synth.value_spikes(cfg, b, layer, h)))
+            for h in range(Hkv)])
         inp["keys"].append(x_bits)
         inp["group_basis"].append(B_bits)
+        inp["values"].append(v_bits)
+        for i, k in enumerate(("w1", "b1", "w2", "b2")):
+            inp[k].append(np.stack([m[i] for m in mlp_bits]))
+        e = builder_expected(cfg, layer, x_bits, B_bits, c_st, range(Hkv), v_bits, mlp_bits)
         if cfg.int4:
-            exp["coeff"].append(c_st[0])
-            exp["coeff_scale"].append(c_st[1])
+            e["coeff"], e["coeff_scale"] = c_st
         else:
-            exp["coeff"].append(c_st)
-        heads = {k: [] for k in inp if k not in ("keys", "group_basis")}
-        hexp = {k: [] for k in exp if k not in ("coeff", "coeff_scale")}
-        for h in range(cfg.n_heads_kv):
-            cols = synth.layer_cols(cfg, layer, h)
-            mlp_st = tuple(codecs.bf16_encode(a) for a in synth.mlp_weights(cfg, b, layer, h))
-            w = [codecs.bf16_decode(a) for a in mlp_st]
-            v_bits = codecs.bf16_encode(exact_values(np.asarray(x[:, cols]), *w, synth.value_noise(cfg, b, layer, h),
-                                                     *synth.value_spikes(cfg, b, layer, h)))
-            blk_st = basis_block(B_bits, cols)
-            hd = compress_from_kv(cfg, x[:, cols], codecs.bf16_decode(v_bits), c_st, blk_st, mlp_st)
-            hd["basis"] = blk_st
-            hd["errors"] = residual_errors(codecs.bf16_decode(v_bits)[:P],
-                                           reconstruct(decode_coeff(c_st, cfg.int4), codecs.bf16_decode(blk_st)), *w)
-            heads["values"].append(v_bits)
-            for k, a in zip(("w1", "b1", "w2", "b2"), mlp_st):
-                heads[k].append(a)
-            for k in hexp:
-                if k in hd:
-                    hexp[k].append(hd[k])
-        for k, v in heads.items():
-            inp[k].append(np.stack(v))
-        for k, v in hexp.items():
-            if v:
-                exp[k].append(np.stack(v))
+            e["coeff"] = c_st
+        for k, v in e.items():
+            exp.setdefault(k, []).append(v)
     inp = {k: np.ascontiguousarray(np.stack(v)) for k, v in inp.items()}
-    exp = {k: np.ascontiguousarray(np.stack(v)) for k, v in exp.items() if v}
+    exp = {k: np.ascontiguousarray(np.stack(v)) for k, v in exp.items()}
     return inp, exp

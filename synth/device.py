@@ -106,3 +106,40 @@ def draw_layer(cfg, seed: int, device) -> dict:
 
 def draw_queries(cfg, nb: int, seed: int, device) -> torch.Tensor:
     return _normal((nb, cfg.n_heads_q, cfg.head_dim), 1.0, _gen(seed, device), device)
+
+
+def draw_build_inputs(cfg, seed: int, device, nb: int = 1, layers=None) -> dict:
+    """Cache-builder inputs of nb sequences of one layer group, drawn on the GPU.
+
+      keys         [NB][T][D] bf16: latents Z ~ N(0, 1) of dim 64 (drawn here)
+                   times the group's host mixing matrix, plus N(0, 0.05^2)
+      group_basis  [NB][r][D] bf16: the host fixture's orthonormal basis
+      per layer l  values [NB][Hkv][T][d] ~ N(0, 0.5^2), and the host
+                   fixture's MLP weights (w1, b1, w2, b2) of the layer
+    Returned as {"keys", "group_basis", "layers": [dict per layer]}.
+    """
+    import numpy as np
+    from . import draws
+    g = _gen(seed, device)
+    T, D, Hkv, d = cfg.ctx, cfg.group_dim, cfg.n_heads_kv, cfg.head_dim
+    layers = list(range(cfg.group_layers)) if layers is None else list(layers)
+    keys = torch.empty((nb, T, D), dtype=BF16, device=device)
+    basis = torch.empty((nb, cfg.rank, D), dtype=BF16, device=device)
+    for b in range(nb):
+        m = torch.from_numpy(draws.mixing(cfg, b, 0)).to(device=device, dtype=torch.float32)
+        for t0 in range(0, T, 32768):
+            t1 = min(T, t0 + 32768)
+            z = torch.randn((t1 - t0, cfg.latent_dim), generator=g, device=device, dtype=torch.float32)
+            x = z @ m
+            x += torch.randn(x.shape, generator=g, device=device, dtype=torch.float32) * cfg.key_noise_std
+            keys[b, t0:t1] = x.to(BF16)
+        basis[b] = torch.from_numpy(draws.basis(cfg, b, 0)).to(device=device, dtype=torch.float32).to(BF16)
+    out = {"keys": keys, "group_basis": basis, "layers": []}
+    for layer in layers:
+        per = {"values": _normal((nb, Hkv, T, d), 0.5, g, device)}
+        ws = [[draws.mlp_weights(cfg, b, layer, h) for h in range(Hkv)] for b in range(nb)]
+        for i, name in enumerate(("w1", "b1", "w2", "b2")):
+            a = np.stack([np.stack([ws[b][h][i] for h in range(Hkv)]) for b in range(nb)])
+            per[name] = torch.from_numpy(a).to(device=device, dtype=torch.float32).to(BF16)
+        out["layers"].append(per)
+    return out

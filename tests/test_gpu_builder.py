@@ -290,3 +290,52 @@ def test_built_cache_decodes_like_oracle_cache():
     ref, _ = decode.decode_step(cfg, cache, q, sel_override=sel.cpu().numpy())
     rel, mx = check_output(down_bf16(out), ref, "built cache")
     print(f"\nbuilt cache decode: rel {rel:.2e} max {mx:.2e}", flush=True)
+
+
+@pytest.mark.timeout(600)
+def test_full_size_sampled_heads():
+    """The 262144-token, rank-512 group in the benchmark's launch configuration.
+
+    Inputs are the benchmark's device draws.  Every coefficient of the group
+    is compared with the oracle's projection; the layer stage then runs on
+    the oracle's stored coefficients, and two KV heads are compressed by the
+    oracle in full (selection over all 261888 prefix tokens, residual rows,
+    descriptors, landmarks, window) and compared; every head's selection
+    must be ascending and in range.
+    """
+    from synth import device as sd
+    cfg, nb, layer = synth.C3, 1, 1
+    heads = [0, 5]
+    P, r, hkv = cfg.prefix, cfg.rank, cfg.n_heads_kv
+    print(f"\nbuilder full size: P={P} D={cfg.group_dim} r={r}: drawing inputs", flush=True)
+    d_in = sd.draw_build_inputs(cfg, 4242, DEV, nb, layers=[layer])
+    ly = d_in["layers"][0]
+    x_bits = d_in["keys"][0].view(torch.int16).cpu().numpy().view(np.uint16)
+    b_bits = d_in["group_basis"][0].view(torch.int16).cpu().numpy().view(np.uint16)
+    print("builder full size: oracle projection", flush=True)
+    x = codecs.bf16_decode(x_bits[:P])
+    c = np.concatenate([compress.project(x[t0:t0 + 16384], codecs.bf16_decode(b_bits))
+                        for t0 in range(0, P, 16384)])
+    del x
+    c_st = compress.store_coeff(c, cfg.int4)
+    del c
+    v_bits = ly["values"][0, heads].view(torch.int16).cpu().numpy().view(np.uint16)
+    mlp_bits = [tuple(ly[k][0, h].view(torch.int16).cpu().numpy().view(np.uint16) for k in ("w1", "b1", "w2", "b2"))
+                for h in heads]
+    print("builder full size: oracle compression of the sampled heads", flush=True)
+    e = fixture.builder_expected(cfg, layer, x_bits, b_bits, c_st, heads, v_bits, mlp_bits)
+    exp = {k: v[None] for k, v in e.items()}
+    exp["coeff"] = c_st[None]
+    inp = {"keys": x_bits[None], "values": v_bits[None],
+           **{k: np.stack([m[i] for m in mlp_bits])[None] for i, k in enumerate(("w1", "b1", "w2", "b2"))}}
+    host_in = {"keys": x_bits[None], "group_basis": b_bits[None],
+               "values": ly["values"].view(torch.int16).cpu().numpy().view(np.uint16),
+               **{k: ly[k].view(torch.int16).cpu().numpy().view(np.uint16) for k in ("w1", "b1", "w2", "b2")}}
+    print("builder full size: GPU build", flush=True)
+    got = run_builder(cfg, host_in, layer, {"coeff": c_st[None]})
+    gi_all = got["res_idx"]
+    assert np.all(np.diff(gi_all, axis=-1) > 0) and gi_all.min() >= 0 and gi_all.max() < P
+    sub = {k: (v[:, heads] if v.ndim >= 3 and k not in ("coeff", "coeff_used") else v) for k, v in got.items()}
+    st = check_layer(cfg.with_(name="c3_sampled", n_heads_kv=len(heads)), inp, exp, sub)
+    assert st["moved_tokens"] == 0
+    print(f"builder full size: {st}", flush=True)
