@@ -253,8 +253,8 @@ typedef struct lowram_layer_build {
 } lowram_layer_build;
 
 /* Workspace bytes lowram_build_layer needs (pure function of the shape):
-   NB * Hkv * P * (4 d + 4) bytes (rounded up), the fp32 residual of every
-   prefix token and its error key. */
+   about NB * Hkv * P * (4 d + 4) bytes, the fp32 residual of every prefix
+   token and its error key, plus the top-nR selection's histograms. */
 int lowram_build_layer_workspace_bytes(const lowram_build_shape* shape, size_t* bytes);
 
 /*

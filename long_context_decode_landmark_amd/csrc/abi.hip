@@ -183,7 +183,7 @@ int check_build_shape(const lowram_build_shape* s) {
 
 struct BuildPlan {
   int P, n_chunks;
-  size_t off_r, off_keys, total;
+  size_t off_r, off_keys, off_sel, total;
 };
 
 BuildPlan make_build_plan(const lowram_build_shape* s) {
@@ -193,7 +193,8 @@ BuildPlan make_build_plan(const lowram_build_shape* s) {
   const size_t heads = (size_t)s->batch * s->n_heads_kv;
   p.off_r = 0;                                                // fp32 residual rows [NB][Hkv][P][d]
   p.off_keys = align_up(heads * (size_t)p.P * kHeadDim * 4);  // uint32 error keys [NB][Hkv][P]
-  p.total = p.off_keys + align_up(heads * (size_t)p.P * 4);
+  p.off_sel = p.off_keys + align_up(heads * (size_t)p.P * 4);  // top-k histograms and counts
+  p.total = p.off_sel + (p.P > 0 ? align_up(split_select_ws_bytes((int)heads, p.P)) : 0);
   return p;
 }
 
@@ -378,8 +379,7 @@ int run_build_layer(const lowram_build_shape* s, int32_t layer_in_group, const l
   }
   if (!mark(2)) return LOWRAM_ERR_HIP;
   if (s->n_resid > 0) {
-    if (launch_select(keys, nullptr, io->res_idx, nullptr, s->batch, p.P, s->n_resid, s->n_heads_kv, hs) !=
-        hipSuccess)
+    if (launch_select_split(keys, io->res_idx, (int)heads, p.P, s->n_resid, w + p.off_sel, hs) != hipSuccess)
       return LOWRAM_ERR_HIP;
   }
   if (!mark(3)) return LOWRAM_ERR_HIP;

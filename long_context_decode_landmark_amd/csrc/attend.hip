@@ -65,35 +65,6 @@ __device__ __forceinline__ float gelu_fast(float x) {
   return x * fmaf(xc, q, 0.5f);
 }
 
-// 2*pi split for the Cody-Waite reduction of large RoPE angles in fp64.
-constexpr double kTwoPiHi = 6.283185307179586;
-constexpr double kTwoPiLo = 2.4492935982947064e-16;
-constexpr double kInvTwoPi = 0.15915494309189535;
-
-// sin and cos on [-pi, pi]: odd / even minimax polynomials (linear-programming
-// fit over the interval), largest error in fp32 7e-7 / 5e-7.  The argument
-// arrives reduced, so no range reduction of a general sinf / cosf is paid.
-constexpr float kSinP[6] = {9.9999964237e-01f, -1.6666558385e-01f, 8.3324396983e-03f,
-                            -1.9809571677e-04f, 2.7007711196e-06f, -2.0404730350e-08f};
-constexpr float kCosP[7] = {1.0000000000e+00f, -5.0000000000e-01f, 4.1666641831e-02f,
-                            -1.3888442190e-03f, 2.4781049433e-05f, -2.7166586847e-07f,
-                            1.7499086624e-09f};
-
-// (cos, sin) of an angle, reduced mod 2 pi in fp64 (Cody-Waite, 2 pi in two parts)
-__device__ __forceinline__ float2 rot_of(double angle) {
-  const double k = rint(angle * kInvTwoPi);
-  double r = fma(-k, kTwoPiHi, angle);
-  r = fma(-k, kTwoPiLo, r);
-  const float x = static_cast<float>(r), u = x * x;
-  float sn = kSinP[5];
-#pragma unroll
-  for (int i = 4; i >= 0; --i) sn = fmaf(sn, u, kSinP[i]);
-  float cs = kCosP[6];
-#pragma unroll
-  for (int i = 5; i >= 0; --i) cs = fmaf(cs, u, kCosP[i]);
-  return make_float2(cs, x * sn);
-}
-
 constexpr int kStage = 16384;  // bytes of one staged operand slice
 constexpr int kStageLd = 4;    // 16-byte loads per thread per stage (256 threads)
 

@@ -214,14 +214,6 @@ hipError_t launch_proj(const uint16_t* keys, const uint16_t* basis, void* coeff,
 // Per-layer arrays that need no MLP: basis blocks, landmarks, window.
 // ---------------------------------------------------------------------------
 
-// RoPE rotation (cos, sin) of an angle: fp64 library sincos rounded to fp32
-// (one evaluation per key element; not a hot loop).
-__device__ __forceinline__ float2 build_rot(double angle) {
-  double s, c;
-  sincos(angle, &s, &c);
-  return make_float2(static_cast<float>(c), static_cast<float>(s));
-}
-
 // Basis blocks: blk[b][h][i][m] = B[b][m][col(layer, h, i)].
 // Grid (r / 64, Hkv, NB); LDS transpose of a 64 x 128 block.
 __global__ __launch_bounds__(256) void basis_block_kernel(const uint16_t* __restrict__ basis,
@@ -256,7 +248,7 @@ __global__ __launch_bounds__(256) void landmark_kernel(const uint16_t* __restric
     const int t = c * kChunk + i;
     const float x1 = bf16_to_f32(xs[(size_t)t * g.D + p]);
     const float x2 = bf16_to_f32(xs[(size_t)t * g.D + p + 64]);
-    const float2 cs = build_rot((double)t * g.inv_freq[p]);
+    const float2 cs = rot_of((double)t * g.inv_freq[p]);
     y1 += x1 * cs.x - x2 * cs.y;
     y2 += x2 * cs.x + x1 * cs.y;
   }
@@ -277,7 +269,7 @@ __global__ __launch_bounds__(256) void window_kernel(const uint16_t* __restrict_
   const uint16_t* xr = keys + ((size_t)b * g.T + t) * g.D + (g.layer_in_group * g.hkv + h) * kHeadDim;
   const float x1 = bf16_to_f32(xr[p]);
   const float x2 = bf16_to_f32(xr[p + 64]);
-  const float2 cs = build_rot((double)t * g.inv_freq[p]);
+  const float2 cs = rot_of((double)t * g.inv_freq[p]);
   uint16_t* ko = wk + (head * g.W + w) * kHeadDim;
   ko[p] = __builtin_bit_cast(uint16_t, (__bf16)(x1 * cs.x - x2 * cs.y));
   ko[p + 64] = __builtin_bit_cast(uint16_t, (__bf16)(x2 * cs.x + x1 * cs.y));

@@ -51,6 +51,12 @@ hipError_t launch_select(const uint32_t* keys, const int32_t* cand_ids, int32_t*
                          int32_t* sel_out, int nb, int n_cand, int k, int hkv, hipStream_t st);
 hipError_t launch_attend(const AttendArgs& a, int rank, bool coeff_int4, bool resid_int4,
                          hipStream_t st);
+// Exact top-k of n_lists long lists (keys [n_lists][n] -> sel [n_lists][k]
+// ascending indices, ties to the lower index), spread over many workgroups;
+// ws of split_select_ws_bytes bytes.
+size_t split_select_ws_bytes(int n_lists, int n);
+hipError_t launch_select_split(const uint32_t* keys, int32_t* sel, int n_lists, int n, int k, void* ws,
+                               hipStream_t st);
 hipError_t launch_merge(const float* part, uint16_t* out, int nb, int hkv, int g, int n_split,
                         hipStream_t st);
 hipError_t launch_dense(const uint16_t* k, const uint16_t* v, const uint16_t* q, float* part,

@@ -240,6 +240,208 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same exact top-k for few long lists (the cache builder's residual
+// ranking: one list of P tokens per KV head): each list is cut into slices
+// of kSplitSlice keys so that many workgroups share the passes.  Per radix
+// pass, every slice adds its LDS histogram to the list's global histogram,
+// then one workgroup per list picks the digit (and clears the histogram for
+// the next pass); finally each slice counts its keys > T and == T, and an
+// ordered compaction places them after the counts of the slices before it.
+// State per list: {prefix, pmask, still needed, k}.
+// ---------------------------------------------------------------------------
+constexpr int kSplitSlice = 8192;
+constexpr int kSplitThreads = 256;
+
+struct SplitWs {
+  uint32_t* hist;    // [L][kSelBins]
+  uint32_t* state;   // [L][4]
+  uint32_t* counts;  // [L][n_slices][2]
+};
+
+__global__ __launch_bounds__(kSplitThreads) void split_init_kernel(SplitWs w, int k) {
+  const int l = blockIdx.x;
+  for (int i = threadIdx.x; i < kSelBins; i += kSplitThreads) w.hist[(size_t)l * kSelBins + i] = 0u;
+  if (threadIdx.x == 0) {
+    w.state[4 * l + 0] = 0u;
+    w.state[4 * l + 1] = 0u;
+    w.state[4 * l + 2] = (uint32_t)k;
+    w.state[4 * l + 3] = (uint32_t)k;
+  }
+}
+
+__global__ __launch_bounds__(kSplitThreads) void split_hist_kernel(const uint32_t* __restrict__ keys, SplitWs w,
+                                                                   int n, int shift, uint32_t dmask) {
+  __shared__ uint32_t hist[kSelBins];
+  const int l = blockIdx.y;
+  const uint32_t prefix = w.state[4 * l], pmask = w.state[4 * l + 1];
+  for (int i = threadIdx.x; i < kSelBins; i += kSplitThreads) hist[i] = 0u;
+  __syncthreads();
+  const uint32_t* kl = keys + (size_t)l * n;
+  const int i0 = blockIdx.x * kSplitSlice, i1 = min(n, i0 + kSplitSlice);
+  for (int i = i0 + threadIdx.x; i < i1; i += kSplitThreads) {
+    const uint32_t key = kl[i];
+    if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+  }
+  __syncthreads();
+  uint32_t* gh = w.hist + (size_t)l * kSelBins;
+  for (int i = threadIdx.x; i <= (int)dmask; i += kSplitThreads)
+    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+}
+
+// One workgroup per list: the digit whose higher bins first reach the
+// needed count; clears the histogram for the next pass.
+__global__ __launch_bounds__(kSelThreads) void split_digit_kernel(SplitWs w, int shift, uint32_t dmask) {
+  __shared__ uint32_t wsum[kSelWaves];
+  __shared__ uint32_t found[2];
+  const int l = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t* gh = w.hist + (size_t)l * kSelBins;
+  const int nbins = (int)dmask + 1;
+  const uint32_t kk = w.state[4 * l + 2];
+  const int bpt = nbins >= kSelThreads ? nbins / kSelThreads : 1;
+  const bool owner = tid * bpt < nbins;
+  uint32_t mine = 0;
+  if (owner)
+    for (int j = 0; j < bpt; ++j) mine += gh[tid * bpt + j];
+  const uint32_t incl = wave_scan_down(mine, lane);
+  if (lane == 0) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t above = incl - mine;
+  for (int v = wave + 1; v < kSelWaves; ++v) above += wsum[v];
+  if (owner) {
+    for (int j = bpt - 1; j >= 0; --j) {
+      const uint32_t c = gh[tid * bpt + j];
+      if (above < kk && kk <= above + c) {
+        found[0] = tid * bpt + j;
+        found[1] = above;
+      }
+      above += c;
+    }
+  }
+  __syncthreads();
+  if (owner)
+    for (int j = 0; j < bpt; ++j) gh[tid * bpt + j] = 0u;
+  if (tid == 0) {
+    w.state[4 * l + 0] |= found[0] << shift;
+    w.state[4 * l + 1] |= dmask << shift;
+    w.state[4 * l + 2] = kk - found[1];
+  }
+}
+
+// Keys > T and == T of each slice (T = the k-th largest key).
+__global__ __launch_bounds__(kSplitThreads) void split_count_kernel(const uint32_t* __restrict__ keys, SplitWs w,
+                                                                    int n, int n_slices) {
+  __shared__ uint32_t part[2][kSplitThreads / 64];
+  const int l = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t T = w.state[4 * l];
+  const uint32_t* kl = keys + (size_t)l * n;
+  const int i0 = blockIdx.x * kSplitSlice, i1 = min(n, i0 + kSplitSlice);
+  uint32_t ngt = 0, neq = 0;
+  for (int i = i0 + threadIdx.x; i < i1; i += kSplitThreads) {
+    const uint32_t key = kl[i];
+    ngt += key > T;
+    neq += key == T;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    ngt += __shfl_xor(ngt, o);
+    neq += __shfl_xor(neq, o);
+  }
+  if (lane == 0) {
+    part[0][wave] = ngt;
+    part[1][wave] = neq;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = 0, e = 0;
+    for (int v = 0; v < kSplitThreads / 64; ++v) {
+      a += part[0][v];
+      e += part[1][v];
+    }
+    w.counts[((size_t)l * n_slices + blockIdx.x) * 2 + 0] = a;
+    w.counts[((size_t)l * n_slices + blockIdx.x) * 2 + 1] = e;
+  }
+}
+
+// Ordered compaction of one slice: wave v walks its quarter of the slice 64
+// keys at a time; ballots rank each key among the earlier ones.
+__global__ __launch_bounds__(kSplitThreads) void split_compact_kernel(const uint32_t* __restrict__ keys, SplitWs w,
+                                                                      int32_t* __restrict__ sel, int n, int n_slices) {
+  constexpr int kW = kSplitThreads / 64;
+  __shared__ uint32_t wsum[2][kW];
+  const int l = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t T = w.state[4 * l], need = w.state[4 * l + 2], k = w.state[4 * l + 3];
+  const uint32_t* kl = keys + (size_t)l * n;
+  int32_t* so = sel + (size_t)l * k;
+  uint32_t gt_run = 0, eq_run = 0;
+  for (int s2 = 0; s2 < (int)blockIdx.x; ++s2) {
+    gt_run += w.counts[((size_t)l * n_slices + s2) * 2 + 0];
+    eq_run += w.counts[((size_t)l * n_slices + s2) * 2 + 1];
+  }
+  const int i0 = blockIdx.x * kSplitSlice, i1 = min(n, i0 + kSplitSlice);
+  const int per = (i1 - i0 + kW - 1) / kW;
+  const int w0 = min(i1, i0 + wave * per), w1 = min(i1, w0 + per);
+  const uint64_t below = (1ull << lane) - 1;
+  uint32_t ngt = 0, neq = 0;
+  for (int i = w0 + lane; i < w1 + 63; i += 64) {
+    const uint32_t key = i < w1 ? kl[i] : 0u;
+    ngt += __popcll(__ballot(i < w1 && key > T));
+    neq += __popcll(__ballot(i < w1 && key == T));
+  }
+  if (lane == 0) {
+    wsum[0][wave] = ngt;
+    wsum[1][wave] = neq;
+  }
+  __syncthreads();
+  for (int v = 0; v < wave; ++v) {
+    gt_run += wsum[0][v];
+    eq_run += wsum[1][v];
+  }
+  for (int i = w0 + lane; i < w1 + 63; i += 64) {
+    const bool in = i < w1;
+    const uint32_t key = in ? kl[i] : 0u;
+    const bool gt = in && key > T, eq = in && key == T;
+    const uint64_t mg = __ballot(gt), me = __ballot(eq);
+    const uint32_t gt_before = gt_run + __popcll(mg & below);
+    const uint32_t eq_before = eq_run + __popcll(me & below);
+    if (gt || (eq && eq_before < need)) {
+      const uint32_t pos = gt_before + min(eq_before, need);
+      if (pos < k) so[pos] = i;
+    }
+    gt_run += __popcll(mg);
+    eq_run += __popcll(me);
+  }
+}
+
+size_t split_select_ws_bytes(int n_lists, int n) {
+  const int n_slices = (n + kSplitSlice - 1) / kSplitSlice;
+  return ((size_t)n_lists * kSelBins + (size_t)n_lists * 4 + (size_t)n_lists * n_slices * 2) * 4;
+}
+
+hipError_t launch_select_split(const uint32_t* keys, int32_t* sel, int n_lists, int n, int k, void* ws,
+                               hipStream_t st) {
+  if (n_lists == 0 || k == 0) return hipSuccess;
+  if (n <= k) return launch_select(keys, nullptr, sel, nullptr, n_lists, n, k, 1, st);  // all selected
+  const int n_slices = (n + kSplitSlice - 1) / kSplitSlice;
+  SplitWs w;
+  w.hist = static_cast<uint32_t*>(ws);
+  w.state = w.hist + (size_t)n_lists * kSelBins;
+  w.counts = w.state + (size_t)n_lists * 4;
+  hipLaunchKernelGGL(split_init_kernel, dim3(n_lists), dim3(kSplitThreads), 0, st, w, k);
+  constexpr int kShift[3] = {20, 8, 0};
+  constexpr int kBits[3] = {12, 12, 8};
+  for (int pass = 0; pass < 3; ++pass) {
+    const uint32_t dmask = (1u << kBits[pass]) - 1u;
+    hipLaunchKernelGGL(split_hist_kernel, dim3(n_slices, n_lists), dim3(kSplitThreads), 0, st, keys, w, n,
+                       kShift[pass], dmask);
+    hipLaunchKernelGGL(split_digit_kernel, dim3(n_lists), dim3(kSelThreads), 0, st, w, kShift[pass], dmask);
+  }
+  hipLaunchKernelGGL(split_count_kernel, dim3(n_slices, n_lists), dim3(kSplitThreads), 0, st, keys, w, n, n_slices);
+  hipLaunchKernelGGL(split_compact_kernel, dim3(n_slices, n_lists), dim3(kSplitThreads), 0, st, keys, w, sel, n,
+                     n_slices);
+  return hipGetLastError();
+}
+
 hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* keys,
                         float* scores_out, int nb, int n_cand, int hq, int hkv, hipStream_t st) {
   if (n_cand <= 0) return hipSuccess;

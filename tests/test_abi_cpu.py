@@ -187,7 +187,8 @@ def test_build_workspace_formula():
     s = native.make_build_shape(cfg, batch=2)
     heads, P = 2 * cfg.n_heads_kv, cfg.prefix
     r_bytes = -(-heads * P * 128 * 4 // 256) * 256
-    assert native.build_layer_workspace_bytes(s) == r_bytes + -(-heads * P * 4 // 256) * 256
+    sel_bytes = -(-(heads * 4096 + heads * 4 + heads * -(-P // 8192) * 2) * 4 // 256) * 256
+    assert native.build_layer_workspace_bytes(s) == r_bytes + -(-heads * P * 4 // 256) * 256 + sel_bytes
     assert native.build_layer_workspace_bytes(bshape(window=4096, n_resid=0)) == 0   # no prefix
 
 

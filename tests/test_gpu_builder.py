@@ -339,3 +339,35 @@ def test_full_size_sampled_heads():
     st = check_layer(cfg.with_(name="c3_sampled", n_heads_kv=len(heads)), inp, exp, sub)
     assert st["moved_tokens"] == 0
     print(f"builder full size: {st}", flush=True)
+
+
+def test_builder_exact_ties():
+    """301 tokens with identical keys and values straddle the residual threshold
+    of head 0: identical errors, so the ranking's tie rule (lower token first)
+    decides which of them keep a residual."""
+    cfg, layer = synth.C0.with_(name="b_ties", resid_frac=0.25), 0
+    P, nR, hkv = cfg.prefix, cfg.n_resid, cfg.n_heads_kv
+    inp, exp0 = fixture.builder_io(cfg, layer)
+    err = exp0["errors"][0, 0]
+    dup = np.arange(100, 400)
+    outside = np.setdiff1d(np.arange(P), dup)
+    order = outside[np.lexsort((outside, -err[outside]))]
+    src = int(order[nR - 150])            # nR - 150 tokens outside the copies rank above it
+    x = inp["keys"][0].copy()
+    x[dup] = x[src]
+    v = inp["values"][0].copy()
+    v[:, dup] = v[:, src:src + 1]
+    B = inp["group_basis"][0]
+    c_st = compress.store_coeff(compress.project(codecs.bf16_decode(x[:P]), codecs.bf16_decode(B)), cfg.int4)
+    mlp = [tuple(inp[k][0, h] for k in ("w1", "b1", "w2", "b2")) for h in range(hkv)]
+    e = fixture.builder_expected(cfg, layer, x, B, c_st, range(hkv), v, mlp)
+    exp = {k: a[None] for k, a in e.items()}
+    exp["coeff"] = c_st[None]
+    inp2 = dict(inp, keys=x[None], values=v[None])
+    sel0 = set(exp["res_idx"][0, 0].tolist())
+    kept = sorted(sel0 & set([src, *dup.tolist()]))
+    assert 0 < len(kept) < 301, len(kept)          # the threshold falls inside the copies
+    got = run_builder(cfg, inp2, layer, {"coeff": c_st[None]})
+    st = check_layer(cfg, inp2, exp, got)
+    assert np.array_equal(got["res_idx"][0, 0], exp["res_idx"][0, 0])
+    print(f"\nbuilder ties: {len(kept)} of 301 copies kept; {st}", flush=True)
