@@ -54,7 +54,10 @@ KERNEL_SOURCES = {
     "score": ("score_select.hip", "common.h", "internal.h"),
     "select": ("score_select.hip", "common.h", "internal.h"),
     "merge": ("attend.hip", "common.h", "internal.h"),
+    "predict": ("build.hip", "common.h", "internal.h"),
+    "proj": ("build.hip", "common.h", "internal.h"),
 }
+BUILD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "build_c3_262k_hbm_traffic.txt")
 
 
 def source_hash(kernel):
@@ -66,12 +69,12 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, workload, nb):
+def measured_traffic(kernel, workload, nb, path=TRAFFIC_FILE):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size), or None when
     the summary is for another workload or the kernel's sources changed since."""
     try:
-        lines = open(TRAFFIC_FILE).read().splitlines()
+        lines = open(path).read().splitlines()
     except OSError:
         return None
     for ln in lines:
@@ -318,8 +321,10 @@ def build_algorithmic(cfg, nb):
     P, D, r, Hkv, d, H = cfg.prefix, cfg.group_dim, cfg.rank, cfg.n_heads_kv, cfg.head_dim, cfg.mlp_hidden
     s_c = 0.5 + 2.0 / 32 if cfg.int4 else 2.0
     f = {"proj": 2.0 * P * D * r, "predict": Hkv * P * (2.0 * d * r + 4.0 * d * H)}
+    # predict: the coefficients once (all KV heads of a token share its row), the
+    # layer's values, the fp32 residual rows and error keys written
     b = {"proj": P * D * 2.0 + r * D * 2.0 + P * r * s_c,
-         "predict": Hkv * P * (r * s_c + d * 2.0 + d * 4.0 + 4.0)}
+         "predict": P * r * s_c + Hkv * P * (d * 2.0 + d * 4.0 + 4.0)}
     return {k: v * nb for k, v in f.items()}, {k: v * nb for k, v in b.items()}
 
 
@@ -443,7 +448,8 @@ def bench_build(args):
                    "group_layers": G, "heads_kv": Hkv, "rank": r, "resid_frac": cfg.resid_frac,
                    "int4": cfg.int4},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFS,
-                     "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4),
+                     "traffic": measured_traffic(dom, cfg.name + "_build", nb, BUILD_TRAFFIC_FILE)},
         "kernels": {k: {"ms_per_launch": round(per_launch[k], 5), "launches_per_step": launches[k] // args.steps,
                         "TFLOP/s": round(flops[k] / (per_launch[k] * 1e-3) / 1e12, 2) if k in flops else None,
                         "GB/s": round(byts[k] / (per_launch[k] * 1e-3) / 1e9, 1) if k in byts else None}
@@ -461,6 +467,8 @@ def main():
               "sequence with no exchange, so N GPUs would each run this single-GPU workload.", file=sys.stderr)
         sys.exit(2)
     if args.build:
+        if args.copy_probe_mib:
+            copy_probe(args.copy_probe_mib)
         bench_build(args)
         return
     import synth
