@@ -159,6 +159,20 @@ int lowram_decode_step_events(const lowram_shape* shape, const lowram_layer_cach
                               void* workspace, size_t ws_bytes, void* stream,
                               void* const* events);
 
+/*
+ * Shared-prefix multi-query decode: shape->batch queries (each a full set of
+ * Hq query heads) attend to ONE compressed context, e.g. many questions over
+ * one long document (review, results and limitations paragraphs: one
+ * test-time fit per context; explainer, "Why it matters").  Every array of
+ * `cache` has the layout of lowram_layer_cache for NB = 1 and is read by all
+ * queries (batch stride 0); q, out, sel_out and the workspace are per query
+ * ([NB][...] with NB = shape->batch).  Each query selects its own top-k
+ * chunks.  `events` as in lowram_decode_step_events (may be NULL).
+ */
+int lowram_decode_shared(const lowram_shape* shape, const lowram_layer_cache* cache,
+                         const uint16_t* q, uint16_t* out, int32_t* sel_out, void* workspace,
+                         size_t ws_bytes, void* stream, void* const* events);
+
 /* Dense GQA decode over the full bf16 cache: the uncompressed baseline the
    LowRAM pages compare against (review, results paragraph). */
 typedef struct dense_shape {

@@ -71,7 +71,7 @@ Plan make_plan(const lowram_shape* s) {
 int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t* q, uint16_t* out,
              int32_t* sel_out, float* scores_out, float* kpre_out, float* kpost_out,
              float* vhat_out, void* ws, size_t ws_bytes, void* stream,
-             void* const* events = nullptr) {
+             void* const* events = nullptr, bool shared = false) {
   int st = check_shape(s);
   if (st) return st;
   if (!c || !q || !out || !ws) return LOWRAM_ERR_NULL;
@@ -113,13 +113,13 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   if (!mark(0)) return LOWRAM_ERR_HIP;
   if (has_prefix) {
     if (launch_score(q, c->landmark, keys, scores_out, s->batch, p.n_cand, s->n_heads_q,
-                     s->n_heads_kv, hs) != hipSuccess)
+                     s->n_heads_kv, hs, shared ? 0 : 1) != hipSuccess)
       return LOWRAM_ERR_HIP;
   }
   if (!mark(1)) return LOWRAM_ERR_HIP;
   if (has_prefix || sel_out) {
     if (launch_select(keys, c->cand_ids, sel, sel_out, s->batch, p.n_cand, s->topk, s->n_heads_kv,
-                      hs) != hipSuccess)
+                      hs, shared ? 0 : 1) != hipSuccess)
       return LOWRAM_ERR_HIP;
   }
   if (!mark(2)) return LOWRAM_ERR_HIP;
@@ -133,6 +133,7 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   a.nb = s->batch; a.hq = s->n_heads_q; a.hkv = s->n_heads_kv; a.g = p.g;
   a.prefix = s->prefix_len; a.window = s->window; a.n_chunks = p.n_chunks; a.k_eff = p.k_eff;
   a.n_resid = s->n_resid;
+  a.cache_bmul = shared ? 0 : 1;
   a.n_sel_tiles = has_prefix ? p.n_sel_tiles : 0;
   a.n_win_tiles = p.n_win_tiles;
   a.n_split = p.n_split;
@@ -241,6 +242,13 @@ int lowram_decode_step_events(const lowram_shape* shape, const lowram_layer_cach
                               size_t ws_bytes, void* stream, void* const* events) {
   return run_step(shape, cache, q, out, sel_out, nullptr, nullptr, nullptr, nullptr, workspace,
                   ws_bytes, stream, events);
+}
+
+int lowram_decode_shared(const lowram_shape* shape, const lowram_layer_cache* cache, const uint16_t* q,
+                         uint16_t* out, int32_t* sel_out, void* workspace, size_t ws_bytes, void* stream,
+                         void* const* events) {
+  return run_step(shape, cache, q, out, sel_out, nullptr, nullptr, nullptr, nullptr, workspace, ws_bytes,
+                  stream, events, true);
 }
 
 int lowram_decode_stages(const lowram_shape* shape, const lowram_layer_cache* cache,

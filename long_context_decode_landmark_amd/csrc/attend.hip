@@ -171,6 +171,9 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
   const int b = bh / a.hkv, h = bh % a.hkv;
   const int g = a.g;
   const size_t head = (size_t)b * a.hkv + h;
+  // cache arrays: per sequence, or one context shared by every query (stride 0)
+  const int cseq = b * a.cache_bmul;
+  const size_t chead = (size_t)cseq * a.hkv + h;
   const uint16_t* qh = a.q + ((size_t)b * a.hq + (size_t)h * g) * kHeadDim;
   unsigned char* buf = L.buf;
 
@@ -192,9 +195,9 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     //      is W1 rows [32 c, 32 c + 32) (pi order, 8 KiB) then W2 columns
     //      [32 c, 32 c + 32) (natural, four rows per line, 8 KiB).  Pieces
     //      are XOR-swizzled inside each 256-byte line by the line index.
-    const __amdgpu_buffer_rsrc_t bas = buffer_rsrc(a.basis + head * (size_t)kHeadDim * RANK, kHeadDim * RANK * 2);
-    const __amdgpu_buffer_rsrc_t w1r = buffer_rsrc(a.w1 + head * (size_t)kHidden * kHeadDim, kHidden * kHeadDim * 2);
-    const __amdgpu_buffer_rsrc_t w2r = buffer_rsrc(a.w2 + head * (size_t)kHeadDim * kHidden, kHeadDim * kHidden * 2);
+    const __amdgpu_buffer_rsrc_t bas = buffer_rsrc(a.basis + chead * (size_t)kHeadDim * RANK, kHeadDim * RANK * 2);
+    const __amdgpu_buffer_rsrc_t w1r = buffer_rsrc(a.w1 + chead * (size_t)kHidden * kHeadDim, kHidden * kHeadDim * 2);
+    const __amdgpu_buffer_rsrc_t w2r = buffer_rsrc(a.w2 + chead * (size_t)kHeadDim * kHidden, kHeadDim * kHidden * 2);
     // basis: load u covers rows 32 u + r0 (r0 = tid / 8), piece tid % 8
     const int r0 = tid >> 3, pb = tid & 7;
     const uint32_t bas_goff = (uint32_t)((row_perm32(r0) * RANK + 8 * pb) * 2);
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     float csc[CI4 ? NR : 1][NT];
     auto gather = [&](int s) {
       if constexpr (!CI4) {
-        const uint16_t* cb = static_cast<const uint16_t*>(a.coeff) + (size_t)b * a.prefix * RANK;
+        const uint16_t* cb = static_cast<const uint16_t*>(a.coeff) + (size_t)cseq * a.prefix * RANK;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -248,8 +251,8 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
             cv[s][ks][nt] = load_bf16x8(cb + (size_t)tok[nt] * RANK + 64 * s + 32 * ks + 8 * grp);
       } else {
         // 16 codes r = 64 s + 16 grp .. + 15 and their group scale
-        const uint8_t* cb = static_cast<const uint8_t*>(a.coeff) + (size_t)b * a.prefix * (RANK / 2);
-        const uint16_t* sb = a.coeff_scale + (size_t)b * a.prefix * (RANK / 32);
+        const uint8_t* cb = static_cast<const uint8_t*>(a.coeff) + (size_t)cseq * a.prefix * (RANK / 2);
+        const uint16_t* sb = a.coeff_scale + (size_t)cseq * a.prefix * (RANK / 32);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           cq[s][nt] = *reinterpret_cast<const u32x2*>(cb + (size_t)tok[nt] * (RANK / 2) + 32 * s + 8 * grp);
@@ -267,8 +270,8 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
 #pragma unroll
     for (int s = 0; s < SL && s < NS; ++s) stage_load(s, sreg[s]);
     // b1 in the order the value section reads it: unit 32 c + row_perm32(p) at 32 c + p
-    const uint16_t b1v = a.b1[head * kHidden + (tid & ~31) + row_perm32(tid & 31)];
-    const uint16_t b2v = tid < kHeadDim ? a.b2[head * kHeadDim + tid] : 0;
+    const uint16_t b1v = a.b1[chead * kHidden + (tid & ~31) + row_perm32(tid & 31)];
+    const uint16_t b2v = tid < kHeadDim ? a.b2[chead * kHeadDim + tid] : 0;
     const u32x4 qv = tid < 16 * g ? *reinterpret_cast<const u32x4*>(qh + 8 * tid) : u32x4{0u, 0u, 0u, 0u};
     constexpr int PPT = kAttChunksWG / 4;  // RoPE base entries per thread (chunks x 64 / 256)
     const int rp0 = (tid % (64 / PPT)) * PPT, rq0 = (tid & 31) * 2;
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) asm volatile("" ::"v"(tok[nt]) : "memory");
     uint32_t rd = 0;
-    if (tid < kAttChunksWG) rd = a.res_desc[head * (size_t)a.n_chunks + rd_chunk];
+    if (tid < kAttChunksWG) rd = a.res_desc[chead * (size_t)a.n_chunks + rd_chunk];
 #pragma unroll
     for (int s = 0; s < LG && s < NR; ++s) gather(s);
     __builtin_amdgcn_sched_barrier(0);
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
           // the end of the buffer, which returns zeros
           const uint32_t nbytes = (uint32_t)a.n_resid * kHeadDim * 2;
           const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(
-              static_cast<const uint16_t*>(a.res_val) + head * (size_t)a.n_resid * kHeadDim, nbytes);
+              static_cast<const uint16_t*>(a.res_val) + chead * (size_t)a.n_resid * kHeadDim, nbytes);
 #pragma unroll
           for (int u = 0; u < RL; ++u) {
             const int tl = 16 * u + (tid >> 4);
@@ -376,9 +379,9 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
           const uint32_t nbytes = (uint32_t)a.n_resid * (kHeadDim / 2);
           const uint32_t sbytes = (uint32_t)a.n_resid * (kHeadDim / 32) * 2;
           const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(
-              static_cast<const uint8_t*>(a.res_val) + head * (size_t)a.n_resid * (kHeadDim / 2), nbytes);
+              static_cast<const uint8_t*>(a.res_val) + chead * (size_t)a.n_resid * (kHeadDim / 2), nbytes);
           const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
-              a.res_scale + head * (size_t)a.n_resid * (kHeadDim / 32), sbytes);
+              a.res_scale + chead * (size_t)a.n_resid * (kHeadDim / 32), sbytes);
 #pragma unroll
           for (int u = 0; u < RL; ++u) {
             const int tl = 64 * u + (tid >> 2);
@@ -656,8 +659,8 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     // ========================================================= exact window
     const int w0 = (split - a.n_sel_tiles) * kAttTokWG + wave * kAttTokWave;
     const int nvalid = max(0, min(kAttTokWave, a.window - w0));
-    const uint16_t* kw = a.win_k + head * (size_t)a.window * kHeadDim;
-    const uint16_t* vw = a.win_v + head * (size_t)a.window * kHeadDim;
+    const uint16_t* kw = a.win_k + chead * (size_t)a.window * kHeadDim;
+    const uint16_t* vw = a.win_v + chead * (size_t)a.window * kHeadDim;
     bf16x8 qn[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)

@@ -40,15 +40,19 @@ struct AttendArgs {
   float* kpost_out;
   float* vhat_out;
   int nb, hq, hkv, g, prefix, window, n_chunks, k_eff, n_resid;
+  int cache_bmul;  // 1: cache arrays per sequence; 0: one context shared by all nb queries
   int n_sel_tiles, n_win_tiles, n_split, total, padded_total;
   float scale_log2;
   double inv_freq[64];
 };
 
+// cache_bmul: 1 = landmarks / candidate ids per sequence, 0 = one shared context
 hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* keys,
-                        float* scores_out, int nb, int n_cand, int hq, int hkv, hipStream_t st);
+                        float* scores_out, int nb, int n_cand, int hq, int hkv, hipStream_t st,
+                        int cache_bmul = 1);
 hipError_t launch_select(const uint32_t* keys, const int32_t* cand_ids, int32_t* sel,
-                         int32_t* sel_out, int nb, int n_cand, int k, int hkv, hipStream_t st);
+                         int32_t* sel_out, int nb, int n_cand, int k, int hkv, hipStream_t st,
+                         int cache_bmul = 1);
 hipError_t launch_attend(const AttendArgs& a, int rank, bool coeff_int4, bool resid_int4,
                          hipStream_t st);
 // Exact top-k of n_lists long lists (keys [n_lists][n] -> sel [n_lists][k]

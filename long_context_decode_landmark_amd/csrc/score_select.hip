@@ -30,7 +30,7 @@ namespace lowram {
 __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ landmark,
     uint32_t* __restrict__ keys, float* __restrict__ scores_out, int n_cand, int n_heads_q,
-    int n_heads_kv, int chunks_per_wg) {
+    int n_heads_kv, int chunks_per_wg, int cache_bmul) {
   const int b = blockIdx.z, h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, col = lane & 15;
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
     qa[ks] = col < g ? load_bf16x8(qb + col * kHeadDim + 32 * ks + 8 * grp) : zero_bf16x8();
 
   const size_t head = (size_t)b * n_heads_kv + h;
-  const uint16_t* lm = landmark + head * (size_t)n_cand * kHeadDim;
+  const uint16_t* lm = landmark + ((size_t)b * cache_bmul * n_heads_kv + h) * (size_t)n_cand * kHeadDim;
   uint32_t* kout = keys + head * (size_t)n_cand;
   float* sout = scores_out ? scores_out + head * (size_t)n_cand : nullptr;
   const int c_begin = blockIdx.x * chunks_per_wg;
@@ -126,14 +126,15 @@ __device__ __forceinline__ uint32_t wave_scan_down(uint32_t x, int lane) {
 template <bool kLds>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint32_t* __restrict__ keys, const int32_t* __restrict__ cand_ids,
-    int32_t* __restrict__ sel, int32_t* __restrict__ sel_out, int n_cand, int k, int n_heads_kv) {
+    int32_t* __restrict__ sel, int32_t* __restrict__ sel_out, int n_cand, int k, int n_heads_kv,
+    int cache_bmul) {
   extern __shared__ unsigned char sel_smem[];
   SelLds& S = *reinterpret_cast<SelLds*>(sel_smem);
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t head = (size_t)b * n_heads_kv + h;
   const uint32_t* kg = keys + head * (size_t)n_cand;
-  const int32_t* ids = cand_ids ? cand_ids + head * (size_t)n_cand : nullptr;
+  const int32_t* ids = cand_ids ? cand_ids + ((size_t)b * cache_bmul * n_heads_kv + h) * (size_t)n_cand : nullptr;
   const int k_eff = min(k, n_cand);
   int32_t* so = sel + head * (size_t)k_eff;
   int32_t* so2 = sel_out ? sel_out + head * (size_t)k : nullptr;
@@ -443,7 +444,8 @@ hipError_t launch_select_split(const uint32_t* keys, int32_t* sel, int n_lists, 
 }
 
 hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* keys,
-                        float* scores_out, int nb, int n_cand, int hq, int hkv, hipStream_t st) {
+                        float* scores_out, int nb, int n_cand, int hq, int hkv, hipStream_t st,
+                        int cache_bmul) {
   if (n_cand <= 0) return hipSuccess;
   // chunks per workgroup: the smallest power of two >= 256 that keeps the
   // grid within LOWRAM_SCORE_MAX_WG workgroups
@@ -452,12 +454,13 @@ hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* k
   while ((long long)((n_cand + cpw - 1) / cpw) * heads > LOWRAM_SCORE_MAX_WG && cpw < 4096) cpw *= 2;
   dim3 grid((n_cand + cpw - 1) / cpw, hkv, nb);
   hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, st, q, landmark, keys, scores_out,
-                     n_cand, hq, hkv, cpw);
+                     n_cand, hq, hkv, cpw, cache_bmul);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const uint32_t* keys, const int32_t* cand_ids, int32_t* sel,
-                         int32_t* sel_out, int nb, int n_cand, int k, int hkv, hipStream_t st) {
+                         int32_t* sel_out, int nb, int n_cand, int k, int hkv, hipStream_t st,
+                         int cache_bmul) {
   if (n_cand <= 0 && !sel_out) return hipSuccess;
   const dim3 grid(hkv, nb), block(kSelThreads);
   static bool attr_set = false;  // dynamic LDS above 64 KiB must be allowed once
@@ -469,10 +472,10 @@ hipError_t launch_select(const uint32_t* keys, const int32_t* cand_ids, int32_t*
   }
   if (n_cand <= kSelLdsKeys) {
     hipLaunchKernelGGL(select_kernel<true>, grid, block, sizeof(SelLds), st, keys, cand_ids, sel, sel_out,
-                       n_cand, k, hkv);
+                       n_cand, k, hkv, cache_bmul);
   } else {
     hipLaunchKernelGGL(select_kernel<false>, grid, block, sizeof(SelLds) - kSelLdsKeys * 4, st, keys,
-                       cand_ids, sel, sel_out, n_cand, k, hkv);
+                       cand_ids, sel, sel_out, n_cand, k, hkv, cache_bmul);
   }
   return hipGetLastError();
 }

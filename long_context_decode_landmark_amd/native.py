@@ -24,6 +24,7 @@ SYMBOLS = (
     "lowram_decode_step",
     "lowram_decode_stages",
     "lowram_decode_step_events",
+    "lowram_decode_shared",
     "dense_workspace_bytes",
     "dense_decode_step",
     "lowram_resid_chunk_desc",
@@ -102,6 +103,8 @@ def lib() -> ctypes.CDLL:
                                            vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lowram_decode_step_events.argtypes = [ctypes.POINTER(LowramShape), ctypes.POINTER(LowramLayerCache),
                                                 vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_void_p)]
+        L.lowram_decode_shared.argtypes = [ctypes.POINTER(LowramShape), ctypes.POINTER(LowramLayerCache),
+                                           vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_void_p)]
         L.dense_workspace_bytes.argtypes = [ctypes.POINTER(DenseShape), ctypes.POINTER(sz)]
         L.dense_decode_step.argtypes = [ctypes.POINTER(DenseShape), ctypes.POINTER(DenseLayerCache),
                                         vp, vp, vp, sz, vp]
@@ -190,6 +193,15 @@ def decode_step_events(shape, cache, q, out, workspace, events, sel_out=None, st
                                            _ptr(sel_out), _ptr(workspace),
                                            workspace.numel() * workspace.element_size(), _stream(stream), arr),
            "lowram_decode_step_events")
+
+
+def decode_shared(shape, cache, q, out, workspace, sel_out=None, events=None, stream=None) -> None:
+    """lowram_decode_shared: shape.batch queries against one context (cache arrays for NB = 1)."""
+    c = cache if isinstance(cache, LowramLayerCache) else make_cache(cache)
+    arr = None if events is None else (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    _check(lib().lowram_decode_shared(ctypes.byref(shape), ctypes.byref(c), _ptr(q), _ptr(out), _ptr(sel_out),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream), arr), "lowram_decode_shared")
 
 
 def decode_stages(shape, cache, q, out, workspace, sel_out=None, scores=None, kpre=None, kpost=None,
