@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-slices", type=int, default=10)
     ap.add_argument("--graph", action="store_true", help="also time a hipGraph replay of the step")
     ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--shared", type=int, default=0, metavar="Q",
+                    help="time Q queries over one shared context (shared-prefix multi-query decode)")
     ap.add_argument("--build", action="store_true",
                     help="time the cache builder (one layer group of one sequence) instead of the decode step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -126,8 +128,9 @@ def algorithmic(cfg, nb):
     return {kk: v * nb for kk, v in b.items()}, {kk: v * nb for kk, v in f.items()}
 
 
-def build_device_cache(cfg, nb, n_layers, seed, dev):
-    """Distinct device buffers for every (sequence, layer); one drawn slice replicated."""
+def build_device_cache(cfg, nb, n_layers, seed, dev, q_nb=None):
+    """Distinct device buffers for every (sequence, layer); one drawn slice replicated.
+    Queries: q_nb (default nb) query sets per layer."""
     import torch
 
     from long_context_decode_landmark_amd import native
@@ -152,18 +155,19 @@ def build_device_cache(cfg, nb, n_layers, seed, dev):
         t = {kk: rep(v) for kk, v in base.items()}
         t.update(groups[li // cfg.group_layers])
         layers.append(t)
-        qs.append(sd.draw_queries(cfg, nb, seed + 100 + li, dev))
+        qs.append(sd.draw_queries(cfg, nb if q_nb is None else q_nb, seed + 100 + li, dev))
     torch.cuda.synchronize()
     return layers, qs
 
 
-def time_lowram(cfg, nb, n_layers, steps, warmup, seed, graph):
+def time_lowram(cfg, nb, n_layers, steps, warmup, seed, graph, shared=False):
+    """Decode steps of nb sequences, or (shared) of nb queries over one context per layer."""
     import torch
 
     from long_context_decode_landmark_amd import native
 
     dev = torch.device("cuda:0")
-    layers, qs = build_device_cache(cfg, nb, n_layers, seed, dev)
+    layers, qs = build_device_cache(cfg, 1 if shared else nb, n_layers, seed, dev, q_nb=nb)
     shape = native.make_shape(cfg, batch=nb)
     ws = torch.empty(native.workspace_bytes(shape), dtype=torch.uint8, device=dev)
     out = torch.empty_like(qs[0])
@@ -172,7 +176,10 @@ def time_lowram(cfg, nb, n_layers, steps, warmup, seed, graph):
 
     def step(events=None):
         for li in range(n_layers):
-            if events is None:
+            if shared:
+                native.decode_shared(shape, caches[li], qs[li], out, ws,
+                                     events=None if events is None else events[li])
+            elif events is None:
                 native.decode_step(shape, caches[li], qs[li], out, ws)
             else:
                 native.decode_step_events(shape, caches[li], qs[li], out, ws, events[li])
@@ -460,6 +467,34 @@ def bench_build(args):
     print(json.dumps(res))
 
 
+def bench_shared(args, cfg, nq, n_layers):
+    """Q queries over one 262K context per layer: every query's own top-k,
+    rebuild and attention; the context is read by all of them."""
+    step_ms, kern, _, _, _ = time_lowram(cfg, nq, n_layers, args.steps, args.warmup, args.seed, False,
+                                         shared=True)
+    byts, flops = algorithmic(cfg, nq)
+    # the context's landmarks, weights and window are read once per layer, not once per query
+    ctx = {"score": byts["score"] / nq, "attend": byts["attend"] / nq}
+    per_kernel = {k: {"ms": round(kern[k], 5),
+                      "TFLOP/s": round(flops[k] / (kern[k] * 1e-3) / 1e12, 2) if kern[k] > 0 else None}
+                  for k in KERNELS}
+    ach = flops["attend"] / (kern["attend"] * 1e-3) / 1e12
+    res = {
+        "metric": "shared-context decode tokens/sec: Q queries over one 262K context",
+        "value": round(nq / (step_ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if not cfg.int4 else "bf16+int4",
+        "data": "synthetic (seeded device draws, one context per layer)",
+        "config": {"workload": cfg.name + "_shared", "queries": nq, "ctx": cfg.ctx, "layers": n_layers,
+                   "heads_q": cfg.n_heads_q, "heads_kv": cfg.n_heads_kv, "topk": cfg.topk, "rank": cfg.rank},
+        "roofline": {"bound": "mfma", "kernel": "attend", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": None},
+        "context_bytes_per_layer_GB": {k: round(v / 1e9, 4) for k, v in ctx.items()},
+        "kernels": per_kernel,
+    }
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -475,6 +510,9 @@ def main():
     cfg = synth.CONFIGS[args.config]
     nb = args.batch or cfg.batch
     n_layers = args.layers or cfg.n_layers
+    if args.shared:
+        bench_shared(args, cfg, args.shared, n_layers)
+        return
 
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)

@@ -89,6 +89,84 @@ __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
   }
 }
 
+// Scoring for many queries against ONE shared context: the 16 A rows of the
+// MFMA tile hold 16 / G queries' G query heads (G a power of two <= 16), so
+// each landmark block streamed serves all of them.  Lane (grp, col) receives
+// rows 4 grp + e of chunk col; a query's G rows lie in one lane (G <= 4,
+// max over e) or span 16-lane groups (G = 8, 16: max across them).
+template <int G>
+__global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_multi_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ landmark,
+    uint32_t* __restrict__ keys, float* __restrict__ scores_out, int n_cand, int n_heads_q,
+    int n_heads_kv, int chunks_per_wg, int nq) {
+  constexpr int QG = 16 / G;  // queries per tile
+  const int qb = blockIdx.z, h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane >> 4, col = lane & 15;
+
+  // A row col = query qb * QG + col / G, head h * G + col % G
+  const int aq = qb * QG + col / G;
+  bf16x8 qa[4];
+  const uint16_t* qrow = q + ((size_t)aq * n_heads_q + (size_t)h * G + col % G) * kHeadDim;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qa[ks] = aq < nq ? load_bf16x8(qrow + 32 * ks + 8 * grp) : zero_bf16x8();
+
+  const uint16_t* lm = landmark + (size_t)h * n_cand * kHeadDim;
+  const int c_begin = blockIdx.x * chunks_per_wg;
+  const int c_end = min(n_cand, c_begin + chunks_per_wg);
+  auto load_group = [&](int c0, bf16x8 (&lv)[4][4]) {
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const int cc = min(c0 + 16 * gi + col, n_cand - 1);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) lv[gi][ks] = load_bf16x8(lm + (size_t)cc * kHeadDim + 32 * ks + 8 * grp);
+    }
+  };
+  bf16x8 cur[4][4], nxt[4][4];
+  int c0 = c_begin + wave * 64;
+  if (c0 < c_end) load_group(c0, cur);
+  for (; c0 < c_end; c0 += 256) {
+    if (c0 + 256 < c_end) load_group(c0 + 256, nxt);
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mfma16(qa[ks], cur[gi][ks], acc);
+      const int c = c0 + 16 * gi + col;
+      if constexpr (G <= 4) {
+        // this lane holds rows 4 grp .. 4 grp + 3 = queries (4 grp) / G ..
+#pragma unroll
+        for (int e0 = 0; e0 < 4; e0 += G) {
+          float sc = acc[e0];
+#pragma unroll
+          for (int e = 1; e < G; ++e) sc = fmaxf(sc, acc[e0 + e]);
+          const int qi = qb * QG + (4 * grp + e0) / G;
+          if (qi < nq && c < c_end) {
+            const size_t o = ((size_t)qi * n_heads_kv + h) * n_cand + c;
+            keys[o] = score_key(sc);
+            if (scores_out) scores_out[o] = sc;
+          }
+        }
+      } else {
+        float sc = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+        sc = fmaxf(sc, __shfl_xor(sc, 16));
+        if constexpr (G == 16) sc = fmaxf(sc, __shfl_xor(sc, 32));
+        const int qi = qb * QG + (4 * grp) / G;
+        const bool writer = G == 16 ? grp == 0 : (grp & 1) == 0;
+        if (writer && qi < nq && c < c_end) {
+          const size_t o = ((size_t)qi * n_heads_kv + h) * n_cand + c;
+          keys[o] = score_key(sc);
+          if (scores_out) scores_out[o] = sc;
+        }
+      }
+    }
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) cur[gi][ks] = nxt[gi][ks];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Exact top-k by radix select on the order-preserving keys.  Three passes on
 // the key bits [31:20], [19:8], [7:0] find the k-th largest key T and how many
@@ -449,12 +527,25 @@ hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* k
   if (n_cand <= 0) return hipSuccess;
   // chunks per workgroup: the smallest power of two >= 256 that keeps the
   // grid within LOWRAM_SCORE_MAX_WG workgroups
-  const long long heads = (long long)nb * hkv;
+  const int g = hq / hkv;
+  const bool multi = cache_bmul == 0 && nb > 1 && (g == 1 || g == 2 || g == 4 || g == 8 || g == 16);
+  const int qblocks = multi ? (nb + 16 / g - 1) / (16 / g) : nb;
+  const long long heads = (long long)qblocks * hkv;
   int cpw = 256;
   while ((long long)((n_cand + cpw - 1) / cpw) * heads > LOWRAM_SCORE_MAX_WG && cpw < 4096) cpw *= 2;
-  dim3 grid((n_cand + cpw - 1) / cpw, hkv, nb);
-  hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, st, q, landmark, keys, scores_out,
-                     n_cand, hq, hkv, cpw, cache_bmul);
+  dim3 grid((n_cand + cpw - 1) / cpw, hkv, qblocks);
+  if (!multi) {
+    hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, st, q, landmark, keys, scores_out,
+                       n_cand, hq, hkv, cpw, cache_bmul);
+  } else {
+    switch (g) {
+      case 1: hipLaunchKernelGGL(score_multi_kernel<1>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb); break;
+      case 2: hipLaunchKernelGGL(score_multi_kernel<2>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb); break;
+      case 4: hipLaunchKernelGGL(score_multi_kernel<4>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb); break;
+      case 8: hipLaunchKernelGGL(score_multi_kernel<8>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb); break;
+      default: hipLaunchKernelGGL(score_multi_kernel<16>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb); break;
+    }
+  }
   return hipGetLastError();
 }
 

@@ -28,6 +28,9 @@ CASES = {
     "ragged_q3": (synth.C0.with_(name="sh_ragged", ctx=4060, window=300, topk=45, rank=128, bias_std=0.1), 0, 3),
     "int4_evict_q4": (synth.C0.with_(name="sh_eq", rank=128, int4=True, evict=True, resid_frac=0.25, topk=48), 1, 4),
     "gqa8_q2": (synth.C0.with_(name="sh_g8", n_heads_q=16, rank=256, topk=40), 0, 2),
+    "gqa16_q3": (synth.C0.with_(name="sh_g16", n_heads_q=32, rank=512, topk=70), 1, 3),
+    "gqa2_q7": (synth.C0.with_(name="sh_g2", n_heads_q=4, topk=33), 0, 7),
+    "gqa1_q9": (synth.C0.with_(name="sh_g1", n_heads_q=2, window=1, ctx=4033, topk=17), 1, 9),
 }
 
 
