@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LOWRAM_ABI_VERSION 1
+#define LOWRAM_ABI_VERSION 2
 
 enum {
   LOWRAM_OK = 0,
@@ -84,9 +84,19 @@ typedef struct lowram_shape {
   float rope_theta;      /* RoPE base; rotate-half pairing (i, i + d/2),
                             angle = position * theta^(-2i/d)                          */
   float softmax_scale;   /* logit scale, usually 1/sqrt(d)                           */
+  /* Capacities, for caches that grow in place (lowram_append_*); 0 = dense.
+     prefix_cap: coefficient rows per sequence, and (prefix_cap / S) landmark
+     and descriptor rows per (sequence, KV head); >= prefix_len, a multiple
+     of S.  window_cap: window rows per (sequence, KV head); >= window.  With
+     cand_ids (eviction) both must be 0.  n_resid is the residual-row stride
+     per (sequence, KV head); rows are reached through the descriptors only. */
+  int32_t prefix_cap;
+  int32_t window_cap;
 } lowram_shape;
 
 /* One layer's compressed cache (all device pointers). */
+/* Layouts below are written for a dense cache; with capacities, P reads
+   prefix_cap, P/S reads prefix_cap/S and W reads window_cap. */
 typedef struct lowram_layer_cache {
   const void* coeff;            /* bf16: [NB][P][r];  int4: [NB][P][r/2] bytes                */
   const uint16_t* coeff_scale;  /* int4 only: [NB][P][r/32] fp16; NULL for bf16               */
@@ -229,6 +239,13 @@ typedef struct lowram_build_shape {
   int32_t coeff_fmt;     /* LOWRAM_FMT_* of the coefficients written                   */
   int32_t resid_fmt;     /* LOWRAM_FMT_* of the residual rows written                  */
   float rope_theta;      /* RoPE base, as in lowram_shape                              */
+  /* Output capacities for a cache that later grows in place (0 = dense):
+     coefficient rows per sequence (and prefix_cap / S landmark and descriptor
+     rows per head), window rows per head, residual rows per head; each >=
+     the size it holds, prefix_cap a multiple of S.  Inputs stay dense. */
+  int32_t prefix_cap;
+  int32_t window_cap;
+  int32_t resid_cap;
 } lowram_build_shape;
 
 /*
@@ -264,6 +281,10 @@ typedef struct lowram_layer_build {
   uint32_t* res_chunk_desc;     /* out: [NB][Hkv][P/S] residual descriptors                   */
   uint16_t* win_k;              /* out: [NB][Hkv][W][d] bf16 post-RoPE keys of the window     */
   uint16_t* win_v;              /* out: [NB][Hkv][W][d] bf16 values of the window             */
+  float* res_thresh;            /* out, optional: [NB][Hkv] the nR-th largest ||R_t|| (0 when
+                                   every token is kept, +inf when nR = 0), the threshold of
+                                   lowram_append_layer                                        */
+  int32_t* res_count;           /* out, optional: [NB][Hkv] residual rows in use (= nR)        */
 } lowram_layer_build;
 
 /* Workspace bytes lowram_build_layer needs (pure function of the shape):
@@ -301,6 +322,52 @@ int lowram_build_layer_events(const lowram_build_shape* shape, int32_t layer_in_
                               const lowram_layer_build* io, void* workspace, size_t ws_bytes,
                               void* stream, void* const* events);
 
+/* ---------------------------------------------------------------------------
+ * Window rollover (incremental append).  As decoding proceeds, the oldest S
+ * tokens of the exact window are compressed into a new prefix chunk: their
+ * coefficients, a landmark, and a residual test against the threshold the
+ * cache was built with (the review's limitations paragraph: long generation
+ * needs the newly generated suffix compressed periodically).  The cache must
+ * have capacities (lowram_shape.prefix_cap / window_cap, n_resid = residual
+ * rows per head) with room for the chunk; eviction (cand_ids) is not
+ * supported.  `shape` describes the cache BEFORE the call (prefix_len = P,
+ * window = W >= S, P + S <= prefix_cap); afterwards the caller's shape is
+ * prefix_len = P + S, window = W - S.
+ * ------------------------------------------------------------------------- */
+
+/* Coefficient rows P .. P+S-1 of one layer group: keys_new [NB][S][D] (the S
+   tokens' pre-RoPE keys of the group, D = group_layers * Hkv * d), basis
+   [NB][r][D]; written into coeff (+ coeff_scale) in the cache layout. */
+int lowram_append_coeff(const lowram_shape* shape, int32_t group_layers, const uint16_t* keys_new,
+                        const uint16_t* basis, void* coeff, uint16_t* coeff_scale, void* stream);
+
+/* One layer's part of the rollover (run after lowram_append_coeff).  The
+   written arrays are the same ones `cache` points to, passed writable. */
+typedef struct lowram_layer_append {
+  const uint16_t* keys_new;     /* in:  [NB][S][D] as for lowram_append_coeff                  */
+  const float* res_thresh;      /* in:  [NB][Hkv] residual threshold (lowram_layer_build)      */
+  int32_t* res_count;           /* in/out: [NB][Hkv] residual rows in use                      */
+  int32_t* res_dropped;         /* in/out: [NB][Hkv] += tokens over the threshold that found no
+                                   free residual row (their values are then predicted only)   */
+  uint16_t* landmark;           /* out: row P/S of each head                                  */
+  int32_t* res_idx;             /* out: appended rows                                         */
+  void* res_val;
+  uint16_t* res_scale;          /* int4 only                                                  */
+  uint32_t* res_chunk_desc;     /* out: entry P/S of each head                                */
+  uint16_t* win_k;              /* in/out: rows S .. W-1 move to 0 .. W-S-1                   */
+  uint16_t* win_v;              /* in/out: rows 0 .. S-1 are the new chunk's values           */
+} lowram_layer_append;
+
+/*
+ * For each (sequence, KV head): landmark P/S = mean of RoPE(x_t, t) over the S
+ * tokens; R_t = v_t - MLP(C_t B_blk) with v_t the window's rows 0 .. S-1,
+ * evaluated to fp32 accuracy; each token with ||R_t|| >= res_thresh takes the
+ * next free residual row (ascending token order); descriptor P/S written;
+ * window rows S .. W-1 moved to 0 .. W-S-1.  Reads cache->coeff (rows P ..
+ * P+S-1 included), coeff_scale, basis and the MLP.
+ */
+int lowram_append_layer(const lowram_shape* shape, int32_t group_layers, int32_t layer_in_group,
+                        const lowram_layer_cache* cache, const lowram_layer_append* io, void* stream);
 #ifdef __cplusplus
 }
 #endif

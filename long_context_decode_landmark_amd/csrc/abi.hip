@@ -46,10 +46,17 @@ int check_shape(const lowram_shape* s) {
   if (s->n_heads_q / s->n_heads_kv > 16) return LOWRAM_ERR_UNSUPPORTED;
   if (s->rank != 64 && s->rank != 128 && s->rank != 256 && s->rank != 512) return LOWRAM_ERR_UNSUPPORTED;
   if (s->coeff_fmt == LOWRAM_FMT_INT4_G32 && s->rank % 128) return LOWRAM_ERR_UNSUPPORTED;
+  if (s->prefix_cap < 0 || s->window_cap < 0) return LOWRAM_ERR_SHAPE;
+  if (s->prefix_cap && (s->prefix_cap < s->prefix_len || s->prefix_cap % s->chunk)) return LOWRAM_ERR_SHAPE;
+  if (s->window_cap && s->window_cap < s->window) return LOWRAM_ERR_SHAPE;
   // 32-bit index arithmetic inside the kernels
-  if ((int64_t)s->batch * s->prefix_len >= (int64_t)1 << 31) return LOWRAM_ERR_UNSUPPORTED;
+  if ((int64_t)s->batch * (s->prefix_cap ? s->prefix_cap : s->prefix_len) >= (int64_t)1 << 31)
+    return LOWRAM_ERR_UNSUPPORTED;
   return LOWRAM_OK;
 }
+
+int prefix_rows(const lowram_shape* s) { return s->prefix_cap ? s->prefix_cap : s->prefix_len; }
+int window_rows(const lowram_shape* s) { return s->window_cap ? s->window_cap : s->window; }
 
 Plan make_plan(const lowram_shape* s) {
   Plan p{};
@@ -86,6 +93,7 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
     if (ci4 && !c->coeff_scale) return LOWRAM_ERR_NULL;
     if (ri4 && s->n_resid > 0 && !c->res_scale) return LOWRAM_ERR_NULL;
     if (!c->cand_ids && p.n_cand != p.n_chunks) return LOWRAM_ERR_SHAPE;
+    if (c->cand_ids && (s->prefix_cap || s->window_cap)) return LOWRAM_ERR_SHAPE;  // eviction: dense only
   }
   if (s->window > 0 && (!c->win_k || !c->win_v)) return LOWRAM_ERR_NULL;
   const void* bulk[] = {q, out, ws, c->coeff, c->basis, c->landmark, c->w1, c->w2, c->res_val,
@@ -113,7 +121,8 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   if (!mark(0)) return LOWRAM_ERR_HIP;
   if (has_prefix) {
     if (launch_score(q, c->landmark, keys, scores_out, s->batch, p.n_cand, s->n_heads_q,
-                     s->n_heads_kv, hs, shared ? 0 : 1) != hipSuccess)
+                     s->n_heads_kv, hs, shared ? 0 : 1, c->cand_ids ? p.n_cand : prefix_rows(s) / s->chunk) !=
+        hipSuccess)
       return LOWRAM_ERR_HIP;
   }
   if (!mark(1)) return LOWRAM_ERR_HIP;
@@ -134,6 +143,8 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   a.prefix = s->prefix_len; a.window = s->window; a.n_chunks = p.n_chunks; a.k_eff = p.k_eff;
   a.n_resid = s->n_resid;
   a.cache_bmul = shared ? 0 : 1;
+  a.prefix_cap = prefix_rows(s);
+  a.window_cap = window_rows(s);
   a.n_sel_tiles = has_prefix ? p.n_sel_tiles : 0;
   a.n_win_tiles = p.n_win_tiles;
   a.n_split = p.n_split;
@@ -176,8 +187,14 @@ int check_build_shape(const lowram_build_shape* s) {
   if (s->rank != 64 && s->rank != 128 && s->rank != 256 && s->rank != 512) return LOWRAM_ERR_UNSUPPORTED;
   if (s->coeff_fmt == LOWRAM_FMT_INT4_G32 && s->rank % 128) return LOWRAM_ERR_UNSUPPORTED;
   if (s->n_resid >= (1 << 24)) return LOWRAM_ERR_UNSUPPORTED;
+  if (s->prefix_cap < 0 || s->window_cap < 0 || s->resid_cap < 0) return LOWRAM_ERR_SHAPE;
+  if (s->prefix_cap && (s->prefix_cap < P || s->prefix_cap % s->chunk)) return LOWRAM_ERR_SHAPE;
+  if (s->window_cap && s->window_cap < s->window) return LOWRAM_ERR_SHAPE;
+  if (s->resid_cap && s->resid_cap < s->n_resid) return LOWRAM_ERR_SHAPE;
+  if (s->resid_cap >= (1 << 24)) return LOWRAM_ERR_UNSUPPORTED;
   // 32-bit token and element indices inside the kernels
   if ((int64_t)s->batch * s->ctx_len >= (int64_t)1 << 31) return LOWRAM_ERR_UNSUPPORTED;
+  if ((int64_t)s->batch * s->prefix_cap >= (int64_t)1 << 31) return LOWRAM_ERR_UNSUPPORTED;
   if ((int64_t)s->group_layers * s->n_heads_kv * kHeadDim >= (int64_t)1 << 20) return LOWRAM_ERR_UNSUPPORTED;
   return LOWRAM_OK;
 }
@@ -320,7 +337,7 @@ int lowram_build_coeff(const lowram_build_shape* shape, const uint16_t* keys, co
     return LOWRAM_ERR_ALIGN;
   const int D = shape->group_layers * shape->n_heads_kv * kHeadDim;
   if (launch_proj(keys, basis, coeff, coeff_scale, shape->batch, shape->ctx_len, P, D, shape->rank, ci4,
-                  static_cast<hipStream_t>(stream)) != hipSuccess)
+                  static_cast<hipStream_t>(stream), shape->prefix_cap ? shape->prefix_cap : P) != hipSuccess)
     return LOWRAM_ERR_HIP;
   return LOWRAM_OK;
 }
@@ -355,7 +372,8 @@ int run_build_layer(const lowram_build_shape* s, int32_t layer_in_group, const l
                         io->basis, io->landmark, io->res_val, io->win_k, io->win_v};
   for (const void* ptr : bulk)
     if (ptr && misaligned(ptr, 16)) return LOWRAM_ERR_ALIGN;
-  const void* small[] = {io->coeff_scale, io->b1, io->b2, io->res_idx, io->res_scale, io->res_chunk_desc};
+  const void* small[] = {io->coeff_scale, io->b1,      io->b2,         io->res_idx,
+                         io->res_scale,   io->res_chunk_desc, io->res_thresh, io->res_count};
   for (const void* ptr : small)
     if (ptr && misaligned(ptr, 4)) return LOWRAM_ERR_ALIGN;
   if (ws_bytes < p.total) return LOWRAM_ERR_WORKSPACE;
@@ -368,13 +386,23 @@ int run_build_layer(const lowram_build_shape* s, int32_t layer_in_group, const l
   g.nb = s->batch; g.T = s->ctx_len; g.P = p.P; g.W = s->window;
   g.D = s->group_layers * s->n_heads_kv * kHeadDim; g.r = s->rank; g.hkv = s->n_heads_kv;
   g.layer_in_group = layer_in_group; g.n_chunks = p.n_chunks; g.n_resid = s->n_resid;
+  g.prefix_cap = s->prefix_cap ? s->prefix_cap : p.P;
+  g.window_cap = s->window_cap ? s->window_cap : s->window;
+  g.resid_cap = s->resid_cap ? s->resid_cap : s->n_resid;
   for (int i = 0; i < 64; ++i) g.inv_freq[i] = std::pow((double)s->rope_theta, -2.0 * i / (double)kHeadDim);
   if (!mark(0)) return LOWRAM_ERR_HIP;
   if (launch_build_layer_arrays(io->keys, io->values, io->group_basis, io->basis, io->landmark, io->win_k,
                                 io->win_v, g, hs) != hipSuccess)
     return LOWRAM_ERR_HIP;
   if (!mark(1)) return LOWRAM_ERR_HIP;
-  if (p.P == 0) return mark(2) && mark(3) && mark(4) ? LOWRAM_OK : LOWRAM_ERR_HIP;
+  if (p.P == 0) {
+    const int heads0 = s->batch * s->n_heads_kv;
+    if (io->res_thresh && launch_select_split(nullptr, nullptr, heads0, 0, 0, nullptr, hs, 0, io->res_thresh) !=
+                              hipSuccess)
+      return LOWRAM_ERR_HIP;  // threshold +inf: no residuals
+    if (io->res_count && launch_fill_i32(io->res_count, heads0, 0, hs) != hipSuccess) return LOWRAM_ERR_HIP;
+    return mark(2) && mark(3) && mark(4) ? LOWRAM_OK : LOWRAM_ERR_HIP;
+  }
 
   unsigned char* w = static_cast<unsigned char*>(workspace);
   float* r = reinterpret_cast<float*>(w + p.off_r);
@@ -386,17 +414,20 @@ int run_build_layer(const lowram_build_shape* s, int32_t layer_in_group, const l
       return LOWRAM_ERR_HIP;
   }
   if (!mark(2)) return LOWRAM_ERR_HIP;
-  if (s->n_resid > 0) {
-    if (launch_select_split(keys, io->res_idx, (int)heads, p.P, s->n_resid, w + p.off_sel, hs) != hipSuccess)
+  if (s->n_resid > 0 || io->res_thresh) {
+    if (launch_select_split(keys, io->res_idx, (int)heads, p.P, s->n_resid, w + p.off_sel, hs, g.resid_cap,
+                            io->res_thresh) != hipSuccess)
       return LOWRAM_ERR_HIP;
   }
+  if (io->res_count && launch_fill_i32(io->res_count, (int)heads, s->n_resid, hs) != hipSuccess)
+    return LOWRAM_ERR_HIP;
   if (!mark(3)) return LOWRAM_ERR_HIP;
   if (s->n_resid > 0) {
     if (launch_resid_store(r, io->res_idx, io->res_val, io->res_scale, g, ri4, hs) != hipSuccess)
       return LOWRAM_ERR_HIP;
   }
-  if (launch_chunk_desc(io->res_idx, (int)heads, s->n_resid, p.n_chunks, s->chunk, io->res_chunk_desc, hs) !=
-      hipSuccess)
+  if (launch_chunk_desc(io->res_idx, (int)heads, s->n_resid, p.n_chunks, s->chunk, io->res_chunk_desc, hs,
+                        g.resid_cap, g.prefix_cap / s->chunk) != hipSuccess)
     return LOWRAM_ERR_HIP;
   if (!mark(4)) return LOWRAM_ERR_HIP;
   return LOWRAM_OK;
@@ -411,6 +442,75 @@ int lowram_build_layer(const lowram_build_shape* s, int32_t layer_in_group, cons
 int lowram_build_layer_events(const lowram_build_shape* s, int32_t layer_in_group, const lowram_layer_build* io,
                               void* workspace, size_t ws_bytes, void* stream, void* const* events) {
   return run_build_layer(s, layer_in_group, io, workspace, ws_bytes, stream, events);
+}
+
+}  // extern "C"
+
+namespace {
+int check_append(const lowram_shape* s, int32_t group_layers) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (group_layers < 1) return LOWRAM_ERR_SHAPE;
+  if (!s->prefix_cap || s->prefix_len + s->chunk > s->prefix_cap) return LOWRAM_ERR_SHAPE;  // no room
+  if (s->window < s->chunk) return LOWRAM_ERR_SHAPE;
+  if (s->n_cand != s->prefix_len / s->chunk) return LOWRAM_ERR_SHAPE;  // no eviction
+  if ((int64_t)group_layers * s->n_heads_kv * kHeadDim >= (int64_t)1 << 20) return LOWRAM_ERR_UNSUPPORTED;
+  return LOWRAM_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int lowram_append_coeff(const lowram_shape* shape, int32_t group_layers, const uint16_t* keys_new,
+                        const uint16_t* basis, void* coeff, uint16_t* coeff_scale, void* stream) {
+  int st = check_append(shape, group_layers);
+  if (st) return st;
+  const bool ci4 = shape->coeff_fmt == LOWRAM_FMT_INT4_G32;
+  if (!keys_new || !basis || !coeff || (ci4 && !coeff_scale)) return LOWRAM_ERR_NULL;
+  if (misaligned(keys_new, 16) || misaligned(basis, 16) || misaligned(coeff, 16) ||
+      (coeff_scale && misaligned(coeff_scale, 4)))
+    return LOWRAM_ERR_ALIGN;
+  const int D = group_layers * shape->n_heads_kv * kHeadDim;
+  if (launch_proj(keys_new, basis, coeff, coeff_scale, shape->batch, shape->chunk, shape->chunk, D, shape->rank,
+                  ci4, static_cast<hipStream_t>(stream), shape->prefix_cap, shape->prefix_len) != hipSuccess)
+    return LOWRAM_ERR_HIP;
+  return LOWRAM_OK;
+}
+
+int lowram_append_layer(const lowram_shape* shape, int32_t group_layers, int32_t layer_in_group,
+                        const lowram_layer_cache* cache, const lowram_layer_append* io, void* stream) {
+  int st = check_append(shape, group_layers);
+  if (st) return st;
+  if (layer_in_group < 0 || layer_in_group >= group_layers) return LOWRAM_ERR_SHAPE;
+  if (!cache || !io) return LOWRAM_ERR_NULL;
+  const bool ci4 = shape->coeff_fmt == LOWRAM_FMT_INT4_G32, ri4 = shape->resid_fmt == LOWRAM_FMT_INT4_G32;
+  if (!cache->coeff || !cache->basis || !cache->w1 || !cache->b1 || !cache->w2 || !cache->b2 || !io->keys_new ||
+      !io->res_thresh || !io->res_count || !io->res_dropped || !io->landmark || !io->res_chunk_desc ||
+      !io->win_k || !io->win_v)
+    return LOWRAM_ERR_NULL;
+  if (ci4 && !cache->coeff_scale) return LOWRAM_ERR_NULL;
+  if (shape->n_resid > 0 && (!io->res_idx || !io->res_val || (ri4 && !io->res_scale))) return LOWRAM_ERR_NULL;
+  const void* bulk[] = {cache->coeff, cache->basis, cache->w1, cache->w2, io->keys_new, io->landmark, io->res_val,
+                        io->win_k, io->win_v};
+  for (const void* ptr : bulk)
+    if (ptr && misaligned(ptr, 16)) return LOWRAM_ERR_ALIGN;
+  const void* small[] = {cache->coeff_scale, cache->b1, cache->b2, io->res_thresh, io->res_count, io->res_dropped,
+                         io->res_idx, io->res_scale, io->res_chunk_desc};
+  for (const void* ptr : small)
+    if (ptr && misaligned(ptr, 4)) return LOWRAM_ERR_ALIGN;
+  AppendArgs a{};
+  a.keys_new = io->keys_new; a.coeff = cache->coeff; a.coeff_scale = cache->coeff_scale; a.blk = cache->basis;
+  a.w1 = cache->w1; a.b1 = cache->b1; a.w2 = cache->w2; a.b2 = cache->b2; a.thresh = io->res_thresh;
+  a.landmark = io->landmark; a.res_idx = io->res_idx; a.res_val = io->res_val; a.res_scale = io->res_scale;
+  a.desc = io->res_chunk_desc; a.count = io->res_count; a.dropped = io->res_dropped;
+  a.win_k = io->win_k; a.win_v = io->win_v;
+  a.D = group_layers * shape->n_heads_kv * kHeadDim; a.r = shape->rank; a.hkv = shape->n_heads_kv;
+  a.layer_in_group = layer_in_group; a.P = shape->prefix_len; a.W = shape->window;
+  a.prefix_cap = shape->prefix_cap; a.window_cap = window_rows(shape); a.resid_cap = shape->n_resid;
+  a.ci4 = ci4; a.ri4 = ri4;
+  for (int i = 0; i < 64; ++i) a.inv_freq[i] = std::pow((double)shape->rope_theta, -2.0 * i / (double)kHeadDim);
+  if (launch_append(a, shape->batch, static_cast<hipStream_t>(stream)) != hipSuccess) return LOWRAM_ERR_HIP;
+  return LOWRAM_OK;
 }
 
 }  // extern "C"

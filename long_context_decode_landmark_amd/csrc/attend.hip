@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     float csc[CI4 ? NR : 1][NT];
     auto gather = [&](int s) {
       if constexpr (!CI4) {
-        const uint16_t* cb = static_cast<const uint16_t*>(a.coeff) + (size_t)cseq * a.prefix * RANK;
+        const uint16_t* cb = static_cast<const uint16_t*>(a.coeff) + (size_t)cseq * a.prefix_cap * RANK;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -251,8 +251,8 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
             cv[s][ks][nt] = load_bf16x8(cb + (size_t)tok[nt] * RANK + 64 * s + 32 * ks + 8 * grp);
       } else {
         // 16 codes r = 64 s + 16 grp .. + 15 and their group scale
-        const uint8_t* cb = static_cast<const uint8_t*>(a.coeff) + (size_t)cseq * a.prefix * (RANK / 2);
-        const uint16_t* sb = a.coeff_scale + (size_t)cseq * a.prefix * (RANK / 32);
+        const uint8_t* cb = static_cast<const uint8_t*>(a.coeff) + (size_t)cseq * a.prefix_cap * (RANK / 2);
+        const uint16_t* sb = a.coeff_scale + (size_t)cseq * a.prefix_cap * (RANK / 32);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           cq[s][nt] = *reinterpret_cast<const u32x2*>(cb + (size_t)tok[nt] * (RANK / 2) + 32 * s + 8 * grp);
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) asm volatile("" ::"v"(tok[nt]) : "memory");
     uint32_t rd = 0;
-    if (tid < kAttChunksWG) rd = a.res_desc[chead * (size_t)a.n_chunks + rd_chunk];
+    if (tid < kAttChunksWG) rd = a.res_desc[chead * (size_t)(a.prefix_cap / kChunk) + rd_chunk];
 #pragma unroll
     for (int s = 0; s < LG && s < NR; ++s) gather(s);
     __builtin_amdgcn_sched_barrier(0);
@@ -659,8 +659,8 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
     // ========================================================= exact window
     const int w0 = (split - a.n_sel_tiles) * kAttTokWG + wave * kAttTokWave;
     const int nvalid = max(0, min(kAttTokWave, a.window - w0));
-    const uint16_t* kw = a.win_k + chead * (size_t)a.window * kHeadDim;
-    const uint16_t* vw = a.win_v + chead * (size_t)a.window * kHeadDim;
+    const uint16_t* kw = a.win_k + chead * (size_t)a.window_cap * kHeadDim;
+    const uint16_t* vw = a.win_v + chead * (size_t)a.window_cap * kHeadDim;
     bf16x8 qn[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)

@@ -89,6 +89,7 @@ struct ProjArgs {
   void* coeff;            // bf16 [NB][P][r] or int4 [NB][P][r/2]
   uint16_t* scale;        // int4: [NB][P][r/32]
   int T, P, D, r, n_tb, n_rb, total, padded_total;
+  int out_rows, row0;  // output row of (b, t): b * out_rows + row0 + t
   bool int4;
 };
 
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const ProjArgs a) {
     const int tl = gi / GPT, j = gi % GPT;
     const int t = t0 + tl;
     if (t >= a.P) continue;
-    const size_t row = (size_t)b * a.P + t;
+    const size_t row = (size_t)b * a.out_rows + a.row0 + t;
     const int m = m0 + 32 * j;
     if (a.int4)
       encode_group32(tile + tl * L::kTileStride + 32 * j, true, nullptr,
@@ -195,11 +196,13 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const ProjArgs a) {
 }
 
 hipError_t launch_proj(const uint16_t* keys, const uint16_t* basis, void* coeff, uint16_t* scale, int nb, int T,
-                       int P, int D, int r, bool int4, hipStream_t st) {
+                       int P, int D, int r, bool int4, hipStream_t st, int out_rows, int row0) {
   if (P == 0) return hipSuccess;
   ProjArgs a{};
   a.keys = keys; a.basis = basis; a.coeff = coeff; a.scale = scale;
   a.T = T; a.P = P; a.D = D; a.r = r; a.int4 = int4;
+  a.out_rows = out_rows < 0 ? P : out_rows;
+  a.row0 = row0;
   const int tn = r >= 128 ? 128 : 64;
   a.n_tb = (P + kProjTM - 1) / kProjTM;
   a.n_rb = r / tn;
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(256) void landmark_kernel(const uint16_t* __restric
     y1 += x1 * cs.x - x2 * cs.y;
     y2 += x2 * cs.x + x1 * cs.y;
   }
-  uint16_t* o = lm + (((size_t)b * g.hkv + h) * g.n_chunks + c) * kHeadDim;
+  uint16_t* o = lm + (((size_t)b * g.hkv + h) * (g.prefix_cap / kChunk) + c) * kHeadDim;
   o[p] = __builtin_bit_cast(uint16_t, (__bf16)(y1 * (1.0f / kChunk)));
   o[p + 64] = __builtin_bit_cast(uint16_t, (__bf16)(y2 * (1.0f / kChunk)));
 }
@@ -270,11 +273,11 @@ __global__ __launch_bounds__(256) void window_kernel(const uint16_t* __restrict_
   const float x1 = bf16_to_f32(xr[p]);
   const float x2 = bf16_to_f32(xr[p + 64]);
   const float2 cs = rot_of((double)t * g.inv_freq[p]);
-  uint16_t* ko = wk + (head * g.W + w) * kHeadDim;
+  uint16_t* ko = wk + (head * g.window_cap + w) * kHeadDim;
   ko[p] = __builtin_bit_cast(uint16_t, (__bf16)(x1 * cs.x - x2 * cs.y));
   ko[p + 64] = __builtin_bit_cast(uint16_t, (__bf16)(x2 * cs.x + x1 * cs.y));
   const uint16_t* vi = values + (head * g.T + t) * kHeadDim;
-  uint16_t* vo = wv + (head * g.W + w) * kHeadDim;
+  uint16_t* vo = wv + (head * g.window_cap + w) * kHeadDim;
   vo[p] = vi[p];
   vo[p + 64] = vi[p + 64];
 }
@@ -336,6 +339,7 @@ struct PredictArgs {
   float* r;                     // out [NB][Hkv][P][d]
   uint32_t* keys;               // out [NB][Hkv][P]
   int T, P, hkv, n_tb, total, padded_total;
+  int coeff_rows;               // coefficient rows per sequence
 };
 
 constexpr int kPredTokWG = 128;   // 4 waves x 32 tokens
@@ -431,7 +435,7 @@ __global__ __launch_bounds__(256, LOWRAM_PRED_WG_PER_CU) void predict_resid_kern
     for (int kl = 0; kl < 2; ++kl)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const size_t row = (size_t)b * a.P + tok[tt];
+        const size_t row = (size_t)b * a.coeff_rows + tok[tt];
         const int ks = 2 * s + kl;
         if constexpr (!CI4) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.coeff) + row * RANK +
@@ -603,9 +607,10 @@ __global__ __launch_bounds__(256) void resid_store_kernel(const float* __restric
                                                           size_t n_rows, const BuildGeo g, bool int4) {
   const size_t gi = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (gi >= n_rows * 4) return;
-  const size_t row = gi >> 2;  // (b * Hkv + h) * nR + i
+  const size_t sel_row = gi >> 2;  // (b * Hkv + h) * nR + i
   const int j = (int)(gi & 3);
-  const size_t head = row / (size_t)g.n_resid;
+  const size_t head = sel_row / (size_t)g.n_resid;
+  const size_t row = head * g.resid_cap + sel_row % (size_t)g.n_resid;  // stored row
   const int t = idx[row];
   const float* src = r + (head * g.P + t) * kHeadDim + 32 * j;
   if (int4)
@@ -641,6 +646,7 @@ hipError_t launch_predict_resid(const void* coeff, const uint16_t* coeff_scale, 
   a.coeff = coeff; a.coeff_scale = coeff_scale; a.blk = blk;
   a.w1 = w1; a.b1 = b1; a.w2 = w2; a.b2 = b2; a.values = values; a.r = r; a.keys = keys;
   a.T = g.T; a.P = g.P; a.hkv = g.hkv;
+  a.coeff_rows = g.prefix_cap;
   a.n_tb = (g.P + kPredTokWG - 1) / kPredTokWG;
   a.total = g.nb * g.hkv * a.n_tb;
   a.padded_total = (a.total + 7) & ~7;
@@ -654,6 +660,191 @@ hipError_t launch_predict_resid(const void* coeff, const uint16_t* coeff_scale, 
     case 512: launch_predict_rank<512>(a, ci4, st); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Window rollover: the oldest S window tokens (positions P .. P+S-1) become
+// prefix chunk P / S.  One workgroup per (sequence, KV head):
+//   landmark   mean of RoPE(x_t, t) over the S tokens (x: pre-RoPE keys)
+//   residuals  R_t = v_t - MLP(C_t B_blk) in fp32 (the coefficient rows of the
+//              S tokens are already in the cache); every token with
+//              ||R_t|| >= the head's threshold gets the next residual row,
+//              while rows remain (otherwise it is counted as dropped)
+//   descriptor (first new row << 8) | mask of the kept tokens
+//   window     rows S .. W-1 move to 0 .. W-S-1 (k and v)
+// ---------------------------------------------------------------------------
+
+
+__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
+  __shared__ float cs[kChunk][512];          // coefficient rows (decoded)
+  __shared__ float kp[kChunk][kHeadDim];     // rebuilt pre-RoPE keys
+  __shared__ float hid[kChunk][kHidden];     // GELU activations
+  __shared__ float res[kChunk][kHeadDim];    // residual rows
+  __shared__ float err2[kChunk];
+  __shared__ int rowmap[kChunk];
+  const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
+  const size_t head = (size_t)b * a.hkv + h;
+  const int r = a.r;
+
+  // coefficient rows of the S tokens
+  for (int idx = tid; idx < kChunk * r; idx += 256) {
+    const int i = idx / r, m = idx % r;
+    const size_t row = (size_t)b * a.prefix_cap + a.P + i;
+    float c;
+    if (!a.ci4) {
+      c = bf16_to_f32(static_cast<const uint16_t*>(a.coeff)[row * r + m]);
+    } else {
+      const uint8_t byte = static_cast<const uint8_t*>(a.coeff)[row * (r / 2) + m / 2];
+      const int code = ((int)((uint32_t)byte << (28 - 4 * (m & 1)) ) ) >> 28;
+      c = (float)code * f16_to_f32(a.coeff_scale[row * (r / 32) + m / 32]);
+    }
+    cs[i][m] = c;
+  }
+  __syncthreads();
+  // K_pre[i][d] = sum_m C[i][m] blk[d][m]: thread -> d = tid % 128, tokens 4 (tid / 128) .. + 3
+  {
+    const int d = tid & 127, i0 = 4 * (tid >> 7);
+    const uint16_t* br = a.blk + (head * kHeadDim + d) * r;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < r; ++m) {
+      const float bv = bf16_to_f32(br[m]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(cs[i0 + e][m], bv, acc[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kp[i0 + e][d] = acc[e];
+  }
+  __syncthreads();
+  // hidden unit j = tid: z = W1[j] . K_pre + b1[j], h = x Phi(x) (erf form)
+  {
+    const int j = tid;
+    const uint16_t* wr = a.w1 + (head * kHidden + j) * kHeadDim;
+    float acc[kChunk];
+    const float bias = bf16_to_f32(a.b1[head * kHidden + j]);
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) acc[i] = bias;
+    for (int d = 0; d < kHeadDim; ++d) {
+      const float wv = bf16_to_f32(wr[d]);
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) acc[i] = fmaf(wv, kp[i][d], acc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) hid[i][j] = 0.5f * acc[i] * (1.0f + erff(acc[i] * 0.70710678118654752f));
+  }
+  __syncthreads();
+  // V~[i][d] = W2[d] . h[i] + b2[d]; R = v - V~  (v: window rows 0 .. S-1)
+  {
+    const int d = tid & 127, i0 = 4 * (tid >> 7);
+    const uint16_t* wr = a.w2 + (head * kHeadDim + d) * kHidden;
+    const float bias = bf16_to_f32(a.b2[head * kHeadDim + d]);
+    float acc[4] = {bias, bias, bias, bias};
+    for (int j = 0; j < kHidden; ++j) {
+      const float wv = bf16_to_f32(wr[j]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(wv, hid[i0 + e][j], acc[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = bf16_to_f32(a.win_v[(head * a.window_cap + i0 + e) * kHeadDim + d]);
+      res[i0 + e][d] = v - acc[e];
+    }
+  }
+  __syncthreads();
+  // ||R_i||^2: token i = tid / 32, 4 dims per lane, 32-lane reduction
+  {
+    const int i = tid >> 5, l = tid & 31;
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ss = fmaf(res[i][l + 32 * k], res[i][l + 32 * k], ss);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if (l == 0) err2[i] = ss;
+  }
+  __syncthreads();
+  const int nc = a.P / kChunk;
+  if (tid == 0) {
+    const float tau = a.thresh[head];
+    int cnt = a.count[head], drop = 0;
+    const int first = cnt;
+    uint32_t mask = 0;
+    for (int i = 0; i < kChunk; ++i) {
+      rowmap[i] = -1;
+      if (sqrtf(err2[i]) >= tau) {
+        if (cnt < a.resid_cap) {
+          rowmap[i] = cnt;
+          a.res_idx[head * a.resid_cap + cnt] = a.P + i;
+          mask |= 1u << i;
+          ++cnt;
+        } else {
+          ++drop;
+        }
+      }
+    }
+    a.desc[head * (a.prefix_cap / kChunk) + nc] = ((uint32_t)first << 8) | mask;
+    a.count[head] = cnt;
+    a.dropped[head] += drop;
+  }
+  // landmark: thread p < 64 owns the rotate-half pair (p, p + 64)
+  if (tid < 64) {
+    const int p = tid;
+    const uint16_t* xs = a.keys_new + (size_t)b * kChunk * a.D + (a.layer_in_group * a.hkv + h) * kHeadDim;
+    float y1 = 0.f, y2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const float x1 = bf16_to_f32(xs[(size_t)i * a.D + p]);
+      const float x2 = bf16_to_f32(xs[(size_t)i * a.D + p + 64]);
+      const float2 cs2 = rot_of((double)(a.P + i) * a.inv_freq[p]);
+      y1 += x1 * cs2.x - x2 * cs2.y;
+      y2 += x2 * cs2.x + x1 * cs2.y;
+    }
+    uint16_t* o = a.landmark + (head * (a.prefix_cap / kChunk) + nc) * kHeadDim;
+    o[p] = __builtin_bit_cast(uint16_t, (__bf16)(y1 * (1.0f / kChunk)));
+    o[p + 64] = __builtin_bit_cast(uint16_t, (__bf16)(y2 * (1.0f / kChunk)));
+  }
+  __syncthreads();
+  // residual rows of the kept tokens: thread -> (token tid / 4, group tid % 4)
+  if (tid < kChunk * 4) {
+    const int i = tid >> 2, j = tid & 3;
+    const int row = rowmap[i];
+    if (row >= 0) {
+      const size_t orow = head * a.resid_cap + row;
+      if (a.ri4)
+        encode_group32(&res[i][32 * j], true, nullptr,
+                       static_cast<uint8_t*>(a.res_val) + orow * (kHeadDim / 2) + 16 * j,
+                       a.res_scale + orow * (kHeadDim / 32) + j);
+      else
+        encode_group32(&res[i][32 * j], false, static_cast<uint16_t*>(a.res_val) + orow * kHeadDim + 32 * j,
+                       nullptr, nullptr);
+    }
+  }
+  // window rows S .. W-1 -> 0 .. W-S-1, 16 rows per pass (read all, then write)
+  for (int arr = 0; arr < 2; ++arr) {
+    uint16_t* wb = (arr == 0 ? a.win_k : a.win_v) + head * a.window_cap * kHeadDim;
+    for (int r0 = 0; r0 < a.W - kChunk; r0 += 16) {
+      const int row = r0 + (tid >> 4), piece = tid & 15;
+      const bool live = row < a.W - kChunk;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (live) v = *reinterpret_cast<const u32x4*>(wb + (size_t)(row + kChunk) * kHeadDim + 8 * piece);
+      __syncthreads();
+      if (live) *reinterpret_cast<u32x4*>(wb + (size_t)row * kHeadDim + 8 * piece) = v;
+      __syncthreads();
+    }
+  }
+}
+
+hipError_t launch_append(const AppendArgs& a, int nb, hipStream_t st) {
+  hipLaunchKernelGGL(append_kernel, dim3(a.hkv, nb), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int n, int32_t v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st) {
+  if (n > 0) hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n, v);
   return hipGetLastError();
 }
 

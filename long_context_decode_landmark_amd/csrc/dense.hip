@@ -146,11 +146,12 @@ hipError_t launch_dense(const uint16_t* k, const uint16_t* v, const uint16_t* q,
 // chunk's tokens present in res_idx[l]
 __global__ __launch_bounds__(256) void chunk_desc_kernel(const int32_t* __restrict__ idx, int n_resid,
                                                          int n_chunks, int chunk,
-                                                         uint32_t* __restrict__ desc) {
+                                                         uint32_t* __restrict__ desc, int idx_stride,
+                                                         int desc_stride) {
   const int l = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= n_chunks) return;
-  const int32_t* r = idx + (size_t)l * n_resid;
+  const int32_t* r = idx + (size_t)l * idx_stride;
   const int key = c * chunk;
   int lo = 0, hi = n_resid;
   while (lo < hi) {
@@ -160,13 +161,14 @@ __global__ __launch_bounds__(256) void chunk_desc_kernel(const int32_t* __restri
   }
   uint32_t mask = 0;
   for (int i = lo; i < n_resid && r[i] < key + chunk; ++i) mask |= 1u << (r[i] - key);
-  desc[(size_t)l * n_chunks + c] = ((uint32_t)lo << 8) | mask;
+  desc[(size_t)l * desc_stride + c] = ((uint32_t)lo << 8) | mask;
 }
 
 hipError_t launch_chunk_desc(const int32_t* res_idx, int n_lists, int n_resid, int n_chunks, int chunk,
-                             uint32_t* desc, hipStream_t st) {
+                             uint32_t* desc, hipStream_t st, int idx_stride, int desc_stride) {
   const dim3 grid((n_chunks + 255) / 256, n_lists);
-  hipLaunchKernelGGL(chunk_desc_kernel, grid, dim3(256), 0, st, res_idx, n_resid, n_chunks, chunk, desc);
+  hipLaunchKernelGGL(chunk_desc_kernel, grid, dim3(256), 0, st, res_idx, n_resid, n_chunks, chunk, desc,
+                     idx_stride < 0 ? n_resid : idx_stride, desc_stride < 0 ? n_chunks : desc_stride);
   return hipGetLastError();
 }
 

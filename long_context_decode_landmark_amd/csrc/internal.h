@@ -41,15 +41,18 @@ struct AttendArgs {
   float* vhat_out;
   int nb, hq, hkv, g, prefix, window, n_chunks, k_eff, n_resid;
   int cache_bmul;  // 1: cache arrays per sequence; 0: one context shared by all nb queries
+  int prefix_cap;  // coefficient rows per sequence (descriptor rows per head = prefix_cap / S)
+  int window_cap;  // window rows per head
   int n_sel_tiles, n_win_tiles, n_split, total, padded_total;
   float scale_log2;
   double inv_freq[64];
 };
 
 // cache_bmul: 1 = landmarks / candidate ids per sequence, 0 = one shared context
+// lm_rows: landmark rows per (sequence, KV head) (>= n_cand)
 hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* keys,
                         float* scores_out, int nb, int n_cand, int hq, int hkv, hipStream_t st,
-                        int cache_bmul = 1);
+                        int cache_bmul = 1, int lm_rows = -1);
 hipError_t launch_select(const uint32_t* keys, const int32_t* cand_ids, int32_t* sel,
                          int32_t* sel_out, int nb, int n_cand, int k, int hkv, hipStream_t st,
                          int cache_bmul = 1);
@@ -60,23 +63,27 @@ hipError_t launch_attend(const AttendArgs& a, int rank, bool coeff_int4, bool re
 // ws of split_select_ws_bytes bytes.
 size_t split_select_ws_bytes(int n_lists, int n);
 hipError_t launch_select_split(const uint32_t* keys, int32_t* sel, int n_lists, int n, int k, void* ws,
-                               hipStream_t st);
+                               hipStream_t st, int sel_stride = -1, float* thresh = nullptr);
 hipError_t launch_merge(const float* part, uint16_t* out, int nb, int hkv, int g, int n_split,
                         hipStream_t st);
 hipError_t launch_dense(const uint16_t* k, const uint16_t* v, const uint16_t* q, float* part,
                         int nb, int ctx, int hq, int hkv, int n_split, int tok_per_split,
                         float scale_log2, hipStream_t st);
 hipError_t launch_chunk_desc(const int32_t* res_idx, int n_lists, int n_resid, int n_chunks,
-                             int chunk, uint32_t* desc, hipStream_t st);
+                             int chunk, uint32_t* desc, hipStream_t st, int idx_stride = -1,
+                             int desc_stride = -1);
 
 // Cache builder.
 struct BuildGeo {
   int nb, T, P, W, D, r, hkv, layer_in_group, n_chunks, n_resid;
+  int prefix_cap, window_cap, resid_cap;  // output strides (coefficient rows, window rows, residual rows)
   double inv_freq[64];
 };
 
+// coefficient rows of token t of sequence b go to row b * out_rows + row0 + t
 hipError_t launch_proj(const uint16_t* keys, const uint16_t* basis, void* coeff, uint16_t* scale, int nb,
-                       int T, int P, int D, int r, bool int4, hipStream_t st);
+                       int T, int P, int D, int r, bool int4, hipStream_t st, int out_rows = -1,
+                       int row0 = 0);
 hipError_t launch_build_layer_arrays(const uint16_t* keys, const uint16_t* values, const uint16_t* basis,
                                      uint16_t* blk, uint16_t* lm, uint16_t* wk, uint16_t* wv,
                                      const BuildGeo& g, hipStream_t st);
@@ -84,6 +91,28 @@ hipError_t launch_predict_resid(const void* coeff, const uint16_t* coeff_scale, 
                                 const uint16_t* w1, const uint16_t* b1, const uint16_t* w2, const uint16_t* b2,
                                 const uint16_t* values, float* r, uint32_t* keys, bool ci4, const BuildGeo& g,
                                 hipStream_t st);
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
+struct AppendArgs {
+  const uint16_t* keys_new;     // [NB][S][D] pre-RoPE keys of the S tokens
+  const void* coeff;            // group coefficients, rows b * prefix_cap + t
+  const uint16_t* coeff_scale;
+  const uint16_t* blk;          // [NB][Hkv][d][r]
+  const uint16_t *w1, *b1, *w2, *b2;
+  const float* thresh;          // [NB][Hkv]
+  uint16_t* landmark;           // [NB][Hkv][prefix_cap / S][d]
+  int32_t* res_idx;             // [NB][Hkv][resid_cap]
+  void* res_val;
+  uint16_t* res_scale;
+  uint32_t* desc;               // [NB][Hkv][prefix_cap / S]
+  int32_t* count;               // [NB][Hkv]
+  int32_t* dropped;             // [NB][Hkv]
+  uint16_t* win_k;              // [NB][Hkv][window_cap][d]
+  uint16_t* win_v;
+  int D, r, hkv, layer_in_group, P, W, prefix_cap, window_cap, resid_cap;
+  bool ci4, ri4;
+  double inv_freq[64];
+};
+hipError_t launch_append(const AppendArgs& a, int nb, hipStream_t st);
 hipError_t launch_resid_store(const float* r, const int32_t* idx, void* res_val, uint16_t* res_scale,
                               const BuildGeo& g, bool int4, hipStream_t st);
 

@@ -30,7 +30,7 @@ namespace lowram {
 __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ landmark,
     uint32_t* __restrict__ keys, float* __restrict__ scores_out, int n_cand, int n_heads_q,
-    int n_heads_kv, int chunks_per_wg, int cache_bmul) {
+    int n_heads_kv, int chunks_per_wg, int cache_bmul, int lm_rows) {
   const int b = blockIdx.z, h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, col = lane & 15;
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
     qa[ks] = col < g ? load_bf16x8(qb + col * kHeadDim + 32 * ks + 8 * grp) : zero_bf16x8();
 
   const size_t head = (size_t)b * n_heads_kv + h;
-  const uint16_t* lm = landmark + ((size_t)b * cache_bmul * n_heads_kv + h) * (size_t)n_cand * kHeadDim;
+  const uint16_t* lm = landmark + ((size_t)b * cache_bmul * n_heads_kv + h) * (size_t)lm_rows * kHeadDim;
   uint32_t* kout = keys + head * (size_t)n_cand;
   float* sout = scores_out ? scores_out + head * (size_t)n_cand : nullptr;
   const int c_begin = blockIdx.x * chunks_per_wg;
@@ -98,7 +98,7 @@ template <int G>
 __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_multi_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ landmark,
     uint32_t* __restrict__ keys, float* __restrict__ scores_out, int n_cand, int n_heads_q,
-    int n_heads_kv, int chunks_per_wg, int nq) {
+    int n_heads_kv, int chunks_per_wg, int nq, int lm_rows) {
   constexpr int QG = 16 / G;  // queries per tile
   const int qb = blockIdx.z, h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_multi_kerne
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qa[ks] = aq < nq ? load_bf16x8(qrow + 32 * ks + 8 * grp) : zero_bf16x8();
 
-  const uint16_t* lm = landmark + (size_t)h * n_cand * kHeadDim;
+  const uint16_t* lm = landmark + (size_t)h * lm_rows * kHeadDim;
   const int c_begin = blockIdx.x * chunks_per_wg;
   const int c_end = min(n_cand, c_begin + chunks_per_wg);
   auto load_group = [&](int c0, bf16x8 (&lv)[4][4]) {
@@ -445,13 +445,14 @@ __global__ __launch_bounds__(kSplitThreads) void split_count_kernel(const uint32
 // Ordered compaction of one slice: wave v walks its quarter of the slice 64
 // keys at a time; ballots rank each key among the earlier ones.
 __global__ __launch_bounds__(kSplitThreads) void split_compact_kernel(const uint32_t* __restrict__ keys, SplitWs w,
-                                                                      int32_t* __restrict__ sel, int n, int n_slices) {
+                                                                      int32_t* __restrict__ sel, int n, int n_slices,
+                                                                      int sel_stride) {
   constexpr int kW = kSplitThreads / 64;
   __shared__ uint32_t wsum[2][kW];
   const int l = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t T = w.state[4 * l], need = w.state[4 * l + 2], k = w.state[4 * l + 3];
   const uint32_t* kl = keys + (size_t)l * n;
-  int32_t* so = sel + (size_t)l * k;
+  int32_t* so = sel + (size_t)l * sel_stride;
   uint32_t gt_run = 0, eq_run = 0;
   for (int s2 = 0; s2 < (int)blockIdx.x; ++s2) {
     gt_run += w.counts[((size_t)l * n_slices + s2) * 2 + 0];
@@ -492,15 +493,43 @@ __global__ __launch_bounds__(kSplitThreads) void split_compact_kernel(const uint
   }
 }
 
+// every index when k >= n: sel[l][i] = i
+__global__ __launch_bounds__(kSplitThreads) void split_all_kernel(int32_t* __restrict__ sel, int n, int sel_stride) {
+  const int l = blockIdx.y;
+  const int i = blockIdx.x * kSplitThreads + threadIdx.x;
+  if (i < n) sel[(size_t)l * sel_stride + i] = i;
+}
+
+// The value of the k-th largest key of each list (the selection threshold).
+__global__ void split_thresh_kernel(SplitWs w, float* __restrict__ thresh, int n_lists) {
+  const int l = blockIdx.x * 256 + threadIdx.x;
+  if (l < n_lists) thresh[l] = key_score(w.state[4 * l]);
+}
+
+__global__ void fill_f32_kernel(float* __restrict__ p, float v, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
 size_t split_select_ws_bytes(int n_lists, int n) {
   const int n_slices = (n + kSplitSlice - 1) / kSplitSlice;
   return ((size_t)n_lists * kSelBins + (size_t)n_lists * 4 + (size_t)n_lists * n_slices * 2) * 4;
 }
 
 hipError_t launch_select_split(const uint32_t* keys, int32_t* sel, int n_lists, int n, int k, void* ws,
-                               hipStream_t st) {
-  if (n_lists == 0 || k == 0) return hipSuccess;
-  if (n <= k) return launch_select(keys, nullptr, sel, nullptr, n_lists, n, k, 1, st);  // all selected
+                               hipStream_t st, int sel_stride, float* thresh) {
+  if (n_lists == 0) return hipSuccess;
+  if (sel_stride < 0) sel_stride = k;
+  if (k == 0 || n <= k) {
+    // nothing selected (threshold +inf) or every index (threshold 0: errors are >= 0)
+    if (thresh)
+      hipLaunchKernelGGL(fill_f32_kernel, dim3((n_lists + 255) / 256), dim3(256), 0, st, thresh,
+                         k == 0 ? __builtin_huge_valf() : 0.f, n_lists);
+    if (k > 0 && n > 0)
+      hipLaunchKernelGGL(split_all_kernel, dim3((n + kSplitThreads - 1) / kSplitThreads, n_lists),
+                         dim3(kSplitThreads), 0, st, sel, n, sel_stride);
+    return hipGetLastError();
+  }
   const int n_slices = (n + kSplitSlice - 1) / kSplitSlice;
   SplitWs w;
   w.hist = static_cast<uint32_t*>(ws);
@@ -517,13 +546,16 @@ hipError_t launch_select_split(const uint32_t* keys, int32_t* sel, int n_lists, 
   }
   hipLaunchKernelGGL(split_count_kernel, dim3(n_slices, n_lists), dim3(kSplitThreads), 0, st, keys, w, n, n_slices);
   hipLaunchKernelGGL(split_compact_kernel, dim3(n_slices, n_lists), dim3(kSplitThreads), 0, st, keys, w, sel, n,
-                     n_slices);
+                     n_slices, sel_stride);
+  if (thresh)
+    hipLaunchKernelGGL(split_thresh_kernel, dim3((n_lists + 255) / 256), dim3(256), 0, st, w, thresh, n_lists);
   return hipGetLastError();
 }
 
 hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* keys,
                         float* scores_out, int nb, int n_cand, int hq, int hkv, hipStream_t st,
-                        int cache_bmul) {
+                        int cache_bmul, int lm_rows) {
+  if (lm_rows < 0) lm_rows = n_cand;
   if (n_cand <= 0) return hipSuccess;
   // chunks per workgroup: the smallest power of two >= 256 that keeps the
   // grid within LOWRAM_SCORE_MAX_WG workgroups
@@ -536,14 +568,14 @@ hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* k
   dim3 grid((n_cand + cpw - 1) / cpw, hkv, qblocks);
   if (!multi) {
     hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, st, q, landmark, keys, scores_out,
-                       n_cand, hq, hkv, cpw, cache_bmul);
+                       n_cand, hq, hkv, cpw, cache_bmul, lm_rows);
   } else {
     switch (g) {
-      case 1: hipLaunchKernelGGL(score_multi_kernel<1>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb); break;
-      case 2: hipLaunchKernelGGL(score_multi_kernel<2>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb); break;
-      case 4: hipLaunchKernelGGL(score_multi_kernel<4>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb); break;
-      case 8: hipLaunchKernelGGL(score_multi_kernel<8>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb); break;
-      default: hipLaunchKernelGGL(score_multi_kernel<16>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb); break;
+      case 1: hipLaunchKernelGGL(score_multi_kernel<1>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb, lm_rows); break;
+      case 2: hipLaunchKernelGGL(score_multi_kernel<2>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb, lm_rows); break;
+      case 4: hipLaunchKernelGGL(score_multi_kernel<4>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb, lm_rows); break;
+      case 8: hipLaunchKernelGGL(score_multi_kernel<8>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb, lm_rows); break;
+      default: hipLaunchKernelGGL(score_multi_kernel<16>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb, lm_rows); break;
     }
   }
   return hipGetLastError();

@@ -32,6 +32,8 @@ SYMBOLS = (
     "lowram_build_layer_workspace_bytes",
     "lowram_build_layer",
     "lowram_build_layer_events",
+    "lowram_append_coeff",
+    "lowram_append_layer",
 )
 
 ERRORS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "UNSUPPORTED", -4: "WORKSPACE", -5: "ALIGN", -6: "HIP"}
@@ -41,7 +43,8 @@ class LowramShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "prefix_len", "window", "chunk", "n_heads_q", "n_heads_kv", "head_dim", "rank",
         "mlp_hidden", "topk", "n_resid", "n_cand", "coeff_fmt", "resid_fmt")] + [
-        ("rope_theta", ctypes.c_float), ("softmax_scale", ctypes.c_float)]
+        ("rope_theta", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+        ("prefix_cap", ctypes.c_int32), ("window_cap", ctypes.c_int32)]
 
 
 CACHE_FIELDS = ("coeff", "coeff_scale", "basis", "landmark", "cand_ids", "w1", "b1", "w2", "b2",
@@ -55,15 +58,25 @@ class LowramLayerCache(ctypes.Structure):
 class LowramBuildShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "ctx_len", "window", "chunk", "n_heads_kv", "head_dim", "rank", "group_layers",
-        "mlp_hidden", "n_resid", "coeff_fmt", "resid_fmt")] + [("rope_theta", ctypes.c_float)]
+        "mlp_hidden", "n_resid", "coeff_fmt", "resid_fmt")] + [("rope_theta", ctypes.c_float)] + [
+        (n, ctypes.c_int32) for n in ("prefix_cap", "window_cap", "resid_cap")]
 
 
 BUILD_FIELDS = ("keys", "group_basis", "coeff", "coeff_scale", "values", "w1", "b1", "w2", "b2",
-                "basis", "landmark", "res_idx", "res_val", "res_scale", "res_chunk_desc", "win_k", "win_v")
+                "basis", "landmark", "res_idx", "res_val", "res_scale", "res_chunk_desc", "win_k", "win_v",
+                "res_thresh", "res_count")
 
 
 class LowramLayerBuild(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in BUILD_FIELDS]
+
+
+APPEND_FIELDS = ("keys_new", "res_thresh", "res_count", "res_dropped", "landmark", "res_idx", "res_val",
+                 "res_scale", "res_chunk_desc", "win_k", "win_v")
+
+
+class LowramLayerAppend(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in APPEND_FIELDS]
 
 
 class DenseShape(ctypes.Structure):
@@ -117,6 +130,9 @@ def lib() -> ctypes.CDLL:
         L.lowram_build_layer_events.argtypes = [ctypes.POINTER(LowramBuildShape), ctypes.c_int32,
                                                 ctypes.POINTER(LowramLayerBuild), vp, sz, vp,
                                                 ctypes.POINTER(ctypes.c_void_p)]
+        L.lowram_append_coeff.argtypes = [ctypes.POINTER(LowramShape), ctypes.c_int32, vp, vp, vp, vp, vp]
+        L.lowram_append_layer.argtypes = [ctypes.POINTER(LowramShape), ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.POINTER(LowramLayerCache), ctypes.POINTER(LowramLayerAppend), vp]
         for name in SYMBOLS:
             getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
         L.lowram_strerror.restype = ctypes.c_char_p
@@ -276,3 +292,18 @@ def build_layer(shape, layer_in_group: int, io: dict, workspace, stream=None, ev
     arr = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e.cuda_event) for e in events])
     _check(lib().lowram_build_layer_events(ctypes.byref(shape), layer_in_group, ctypes.byref(b), ws_ptr, ws_n,
                                            _stream(stream), arr), "lowram_build_layer_events")
+
+
+# ----------------------------------------------------------- window rollover --
+def append_coeff(shape, group_layers: int, keys_new, basis, coeff, coeff_scale=None, stream=None) -> None:
+    """lowram_append_coeff: coefficient rows P .. P+S-1 of the group."""
+    _check(lib().lowram_append_coeff(ctypes.byref(shape), group_layers, _ptr(keys_new), _ptr(basis), _ptr(coeff),
+                                     _ptr(coeff_scale), _stream(stream)), "lowram_append_coeff")
+
+
+def append_layer(shape, group_layers: int, layer_in_group: int, cache, io: dict, stream=None) -> None:
+    """lowram_append_layer; io maps the lowram_layer_append field names to device tensors."""
+    c = cache if isinstance(cache, LowramLayerCache) else make_cache(cache)
+    a = LowramLayerAppend(**{n: (io[n].data_ptr() if io.get(n) is not None else None) for n in APPEND_FIELDS})
+    _check(lib().lowram_append_layer(ctypes.byref(shape), group_layers, layer_in_group, ctypes.byref(c),
+                                     ctypes.byref(a), _stream(stream)), "lowram_append_layer")

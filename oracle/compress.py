@@ -64,6 +64,37 @@ def select_worst(err: np.ndarray, n_resid: int) -> np.ndarray:
     return np.sort(order[:n_resid]).astype(np.int32)
 
 
+def residual_threshold(err: np.ndarray, n_resid: int) -> float:
+    """The error a token must reach to be kept: the n_resid-th largest error
+    (0 when every token is kept, +inf when none is)."""
+    err = np.asarray(err, np.float64)
+    if n_resid == 0:
+        return np.inf
+    if n_resid >= len(err):
+        return 0.0
+    return float(np.sort(err)[::-1][n_resid - 1])
+
+
+def append_chunk(x_new: np.ndarray, v_new: np.ndarray, c_new_dec: np.ndarray, blk, w1, b1, w2, b2,
+                 tau: float, pos0: int, theta: float):
+    """Window rollover: the S tokens at positions pos0 .. pos0+S-1 become a prefix chunk.
+
+    x_new: their exact pre-RoPE keys [S][d]; v_new: exact values [S][d];
+    c_new_dec: their coefficients as stored (decoded) [S][r]; blk: basis block
+    [d][r].  Returns the chunk's landmark (mean post-RoPE key, as at build
+    time), the offsets of the tokens whose residual error reaches the
+    build-time threshold tau (the same test the build applied to the prefix:
+    keep a residual when ||R|| is at least the nR-th largest error), their
+    residual rows, and every token's error.
+    """
+    x_new = np.asarray(x_new, np.float64)
+    S = x_new.shape[0]
+    lm = rope(x_new, pos0 + np.arange(S), theta).mean(axis=0)
+    r, err = residuals(v_new, reconstruct(c_new_dec, blk), w1, b1, w2, b2)
+    keep = np.nonzero(err >= tau)[0].astype(np.int32)
+    return dict(landmark=lm, keep=keep, rows=r[keep], errors=err)
+
+
 def residual_select(v_prefix: np.ndarray, k_pre_prefix: np.ndarray, w1, b1, w2, b2, n_resid: int):
     """Indices (ascending) and rows of the n_resid worst-predicted prefix tokens."""
     r, err = residuals(v_prefix, k_pre_prefix, w1, b1, w2, b2)
@@ -130,6 +161,7 @@ def compress_from_kv(cfg, x_head: np.ndarray, v_head: np.ndarray, coeff_stored, 
         win_k=_store(rope(x_head[P:], np.arange(P, P + W), cfg.rope_theta), exact),
         win_v=_store(v[P:], exact),
         errors=err,   # not stored by the cache: every prefix token's ||R||, for near-tie checks
+        res_thresh=residual_threshold(err, cfg.n_resid),
     )
     if cfg.int4 and not exact:
         out["res_val"], out["res_scale"] = codecs.int4_encode(rows)

@@ -26,7 +26,7 @@ def test_library_loads_and_exports_every_symbol():
     L = native.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert native.abi_version() == 1
+    assert native.abi_version() == 2
     assert native.strerror(-4) == "workspace too small"
 
 
@@ -230,3 +230,52 @@ def test_build_coeff_rejects():
         native.build_coeff(bshape(rank=128, coeff_fmt=1), FakeTensor(0x1000), FakeTensor(0x2000),
                            FakeTensor(0x3000), stream=0)
     assert e.value.status == -1                                   # int4 scales missing
+
+
+# ------------------------------------------------------ capacities / rollover --
+@pytest.mark.parametrize("kw,code", [
+    (dict(prefix_cap=4000), -2),        # below prefix_len
+    (dict(prefix_cap=4036), -2),        # not a multiple of S
+    (dict(window_cap=10), -2),          # below window
+    (dict(prefix_cap=-8), -2),
+])
+def test_caps_rejected(kw, code):
+    with pytest.raises(native.LowramError) as e:
+        ws_bytes(**kw)
+    assert e.value.status == code
+
+
+def test_caps_with_eviction_rejected():
+    s = shape(n_cand=200, prefix_cap=4040)
+    c = fake_cache()
+    c["cand_ids"] = FakeTensor(0x7300000000)
+    assert call_step(s, c) == -2
+
+
+def test_append_rejects():
+    s = shape(prefix_cap=4040, n_resid=600)
+    io = {n: FakeTensor(0x7400000000 + 0x100000 * i) for i, n in enumerate(native.APPEND_FIELDS)}
+    def status(fn):
+        with pytest.raises(native.LowramError) as e:
+            fn()
+        return e.value.status
+    assert status(lambda: native.append_layer(s, 2, 0, fake_cache(), dict(io, res_thresh=None), stream=0)) == -1
+    assert status(lambda: native.append_layer(s, 2, 2, fake_cache(), io, stream=0)) == -2       # layer >= G
+    assert status(lambda: native.append_layer(shape(prefix_cap=4032, n_resid=600), 2, 0, fake_cache(), io,
+                                              stream=0)) == -2                                   # no room
+    assert status(lambda: native.append_layer(shape(prefix_cap=0), 2, 0, fake_cache(), io, stream=0)) == -2
+    assert status(lambda: native.append_layer(shape(prefix_cap=4040, window=4, prefix_len=4032), 2, 0,
+                                              fake_cache(), io, stream=0)) == -2                 # window < S
+    assert status(lambda: native.append_coeff(s, 2, FakeTensor(0x1008), FakeTensor(0x2000), FakeTensor(0x3000),
+                                              stream=0)) == -5
+    assert status(lambda: native.append_coeff(s, 0, FakeTensor(0x1000), FakeTensor(0x2000), FakeTensor(0x3000),
+                                              stream=0)) == -2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(prefix_cap=4000), -2), (dict(window_cap=10), -2), (dict(resid_cap=100), -2),
+])
+def test_build_caps_rejected(kw, code):
+    with pytest.raises(native.LowramError) as e:
+        native.build_layer_workspace_bytes(bshape(**kw))
+    assert e.value.status == code

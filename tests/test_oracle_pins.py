@@ -376,3 +376,33 @@ def test_int4_eviction_cache_decodes():
     assert np.all(np.isfinite(out))
     for h in range(cfg.n_heads_kv):
         assert np.all(np.isin(st_[(0, h)]["sel"], cache["cand_ids"][0, h]))
+
+
+def test_append_chunk_matches_a_longer_build():
+    """Rolling the first window chunk into the prefix gives that chunk the
+    landmark a build over the longer prefix gives it, and residuals exactly
+    for the tokens whose error reaches the build threshold (brute force)."""
+    cfg = synth.C0.with_(name="roll", ctx=512, window=64, resid_frac=0.125, bias_std=0.1)
+    longer = cfg.with_(name="roll2", window=56)
+    P, layer, h = cfg.prefix, 1, 0
+    x = synth.exact_keys(cfg, 0, 0)
+    B = synth.basis(cfg, 0, 0)
+    cols = synth.layer_cols(cfg, layer, h)
+    w = synth.mlp_weights(cfg.with_(bias_std=0.1), 0, layer, h)
+    v = compress.exact_values(x[:, cols], *w, synth.value_noise(cfg, 0, layer, h), *synth.value_spikes(cfg, 0, layer, h))
+    blk = compress.basis_block(B, cols)
+    c = compress.project(x, B)
+    base = compress.compress_from_kv(cfg, x[:, cols], v, c[:P], blk, w, exact=True)
+    big = compress.compress_from_kv(longer, x[:, cols], v, c[:P + 8], blk, w, exact=True)
+    app = compress.append_chunk(x[P:P + 8, cols], v[P:P + 8], c[P:P + 8], blk, *w, base["res_thresh"], P,
+                                cfg.rope_theta)
+    assert np.allclose(app["landmark"], big["landmark"][-1], atol=1e-12)
+    assert np.allclose(app["landmark"], complex_rope(x[P:P + 8, cols], np.arange(P, P + 8), cfg.rope_theta).mean(0),
+                       atol=1e-12)
+    # brute force: the error of each new token against the build threshold
+    pred = steps.value_mlp((c[P:P + 8] @ B)[:, cols], *w)
+    errs = [float(np.linalg.norm(v[P + i] - pred[i])) for i in range(8)]
+    assert list(app["keep"]) == [i for i in range(8) if errs[i] >= base["res_thresh"]]
+    assert np.allclose(app["rows"], (v[P:P + 8] - pred)[app["keep"]], atol=1e-10)
+    # the threshold is the nR-th largest prefix error
+    assert np.sum(base["errors"] >= base["res_thresh"]) == cfg.n_resid
