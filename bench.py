@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--shared", type=int, default=0, metavar="Q",
                     help="time Q queries over one shared context (shared-prefix multi-query decode)")
+    ap.add_argument("--append", action="store_true",
+                    help="time the window rollover (one chunk into the prefix) for one layer group")
     ap.add_argument("--build", action="store_true",
                     help="time the cache builder (one layer group of one sequence) instead of the decode step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -467,6 +469,108 @@ def bench_build(args):
     print(json.dumps(res))
 
 
+def bench_append(args):
+    """Window rollover at 262K, batch 28: one step moves the oldest 8 window
+    tokens of every sequence into the prefix, for the G layers of one group
+    (lowram_append_coeff once, lowram_append_layer per layer).  Every token is
+    given a residual (threshold 0), the most work the step can do."""
+    import torch
+    import synth
+    from long_context_decode_landmark_amd import native
+    from synth import device as sd
+    cfg = synth.CONFIGS[args.config]
+    nb = args.batch or cfg.batch
+    dev = torch.device("cuda:0")
+    G, Hkv, d, r, P, W, S = cfg.group_layers, cfg.n_heads_kv, cfg.head_dim, cfg.rank, cfg.prefix, cfg.window, cfg.chunk
+    n_app = args.warmup + args.steps
+    assert n_app * S <= W, "more rollovers than window chunks"
+    pcap, rcap = P + n_app * S, cfg.n_resid + n_app * S
+    base = sd.draw_layer(cfg, args.seed, dev)
+    bf = torch.bfloat16
+
+    def rep(t, shape_):
+        return t.unsqueeze(0).expand((nb,) + tuple(t.shape)).reshape(shape_) if t is not None else None
+
+    coeff = torch.zeros((nb, pcap, r), dtype=bf, device=dev)
+    coeff[:, :P] = sd.draw_coeff(cfg, args.seed + 1, dev).unsqueeze(0)
+    basis_g = torch.randn((nb, r, cfg.group_dim), device=dev).mul_(1.0 / 64).to(bf)
+    keys_all = torch.randn((nb, n_app * S, cfg.group_dim), device=dev).to(bf)
+    layers = []
+    for _ in range(G):
+        L = {"coeff": coeff, "basis": rep(base["basis"], (nb, Hkv, d, r)).contiguous()}
+        for k in ("w1", "b1", "w2", "b2"):
+            L[k] = base[k].unsqueeze(0).expand((nb,) + tuple(base[k].shape)).contiguous()
+        L["landmark"] = torch.zeros((nb, Hkv, pcap // S, d), dtype=bf, device=dev)
+        L["res_idx"] = torch.zeros((nb, Hkv, rcap), dtype=torch.int32, device=dev)
+        L["res_val"] = torch.zeros((nb, Hkv, rcap, d), dtype=bf, device=dev)
+        L["res_chunk_desc"] = torch.zeros((nb, Hkv, pcap // S), dtype=torch.int32, device=dev)
+        L["win_k"] = base["win_k"].unsqueeze(0).expand(nb, Hkv, W, d).contiguous()
+        L["win_v"] = base["win_v"].unsqueeze(0).expand(nb, Hkv, W, d).contiguous()
+        L["thresh"] = torch.zeros((nb, Hkv), dtype=torch.float32, device=dev)
+        L["count"] = torch.full((nb, Hkv), cfg.n_resid, dtype=torch.int32, device=dev)
+        L["dropped"] = torch.zeros((nb, Hkv), dtype=torch.int32, device=dev)
+        layers.append(L)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 + G)]
+    acc = {"coeff": 0.0, "layer": 0.0}
+
+    def step(k, record):
+        P0, W0 = P + k * S, W - k * S
+        sh = native.make_shape(cfg, batch=nb, prefix_len=P0, window=W0, n_cand=P0 // S, n_resid=rcap,
+                               prefix_cap=pcap, window_cap=W)
+        kn = keys_all[:, k * S:(k + 1) * S]
+        if record:
+            ev[0].record()
+        native.append_coeff(sh, G, kn, basis_g, coeff)
+        if record:
+            ev[1].record()
+        for li, L in enumerate(layers):
+            io = dict(keys_new=kn, res_thresh=L["thresh"], res_count=L["count"], res_dropped=L["dropped"],
+                      landmark=L["landmark"], res_idx=L["res_idx"], res_val=L["res_val"],
+                      res_chunk_desc=L["res_chunk_desc"], win_k=L["win_k"], win_v=L["win_v"])
+            native.append_layer(sh, G, li, L, io)
+            if record:
+                ev[2 + li].record()
+
+    for k in range(args.warmup):
+        step(k, False)
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tot = 0.0
+    for k in range(args.warmup, n_app):
+        t0.record()
+        step(k, True)
+        t1.record()
+        torch.cuda.synchronize()
+        tot += t0.elapsed_time(t1)
+        acc["coeff"] += ev[0].elapsed_time(ev[1])
+        acc["layer"] += ev[1].elapsed_time(ev[1 + G]) / G
+    step_ms = tot / args.steps
+    per_layer_us = acc["layer"] / args.steps * 1e3
+    coeff_us = acc["coeff"] / args.steps * 1e3
+    # fp32 FMA work of the rollover kernel per layer: per (sequence, head, token) the
+    # rebuild (d r) and the MLP (2 d H) multiply-adds
+    H = cfg.mlp_hidden
+    flops = 2.0 * nb * Hkv * S * (d * r + 2 * d * H)
+    ach = flops / (per_layer_us * 1e-6) / 1e12
+    res = {
+        "metric": "window rollover: 8-token chunks moved into the compressed prefix per second (262K, batch 28)",
+        "value": round(nb / (step_ms * 1e-3 / G), 1), "unit": "chunks/s per layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32 (bf16 storage)",
+        "data": "synthetic (seeded device draws)",
+        "config": {"workload": cfg.name + "_rollover", "batch": nb, "ctx": cfg.ctx, "group_layers": G,
+                   "heads_kv": Hkv, "rank": r, "chunk": S},
+        "roofline": {"bound": "alu", "kernel": "append", "achieved": round(ach, 3), "peak": 157.3,
+                     "unit": "TFLOP/s", "frac": round(ach / 157.3, 4), "traffic": None},
+        "kernels": {"append_coeff_us": round(coeff_us, 2), "append_layer_us": round(per_layer_us, 2)},
+        "note": "step = one group (4 layers); a full 32-layer model rolls over 8 groups",
+    }
+    print(json.dumps(res))
+
+
 def bench_shared(args, cfg, nq, n_layers):
     """Q queries over one 262K context per layer: every query's own top-k,
     rebuild and attention; the context is read by all of them."""
@@ -501,6 +605,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode step shards by "
               "sequence with no exchange, so N GPUs would each run this single-GPU workload.", file=sys.stderr)
         sys.exit(2)
+    if args.append:
+        bench_append(args)
+        return
     if args.build:
         if args.copy_probe_mib:
             copy_probe(args.copy_probe_mib)
