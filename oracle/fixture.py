@@ -39,6 +39,22 @@ def _group_state(cfg, b: int, grp: int, exact: bool):
     return x, B, c_st
 
 
+_BASIS_OVERRIDE = {}
+
+
+def build_layer_with_basis(cfg, layer: int, basis_rows: np.ndarray):
+    """build_layer for batch element 0 with the group's basis replaced by
+    ``basis_rows`` [r][D] (orthonormal rows), e.g. a fitted basis."""
+    grp = layer // cfg.group_layers
+    x = synth.exact_keys(cfg, 0, grp, dtype=_key_dtype(cfg))
+    B = np.asarray(basis_rows, np.float64)
+    _BASIS_OVERRIDE[(cfg, 0, grp)] = (x, B, store_coeff(project(x[: cfg.prefix], B), cfg.int4, False))
+    try:
+        return build_layer(cfg, layer, batch=[0])
+    finally:
+        _BASIS_OVERRIDE.pop((cfg, 0, grp), None)
+
+
 def build_layer(cfg, layer: int, batch=None, exact: bool = False):
     """Compressed cache + queries of ``layer`` for the batch elements ``batch``."""
     batch = list(range(cfg.batch)) if batch is None else list(batch)
@@ -46,7 +62,7 @@ def build_layer(cfg, layer: int, batch=None, exact: bool = False):
     grp = layer // G
     per_b = []
     for b in batch:
-        x, B, c_st = _group_state(cfg, b, grp, exact)
+        x, B, c_st = _BASIS_OVERRIDE.get((cfg, b, grp)) or _group_state(cfg, b, grp, exact)
         heads = []
         for h in range(Hkv):
             cols = synth.layer_cols(cfg, layer, h)

@@ -406,3 +406,62 @@ def test_append_chunk_matches_a_longer_build():
     assert np.allclose(app["rows"], (v[P:P + 8] - pred)[app["keep"]], atol=1e-10)
     # the threshold is the nR-th largest prefix error
     assert np.sum(base["errors"] >= base["res_thresh"]) == cfg.n_resid
+
+
+# ------------------------------------------------------------- basis fit --
+def test_cholqr_equals_householder_qr():
+    """Cholesky-QR equals LAPACK's Householder QR with the diagonal of R made positive."""
+    from oracle import basis
+    rng = np.random.default_rng(21)
+    y = rng.standard_normal((300, 40)) @ np.diag(np.logspace(0, 2, 40))
+    q, r = basis.cholqr(y)
+    q2, r2 = np.linalg.qr(y)
+    s = np.sign(np.diag(r2))
+    assert np.allclose(q, q2 * s, atol=1e-10)
+    assert np.allclose(r, s[:, None] * r2, atol=1e-9)
+
+
+def test_randomized_basis_against_exact_svd():
+    """On the synthetic keys (a 64-dimensional latent subspace plus noise) the
+    randomised Cholesky-QR basis is orthonormal, contains the latent subspace
+    (the SVD's top 64 directions) to within a small angle, and its projection
+    error is within 1% of the SVD optimum, which it cannot beat (Eckart-Young)."""
+    from oracle import basis
+    cfg = synth.C0.with_(name="fit", rank=128)
+    x = synth.exact_keys(cfg, 0, 0)[: cfg.prefix]
+    rng = np.random.default_rng(22)
+    omega = rng.standard_normal((cfg.prefix, cfg.rank))
+    b_r = basis.randomized_cholqr(x, omega)
+    b_s = basis.svd_basis(x, cfg.rank)
+    assert np.allclose(b_r @ b_r.T, np.eye(cfg.rank), atol=1e-12)
+    assert basis.max_angle(b_s[:64], b_r) < 1e-3
+    e_r, e_s = basis.projection_error(x, b_r), basis.projection_error(x, b_s)
+    assert e_s <= e_r + 1e-12
+    assert e_r <= 1.05 * e_s
+    # without the power pass the sketch is visibly worse; a second pass does not hurt
+    b_0 = basis.randomized_cholqr(x, omega, power=0)
+    assert basis.projection_error(x, b_0) > 1.2 * e_s and basis.max_angle(b_s[:64], b_0) > 1e-2
+    b_2 = basis.randomized_cholqr(x, omega, power=2)
+    assert basis.projection_error(x, b_2) <= e_r + 1e-12
+
+
+def test_randomized_basis_downstream_decode():
+    """Decode with a cache compressed in the randomised basis matches decode with
+    the exact-SVD basis: both within bf16-scale distance of dense attention on
+    the exact keys, and of each other."""
+    from oracle import basis, fixture
+    cfg = synth.C0.with_(name="fit2", ctx=1024, window=32, rank=128, topk=10 ** 6, resid_frac=1.0)
+    layer = 1
+    x = synth.exact_keys(cfg, 0, 0)
+    rng = np.random.default_rng(23)
+    omega = rng.standard_normal((cfg.prefix, cfg.rank))
+    outs = {}
+    for name, B in (("svd", basis.svd_basis(x[: cfg.prefix], cfg.rank)),
+                    ("rand", basis.randomized_cholqr(x[: cfg.prefix], omega))):
+        cache = fixture.build_layer_with_basis(cfg, layer, B)
+        outs[name], _ = decode.decode_step(cfg, cache, cache["q"])
+    k, v, q = fixture.dense_layer(cfg, layer)
+    dense = decode.dense_step(codecs.bf16_decode(k), codecs.bf16_decode(v), codecs.bf16_decode(q), cfg.n_heads_kv)
+    for name in outs:
+        assert np.linalg.norm(outs[name] - dense) / np.linalg.norm(dense) < 2e-2, name
+    assert np.linalg.norm(outs["svd"] - outs["rand"]) / np.linalg.norm(outs["svd"]) < 1e-2
