@@ -514,3 +514,46 @@ int lowram_append_layer(const lowram_shape* shape, int32_t group_layers, int32_t
 }
 
 }  // extern "C"
+
+namespace {
+int check_fit(const lowram_fit_shape* s) {
+  if (!s) return LOWRAM_ERR_NULL;
+  if (s->batch < 1 || s->ctx_len < 1 || s->prefix_len < 1 || s->prefix_len > s->ctx_len || s->group_dim < 1 ||
+      s->rank < 1 || s->power < 0)
+    return LOWRAM_ERR_SHAPE;
+  if (s->prefix_len % 64 || s->group_dim % 128) return LOWRAM_ERR_UNSUPPORTED;
+  if (s->rank != 64 && s->rank != 128 && s->rank != 256 && s->rank != 512) return LOWRAM_ERR_UNSUPPORTED;
+  if (s->rank > s->group_dim || s->rank > s->prefix_len) return LOWRAM_ERR_SHAPE;
+  if (s->power > 4) return LOWRAM_ERR_UNSUPPORTED;
+  if ((int64_t)s->ctx_len * s->group_dim >= (int64_t)1 << 31 || (int64_t)s->prefix_len * s->rank >= (int64_t)1 << 31)
+    return LOWRAM_ERR_UNSUPPORTED;
+  return LOWRAM_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int lowram_fit_basis_workspace_bytes(const lowram_fit_shape* shape, size_t* bytes) {
+  if (!bytes) return LOWRAM_ERR_NULL;
+  const int st = check_fit(shape);
+  if (st) return st;
+  *bytes = fit_basis_ws_bytes(shape->prefix_len, shape->group_dim, shape->rank);
+  return LOWRAM_OK;
+}
+
+int lowram_fit_basis(const lowram_fit_shape* shape, const uint16_t* keys, const uint16_t* omega_t, uint16_t* basis,
+                     int32_t* status, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_fit(shape);
+  if (st) return st;
+  if (!keys || !omega_t || !basis || !status || !workspace) return LOWRAM_ERR_NULL;
+  if (misaligned(keys, 16) || misaligned(omega_t, 16) || misaligned(basis, 16) || misaligned(workspace, 256) ||
+      misaligned(status, 4))
+    return LOWRAM_ERR_ALIGN;
+  if (ws_bytes < fit_basis_ws_bytes(shape->prefix_len, shape->group_dim, shape->rank)) return LOWRAM_ERR_WORKSPACE;
+  if (launch_fit_basis(keys, omega_t, basis, shape->batch, shape->ctx_len, shape->prefix_len, shape->group_dim,
+                       shape->rank, shape->power, workspace, status, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LOWRAM_ERR_HIP;
+  return LOWRAM_OK;
+}
+
+}  // extern "C"

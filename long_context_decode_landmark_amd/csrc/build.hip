@@ -91,6 +91,11 @@ struct ProjArgs {
   int T, P, D, r, n_tb, n_rb, total, padded_total;
   int out_rows, row0;  // output row of (b, t): b * out_rows + row0 + t
   bool int4;
+  int mode;            // 0: cache encoding (bf16 / int4); 1: fp32 rows [row][r] into out_f32;
+                       // 2: bf16 transposed into out_t[(b * r + m) * ld_t + t]
+  float* out_f32;
+  uint16_t* out_t;
+  int ld_t;
 };
 
 template <int TN>
@@ -179,6 +184,39 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const ProjArgs a) {
       for (int e = 0; e < 4; ++e)
         tile[(64 * wm + 16 * mt + 4 * grp + e) * L::kTileStride + (TN / 2) * wn + 16 * nt + col] = acc[mt][nt][e];
   __syncthreads();
+  if (a.mode == 1) {
+    // fp32 rows: thread -> (row tl, 4 consecutive m); 128 x TN values
+    for (int idx = tid; idx < kProjTM * (TN / 4); idx += 256) {
+      const int tl = idx / (TN / 4), m4 = 4 * (idx % (TN / 4));
+      const int t = t0 + tl;
+      if (t >= a.P) continue;
+      const float* src = tile + tl * L::kTileStride + m4;
+      *reinterpret_cast<f32x4*>(a.out_f32 + ((size_t)b * a.out_rows + a.row0 + t) * a.r + m0 + m4) =
+          f32x4{src[0], src[1], src[2], src[3]};
+    }
+    return;
+  }
+  if (a.mode == 2) {
+    // bf16 transposed: thread -> (m, 8 consecutive rows t)
+    for (int idx = tid; idx < TN * (kProjTM / 8); idx += 256) {
+      const int ml = idx / (kProjTM / 8), t8 = 8 * (idx % (kProjTM / 8));
+      if (t0 + t8 >= a.P) continue;
+      f32x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = tile[(t8 + e) * L::kTileStride + ml];
+        hi[e] = tile[(t8 + 4 + e) * L::kTileStride + ml];
+      }
+      uint16_t* dst = a.out_t + ((size_t)b * a.r + m0 + ml) * a.ld_t + t0 + t8;
+      if (t0 + t8 + 8 <= a.P) {
+        *reinterpret_cast<bf16x8*>(dst) = pack8(lo, hi);
+      } else {
+        const bf16x8 v = pack8(lo, hi);
+        for (int e = 0; e < 8 && t0 + t8 + e < a.P; ++e) dst[e] = __builtin_bit_cast(uint16_t, v[e]);
+      }
+    }
+    return;
+  }
   constexpr int GPT = TN / 32;  // groups per token row of the tile
   for (int gi = tid; gi < kProjTM * GPT; gi += 256) {
     const int tl = gi / GPT, j = gi % GPT;
@@ -203,8 +241,29 @@ hipError_t launch_proj(const uint16_t* keys, const uint16_t* basis, void* coeff,
   a.T = T; a.P = P; a.D = D; a.r = r; a.int4 = int4;
   a.out_rows = out_rows < 0 ? P : out_rows;
   a.row0 = row0;
+  a.mode = 0;
   const int tn = r >= 128 ? 128 : 64;
   a.n_tb = (P + kProjTM - 1) / kProjTM;
+  a.n_rb = r / tn;
+  a.total = nb * a.n_tb * a.n_rb;
+  a.padded_total = (a.total + 7) & ~7;
+  if (tn == 128) hipLaunchKernelGGL(proj_kernel<128>, dim3(a.padded_total), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(proj_kernel<64>, dim3(a.padded_total), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// C[t][m] = sum_j A[b][t][j] B[b][m][j] for t < rows, m < r (A: T rows per
+// sequence, K columns; B: [NB][r][K]); K a multiple of 64.  mode 1: fp32
+// [NB][rows][r]; mode 2: bf16 transposed [NB][r][ld_t].
+hipError_t launch_gemm_nt(const uint16_t* A, const uint16_t* B, int nb, int T, int rows, int K, int r, int mode,
+                          float* out_f32, uint16_t* out_t, int ld_t, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  ProjArgs a{};
+  a.keys = A; a.basis = B;
+  a.T = T; a.P = rows; a.D = K; a.r = r;
+  a.out_rows = rows; a.row0 = 0; a.mode = mode; a.out_f32 = out_f32; a.out_t = out_t; a.ld_t = ld_t;
+  const int tn = r >= 128 ? 128 : 64;
+  a.n_tb = (rows + kProjTM - 1) / kProjTM;
   a.n_rb = r / tn;
   a.total = nb * a.n_tb * a.n_rb;
   a.padded_total = (a.total + 7) & ~7;

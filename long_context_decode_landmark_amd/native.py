@@ -34,6 +34,8 @@ SYMBOLS = (
     "lowram_build_layer_events",
     "lowram_append_coeff",
     "lowram_append_layer",
+    "lowram_fit_basis_workspace_bytes",
+    "lowram_fit_basis",
 )
 
 ERRORS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "UNSUPPORTED", -4: "WORKSPACE", -5: "ALIGN", -6: "HIP"}
@@ -77,6 +79,10 @@ APPEND_FIELDS = ("keys_new", "res_thresh", "res_count", "res_dropped", "landmark
 
 class LowramLayerAppend(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in APPEND_FIELDS]
+
+
+class LowramFitShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("batch", "ctx_len", "prefix_len", "group_dim", "rank", "power")]
 
 
 class DenseShape(ctypes.Structure):
@@ -133,6 +139,8 @@ def lib() -> ctypes.CDLL:
         L.lowram_append_coeff.argtypes = [ctypes.POINTER(LowramShape), ctypes.c_int32, vp, vp, vp, vp, vp]
         L.lowram_append_layer.argtypes = [ctypes.POINTER(LowramShape), ctypes.c_int32, ctypes.c_int32,
                                           ctypes.POINTER(LowramLayerCache), ctypes.POINTER(LowramLayerAppend), vp]
+        L.lowram_fit_basis_workspace_bytes.argtypes = [ctypes.POINTER(LowramFitShape), ctypes.POINTER(sz)]
+        L.lowram_fit_basis.argtypes = [ctypes.POINTER(LowramFitShape), vp, vp, vp, vp, vp, sz, vp]
         for name in SYMBOLS:
             getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
         L.lowram_strerror.restype = ctypes.c_char_p
@@ -307,3 +315,23 @@ def append_layer(shape, group_layers: int, layer_in_group: int, cache, io: dict,
     a = LowramLayerAppend(**{n: (io[n].data_ptr() if io.get(n) is not None else None) for n in APPEND_FIELDS})
     _check(lib().lowram_append_layer(ctypes.byref(shape), group_layers, layer_in_group, ctypes.byref(c),
                                      ctypes.byref(a), _stream(stream)), "lowram_append_layer")
+
+
+# ------------------------------------------------------------------ basis fit --
+def fit_shape(batch, ctx_len, prefix_len, group_dim, rank, power=1) -> LowramFitShape:
+    return LowramFitShape(batch=batch, ctx_len=ctx_len, prefix_len=prefix_len, group_dim=group_dim, rank=rank,
+                          power=power)
+
+
+def fit_basis_workspace_bytes(shape: LowramFitShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().lowram_fit_basis_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)),
+           "lowram_fit_basis_workspace_bytes")
+    return n.value
+
+
+def fit_basis(shape, keys, omega_t, basis, status, workspace, stream=None) -> None:
+    """lowram_fit_basis: keys [NB][T][D], omega_t [NB][r][P] -> basis [NB][r][D], status [NB]."""
+    _check(lib().lowram_fit_basis(ctypes.byref(shape), _ptr(keys), _ptr(omega_t), _ptr(basis), _ptr(status),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "lowram_fit_basis")

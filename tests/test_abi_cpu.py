@@ -279,3 +279,21 @@ def test_build_caps_rejected(kw, code):
     with pytest.raises(native.LowramError) as e:
         native.build_layer_workspace_bytes(bshape(**kw))
     assert e.value.status == code
+
+
+def test_fit_basis_rejects():
+    def st(s):
+        with pytest.raises(native.LowramError) as e:
+            native.fit_basis_workspace_bytes(s)
+        return e.value.status
+    assert st(native.fit_shape(1, 4096, 4000, 512, 64)) == -3      # P not a multiple of 64
+    assert st(native.fit_shape(1, 4096, 4032, 500, 64)) == -3      # D not a multiple of 128
+    assert st(native.fit_shape(1, 4096, 4032, 512, 96)) == -3      # rank
+    assert st(native.fit_shape(1, 4096, 8192, 512, 64)) == -2      # P > T
+    assert st(native.fit_shape(1, 4096, 4032, 512, 64, power=-1)) == -2
+    s = native.fit_shape(1, 4096, 4032, 512, 64)
+    need = native.fit_basis_workspace_bytes(s)
+    with pytest.raises(native.LowramError) as e:
+        native.fit_basis(s, FakeTensor(0x1000), FakeTensor(0x2000), FakeTensor(0x3000), FakeTensor(0x4000),
+                         FakeTensor(0x5000, n=need - 1), stream=0)
+    assert e.value.status == -4
