@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--shared", type=int, default=0, metavar="Q",
                     help="time Q queries over one shared context (shared-prefix multi-query decode)")
+    ap.add_argument("--fit", action="store_true",
+                    help="time the randomised Cholesky-QR basis fit of one 262K-token layer group")
     ap.add_argument("--append", action="store_true",
                     help="time the window rollover (one chunk into the prefix) for one layer group")
     ap.add_argument("--build", action="store_true",
@@ -469,6 +471,79 @@ def bench_build(args):
     print(json.dumps(res))
 
 
+def fit_cpu_baseline(cfg, n_tok):
+    """The oracle's randomised Cholesky-QR fit and its exact SVD fit on the first
+    n_tok tokens of the group (fp64 NumPy / LAPACK on the host), scaled to P."""
+    import numpy as np
+    from oracle import basis, codecs
+    import synth
+    x = codecs.bf16_round(synth.exact_keys(cfg, 0, 0, 0, n_tok, dtype=np.float32))
+    om = np.random.default_rng(5).standard_normal((n_tok, cfg.rank))
+    t0 = time.perf_counter()
+    basis.randomized_cholqr(x, om, power=1)
+    t_rand = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    basis.svd_basis(x, cfg.rank)
+    t_svd = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    scale = cfg.prefix / n_tok
+    return {"value": round(cfg.prefix / (t_rand * scale), 1), "unit": "prefix tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"randomised CholQR (one power pass) of the first {n_tok} tokens x {cfg.group_dim} dims in "
+                      f"{t_rand:.2f} s, scaled x{scale:.1f} (linear in tokens); exact SVD of the same sample "
+                      f"{t_svd:.2f} s ({t_svd / t_rand:.1f}x the randomised fit)"}
+
+
+def bench_fit(args):
+    """lowram_fit_basis for one 262K-token layer group (keys 261888 x 4096,
+    rank 512, one power pass): three MFMA GEMMs of 2 P D r flops each plus
+    four fp64 Cholesky-QR passes."""
+    import torch
+    import synth
+    from long_context_decode_landmark_amd import native
+    from synth import device as sd
+    cfg = synth.CONFIGS[args.config]
+    P, D, r = cfg.prefix, cfg.group_dim, cfg.rank
+    dev = torch.device("cuda:0")
+    d_in = sd.draw_build_inputs(cfg, args.seed, dev, 1, layers=[])
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    om = torch.randn((1, r, P), generator=g, device=dev).to(torch.bfloat16)
+    shape = native.fit_shape(1, cfg.ctx, P, D, r, 1)
+    ws = torch.empty(native.fit_basis_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    out = torch.empty((1, r, D), dtype=torch.bfloat16, device=dev)
+    status = torch.empty((1,), dtype=torch.int32, device=dev)
+    for _ in range(args.warmup):
+        native.fit_basis(shape, d_in["keys"], om, out, status, ws)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        native.fit_basis(shape, d_in["keys"], om, out, status, ws)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    gemm_flops = 3 * 2.0 * P * D * r
+    ach = gemm_flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "basis fit: prefix tokens per second (randomised Cholesky-QR, one power pass, one layer group)",
+        "value": round(P / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 GEMMs, fp64 Cholesky-QR", "data": "synthetic (seeded device draws)",
+        "config": {"workload": cfg.name + "_fit", "prefix": P, "group_dim": D, "rank": r, "power": 1},
+        "roofline": {"bound": "mfma", "kernel": "whole fit (GEMM flops)", "achieved": round(ach, 2),
+                     "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4),
+                     "traffic": None},
+        "status": int(status.cpu()[0]),
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = fit_cpu_baseline(cfg, 32768)
+    print(json.dumps(res))
+
+
 def bench_append(args):
     """Window rollover at 262K, batch 28: one step moves the oldest 8 window
     tokens of every sequence into the prefix, for the G layers of one group
@@ -605,6 +680,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode step shards by "
               "sequence with no exchange, so N GPUs would each run this single-GPU workload.", file=sys.stderr)
         sys.exit(2)
+    if args.fit:
+        bench_fit(args)
+        return
     if args.append:
         bench_append(args)
         return

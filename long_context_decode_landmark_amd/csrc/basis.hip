@@ -55,16 +55,20 @@ __global__ __launch_bounds__(256) void transpose_f32_bf16_kernel(const float* __
   }
 }
 
-// G[i][j] = sum_n Y[n][i] Y[n][j] (fp64) for one 64 x 64 block (grid r/64 x r/64)
-__global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ y, double* __restrict__ g, int n, int r) {
+// Partial G[z][i][j] = sum over rows n of chunk z of Y[n][i] Y[n][j] (fp64), one 64 x 64
+// block per workgroup (grid r/64 x r/64 x chunks; chunk = rows per split)
+__global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ y, double* __restrict__ g, int n, int r,
+                                                   int chunk) {
   __shared__ float ya[16][kBlk + 1], yb[16][kBlk + 1];
   const int i0 = blockIdx.x * kBlk, j0 = blockIdx.y * kBlk, tid = threadIdx.x;
   const int ti = tid / 16, tj = tid % 16;  // 4 x 4 outputs: rows ti + 16 a, cols tj + 16 b
+  const int nbeg = blockIdx.z * chunk, nend = min(n, nbeg + chunk);
+  g += (size_t)blockIdx.z * r * r;
   double acc[4][4] = {};
-  for (int n0 = 0; n0 < n; n0 += 16) {
+  for (int n0 = nbeg; n0 < nend; n0 += 16) {
     for (int idx = tid; idx < 16 * kBlk; idx += 256) {
       const int rr = idx / kBlk, cc = idx % kBlk;
-      const bool in = n0 + rr < n;
+      const bool in = n0 + rr < nend;
       ya[rr][cc] = in ? y[(size_t)(n0 + rr) * r + i0 + cc] : 0.f;
       yb[rr][cc] = in ? y[(size_t)(n0 + rr) * r + j0 + cc] : 0.f;
     }
@@ -89,57 +93,71 @@ __global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ y, 
     for (int b = 0; b < 4; ++b) g[(size_t)(i0 + ti + 16 * a) * r + j0 + tj + 16 * b] = acc[a][b];
 }
 
-// Diagonal block kb: factor A_kk = R_kk^T R_kk in LDS (unblocked right-looking),
-// write R_kk into the upper triangle of g and R_kk^-1 into dinv[kb].
+// Diagonal block kb: factor A_kk = R_kk^T R_kk in LDS, write R_kk into the
+// upper triangle of g and R_kk^-1 into dinv[kb].  Symmetric elimination with
+// one barrier per step (a_ik -= a_ji a_jk / a_jj on the upper triangle, rows
+// below j), then R[j][k] = a[j][k] / sqrt(a[j][j]); the inverse by the same
+// kind of sweep, bottom row first (x_j = b_j / R_jj, then b_i -= R_ij x_j).
 // A non-positive pivot sets *status = 1 and continues with pivot 1.
 __global__ __launch_bounds__(256) void chol_diag_kernel(double* __restrict__ g, double* __restrict__ dinv, int r, int kb,
                                                         int* __restrict__ status) {
   __shared__ double a[kBlk][kBlk + 1];
-  __shared__ double piv;
+  __shared__ double xs[kBlk][kBlk + 1];
   const int tid = threadIdx.x, o = kb * kBlk;
   for (int idx = tid; idx < kBlk * kBlk; idx += 256) a[idx / kBlk][idx % kBlk] = g[(size_t)(o + idx / kBlk) * r + o + idx % kBlk];
   __syncthreads();
+  // thread -> column k = tid % 64, rows i = tid / 64 + 4 q
+  const int k = tid & 63, i0 = tid >> 6;
   for (int j = 0; j < kBlk; ++j) {
-    if (tid == 0) {
-      double d = a[j][j];
-      if (!(d > 0.0)) {
-        *status = 1;
-        d = 1.0;
-      }
-      piv = sqrt(d);
-      a[j][j] = piv;
+    double d = a[j][j];
+    if (!(d > 0.0)) d = 1.0;
+    const double ajk = a[j][k] / d;
+    // all loads of the step first (row j is not written in step j), then the updates
+    double rj[kBlk / 4], aik[kBlk / 4];
+#pragma unroll
+    for (int q = 0; q < kBlk / 4; ++q) {
+      rj[q] = a[j][i0 + 4 * q];
+      aik[q] = a[i0 + 4 * q][k];
     }
-    __syncthreads();
-    for (int k = j + 1 + tid; k < kBlk; k += 256) a[j][k] /= piv;
-    __syncthreads();
-    for (int idx = tid; idx < kBlk * kBlk; idx += 256) {
-      const int i = idx / kBlk, k = idx % kBlk;
-      if (i > j && k >= i) a[i][k] -= a[j][i] * a[j][k];
+#pragma unroll
+    for (int q = 0; q < kBlk / 4; ++q) {
+      const int i = i0 + 4 * q;
+      if (k > j && i > j && i <= k) a[i][k] = aik[q] - rj[q] * ajk;
     }
     __syncthreads();
   }
-  // R_kk (upper) back to g
+  if (tid < kBlk && !(a[tid][tid] > 0.0)) *status = 1;
+  // R = a / sqrt(diag) by rows (upper); lower part 0
   for (int idx = tid; idx < kBlk * kBlk; idx += 256) {
-    const int i = idx / kBlk, k = idx % kBlk;
-    g[(size_t)(o + i) * r + o + k] = k >= i ? a[i][k] : 0.0;
-  }
-  // inverse of the upper-triangular R_kk, one column per thread (back substitution)
-  __shared__ double xs[kBlk][kBlk + 1];
-  if (tid < kBlk) {
-    const int c = tid;
-    for (int i = kBlk - 1; i >= 0; --i) {
-      double v = 0.0;
-      if (i <= c) {
-        v = (i == c) ? 1.0 : 0.0;
-        for (int k = i + 1; k <= c; ++k) v -= a[i][k] * xs[k][c];
-        v /= a[i][i];
-      }
-      xs[i][c] = v;
-    }
+    const int ii = idx / kBlk, kk = idx % kBlk;
+    const double dd = a[ii][ii] > 0.0 ? a[ii][ii] : 1.0;
+    xs[ii][kk] = kk >= ii ? a[ii][kk] / sqrt(dd) : 0.0;
   }
   __syncthreads();
+  for (int idx = tid; idx < kBlk * kBlk; idx += 256) {
+    const int ii = idx / kBlk, kk = idx % kBlk;
+    g[(size_t)(o + ii) * r + o + kk] = xs[ii][kk];
+    a[ii][kk] = ii == kk ? 1.0 : 0.0;  // b = I
+  }
+  __syncthreads();
+  // inverse: rows of x from the bottom; x_j = b_j / R_jj; b_i -= R_ij x_j (i < j)
+  for (int jj = kBlk - 1; jj >= 0; --jj) {
+    const double xj = a[jj][k] / xs[jj][jj];
+    double rij[kBlk / 4], bik[kBlk / 4];
+#pragma unroll
+    for (int q = 0; q < kBlk / 4; ++q) {
+      rij[q] = xs[i0 + 4 * q][jj];
+      bik[q] = a[i0 + 4 * q][k];
+    }
+#pragma unroll
+    for (int q = 0; q < kBlk / 4; ++q)
+      if (i0 + 4 * q < jj) a[i0 + 4 * q][k] = bik[q] - rij[q] * xj;
+    __syncthreads();
+    if (tid < kBlk) a[jj][k] = xj;  // row jj is final (not read again by the update)
+    __syncthreads();
+  }
   double* inv = dinv + (size_t)kb * kBlk * kBlk;
-  for (int idx = tid; idx < kBlk * kBlk; idx += 256) inv[idx] = xs[idx / kBlk][idx % kBlk];
+  for (int idx = tid; idx < kBlk * kBlk; idx += 256) inv[idx] = a[idx / kBlk][idx % kBlk];
 }
 
 // Panel: R_kj = R_kk^-T A_kj for every block column j > kb (one per workgroup).
@@ -247,10 +265,27 @@ __global__ __launch_bounds__(256) void trsm_kernel(float* __restrict__ y, const 
 
 __global__ void zero_i32_kernel(int* p) { *p = 0; }
 
-// One Cholesky-QR pass over y [n][r] in place; g [r][r], dinv [r/64][64][64] scratch.
-static hipError_t cholqr_pass(float* y, int n, int r, double* g, double* dinv, int* status, hipStream_t st) {
+// g[i] = sum_z part[z][i] (fp64)
+__global__ __launch_bounds__(256) void gram_sum_kernel(double* __restrict__ g, const double* __restrict__ part, int n,
+                                                       int splits) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  double v = 0.0;
+  for (int z = 0; z < splits; ++z) v += part[(size_t)z * n + i];
+  g[i] = v;
+}
+
+constexpr int kGramRows = 256;   // rows of Y per Gram split
+constexpr int kGemmSplits = 16;  // K splits of the token-contraction GEMMs
+
+// One Cholesky-QR pass over y [n][r] in place; g [r][r], dinv [r/64][64][64], gpart
+// [ceil(n / kGramRows)][r][r] scratch.
+static hipError_t cholqr_pass(float* y, int n, int r, double* g, double* dinv, double* gpart, int* status,
+                              hipStream_t st) {
   const int nbk = r / kBlk;
-  hipLaunchKernelGGL(gram_kernel, dim3(nbk, nbk), dim3(256), 0, st, y, g, n, r);
+  const int gs = (n + kGramRows - 1) / kGramRows;
+  hipLaunchKernelGGL(gram_kernel, dim3(nbk, nbk, gs), dim3(256), 0, st, y, gpart, n, r, kGramRows);
+  hipLaunchKernelGGL(gram_sum_kernel, dim3((r * r + 255) / 256), dim3(256), 0, st, g, gpart, r * r, gs);
   for (int kb = 0; kb < nbk; ++kb) {
     hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, st, g, dinv, r, kb, status);
     const int rest = nbk - kb - 1;
@@ -278,6 +313,10 @@ hipError_t launch_fit_basis(const uint16_t* keys, const uint16_t* omega_t, uint1
   uint16_t* qt = reinterpret_cast<uint16_t*>(w);                        // [r][D] bf16
   w += ((size_t)r * D * 2 + 255) & ~(size_t)255;
   uint16_t* wt = reinterpret_cast<uint16_t*>(w);                        // [r][P] bf16
+  w += ((size_t)r * P * 2 + 255) & ~(size_t)255;
+  double* gpart = reinterpret_cast<double*>(w);                         // [D/256][r][r]
+  w += ((size_t)((D + kGramRows - 1) / kGramRows) * r * r * 8 + 255) & ~(size_t)255;
+  float* ypart = reinterpret_cast<float*>(w);                           // [splits][D][r]
   for (int b = 0; b < nb; ++b) {
     const uint16_t* xb = keys + (size_t)b * T * D;
     int* sb = status + b;
@@ -285,18 +324,20 @@ hipError_t launch_fit_basis(const uint16_t* keys, const uint16_t* omega_t, uint1
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3((P + 63) / 64, (D + 63) / 64), dim3(256), 0, st, xb, xt, P, D, D,
                        P);
     // Y = X^T Omega: rows D, contraction P
-    hipError_t e = launch_gemm_nt(xt, omega_t + (size_t)b * r * P, 1, D, D, P, r, 1, y, nullptr, 0, st);
+    hipError_t e = launch_gemm_nt(xt, omega_t + (size_t)b * r * P, 1, D, D, P, r, 1, y, nullptr, 0, st,
+                                  kGemmSplits, ypart);
     if (e != hipSuccess) return e;
     for (int pass = 0; pass < 2; ++pass)
-      if ((e = cholqr_pass(y, D, r, g, dinv, sb, st)) != hipSuccess) return e;
+      if ((e = cholqr_pass(y, D, r, g, dinv, gpart, sb, st)) != hipSuccess) return e;
     for (int it = 0; it < power; ++it) {
       hipLaunchKernelGGL(transpose_f32_bf16_kernel, dim3((D + 63) / 64, (r + 63) / 64), dim3(256), 0, st, y, qt, D, r);
       // W^T = (X Q)^T: rows P (tokens), contraction D
       if ((e = launch_gemm_nt(xb, qt, 1, T, P, D, r, 2, nullptr, wt, P, st)) != hipSuccess) return e;
       // Y = X^T W: rows D, contraction P
-      if ((e = launch_gemm_nt(xt, wt, 1, D, D, P, r, 1, y, nullptr, 0, st)) != hipSuccess) return e;
+      if ((e = launch_gemm_nt(xt, wt, 1, D, D, P, r, 1, y, nullptr, 0, st, kGemmSplits, ypart)) != hipSuccess)
+        return e;
       for (int pass = 0; pass < 2; ++pass)
-        if ((e = cholqr_pass(y, D, r, g, dinv, sb, st)) != hipSuccess) return e;
+        if ((e = cholqr_pass(y, D, r, g, dinv, gpart, sb, st)) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(transpose_f32_bf16_kernel, dim3((D + 63) / 64, (r + 63) / 64), dim3(256), 0, st, y,
                        basis_out + (size_t)b * r * D, D, r);
@@ -307,7 +348,8 @@ hipError_t launch_fit_basis(const uint16_t* keys, const uint16_t* omega_t, uint1
 size_t fit_basis_ws_bytes(int P, int D, int r) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   return al((size_t)D * P * 2) + al((size_t)D * r * 4) + al((size_t)r * r * 8) + al((size_t)r * kBlk * 8) +
-         al((size_t)r * D * 2) + al((size_t)r * P * 2);
+         al((size_t)r * D * 2) + al((size_t)r * P * 2) + al((size_t)((D + kGramRows - 1) / kGramRows) * r * r * 8) +
+         al((size_t)kGemmSplits * D * r * 4);
 }
 
 }  // namespace lowram

@@ -96,6 +96,8 @@ struct ProjArgs {
   float* out_f32;
   uint16_t* out_t;
   int ld_t;
+  int splits;          // K split into `splits` ranges of k_split columns (mode 1: partial sums
+  int k_split;         // go to out_f32 + split * rows * r)
 };
 
 template <int TN>
@@ -112,10 +114,13 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const ProjArgs a) {
   if (logical >= a.total) return;
   const int rb = logical % a.n_rb;
   const int tb = (logical / a.n_rb) % a.n_tb;
-  const int b = logical / (a.n_rb * a.n_tb);
+  const int bs_ = logical / (a.n_rb * a.n_tb);  // (split, sequence)
+  const int b = bs_ % (a.total / (a.n_rb * a.n_tb * a.splits));
+  const int split = bs_ / (a.total / (a.n_rb * a.n_tb * a.splits));
   const int t0 = tb * kProjTM, m0 = rb * TN;
-  const uint16_t* xs = a.keys + (size_t)b * a.T * a.D;
-  const uint16_t* bs = a.basis + ((size_t)b * a.r + m0) * a.D;
+  const int kbeg = split * a.k_split;
+  const uint16_t* xs = a.keys + (size_t)b * a.T * a.D + kbeg;
+  const uint16_t* bs = a.basis + ((size_t)b * a.r + m0) * a.D + kbeg;
 
   // staging assignment: piece tid % 8 of rows tid / 8 + 32 u
   const int srow = tid >> 3, spc = tid & 7;
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const ProjArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = a.D / kProjBK;
+  const int nk = min(a.k_split, a.D - kbeg) / kProjBK;
   load_stage(0);
   store_stage(0);
   __syncthreads();
@@ -191,7 +196,8 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(const ProjArgs a) {
       const int t = t0 + tl;
       if (t >= a.P) continue;
       const float* src = tile + tl * L::kTileStride + m4;
-      *reinterpret_cast<f32x4*>(a.out_f32 + ((size_t)b * a.out_rows + a.row0 + t) * a.r + m0 + m4) =
+      *reinterpret_cast<f32x4*>(a.out_f32 + (size_t)split * a.P * a.r +
+                                ((size_t)b * a.out_rows + a.row0 + t) * a.r + m0 + m4) =
           f32x4{src[0], src[1], src[2], src[3]};
     }
     return;
@@ -242,6 +248,8 @@ hipError_t launch_proj(const uint16_t* keys, const uint16_t* basis, void* coeff,
   a.out_rows = out_rows < 0 ? P : out_rows;
   a.row0 = row0;
   a.mode = 0;
+  a.splits = 1;
+  a.k_split = D;
   const int tn = r >= 128 ? 128 : 64;
   a.n_tb = (P + kProjTM - 1) / kProjTM;
   a.n_rb = r / tn;
@@ -255,20 +263,43 @@ hipError_t launch_proj(const uint16_t* keys, const uint16_t* basis, void* coeff,
 // C[t][m] = sum_j A[b][t][j] B[b][m][j] for t < rows, m < r (A: T rows per
 // sequence, K columns; B: [NB][r][K]); K a multiple of 64.  mode 1: fp32
 // [NB][rows][r]; mode 2: bf16 transposed [NB][r][ld_t].
+__global__ __launch_bounds__(256) void split_sum_kernel(float* __restrict__ out, const float* __restrict__ part,
+                                                        size_t n, int splits) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
+  for (int s = 1; s < splits; ++s) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part + (size_t)s * n + i);
+    acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
+  }
+  *reinterpret_cast<f32x4*>(out + i) = acc;
+}
+
 hipError_t launch_gemm_nt(const uint16_t* A, const uint16_t* B, int nb, int T, int rows, int K, int r, int mode,
-                          float* out_f32, uint16_t* out_t, int ld_t, hipStream_t st) {
+                          float* out_f32, uint16_t* out_t, int ld_t, hipStream_t st, int splits,
+                          float* partials) {
   if (rows == 0) return hipSuccess;
   ProjArgs a{};
   a.keys = A; a.basis = B;
   a.T = T; a.P = rows; a.D = K; a.r = r;
   a.out_rows = rows; a.row0 = 0; a.mode = mode; a.out_f32 = out_f32; a.out_t = out_t; a.ld_t = ld_t;
+  if (mode != 1 || nb != 1 || !partials) splits = 1;
+  a.k_split = ((K / kProjBK + splits - 1) / splits) * kProjBK;
+  splits = (K + a.k_split - 1) / a.k_split;  // no empty split
+  a.splits = splits;
+  if (splits > 1) a.out_f32 = partials;
   const int tn = r >= 128 ? 128 : 64;
   a.n_tb = (rows + kProjTM - 1) / kProjTM;
   a.n_rb = r / tn;
-  a.total = nb * a.n_tb * a.n_rb;
+  a.total = nb * a.n_tb * a.n_rb * splits;
   a.padded_total = (a.total + 7) & ~7;
   if (tn == 128) hipLaunchKernelGGL(proj_kernel<128>, dim3(a.padded_total), dim3(256), 0, st, a);
   else hipLaunchKernelGGL(proj_kernel<64>, dim3(a.padded_total), dim3(256), 0, st, a);
+  if (splits > 1) {
+    const size_t n = (size_t)rows * r;
+    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, st, out_f32, partials,
+                       n, splits);
+  }
   return hipGetLastError();
 }
 

@@ -93,7 +93,8 @@ hipError_t launch_predict_resid(const void* coeff, const uint16_t* coeff_scale, 
                                 hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
 hipError_t launch_gemm_nt(const uint16_t* A, const uint16_t* B, int nb, int T, int rows, int K, int r, int mode,
-                          float* out_f32, uint16_t* out_t, int ld_t, hipStream_t st);
+                          float* out_f32, uint16_t* out_t, int ld_t, hipStream_t st, int splits = 1,
+                          float* partials = nullptr);
 hipError_t launch_fit_basis(const uint16_t* keys, const uint16_t* omega_t, uint16_t* basis_out, int nb, int T,
                             int P, int D, int r, int power, void* ws, int* status, hipStream_t st);
 size_t fit_basis_ws_bytes(int P, int D, int r);
