@@ -145,17 +145,35 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   a.cache_bmul = shared ? 0 : 1;
   a.prefix_cap = prefix_rows(s);
   a.window_cap = window_rows(s);
-  a.n_sel_tiles = has_prefix ? p.n_sel_tiles : 0;
+  // Selected chunks: the producer/consumer kernel, one partial slot per group
+  // of tiles; with stage outputs requested, the 4-wave kernel, one slot per
+  // tile.  The exact window always goes to the 4-wave kernel, in the slots
+  // after the selection's.
+  const bool stages = kpre_out || kpost_out || vhat_out;
+  const int heads = s->batch * s->n_heads_kv;
+  int n_grp = 0, tpw = 0;
+  if (has_prefix && !stages) plan_pipe_groups(heads, p.n_sel_tiles, &n_grp, &tpw);
+  const int sel_slots = !has_prefix ? 0 : stages ? p.n_sel_tiles : n_grp;
+  const int n_split = sel_slots + p.n_win_tiles;
+  a.n_sel_tiles = sel_slots;
   a.n_win_tiles = p.n_win_tiles;
-  a.n_split = p.n_split;
-  a.total = s->batch * s->n_heads_kv * p.n_split;
+  a.n_split = n_split;
+  a.split_base = stages ? 0 : sel_slots;
+  a.n_split_launch = stages ? n_split : p.n_win_tiles;
+  a.total = heads * a.n_split_launch;
   a.padded_total = (a.total + 7) & ~7;
+  a.pipe_tiles = p.n_sel_tiles;
+  a.n_grp = n_grp;
+  a.tpw = tpw;
+  a.pipe_total = heads * n_grp;
+  a.pipe_padded = (a.pipe_total + 7) & ~7;
   a.scale_log2 = s->softmax_scale * 1.4426950408889634f;
   for (int i = 0; i < 64; ++i)
     a.inv_freq[i] = std::pow((double)s->rope_theta, -2.0 * i / (double)kHeadDim);
   if (launch_attend(a, s->rank, ci4, ri4, hs) != hipSuccess) return LOWRAM_ERR_HIP;
+  if (launch_attend_pipe(a, s->rank, ci4, ri4, hs) != hipSuccess) return LOWRAM_ERR_HIP;
   if (!mark(3)) return LOWRAM_ERR_HIP;
-  if (launch_merge(part, out, s->batch, s->n_heads_kv, p.g, p.n_split, hs) != hipSuccess)
+  if (launch_merge(part, out, s->batch, s->n_heads_kv, p.g, n_split, hs) != hipSuccess)
     return LOWRAM_ERR_HIP;
   if (!mark(4)) return LOWRAM_ERR_HIP;
   return LOWRAM_OK;

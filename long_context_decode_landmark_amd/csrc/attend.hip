@@ -40,36 +40,11 @@
 // they are consumed, so the in-order vmcnt waits never hold a step on data
 // it does not need.  The selected tokens' residual rows go to LDS as one
 // dense tile (zero rows where a token has none) after the last stage.
+#include "attend_ops.h"
 #include "common.h"
 #include "internal.h"
 
 namespace lowram {
-
-// GELU without transcendental instructions (v_exp / v_rcp issue at a
-// quarter of the FMA rate): Phi(x) = 0.5 + x Q(x^2) for |x| <= 4, with Q of
-// degree 6 fitted by linear-programming minimax of the GELU error x (Phi~ - Phi)
-// under the constraint Phi~(4) = 1, and x clamped to +-4 (so Phi~ is exactly
-// 1 or 0 beyond).  Largest deviation from x Phi(x) (erf form) over the real
-// line in fp32: 1.9e-4, a fortieth of a bf16 step at 1, and the hidden
-// activations are rounded to bf16 right after.
-constexpr float kGeluClamp = 4.0f;
-constexpr float kGeluQ[7] = {3.978703618e-01f, -6.455454975e-02f, 8.763747290e-03f, -8.121979772e-04f,
-                             4.776486458e-05f, -1.588871555e-06f, 2.258899912e-08f};
-
-__device__ __forceinline__ float gelu_fast(float x) {
-  const float xc = __builtin_amdgcn_fmed3f(x, -kGeluClamp, kGeluClamp);
-  const float u = xc * xc;
-  float q = kGeluQ[6];
-#pragma unroll
-  for (int k = 5; k >= 0; --k) q = fmaf(q, u, kGeluQ[k]);
-  return x * fmaf(xc, q, 0.5f);
-}
-
-constexpr int kStage = 16384;  // bytes of one staged operand slice
-constexpr int kStageLd = 4;    // 16-byte loads per thread per stage (256 threads)
-
-constexpr int kResRow = 272;   // LDS stride of a bf16 residual row (256 + 16: rows on different banks)
-constexpr int kResRow4 = 80;   // int4 residual row: 64 bytes of codes, 8 of scales, 8 unused
 
 struct AttLds {
   // stage ring; then the residual tile (one row of kResRow per token); then the wave merge
@@ -82,22 +57,6 @@ struct AttLds {
   uint32_t rdesc[kAttChunksWG];
   alignas(16) uint16_t qs[16][kHeadDim];  // this KV head's query rows
 };
-
-// int4 x 8 (one 32-bit word, element e in bits 4e..4e+3) times scale -> bf16x8
-__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float scale) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int code = static_cast<int>(w << (28 - 4 * e)) >> 28;
-    r[e] = (__bf16)(static_cast<float>(code) * scale);
-  }
-  return r;
-}
-
-__device__ __forceinline__ bf16x8 lds16(const unsigned char* base, int off) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + off));
-}
-
 
 // Softmax state of one wave's 16 NT tokens for query head j = col: the logits
 // z[t][j] sit in rows t = 16 nt + 4 grp + e of zacc[nt].  Returns the wave's
@@ -167,7 +126,8 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
   const int grp = lane >> 4, col = lane & 15;
   const int logical = xcd_logical_block(blockIdx.x, a.padded_total);
   if (logical >= a.total) return;
-  const int bh = logical / a.n_split, split = logical % a.n_split;
+  // this launch covers splits [split_base, split_base + n_split_launch) of every head
+  const int bh = logical / a.n_split_launch, split = a.split_base + logical % a.n_split_launch;
   const int b = bh / a.hkv, h = bh % a.hkv;
   const int g = a.g;
   const size_t head = (size_t)b * a.hkv + h;

@@ -1,0 +1,638 @@
+// Producer/consumer form of the fused selective-reconstruction attention over
+// the selected chunks (gfx950).  It computes what the selected-chunk branch of
+// the 4-wave kernel in attend.hip computes, with the same operand layouts and
+// the same algebra of the value section (LowRAM review, key and value
+// paragraphs; explainer "How the method works"):
+//   K_pre = C[t] . B_blk, K_post = RoPE(K_pre, t), z = q . K_post,
+//   sum_t p_t V_t = W2 (sum_t p_t gelu(W1 K_pre + b1)) + b2 sum_t p_t + sum_t p_t R_t.
+// What changes is which wave does what, and when.
+//
+// In the 4-wave kernel every wave runs the MFMA-only reconstruction and then
+// the VALU-heavy value section of its own tokens, so the two co-resident
+// workgroups of a CU keep the matrix cores and the vector ALUs busy in turn
+// rather than together.  Here one workgroup of 8 waves holds a CU (about
+// 151 KiB of LDS) and works through tpw consecutive 128-token tiles of one
+// (sequence, KV head).  Waves 0-3 are producers and waves 4-7 consumers;
+// producer w and consumer w + 4 own the same 32 tokens (slot w) of every
+// tile.  Time runs in tile-steps of 8 steps with a workgroup barrier after
+// each step:
+//   producer, tile-step i      rebuild K_pre of tile i from the basis stream
+//                              (one r-slice of 64 per step); after the last
+//                              slice hand K_pre to the consumer through LDS,
+//                              then RoPE, QK and the running softmax, and
+//                              hand over the weights p
+//   consumer, tile-step i + 1  the value MLP of tile i from the W1/W2 stream
+//                              (32 hidden units per step), then the tile's
+//                              residual rows
+// so on every SIMD the reconstruction of one tile runs beside the value
+// section of the one before.  Producer and consumer run separate loops with
+// the same number of barriers; the role is a scalar (wave-uniform) branch.
+//
+// Running softmax.  A producer keeps (m, l) per query head of its slot over
+// the tiles so far.  For a new tile it takes m' = max(m, max_t z_t), sends the
+// consumer p_t = exp2(z_t - m') and alpha = exp2(m - m'), and sets
+// l = l alpha + sum_t p_t.  The consumer scales its output accumulator by
+// alpha before adding the tile.  At the end the 4 slots are merged by the
+// usual log-sum-exp rule, b2 l is added, and one partial (m, l, o) per query
+// head is written for the group; the merge kernel combines the groups and the
+// window splits.
+#include "attend_ops.h"
+#include "common.h"
+#include "internal.h"
+
+namespace lowram {
+
+constexpr int kPipeSlots = 4;                 // producer/consumer pairs
+constexpr int kPipeThreads = 2 * kPipeSlots * 64;
+constexpr int kPipeSteps = kHidden / 32;      // value stages = steps per tile-step
+constexpr int kHandSlot = 9216;               // per slot: K_pre operands (8 KiB), then p (1 KiB)
+constexpr int kHandP = 8192;
+static_assert(kAttSelNT == 2 && kAttChunksWG == 16, "tiles of 128 tokens, 32 per slot");
+
+struct PipeLds {
+  alignas(16) unsigned char bring[2][kStage];                   // basis stages (producers)
+  alignas(16) unsigned char mring[2][kStage];                   // W1/W2 stages (consumers)
+  alignas(16) unsigned char hand[2][kPipeSlots][kHandSlot];     // by tile parity; consumer residual rows too
+  alignas(16) float2 rope_off[kChunk][66];           // rotation by the offset 0..7 inside a chunk (padded row)
+  alignas(16) float2 rope_base[kPipeSlots][4][64];   // rotation to each chunk start, per producer (its 4 chunks)
+  f32x4 b1q[kHidden];                    // unit 32 c + row_perm32(p) at 32 c + p, x4 (an MFMA C operand)
+  float b2f[kHeadDim];
+  float alpha[2][kPipeSlots][16];        // accumulator rescale per query head, by tile parity
+  uint32_t rdesc[2][kPipeSlots][4];     // residual descriptors of each slot's 4 chunks, by tile parity
+  float mfin[kPipeSlots][16];
+  float lfin[kPipeSlots][16];
+};
+static_assert(sizeof(PipeLds) <= 160 * 1024, "one workgroup per CU");
+
+// One tile's softmax weights of a slot, relative to the running max, as an
+// fp16 MFMA operand.  z[t][j] sits in rows t = 16 nt + 4 grp + e of zacc[nt]
+// (column j = lane % 16).
+__device__ __forceinline__ void pipe_softmax(const f32x4 (&zacc)[2], int nvalid, float scale_log2, int grp,
+                                             float& mrun, float& lrun, float& alpha, f16x8& pa) {
+  float p[2][4];
+  float m = -__builtin_huge_valf();
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * nt + 4 * grp + e;
+      p[nt][e] = t < nvalid ? zacc[nt][e] * scale_log2 : -__builtin_huge_valf();
+      m = fmaxf(m, p[nt][e]);
+    }
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  const float mnew = fmaxf(mrun, m);
+  const float msafe = mnew == -__builtin_huge_valf() ? 0.f : mnew;
+  float lsum = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[nt][e] = __builtin_amdgcn_exp2f(p[nt][e] - msafe);
+      lsum += p[nt][e];
+    }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  alpha = mrun == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(mrun - mnew);
+  lrun = lrun * alpha + lsum;
+  mrun = mnew;
+  pa = pack8h(f32x4{p[0][0], p[0][1], p[0][2], p[0][3]}, f32x4{p[1][0], p[1][1], p[1][2], p[1][3]});
+}
+
+template <int RANK, bool CI4, bool RI4>
+__global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const AttendArgs a) {
+  __shared__ PipeLds L;
+  constexpr int NR = RANK / 64;                 // basis stages per tile
+  constexpr int NS = kPipeSteps;                // steps per tile-step
+  static_assert(NR >= 1 && NR <= NS, "rank 64 .. 512");
+  constexpr int SL = NR < 2 ? NR : 2;           // basis stage registers run SL stages ahead
+  constexpr int LG = NR - 1 < 2 ? NR - 1 : 2;   // coefficient gathers run LG stages ahead (0: same step)
+  constexpr int NT = 2;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: the role branch is uniform
+  const int grp = lane >> 4, col = lane & 15;
+  const bool producer = wave < kPipeSlots;
+  const int slot = wave & (kPipeSlots - 1), rt = tid & 255;
+  const int logical = xcd_logical_block(blockIdx.x, a.pipe_padded);
+  if (logical >= a.pipe_total) return;
+  const int bh = logical / a.n_grp, gx = logical % a.n_grp;
+  const int b = bh / a.hkv, h = bh % a.hkv;
+  const int g = a.g;
+  const size_t head = (size_t)b * a.hkv + h;
+  const int cseq = b * a.cache_bmul;             // cache arrays: per sequence, or one shared context
+  const size_t chead = (size_t)cseq * a.hkv + h;
+  const int tile0 = gx * a.tpw;
+  const int ntiles = min(a.tpw, a.pipe_tiles - tile0);
+  const int32_t* selh = a.sel + head * (size_t)a.k_eff;
+  // chunk id at selection position i (clamped into the list and the prefix)
+  auto chunk_at = [&](int i) { return min(max(selh[min(i, a.k_eff - 1)], 0), a.n_chunks - 1); };
+  // valid tokens of this slot in local tile i
+  auto slot_valid = [&](int i) {
+    const int nch = min(kAttChunksWG, a.k_eff - (tile0 + i) * kAttChunksWG);
+    return max(0, min(32, (nch - 4 * slot) * kChunk));
+  };
+
+  // tables
+  if (tid < kHidden) {
+    const float v = bf16_to_f32(a.b1[chead * kHidden + (tid & ~31) + row_perm32(tid & 31)]);
+    L.b1q[tid] = f32x4{v, v, v, v};
+  } else if (tid < kHidden + kHeadDim) {
+    L.b2f[tid - kHidden] = bf16_to_f32(a.b2[chead * kHeadDim + tid - kHidden]);
+  }
+  L.rope_off[tid >> 6][tid & 63] = rot_of((double)(tid >> 6) * a.inv_freq[tid & 63]);
+
+  if (producer) {
+    // ===================================================================== producer
+    const __amdgpu_buffer_rsrc_t bas = buffer_rsrc(a.basis + chead * (size_t)kHeadDim * RANK, kHeadDim * RANK * 2);
+    // basis stage s = columns [64 s, 64 s + 64), 128 rows in pi order, two rows per
+    // 256-byte line, 16-byte pieces XOR-swizzled by the line index
+    const int r0 = rt >> 3, pb = rt & 7;
+    const uint32_t bas_goff = (uint32_t)((row_perm32(r0) * RANK + 8 * pb) * 2);
+    const int bas_loff = (r0 >> 1) * 256 + ((((r0 & 1) << 3) | pb) ^ ((r0 >> 1) & 15)) * 16;
+    auto stage_load = [&](int s, u32x4 (&r)[kStageLd]) {
+#pragma unroll
+      for (int u = 0; u < kStageLd; ++u) r[u] = buffer_ld16(bas, bas_goff, (32 * u * RANK + 64 * s) * 2);
+    };
+    auto stage_store = [&](int buf, const u32x4 (&r)[kStageLd]) {
+      unsigned char* dst = L.bring[buf];
+#pragma unroll
+      for (int u = 0; u < kStageLd; ++u) *reinterpret_cast<u32x4*>(dst + bas_loff + 4096 * u) = r[u];
+    };
+    // this lane's gather rows of local tile i: token 16 nt + col of the slot
+    auto tokens_of = [&](int i, int (&tk)[NT]) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        tk[nt] = chunk_at((tile0 + i) * kAttChunksWG + 4 * slot + 2 * nt + (col >> 3)) * kChunk + (col & 7);
+    };
+    bf16x8 cv[CI4 ? 1 : NR][2][NT];
+    u32x2 cq[CI4 ? NR : 1][NT];
+    float csc[CI4 ? NR : 1][NT];
+    auto gather = [&](int s, const int (&tk)[NT]) {
+      if constexpr (!CI4) {
+        const uint16_t* cb = static_cast<const uint16_t*>(a.coeff) + (size_t)cseq * a.prefix_cap * RANK;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            cv[s][ks][nt] = load_bf16x8(cb + (size_t)tk[nt] * RANK + 64 * s + 32 * ks + 8 * grp);
+      } else {
+        const uint8_t* cb = static_cast<const uint8_t*>(a.coeff) + (size_t)cseq * a.prefix_cap * (RANK / 2);
+        const uint16_t* sb = a.coeff_scale + (size_t)cseq * a.prefix_cap * (RANK / 32);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          cq[s][nt] = *reinterpret_cast<const u32x2*>(cb + (size_t)tk[nt] * (RANK / 2) + 32 * s + 8 * grp);
+          csc[s][nt] = f16_to_f32(sb[(size_t)tk[nt] * (RANK / 32) + 2 * s + (grp >> 1)]);
+        }
+      }
+    };
+    // recon A operand offsets (see attend.hip): k-step ks, m-tile parity q
+    int ra[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int p = CI4 ? 2 * grp + ks : 4 * ks + grp;
+        ra[ks][q] = (col >> 1) * 256 + ((((col & 1) ^ q) << 3) | (p ^ (col >> 1))) * 16;
+      }
+
+    // ---- prologue
+    u32x4 sreg[NR][kStageLd];
+    int tokA[NT], tokB[NT];
+    tokens_of(0, tokA);
+    const uint16_t* qh = a.q + ((size_t)b * a.hq + (size_t)h * g) * kHeadDim;
+    bf16x8 qp[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qp[ks] = col < g ? load_bf16x8(qh + col * kHeadDim + 32 * ks + 8 * grp) : zero_bf16x8();
+    double fb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) fb[k] = a.inv_freq[(lane & 15) * 4 + k];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) stage_load(s, sreg[s]);
+#pragma unroll
+    for (int s = 0; s < LG; ++s) gather(s, tokA);
+    {
+      const double pos = (double)chunk_at(tile0 * kAttChunksWG + 4 * slot + (lane >> 4)) * kChunk;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) L.rope_base[slot][lane >> 4][(lane & 15) * 4 + k] = rot_of(pos * fb[k]);
+    }
+    stage_store(0, sreg[0]);
+    float mrun = -__builtin_huge_valf(), lrun = 0.f;
+    __syncthreads();
+
+    f32x4 acc[NT][8];
+    const size_t desc_rows = (size_t)(a.prefix_cap / kChunk);
+    for (int i = 0; i < ntiles; ++i) {
+      int rc_next = 0;
+      uint32_t rdv = 0;
+      float2 rot_next[4];  // rotations to the next tile's chunk starts (written after this tile's RoPE)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (s < NR) {
+          if (s == 0) {
+            tokens_of(i + 1, tokB);  // clamped: harmless past the last tile
+            rc_next = chunk_at((tile0 + i + 1) * kAttChunksWG + 4 * slot + (lane >> 4));
+            // residual descriptors of this tile's 4 chunks (lane k < 4: chunk k),
+            // handed to the consumer with K_pre; token 0 of chunk k sits in
+            // tokA[k / 2] of lane 8 (k % 2)
+            const int c0 = __shfl(tokA[0], 8 * (lane & 1)), c1 = __shfl(tokA[1], 8 * (lane & 1));
+            if (lane < 4) rdv = a.res_desc[chead * desc_rows + ((lane & 2) ? c1 : c0) / kChunk];
+          }
+          if constexpr (LG == 0) gather(s, tokA);  // rank 64: the stage's own rows
+          __builtin_amdgcn_sched_barrier(0);
+
+          if (s == 0) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+              for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          const unsigned char* sb = L.bring[(i * NR + s) & 1];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 bop[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              if constexpr (!CI4) bop[nt] = cv[s][ks][nt];
+              else bop[nt] = dequant8(cq[s][nt][ks], csc[s][nt]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+              const bf16x8 aop = lds16(sb, ra[ks][mt & 1] + 2048 * mt);
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mfma16(aop, bop[nt], acc[nt][mt]);
+            }
+          }
+          if (s == (NR > 1 ? 1 : 0)) {
+            // fp64 angle reduction for the next tile, off the tail of the last stage
+            const double pos = (double)rc_next * kChunk;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) rot_next[k] = rot_of(pos * fb[k]);
+          }
+
+          if (s == NR - 1) {
+            // ---- K_pre done: acc[nt][mt][e] = K_pre[t][d], t = 16 nt + col,
+            //      d = 32 (mt / 2) + 8 grp + 4 (mt % 2) + e.  Hand the bf16
+            //      operands to the consumer in its register layout.
+            unsigned char* hb = L.hand[i & 1][slot];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+              for (int ks = 0; ks < 4; ++ks)
+                *reinterpret_cast<u32x4*>(hb + (nt * 4 + ks) * 1024 + lane * 16) =
+                    __builtin_bit_cast(u32x4, pack8(acc[nt][2 * ks], acc[nt][2 * ks + 1]));
+            // RoPE: pair (d, d + 64) = m-tiles (mt, mt + 4) of the same lane.
+            // The frequencies p0 .. p0 + 3 of a tile row are 32 contiguous
+            // bytes of each table: two 16-byte reads per table and chunk.
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+              const int p0 = 32 * (mt >> 1) + 8 * grp + 4 * (mt & 1);
+              float of[8], bs[NT][8];
+              *reinterpret_cast<f32x4*>(&of[0]) = *reinterpret_cast<const f32x4*>(&L.rope_off[col & 7][p0]);
+              *reinterpret_cast<f32x4*>(&of[4]) = *reinterpret_cast<const f32x4*>(&L.rope_off[col & 7][p0 + 2]);
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) {
+                const int cs = 2 * nt + (col >> 3);
+                *reinterpret_cast<f32x4*>(&bs[nt][0]) = *reinterpret_cast<const f32x4*>(&L.rope_base[slot][cs][p0]);
+                *reinterpret_cast<f32x4*>(&bs[nt][4]) = *reinterpret_cast<const f32x4*>(&L.rope_base[slot][cs][p0 + 2]);
+              }
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float bc = bs[nt][2 * e], bsn = bs[nt][2 * e + 1], oc = of[2 * e], osn = of[2 * e + 1];
+                  const float c = bc * oc - bsn * osn;
+                  const float sn = bsn * oc + bc * osn;
+                  const float x1 = acc[nt][mt][e], x2 = acc[nt][mt + 4][e];
+                  acc[nt][mt][e] = x1 * c - x2 * sn;
+                  acc[nt][mt + 4][e] = x2 * c + x1 * sn;
+                }
+            }
+            // QK with K_post rounded to bf16, then the running softmax
+            f32x4 zacc[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int ks = 0; ks < 4; ++ks) z = mfma16(pack8(acc[nt][2 * ks], acc[nt][2 * ks + 1]), qp[ks], z);
+              zacc[nt] = z;
+            }
+            float alpha;
+            f16x8 pa;
+            pipe_softmax(zacc, slot_valid(i), a.scale_log2, grp, mrun, lrun, alpha, pa);
+            *reinterpret_cast<u32x4*>(hb + kHandP + lane * 16) = __builtin_bit_cast(u32x4, pa);
+            if (grp == 0) L.alpha[i & 1][slot][col] = alpha;
+            if (lane < 4) L.rdesc[i & 1][slot][lane] = rdv;
+            // this wave's rotation table for the next tile
+#pragma unroll
+            for (int k = 0; k < 4; ++k) L.rope_base[slot][lane >> 4][(lane & 15) * 4 + k] = rot_next[k];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) tokA[nt] = tokB[nt];
+          }
+          // Loads for later stages, issued after this step's products so that
+          // a full memory pipeline stalls nothing the step needs.  (Past the
+          // last tile they repeat the basis and read clamped rows: harmless,
+          // and they keep the code branch-free.)
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (SL > 0) stage_load((s + SL) % NR, sreg[(s + SL) % NR]);
+          if constexpr (LG > 0) {
+            if (s + LG < NR) gather(s + LG, tokA);
+            else gather(s + LG - NR, tokB);
+          }
+          // next basis stage into the buffer the previous step read
+          stage_store((i * NR + s + 1) & 1, sreg[(s + 1) % NR]);
+        }
+        __syncthreads();
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) __syncthreads();  // the consumers' last tile
+    if (grp == 0) {
+      L.mfin[slot][col] = mrun;
+      L.lfin[slot][col] = lrun;
+    }
+  } else {
+    // ===================================================================== consumer
+    // Software-pipelined by one value stage: step c runs GELU, PH and OUT of
+    // stage c - 1 (VALU work that overlaps the producer's reconstruction
+    // MFMAs and this wave's own next products) and then MLP1 of stage c.
+    // The last stage of a tile finishes at step 0 of the next tile-step (or
+    // after the loop).  Accordingly the W1 half of stage c is stored at the
+    // end of step c - 1 and read at step c, the W2 half stored at the end of
+    // step c and read at step c + 1, each half in a ring of two buffers.
+    const __amdgpu_buffer_rsrc_t w1r = buffer_rsrc(a.w1 + chead * (size_t)kHidden * kHeadDim, kHidden * kHeadDim * 2);
+    const __amdgpu_buffer_rsrc_t w2r = buffer_rsrc(a.w2 + chead * (size_t)kHeadDim * kHidden, kHeadDim * kHidden * 2);
+    // stage c: W1 rows [32 c, 32 c + 32) in pi order (8 KiB at offset 0 of a
+    // ring buffer), W2 columns [32 c, 32 c + 32) (natural, four rows per
+    // 256-byte line, 8 KiB at offset 8192)
+    const int w1row = rt >> 4, w1p = rt & 15;
+    const uint32_t w1_goff = (uint32_t)(((8 * ((w1row >> 2) & 3) + (w1row & 3)) * kHeadDim + 8 * w1p) * 2);
+    const int w1_loff = w1row * 256 + (w1p ^ (w1row & 15)) * 16;
+    const uint32_t w2_goff = (uint32_t)(((rt >> 2) * kHidden + 8 * (rt & 3)) * 2);
+    const int w2_loff = 8192 + (rt >> 4) * 256 + ((rt & 15) ^ ((rt >> 4) & 15)) * 16;
+    auto w1_load = [&](int c, u32x4 (&r)[2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) r[u] = buffer_ld16(w1r, w1_goff, (32 * c + 4 * u) * kHeadDim * 2);
+    };
+    auto w2_load = [&](int c, u32x4 (&r)[2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) r[u] = buffer_ld16(w2r, w2_goff, (u * 64 * kHidden + 32 * c) * 2);
+    };
+    auto w1_store = [&](int buf, const u32x4 (&r)[2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(L.mring[buf] + w1_loff + 4096 * u) = r[u];
+    };
+    auto w2_store = [&](int buf, const u32x4 (&r)[2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(L.mring[buf] + w2_loff + 4096 * u) = r[u];
+    };
+    // W1 position row 16 hn + col, piece 4 ks + grp; W2 row 16 nd + col, piece grp
+    int rw1[4], rw2[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) rw1[s] = col * 256 + ((4 * s + grp) ^ col) * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      rw2[q] = 8192 + (col >> 2) * 256 + ((((col & 3) ^ q) << 2) | (grp ^ (col >> 2))) * 16;
+
+    u32x4 w1reg[NS][2], w2reg[NS][2];
+    w1_load(0, w1reg[0]);
+    w1_load(1, w1reg[1]);
+    w2_load(0, w2reg[0]);
+    w1_store(0, w1reg[0]);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) __syncthreads();  // the producers' first tile
+
+    f32x4 oacc[8];
+#pragma unroll
+    for (int nd = 0; nd < 8; ++nd) oacc[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 hprev[NT][2];  // MLP1 of the previous stage, before GELU
+    f16x8 pa;            // softmax weights of the current tile (fp16: the PH product)
+    // GELU, PH and OUT of stage cs (W2 in ring buffer cs & 1):
+    //   PH  D[h][j] = gelu(hid)^T[h][t] x p^T[t][j];  OUT D[d][j] += W2[d][h] x PH[h][j]
+    auto finish_stage = [&](int cs) {
+      f32x4 pht[2];
+#pragma unroll
+      for (int hn = 0; hn < 2; ++hn) pht[hn] = mfma16h(gelu8_h(hprev[0][hn], hprev[1][hn]), pa, f32x4{0.f, 0.f, 0.f, 0.f});
+      const bf16x8 hbv = pack8(pht[0], pht[1]);
+      const unsigned char* sb = L.mring[cs & 1];
+#pragma unroll
+      for (int nd = 0; nd < 8; ++nd) oacc[nd] = mfma16(lds16(sb, rw2[nd & 3] + 1024 * nd), hbv, oacc[nd]);
+    };
+    constexpr int RL = RI4 ? 2 : 8;  // 16-byte residual pieces per lane
+    for (int i = 0; i < ntiles; ++i) {
+      unsigned char* hb = L.hand[i & 1][slot];
+      bf16x8 kpre_b[NT][4];
+      bf16x8 pab;  // the softmax weights in bf16 (the residual product)
+      u32x4 rres[RL];
+      u32x2 rsc = {0u, 0u};
+#pragma unroll
+      for (int c = 0; c < NS; ++c) {
+        __builtin_amdgcn_sched_barrier(0);
+
+        if (c == 0) {
+          if (i > 0) finish_stage(NS - 1);  // the previous tile's last stage (its p still in pa)
+          // the producer's handoff of this tile; rescale the accumulator
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+              kpre_b[nt][ks] = lds16(hb, (nt * 4 + ks) * 1024 + lane * 16);
+          pa = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(hb + kHandP + lane * 16));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pab[e] = (__bf16)(float)pa[e];
+          const float alpha = L.alpha[i & 1][slot][col];
+#pragma unroll
+          for (int nd = 0; nd < 8; ++nd) oacc[nd] *= alpha;
+        } else {
+          finish_stage(c - 1);
+        }
+        // MLP1 of stage c: D[t][h] = K_pre[t][d] x W1^T[d][h] (b1 initial value),
+        // hidden units [32 c, 32 c + 32)
+        {
+          const unsigned char* sb = L.mring[c & 1];
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int hn = 0; hn < 2; ++hn) {
+              const bf16x8 bop = lds16(sb, rw1[ks] + 4096 * hn);
+              const f32x4 bias = L.b1q[32 * c + 16 * hn + col];
+#pragma unroll
+              for (int tt = 0; tt < NT; ++tt)
+                hprev[tt][hn] = mfma16(kpre_b[tt][ks], bop, ks == 0 ? bias : hprev[tt][hn]);
+            }
+          }
+        }
+
+        if (c == NS - 1) {
+          // ---- residuals: rows -> this slot's handoff region (read at step 0,
+          //      not written again before the tile after next), then
+          //      OUT += R^T[d][t] x p^T[t][j]
+          if constexpr (!RI4) {
+#pragma unroll
+            for (int u = 0; u < RL; ++u)
+              *reinterpret_cast<u32x4*>(hb + (4 * u + (lane >> 4)) * kResRow + (lane & 15) * 16) = rres[u];
+#pragma unroll
+            for (int nd = 0; nd < 8; ++nd) {
+              bf16x8 rop;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int t = e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4;
+                rop[e] = *reinterpret_cast<const __bf16*>(hb + t * kResRow + (16 * nd + col) * 2);
+              }
+              oacc[nd] = mfma16(rop, pab, oacc[nd]);
+            }
+          } else {
+#pragma unroll
+            for (int u = 0; u < RL; ++u)
+              *reinterpret_cast<u32x4*>(hb + (16 * u + (lane >> 2)) * kResRow4 + (lane & 3) * 16) = rres[u];
+            if (lane < 32) *reinterpret_cast<u32x2*>(hb + lane * kResRow4 + 64) = rsc;
+            auto resid_at = [&](int t, int d) -> float {
+              const uint32_t byte = hb[t * kResRow4 + (d >> 1)];
+              const int code = static_cast<int>(((byte >> (4 * (d & 1))) & 0xFu) ^ 8u) - 8;
+              const uint16_t sc = *reinterpret_cast<const uint16_t*>(hb + t * kResRow4 + 64 + (d >> 5) * 2);
+              return static_cast<float>(code) * f16_to_f32(sc);
+            };
+#pragma unroll
+            for (int nd = 0; nd < 8; ++nd) {
+              f32x4 lo, hi;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                lo[e] = resid_at(4 * grp + e, 16 * nd + col);
+                hi[e] = resid_at(16 + 4 * grp + e, 16 * nd + col);
+              }
+              oacc[nd] = mfma16(pack8(lo, hi), pab, oacc[nd]);
+            }
+          }
+        }
+        // Loads for later steps after this step's work (see the producer):
+        // the same weights every tile, W1 two stages ahead and W2 one, and
+        // the tile's residual rows for step NS - 1
+        __builtin_amdgcn_sched_barrier(0);
+        w1_load((c + 2) % NS, w1reg[(c + 2) % NS]);
+        w2_load((c + 1) % NS, w2reg[(c + 1) % NS]);
+        if (c == 2) {
+          // this slot's residual rows (zeros where a token has none: reads
+          // past the end of the buffer return 0); descriptors from the producer
+          auto row_of = [&](uint32_t dsc, int t) -> int {
+            const int bit = t & 7;
+            if (!((dsc >> bit) & 1u)) return -1;
+            return (int)(dsc >> 8) + __popc(dsc & ((1u << bit) - 1u) & 0xFFu);
+          };
+          if constexpr (!RI4) {
+            const uint32_t nbytes = (uint32_t)a.n_resid * kHeadDim * 2;
+            const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(
+                static_cast<const uint16_t*>(a.res_val) + chead * (size_t)a.n_resid * kHeadDim, nbytes);
+#pragma unroll
+            for (int u = 0; u < RL; ++u) {
+              const int t = 4 * u + (lane >> 4);
+              const int rn = row_of(L.rdesc[i & 1][slot][u >> 1], t);
+              rres[u] = buffer_ld16(rv, rn >= 0 ? (uint32_t)rn * 256 + (lane & 15) * 16 : nbytes, 0);
+            }
+          } else {
+            const uint32_t nbytes = (uint32_t)a.n_resid * (kHeadDim / 2);
+            const uint32_t sbytes = (uint32_t)a.n_resid * (kHeadDim / 32) * 2;
+            const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(
+                static_cast<const uint8_t*>(a.res_val) + chead * (size_t)a.n_resid * (kHeadDim / 2), nbytes);
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
+                a.res_scale + chead * (size_t)a.n_resid * (kHeadDim / 32), sbytes);
+#pragma unroll
+            for (int u = 0; u < RL; ++u) {
+              const int t = 16 * u + (lane >> 2);
+              const int rn = row_of(L.rdesc[i & 1][slot][2 * u + (lane >> 5)], t);
+              rres[u] = buffer_ld16(rv, rn >= 0 ? (uint32_t)rn * 64 + (lane & 3) * 16 : nbytes, 0);
+            }
+            const int t = lane & 31;
+            const int rn = row_of(L.rdesc[i & 1][slot][t >> 3], t);
+            rsc = __builtin_amdgcn_raw_buffer_load_b64(rs, rn >= 0 ? (uint32_t)rn * 8 : sbytes, 0, 0);
+          }
+        }
+        // W1 of stage c + 1 into the buffer step c - 1 read; W2 of stage c
+        // into the buffer step c - 1 read (stage c - 2)
+        w1_store((c + 1) & 1, w1reg[(c + 1) % NS]);
+        w2_store(c & 1, w2reg[c]);
+        __syncthreads();
+      }
+    }
+    finish_stage(NS - 1);  // the last tile's last stage (W2 buffer not written again)
+    // this slot's o^T[d][j] (rows d = 16 nd + 4 grp + e, column j = col) -> LDS
+    float* mo = reinterpret_cast<float*>(&L.hand[0][0][0]);
+    if (col < g)
+#pragma unroll
+      for (int nd = 0; nd < 8; ++nd)
+        *reinterpret_cast<f32x4*>(&mo[(slot * 16 + col) * kHeadDim + 16 * nd + 4 * grp]) = oacc[nd];
+  }
+  __syncthreads();
+
+  // ================================= merge the 4 slots, add b2 l, write the partial
+  const float* mo = reinterpret_cast<const float*>(&L.hand[0][0][0]);
+  float* part = a.part + (head * (size_t)a.n_split + gx) * g * kPartStride;
+  for (int idx = tid; idx < g * kHeadDim; idx += kPipeThreads) {
+    const int j = idx / kHeadDim, d = idx % kHeadDim;
+    float M = -__builtin_huge_valf();
+#pragma unroll
+    for (int w = 0; w < kPipeSlots; ++w) M = fmaxf(M, L.mfin[w][j]);
+    float lt = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kPipeSlots; ++w) {
+      const float mw = L.mfin[w][j];
+      const float sc = mw == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      lt += L.lfin[w][j] * sc;
+      o += mo[(w * 16 + j) * kHeadDim + d] * sc;
+    }
+    if (d == 0) {
+      part[j * kPartStride] = M;
+      part[j * kPartStride + 1] = lt;
+    }
+    part[j * kPartStride + 2 + d] = fmaf(L.b2f[d], lt, o);
+  }
+}
+
+void plan_pipe_groups(int heads, int n_tiles, int* n_grp, int* tpw) {
+  // A workgroup of t tiles lives about t + 1 tile-steps (the pipeline fills
+  // and drains once); workgroups run one per CU in rounds.  Take the t with
+  // the least rounds x (t + 1), the smallest on ties.
+  constexpr long kCUs = 256;
+  long best = -1;
+  int bt = 1;
+  for (int t = 1; t <= n_tiles; ++t) {
+    const long groups = (n_tiles + t - 1) / t;
+    const long rounds = ((long)heads * groups + kCUs - 1) / kCUs;
+    const long cost = rounds * (t + 1);
+    if (best < 0 || cost < best) {
+      best = cost;
+      bt = t;
+    }
+  }
+  *tpw = bt;
+  *n_grp = n_tiles > 0 ? (n_tiles + bt - 1) / bt : 0;
+}
+
+template <int RANK>
+static hipError_t launch_pipe_rank(const AttendArgs& a, bool ci4, bool ri4, hipStream_t st) {
+  const dim3 grid(a.pipe_padded), block(kPipeThreads);
+  if (!ci4 && !ri4) hipLaunchKernelGGL((attend_pipe_kernel<RANK, false, false>), grid, block, 0, st, a);
+  else if (ci4 && ri4) hipLaunchKernelGGL((attend_pipe_kernel<RANK, true, true>), grid, block, 0, st, a);
+  else if (ci4) hipLaunchKernelGGL((attend_pipe_kernel<RANK, true, false>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((attend_pipe_kernel<RANK, false, true>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_pipe(const AttendArgs& a, int rank, bool ci4, bool ri4, hipStream_t st) {
+  if (a.pipe_total == 0) return hipSuccess;
+  switch (rank) {
+    case 128: return launch_pipe_rank<128>(a, ci4, ri4, st);
+    case 256: return launch_pipe_rank<256>(a, ci4, ri4, st);
+    case 512: return launch_pipe_rank<512>(a, ci4, ri4, st);
+    default: break;
+  }
+  // rank 64: the int4 coefficient path needs rank % 128 == 0
+  if (ci4) return hipErrorInvalidValue;
+  const dim3 grid(a.pipe_padded), block(kPipeThreads);
+  if (ri4) hipLaunchKernelGGL((attend_pipe_kernel<64, false, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((attend_pipe_kernel<64, false, false>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace lowram

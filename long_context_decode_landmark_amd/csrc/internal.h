@@ -43,10 +43,25 @@ struct AttendArgs {
   int cache_bmul;  // 1: cache arrays per sequence; 0: one context shared by all nb queries
   int prefix_cap;  // coefficient rows per sequence (descriptor rows per head = prefix_cap / S)
   int window_cap;  // window rows per head
+  // partial slots per head: n_split.  The 4-wave kernel treats slots below
+  // n_sel_tiles as selection tiles and the rest as window tiles; one launch of
+  // it covers slots [split_base, split_base + n_split_launch) of every head
+  // (total = heads * n_split_launch workgroups, padded to a multiple of 8).
   int n_sel_tiles, n_win_tiles, n_split, total, padded_total;
+  int split_base, n_split_launch;
+  // producer/consumer kernel: the pipe_tiles selection tiles of a head are cut
+  // into n_grp groups of tpw consecutive tiles (the last may be shorter), one
+  // workgroup and one partial slot (slot = group) each
+  int pipe_tiles, n_grp, tpw, pipe_total, pipe_padded;
   float scale_log2;
   double inv_freq[64];
 };
+
+// Tiles per group and groups per head for the producer/consumer attention
+// kernel (one workgroup per CU at a time).
+void plan_pipe_groups(int heads, int n_tiles, int* n_grp, int* tpw);
+hipError_t launch_attend_pipe(const AttendArgs& a, int rank, bool coeff_int4, bool resid_int4,
+                              hipStream_t st);
 
 // cache_bmul: 1 = landmarks / candidate ids per sequence, 0 = one shared context
 // lm_rows: landmark rows per (sequence, KV head) (>= n_cand)
