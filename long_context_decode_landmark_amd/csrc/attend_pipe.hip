@@ -53,8 +53,12 @@ struct PipeLds {
   alignas(16) unsigned char bring[2][kStage];                   // basis stages (producers)
   alignas(16) unsigned char mring[2][kStage];                   // W1/W2 stages (consumers)
   alignas(16) unsigned char hand[2][kPipeSlots][kHandSlot];     // by tile parity; consumer residual rows too
-  alignas(16) float2 rope_off[kChunk][66];           // rotation by the offset 0..7 inside a chunk (padded row)
-  alignas(16) float2 rope_base[kPipeSlots][4][64];   // rotation to each chunk start, per producer (its 4 chunks)
+  // RoPE rotations as fp16 (cos, sin) tables, frequency-contiguous: by the
+  // offset 0..7 inside a chunk, and to each chunk start (per producer, its 4 chunks)
+  alignas(16) _Float16 rope_oc[kChunk][64];
+  alignas(16) _Float16 rope_os[kChunk][64];
+  alignas(16) _Float16 rope_bc[kPipeSlots][4][64];
+  alignas(16) _Float16 rope_bs[kPipeSlots][4][64];
   f32x4 b1q[kHidden];                    // unit 32 c + row_perm32(p) at 32 c + p, x4 (an MFMA C operand)
   float b2f[kHeadDim];
   float alpha[2][kPipeSlots][16];        // accumulator rescale per query head, by tile parity
@@ -140,7 +144,13 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
   } else if (tid < kHidden + kHeadDim) {
     L.b2f[tid - kHidden] = bf16_to_f32(a.b2[chead * kHeadDim + tid - kHidden]);
   }
-  L.rope_off[tid >> 6][tid & 63] = rot_of((double)(tid >> 6) * a.inv_freq[tid & 63]);
+  if (tid < 256) {
+    // offset tables: two consecutive frequencies per thread, as fp16 pairs
+    const int io = tid >> 5, p = 2 * (tid & 31);
+    const float2 r0 = rot_of((double)io * a.inv_freq[p]), r1 = rot_of((double)io * a.inv_freq[p + 1]);
+    reinterpret_cast<h2*>(&L.rope_oc[io][p])[0] = __builtin_convertvector(f32x2{r0.x, r1.x}, h2);
+    reinterpret_cast<h2*>(&L.rope_os[io][p])[0] = __builtin_convertvector(f32x2{r0.y, r1.y}, h2);
+  }
 
   if (producer) {
     // ===================================================================== producer
@@ -201,13 +211,29 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     int tokA[NT], tokB[NT];
     tokens_of(0, tokA);
     const uint16_t* qh = a.q + ((size_t)b * a.hq + (size_t)h * g) * kHeadDim;
-    bf16x8 qp[4];
+    f16x8 qp[4];  // the queries as fp16 operands of QK
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qp[ks] = col < g ? load_bf16x8(qh + col * kHeadDim + 32 * ks + 8 * grp) : zero_bf16x8();
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 qb = col < g ? load_bf16x8(qh + col * kHeadDim + 32 * ks + 8 * grp) : zero_bf16x8();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qp[ks][e] = (_Float16)(float)qb[e];
+    }
     double fb[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) fb[k] = a.inv_freq[(lane & 15) * 4 + k];
+    // this wave's rotation table row: chunk lane / 16, frequencies 4 (lane % 16) + k,
+    // written as fp16 pairs, the access type the RoPE reads use
+    auto store_rot = [&](float2 r0, float2 r1, float2 r2, float2 r3) {
+      const h2 c01 = __builtin_convertvector(f32x2{r0.x, r1.x}, h2), c23 = __builtin_convertvector(f32x2{r2.x, r3.x}, h2);
+      const h2 s01 = __builtin_convertvector(f32x2{r0.y, r1.y}, h2), s23 = __builtin_convertvector(f32x2{r2.y, r3.y}, h2);
+      h2* pc = reinterpret_cast<h2*>(&L.rope_bc[slot][lane >> 4][(lane & 15) * 4]);
+      h2* ps = reinterpret_cast<h2*>(&L.rope_bs[slot][lane >> 4][(lane & 15) * 4]);
+      pc[0] = c01;
+      pc[1] = c23;
+      ps[0] = s01;
+      ps[1] = s23;
+    };
+    float2 rot_next[4];  // rotations to the chunk starts: tile 0 here, later the next tile's
 #pragma unroll
     for (int s = 0; s < SL; ++s) stage_load(s, sreg[s]);
 #pragma unroll
@@ -215,7 +241,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     {
       const double pos = (double)chunk_at(tile0 * kAttChunksWG + 4 * slot + (lane >> 4)) * kChunk;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) L.rope_base[slot][lane >> 4][(lane & 15) * 4 + k] = rot_of(pos * fb[k]);
+      for (int k = 0; k < 4; ++k) rot_next[k] = rot_of(pos * fb[k]);
+      store_rot(rot_next[0], rot_next[1], rot_next[2], rot_next[3]);
     }
     stage_store(0, sreg[0]);
     float mrun = -__builtin_huge_valf(), lrun = 0.f;
@@ -226,7 +253,6 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     for (int i = 0; i < ntiles; ++i) {
       int rc_next = 0;
       uint32_t rdv = 0;
-      float2 rot_next[4];  // rotations to the next tile's chunk starts (written after this tile's RoPE)
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         if (s < NR) {
@@ -248,7 +274,15 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 #pragma unroll
               for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
+          // all 16 basis operands of the stage are read first, so that the
+          // matrix core is not left waiting on one LDS round trip per pair
           const unsigned char* sb = L.bring[(i * NR + s) & 1];
+          bf16x8 aop[2][8];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) aop[ks][mt] = lds16(sb, ra[ks][mt & 1] + 2048 * mt);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             bf16x8 bop[NT];
@@ -258,17 +292,19 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
               else bop[nt] = dequant8(cq[s][nt][ks], csc[s][nt]);
             }
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-              const bf16x8 aop = lds16(sb, ra[ks][mt & 1] + 2048 * mt);
+            for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-              for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mfma16(aop, bop[nt], acc[nt][mt]);
-            }
+              for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mfma16(aop[ks][mt], bop[nt], acc[nt][mt]);
           }
           if (s == (NR > 1 ? 1 : 0)) {
             // fp64 angle reduction for the next tile, off the tail of the last stage
             const double pos = (double)rc_next * kChunk;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) rot_next[k] = rot_of(pos * fb[k]);
+            for (int k = 0; k < 4; ++k) {
+              rot_next[k] = rot_of(pos * fb[k]);
+              // keep the work here (the compiler would otherwise sink it into the tail)
+              asm volatile("" : "+v"(rot_next[k].x), "+v"(rot_next[k].y));
+            }
           }
 
           if (s == NR - 1) {
@@ -282,40 +318,46 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
               for (int ks = 0; ks < 4; ++ks)
                 *reinterpret_cast<u32x4*>(hb + (nt * 4 + ks) * 1024 + lane * 16) =
                     __builtin_bit_cast(u32x4, pack8(acc[nt][2 * ks], acc[nt][2 * ks + 1]));
-            // RoPE: pair (d, d + 64) = m-tiles (mt, mt + 4) of the same lane.
-            // The frequencies p0 .. p0 + 3 of a tile row are 32 contiguous
-            // bytes of each table: two 16-byte reads per table and chunk.
+            // RoPE on packed fp16 pairs of consecutive frequencies: pair (d, d + 64)
+            // = m-tiles (mt, mt + 4) of the same lane; the rotation is the chunk
+            // start's composed with the offset's.  K_post stays fp16 (relative
+            // error ~3 2^-11, below the 2^-9 of a bf16 operand) and feeds an fp16 QK.
+            h2 kp[NT][8][2];  // K_post, [nt][mt][e pair]
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
               const int p0 = 32 * (mt >> 1) + 8 * grp + 4 * (mt & 1);
-              float of[8], bs[NT][8];
-              *reinterpret_cast<f32x4*>(&of[0]) = *reinterpret_cast<const f32x4*>(&L.rope_off[col & 7][p0]);
-              *reinterpret_cast<f32x4*>(&of[4]) = *reinterpret_cast<const f32x4*>(&L.rope_off[col & 7][p0 + 2]);
+              const h2* oc = reinterpret_cast<const h2*>(&L.rope_oc[col & 7][p0]);
+              const h2* os = reinterpret_cast<const h2*>(&L.rope_os[col & 7][p0]);
 #pragma unroll
               for (int nt = 0; nt < NT; ++nt) {
                 const int cs = 2 * nt + (col >> 3);
-                *reinterpret_cast<f32x4*>(&bs[nt][0]) = *reinterpret_cast<const f32x4*>(&L.rope_base[slot][cs][p0]);
-                *reinterpret_cast<f32x4*>(&bs[nt][4]) = *reinterpret_cast<const f32x4*>(&L.rope_base[slot][cs][p0 + 2]);
-              }
+                const h2* bc = reinterpret_cast<const h2*>(&L.rope_bc[slot][cs][p0]);
+                const h2* bs = reinterpret_cast<const h2*>(&L.rope_bs[slot][cs][p0]);
 #pragma unroll
-              for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const float bc = bs[nt][2 * e], bsn = bs[nt][2 * e + 1], oc = of[2 * e], osn = of[2 * e + 1];
-                  const float c = bc * oc - bsn * osn;
-                  const float sn = bsn * oc + bc * osn;
-                  const float x1 = acc[nt][mt][e], x2 = acc[nt][mt + 4][e];
-                  acc[nt][mt][e] = x1 * c - x2 * sn;
-                  acc[nt][mt + 4][e] = x2 * c + x1 * sn;
+                for (int q = 0; q < 2; ++q) {
+                  const h2 o_c = oc[q], o_s = os[q], b_c = bc[q], b_s = bs[q];
+                  const h2 c = __builtin_elementwise_fma(b_c, o_c, -(b_s * o_s));
+                  const h2 sn = __builtin_elementwise_fma(b_s, o_c, b_c * o_s);
+                  const h2 x1 = __builtin_convertvector(f32x2{acc[nt][mt][2 * q], acc[nt][mt][2 * q + 1]}, h2);
+                  const h2 x2 = __builtin_convertvector(f32x2{acc[nt][mt + 4][2 * q], acc[nt][mt + 4][2 * q + 1]}, h2);
+                  kp[nt][mt][q] = __builtin_elementwise_fma(x1, c, -(x2 * sn));
+                  kp[nt][mt + 4][q] = __builtin_elementwise_fma(x2, c, x1 * sn);
                 }
+              }
             }
-            // QK with K_post rounded to bf16, then the running softmax
+            // QK (fp16 operands), then the running softmax
             f32x4 zacc[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
               f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-              for (int ks = 0; ks < 4; ++ks) z = mfma16(pack8(acc[nt][2 * ks], acc[nt][2 * ks + 1]), qp[ks], z);
+              for (int ks = 0; ks < 4; ++ks) {
+                const f16x8 kop = __builtin_shufflevector(
+                    __builtin_shufflevector(kp[nt][2 * ks][0], kp[nt][2 * ks][1], 0, 1, 2, 3),
+                    __builtin_shufflevector(kp[nt][2 * ks + 1][0], kp[nt][2 * ks + 1][1], 0, 1, 2, 3),
+                    0, 1, 2, 3, 4, 5, 6, 7);
+                z = mfma16h(kop, qp[ks], z);
+              }
               zacc[nt] = z;
             }
             float alpha;
@@ -325,8 +367,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
             if (grp == 0) L.alpha[i & 1][slot][col] = alpha;
             if (lane < 4) L.rdesc[i & 1][slot][lane] = rdv;
             // this wave's rotation table for the next tile
-#pragma unroll
-            for (int k = 0; k < 4; ++k) L.rope_base[slot][lane >> 4][(lane & 15) * 4 + k] = rot_next[k];
+            store_rot(rot_next[0], rot_next[1], rot_next[2], rot_next[3]);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) tokA[nt] = tokB[nt];
           }
@@ -407,18 +448,27 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     f32x4 oacc[8];
 #pragma unroll
     for (int nd = 0; nd < 8; ++nd) oacc[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 hprev[NT][2];  // MLP1 of the previous stage, before GELU
-    f16x8 pa;            // softmax weights of the current tile (fp16: the PH product)
-    // GELU, PH and OUT of stage cs (W2 in ring buffer cs & 1):
+    f32x4 hacc[2][NT][2];  // MLP1 of stage c in hacc[c & 1] (before GELU)
+    f16x8 pa;              // softmax weights of the current tile (fp16: the PH product)
+    // GELU, PH and OUT of stage cs (MLP1 result in hacc[cs & 1], W2 operands
+    // already read), softmax weights pw:
     //   PH  D[h][j] = gelu(hid)^T[h][t] x p^T[t][j];  OUT D[d][j] += W2[d][h] x PH[h][j]
-    auto finish_stage = [&](int cs) {
+    auto finish_stage = [&](int cs, const bf16x8 (&w2op)[8], const f16x8& pw) {
+      const f32x4 lo[2] = {hacc[cs & 1][0][0], hacc[cs & 1][0][1]};
+      const f32x4 hi[2] = {hacc[cs & 1][1][0], hacc[cs & 1][1][1]};
+      f16x8 gl[2];
+      gelu16_h(lo, hi, gl);
       f32x4 pht[2];
 #pragma unroll
-      for (int hn = 0; hn < 2; ++hn) pht[hn] = mfma16h(gelu8_h(hprev[0][hn], hprev[1][hn]), pa, f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int hn = 0; hn < 2; ++hn) pht[hn] = mfma16h(gl[hn], pw, f32x4{0.f, 0.f, 0.f, 0.f});
       const bf16x8 hbv = pack8(pht[0], pht[1]);
+#pragma unroll
+      for (int nd = 0; nd < 8; ++nd) oacc[nd] = mfma16(w2op[nd], hbv, oacc[nd]);
+    };
+    auto read_w2 = [&](int cs, bf16x8 (&w2op)[8]) {
       const unsigned char* sb = L.mring[cs & 1];
 #pragma unroll
-      for (int nd = 0; nd < 8; ++nd) oacc[nd] = mfma16(lds16(sb, rw2[nd & 3] + 1024 * nd), hbv, oacc[nd]);
+      for (int nd = 0; nd < 8; ++nd) w2op[nd] = lds16(sb, rw2[nd & 3] + 1024 * nd);
     };
     constexpr int RL = RI4 ? 2 : 8;  // 16-byte residual pieces per lane
     for (int i = 0; i < ntiles; ++i) {
@@ -429,40 +479,51 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
       u32x2 rsc = {0u, 0u};
 #pragma unroll
       for (int c = 0; c < NS; ++c) {
-        __builtin_amdgcn_sched_barrier(0);
-
+        // ---- LDS operands first: MLP1 of stage c, OUT of stage c - 1, and at a
+        //      tile start the handoff (at the very first step the W2 read is unused)
+        bf16x8 w1op[4][2];
+        f32x4 b1v[2];
+        {
+          const unsigned char* sb = L.mring[c & 1];
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int hn = 0; hn < 2; ++hn) w1op[ks][hn] = lds16(sb, rw1[ks] + 4096 * hn);
+#pragma unroll
+          for (int hn = 0; hn < 2; ++hn) b1v[hn] = L.b1q[32 * c + 16 * hn + col];
+        }
+        bf16x8 w2op[8];  // W2 operands of the previous stage
+        read_w2((c + NS - 1) % NS, w2op);
+        f16x8 pnew;
+        float alpha = 1.f;
         if (c == 0) {
-          if (i > 0) finish_stage(NS - 1);  // the previous tile's last stage (its p still in pa)
-          // the producer's handoff of this tile; rescale the accumulator
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
               kpre_b[nt][ks] = lds16(hb, (nt * 4 + ks) * 1024 + lane * 16);
-          pa = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(hb + kHandP + lane * 16));
+          pnew = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(hb + kHandP + lane * 16));
+          alpha = L.alpha[i & 1][slot][col];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- MLP1 of stage c: D[t][h] = K_pre[t][d] x W1^T[d][h] (b1 initial value),
+        //      hidden units [32 c, 32 c + 32); its matrix work runs under the GELU below
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int hn = 0; hn < 2; ++hn)
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+              hacc[c & 1][tt][hn] = mfma16(kpre_b[tt][ks], w1op[ks][hn], ks == 0 ? b1v[hn] : hacc[c & 1][tt][hn]);
+        // ---- the previous stage: GELU, PH, OUT (at a tile start: the previous
+        //      tile's last stage with that tile's weights, then the rescale)
+        if (c > 0 || i > 0) finish_stage((c + NS - 1) % NS, w2op, pa);
+        if (c == 0) {
+          pa = pnew;
 #pragma unroll
           for (int e = 0; e < 8; ++e) pab[e] = (__bf16)(float)pa[e];
-          const float alpha = L.alpha[i & 1][slot][col];
 #pragma unroll
           for (int nd = 0; nd < 8; ++nd) oacc[nd] *= alpha;
-        } else {
-          finish_stage(c - 1);
-        }
-        // MLP1 of stage c: D[t][h] = K_pre[t][d] x W1^T[d][h] (b1 initial value),
-        // hidden units [32 c, 32 c + 32)
-        {
-          const unsigned char* sb = L.mring[c & 1];
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-            for (int hn = 0; hn < 2; ++hn) {
-              const bf16x8 bop = lds16(sb, rw1[ks] + 4096 * hn);
-              const f32x4 bias = L.b1q[32 * c + 16 * hn + col];
-#pragma unroll
-              for (int tt = 0; tt < NT; ++tt)
-                hprev[tt][hn] = mfma16(kpre_b[tt][ks], bop, ks == 0 ? bias : hprev[tt][hn]);
-            }
-          }
         }
 
         if (c == NS - 1) {
@@ -473,6 +534,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 #pragma unroll
             for (int u = 0; u < RL; ++u)
               *reinterpret_cast<u32x4*>(hb + (4 * u + (lane >> 4)) * kResRow + (lane & 15) * 16) = rres[u];
+            // the reads below take the bytes just written under another type
+            asm volatile("" ::: "memory");
 #pragma unroll
             for (int nd = 0; nd < 8; ++nd) {
               bf16x8 rop;
@@ -488,6 +551,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
             for (int u = 0; u < RL; ++u)
               *reinterpret_cast<u32x4*>(hb + (16 * u + (lane >> 2)) * kResRow4 + (lane & 3) * 16) = rres[u];
             if (lane < 32) *reinterpret_cast<u32x2*>(hb + lane * kResRow4 + 64) = rsc;
+            asm volatile("" ::: "memory");  // the reads below take these bytes under other types
             auto resid_at = [&](int t, int d) -> float {
               const uint32_t byte = hb[t * kResRow4 + (d >> 1)];
               const int code = static_cast<int>(((byte >> (4 * (d & 1))) & 0xFu) ^ 8u) - 8;
@@ -555,7 +619,12 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
         __syncthreads();
       }
     }
-    finish_stage(NS - 1);  // the last tile's last stage (W2 buffer not written again)
+    {
+      // the last tile's last stage (its W2 buffer is not written again)
+      bf16x8 w2op[8];
+      read_w2(NS - 1, w2op);
+      finish_stage(NS - 1, w2op, pa);
+    }
     // this slot's o^T[d][j] (rows d = 16 nd + 4 grp + e, column j = col) -> LDS
     float* mo = reinterpret_cast<float*>(&L.hand[0][0][0]);
     if (col < g)
