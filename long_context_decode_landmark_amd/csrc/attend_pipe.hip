@@ -61,6 +61,7 @@ struct PipeLds {
   alignas(16) _Float16 rope_bs[kPipeSlots][4][64];
   f32x4 b1q[kHidden];                    // unit 32 c + row_perm32(p) at 32 c + p, x4 (an MFMA C operand)
   float b2f[kHeadDim];
+  double invf[64];                       // RoPE frequencies (read where needed: no registers held)
   float alpha[2][kPipeSlots][16];        // accumulator rescale per query head, by tile parity
   uint32_t rdesc[2][kPipeSlots][4];     // residual descriptors of each slot's 4 chunks, by tile parity
   float mfin[kPipeSlots][16];
@@ -130,7 +131,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
   const int ntiles = min(a.tpw, a.pipe_tiles - tile0);
   const int32_t* selh = a.sel + head * (size_t)a.k_eff;
   // chunk id at selection position i (clamped into the list and the prefix)
-  auto chunk_at = [&](int i) { return min(max(selh[min(i, a.k_eff - 1)], 0), a.n_chunks - 1); };
+  auto clamp_chunk = [&](int c) { return min(max(c, 0), a.n_chunks - 1); };
+  auto chunk_at = [&](int i) { return clamp_chunk(selh[min(i, a.k_eff - 1)]); };
   // valid tokens of this slot in local tile i
   auto slot_valid = [&](int i) {
     const int nch = min(kAttChunksWG, a.k_eff - (tile0 + i) * kAttChunksWG);
@@ -144,6 +146,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
   } else if (tid < kHidden + kHeadDim) {
     L.b2f[tid - kHidden] = bf16_to_f32(a.b2[chead * kHeadDim + tid - kHidden]);
   }
+  if (tid < 64) L.invf[tid] = a.inv_freq[tid];
   if (tid < 256) {
     // offset tables: two consecutive frequencies per thread, as fp16 pairs
     const int io = tid >> 5, p = 2 * (tid & 31);
@@ -210,6 +213,17 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     u32x4 sreg[NR][kStageLd];
     int tokA[NT], tokB[NT];
     tokens_of(0, tokA);
+    // raw chunk ids of the next tile (gather rows, rotation-table row): issued a
+    // tile ahead, carried through the loop and clamped at step 1, so that neither
+    // the compiler nor the in-order load counter ties them to a wait right away
+    int selN[NT], rcN;
+    auto load_next_ids = [&](int t) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        selN[nt] = selh[min((tile0 + t) * kAttChunksWG + 4 * slot + 2 * nt + (col >> 3), a.k_eff - 1)];
+      rcN = selh[min((tile0 + t) * kAttChunksWG + 4 * slot + (lane >> 4), a.k_eff - 1)];
+    };
+    load_next_ids(1);
     const uint16_t* qh = a.q + ((size_t)b * a.hq + (size_t)h * g) * kHeadDim;
     f16x8 qp[4];  // the queries as fp16 operands of QK
 #pragma unroll
@@ -218,9 +232,6 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 #pragma unroll
       for (int e = 0; e < 8; ++e) qp[ks][e] = (_Float16)(float)qb[e];
     }
-    double fb[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) fb[k] = a.inv_freq[(lane & 15) * 4 + k];
     // this wave's rotation table row: chunk lane / 16, frequencies 4 (lane % 16) + k,
     // written as fp16 pairs, the access type the RoPE reads use
     auto store_rot = [&](float2 r0, float2 r1, float2 r2, float2 r3) {
@@ -241,7 +252,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     {
       const double pos = (double)chunk_at(tile0 * kAttChunksWG + 4 * slot + (lane >> 4)) * kChunk;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) rot_next[k] = rot_of(pos * fb[k]);
+      for (int k = 0; k < 4; ++k) rot_next[k] = rot_of(pos * a.inv_freq[(lane & 15) * 4 + k]);
       store_rot(rot_next[0], rot_next[1], rot_next[2], rot_next[3]);
     }
     stage_store(0, sreg[0]);
@@ -251,19 +262,22 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     f32x4 acc[NT][8];
     const size_t desc_rows = (size_t)(a.prefix_cap / kChunk);
     for (int i = 0; i < ntiles; ++i) {
-      int rc_next = 0;
+      int rc_next = 0;   // the next tile's rotation-table chunk (clamped)
       uint32_t rdv = 0;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         if (s < NR) {
           if (s == 0) {
-            tokens_of(i + 1, tokB);  // clamped: harmless past the last tile
-            rc_next = chunk_at((tile0 + i + 1) * kAttChunksWG + 4 * slot + (lane >> 4));
             // residual descriptors of this tile's 4 chunks (lane k < 4: chunk k),
             // handed to the consumer with K_pre; token 0 of chunk k sits in
             // tokA[k / 2] of lane 8 (k % 2)
             const int c0 = __shfl(tokA[0], 8 * (lane & 1)), c1 = __shfl(tokA[1], 8 * (lane & 1));
             if (lane < 4) rdv = a.res_desc[chead * desc_rows + ((lane & 2) ? c1 : c0) / kChunk];
+          }
+          if (s == (NR > 1 ? 1 : 0)) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) tokB[nt] = clamp_chunk(selN[nt]) * kChunk + (col & 7);
+            rc_next = clamp_chunk(rcN);
           }
           if constexpr (LG == 0) gather(s, tokA);  // rank 64: the stage's own rows
           __builtin_amdgcn_sched_barrier(0);
@@ -296,13 +310,13 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 #pragma unroll
               for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mfma16(aop[ks][mt], bop[nt], acc[nt][mt]);
           }
-          if (s == (NR > 1 ? 1 : 0)) {
-            // fp64 angle reduction for the next tile, off the tail of the last stage
-            const double pos = (double)rc_next * kChunk;
+          // fp64 angle reductions for the next tile, one per step from step 1 on,
+          // off the tail of the last stage
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              rot_next[k] = rot_of(pos * fb[k]);
-              // keep the work here (the compiler would otherwise sink it into the tail)
+          for (int k = 0; k < 4; ++k) {
+            if (s == (NR > 1 ? (1 + k < NR - 1 ? 1 + k : NR - 1) : 0)) {
+              rot_next[k] = rot_of((double)rc_next * kChunk * L.invf[(lane & 15) * 4 + k]);
+              // keep the work in this step (the compiler would otherwise sink it into the tail)
               asm volatile("" : "+v"(rot_next[k].x), "+v"(rot_next[k].y));
             }
           }
@@ -370,6 +384,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
             store_rot(rot_next[0], rot_next[1], rot_next[2], rot_next[3]);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) tokA[nt] = tokB[nt];
+            load_next_ids(i + 2);
           }
           // Loads for later stages, issued after this step's products so that
           // a full memory pipeline stalls nothing the step needs.  (Past the
@@ -576,9 +591,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
         __builtin_amdgcn_sched_barrier(0);
         w1_load((c + 2) % NS, w1reg[(c + 2) % NS]);
         w2_load((c + 1) % NS, w2reg[(c + 1) % NS]);
-        if (c == 2) {
-          // this slot's residual rows (zeros where a token has none: reads
-          // past the end of the buffer return 0); descriptors from the producer
+        if (c >= 2 && c <= 5) {
+          // this slot's residual rows, spread over steps 2-5 (zeros where a
+          // token has none: reads past the end of the buffer return 0);
+          // descriptors from the producer
           auto row_of = [&](uint32_t dsc, int t) -> int {
             const int bit = t & 7;
             if (!((dsc >> bit) & 1u)) return -1;
@@ -589,7 +605,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
             const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(
                 static_cast<const uint16_t*>(a.res_val) + chead * (size_t)a.n_resid * kHeadDim, nbytes);
 #pragma unroll
-            for (int u = 0; u < RL; ++u) {
+            for (int u = 2 * (c - 2); u < 2 * (c - 1); ++u) {
               const int t = 4 * u + (lane >> 4);
               const int rn = row_of(L.rdesc[i & 1][slot][u >> 1], t);
               rres[u] = buffer_ld16(rv, rn >= 0 ? (uint32_t)rn * 256 + (lane & 15) * 16 : nbytes, 0);
@@ -601,15 +617,16 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
                 static_cast<const uint8_t*>(a.res_val) + chead * (size_t)a.n_resid * (kHeadDim / 2), nbytes);
             const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
                 a.res_scale + chead * (size_t)a.n_resid * (kHeadDim / 32), sbytes);
-#pragma unroll
-            for (int u = 0; u < RL; ++u) {
+            if (c - 1 <= RL) {
+              const int u = c - 2;
               const int t = 16 * u + (lane >> 2);
               const int rn = row_of(L.rdesc[i & 1][slot][2 * u + (lane >> 5)], t);
               rres[u] = buffer_ld16(rv, rn >= 0 ? (uint32_t)rn * 64 + (lane & 3) * 16 : nbytes, 0);
+            } else if (c == RL + 2) {
+              const int t = lane & 31;
+              const int rn = row_of(L.rdesc[i & 1][slot][t >> 3], t);
+              rsc = __builtin_amdgcn_raw_buffer_load_b64(rs, rn >= 0 ? (uint32_t)rn * 8 : sbytes, 0, 0);
             }
-            const int t = lane & 31;
-            const int rn = row_of(L.rdesc[i & 1][slot][t >> 3], t);
-            rsc = __builtin_amdgcn_raw_buffer_load_b64(rs, rn >= 0 ? (uint32_t)rn * 8 : sbytes, 0, 0);
           }
         }
         // W1 of stage c + 1 into the buffer step c - 1 read; W2 of stage c
