@@ -56,7 +56,7 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c3_262k_b28_hbm_traffic.txt")
 KERNEL_SOURCES = {
-    "attend": ("attend.hip", "common.h", "internal.h"),
+    "attend": ("attend.hip", "attend_pipe.hip", "attend_ops.h", "common.h", "internal.h"),
     "score": ("score_select.hip", "common.h", "internal.h"),
     "select": ("score_select.hip", "common.h", "internal.h"),
     "merge": ("attend.hip", "common.h", "internal.h"),

@@ -4,6 +4,10 @@ Parity bar: selected chunk sets equal except for ties within 1e-3 relative of
 the k-th landmark score; output within 1e-2 relative L2 and 3e-2 max-abs,
 compared with the oracle re-run on the GPU's selection.  Stage outputs
 (scores, rebuilt keys before/after RoPE, predicted values) are checked too.
+
+The step with stage outputs runs the selected chunks on the 4-wave attention
+kernel (the one that can write them); the plain step runs them on the
+producer/consumer kernel.  Every case checks both against the oracle.
 """
 import numpy as np
 import pytest
@@ -16,7 +20,7 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_util import full_parity, run_gpu  # noqa: E402
+from gpu_util import check_output, full_parity, run_gpu  # noqa: E402
 from oracle import fixture  # noqa: E402
 
 
@@ -46,12 +50,29 @@ def check_stages(cfg, res):
         assert np.array_equal(np.sort(sel[b, h][:keff]), s["sel"])
 
 
-def run_case(cfg, layer=0, stages=True):
-    cache = fixture.build_layer(cfg, layer)
+def run_case(cfg, layer=0, stages=True, batch=None):
+    cache = fixture.build_layer(cfg, layer, batch=batch)
     res = full_parity(cfg, cache, stages=stages)
     if stages:
         check_stages(cfg, res)
+        # the plain step (producer/consumer kernel) against the same oracle output
+        got, sel, _ = run_gpu(cfg, cache, stages=False)
+        assert np.array_equal(sel, res["sel"])
+        res["rel_plain"], res["max_plain"] = check_output(got, res["ref"], cfg.name + " (plain step)")
     return res
+
+
+def pipe_tiles_per_group(heads, n_tiles, n_cu=256):
+    """Tiles per workgroup the library plans for the producer/consumer kernel
+    (least rounds x (tiles + 1), smallest on ties); restated to document which
+    cases run several tiles per workgroup."""
+    best = None
+    for t in range(1, n_tiles + 1):
+        groups = -(-n_tiles // t)
+        cost = -(-heads * groups // n_cu) * (t + 1)
+        if best is None or cost < best[0]:
+            best = (cost, t)
+    return best[1]
 
 
 def test_c0_both_layers():
@@ -76,7 +97,22 @@ VARIANTS = {
                                  topk=48, rank=128),
     # batch 3, residual fraction 1 (every token has a residual)
     "batch3_allres": synth.C0.with_(name="batch3_allres", batch=3, resid_frac=1.0, topk=20),
+    # 64 (sequence, KV head) pairs x 16 tiles: the producer/consumer kernel plans
+    # 4 tiles per workgroup (running softmax, handoff buffers and weight rings
+    # cycle through several tiles; a ragged last tile of 10 chunks), biases on
+    "multitile_b8": synth.C0.with_(name="multitile_b8", batch=8, n_heads_q=32, n_heads_kv=8, rank=128,
+                                   topk=250, bias_std=0.1),
+    # the same with int4 coefficients and residuals and eviction (13 tiles, 4 per workgroup)
+    "multitile_int4_evict": synth.C4.with_(name="multitile_int4_evict", batch=8, ctx=4096, window=64, n_layers=4,
+                                           topk=200, rank=128),
 }
+
+
+@pytest.mark.parametrize("name", ["multitile_b8", "multitile_int4_evict"])
+def test_multitile_cases_plan_several_tiles(name):
+    cfg = VARIANTS[name]
+    n_tiles = -(-min(cfg.topk, cfg.n_cand) // 16)
+    assert pipe_tiles_per_group(cfg.batch * cfg.n_heads_kv, n_tiles) >= 4
 
 
 @pytest.mark.parametrize("name", list(VARIANTS))
