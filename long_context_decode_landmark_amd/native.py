@@ -165,8 +165,9 @@ def _ptr(t):
 
 
 def _stream(stream):
+    """A raw hipStream_t handle, a torch.cuda.Stream, or None (torch's current stream)."""
     if stream is not None:
-        return ctypes.c_void_p(int(stream))
+        return ctypes.c_void_p(int(getattr(stream, "cuda_stream", stream)))
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
