@@ -4,6 +4,7 @@
 //   split-K attention, window included) -> merge (log-sum-exp of the splits).
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/lowram.h"
@@ -57,6 +58,16 @@ int check_shape(const lowram_shape* s) {
 
 int prefix_rows(const lowram_shape* s) { return s->prefix_cap ? s->prefix_cap : s->prefix_len; }
 int window_rows(const lowram_shape* s) { return s->window_cap ? s->window_cap : s->window; }
+
+// Kernel for the selected chunks: 0 automatic, 1 producer/consumer, 2 four-wave
+// (environment variable LOWRAM_ATTEND = pipe | wave; anything else: automatic).
+int attend_mode() {
+  const char* v = std::getenv("LOWRAM_ATTEND");
+  if (!v) return 0;
+  if (std::strcmp(v, "pipe") == 0) return 1;
+  if (std::strcmp(v, "wave") == 0) return 2;
+  return 0;
+}
 
 Plan make_plan(const lowram_shape* s) {
   Plan p{};
@@ -149,23 +160,29 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   // of tiles; with stage outputs requested, the 4-wave kernel, one slot per
   // tile.  The exact window always goes to the 4-wave kernel, in the slots
   // after the selection's.
-  const bool stages = kpre_out || kpost_out || vhat_out;
   const int heads = s->batch * s->n_heads_kv;
   int n_grp = 0, tpw = 0;
-  if (has_prefix && !stages) plan_pipe_groups(heads, p.n_sel_tiles, &n_grp, &tpw);
-  const int sel_slots = !has_prefix ? 0 : stages ? p.n_sel_tiles : n_grp;
+  if (has_prefix) plan_pipe_groups(heads, p.n_sel_tiles, &n_grp, &tpw);
+  // The producer/consumer kernel pays off once a workgroup gets several tiles
+  // (its pipeline fills and drains once per workgroup); small problems, and
+  // every call that asks for stage outputs, run the 4-wave kernel.
+  // LOWRAM_ATTEND=pipe or =wave overrides the choice (not the stage rule).
+  const int mode = attend_mode();
+  const bool wave4 = kpre_out || kpost_out || vhat_out ||
+                      (mode == 0 ? tpw < 2 : mode == 2);
+  const int sel_slots = !has_prefix ? 0 : wave4 ? p.n_sel_tiles : n_grp;
   const int n_split = sel_slots + p.n_win_tiles;
   a.n_sel_tiles = sel_slots;
   a.n_win_tiles = p.n_win_tiles;
   a.n_split = n_split;
-  a.split_base = stages ? 0 : sel_slots;
-  a.n_split_launch = stages ? n_split : p.n_win_tiles;
+  a.split_base = wave4 ? 0 : sel_slots;
+  a.n_split_launch = wave4 ? n_split : p.n_win_tiles;
   a.total = heads * a.n_split_launch;
   a.padded_total = (a.total + 7) & ~7;
   a.pipe_tiles = p.n_sel_tiles;
   a.n_grp = n_grp;
   a.tpw = tpw;
-  a.pipe_total = heads * n_grp;
+  a.pipe_total = wave4 ? 0 : heads * n_grp;
   a.pipe_padded = (a.pipe_total + 7) & ~7;
   a.scale_log2 = s->softmax_scale * 1.4426950408889634f;
   for (int i = 0; i < 64; ++i)

@@ -31,8 +31,27 @@ def cache_to_device(cache):
     return {k: up(v) for k, v in cache.items() if k not in ("q", "needle")}
 
 
-def run_gpu(cfg, cache, stages=False, nb=None):
-    """Run the library on a fixture cache; returns (out fp64, sel, stage dict)."""
+def run_gpu(cfg, cache, stages=False, nb=None, attend=None):
+    """Run the library on a fixture cache; returns (out fp64, sel, stage dict).
+
+    attend: None (the library's own choice of kernel for the selected chunks),
+    "pipe" (producer/consumer kernel) or "wave" (4-wave kernel); calls with
+    stage outputs always take the 4-wave kernel."""
+    import os
+    if attend is None:
+        return _run_gpu(cfg, cache, stages, nb)
+    old = os.environ.get("LOWRAM_ATTEND")
+    os.environ["LOWRAM_ATTEND"] = attend
+    try:
+        return _run_gpu(cfg, cache, stages, nb)
+    finally:
+        if old is None:
+            del os.environ["LOWRAM_ATTEND"]
+        else:
+            os.environ["LOWRAM_ATTEND"] = old
+
+
+def _run_gpu(cfg, cache, stages, nb):
     nb = cache["q"].shape[0] if nb is None else nb
     t = cache_to_device(cache)
     q = up(cache["q"])

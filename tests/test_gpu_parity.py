@@ -7,7 +7,9 @@ compared with the oracle re-run on the GPU's selection.  Stage outputs
 
 The step with stage outputs runs the selected chunks on the 4-wave attention
 kernel (the one that can write them); the plain step runs them on the
-producer/consumer kernel.  Every case checks both against the oracle.
+producer/consumer kernel when the library plans several tiles per workgroup,
+else on the 4-wave kernel.  Every staged case also runs the plain step with
+the producer/consumer kernel forced and with the library's own choice.
 """
 import numpy as np
 import pytest
@@ -55,10 +57,13 @@ def run_case(cfg, layer=0, stages=True, batch=None):
     res = full_parity(cfg, cache, stages=stages)
     if stages:
         check_stages(cfg, res)
-        # the plain step (producer/consumer kernel) against the same oracle output
-        got, sel, _ = run_gpu(cfg, cache, stages=False)
-        assert np.array_equal(sel, res["sel"])
-        res["rel_plain"], res["max_plain"] = check_output(got, res["ref"], cfg.name + " (plain step)")
+        # the plain step on each kernel against the same oracle output: the
+        # producer/consumer kernel (forced; small cases would not pick it) and
+        # the library's own choice
+        for attend in ("pipe", None):
+            got, sel, _ = run_gpu(cfg, cache, stages=False, attend=attend)
+            assert np.array_equal(sel, res["sel"])
+            check_output(got, res["ref"], f"{cfg.name} (plain step, {attend or 'auto'})")
     return res
 
 
@@ -143,4 +148,9 @@ def test_c2_needle_is_selected():
     res = full_parity(cfg, cache, stages=False)
     for h in range(cfg.n_heads_kv):
         assert int(cache["needle"][0][h]) in set(res["sel"][0, h].tolist()), h
+    # the needle concentrates the softmax on 8 tokens: a sharp check of the
+    # producer/consumer kernel's fp16 RoPE and QK (one sequence would not pick it)
+    got, sel, _ = run_gpu(cfg, cache, attend="pipe")
+    assert np.array_equal(sel, res["sel"])
+    check_output(got, res["ref"], "c2 (producer/consumer kernel)")
     print(f"c2 layer 9: rel {res['rel']:.2e} max {res['max_abs']:.2e} flips {res['flips']}")
