@@ -138,12 +138,14 @@ int lowram_workspace_bytes(const lowram_shape* shape, size_t* bytes);
  * Score of a candidate chunk c for KV head h: max over h's query heads j of
  * q_j . landmark[c] (raw dot product); the k largest are kept, exact ties
  * going to the lower chunk id.
- * The selected chunks run on one of two attention kernels: a
- * producer/consumer kernel (several 128-token tiles per workgroup, fp16 RoPE,
- * QK and GELU operands) once the problem gives every workgroup at least two
- * tiles, else a 4-wave kernel (bf16 operands).  The environment variable
- * LOWRAM_ATTEND=pipe or =wave, read at each call, overrides the choice; both
- * meet the same accuracy bound.
+ * The selected chunks run on one of two attention kernels: a persistent
+ * producer/consumer kernel (one workgroup per CU working through groups of
+ * 128-token tiles; fp16 RoPE, QK and GELU operands) once the problem gives
+ * every CU at least two tiles, else a 4-wave kernel (bf16 operands).  The
+ * environment variable LOWRAM_ATTEND=pipe or =wave, read at each call,
+ * overrides the choice; both meet the same accuracy bound.  LOWRAM_PIPE_CUS=n
+ * (n >= 1) plans the producer/consumer kernel for n CUs instead of the
+ * device's count (fewer, longer workgroups; a testing aid, same results).
  */
 int lowram_decode_step(const lowram_shape* shape, const lowram_layer_cache* cache,
                        const uint16_t* q, uint16_t* out, int32_t* sel_out,

@@ -21,7 +21,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 struct Plan {
-  int g, n_chunks, n_cand, k_eff, n_sel_tiles, n_win_tiles, n_split;
+  // n_split: partial slots per head of the 4-wave kernel (one per tile);
+  // n_part: slots reserved per head, enough for either attention kernel
+  int g, n_chunks, n_cand, k_eff, n_sel_tiles, n_win_tiles, n_split, n_part;
   size_t off_keys, off_sel, off_part, total;
 };
 
@@ -69,6 +71,15 @@ int attend_mode() {
   return 0;
 }
 
+// CUs to plan the producer/consumer kernel for (environment variable
+// LOWRAM_PIPE_CUS = n >= 1); 0: the device's count.
+int pipe_cus_override() {
+  const char* v = std::getenv("LOWRAM_PIPE_CUS");
+  if (!v) return 0;
+  const long n = std::strtol(v, nullptr, 10);
+  return n >= 1 && n <= 65536 ? (int)n : 0;
+}
+
 Plan make_plan(const lowram_shape* s) {
   Plan p{};
   p.g = s->n_heads_q / s->n_heads_kv;
@@ -78,11 +89,14 @@ Plan make_plan(const lowram_shape* s) {
   p.n_sel_tiles = (p.k_eff + kAttChunksWG - 1) / kAttChunksWG;
   p.n_win_tiles = (s->window + kAttTokWG - 1) / kAttTokWG;
   p.n_split = p.n_sel_tiles + p.n_win_tiles;
+  // The producer/consumer kernel writes 4 slots per group of tiles, and its
+  // groups hold at least 2 tiles where a head has 2: 2 n + 6 slots cover it.
+  p.n_part = (p.n_sel_tiles > 0 ? 2 * p.n_sel_tiles + 6 : 0) + p.n_win_tiles;
   const size_t heads = (size_t)s->batch * s->n_heads_kv;
   p.off_keys = 0;
   p.off_sel = align_up(heads * (size_t)p.n_cand * 4);
   p.off_part = p.off_sel + align_up(heads * (size_t)p.k_eff * 4);
-  p.total = p.off_part + align_up(heads * (size_t)p.n_split * p.g * kPartStride * 4);
+  p.total = p.off_part + align_up(heads * (size_t)p.n_part * p.g * kPartStride * 4);
   return p;
 }
 
@@ -117,7 +131,7 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
     if (ptr && misaligned(ptr, 4)) return LOWRAM_ERR_ALIGN;
   if (kpre_out && misaligned(kpre_out, 16)) return LOWRAM_ERR_ALIGN;
   if (kpost_out && misaligned(kpost_out, 16)) return LOWRAM_ERR_ALIGN;
-  if ((long long)p.n_split * (p.g < 16 ? p.g : 16) > kMergeMaxWeights) return LOWRAM_ERR_UNSUPPORTED;
+  if (p.n_split > kMergeMaxSplits) return LOWRAM_ERR_UNSUPPORTED;
   if (ws_bytes < p.total) return LOWRAM_ERR_WORKSPACE;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -156,21 +170,35 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   a.cache_bmul = shared ? 0 : 1;
   a.prefix_cap = prefix_rows(s);
   a.window_cap = window_rows(s);
-  // Selected chunks: the producer/consumer kernel, one partial slot per group
-  // of tiles; with stage outputs requested, the 4-wave kernel, one slot per
-  // tile.  The exact window always goes to the 4-wave kernel, in the slots
-  // after the selection's.
+  // Selected chunks: the producer/consumer kernel, one workgroup per CU
+  // working through groups of tiles, 4 partial slots per group; with stage
+  // outputs requested, the 4-wave kernel, one slot per tile.  The exact
+  // window always goes to the 4-wave kernel, in the slots after the
+  // selection's.
   const int heads = s->batch * s->n_heads_kv;
-  int n_grp = 0, tpw = 0;
-  if (has_prefix) plan_pipe_groups(heads, p.n_sel_tiles, &n_grp, &tpw);
-  // The producer/consumer kernel pays off once a workgroup gets several tiles
-  // (its pipeline fills and drains once per workgroup); small problems, and
-  // every call that asks for stage outputs, run the 4-wave kernel.
-  // LOWRAM_ATTEND=pipe or =wave overrides the choice (not the stage rule).
+  int n_cu = pipe_cus_override();
+  if (n_cu <= 0) {
+    n_cu = 256;
+    int dev = 0, cu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0)
+      n_cu = cu;
+  }
+  int n_wg = 0, tpw = 0, n_grp = 0;
+  if (has_prefix) plan_pipe(heads, p.n_sel_tiles, n_cu, &n_wg, &tpw, &n_grp);
+  const long long all_tiles = (long long)heads * p.n_sel_tiles;
+  const int pipe_split = kPipeSplitsPerSeg * n_grp + p.n_win_tiles;
+  // The producer/consumer kernel pays off once every CU gets several tiles
+  // (its pipeline fills and drains once per workgroup); small problems, every
+  // call that asks for stage outputs, and shapes whose partial slots would not
+  // fit the reserve or the merge run the 4-wave kernel.
+  // LOWRAM_ATTEND=pipe or =wave overrides the choice (not those rules).
   const int mode = attend_mode();
-  const bool wave4 = kpre_out || kpost_out || vhat_out ||
-                      (mode == 0 ? tpw < 2 : mode == 2);
-  const int sel_slots = !has_prefix ? 0 : wave4 ? p.n_sel_tiles : n_grp;
+  const bool pipe_fits = n_wg > 0 && pipe_split <= p.n_part &&
+                         pipe_split <= kMergeMaxSplits;
+  const bool wave4 = kpre_out || kpost_out || vhat_out || !pipe_fits ||
+                     (mode == 0 ? all_tiles < 2LL * n_cu : mode == 2);
+  const int sel_slots = !has_prefix ? 0 : wave4 ? p.n_sel_tiles : kPipeSplitsPerSeg * n_grp;
   const int n_split = sel_slots + p.n_win_tiles;
   a.n_sel_tiles = sel_slots;
   a.n_win_tiles = p.n_win_tiles;
@@ -180,10 +208,13 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   a.total = heads * a.n_split_launch;
   a.padded_total = (a.total + 7) & ~7;
   a.pipe_tiles = p.n_sel_tiles;
-  a.n_grp = n_grp;
-  a.tpw = tpw;
-  a.pipe_total = wave4 ? 0 : heads * n_grp;
-  a.pipe_padded = (a.pipe_total + 7) & ~7;
+  a.pipe_grp = n_grp;
+  a.pipe_tpw = tpw;
+  a.pipe_groups = wave4 ? 0 : heads * n_grp;
+  a.pipe_wgs = wave4 ? 0 : n_wg;
+  a.pipe_padded = (a.pipe_wgs + 7) & ~7;
+  a.grp_div = make_fastdiv(n_grp);
+  a.hkv_div = make_fastdiv(s->n_heads_kv);
   a.scale_log2 = s->softmax_scale * 1.4426950408889634f;
   for (int i = 0; i < 64; ++i)
     a.inv_freq[i] = std::pow((double)s->rope_theta, -2.0 * i / (double)kHeadDim);
@@ -329,7 +360,7 @@ int dense_decode_step(const dense_shape* shape, const dense_layer_cache* cache, 
     if (misaligned(ptr, 16)) return LOWRAM_ERR_ALIGN;
   size_t need = 0;
   dense_workspace_bytes(shape, &need);
-  if ((long long)dense_splits(shape) * (shape->n_heads_q / shape->n_heads_kv < 16 ? shape->n_heads_q / shape->n_heads_kv : 16) > kMergeMaxWeights)
+  if (dense_splits(shape) > kMergeMaxSplits)
     return LOWRAM_ERR_UNSUPPORTED;
   if (ws_bytes < need) return LOWRAM_ERR_WORKSPACE;
   const int n_split = dense_splits(shape);

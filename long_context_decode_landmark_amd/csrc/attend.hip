@@ -717,67 +717,80 @@ hipError_t launch_attend(const AttendArgs& a, int rank, bool ci4, bool ri4, hipS
 }
 
 // ---------------------------------------------------------------------------
-// Split merge: one workgroup per (sequence, KV head).  The per-split weights
-// w[s][j] = exp2(m_sj - M_j) / L_j go to LDS first, then every thread sums
-// its (j, d) outputs over the splits with independent loads.
+// Split merge: one workgroup per (sequence, KV head, query head j), 512
+// threads = 128 output dims d x 4 split groups.  Every thread first issues the
+// loads of its o values (splits sg, sg + 4, ... in batches of kMergeBatch), then
+// wave 0 forms the weights w_s = exp2(m_s - M) / L in LDS (M = max_s m_s,
+// L = sum_s exp2(m_s - M) l_s) while those loads are in flight; the 4 split
+// groups' sums meet in LDS.
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 512;
-constexpr int kMergeMaxSplit = 1024;
+constexpr int kMergeBatch = 8;
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part,
                                                               uint16_t* __restrict__ out, int hkv,
                                                               int g, int n_split) {
-  __shared__ float wgt[kMergeMaxSplit * 4];
-  __shared__ float inv_l[16];
-  const int tid = threadIdx.x;
-  const size_t head = (size_t)blockIdx.y * hkv + blockIdx.x;
-  const float* ph = part + head * (size_t)n_split * g * kPartStride;
-  const size_t st = (size_t)g * kPartStride;
-  uint16_t* oh = out + head * (size_t)g * kHeadDim;
-  const int ns = n_split;  // n_split * min(g, 16) <= 4096 is checked at launch
-  for (int j0 = 0; j0 < g; j0 += 16) {
-    const int gj = min(16, g - j0);
-    // M_j: one wave per query head
-    const int wave = tid >> 6, lane = tid & 63;
-    for (int j = wave; j < gj; j += kMergeThreads / 64) {
-      float m = -__builtin_huge_valf();
-      for (int s = lane; s < ns; s += 64) m = fmaxf(m, ph[s * st + (j0 + j) * kPartStride]);
-      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-      float l = 0.f;
-      for (int s = lane; s < ns; s += 64) {
-        const float ms = ph[s * st + (j0 + j) * kPartStride];
-        const float w = ms == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(ms - m);
-        wgt[s * gj + j] = w;
-        l += w * ph[s * st + (j0 + j) * kPartStride + 1];
-      }
-      for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
-      if (lane == 0) inv_l[j] = 1.f / l;
+  __shared__ float wgt[kMergeMaxSplits];
+  __shared__ float red[3][kHeadDim];
+  __shared__ float inv_l;
+  const int tid = threadIdx.x, d = tid & (kHeadDim - 1), sg = tid >> 7;
+  const int j = blockIdx.x;
+  const size_t head = (size_t)blockIdx.z * hkv + blockIdx.y;
+  const size_t st = (size_t)g * kPartStride;  // between splits
+  const float* pj = part + head * (size_t)n_split * st + (size_t)j * kPartStride;
+  const int ns = n_split;
+  // this thread's first batch of o values
+  float ov[kMergeBatch];
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k) {
+    const int sp = sg + 4 * k;
+    ov[k] = sp < ns ? pj[sp * st + 2 + d] : 0.f;
+  }
+  if (tid < 64) {
+    float m = -__builtin_huge_valf();
+    for (int sp = tid; sp < ns; sp += 64) m = fmaxf(m, pj[sp * st]);
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float l = 0.f;
+    for (int sp = tid; sp < ns; sp += 64) {
+      const float ms = pj[sp * st];
+      const float w = ms == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(ms - m);
+      wgt[sp] = w;
+      l += w * pj[sp * st + 1];
     }
-    __syncthreads();
-    for (int idx = tid; idx < gj * kHeadDim; idx += kMergeThreads) {
-      const int j = idx / kHeadDim, d = idx % kHeadDim;
-      const float* p = ph + (j0 + j) * kPartStride + 2 + d;
-      float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-      int s = 0;
-      for (; s + 4 <= ns; s += 4) {
-        const float a0 = p[s * st], a1 = p[(s + 1) * st], a2 = p[(s + 2) * st], a3 = p[(s + 3) * st];
-        o0 += a0 * wgt[s * gj + j];
-        o1 += a1 * wgt[(s + 1) * gj + j];
-        o2 += a2 * wgt[(s + 2) * gj + j];
-        o3 += a3 * wgt[(s + 3) * gj + j];
-      }
-      for (; s < ns; ++s) o0 += p[s * st] * wgt[s * gj + j];
-      const __bf16 r = (__bf16)(((o0 + o1) + (o2 + o3)) * inv_l[j]);
-      oh[(j0 + j) * kHeadDim + d] = __builtin_bit_cast(uint16_t, r);
+    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
+    if (tid == 0) inv_l = 1.f / l;
+  }
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k) {
+    const int sp = sg + 4 * k;
+    if (sp < ns) acc += ov[k] * wgt[sp];
+  }
+  for (int base = 4 * kMergeBatch; base < ns; base += 4 * kMergeBatch) {
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int sp = base + sg + 4 * k;
+      ov[k] = sp < ns ? pj[sp * st + 2 + d] : 0.f;
     }
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int sp = base + sg + 4 * k;
+      if (sp < ns) acc += ov[k] * wgt[sp];
+    }
+  }
+  if (sg > 0) red[sg - 1][d] = acc;
+  __syncthreads();
+  if (sg == 0) {
+    const float o = ((acc + red[0][d]) + (red[1][d] + red[2][d])) * inv_l;
+    out[(head * g + j) * kHeadDim + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
   }
 }
 
 hipError_t launch_merge(const float* part, uint16_t* out, int nb, int hkv, int g, int n_split,
                         hipStream_t st) {
-  if ((long long)n_split * (g < 16 ? g : 16) > kMergeMaxSplit * 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_kernel, dim3(hkv, nb), dim3(kMergeThreads), 0, st, part, out, hkv, g, n_split);
+  if (n_split > kMergeMaxSplits || n_split < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_kernel, dim3(g, hkv, nb), dim3(kMergeThreads), 0, st, part, out, hkv, g, n_split);
   return hipGetLastError();
 }
 

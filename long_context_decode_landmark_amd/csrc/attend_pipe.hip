@@ -11,11 +11,16 @@
 // the VALU-heavy value section of its own tokens, so the two co-resident
 // workgroups of a CU keep the matrix cores and the vector ALUs busy in turn
 // rather than together.  Here one workgroup of 8 waves holds a CU (about
-// 151 KiB of LDS) and works through tpw consecutive 128-token tiles of one
-// (sequence, KV head).  Waves 0-3 are producers and waves 4-7 consumers;
-// producer w and consumer w + 4 own the same 32 tokens (slot w) of every
-// tile.  Time runs in tile-steps of 8 steps with a workgroup barrier after
-// each step:
+// 158 KiB of LDS) for the whole launch.  The 128-token tiles of every
+// (sequence, KV head) are cut into groups of tpw consecutive tiles; the grid
+// has one workgroup per CU (W of them), and workgroup w takes groups
+// w, w + W, w + 2 W, ... one after another inside one pipeline, so the
+// pipeline fills and drains once per CU, and at any time the neighbouring
+// workgroups of an XCD work on the groups of the same few heads (their
+// basis and W1/W2 stay in that XCD's L2).  Waves 0-3 are producers and
+// waves 4-7 consumers; producer w and consumer w + 4 own the same 32 tokens
+// (slot w) of every tile.  Time runs in tile-steps of 8 steps with a
+// workgroup barrier after each step:
 //   producer, tile-step i      rebuild K_pre of tile i from the basis stream
 //                              (one r-slice of 64 per step); after the last
 //                              slice hand K_pre to the consumer through LDS,
@@ -27,22 +32,27 @@
 // so on every SIMD the reconstruction of one tile runs beside the value
 // section of the one before.  Producer and consumer run separate loops with
 // the same number of barriers; the role is a scalar (wave-uniform) branch.
+// Everything that depends on the head (basis, W1/W2, biases, queries,
+// selection list, descriptors) is looked up per tile, and the loads issued
+// for the next tile use the next tile's head.
 //
 // Running softmax.  A producer keeps (m, l) per query head of its slot over
-// the tiles so far.  For a new tile it takes m' = max(m, max_t z_t), sends the
-// consumer p_t = exp2(z_t - m') and alpha = exp2(m - m'), and sets
-// l = l alpha + sum_t p_t.  The consumer scales its output accumulator by
-// alpha before adding the tile.  At the end the 4 slots are merged by the
-// usual log-sum-exp rule, b2 l is added, and one partial (m, l, o) per query
-// head is written for the group; the merge kernel combines the groups and the
-// window splits.
+// the tiles of the current group.  For a new tile it takes
+// m' = max(m, max_t z_t), sends the consumer p_t = exp2(z_t - m') and
+// alpha = exp2(m - m'), and sets l = l alpha + sum_t p_t; a group starts from
+// m = -inf, so its first alpha is 0 and clears the consumer's accumulator.
+// The consumer scales its output accumulator by alpha before adding the
+// tile.  When a group ends, each consumer writes its slot's partial
+// (m, l, o + b2 l) per query head to partial slot 4 gx + slot of the head
+// (gx = the group's index in the head); the merge kernel combines them with
+// the window's.
 #include "attend_ops.h"
 #include "common.h"
 #include "internal.h"
 
 namespace lowram {
 
-constexpr int kPipeSlots = 4;                 // producer/consumer pairs
+constexpr int kPipeSlots = kPipeSplitsPerSeg;  // producer/consumer pairs (one partial slot each)
 constexpr int kPipeThreads = 2 * kPipeSlots * 64;
 constexpr int kPipeSteps = kHidden / 32;      // value stages = steps per tile-step
 constexpr int kHandSlot = 9216;               // per slot: K_pre operands (8 KiB), then p (1 KiB)
@@ -59,13 +69,18 @@ struct PipeLds {
   alignas(16) _Float16 rope_os[kChunk][64];
   alignas(16) _Float16 rope_bc[kPipeSlots][4][64];
   alignas(16) _Float16 rope_bs[kPipeSlots][4][64];
-  f32x4 b1q[kHidden];                    // unit 32 c + row_perm32(p) at 32 c + p, x4 (an MFMA C operand)
-  float b2f[kHeadDim];
+  // the queries of the current tile's head as fp16: row j < g (zeros above),
+  // 16-byte piece p of the row at piece p ^ j
+  alignas(16) _Float16 qh[16][kHeadDim];
+  // per tile parity: b1 of unit 32 c + row_perm32(p) at 32 c + p, x4 (an MFMA
+  // C operand), and b2 (read when a segment's partial is written)
+  f32x4 b1q[2][kHidden];
+  float b2f[2][kHeadDim];
   double invf[64];                       // RoPE frequencies (read where needed: no registers held)
-  float alpha[2][kPipeSlots][16];        // accumulator rescale per query head, by tile parity
+  // per query head after each tile, by tile parity: the accumulator rescale
+  // alpha and the running (m, l)
+  f32x4 sm[2][kPipeSlots][16];
   uint32_t rdesc[2][kPipeSlots][4];     // residual descriptors of each slot's 4 chunks, by tile parity
-  float mfin[kPipeSlots][16];
-  float lfin[kPipeSlots][16];
 };
 static_assert(sizeof(PipeLds) <= 160 * 1024, "one workgroup per CU");
 
@@ -104,6 +119,44 @@ __device__ __forceinline__ void pipe_softmax(const f32x4 (&zacc)[2], int nvalid,
   pa = pack8h(f32x4{p[0][0], p[0][1], p[0][2], p[0][3]}, f32x4{p[1][0], p[1][1], p[1][2], p[1][3]});
 }
 
+// x as a value the compiler cannot trace to its definition: addresses built
+// from it are formed where they are used instead of being hoisted out of the
+// tile loop and held (or spilled) for its whole length
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Position in a workgroup's tile sequence: tile lt of the head of group g,
+// with what the group fixes (derived once per group, so that the per-tile
+// scalar work stays small): head bh = g / n_grp = sequence * hkv + KV head,
+// group gx = g % n_grp of the head, the group's end tile, and the cache
+// sequence and cache head (per sequence, or the shared context) it reads.
+struct PipeCur {
+  int g, lt, bh, gx, gend, cseq, chead;
+};
+__device__ __forceinline__ PipeCur pipe_first(const AttendArgs& a, int g) {
+  PipeCur c;
+  c.g = g;
+  c.bh = fdiv(g, a.grp_div);
+  c.gx = g - c.bh * a.pipe_grp;
+  c.lt = c.gx * a.pipe_tpw;
+  c.gend = min(c.lt + a.pipe_tpw, a.pipe_tiles);
+  const int b = fdiv(c.bh, a.hkv_div);
+  c.cseq = b * a.cache_bmul;
+  c.chead = c.cseq * a.hkv + (c.bh - b * a.hkv);
+  return c;
+}
+// the tile after c in this workgroup's sequence (groups g, g + W, ...); past
+// the last one, c itself, so that look-ahead loads stay in bounds
+__device__ __forceinline__ PipeCur pipe_next(const AttendArgs& a, PipeCur c) {
+  if (c.lt + 1 < c.gend) {
+    ++c.lt;
+    return c;
+  }
+  return c.g + a.pipe_wgs < a.pipe_groups ? pipe_first(a, c.g + a.pipe_wgs) : c;
+}
+
 template <int RANK, bool CI4, bool RI4>
 __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const AttendArgs a) {
   __shared__ PipeLds L;
@@ -119,33 +172,26 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
   const int grp = lane >> 4, col = lane & 15;
   const bool producer = wave < kPipeSlots;
   const int slot = wave & (kPipeSlots - 1), rt = tid & 255;
-  const int logical = xcd_logical_block(blockIdx.x, a.pipe_padded);
-  if (logical >= a.pipe_total) return;
-  const int bh = logical / a.n_grp, gx = logical % a.n_grp;
-  const int b = bh / a.hkv, h = bh % a.hkv;
+  const int wg = xcd_logical_block(blockIdx.x, a.pipe_padded);
+  if (wg >= a.pipe_wgs) return;
   const int g = a.g;
-  const size_t head = (size_t)b * a.hkv + h;
-  const int cseq = b * a.cache_bmul;             // cache arrays: per sequence, or one shared context
-  const size_t chead = (size_t)cseq * a.hkv + h;
-  const int tile0 = gx * a.tpw;
-  const int ntiles = min(a.tpw, a.pipe_tiles - tile0);
-  const int32_t* selh = a.sel + head * (size_t)a.k_eff;
-  // chunk id at selection position i (clamped into the list and the prefix)
+  // this workgroup's tiles: groups wg, wg + W, ... in turn
+  int ntiles = 0;
+  for (int gg = wg; gg < a.pipe_groups; gg += a.pipe_wgs)
+    ntiles += min(a.pipe_tpw, a.pipe_tiles - (gg - fdiv(gg, a.grp_div) * a.pipe_grp) * a.pipe_tpw);
   auto clamp_chunk = [&](int c) { return min(max(c, 0), a.n_chunks - 1); };
-  auto chunk_at = [&](int i) { return clamp_chunk(selh[min(i, a.k_eff - 1)]); };
-  // valid tokens of this slot in local tile i
-  auto slot_valid = [&](int i) {
-    const int nch = min(kAttChunksWG, a.k_eff - (tile0 + i) * kAttChunksWG);
+  // raw chunk id at position p of the selection rows of tile lt of head bh
+  // (clamped into the list)
+  auto sel_at = [&](int bh, int lt, int p) {
+    return a.sel[(size_t)bh * a.k_eff + min(lt * kAttChunksWG + p, a.k_eff - 1)];
+  };
+  // valid tokens of this slot in tile lt
+  auto slot_valid = [&](int lt) {
+    const int nch = min(kAttChunksWG, a.k_eff - lt * kAttChunksWG);
     return max(0, min(32, (nch - 4 * slot) * kChunk));
   };
 
   // tables
-  if (tid < kHidden) {
-    const float v = bf16_to_f32(a.b1[chead * kHidden + (tid & ~31) + row_perm32(tid & 31)]);
-    L.b1q[tid] = f32x4{v, v, v, v};
-  } else if (tid < kHidden + kHeadDim) {
-    L.b2f[tid - kHidden] = bf16_to_f32(a.b2[chead * kHeadDim + tid - kHidden]);
-  }
   if (tid < 64) L.invf[tid] = a.inv_freq[tid];
   if (tid < 256) {
     // offset tables: two consecutive frequencies per thread, as fp16 pairs
@@ -157,13 +203,18 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 
   if (producer) {
     // ===================================================================== producer
-    const __amdgpu_buffer_rsrc_t bas = buffer_rsrc(a.basis + chead * (size_t)kHeadDim * RANK, kHeadDim * RANK * 2);
     // basis stage s = columns [64 s, 64 s + 64), 128 rows in pi order, two rows per
     // 256-byte line, 16-byte pieces XOR-swizzled by the line index
+    // The basis of one cache head through a descriptor carried across tiles:
+    // it moves to the next tile's head at the step whose stage loads start
+    // reading the next tile (step NR - SL), so every load keeps constant offsets.
+    auto bas_of = [&](int chead) {
+      return buffer_rsrc(a.basis + (size_t)chead * kHeadDim * RANK, kHeadDim * RANK * 2);
+    };
     const int r0 = rt >> 3, pb = rt & 7;
     const uint32_t bas_goff = (uint32_t)((row_perm32(r0) * RANK + 8 * pb) * 2);
     const int bas_loff = (r0 >> 1) * 256 + ((((r0 & 1) << 3) | pb) ^ ((r0 >> 1) & 15)) * 16;
-    auto stage_load = [&](int s, u32x4 (&r)[kStageLd]) {
+    auto stage_load = [&](__amdgpu_buffer_rsrc_t bas, int s, u32x4 (&r)[kStageLd]) {
 #pragma unroll
       for (int u = 0; u < kStageLd; ++u) r[u] = buffer_ld16(bas, bas_goff, (32 * u * RANK + 64 * s) * 2);
     };
@@ -172,16 +223,17 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 #pragma unroll
       for (int u = 0; u < kStageLd; ++u) *reinterpret_cast<u32x4*>(dst + bas_loff + 4096 * u) = r[u];
     };
-    // this lane's gather rows of local tile i: token 16 nt + col of the slot
-    auto tokens_of = [&](int i, int (&tk)[NT]) {
+    // this lane's gather rows of tile lt of head bh: token 16 nt + col of the slot
+    auto tokens_of = [&](int bh, int lt, int (&tk)[NT]) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        tk[nt] = chunk_at((tile0 + i) * kAttChunksWG + 4 * slot + 2 * nt + (col >> 3)) * kChunk + (col & 7);
+        tk[nt] = clamp_chunk(sel_at(bh, lt, 4 * slot + 2 * nt + (col >> 3))) * kChunk + (col & 7);
     };
     bf16x8 cv[CI4 ? 1 : NR][2][NT];
     u32x2 cq[CI4 ? NR : 1][NT];
     float csc[CI4 ? NR : 1][NT];
-    auto gather = [&](int s, const int (&tk)[NT]) {
+    // coefficient rows tk of cache sequence cseq, stage s
+    auto gather = [&](int s, const int (&tk)[NT], int cseq) {
       if constexpr (!CI4) {
         const uint16_t* cb = static_cast<const uint16_t*>(a.coeff) + (size_t)cseq * a.prefix_cap * RANK;
 #pragma unroll
@@ -212,45 +264,65 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     // ---- prologue
     u32x4 sreg[NR][kStageLd];
     int tokA[NT], tokB[NT];
-    tokens_of(0, tokA);
+    // this tile, the next and the one after (look-ahead loads)
+    PipeCur tc = pipe_first(a, wg);
+    PipeCur tn = pipe_next(a, tc);
+    PipeCur tnn = pipe_next(a, tn);
+    const int bh0 = tc.bh;
+    tokens_of(bh0, tc.lt, tokA);
     // raw chunk ids of the next tile (gather rows, rotation-table row): issued a
     // tile ahead, carried through the loop and clamped at step 1, so that neither
     // the compiler nor the in-order load counter ties them to a wait right away
     int selN[NT], rcN;
-    auto load_next_ids = [&](int t) {
+    auto load_next_ids = [&](const PipeCur& t) {
+      const int bh = t.bh;
+      const int ln = fresh(lane);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        selN[nt] = selh[min((tile0 + t) * kAttChunksWG + 4 * slot + 2 * nt + (col >> 3), a.k_eff - 1)];
-      rcN = selh[min((tile0 + t) * kAttChunksWG + 4 * slot + (lane >> 4), a.k_eff - 1)];
+      for (int nt = 0; nt < NT; ++nt) selN[nt] = sel_at(bh, t.lt, 4 * slot + 2 * nt + ((ln & 15) >> 3));
+      rcN = sel_at(bh, t.lt, 4 * slot + (ln >> 4));
     };
-    load_next_ids(1);
-    const uint16_t* qh = a.q + ((size_t)b * a.hq + (size_t)h * g) * kHeadDim;
-    f16x8 qp[4];  // the queries as fp16 operands of QK
+    load_next_ids(tn);
+    // The queries of a tile's head go to LDS as fp16 before its tail (step 0
+    // of its tile-step; rank 64: the last step of the tile-step before), from
+    // 16 bytes per thread loaded at the previous tail.
+    constexpr int kQStep = NR >= 2 ? 0 : NS - 1;
+    bf16x8 qld;
+    auto load_q = [&](int bh) {
+      const int r = fresh(rt), j = r >> 4;
+      const bf16x8 v = load_bf16x8(a.q + ((size_t)bh * g + min(j, g - 1)) * kHeadDim + 8 * (r & 15));
+      qld = j < g ? v : zero_bf16x8();
+    };
+    auto store_q = [&]() {
+      const int r = fresh(rt), j = r >> 4;
+      f16x8 h;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 qb = col < g ? load_bf16x8(qh + col * kHeadDim + 32 * ks + 8 * grp) : zero_bf16x8();
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qp[ks][e] = (_Float16)(float)qb[e];
-    }
+      for (int e = 0; e < 8; ++e) h[e] = (_Float16)(float)qld[e];
+      *reinterpret_cast<f16x8*>(&L.qh[j][8 * ((r & 15) ^ j)]) = h;
+    };
+    load_q(bh0);
+    if constexpr (NR == 1) store_q();  // the first tail is at step 0
     // this wave's rotation table row: chunk lane / 16, frequencies 4 (lane % 16) + k,
     // written as fp16 pairs, the access type the RoPE reads use
     auto store_rot = [&](float2 r0, float2 r1, float2 r2, float2 r3) {
       const h2 c01 = __builtin_convertvector(f32x2{r0.x, r1.x}, h2), c23 = __builtin_convertvector(f32x2{r2.x, r3.x}, h2);
       const h2 s01 = __builtin_convertvector(f32x2{r0.y, r1.y}, h2), s23 = __builtin_convertvector(f32x2{r2.y, r3.y}, h2);
-      h2* pc = reinterpret_cast<h2*>(&L.rope_bc[slot][lane >> 4][(lane & 15) * 4]);
-      h2* ps = reinterpret_cast<h2*>(&L.rope_bs[slot][lane >> 4][(lane & 15) * 4]);
+      // [slot][lane / 16][4 (lane % 16)] = slot base + 4 lane
+      const int ln = fresh(lane);
+      h2* pc = reinterpret_cast<h2*>(&L.rope_bc[slot][0][0] + 4 * ln);
+      h2* ps = reinterpret_cast<h2*>(&L.rope_bs[slot][0][0] + 4 * ln);
       pc[0] = c01;
       pc[1] = c23;
       ps[0] = s01;
       ps[1] = s23;
     };
     float2 rot_next[4];  // rotations to the chunk starts: tile 0 here, later the next tile's
+    __amdgpu_buffer_rsrc_t bas = bas_of(tc.chead);
 #pragma unroll
-    for (int s = 0; s < SL; ++s) stage_load(s, sreg[s]);
+    for (int s = 0; s < SL; ++s) stage_load(bas, s, sreg[s]);
 #pragma unroll
-    for (int s = 0; s < LG; ++s) gather(s, tokA);
+    for (int s = 0; s < LG; ++s) gather(s, tokA, tc.cseq);
     {
-      const double pos = (double)chunk_at(tile0 * kAttChunksWG + 4 * slot + (lane >> 4)) * kChunk;
+      const double pos = (double)clamp_chunk(sel_at(bh0, tc.lt, 4 * slot + (lane >> 4))) * kChunk;
 #pragma unroll
       for (int k = 0; k < 4; ++k) rot_next[k] = rot_of(pos * a.inv_freq[(lane & 15) * 4 + k]);
       store_rot(rot_next[0], rot_next[1], rot_next[2], rot_next[3]);
@@ -262,24 +334,40 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     f32x4 acc[NT][8];
     const size_t desc_rows = (size_t)(a.prefix_cap / kChunk);
     for (int i = 0; i < ntiles; ++i) {
+      const int bh_n = tn.bh, chead_c = tc.chead, cseq_c = tc.cseq, cseq_n = tn.cseq;
+      const bool grp_end = tc.lt + 1 == tc.gend;  // the group ends with this tile
       int rc_next = 0;   // the next tile's rotation-table chunk (clamped)
       uint32_t rdv = 0;
+      uint16_t b1raw = 0, b2raw = 0;  // this tile's biases, to LDS at the last step
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
+        if (s == kQStep) store_q();  // rank >= 128: this tile's; rank 64: the next tile's
+        if (s == NS - 1) {
+          // this tile's biases for its consumer tile-step (b2: for its
+          // partial), ahead of the tail so that they are not held through it
+          // (indexed as slot base + lane, the lane offsets the other writes use)
+          const float v = bf16_to_f32(b1raw);
+          const int ln = fresh(lane);
+          (&L.b1q[i & 1][slot * 64])[ln] = f32x4{v, v, v, v};
+          if (slot < kHeadDim / 64) (&L.b2f[i & 1][slot * 64])[ln] = bf16_to_f32(b2raw);
+        }
         if (s < NR) {
           if (s == 0) {
             // residual descriptors of this tile's 4 chunks (lane k < 4: chunk k),
             // handed to the consumer with K_pre; token 0 of chunk k sits in
             // tokA[k / 2] of lane 8 (k % 2)
             const int c0 = __shfl(tokA[0], 8 * (lane & 1)), c1 = __shfl(tokA[1], 8 * (lane & 1));
-            if (lane < 4) rdv = a.res_desc[chead * desc_rows + ((lane & 2) ? c1 : c0) / kChunk];
+            if (lane < 4) rdv = a.res_desc[(size_t)chead_c * desc_rows + ((lane & 2) ? c1 : c0) / kChunk];
+            const int r = fresh(rt);
+            b1raw = a.b1[(size_t)chead_c * kHidden + (r & ~31) + row_perm32(r & 31)];
+            b2raw = a.b2[(size_t)chead_c * kHeadDim + (r & (kHeadDim - 1))];
           }
           if (s == (NR > 1 ? 1 : 0)) {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) tokB[nt] = clamp_chunk(selN[nt]) * kChunk + (col & 7);
             rc_next = clamp_chunk(rcN);
           }
-          if constexpr (LG == 0) gather(s, tokA);  // rank 64: the stage's own rows
+          if constexpr (LG == 0) gather(s, tokA, cseq_c);  // rank 64: the stage's own rows
           __builtin_amdgcn_sched_barrier(0);
 
           if (s == 0) {
@@ -335,16 +423,24 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
             // RoPE on packed fp16 pairs of consecutive frequencies: pair (d, d + 64)
             // = m-tiles (mt, mt + 4) of the same lane; the rotation is the chunk
             // start's composed with the offset's.  K_post stays fp16 (relative
-            // error ~3 2^-11, below the 2^-9 of a bf16 operand) and feeds an fp16 QK.
-            h2 kp[NT][8][2];  // K_post, [nt][mt][e pair]
+            // error ~3 2^-11, below the 2^-9 of a bf16 operand) and feeds an fp16
+            // QK.  One 16-token half at a time, so that only half of K_post is
+            // held at once.
+            const int cl = fresh(lane) & 15;
+            f16x8 qp[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-              const int p0 = 32 * (mt >> 1) + 8 * grp + 4 * (mt & 1);
-              const h2* oc = reinterpret_cast<const h2*>(&L.rope_oc[col & 7][p0]);
-              const h2* os = reinterpret_cast<const h2*>(&L.rope_os[col & 7][p0]);
+            for (int ks = 0; ks < 4; ++ks)
+              qp[ks] = *reinterpret_cast<const f16x8*>(&L.qh[cl][8 * ((4 * ks + grp) ^ cl)]);
+            f32x4 zacc[NT];
 #pragma unroll
-              for (int nt = 0; nt < NT; ++nt) {
-                const int cs = 2 * nt + (col >> 3);
+            for (int nt = 0; nt < NT; ++nt) {
+              const int cs = 2 * nt + (cl >> 3);
+              h2 kp[8][2];  // K_post of this half, [mt][e pair]
+#pragma unroll
+              for (int mt = 0; mt < 4; ++mt) {
+                const int p0 = 32 * (mt >> 1) + 8 * grp + 4 * (mt & 1);
+                const h2* oc = reinterpret_cast<const h2*>(&L.rope_oc[cl & 7][p0]);
+                const h2* os = reinterpret_cast<const h2*>(&L.rope_os[cl & 7][p0]);
                 const h2* bc = reinterpret_cast<const h2*>(&L.rope_bc[slot][cs][p0]);
                 const h2* bs = reinterpret_cast<const h2*>(&L.rope_bs[slot][cs][p0]);
 #pragma unroll
@@ -354,60 +450,66 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
                   const h2 sn = __builtin_elementwise_fma(b_s, o_c, b_c * o_s);
                   const h2 x1 = __builtin_convertvector(f32x2{acc[nt][mt][2 * q], acc[nt][mt][2 * q + 1]}, h2);
                   const h2 x2 = __builtin_convertvector(f32x2{acc[nt][mt + 4][2 * q], acc[nt][mt + 4][2 * q + 1]}, h2);
-                  kp[nt][mt][q] = __builtin_elementwise_fma(x1, c, -(x2 * sn));
-                  kp[nt][mt + 4][q] = __builtin_elementwise_fma(x2, c, x1 * sn);
+                  kp[mt][q] = __builtin_elementwise_fma(x1, c, -(x2 * sn));
+                  kp[mt + 4][q] = __builtin_elementwise_fma(x2, c, x1 * sn);
                 }
               }
-            }
-            // QK (fp16 operands), then the running softmax
-            f32x4 zacc[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
+              // QK of this half (fp16 operands)
               f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
               for (int ks = 0; ks < 4; ++ks) {
                 const f16x8 kop = __builtin_shufflevector(
-                    __builtin_shufflevector(kp[nt][2 * ks][0], kp[nt][2 * ks][1], 0, 1, 2, 3),
-                    __builtin_shufflevector(kp[nt][2 * ks + 1][0], kp[nt][2 * ks + 1][1], 0, 1, 2, 3),
+                    __builtin_shufflevector(kp[2 * ks][0], kp[2 * ks][1], 0, 1, 2, 3),
+                    __builtin_shufflevector(kp[2 * ks + 1][0], kp[2 * ks + 1][1], 0, 1, 2, 3),
                     0, 1, 2, 3, 4, 5, 6, 7);
                 z = mfma16h(kop, qp[ks], z);
               }
               zacc[nt] = z;
             }
+            // the running softmax
             float alpha;
             f16x8 pa;
-            pipe_softmax(zacc, slot_valid(i), a.scale_log2, grp, mrun, lrun, alpha, pa);
+            pipe_softmax(zacc, slot_valid(tc.lt), a.scale_log2, grp, mrun, lrun, alpha, pa);
             *reinterpret_cast<u32x4*>(hb + kHandP + lane * 16) = __builtin_bit_cast(u32x4, pa);
-            if (grp == 0) L.alpha[i & 1][slot][col] = alpha;
-            if (lane < 4) L.rdesc[i & 1][slot][lane] = rdv;
+            {
+              const int ln = fresh(lane);
+              if (lane < 16) (&L.sm[i & 1][slot][0])[ln] = f32x4{alpha, mrun, lrun, 0.f};
+              if (lane < 4) (&L.rdesc[i & 1][slot][0])[ln] = rdv;
+            }
+            // a new group starts from nothing (its first alpha is 0)
+            if (grp_end) {
+              mrun = -__builtin_huge_valf();
+              lrun = 0.f;
+            }
             // this wave's rotation table for the next tile
             store_rot(rot_next[0], rot_next[1], rot_next[2], rot_next[3]);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) tokA[nt] = tokB[nt];
-            load_next_ids(i + 2);
+            load_next_ids(tnn);
+            load_q(bh_n);
           }
           // Loads for later stages, issued after this step's products so that
           // a full memory pipeline stalls nothing the step needs.  (Past the
-          // last tile they repeat the basis and read clamped rows: harmless,
-          // and they keep the code branch-free.)
+          // last tile they repeat the last tile: harmless, and they keep the
+          // code branch-free.)
           __builtin_amdgcn_sched_barrier(0);
-          if constexpr (SL > 0) stage_load((s + SL) % NR, sreg[(s + SL) % NR]);
+          if (s == NR - SL) bas = bas_of(tn.chead);  // from here on the loads are the next tile's
+          if constexpr (SL > 0) stage_load(bas, (s + SL) % NR, sreg[(s + SL) % NR]);
           if constexpr (LG > 0) {
-            if (s + LG < NR) gather(s + LG, tokA);
-            else gather(s + LG - NR, tokB);
+            if (s + LG < NR) gather(s + LG, tokA, cseq_c);
+            else gather(s + LG - NR, tokB, cseq_n);
           }
           // next basis stage into the buffer the previous step read
           stage_store((i * NR + s + 1) & 1, sreg[(s + 1) % NR]);
         }
         __syncthreads();
       }
+      tc = tn;
+      tn = tnn;
+      tnn = pipe_next(a, tnn);
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s) __syncthreads();  // the consumers' last tile
-    if (grp == 0) {
-      L.mfin[slot][col] = mrun;
-      L.lfin[slot][col] = lrun;
-    }
   } else {
     // ===================================================================== consumer
     // Software-pipelined by one value stage: step c runs GELU, PH and OUT of
@@ -417,8 +519,11 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     // after the loop).  Accordingly the W1 half of stage c is stored at the
     // end of step c - 1 and read at step c, the W2 half stored at the end of
     // step c and read at step c + 1, each half in a ring of two buffers.
-    const __amdgpu_buffer_rsrc_t w1r = buffer_rsrc(a.w1 + chead * (size_t)kHidden * kHeadDim, kHidden * kHeadDim * 2);
-    const __amdgpu_buffer_rsrc_t w2r = buffer_rsrc(a.w2 + chead * (size_t)kHeadDim * kHidden, kHeadDim * kHidden * 2);
+    // W1 and W2 of one cache head through descriptors carried across tiles,
+    // moved to the next tile's head at the steps whose loads start reading it
+    // (W1: step NS - 2, W2: step NS - 1)
+    auto w1_of = [&](int chead) { return buffer_rsrc(a.w1 + (size_t)chead * kHidden * kHeadDim, kHidden * kHeadDim * 2); };
+    auto w2_of = [&](int chead) { return buffer_rsrc(a.w2 + (size_t)chead * kHeadDim * kHidden, kHeadDim * kHidden * 2); };
     // stage c: W1 rows [32 c, 32 c + 32) in pi order (8 KiB at offset 0 of a
     // ring buffer), W2 columns [32 c, 32 c + 32) (natural, four rows per
     // 256-byte line, 8 KiB at offset 8192)
@@ -427,11 +532,11 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     const int w1_loff = w1row * 256 + (w1p ^ (w1row & 15)) * 16;
     const uint32_t w2_goff = (uint32_t)(((rt >> 2) * kHidden + 8 * (rt & 3)) * 2);
     const int w2_loff = 8192 + (rt >> 4) * 256 + ((rt & 15) ^ ((rt >> 4) & 15)) * 16;
-    auto w1_load = [&](int c, u32x4 (&r)[2]) {
+    auto w1_load = [&](__amdgpu_buffer_rsrc_t w1r, int c, u32x4 (&r)[2]) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) r[u] = buffer_ld16(w1r, w1_goff, (32 * c + 4 * u) * kHeadDim * 2);
     };
-    auto w2_load = [&](int c, u32x4 (&r)[2]) {
+    auto w2_load = [&](__amdgpu_buffer_rsrc_t w2r, int c, u32x4 (&r)[2]) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) r[u] = buffer_ld16(w2r, w2_goff, (u * 64 * kHidden + 32 * c) * 2);
     };
@@ -452,9 +557,15 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
       rw2[q] = 8192 + (col >> 2) * 256 + ((((col & 3) ^ q) << 2) | (grp ^ (col >> 2))) * 16;
 
     u32x4 w1reg[NS][2], w2reg[NS][2];
-    w1_load(0, w1reg[0]);
-    w1_load(1, w1reg[1]);
-    w2_load(0, w2reg[0]);
+    __amdgpu_buffer_rsrc_t w1r, w2r;
+    {
+      const int chead0 = pipe_first(a, wg).chead;
+      w1r = w1_of(chead0);
+      w2r = w2_of(chead0);
+      w1_load(w1r, 0, w1reg[0]);
+      w1_load(w1r, 1, w1reg[1]);
+      w2_load(w2r, 0, w2reg[0]);
+    }
     w1_store(0, w1reg[0]);
     __syncthreads();
 #pragma unroll
@@ -485,8 +596,31 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 #pragma unroll
       for (int nd = 0; nd < 8; ++nd) w2op[nd] = lds16(sb, rw2[nd & 3] + 1024 * nd);
     };
+    // group grp_id's partial: slot 4 gx + slot of its head bh; (m, l) from the
+    // producer, b2 of the head from LDS (parity par)
+    auto write_part = [&](const PipeCur& t, float m, float l, int par) {
+      if (col >= g) return;
+      float* pp = a.part + (((size_t)t.bh * a.n_split + kPipeSlots * t.gx + slot) * g + col) * kPartStride;
+      if (grp == 0) {
+        pp[0] = m;
+        pp[1] = l;
+      }
+#pragma unroll
+      for (int nd = 0; nd < 8; ++nd)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = 16 * nd + 4 * grp + e;
+          pp[2 + d] = fmaf(L.b2f[par][d], l, oacc[nd][e]);
+        }
+    };
     constexpr int RL = RI4 ? 2 : 8;  // 16-byte residual pieces per lane
+    float m_cur = 0.f, l_cur = 0.f;    // the producer's (m, l) after the tile being consumed
+    PipeCur tc = pipe_first(a, wg), tp = tc;  // this tile and the one before
+    PipeCur tn = pipe_next(a, tc);
     for (int i = 0; i < ntiles; ++i) {
+      const int chead_c = tc.chead;
+      // the previous tile ended its group
+      const bool prev_end = i > 0 && tp.lt + 1 == tp.gend;
       unsigned char* hb = L.hand[i & 1][slot];
       bf16x8 kpre_b[NT][4];
       bf16x8 pab;  // the softmax weights in bf16 (the residual product)
@@ -505,20 +639,26 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 #pragma unroll
             for (int hn = 0; hn < 2; ++hn) w1op[ks][hn] = lds16(sb, rw1[ks] + 4096 * hn);
 #pragma unroll
-          for (int hn = 0; hn < 2; ++hn) b1v[hn] = L.b1q[32 * c + 16 * hn + col];
+          for (int hn = 0; hn < 2; ++hn) b1v[hn] = L.b1q[i & 1][32 * c + 16 * hn + col];
         }
         bf16x8 w2op[8];  // W2 operands of the previous stage
         read_w2((c + NS - 1) % NS, w2op);
         f16x8 pnew;
         float alpha = 1.f;
+        float m_prev = 0.f, l_prev = 0.f;
         if (c == 0) {
+          m_prev = m_cur;
+          l_prev = l_cur;
+          const f32x4 sm = L.sm[i & 1][slot][col];
+          m_cur = sm[1];
+          l_cur = sm[2];
+          alpha = sm[0];
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
               kpre_b[nt][ks] = lds16(hb, (nt * 4 + ks) * 1024 + lane * 16);
           pnew = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(hb + kHandP + lane * 16));
-          alpha = L.alpha[i & 1][slot][col];
         }
         __builtin_amdgcn_sched_barrier(0);
         // ---- MLP1 of stage c: D[t][h] = K_pre[t][d] x W1^T[d][h] (b1 initial value),
@@ -534,6 +674,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
         //      tile's last stage with that tile's weights, then the rescale)
         if (c > 0 || i > 0) finish_stage((c + NS - 1) % NS, w2op, pa);
         if (c == 0) {
+          if (prev_end) write_part(tp, m_prev, l_prev, (i - 1) & 1);
           pa = pnew;
 #pragma unroll
           for (int e = 0; e < 8; ++e) pab[e] = (__bf16)(float)pa[e];
@@ -589,8 +730,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
         // the same weights every tile, W1 two stages ahead and W2 one, and
         // the tile's residual rows for step NS - 1
         __builtin_amdgcn_sched_barrier(0);
-        w1_load((c + 2) % NS, w1reg[(c + 2) % NS]);
-        w2_load((c + 1) % NS, w2reg[(c + 1) % NS]);
+        if (c == NS - 2) w1r = w1_of(tn.chead);  // from here on the loads are the next tile's
+        if (c == NS - 1) w2r = w2_of(tn.chead);
+        w1_load(w1r, (c + 2) % NS, w1reg[(c + 2) % NS]);
+        w2_load(w2r, (c + 1) % NS, w2reg[(c + 1) % NS]);
         if (c >= 2 && c <= 5) {
           // this slot's residual rows, spread over steps 2-5 (zeros where a
           // token has none: reads past the end of the buffer return 0);
@@ -603,7 +746,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
           if constexpr (!RI4) {
             const uint32_t nbytes = (uint32_t)a.n_resid * kHeadDim * 2;
             const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(
-                static_cast<const uint16_t*>(a.res_val) + chead * (size_t)a.n_resid * kHeadDim, nbytes);
+                static_cast<const uint16_t*>(a.res_val) + (size_t)chead_c * a.n_resid * kHeadDim, nbytes);
 #pragma unroll
             for (int u = 2 * (c - 2); u < 2 * (c - 1); ++u) {
               const int t = 4 * u + (lane >> 4);
@@ -614,9 +757,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
             const uint32_t nbytes = (uint32_t)a.n_resid * (kHeadDim / 2);
             const uint32_t sbytes = (uint32_t)a.n_resid * (kHeadDim / 32) * 2;
             const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(
-                static_cast<const uint8_t*>(a.res_val) + chead * (size_t)a.n_resid * (kHeadDim / 2), nbytes);
+                static_cast<const uint8_t*>(a.res_val) + (size_t)chead_c * a.n_resid * (kHeadDim / 2), nbytes);
             const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
-                a.res_scale + chead * (size_t)a.n_resid * (kHeadDim / 32), sbytes);
+                a.res_scale + (size_t)chead_c * a.n_resid * (kHeadDim / 32), sbytes);
             if (c - 1 <= RL) {
               const int u = c - 2;
               const int t = 16 * u + (lane >> 2);
@@ -635,64 +778,43 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
         w2_store(c & 1, w2reg[c]);
         __syncthreads();
       }
+      tp = tc;
+      tc = tn;
+      tn = pipe_next(a, tn);
     }
     {
-      // the last tile's last stage (its W2 buffer is not written again)
+      // the last tile's last stage (its W2 buffer is not written again), and
+      // the partial of the last segment
       bf16x8 w2op[8];
       read_w2(NS - 1, w2op);
       finish_stage(NS - 1, w2op, pa);
+      write_part(tp, m_cur, l_cur, (ntiles - 1) & 1);
     }
-    // this slot's o^T[d][j] (rows d = 16 nd + 4 grp + e, column j = col) -> LDS
-    float* mo = reinterpret_cast<float*>(&L.hand[0][0][0]);
-    if (col < g)
-#pragma unroll
-      for (int nd = 0; nd < 8; ++nd)
-        *reinterpret_cast<f32x4*>(&mo[(slot * 16 + col) * kHeadDim + 16 * nd + 4 * grp]) = oacc[nd];
-  }
-  __syncthreads();
-
-  // ================================= merge the 4 slots, add b2 l, write the partial
-  const float* mo = reinterpret_cast<const float*>(&L.hand[0][0][0]);
-  float* part = a.part + (head * (size_t)a.n_split + gx) * g * kPartStride;
-  for (int idx = tid; idx < g * kHeadDim; idx += kPipeThreads) {
-    const int j = idx / kHeadDim, d = idx % kHeadDim;
-    float M = -__builtin_huge_valf();
-#pragma unroll
-    for (int w = 0; w < kPipeSlots; ++w) M = fmaxf(M, L.mfin[w][j]);
-    float lt = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < kPipeSlots; ++w) {
-      const float mw = L.mfin[w][j];
-      const float sc = mw == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      lt += L.lfin[w][j] * sc;
-      o += mo[(w * 16 + j) * kHeadDim + d] * sc;
-    }
-    if (d == 0) {
-      part[j * kPartStride] = M;
-      part[j * kPartStride + 1] = lt;
-    }
-    part[j * kPartStride + 2 + d] = fmaf(L.b2f[d], lt, o);
   }
 }
 
-void plan_pipe_groups(int heads, int n_tiles, int* n_grp, int* tpw) {
-  // A workgroup of t tiles lives about t + 1 tile-steps (the pipeline fills
-  // and drains once); workgroups run one per CU in rounds.  Take the t with
-  // the least rounds x (t + 1), the smallest on ties.
-  constexpr long kCUs = 256;
-  long best = -1;
+void plan_pipe(int heads, int n_tiles, int n_cu, int* n_wg, int* tpw, int* n_grp) {
+  // Groups of t tiles (t >= 2 where a head has 2 tiles), dealt round-robin to
+  // W = min(n_cu, groups) workgroups; a workgroup's pipeline holds at most
+  // ceil(groups / W) x t tiles.  Take the t with the fewest, the largest on
+  // ties (fewer partial slots).
+  *n_wg = *tpw = *n_grp = 0;
+  if (heads <= 0 || n_tiles <= 0 || n_cu <= 0) return;
+  long long best = -1;
   int bt = 1;
-  for (int t = 1; t <= n_tiles; ++t) {
-    const long groups = (n_tiles + t - 1) / t;
-    const long rounds = ((long)heads * groups + kCUs - 1) / kCUs;
-    const long cost = rounds * (t + 1);
-    if (best < 0 || cost < best) {
+  for (int t = n_tiles < 2 ? 1 : 2; t <= n_tiles; ++t) {
+    const long long groups = (long long)heads * ((n_tiles + t - 1) / t);
+    const long long w = groups < n_cu ? groups : n_cu;
+    const long long cost = (groups + w - 1) / w * t;
+    if (best < 0 || cost <= best) {
       best = cost;
       bt = t;
     }
   }
   *tpw = bt;
-  *n_grp = n_tiles > 0 ? (n_tiles + bt - 1) / bt : 0;
+  *n_grp = (n_tiles + bt - 1) / bt;
+  const long long groups = (long long)heads * *n_grp;
+  *n_wg = (int)(groups < n_cu ? groups : n_cu);
 }
 
 template <int RANK>
@@ -706,7 +828,7 @@ static hipError_t launch_pipe_rank(const AttendArgs& a, bool ci4, bool ri4, hipS
 }
 
 hipError_t launch_attend_pipe(const AttendArgs& a, int rank, bool ci4, bool ri4, hipStream_t st) {
-  if (a.pipe_total == 0) return hipSuccess;
+  if (a.pipe_wgs == 0) return hipSuccess;
   switch (rank) {
     case 128: return launch_pipe_rank<128>(a, ci4, ri4, st);
     case 256: return launch_pipe_rank<256>(a, ci4, ri4, st);

@@ -17,7 +17,26 @@ constexpr int kAttChunksWG = kAttWaves * 16 * kAttSelNT / 8;  // selected chunks
 constexpr int kAttTokWave = 32;                              // window tokens per wave
 constexpr int kAttTokWG = kAttWaves * kAttTokWave;           // window tokens per workgroup
 constexpr int kPartStride = 2 + 128;                       // m, l, o[128] per query head
-constexpr int kMergeMaxWeights = 4096;                     // n_split * min(g, 16) limit of the merge
+constexpr int kMergeMaxSplits = 4096;                      // partial slots per head the merge takes
+constexpr int kPipeSplitsPerSeg = 4;                       // producer/consumer kernel: partial slots per segment
+
+// Division by a runtime divisor d >= 1 without a divide loop, for
+// 0 <= x < 2^31: q = (mulhi(x, m) + x) >> s with s = ceil(log2 d) and
+// m = floor(2^32 (2^s - d) / d) + 1 (the round-up method of Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994).
+struct FastDiv {
+  uint32_t m;
+  int s, d;
+};
+inline FastDiv make_fastdiv(int d) {
+  FastDiv f{0u, 0, d < 1 ? 1 : d};
+  while ((1ll << f.s) < f.d) ++f.s;
+  f.m = (uint32_t)((((1ull << 32) * ((1ull << f.s) - (unsigned long long)f.d)) / (unsigned long long)f.d) + 1ull);
+  return f;
+}
+__device__ __forceinline__ int fdiv(int x, const FastDiv& f) {
+  return (int)(((unsigned long long)__umulhi((uint32_t)x, f.m) + (uint32_t)x) >> f.s);
+}
 
 struct AttendArgs {
   const void* coeff;
@@ -49,17 +68,20 @@ struct AttendArgs {
   // (total = heads * n_split_launch workgroups, padded to a multiple of 8).
   int n_sel_tiles, n_win_tiles, n_split, total, padded_total;
   int split_base, n_split_launch;
-  // producer/consumer kernel: the pipe_tiles selection tiles of a head are cut
-  // into n_grp groups of tpw consecutive tiles (the last may be shorter), one
-  // workgroup and one partial slot (slot = group) each
-  int pipe_tiles, n_grp, tpw, pipe_total, pipe_padded;
+  // producer/consumer kernel: the pipe_tiles selection tiles of a head are
+  // cut into pipe_grp groups of pipe_tpw consecutive tiles (the last may be
+  // shorter); group g = head * pipe_grp + gx of the pipe_groups goes to
+  // workgroup g % pipe_wgs (grid padded to pipe_padded), and its 4 slots'
+  // partials to partial slots 4 gx .. 4 gx + 3 of the head
+  int pipe_tiles, pipe_grp, pipe_tpw, pipe_groups, pipe_wgs, pipe_padded;
+  FastDiv grp_div, hkv_div;  // by pipe_grp and by hkv
   float scale_log2;
   double inv_freq[64];
 };
 
-// Tiles per group and groups per head for the producer/consumer attention
-// kernel (one workgroup per CU at a time).
-void plan_pipe_groups(int heads, int n_tiles, int* n_grp, int* tpw);
+// Plan of the producer/consumer attention kernel: workgroups (one per CU at
+// most), tiles per group, groups per head.
+void plan_pipe(int heads, int n_tiles, int n_cu, int* n_wg, int* tpw, int* n_grp);
 hipError_t launch_attend_pipe(const AttendArgs& a, int rank, bool coeff_int4, bool resid_int4,
                               hipStream_t st);
 

@@ -31,24 +31,27 @@ def cache_to_device(cache):
     return {k: up(v) for k, v in cache.items() if k not in ("q", "needle")}
 
 
-def run_gpu(cfg, cache, stages=False, nb=None, attend=None):
+def run_gpu(cfg, cache, stages=False, nb=None, attend=None, pipe_cus=None):
     """Run the library on a fixture cache; returns (out fp64, sel, stage dict).
 
     attend: None (the library's own choice of kernel for the selected chunks),
     "pipe" (producer/consumer kernel) or "wave" (4-wave kernel); calls with
-    stage outputs always take the 4-wave kernel."""
+    stage outputs always take the 4-wave kernel.  pipe_cus: plan the
+    producer/consumer kernel for that many CUs (fewer, longer workgroups)."""
     import os
-    if attend is None:
-        return _run_gpu(cfg, cache, stages, nb)
-    old = os.environ.get("LOWRAM_ATTEND")
-    os.environ["LOWRAM_ATTEND"] = attend
+    env = {"LOWRAM_ATTEND": attend, "LOWRAM_PIPE_CUS": None if pipe_cus is None else str(pipe_cus)}
+    old = {k: os.environ.get(k) for k in env}
+    for k, v in env.items():
+        if v is not None:
+            os.environ[k] = v
     try:
         return _run_gpu(cfg, cache, stages, nb)
     finally:
-        if old is None:
-            del os.environ["LOWRAM_ATTEND"]
-        else:
-            os.environ["LOWRAM_ATTEND"] = old
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 def _run_gpu(cfg, cache, stages, nb):

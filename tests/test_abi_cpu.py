@@ -67,10 +67,13 @@ def test_workspace_bytes_formula():
     s = native.make_shape(cfg, batch=28)
     heads = 28 * 8
     keff = min(cfg.topk, cfg.n_cand)
-    # selected-chunk workgroups cover 16 chunks (4 waves x 32 tokens), window ones 128 tokens
-    n_split = -(-keff // 16) + -(-cfg.window // 128)
+    # selection tiles of 16 chunks (4 waves x 32 tokens), window tiles of 128
+    # tokens; partial slots reserved per head: 2 per selection tile + 6 (the
+    # producer/consumer kernel's 4 per group of >= 2 tiles) and 1 per window tile
+    n_sel = -(-keff // 16)
+    n_part = 2 * n_sel + 6 + -(-cfg.window // 128)
     al = lambda x: (x + 255) // 256 * 256
-    want = al(heads * cfg.n_cand * 4) + al(heads * keff * 4) + al(heads * n_split * 4 * 130 * 4)
+    want = al(heads * cfg.n_cand * 4) + al(heads * keff * 4) + al(heads * n_part * 4 * 130 * 4)
     assert native.workspace_bytes(s) == want
 
 

@@ -67,17 +67,27 @@ def run_case(cfg, layer=0, stages=True, batch=None):
     return res
 
 
-def pipe_tiles_per_group(heads, n_tiles, n_cu=256):
-    """Tiles per workgroup the library plans for the producer/consumer kernel
-    (least rounds x (tiles + 1), smallest on ties); restated to document which
-    cases run several tiles per workgroup."""
+def pipe_plan(heads, n_tiles, n_cu=256):
+    """The library's plan for the producer/consumer kernel, restated to document
+    what each case exercises: groups of t tiles (t >= 2 where a head has 2)
+    dealt round-robin to W = min(n_cu, groups) workgroups, t giving the fewest
+    ceil(groups / W) * t, the largest on ties.  Returns (W, t, groups per head,
+    the most tiles one workgroup runs, whether some workgroup runs several heads)."""
     best = None
-    for t in range(1, n_tiles + 1):
-        groups = -(-n_tiles // t)
-        cost = -(-heads * groups // n_cu) * (t + 1)
-        if best is None or cost < best[0]:
+    for t in range(min(2, n_tiles), n_tiles + 1):
+        groups = heads * -(-n_tiles // t)
+        w = min(n_cu, groups)
+        cost = -(-groups // w) * t
+        if best is None or cost <= best[0]:
             best = (cost, t)
-    return best[1]
+    t = best[1]
+    n_grp = -(-n_tiles // t)
+    groups = heads * n_grp
+    w = min(n_cu, groups)
+    size = [min(t, n_tiles - (g % n_grp) * t) for g in range(groups)]
+    load = [sum(size[g] for g in range(i, groups, w)) for i in range(w)]
+    several = any(len({g // n_grp for g in range(i, groups, w)}) > 1 for i in range(w))
+    return w, t, n_grp, max(load), several
 
 
 def test_c0_both_layers():
@@ -103,11 +113,13 @@ VARIANTS = {
     # batch 3, residual fraction 1 (every token has a residual)
     "batch3_allres": synth.C0.with_(name="batch3_allres", batch=3, resid_frac=1.0, topk=20),
     # 64 (sequence, KV head) pairs x 16 tiles: the producer/consumer kernel plans
-    # 4 tiles per workgroup (running softmax, handoff buffers and weight rings
-    # cycle through several tiles; a ragged last tile of 10 chunks), biases on
+    # 256 workgroups running 4 tiles (running softmax, handoff buffers and
+    # weight rings cycle through several tiles; a ragged last tile of 10
+    # chunks), biases on
     "multitile_b8": synth.C0.with_(name="multitile_b8", batch=8, n_heads_q=32, n_heads_kv=8, rank=128,
                                    topk=250, bias_std=0.1),
-    # the same with int4 coefficients and residuals and eviction (13 tiles, 4 per workgroup)
+    # the same with int4 coefficients and residuals and eviction (13 tiles per
+    # head: groups of unequal length)
     "multitile_int4_evict": synth.C4.with_(name="multitile_int4_evict", batch=8, ctx=4096, window=64, n_layers=4,
                                            topk=200, rank=128),
 }
@@ -117,7 +129,34 @@ VARIANTS = {
 def test_multitile_cases_plan_several_tiles(name):
     cfg = VARIANTS[name]
     n_tiles = -(-min(cfg.topk, cfg.n_cand) // 16)
-    assert pipe_tiles_per_group(cfg.batch * cfg.n_heads_kv, n_tiles) >= 4
+    heads = cfg.batch * cfg.n_heads_kv
+    # the library's own choice is the producer/consumer kernel (>= 2 tiles per CU)
+    assert heads * n_tiles >= 2 * 256
+    w, t, n_grp, most, several = pipe_plan(heads, n_tiles)
+    assert w == 256 and most >= 3 and n_grp >= 2
+
+
+# CU counts to plan for: one workgroup over every group, and few workgroups
+# each running the groups of many heads
+PIPE_CUS = (1, 7, 100)
+
+
+@pytest.mark.parametrize("name", ["multitile_b8", "multitile_int4_evict"])
+def test_pipe_long_ranges(name):
+    """The producer/consumer kernel planned for few CUs: each workgroup runs
+    many groups of different heads in one pipeline (head changes at group
+    boundaries, several groups per head), against the same oracle output."""
+    cfg = VARIANTS[name]
+    cache = fixture.build_layer(cfg, 1 if cfg.n_layers > 1 else 0)
+    res = full_parity(cfg, cache, stages=False)
+    n_tiles = -(-min(cfg.topk, cfg.n_cand) // 16)
+    for cus in PIPE_CUS:
+        w, t, n_grp, most, several = pipe_plan(cfg.batch * cfg.n_heads_kv, n_tiles, cus)
+        assert several
+        got, sel, _ = run_gpu(cfg, cache, stages=False, attend="pipe", pipe_cus=cus)
+        assert np.array_equal(sel, res["sel"])
+        check_output(got, res["ref"], f"{cfg.name} (pipe planned for {cus} CUs: {w} workgroups, "
+                                      f"groups of {t} tiles, {n_grp} per head, up to {most} tiles)")
 
 
 @pytest.mark.parametrize("name", list(VARIANTS))
