@@ -188,8 +188,9 @@ struct SelLds {  // the key array comes last: the L2-reading variant omits it
   uint32_t hist[kSelBins];
   uint32_t wsum[2][kSelWaves];
   uint32_t found[2];
-  uint32_t keys[kSelLdsKeys];
+  alignas(16) uint32_t keys[kSelLdsKeys];
 };
+constexpr int kSelBatch = 8;  // loads a thread has in flight at once
 
 // inclusive scan of x over the 64 lanes of a wave, from the highest lane down
 __device__ __forceinline__ uint32_t wave_scan_down(uint32_t x, int lane) {
@@ -228,7 +229,32 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     return;
   }
   if constexpr (kLds) {
-    for (int i = tid; i < n_cand; i += kSelThreads) S.keys[i] = kg[i];
+    // Every load of a batch goes out before the first store waits on one
+    // (a plain copy loop kept one load per thread in flight): 16-byte pieces
+    // when the list is 16-byte aligned, single keys otherwise.  Indices past
+    // the end are clamped to the last element, which is then stored again
+    // with its own value: no branch for the compiler to sink a load into.
+    if ((reinterpret_cast<uintptr_t>(kg) & 15) == 0 && n_cand >= 4) {
+      const int n4 = n_cand >> 2;
+      const uint4* kg4 = reinterpret_cast<const uint4*>(kg);
+      uint4* ks4 = reinterpret_cast<uint4*>(S.keys);
+      for (int i0 = tid; i0 < n4; i0 += kSelThreads * kSelBatch) {
+        uint4 v[kSelBatch];
+#pragma unroll
+        for (int u = 0; u < kSelBatch; ++u) v[u] = kg4[min(i0 + u * kSelThreads, n4 - 1)];
+#pragma unroll
+        for (int u = 0; u < kSelBatch; ++u) ks4[min(i0 + u * kSelThreads, n4 - 1)] = v[u];
+      }
+      for (int i = 4 * n4 + tid; i < n_cand; i += kSelThreads) S.keys[i] = kg[i];
+    } else {
+      for (int i0 = tid; i0 < n_cand; i0 += kSelThreads * kSelBatch) {
+        uint32_t v[kSelBatch];
+#pragma unroll
+        for (int u = 0; u < kSelBatch; ++u) v[u] = kg[min(i0 + u * kSelThreads, n_cand - 1)];
+#pragma unroll
+        for (int u = 0; u < kSelBatch; ++u) S.keys[min(i0 + u * kSelThreads, n_cand - 1)] = v[u];
+      }
+    }
   }
   const uint32_t* kv = kLds ? S.keys : kg;
 
@@ -241,9 +267,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint32_t dmask = (uint32_t)nbins - 1;
     for (int i = tid; i < nbins; i += kSelThreads) S.hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n_cand; i += kSelThreads) {
-      const uint32_t key = kv[i];
-      if ((key & pmask) == prefix) atomicAdd(&S.hist[(key >> shift) & dmask], 1u);
+    for (int i0 = tid; i0 < n_cand; i0 += kSelThreads * kSelBatch) {
+      uint32_t kx[kSelBatch];  // a batch of reads before its atomics
+#pragma unroll
+      for (int u = 0; u < kSelBatch; ++u) kx[u] = kv[min(i0 + u * kSelThreads, n_cand - 1)];
+#pragma unroll
+      for (int u = 0; u < kSelBatch; ++u)
+        if (i0 + u * kSelThreads < n_cand && (kx[u] & pmask) == prefix)
+          atomicAdd(&S.hist[(kx[u] >> shift) & dmask], 1u);
     }
     __syncthreads();
     // thread t owns bins [bpt*t, bpt*t + bpt); the digit D is the bin where
@@ -284,10 +315,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int w0 = min(n_cand, wave * per), w1 = min(n_cand, w0 + per);
   const uint64_t below = (1ull << lane) - 1;  // lanes under this one
   uint32_t ngt = 0, neq = 0;
-  for (int i = w0 + lane; i < w1 + 63; i += 64) {
-    const uint32_t key = i < w1 ? kv[i] : 0u;
-    ngt += __popcll(__ballot(i < w1 && key > T));
-    neq += __popcll(__ballot(i < w1 && key == T));
+  // batches of kSelBatch x 64 keys, read before they are counted (the batch
+  // loop is uniform over the wave, so every ballot sees all 64 lanes)
+  for (int b0 = w0; b0 < w1; b0 += 64 * kSelBatch) {
+    uint32_t kx[kSelBatch];
+#pragma unroll
+    for (int u = 0; u < kSelBatch; ++u) kx[u] = kv[min(b0 + 64 * u + lane, n_cand - 1)];
+#pragma unroll
+    for (int u = 0; u < kSelBatch; ++u) {
+      const bool in = b0 + 64 * u + lane < w1;
+      ngt += __popcll(__ballot(in && kx[u] > T));
+      neq += __popcll(__ballot(in && kx[u] == T));
+    }
   }
   if (lane == 0) {
     S.wsum[0][wave] = ngt;
@@ -299,23 +338,29 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     gt_run += S.wsum[0][w];
     eq_run += S.wsum[1][w];
   }
-  for (int i = w0 + lane; i < w1 + 63; i += 64) {
-    const bool in = i < w1;
-    const uint32_t key = in ? kv[i] : 0u;
-    const bool gt = in && key > T, eq = in && key == T;
-    const uint64_t mg = __ballot(gt), me = __ballot(eq);
-    const uint32_t gt_before = gt_run + __popcll(mg & below);
-    const uint32_t eq_before = eq_run + __popcll(me & below);
-    if (gt || (eq && eq_before < need)) {
-      const uint32_t pos = gt_before + min(eq_before, need);
-      if (pos < (uint32_t)k_eff) {
-        const int32_t c = ids ? ids[i] : i;
-        so[pos] = c;
-        if (so2) so2[pos] = c;
+  for (int b0 = w0; b0 < w1; b0 += 64 * kSelBatch) {
+    uint32_t kx[kSelBatch];
+#pragma unroll
+    for (int u = 0; u < kSelBatch; ++u) kx[u] = kv[min(b0 + 64 * u + lane, n_cand - 1)];
+#pragma unroll
+    for (int u = 0; u < kSelBatch; ++u) {
+      const int i = b0 + 64 * u + lane;
+      const bool in = i < w1;
+      const bool gt = in && kx[u] > T, eq = in && kx[u] == T;
+      const uint64_t mg = __ballot(gt), me = __ballot(eq);
+      const uint32_t gt_before = gt_run + __popcll(mg & below);
+      const uint32_t eq_before = eq_run + __popcll(me & below);
+      if (gt || (eq && eq_before < need)) {
+        const uint32_t pos = gt_before + min(eq_before, need);
+        if (pos < (uint32_t)k_eff) {
+          const int32_t c = ids ? ids[i] : i;
+          so[pos] = c;
+          if (so2) so2[pos] = c;
+        }
       }
+      gt_run += __popcll(mg);
+      eq_run += __popcll(me);
     }
-    gt_run += __popcll(mg);
-    eq_run += __popcll(me);
   }
 }
 
