@@ -725,7 +725,7 @@ hipError_t launch_attend(const AttendArgs& a, int rank, bool ci4, bool ri4, hipS
 // groups' sums meet in LDS.
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 512;
-constexpr int kMergeBatch = 8;
+constexpr int kMergeBatch = 16;
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part,
                                                               uint16_t* __restrict__ out, int hkv,
@@ -739,13 +739,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   const size_t st = (size_t)g * kPartStride;  // between splits
   const float* pj = part + head * (size_t)n_split * st + (size_t)j * kPartStride;
   const int ns = n_split;
-  // this thread's first batch of o values
+  // this thread's first batch of o values (indices clamped into the list,
+  // so that the loads are unconditional and all in flight together; the
+  // extra ones are not summed)
   float ov[kMergeBatch];
 #pragma unroll
-  for (int k = 0; k < kMergeBatch; ++k) {
-    const int sp = sg + 4 * k;
-    ov[k] = sp < ns ? pj[sp * st + 2 + d] : 0.f;
-  }
+  for (int k = 0; k < kMergeBatch; ++k) ov[k] = pj[min(sg + 4 * k, ns - 1) * st + 2 + d];
   if (tid < 64) {
     float m = -__builtin_huge_valf();
     for (int sp = tid; sp < ns; sp += 64) m = fmaxf(m, pj[sp * st]);
@@ -765,18 +764,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
 #pragma unroll
   for (int k = 0; k < kMergeBatch; ++k) {
     const int sp = sg + 4 * k;
-    if (sp < ns) acc += ov[k] * wgt[sp];
+    acc += sp < ns ? ov[k] * wgt[min(sp, ns - 1)] : 0.f;
   }
   for (int base = 4 * kMergeBatch; base < ns; base += 4 * kMergeBatch) {
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
-      const int sp = base + sg + 4 * k;
-      ov[k] = sp < ns ? pj[sp * st + 2 + d] : 0.f;
-    }
+    for (int k = 0; k < kMergeBatch; ++k) ov[k] = pj[min(base + sg + 4 * k, ns - 1) * st + 2 + d];
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) {
       const int sp = base + sg + 4 * k;
-      if (sp < ns) acc += ov[k] * wgt[sp];
+      acc += sp < ns ? ov[k] * wgt[min(sp, ns - 1)] : 0.f;
     }
   }
   if (sg > 0) red[sg - 1][d] = acc;
