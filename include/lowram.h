@@ -152,6 +152,28 @@ int lowram_decode_step(const lowram_shape* shape, const lowram_layer_cache* cach
                        void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * How lowram_decode_step schedules the selected chunks for `shape` on a
+ * device of n_cu CUs (a scheduling query, not an operation of the method;
+ * pure host computation, no HIP call).  mode: 0 the library's own choice,
+ * 1 producer/consumer kernel forced, 2 4-wave kernel forced (as
+ * LOWRAM_ATTEND=pipe / =wave).
+ *   kernel           0 no selected chunks, 1 producer/consumer, 2 4-wave
+ *   workgroups       producer/consumer kernel: min(n_cu, groups) (else 0)
+ *   tiles_per_group  128-token tiles per group (else 0)
+ *   groups_per_head  groups per (sequence, KV head) (else 0)
+ *   partial_slots    partial states per (sequence, KV head) the merge
+ *                    combines, window tiles included
+ *   reserved_slots   partial slots per (sequence, KV head) in the workspace
+ *                    (lowram_workspace_bytes), >= partial_slots
+ * Returns LOWRAM_ERR_NULL, the shape errors of lowram_workspace_bytes, or
+ * LOWRAM_ERR_SHAPE for n_cu < 1 or a mode outside 0..2.
+ */
+typedef struct lowram_attend_plan {
+  int32_t kernel, workgroups, tiles_per_group, groups_per_head, partial_slots, reserved_slots;
+} lowram_attend_plan;
+int lowram_decode_plan(const lowram_shape* shape, int n_cu, int mode, lowram_attend_plan* plan);
+
+/*
  * lowram_decode_step that also writes its intermediate stages (for stage
  * parity checks).  Every stage pointer may be NULL.
  *   scores_out [NB][Hkv][n_cand] fp32 landmark scores

@@ -100,6 +100,34 @@ Plan make_plan(const lowram_shape* s) {
   return p;
 }
 
+// Which kernel runs the selected chunks, and the producer/consumer kernel's
+// plan.  mode: 0 automatic, 1 producer/consumer forced, 2 4-wave forced.
+struct AttendPlan {
+  bool pipe;
+  int n_wg, tpw, n_grp, sel_slots, n_split;
+};
+AttendPlan attend_plan(const lowram_shape* s, const Plan& p, bool stage_outputs, int n_cu, int mode) {
+  // The producer/consumer kernel: one workgroup per CU working through
+  // groups of tiles, 4 partial slots per group.  It pays off once every CU
+  // gets several tiles (its pipeline fills and drains once per workgroup);
+  // small problems, every call that asks for stage outputs, and shapes whose
+  // partial slots would not fit the reserve or the merge run the 4-wave
+  // kernel (one slot per tile).  A forced mode overrides the size rule only.
+  // The exact window always goes to the 4-wave kernel, in the slots after
+  // the selection's.
+  const bool has_prefix = s->prefix_len > 0 && p.n_cand > 0;
+  const int heads = s->batch * s->n_heads_kv;
+  AttendPlan a{false, 0, 0, 0, 0, 0};
+  if (has_prefix) plan_pipe(heads, p.n_sel_tiles, n_cu, &a.n_wg, &a.tpw, &a.n_grp);
+  const long long all_tiles = (long long)heads * p.n_sel_tiles;
+  const int pipe_split = kPipeSplitsPerGroup * a.n_grp + p.n_win_tiles;
+  const bool fits = a.n_wg > 0 && pipe_split <= p.n_part && pipe_split <= kMergeMaxSplits;
+  a.pipe = has_prefix && !stage_outputs && fits && (mode == 0 ? all_tiles >= 2LL * n_cu : mode == 1);
+  a.sel_slots = !has_prefix ? 0 : a.pipe ? kPipeSplitsPerGroup * a.n_grp : p.n_sel_tiles;
+  a.n_split = a.sel_slots + p.n_win_tiles;
+  return a;
+}
+
 int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t* q, uint16_t* out,
              int32_t* sel_out, float* scores_out, float* kpre_out, float* kpost_out,
              float* vhat_out, void* ws, size_t ws_bytes, void* stream,
@@ -170,11 +198,6 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   a.cache_bmul = shared ? 0 : 1;
   a.prefix_cap = prefix_rows(s);
   a.window_cap = window_rows(s);
-  // Selected chunks: the producer/consumer kernel, one workgroup per CU
-  // working through groups of tiles, 4 partial slots per group; with stage
-  // outputs requested, the 4-wave kernel, one slot per tile.  The exact
-  // window always goes to the 4-wave kernel, in the slots after the
-  // selection's.
   const int heads = s->batch * s->n_heads_kv;
   int n_cu = pipe_cus_override();
   if (n_cu <= 0) {
@@ -184,36 +207,23 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
         hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0)
       n_cu = cu;
   }
-  int n_wg = 0, tpw = 0, n_grp = 0;
-  if (has_prefix) plan_pipe(heads, p.n_sel_tiles, n_cu, &n_wg, &tpw, &n_grp);
-  const long long all_tiles = (long long)heads * p.n_sel_tiles;
-  const int pipe_split = kPipeSplitsPerSeg * n_grp + p.n_win_tiles;
-  // The producer/consumer kernel pays off once every CU gets several tiles
-  // (its pipeline fills and drains once per workgroup); small problems, every
-  // call that asks for stage outputs, and shapes whose partial slots would not
-  // fit the reserve or the merge run the 4-wave kernel.
-  // LOWRAM_ATTEND=pipe or =wave overrides the choice (not those rules).
-  const int mode = attend_mode();
-  const bool pipe_fits = n_wg > 0 && pipe_split <= p.n_part &&
-                         pipe_split <= kMergeMaxSplits;
-  const bool wave4 = kpre_out || kpost_out || vhat_out || !pipe_fits ||
-                     (mode == 0 ? all_tiles < 2LL * n_cu : mode == 2);
-  const int sel_slots = !has_prefix ? 0 : wave4 ? p.n_sel_tiles : kPipeSplitsPerSeg * n_grp;
-  const int n_split = sel_slots + p.n_win_tiles;
-  a.n_sel_tiles = sel_slots;
+  const AttendPlan ap = attend_plan(s, p, kpre_out || kpost_out || vhat_out, n_cu, attend_mode());
+  const bool wave4 = !ap.pipe;
+  const int n_split = ap.n_split;
+  a.n_sel_tiles = ap.sel_slots;
   a.n_win_tiles = p.n_win_tiles;
   a.n_split = n_split;
-  a.split_base = wave4 ? 0 : sel_slots;
+  a.split_base = wave4 ? 0 : ap.sel_slots;
   a.n_split_launch = wave4 ? n_split : p.n_win_tiles;
   a.total = heads * a.n_split_launch;
   a.padded_total = (a.total + 7) & ~7;
   a.pipe_tiles = p.n_sel_tiles;
-  a.pipe_grp = n_grp;
-  a.pipe_tpw = tpw;
-  a.pipe_groups = wave4 ? 0 : heads * n_grp;
-  a.pipe_wgs = wave4 ? 0 : n_wg;
+  a.pipe_grp = ap.n_grp;
+  a.pipe_tpw = ap.tpw;
+  a.pipe_groups = wave4 ? 0 : heads * ap.n_grp;
+  a.pipe_wgs = wave4 ? 0 : ap.n_wg;
   a.pipe_padded = (a.pipe_wgs + 7) & ~7;
-  a.grp_div = make_fastdiv(n_grp);
+  a.grp_div = make_fastdiv(ap.n_grp);
   a.hkv_div = make_fastdiv(s->n_heads_kv);
   a.scale_log2 = s->softmax_scale * 1.4426950408889634f;
   for (int i = 0; i < 64; ++i)
@@ -310,6 +320,23 @@ int lowram_workspace_bytes(const lowram_shape* shape, size_t* bytes) {
   const int st = check_shape(shape);
   if (st) return st;
   *bytes = make_plan(shape).total;
+  return LOWRAM_OK;
+}
+
+int lowram_decode_plan(const lowram_shape* shape, int n_cu, int mode, lowram_attend_plan* plan) {
+  if (!plan) return LOWRAM_ERR_NULL;
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (n_cu < 1 || mode < 0 || mode > 2) return LOWRAM_ERR_SHAPE;
+  const Plan p = make_plan(shape);
+  const AttendPlan a = attend_plan(shape, p, false, n_cu, mode);
+  const bool has_prefix = shape->prefix_len > 0 && p.n_cand > 0;
+  plan->kernel = !has_prefix ? 0 : a.pipe ? 1 : 2;
+  plan->workgroups = a.pipe ? a.n_wg : 0;
+  plan->tiles_per_group = a.pipe ? a.tpw : 0;
+  plan->groups_per_head = a.pipe ? a.n_grp : 0;
+  plan->partial_slots = a.n_split;
+  plan->reserved_slots = p.n_part;
   return LOWRAM_OK;
 }
 

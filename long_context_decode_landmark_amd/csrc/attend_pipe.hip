@@ -52,7 +52,7 @@
 
 namespace lowram {
 
-constexpr int kPipeSlots = kPipeSplitsPerSeg;  // producer/consumer pairs (one partial slot each)
+constexpr int kPipeSlots = kPipeSplitsPerGroup;  // producer/consumer pairs (one partial slot each)
 constexpr int kPipeThreads = 2 * kPipeSlots * 64;
 constexpr int kPipeSteps = kHidden / 32;      // value stages = steps per tile-step
 constexpr int kHandSlot = 9216;               // per slot: K_pre operands (8 KiB), then p (1 KiB)
@@ -73,7 +73,7 @@ struct PipeLds {
   // 16-byte piece p of the row at piece p ^ j
   alignas(16) _Float16 qh[16][kHeadDim];
   // per tile parity: b1 of unit 32 c + row_perm32(p) at 32 c + p, x4 (an MFMA
-  // C operand), and b2 (read when a segment's partial is written)
+  // C operand), and b2 (read when a group's partial is written)
   f32x4 b1q[2][kHidden];
   float b2f[2][kHeadDim];
   double invf[64];                       // RoPE frequencies (read where needed: no registers held)
@@ -784,7 +784,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     }
     {
       // the last tile's last stage (its W2 buffer is not written again), and
-      // the partial of the last segment
+      // the partial of the last group
       bf16x8 w2op[8];
       read_w2(NS - 1, w2op);
       finish_stage(NS - 1, w2op, pa);

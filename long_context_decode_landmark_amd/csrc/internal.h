@@ -18,7 +18,7 @@ constexpr int kAttTokWave = 32;                              // window tokens pe
 constexpr int kAttTokWG = kAttWaves * kAttTokWave;           // window tokens per workgroup
 constexpr int kPartStride = 2 + 128;                       // m, l, o[128] per query head
 constexpr int kMergeMaxSplits = 4096;                      // partial slots per head the merge takes
-constexpr int kPipeSplitsPerSeg = 4;                       // producer/consumer kernel: partial slots per segment
+constexpr int kPipeSplitsPerGroup = 4;                     // producer/consumer kernel: partial slots per group of tiles
 
 // Division by a runtime divisor d >= 1 without a divide loop, for
 // 0 <= x < 2^31: q = (mulhi(x, m) + x) >> s with s = ceil(log2 d) and

@@ -21,6 +21,7 @@ SYMBOLS = (
     "lowram_abi_version",
     "lowram_strerror",
     "lowram_workspace_bytes",
+    "lowram_decode_plan",
     "lowram_decode_step",
     "lowram_decode_stages",
     "lowram_decode_step_events",
@@ -39,6 +40,11 @@ SYMBOLS = (
 )
 
 ERRORS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "UNSUPPORTED", -4: "WORKSPACE", -5: "ALIGN", -6: "HIP"}
+
+
+class LowramAttendPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "kernel", "workgroups", "tiles_per_group", "groups_per_head", "partial_slots", "reserved_slots")]
 
 
 class LowramShape(ctypes.Structure):
@@ -116,6 +122,8 @@ def lib() -> ctypes.CDLL:
         L.lowram_strerror.restype = ctypes.c_char_p
         L.lowram_strerror.argtypes = [ctypes.c_int]
         L.lowram_workspace_bytes.argtypes = [ctypes.POINTER(LowramShape), ctypes.POINTER(sz)]
+        L.lowram_decode_plan.argtypes = [ctypes.POINTER(LowramShape), ctypes.c_int, ctypes.c_int,
+                                         ctypes.POINTER(LowramAttendPlan)]
         L.lowram_decode_step.argtypes = [ctypes.POINTER(LowramShape), ctypes.POINTER(LowramLayerCache),
                                          vp, vp, vp, vp, sz, vp]
         L.lowram_decode_stages.argtypes = [ctypes.POINTER(LowramShape), ctypes.POINTER(LowramLayerCache),
@@ -205,6 +213,15 @@ def workspace_bytes(shape: LowramShape) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().lowram_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)), "lowram_workspace_bytes")
     return n.value
+
+
+def decode_plan(shape: LowramShape, n_cu: int, mode: int = 0) -> dict:
+    """lowram_decode_plan: how the selected chunks are scheduled on n_cu CUs
+    (mode 0 automatic, 1 producer/consumer forced, 2 4-wave forced)."""
+    p = LowramAttendPlan()
+    _check(lib().lowram_decode_plan(ctypes.byref(shape), int(n_cu), int(mode), ctypes.byref(p)),
+           "lowram_decode_plan")
+    return {n: getattr(p, n) for n, _ in LowramAttendPlan._fields_}
 
 
 def decode_step(shape, cache, q, out, workspace, sel_out=None, stream=None) -> None:

@@ -23,6 +23,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("no GPU", allow_module_level=True)
 
 from gpu_util import check_output, full_parity, run_gpu  # noqa: E402
+from plan_util import pipe_plan  # noqa: E402
 from oracle import fixture  # noqa: E402
 
 
@@ -65,29 +66,6 @@ def run_case(cfg, layer=0, stages=True, batch=None):
             assert np.array_equal(sel, res["sel"])
             check_output(got, res["ref"], f"{cfg.name} (plain step, {attend or 'auto'})")
     return res
-
-
-def pipe_plan(heads, n_tiles, n_cu=256):
-    """The library's plan for the producer/consumer kernel, restated to document
-    what each case exercises: groups of t tiles (t >= 2 where a head has 2)
-    dealt round-robin to W = min(n_cu, groups) workgroups, t giving the fewest
-    ceil(groups / W) * t, the largest on ties.  Returns (W, t, groups per head,
-    the most tiles one workgroup runs, whether some workgroup runs several heads)."""
-    best = None
-    for t in range(min(2, n_tiles), n_tiles + 1):
-        groups = heads * -(-n_tiles // t)
-        w = min(n_cu, groups)
-        cost = -(-groups // w) * t
-        if best is None or cost <= best[0]:
-            best = (cost, t)
-    t = best[1]
-    n_grp = -(-n_tiles // t)
-    groups = heads * n_grp
-    w = min(n_cu, groups)
-    size = [min(t, n_tiles - (g % n_grp) * t) for g in range(groups)]
-    load = [sum(size[g] for g in range(i, groups, w)) for i in range(w)]
-    several = any(len({g // n_grp for g in range(i, groups, w)}) > 1 for i in range(w))
-    return w, t, n_grp, max(load), several
 
 
 def test_c0_both_layers():
