@@ -8,8 +8,10 @@
 #include "common.h"
 #include "internal.h"
 
+// Grid cap of the score kernel (measured at 262K context, batch 28: 16384,
+// i.e. 512 chunks per workgroup, beat 2048-8192 by 3-5% and 32768 by 1-2%)
 #ifndef LOWRAM_SCORE_MAX_WG
-#define LOWRAM_SCORE_MAX_WG 8192
+#define LOWRAM_SCORE_MAX_WG 16384
 #endif
 
 namespace lowram {
