@@ -7,6 +7,10 @@ sampled (sequence, KV head) slices one by one from the same arrays copied to
 the host: selection within the tie band, that head's output within the
 decode tolerance against the oracle re-run on the GPU's selection.  Every
 output of the batch must be finite, and every selection ascending and full.
+Every (sequence, KV head) is then checked by a property: the 4-wave kernel on
+the same batch selects the same chunks and agrees within twice the tolerance
+(at these sizes the library runs the producer/consumer kernel, whose
+workgroups switch heads inside their pipelines).
 """
 import numpy as np
 import pytest
@@ -19,7 +23,7 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("no GPU", allow_module_level=True)
 
-from gpu_util import DEV, check_output, check_selection, down_bf16  # noqa: E402
+from gpu_util import DEV, MAX_ABS, REL_L2, check_output, check_selection, down_bf16  # noqa: E402
 from long_context_decode_landmark_amd import native  # noqa: E402
 from oracle import decode  # noqa: E402
 from synth import device as sd  # noqa: E402
@@ -94,3 +98,29 @@ def test_full_size_sampled_heads(name, nb):
         ref, _ = decode.decode_head(cfg, sl, qs, 0, 0, sel_override=sel_h[b, h])
         rel, mx = check_output(got[b, h * g:(h + 1) * g], ref, f"{name} b{b} h{h}")
         print(f"{name} b{b} h{h}: rel {rel:.2e} max {mx:.2e} flips {nflip}", flush=True)
+
+    # Every head, by a property: the same batch through the other attention
+    # kernel (LOWRAM_ATTEND=wave) must select the same chunks, and since each
+    # kernel meets the decode tolerance against the oracle, the two outputs of
+    # each (sequence, KV head) must agree within twice it.
+    import os
+    old = os.environ.get("LOWRAM_ATTEND")
+    os.environ["LOWRAM_ATTEND"] = "wave"
+    try:
+        out_w = torch.empty_like(q)
+        sel_w = torch.full_like(sel, -7)
+        native.decode_step(shape, native.make_cache(cache), q, out_w, ws, sel_out=sel_w)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            os.environ.pop("LOWRAM_ATTEND", None)
+        else:
+            os.environ["LOWRAM_ATTEND"] = old
+    assert torch.equal(sel_w, sel)
+    a = got.reshape(nb, cfg.n_heads_kv, -1)
+    w = down_bf16(out_w).reshape(nb, cfg.n_heads_kv, -1)
+    rel = np.linalg.norm(a - w, axis=-1) / np.linalg.norm(w, axis=-1)
+    mx = np.max(np.abs(a - w), axis=-1)
+    print(f"{name}: every head against the 4-wave kernel: rel <= {rel.max():.2e}, max <= {mx.max():.2e}",
+          flush=True)
+    assert rel.max() <= 2 * REL_L2 and mx.max() <= 2 * MAX_ABS
