@@ -69,12 +69,12 @@ typedef struct lowram_shape {
   int32_t batch;         /* NB >= 1 sequences                                        */
   int32_t prefix_len;    /* P >= 0 compressed tokens, a multiple of chunk            */
   int32_t window;        /* W >= 0 exact recent tokens at positions P .. P+W-1       */
-  int32_t chunk;         /* S, tokens per chunk; this build supports 8               */
+  int32_t chunk;         /* S, tokens per chunk; the library supports 8              */
   int32_t n_heads_q;     /* Hq, a multiple of n_heads_kv, Hq/Hkv <= 16               */
   int32_t n_heads_kv;    /* Hkv >= 1                                                 */
-  int32_t head_dim;      /* d; this build supports 128                               */
+  int32_t head_dim;      /* d; the library supports 128                              */
   int32_t rank;          /* r, coefficients per token; 64, 128, 256 or 512           */
-  int32_t mlp_hidden;    /* H, value-MLP width; this build supports 256              */
+  int32_t mlp_hidden;    /* H, value-MLP width; the library supports 256             */
   int32_t topk;          /* k >= 1 chunks kept per KV head (all if fewer candidates) */
   int32_t n_resid;       /* nR >= 0 stored residual rows per (sequence, KV head)     */
   int32_t n_cand;        /* candidates per (sequence, KV head): P/S without eviction,
@@ -259,12 +259,12 @@ typedef struct lowram_build_shape {
   int32_t batch;         /* NB >= 1 sequences                                          */
   int32_t ctx_len;       /* T >= 1 tokens of exact keys / values per sequence          */
   int32_t window;        /* W, 0 <= W <= T: tokens P .. T-1 stay exact, P = T - W      */
-  int32_t chunk;         /* S; P must be a multiple of it; this build supports 8       */
+  int32_t chunk;         /* S; P must be a multiple of it; the library supports 8      */
   int32_t n_heads_kv;    /* Hkv >= 1                                                   */
-  int32_t head_dim;      /* d; this build supports 128                                 */
+  int32_t head_dim;      /* d; the library supports 128                                */
   int32_t rank;          /* r; 64, 128, 256 or 512 (int4 coefficients: 128 and up)     */
   int32_t group_layers;  /* G >= 1 layers sharing one basis; key width D = G * Hkv * d */
-  int32_t mlp_hidden;    /* H; this build supports 256                                 */
+  int32_t mlp_hidden;    /* H; the library supports 256                                */
   int32_t n_resid;       /* nR, 0 <= nR <= P residual rows kept per (sequence, head)   */
   int32_t coeff_fmt;     /* LOWRAM_FMT_* of the coefficients written                   */
   int32_t resid_fmt;     /* LOWRAM_FMT_* of the residual rows written                  */

@@ -307,7 +307,7 @@ const char* lowram_strerror(int status) {
     case LOWRAM_OK: return "ok";
     case LOWRAM_ERR_NULL: return "a required pointer is NULL";
     case LOWRAM_ERR_SHAPE: return "inconsistent shape";
-    case LOWRAM_ERR_UNSUPPORTED: return "shape not supported by this build";
+    case LOWRAM_ERR_UNSUPPORTED: return "shape not supported by this library";
     case LOWRAM_ERR_WORKSPACE: return "workspace too small";
     case LOWRAM_ERR_ALIGN: return "misaligned pointer";
     case LOWRAM_ERR_HIP: return "HIP launch failed";

@@ -197,7 +197,7 @@ def make_shape(cfg, batch: int | None = None, **over) -> LowramShape:
 def make_cache(tensors: dict) -> LowramLayerCache:
     """The C struct of device pointers. It keeps references to the tensors, so
     their memory stays allocated for as long as the struct is in use (a freed
-    block can be returned to the driver, e.g. by torch.cuda.empty_cache())."""
+    block can be returned to the HIP runtime, e.g. by torch.cuda.empty_cache())."""
     c = LowramLayerCache(**{n: (tensors[n].data_ptr() if tensors.get(n) is not None else None)
                             for n in CACHE_FIELDS})
     c._tensors = dict(tensors)
