@@ -587,10 +587,13 @@ def bench_append(args):
         L["dropped"] = torch.zeros((nb, Hkv), dtype=torch.int32, device=dev)
         layers.append(L)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 + G)]
-    acc = {"coeff": 0.0, "layer": 0.0}
+    # one event set per timed step, so that the steps are enqueued back to back
+    # (a host synchronisation between them would leave the GPU idle while the
+    # next step's first launch is submitted, inside the first kernel's interval)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + G)] for _ in range(args.steps)]
 
-    def step(k, record):
+    def step(k, ev):
+        record = ev is not None
         P0, W0 = P + k * S, W - k * S
         sh = native.make_shape(cfg, batch=nb, prefix_len=P0, window=W0, n_cand=P0 // S, n_resid=rcap,
                                prefix_cap=pcap, window_cap=W)
@@ -609,23 +612,20 @@ def bench_append(args):
                 ev[2 + li].record()
 
     for k in range(args.warmup):
-        step(k, False)
-    for e in ev:
-        e.record()
+        step(k, None)
+    for ev in evs:
+        for e in ev:
+            e.record()  # creates the underlying hipEvent
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    tot = 0.0
-    for k in range(args.warmup, n_app):
-        t0.record()
-        step(k, True)
-        t1.record()
-        torch.cuda.synchronize()
-        tot += t0.elapsed_time(t1)
-        acc["coeff"] += ev[0].elapsed_time(ev[1])
-        acc["layer"] += ev[1].elapsed_time(ev[1 + G]) / G
-    step_ms = tot / args.steps
-    per_layer_us = acc["layer"] / args.steps * 1e3
-    coeff_us = acc["coeff"] / args.steps * 1e3
+    t0.record()
+    for i, k in enumerate(range(args.warmup, n_app)):
+        step(k, evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / args.steps
+    per_layer_us = sum(ev[1].elapsed_time(ev[1 + G]) / G for ev in evs) / args.steps * 1e3
+    coeff_us = sum(ev[0].elapsed_time(ev[1]) for ev in evs) / args.steps * 1e3
     # fp32 FMA work of the rollover kernel per layer: per (sequence, head, token) the
     # rebuild (d r) and the MLP (2 d H) multiply-adds
     H = cfg.mlp_hidden
