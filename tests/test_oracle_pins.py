@@ -150,6 +150,21 @@ def test_dense_step_against_sdpa():
     assert np.allclose(ours, ref, atol=1e-12)
 
 
+def test_decode_without_prefix_is_window_attention():
+    """With no compressed prefix (a sequence still inside its first window)
+    the decode step has nothing to score or rebuild: it is exact GQA
+    attention of the queries over the window's keys and values."""
+    cfg = synth.C0.with_(name="window_only", batch=2, ctx=40, window=40, topk=4)
+    cache = fixture.build_layer(cfg, 0)
+    out, st = decode.decode_step(cfg, cache, cache["q"])
+    assert all(len(v["sel"]) == 0 for v in st.values())
+    k = torch.from_numpy(decode.widen(cache["win_k"])).repeat_interleave(cfg.gqa, dim=1)
+    v = torch.from_numpy(decode.widen(cache["win_v"])).repeat_interleave(cfg.gqa, dim=1)
+    q = torch.from_numpy(decode.widen(cache["q"]))[:, :, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v)[:, :, 0].numpy()
+    assert np.allclose(out, ref, atol=1e-12)
+
+
 # ---------------------------------------------------- landmark / topk --
 def test_landmark_scores_max_over_group():
     rng = np.random.default_rng(9)
