@@ -131,6 +131,16 @@ def test_step_rejects_misalignment():
     assert call_step(s, c) == -5
 
 
+def test_step_rejects_more_partial_states_than_the_merge_combines():
+    # a window of 4096 tiles of 128 tokens gives the merge its most partial
+    # states per (sequence, KV head), 4096; one token more is refused before
+    # any HIP call
+    s = shape(prefix_len=0, n_cand=0, n_resid=0, window=4096 * 128 + 1)
+    assert call_step(s, fake_cache()) == -3
+    assert native.decode_plan(shape(prefix_len=0, n_cand=0, n_resid=0, window=4096 * 128), 256)[
+        "partial_slots"] == 4096
+
+
 def test_step_requires_int4_scales_and_candidates():
     s = shape(rank=128, coeff_fmt=1)
     assert call_step(s, fake_cache()) == -1          # coeff_scale missing

@@ -154,6 +154,18 @@ def test_variants(name):
     print(f"{name}: rel {res['rel']:.2e} max {res['max_abs']:.2e} flips {res['flips']}")
 
 
+def test_merge_at_its_split_limit():
+    """The most partial states the merge combines per (sequence, KV head),
+    4096: a window-only step over 4096 tiles of 128 tokens (524288 exact
+    window tokens), one 4-wave workgroup per tile."""
+    from long_context_decode_landmark_amd import native
+    cfg = synth.C0.with_(name="merge_limit", ctx=4096 * 128, window=4096 * 128, n_heads_q=4, n_heads_kv=1,
+                         topk=4)
+    assert native.decode_plan(native.make_shape(cfg), 256)["partial_slots"] == 4096
+    res = run_case(cfg, layer=1)
+    print(f"merge_limit: rel {res['rel']:.2e} max {res['max_abs']:.2e}")
+
+
 def test_deterministic_bitwise():
     cfg = synth.C0
     cache = fixture.build_layer(cfg, 0)
