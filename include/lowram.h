@@ -48,7 +48,8 @@ enum {
   LOWRAM_OK = 0,
   LOWRAM_ERR_NULL = -1,        /* a required pointer is NULL                         */
   LOWRAM_ERR_SHAPE = -2,       /* inconsistent sizes (e.g. Hq % Hkv, P % S, k < 1)   */
-  LOWRAM_ERR_UNSUPPORTED = -3, /* valid but not built (d != 128, S != 8, H != 256...) */
+  LOWRAM_ERR_UNSUPPORTED = -3, /* valid but not built (d != 128, S != 8, H != 256,
+                                  or NB * Hkv * (attention tiles) >= 2^31) */
   LOWRAM_ERR_WORKSPACE = -4,   /* workspace smaller than *_workspace_bytes reports    */
   LOWRAM_ERR_ALIGN = -5,       /* misaligned pointer                                 */
   LOWRAM_ERR_HIP = -6          /* a HIP launch failed                                */
@@ -66,12 +67,12 @@ enum {
 
 /* Sizes of one layer's decode step. */
 typedef struct lowram_shape {
-  int32_t batch;         /* NB >= 1 sequences                                        */
+  int32_t batch;         /* 1 <= NB <= 65535 sequences                               */
   int32_t prefix_len;    /* P >= 0 compressed tokens, a multiple of chunk            */
   int32_t window;        /* W >= 0 exact recent tokens at positions P .. P+W-1       */
   int32_t chunk;         /* S, tokens per chunk; the library supports 8              */
   int32_t n_heads_q;     /* Hq, a multiple of n_heads_kv, Hq/Hkv <= 16               */
-  int32_t n_heads_kv;    /* Hkv >= 1                                                 */
+  int32_t n_heads_kv;    /* 1 <= Hkv <= 65535                                        */
   int32_t head_dim;      /* d; the library supports 128                              */
   int32_t rank;          /* r, coefficients per token; 64, 128, 256 or 512           */
   int32_t mlp_hidden;    /* H, value-MLP width; the library supports 256             */

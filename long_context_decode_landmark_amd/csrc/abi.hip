@@ -55,6 +55,13 @@ int check_shape(const lowram_shape* s) {
   // 32-bit index arithmetic inside the kernels
   if ((int64_t)s->batch * (s->prefix_cap ? s->prefix_cap : s->prefix_len) >= (int64_t)1 << 31)
     return LOWRAM_ERR_UNSUPPORTED;
+  // grid limits: sequences and KV heads index the y and z grid dimensions
+  // (at most 65535), and the 4-wave grid has one workgroup per (sequence,
+  // KV head, tile), counted in 32 bits
+  if (s->batch > 65535 || s->n_heads_kv > 65535) return LOWRAM_ERR_UNSUPPORTED;
+  const int64_t k_eff = s->n_cand < s->topk ? s->n_cand : s->topk;
+  const int64_t tiles = (k_eff + kAttChunksWG - 1) / kAttChunksWG + (s->window + kAttTokWG - 1) / kAttTokWG;
+  if ((int64_t)s->batch * s->n_heads_kv * tiles >= (int64_t)1 << 31) return LOWRAM_ERR_UNSUPPORTED;
   return LOWRAM_OK;
 }
 

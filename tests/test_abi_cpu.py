@@ -54,6 +54,10 @@ def ws_bytes(**kw):
     (dict(rank=96), -3),
     (dict(n_heads_q=64, n_heads_kv=2), -3),   # GQA group above 16
     (dict(coeff_fmt=1), -3),            # int4 needs rank % 128 == 0 (rank 64 here)
+    (dict(batch=65536), -3),            # sequences index a grid dimension of at most 65535
+    (dict(n_heads_q=65536, n_heads_kv=65536), -3),
+    # (sequence, KV head, tile) workgroups of the 4-wave grid counted in 32 bits
+    (dict(batch=32768, n_heads_q=32, n_heads_kv=16, prefix_len=0, n_cand=0, n_resid=0, window=4096 * 128), -3),
 ])
 def test_workspace_bytes_rejects_shapes(kw, code):
     with pytest.raises(native.LowramError) as e:
