@@ -244,6 +244,7 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   return LOWRAM_OK;
 }
 
+constexpr int kDenseTokPerSplit = 2048;
 int check_dense(const dense_shape* s) {
   if (!s) return LOWRAM_ERR_NULL;
   if (s->batch < 1 || s->ctx_len < 1 || s->n_heads_q < 1 || s->n_heads_kv < 1 || s->head_dim < 1)
@@ -251,6 +252,11 @@ int check_dense(const dense_shape* s) {
   if (s->n_heads_q % s->n_heads_kv) return LOWRAM_ERR_SHAPE;
   if (!std::isfinite(s->softmax_scale)) return LOWRAM_ERR_SHAPE;
   if (s->head_dim != kHeadDim || s->n_heads_q / s->n_heads_kv > 16) return LOWRAM_ERR_UNSUPPORTED;
+  // grid limits, as for the decode step
+  if (s->batch > 65535 || s->n_heads_kv > 65535) return LOWRAM_ERR_UNSUPPORTED;
+  if ((int64_t)s->batch * s->n_heads_kv * ((s->ctx_len + kDenseTokPerSplit - 1) / kDenseTokPerSplit) >=
+      (int64_t)1 << 31)
+    return LOWRAM_ERR_UNSUPPORTED;
   return LOWRAM_OK;
 }
 
@@ -279,6 +285,7 @@ int check_build_shape(const lowram_build_shape* s) {
   if ((int64_t)s->batch * s->ctx_len >= (int64_t)1 << 31) return LOWRAM_ERR_UNSUPPORTED;
   if ((int64_t)s->batch * s->prefix_cap >= (int64_t)1 << 31) return LOWRAM_ERR_UNSUPPORTED;
   if ((int64_t)s->group_layers * s->n_heads_kv * kHeadDim >= (int64_t)1 << 20) return LOWRAM_ERR_UNSUPPORTED;
+  if (s->batch > 65535) return LOWRAM_ERR_UNSUPPORTED;  // a grid dimension of at most 65535
   return LOWRAM_OK;
 }
 
@@ -299,7 +306,6 @@ BuildPlan make_build_plan(const lowram_build_shape* s) {
   return p;
 }
 
-constexpr int kDenseTokPerSplit = 2048;
 
 int dense_splits(const dense_shape* s) { return (s->ctx_len + kDenseTokPerSplit - 1) / kDenseTokPerSplit; }
 
@@ -627,6 +633,7 @@ int check_fit(const lowram_fit_shape* s) {
   if (s->power > 4) return LOWRAM_ERR_UNSUPPORTED;
   if ((int64_t)s->ctx_len * s->group_dim >= (int64_t)1 << 31 || (int64_t)s->prefix_len * s->rank >= (int64_t)1 << 31)
     return LOWRAM_ERR_UNSUPPORTED;
+  if (s->batch > 65535) return LOWRAM_ERR_UNSUPPORTED;  // a grid dimension of at most 65535
   return LOWRAM_OK;
 }
 }  // namespace

@@ -156,6 +156,11 @@ def test_dense_rejects():
     with pytest.raises(native.LowramError) as e:
         native.dense_workspace_bytes(native.dense_shape(1, 100, 7, 2))
     assert e.value.status == -2
+    for bad in (native.dense_shape(65536, 100, 8, 2),          # grid dimension limit
+                native.dense_shape(32768, 4096 * 2048, 32, 16)):  # 2^31 (sequence, head, split) workgroups
+        with pytest.raises(native.LowramError) as e:
+            native.dense_workspace_bytes(bad)
+        assert e.value.status == -3
     s = native.dense_shape(1, 100, 8, 2)
     need = native.dense_workspace_bytes(s)
     with pytest.raises(native.LowramError) as e:
@@ -191,6 +196,7 @@ def bshape(**kw):
     (dict(rank=96), -3),
     (dict(mlp_hidden=512), -3),
     (dict(coeff_fmt=1), -3),            # int4 coefficients need rank % 128 == 0
+    (dict(batch=65536), -3),            # sequences index a grid dimension of at most 65535
 ])
 def test_build_workspace_rejects_shapes(kw, code):
     with pytest.raises(native.LowramError) as e:
@@ -304,6 +310,7 @@ def test_fit_basis_rejects():
             native.fit_basis_workspace_bytes(s)
         return e.value.status
     assert st(native.fit_shape(1, 4096, 4000, 512, 64)) == -3      # P not a multiple of 64
+    assert st(native.fit_shape(65536, 4096, 4096, 512, 64)) == -3  # a grid dimension of at most 65535
     assert st(native.fit_shape(1, 4096, 4032, 500, 64)) == -3      # D not a multiple of 128
     assert st(native.fit_shape(1, 4096, 4032, 512, 96)) == -3      # rank
     assert st(native.fit_shape(1, 4096, 8192, 512, 64)) == -2      # P > T
