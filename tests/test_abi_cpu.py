@@ -145,6 +145,15 @@ def test_step_rejects_more_partial_states_than_the_merge_combines():
         "partial_slots"] == 4096
 
 
+def test_shapes_at_the_grid_limits_are_accepted():
+    # one below each limit that a rejection test above crosses
+    assert ws_bytes(batch=65535) > 0
+    assert ws_bytes(batch=32767, n_heads_q=32, n_heads_kv=16, prefix_len=0, n_cand=0, n_resid=0,
+                    window=4096 * 128) > 0
+    assert native.dense_workspace_bytes(native.dense_shape(65535, 100, 8, 2)) > 0
+    assert native.dense_workspace_bytes(native.dense_shape(32767, 4096 * 2048, 32, 16)) > 0
+
+
 def test_step_requires_int4_scales_and_candidates():
     s = shape(rank=128, coeff_fmt=1)
     assert call_step(s, fake_cache()) == -1          # coeff_scale missing
