@@ -5,6 +5,8 @@
 // current query and rebuilds only the top-k.  The score of chunk c for KV
 // head h is the maximum over h's query heads j of q_j . L[c]; the k largest
 // are kept, exact ties to the lower chunk id, output in ascending chunk id.
+#include <atomic>
+
 #include "common.h"
 #include "internal.h"
 
@@ -633,12 +635,17 @@ hipError_t launch_select(const uint32_t* keys, const int32_t* cand_ids, int32_t*
                          int cache_bmul) {
   if (n_cand <= 0 && !sel_out) return hipSuccess;
   const dim3 grid(hkv, nb), block(kSelThreads);
-  static bool attr_set = false;  // dynamic LDS above 64 KiB must be allowed once
-  if (!attr_set) {
+  // dynamic LDS above 64 KiB must be allowed once per device (the attribute
+  // belongs to the function on the current device); bit d: done on device d
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  const uint64_t bit = dev >= 0 && dev < 64 ? 1ull << dev : 0;  // devices past 63: set on every call
+  if (!bit || !(attr_set.load(std::memory_order_acquire) & bit)) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(select_kernel<true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SelLds)) != hipSuccess)
       return hipErrorInvalidValue;
-    attr_set = true;
+    attr_set.fetch_or(bit, std::memory_order_release);
   }
   if (n_cand <= kSelLdsKeys) {
     hipLaunchKernelGGL(select_kernel<true>, grid, block, sizeof(SelLds), st, keys, cand_ids, sel, sel_out,
