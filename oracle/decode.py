@@ -47,6 +47,19 @@ def resid_rows(cfg, cache, b: int, h: int, rows: np.ndarray) -> np.ndarray:
     return widen(cache["res_val"][b, h][rows])
 
 
+def residual_hits(tokens: np.ndarray, ridx: np.ndarray):
+    """Which rebuilt tokens have a stored residual, and where it is stored.
+
+    Returns (at, rows): tokens[at[n]] == ridx[rows[n]] for every stored row
+    whose token is among ``tokens``; the row is found by the token id it
+    names, never by its place in either list.
+    """
+    rows = np.nonzero(np.isin(ridx, tokens))[0]
+    where = {int(t): i for i, t in enumerate(tokens)}
+    at = np.array([where[int(t)] for t in ridx[rows]], dtype=np.int64)
+    return at, rows
+
+
 def decode_head(cfg, cache, q_b: np.ndarray, b: int, h: int, sel_override=None):
     """Decode step of one (sequence, KV head); returns (out [g][d], stages)."""
     g, S = cfg.gqa, cfg.chunk
@@ -67,12 +80,8 @@ def decode_head(cfg, cache, q_b: np.ndarray, b: int, h: int, sel_override=None):
     k_post = rope(k_pre, tokens, cfg.rope_theta)                         # step 5
     v_hat = value_mlp(k_pre, widen(cache["w1"][b, h]), widen(cache["b1"][b, h]),
                       widen(cache["w2"][b, h]), widen(cache["b2"][b, h]))  # step 6
-    ridx = np.asarray(cache["res_idx"][b, h])
-    hit = np.isin(ridx, tokens)
-    if np.any(hit):
-        rows = np.nonzero(hit)[0]
-        where = {int(t): i for i, t in enumerate(tokens)}
-        at = np.array([where[int(t)] for t in ridx[rows]])
+    at, rows = residual_hits(tokens, np.asarray(cache["res_idx"][b, h]))
+    if len(rows):
         v_hat[at] += resid_rows(cfg, cache, b, h, rows)
 
     keys = np.concatenate([k_post, widen(cache["win_k"][b, h])], axis=0)  # step 7

@@ -354,6 +354,129 @@ def test_ns3_mlp_plus_residual_reproduces_values():
                 assert np.all(np.abs(got - want) <= np.abs(r) * 2.0 ** -8 + 1e-12)
 
 
+# ----------------------------- top-k smaller than the candidate count --
+def subset_cfg(evict: bool, resid_frac: float = 1.0):
+    """Full rank and exact storage as in full_cfg, but k below the number of
+    candidates, so only a strict subset of the prefix is rebuilt (the review's
+    keys paragraph: only the top-k chunks are rebuilt, at their positions)."""
+    return full_cfg().with_(name="subset_ev" if evict else "subset", topk=7, evict=evict,
+                            resid_frac=resid_frac)
+
+
+def brute_topk(scores, ids, k):
+    """Chunk ids whose score is beaten (or tied by a lower id) fewer than k times."""
+    n = len(scores)
+    keep = [int(ids[i]) for i in range(n)
+            if sum(1 for j in range(n) if scores[j] > scores[i] or (scores[j] == scores[i] and ids[j] < ids[i])) < k]
+    return sorted(keep)
+
+
+def subset_reference(cfg, cache, layer):
+    """Torch SDPA over the exact post-RoPE keys (complex form) and exact values
+    of exactly the brute-force top-k chunks' tokens and the window."""
+    k, v = dense_reference(cfg, layer)
+    q = cache["q"][0]
+    g, P, S = cfg.gqa, cfg.prefix, cfg.chunk
+    out = np.zeros((1, cfg.n_heads_q, cfg.head_dim))
+    sels = []
+    for h in range(cfg.n_heads_kv):
+        lm = cache["landmark"][0, h]
+        ids = cache["cand_ids"][0, h] if cfg.evict else np.arange(cfg.n_chunks)
+        s = [max(sum(float(q[j, i]) * float(lm[c, i]) for i in range(cfg.head_dim)) for j in range(h * g, (h + 1) * g))
+             for c in range(len(lm))]
+        sel = brute_topk(s, ids, cfg.topk)
+        tok = [S * c + i for c in sel for i in range(S)] + list(range(P, cfg.ctx))
+        kk = torch.from_numpy(k[0, h][tok])[None]
+        vv = torch.from_numpy(v[0, h][tok])[None]
+        qq = torch.from_numpy(q[h * g:(h + 1) * g])[:, None, :]
+        out[0, h * g:(h + 1) * g] = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)[:, 0].numpy()
+        sels.append(sel)
+    return out, sels
+
+
+@pytest.mark.parametrize("evict", [False, True])
+@pytest.mark.parametrize("layer", [0, 1])
+def test_subset_full_rank_all_residuals_equals_sdpa_over_selected(layer, evict):
+    cfg = subset_cfg(evict)
+    assert cfg.topk < cfg.n_cand
+    cache = fixture.build_layer(cfg, layer, exact=True)
+    out, st_ = decode.decode_step(cfg, cache, cache["q"])
+    ref, sels = subset_reference(cfg, cache, layer)
+    for h in range(cfg.n_heads_kv):
+        assert list(st_[(0, h)]["sel"]) == sels[h]
+        assert sels[h] != list(range(cfg.topk))      # not simply the first chunks
+    assert np.max(np.abs(out - ref)) < 1e-10
+
+
+def _mut_rope_at_list_positions(mp):
+    mp.setattr(decode, "rope", lambda x, pos, theta: steps.rope(x, np.arange(len(pos)), theta))
+
+
+def _mut_residual_rows_by_list_index(mp):
+    mp.setattr(decode, "residual_hits", lambda tokens, ridx: (np.arange(len(tokens)), np.arange(len(tokens))))
+
+
+def _mut_dropped_chunk(mp):
+    mp.setattr(decode, "select_topk", lambda s, k, c=None: steps.select_topk(s, k, c)[:-1])
+
+
+def _mut_candidate_positions_as_ids(mp):
+    mp.setattr(decode, "select_topk", lambda s, k, c=None: steps.select_topk(s, k, None))
+
+
+@pytest.mark.parametrize("mutate,evict", [(_mut_rope_at_list_positions, False),
+                                          (_mut_residual_rows_by_list_index, False),
+                                          (_mut_dropped_chunk, False),
+                                          (_mut_candidate_positions_as_ids, True)])
+def test_subset_pin_catches_planted_mistakes(monkeypatch, mutate, evict):
+    """Each planted mistake in the oracle's subset path fails the SDPA pin."""
+    cfg = subset_cfg(evict)
+    cache = fixture.build_layer(cfg, 1, exact=True)
+    ref, _ = subset_reference(cfg, cache, 1)
+    with monkeypatch.context() as mp:
+        mutate(mp)
+        bad, _ = decode.decode_step(cfg, cache, cache["q"])
+    assert not np.max(np.abs(bad - ref)) < 1e-3
+
+
+def _ns3_subset_check(cfg, cache, v, w):
+    """Selected residual tokens come back as exact V; the other selected tokens
+    as the torch MLP of their exact (full-rank) keys."""
+    x = synth.exact_keys(cfg, 0, 0)
+    _, st_ = decode.decode_step(cfg, cache, cache["q"])
+    n_hit = n_miss = 0
+    for h in range(cfg.n_heads_kv):
+        s = st_[(0, h)]
+        tok = s["tokens"]
+        has = np.isin(tok, cache["res_idx"][0, h])
+        tt = torch.from_numpy
+        w1, b1, w2, b2 = (tt(np.asarray(a, np.float64)) for a in w[h])
+        pred = torch.nn.functional.linear(torch.nn.functional.gelu(torch.nn.functional.linear(
+            tt(x[tok][:, synth.layer_cols(cfg, 0, h)]), w1, b1)), w2, b2).numpy()
+        if np.max(np.abs(s["v_hat"][has] - v[0, h][tok[has]]), initial=0) >= 1e-10:
+            return False
+        if np.max(np.abs(s["v_hat"][~has] - pred[~has]), initial=0) >= 1e-10:
+            return False
+        n_hit, n_miss = n_hit + has.sum(), n_miss + (~has).sum()
+    assert n_hit > 0 and n_miss > 0
+    return True
+
+
+def test_ns3_subset_mlp_plus_residual_reproduces_values(monkeypatch):
+    """NS-3 with k below the candidates and a quarter of the tokens holding
+    residuals: the rows are found for a strict subset of the prefix."""
+    cfg = subset_cfg(False, resid_frac=0.25)
+    cache = fixture.build_layer(cfg, 0, exact=True)
+    _, v = dense_reference(cfg, 0)
+    w = [synth.mlp_weights(cfg, 0, 0, h) for h in range(cfg.n_heads_kv)]
+    assert _ns3_subset_check(cfg, cache, v, w)
+    # planted: the hit rows matched to the rebuilt tokens in list order
+    with monkeypatch.context() as mp:
+        mp.setattr(decode, "residual_hits",
+                   lambda tokens, ridx: (np.arange(int(np.isin(ridx, tokens).sum())), np.nonzero(np.isin(ridx, tokens))[0]))
+        assert not _ns3_subset_check(cfg, cache, v, w)
+
+
 def test_eviction_that_evicts_nothing_is_the_plain_path():
     cfg = synth.C0
     cache = fixture.build_layer(cfg, 0)
