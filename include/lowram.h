@@ -49,7 +49,9 @@ enum {
   LOWRAM_ERR_NULL = -1,        /* a required pointer is NULL                         */
   LOWRAM_ERR_SHAPE = -2,       /* inconsistent sizes (e.g. Hq % Hkv, P % S, k < 1)   */
   LOWRAM_ERR_UNSUPPORTED = -3, /* valid but not built (d != 128, S != 8, H != 256,
-                                  or NB * Hkv * (attention tiles) >= 2^31) */
+                                  or a grid past HIP's limits: more than 65535 in
+                                  a y/z dimension, or more than (2^32 - 1) / 256
+                                  workgroups of 256 work-items in a 1-D grid) */
   LOWRAM_ERR_WORKSPACE = -4,   /* workspace smaller than *_workspace_bytes reports    */
   LOWRAM_ERR_ALIGN = -5,       /* misaligned pointer                                 */
   LOWRAM_ERR_HIP = -6          /* a HIP launch failed                                */

@@ -20,6 +20,12 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
+// Workgroups of a 1-D grid of 256-thread workgroups: a dispatch counts its
+// work-items (workgroups x 256) in 32 bits, and the launches pad the grid to
+// a multiple of 8 workgroups, so the limit is the largest multiple of 8 below
+// (2^32 - 1) / 256.
+constexpr int64_t kMaxGrid1D = ((int64_t)0xFFFFFFFF / 256) & ~(int64_t)7;
+
 struct Plan {
   // n_split: partial slots per head of the 4-wave kernel (one per tile);
   // n_part: slots reserved per head, enough for either attention kernel
@@ -57,11 +63,13 @@ int check_shape(const lowram_shape* s) {
     return LOWRAM_ERR_UNSUPPORTED;
   // grid limits: sequences and KV heads index the y and z grid dimensions
   // (at most 65535), and the 4-wave grid has one workgroup per (sequence,
-  // KV head, tile), counted in 32 bits
+  // KV head, tile)
   if (s->batch > 65535 || s->n_heads_kv > 65535) return LOWRAM_ERR_UNSUPPORTED;
   const int64_t k_eff = s->n_cand < s->topk ? s->n_cand : s->topk;
   const int64_t tiles = (k_eff + kAttChunksWG - 1) / kAttChunksWG + (s->window + kAttTokWG - 1) / kAttTokWG;
-  if ((int64_t)s->batch * s->n_heads_kv * tiles >= (int64_t)1 << 31) return LOWRAM_ERR_UNSUPPORTED;
+  if ((int64_t)s->batch * s->n_heads_kv * tiles > kMaxGrid1D) return LOWRAM_ERR_UNSUPPORTED;
+  // nothing to attend: no candidate chunk and no window token gives no split
+  if (s->n_cand == 0 && s->window == 0) return LOWRAM_ERR_SHAPE;
   return LOWRAM_OK;
 }
 
@@ -254,8 +262,8 @@ int check_dense(const dense_shape* s) {
   if (s->head_dim != kHeadDim || s->n_heads_q / s->n_heads_kv > 16) return LOWRAM_ERR_UNSUPPORTED;
   // grid limits, as for the decode step
   if (s->batch > 65535 || s->n_heads_kv > 65535) return LOWRAM_ERR_UNSUPPORTED;
-  if ((int64_t)s->batch * s->n_heads_kv * ((s->ctx_len + kDenseTokPerSplit - 1) / kDenseTokPerSplit) >=
-      (int64_t)1 << 31)
+  if ((int64_t)s->batch * s->n_heads_kv * ((s->ctx_len + kDenseTokPerSplit - 1) / kDenseTokPerSplit) >
+      kMaxGrid1D)
     return LOWRAM_ERR_UNSUPPORTED;
   return LOWRAM_OK;
 }
@@ -286,6 +294,16 @@ int check_build_shape(const lowram_build_shape* s) {
   if ((int64_t)s->batch * s->prefix_cap >= (int64_t)1 << 31) return LOWRAM_ERR_UNSUPPORTED;
   if ((int64_t)s->group_layers * s->n_heads_kv * kHeadDim >= (int64_t)1 << 20) return LOWRAM_ERR_UNSUPPORTED;
   if (s->batch > 65535) return LOWRAM_ERR_UNSUPPORTED;  // a grid dimension of at most 65535
+  // the residual top-k and descriptor grids index (sequence, KV head) lists
+  // in a grid dimension of at most 65535
+  if ((int64_t)s->batch * s->n_heads_kv > 65535) return LOWRAM_ERR_UNSUPPORTED;
+  // 1-D grids of 256-thread workgroups: the projection (128-token tiles x
+  // 128-column blocks of the rank) and the residual prediction (128-token
+  // tiles per (sequence, KV head))
+  const int64_t tok_tiles = (P + 127) / 128;
+  if ((int64_t)s->batch * tok_tiles * ((s->rank + 127) / 128) > kMaxGrid1D ||
+      (int64_t)s->batch * s->n_heads_kv * tok_tiles > kMaxGrid1D)
+    return LOWRAM_ERR_UNSUPPORTED;
   return LOWRAM_OK;
 }
 
@@ -421,6 +439,7 @@ int lowram_resid_chunk_desc(const int32_t* res_idx, int32_t n_lists, int32_t n_r
   if (!desc || (n_resid > 0 && !res_idx)) return LOWRAM_ERR_NULL;
   if (n_lists < 0 || n_resid < 0 || n_chunks < 0 || chunk < 1) return LOWRAM_ERR_SHAPE;
   if (chunk > 8 || n_resid >= (1 << 24)) return LOWRAM_ERR_UNSUPPORTED;
+  if (n_lists > 65535) return LOWRAM_ERR_UNSUPPORTED;  // lists index a grid dimension of at most 65535
   if (misaligned(desc, 4) || (res_idx && misaligned(res_idx, 4))) return LOWRAM_ERR_ALIGN;
   if (n_lists == 0 || n_chunks == 0) return LOWRAM_OK;
   if (launch_chunk_desc(res_idx, n_lists, n_resid, n_chunks, chunk, desc,
@@ -634,6 +653,9 @@ int check_fit(const lowram_fit_shape* s) {
   if ((int64_t)s->ctx_len * s->group_dim >= (int64_t)1 << 31 || (int64_t)s->prefix_len * s->rank >= (int64_t)1 << 31)
     return LOWRAM_ERR_UNSUPPORTED;
   if (s->batch > 65535) return LOWRAM_ERR_UNSUPPORTED;  // a grid dimension of at most 65535
+  // the transposes index 64-column blocks of the keys in a grid dimension of
+  // at most 65535
+  if (s->group_dim >= (1 << 20)) return LOWRAM_ERR_UNSUPPORTED;
   return LOWRAM_OK;
 }
 }  // namespace

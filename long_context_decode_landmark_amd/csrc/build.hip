@@ -401,8 +401,10 @@ __device__ __forceinline__ void split3(f32x4 lo4, f32x4 hi4, bf16x8 (&s)[3]) {
 }
 
 // Exact-GELU x Phi(x) to fp32 accuracy without a branchy library erf:
-// with z = |x| / sqrt(2) and t = 1 / (1 + z / 2), erfc(z) = t exp(P(t) - z^2)
-// where P is a degree-7 polynomial fitted here (weighted least squares on
+// with z = |x| / sqrt(2) and t = 1 / (1 + z / 2), erfc(z) = t exp(P(t) - z^2).
+// That form is the Chebyshev-fitted erfc of Press, Teukolsky, Vetterling and
+// Flannery, Numerical Recipes (routine erfcc); here P is a degree-7 polynomial
+// refitted for this use (weighted least squares on
 // z in [0, 6], largest error of log erfc 4.3e-7); Phi(x) = 1 - erfc(z) / 2 for
 // x >= 0 and erfc(z) / 2 below.  Largest deviation of the fp32 evaluation from
 // x Phi(x) over the reals: 2.4e-7 absolute (the rounding of x - x erfc / 2).

@@ -2,7 +2,7 @@
 // baseline of the LowRAM review's results paragraph), gfx950, and the
 // residual chunk-descriptor helper of the compressed cache layout.
 //
-// One workgroup = 8 waves covers a split of the context; each wave walks
+// One workgroup = 4 waves covers a split of the context; each wave walks
 // 32-token blocks with an online softmax.  QK on MFMA (K rows straight from
 // HBM as the A operand, 16 B per lane), PV on MFMA with V as the B operand.
 // Partial states go through the same split merge as the LowRAM step.

@@ -70,6 +70,11 @@ def projection_error(x: np.ndarray, basis: np.ndarray) -> float:
     return float(np.linalg.norm(x - (x @ b.T) @ b) / np.linalg.norm(x))
 
 
+def principal_angles(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Every principal angle (radians) between span(rows of a) and span(rows of b)."""
+    return scipy.linalg.subspace_angles(np.asarray(a, np.float64).T, np.asarray(b, np.float64).T)
+
+
 def max_angle(a: np.ndarray, b: np.ndarray) -> float:
     """Largest principal angle (radians) between span(rows of a) and span(rows of b).
 

@@ -123,5 +123,5 @@ def full_parity(cfg, cache, stages=True, nb=None):
         nflip += check_selection(cfg, ost, sel, b, h)
     ref, ost2 = decode.decode_step(cfg, cache, cache["q"], sel_override=sel)
     rel, mx = check_output(got, ref, cfg.name)
-    return dict(got=got, ref=ref, sel=sel, gpu_stages=st, oracle_stages=ost2, rel=rel, max_abs=mx,
-                flips=nflip)
+    return dict(got=got, ref=ref, sel=sel, gpu_stages=st, oracle_stages=ost2, oracle_own_stages=ost, rel=rel,
+                max_abs=mx, flips=nflip)

@@ -56,8 +56,9 @@ def ws_bytes(**kw):
     (dict(coeff_fmt=1), -3),            # int4 needs rank % 128 == 0 (rank 64 here)
     (dict(batch=65536), -3),            # sequences index a grid dimension of at most 65535
     (dict(n_heads_q=65536, n_heads_kv=65536), -3),
-    # (sequence, KV head, tile) workgroups of the 4-wave grid counted in 32 bits
-    (dict(batch=32768, n_heads_q=32, n_heads_kv=16, prefix_len=0, n_cand=0, n_resid=0, window=4096 * 128), -3),
+    # (sequence, KV head, tile) workgroups of 256 work-items: at most (2^32 - 1) / 256, padded to 8
+    (dict(batch=1024, n_heads_q=32, n_heads_kv=16, prefix_len=0, n_cand=0, n_resid=0, window=1025 * 128), -3),
+    (dict(n_cand=0, window=0), -2),     # a prefix but no candidate and no window: nothing to attend
 ])
 def test_workspace_bytes_rejects_shapes(kw, code):
     with pytest.raises(native.LowramError) as e:
@@ -148,10 +149,11 @@ def test_step_rejects_more_partial_states_than_the_merge_combines():
 def test_shapes_at_the_grid_limits_are_accepted():
     # one below each limit that a rejection test above crosses
     assert ws_bytes(batch=65535) > 0
-    assert ws_bytes(batch=32767, n_heads_q=32, n_heads_kv=16, prefix_len=0, n_cand=0, n_resid=0,
-                    window=4096 * 128) > 0
+    assert ws_bytes(batch=1023, n_heads_q=32, n_heads_kv=16, prefix_len=0, n_cand=0, n_resid=0,
+                    window=1025 * 128) > 0
+    assert ws_bytes(n_cand=0, window=1) > 0
     assert native.dense_workspace_bytes(native.dense_shape(65535, 100, 8, 2)) > 0
-    assert native.dense_workspace_bytes(native.dense_shape(32767, 4096 * 2048, 32, 16)) > 0
+    assert native.dense_workspace_bytes(native.dense_shape(1023, 1025 * 2048, 32, 16)) > 0
 
 
 def test_step_requires_int4_scales_and_candidates():
@@ -166,7 +168,7 @@ def test_dense_rejects():
         native.dense_workspace_bytes(native.dense_shape(1, 100, 7, 2))
     assert e.value.status == -2
     for bad in (native.dense_shape(65536, 100, 8, 2),          # grid dimension limit
-                native.dense_shape(32768, 4096 * 2048, 32, 16)):  # 2^31 (sequence, head, split) workgroups
+                native.dense_shape(1024, 1025 * 2048, 32, 16)):  # over (2^32 - 1) / 256 workgroups
         with pytest.raises(native.LowramError) as e:
             native.dense_workspace_bytes(bad)
         assert e.value.status == -3
@@ -178,12 +180,21 @@ def test_dense_rejects():
     assert e.value.status == -4
 
 
+def test_build_shapes_at_the_grid_limits_are_accepted():
+    assert native.build_layer_workspace_bytes(bshape(batch=32767)) > 0     # 65534 lists
+    assert native.build_layer_workspace_bytes(bshape(n_heads_kv=8, ctx_len=(1 << 28) - 1024, window=0,
+                                                     n_resid=0)) > 0
+
+
 def test_chunk_desc_rejects():
     with pytest.raises(native.LowramError) as e:
         native.resid_chunk_desc(FakeTensor(0x1002), 4, 16, 10, 8, FakeTensor(0x2000), stream=0)
     assert e.value.status == -5
     with pytest.raises(native.LowramError) as e:
         native.resid_chunk_desc(FakeTensor(0x1000), 4, 16, 10, 16, FakeTensor(0x2000), stream=0)
+    assert e.value.status == -3
+    with pytest.raises(native.LowramError) as e:      # lists index a grid dimension of at most 65535
+        native.resid_chunk_desc(FakeTensor(0x1000), 65536, 16, 10, 8, FakeTensor(0x2000), stream=0)
     assert e.value.status == -3
 
 
@@ -206,6 +217,9 @@ def bshape(**kw):
     (dict(mlp_hidden=512), -3),
     (dict(coeff_fmt=1), -3),            # int4 coefficients need rank % 128 == 0
     (dict(batch=65536), -3),            # sequences index a grid dimension of at most 65535
+    (dict(batch=32768), -3),            # (sequence, KV head) lists index one of at most 65535
+    # 128-token prediction tiles of (sequence, KV head): at most (2^32 - 1) / 256 workgroups
+    (dict(n_heads_kv=8, ctx_len=1 << 28, window=0, n_resid=0), -3),
 ])
 def test_build_workspace_rejects_shapes(kw, code):
     with pytest.raises(native.LowramError) as e:
@@ -320,6 +334,8 @@ def test_fit_basis_rejects():
         return e.value.status
     assert st(native.fit_shape(1, 4096, 4000, 512, 64)) == -3      # P not a multiple of 64
     assert st(native.fit_shape(65536, 4096, 4096, 512, 64)) == -3  # a grid dimension of at most 65535
+    assert st(native.fit_shape(1, 64, 64, 1 << 20, 64)) == -3      # 64-column key blocks in such a dimension
+    assert native.fit_basis_workspace_bytes(native.fit_shape(1, 64, 64, (1 << 20) - 128, 64)) > 0
     assert st(native.fit_shape(1, 4096, 4032, 500, 64)) == -3      # D not a multiple of 128
     assert st(native.fit_shape(1, 4096, 4032, 512, 96)) == -3      # rank
     assert st(native.fit_shape(1, 4096, 8192, 512, 64)) == -2      # P > T

@@ -10,6 +10,15 @@ rounding rotates the basis.  So the comparison is on what is unique:
   - the projection error of the keys within 1% of the oracle fit's (rounded
     to bf16), and never below the exact SVD optimum (small cases);
   - status 0 (every Cholesky pivot positive).
+For a given test matrix the fit is also unique as a basis: Cholesky-QR with
+a positive-diagonal R fixes every row's sign.  So the GPU basis is compared
+with the oracle's directly as well:
+  - all r principal angles between the two spans;
+  - the entries, row by row after aligning each row's sign.
+The bounds are about three times what the GPU's roundings give in a numpy
+emulation of them (fp32 products, bf16 intermediates, bf16 output): at c0
+sizes the largest angle 0.002-0.021 rad and the largest entry difference
+0.0005-0.0033; at the 32K size 0.056 rad and 0.0034.
 """
 import numpy as np
 import pytest
@@ -41,6 +50,18 @@ def run_fit(x_bits, om_t_bits, rank, power):
     native.fit_basis(shape, up(x_bits), up(om_t_bits), out, status, ws)
     torch.cuda.synchronize()
     return codecs.bf16_decode(host16(out)), status.cpu().numpy()
+
+
+def compare_bases(b_g, b_or, angle_tol, entry_tol, what):
+    """All principal angles between the spans, and the sign-aligned entries."""
+    ang = float(np.max(basis.principal_angles(b_or, b_g)))
+    sign = np.sign(np.sum(b_or * b_g, axis=1))[:, None]
+    ent = float(np.max(np.abs(b_or - sign * b_g)))
+    print(f"{what}: largest of {len(b_or)} principal angles to the oracle's basis {ang:.1e} rad, "
+          f"largest sign-aligned entry difference {ent:.1e}", flush=True)
+    assert np.all(sign != 0)
+    assert ang <= angle_tol, (what, ang)
+    assert ent <= entry_tol, (what, ent)
 
 
 def latent_rows(cfg, b, grp):
@@ -77,6 +98,7 @@ def test_fit_matches_oracle(name, cfg, power):
         e_svd = basis.projection_error(x, basis.svd_basis(x, r))
         assert abs(e_g - e_ref) <= 1e-2 * e_ref, (e_g, e_ref)
         assert e_g >= e_svd * (1 - 1e-3)
+        compare_bases(b_g, b_or, 0.06, 0.01, f"fit {name} b{b}")
         print(f"\nfit {name} b{b}: ortho {ortho:.1e} (ref {ortho_ref:.1e}) latent angle {a_g:.1e} "
               f"(ref {a_ref:.1e}) proj err {e_g:.4f} (ref {e_ref:.4f}, svd {e_svd:.4f})", flush=True)
 
@@ -101,6 +123,7 @@ def test_fit_c1_size():
     assert ortho <= 2e-2
     assert a_g <= 4 * a_ref + 2e-3
     assert abs(e_g - e_ref) <= 1e-2 * e_ref
+    compare_bases(b_g, basis.randomized_cholqr(x, codecs.bf16_decode(om).T, power=power), 0.17, 0.012, "fit c1")
 
 
 def test_fit_full_size_properties():

@@ -46,6 +46,34 @@ def test_dense_matches_oracle(name, over):
     print(f"dense {name}: rel {rel:.2e} max {mx:.2e}")
 
 
+def test_dense_full_size_sampled_heads():
+    """The 262144-token dense step at batch 8 (128 splits of 2048 tokens per
+    head, the launch the benchmark times), K/V/q drawn as the benchmark draws
+    them; sampled (sequence, KV head) slices against the oracle."""
+    nb, T, hq, hkv, d = 8, 262144, 32, 8, 128
+    g_ = torch.Generator(device=DEV)
+    g_.manual_seed(77)
+    k = torch.randn((nb, hkv, T, d), generator=g_, device=DEV, dtype=torch.bfloat16)
+    v = torch.randn((nb, hkv, T, d), generator=g_, device=DEV, dtype=torch.bfloat16)
+    q = torch.randn((nb, hq, d), generator=g_, device=DEV, dtype=torch.bfloat16)
+    out = torch.empty_like(q)
+    ds = native.dense_shape(nb, T, hq, hkv, d)
+    ws = torch.empty(native.dense_workspace_bytes(ds), dtype=torch.uint8, device=DEV)
+    native.dense_decode_step(ds, k, v, q, out, ws)
+    torch.cuda.synchronize()
+    got = down_bf16(out)
+    assert np.all(np.isfinite(got))
+    gq = hq // hkv
+    bits = lambda t: t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    for b, h in [(0, 0), (3, 5), (7, 7)]:
+        ref = decode.dense_step(bits(k[b:b + 1, h:h + 1]), bits(v[b:b + 1, h:h + 1]),
+                                bits(q[b:b + 1, h * gq:(h + 1) * gq]), 1)
+        rel, mx = check_output(got[b:b + 1, h * gq:(h + 1) * gq], ref, f"dense 262k b{b} h{h}")
+        print(f"dense 262k b{b} h{h}: rel {rel:.2e} max {mx:.2e}", flush=True)
+    del k, v
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("n_chunks,n_resid,seed", [(5000, 625, 0), (4096, 0, 1), (777, 777 * 8, 2), (1, 3, 3),
                                                     (32736, 32736, 4)])
 def test_resid_chunk_desc_matches_oracle(n_chunks, n_resid, seed):

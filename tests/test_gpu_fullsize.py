@@ -7,10 +7,15 @@ sampled (sequence, KV head) slices one by one from the same arrays copied to
 the host: selection within the tie band, that head's output within the
 decode tolerance against the oracle re-run on the GPU's selection.  Every
 output of the batch must be finite, and every selection ascending and full.
-Every (sequence, KV head) is then checked by a property: the 4-wave kernel on
-the same batch selects the same chunks and agrees within twice the tolerance
-(at these sizes the library runs the producer/consumer kernel, whose
-workgroups switch heads inside their pipelines).
+Every (sequence, KV head)'s selection is checked against the oracle's own
+scores and top-k (tie band).  Every output is then checked by a property: the
+4-wave kernel on the same batch selects the same chunks and agrees within
+twice the tolerance (at these sizes the library runs the producer/consumer
+kernel, whose workgroups switch heads inside their pipelines).
+
+A third case has 40960 candidate chunks per head, more than the selection
+kernel keeps in LDS (32768): it runs the variant that reads its keys from
+the cache hierarchy.
 """
 import numpy as np
 import pytest
@@ -25,7 +30,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 
 from gpu_util import DEV, MAX_ABS, REL_L2, check_output, check_selection, down_bf16  # noqa: E402
 from long_context_decode_landmark_amd import native  # noqa: E402
-from oracle import decode  # noqa: E402
+from oracle import decode, steps  # noqa: E402
 from synth import device as sd  # noqa: E402
 
 
@@ -65,9 +70,16 @@ def head_slice(cfg, cache, b, h):
     return out
 
 
-@pytest.mark.parametrize("name,nb", [("c3_llama8b_262k", 28), ("c4_eq_int4_evict_262k", 16)])
+# 40960 chunks of 8 tokens per head (327680-token prefix plus a 256-token window)
+WIDE = synth.C3.with_(name="wide_list_328k", batch=2, n_heads_q=8, n_heads_kv=2, ctx=327936)
+
+
+@pytest.mark.parametrize("name,nb", [("c3_llama8b_262k", 28), ("c4_eq_int4_evict_262k", 16),
+                                     ("wide_list_328k", 2)])
 def test_full_size_sampled_heads(name, nb):
-    cfg = synth.CONFIGS[name]
+    cfg = WIDE if name == WIDE.name else synth.CONFIGS[name]
+    if name == WIDE.name:
+        assert cfg.n_cand > 32768
     g, keff = cfg.gqa, min(cfg.topk, cfg.n_cand)
     print(f"\n{name} batch {nb}: drawing caches", flush=True)
     cache = draw_batch(cfg, nb, seed=4242)
@@ -86,7 +98,21 @@ def test_full_size_sampled_heads(name, nb):
     print(f"{name}: step done, checking sampled heads", flush=True)
 
     q_h = host(q)
-    samples = [(0, 0), (nb // 2, 3), (nb - 1, cfg.n_heads_kv - 1)]
+    # every head's selection against the oracle's own scores and top-k
+    nflips = 0
+    for b in range(nb):
+        lm_b = host(cache["landmark"][b])
+        cand_b = host(cache["cand_ids"][b]) if "cand_ids" in cache else None
+        for h in range(cfg.n_heads_kv):
+            sc = steps.landmark_scores(decode.widen(q_h[b, h * g:(h + 1) * g]), decode.widen(lm_b[h]))
+            st = {"scores": sc, "sel": steps.select_topk(sc, cfg.topk, None if cand_b is None else cand_b[h])}
+            if cand_b is not None:
+                st["cand"] = cand_b[h]
+            nflips += check_selection(cfg, {(0, 0): st}, sel_h[b:b + 1, h:h + 1], 0, 0)
+        del lm_b
+    print(f"{name}: every head's selection within the tie band of the oracle's ({nflips} tie flips)", flush=True)
+
+    samples = sorted({(0, 0), (nb // 2, min(3, cfg.n_heads_kv - 1)), (nb - 1, cfg.n_heads_kv - 1)})
     for b, h in samples:
         sl = head_slice(cfg, cache, b, h)
         qs = decode.widen(q_h[b, h * g:(h + 1) * g])
