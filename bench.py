@@ -50,6 +50,8 @@ def parse():
                     help="time the window rollover (one chunk into the prefix) for one layer group")
     ap.add_argument("--build", action="store_true",
                     help="time the cache builder (one layer group of one sequence) instead of the decode step")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure achievable peaks: a streaming device copy and a large bf16 GEMM")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first copy a buffer of this size 3 times (HBM counter calibration)")
     return ap.parse_args()
@@ -88,6 +90,48 @@ def measured_traffic(kernel, workload, nb, path=TRAFFIC_FILE):
         f = ln.split()
         if len(f) == 6 and f[0] == "traffic" and f[1] == kernel and f[2] == workload and int(f[3]) == nb:
             return float(f[5]) if f[4] == source_hash(kernel) else None
+    return None
+
+
+COUNTER_FILES = {
+    ("c3_llama8b_262k", 28): os.path.join(ROOT, "profiles", "decode_c3_262k_b28_counters.txt"),
+    ("c4_eq_int4_evict_262k", 16): os.path.join(ROOT, "profiles", "decode_c4_int4_evict_262k_b16_counters.txt"),
+}
+
+
+def measured_mfma_flops(kernel, workload, nb):
+    """MFMA flops per launch of `kernel` counted by rocprofv3 (512 x the
+    SQ_INSTS_VALU_MFMA_MOPS_* counters) from the committed counter summary, or
+    None when there is none for this workload or the sources changed since."""
+    path = COUNTER_FILES.get((workload, nb))
+    if path is None:
+        return None
+    try:
+        lines = open(path).read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        f = ln.split()
+        if len(f) == 6 and f[0] == "mfma_flops" and f[1] == kernel and f[2] == workload and int(f[3]) == nb:
+            return float(f[5]) if f[4] == source_hash(kernel) else None
+    return None
+
+
+def step_stats(ms):
+    """Median, 10th and 90th percentile of per-step times (ms)."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "n": int(a.size)}
+
+
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
     return None
 
 
@@ -209,6 +253,7 @@ def time_lowram(cfg, nb, n_layers, steps, warmup, seed, graph, shared=False):
     t1.record(stream)
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
+    eager_steps = [s[0][0].elapsed_time(s[-1][4]) for s in evs]
     kern = {k: 0.0 for k in KERNELS}
     for s in evs:
         for lay in s:
@@ -216,7 +261,7 @@ def time_lowram(cfg, nb, n_layers, steps, warmup, seed, graph, shared=False):
                 kern[k] += lay[i].elapsed_time(lay[i + 1])
     kern = {k: v / (steps * n_layers) for k, v in kern.items()}  # ms per launch
 
-    graph_ms = None
+    graph_ms, graph_steps = None, None
     if graph:
         g = torch.cuda.CUDAGraph()
         s2 = torch.cuda.Stream()
@@ -229,13 +274,14 @@ def time_lowram(cfg, nb, n_layers, steps, warmup, seed, graph, shared=False):
         for _ in range(2):
             g.replay()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(steps):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        marks[0].record()
+        for i in range(steps):
             g.replay()
-        b.record()
+            marks[i + 1].record()
         torch.cuda.synchronize()
-        graph_ms = a.elapsed_time(b) / steps
+        graph_ms = marks[0].elapsed_time(marks[-1]) / steps
+        graph_steps = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
 
     # one slice back to the host for the CPU baseline
     host = {kk: v[0].cpu() for kk, v in layers[0].items()}
@@ -243,7 +289,7 @@ def time_lowram(cfg, nb, n_layers, steps, warmup, seed, graph, shared=False):
     del layers, qs, caches, ws, out
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
-    return step_ms, kern, graph_ms, host, q0
+    return step_ms, kern, graph_ms, host, q0, (graph_steps if graph_steps is not None else eager_steps)
 
 
 def time_dense(cfg, nb, n_layers, steps, warmup, seed):
@@ -315,6 +361,7 @@ def cpu_baseline(cfg, host, q0, n_slices):
     except Exception:
         pass
     return {"value": 1.0 / (dt * cfg.n_layers), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{n_slices} (sequence, layer) slices of the same workload (all {cfg.n_heads_kv} KV heads), "
                       f"{dt:.2f} s each, extrapolated x{cfg.n_layers} layers per token"}
 
@@ -650,8 +697,8 @@ def bench_append(args):
 def bench_shared(args, cfg, nq, n_layers):
     """Q queries over one 262K context per layer: every query's own top-k,
     rebuild and attention; the context is read by all of them."""
-    step_ms, kern, _, _, _ = time_lowram(cfg, nq, n_layers, args.steps, args.warmup, args.seed, False,
-                                         shared=True)
+    step_ms, kern, _, _, _, _ = time_lowram(cfg, nq, n_layers, args.steps, args.warmup, args.seed, False,
+                                            shared=True)
     byts, flops = algorithmic(cfg, nq)
     # the context's landmarks, weights and window are read once per layer, not once per query
     ctx = {"score": byts["score"] / nq, "attend": byts["attend"] / nq}
@@ -675,12 +722,61 @@ def bench_shared(args, cfg, nq, n_layers):
     print(json.dumps(res))
 
 
+def bench_peaks(args):
+    """What the chip reaches on plain work, beside the published peaks: a
+    device-to-device copy of 4 GiB (HBM read + write bytes / time) and an
+    8192^3 bf16 matrix product through torch (hipBLASLt; 2 n^3 flops / time)."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = 4 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(5, args.steps)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * n * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    m = 8192
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    x = torch.randn((m, m), generator=g, device=dev, dtype=torch.bfloat16)
+    y = torch.randn((m, m), generator=g, device=dev, dtype=torch.bfloat16)
+    z = torch.empty((m, m), device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(x, y, out=z)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        torch.mm(x, y, out=z)
+    b.record()
+    torch.cuda.synchronize()
+    mm_tfs = 2.0 * m ** 3 * reps / (a.elapsed_time(b) * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "achievable peaks on this MI355X", "n_gpus": 1, "steps": reps,
+        "copy": {"GB/s": round(copy_gbs, 1), "frac_of_8TB/s": round(copy_gbs / HBM_PEAK_GBS, 4),
+                 "what": "device-to-device copy of 4 GiB, read + write bytes"},
+        "bf16_gemm": {"TFLOP/s": round(mm_tfs, 1), "frac_of_2.5PF": round(mm_tfs / MFMA_BF16_PEAK_TFS, 4),
+                      "what": "torch.mm bf16 8192 x 8192 x 8192 (hipBLASLt)"},
+    }))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode step shards by "
               "sequence with no exchange, so N GPUs would each run this single-GPU workload.", file=sys.stderr)
         sys.exit(2)
+    if args.peaks:
+        bench_peaks(args)
+        return
     if args.fit:
         bench_fit(args)
         return
@@ -702,8 +798,8 @@ def main():
 
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
-    eager_ms, kern, graph_ms, host, q0 = time_lowram(cfg, nb, n_layers, args.steps, args.warmup, args.seed,
-                                                     not args.eager)
+    eager_ms, kern, graph_ms, host, q0, per_step = time_lowram(cfg, nb, n_layers, args.steps, args.warmup,
+                                                               args.seed, not args.eager)
     # the step as a serving loop runs it: one hipGraph replay per decode step
     # (the same launches; the eager pass, with HIP events between kernels,
     # gives the per-kernel times)
@@ -750,6 +846,11 @@ def main():
                           "mfma_util": round(step_flops / (step_ms * 1e-3) / (MFMA_BF16_PEAK_TFS * 1e12), 4)},
         "kernels": per_kernel,
     }
+    res["step_ms_stats"] = step_stats(per_step)
+    counted = measured_mfma_flops(dom, cfg.name, nb)
+    res["roofline"]["mfma_util_algorithmic"] = round(flops[dom] / t_dom / 1e12 / MFMA_BF16_PEAK_TFS, 4)
+    res["roofline"]["mfma_util_counted"] = (round(counted / t_dom / 1e12 / MFMA_BF16_PEAK_TFS, 4)
+                                            if counted is not None else None)
     res["timing"] = ("hipGraph replay of the whole step (all layers' launches)" if graph_ms is not None
                      else "eager launches with per-kernel HIP events")
     res["eager_ms_per_step"] = round(eager_ms, 4)
