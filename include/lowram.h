@@ -54,8 +54,15 @@ enum {
                                   workgroups of 256 work-items in a 1-D grid) */
   LOWRAM_ERR_WORKSPACE = -4,   /* workspace smaller than *_workspace_bytes reports    */
   LOWRAM_ERR_ALIGN = -5,       /* misaligned pointer                                 */
-  LOWRAM_ERR_HIP = -6          /* a HIP launch failed                                */
+  LOWRAM_ERR_HIP = -6,         /* a HIP launch failed                                */
+  LOWRAM_ERR_SCRATCH = -7      /* lowram_decode_step_noalloc: the shape needs more
+                                  workspace than LOWRAM_NOALLOC_SCRATCH_BYTES       */
 };
+
+/* Size of the fixed device scratch of lowram_decode_step_noalloc: 64 MiB per
+   GPU the library runs on, held from the library's load to the end of the
+   process. */
+#define LOWRAM_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* Storage format of the coefficients C and of the residual values. */
 enum {
@@ -153,6 +160,29 @@ int lowram_workspace_bytes(const lowram_shape* shape, size_t* bytes);
 int lowram_decode_step(const lowram_shape* shape, const lowram_layer_cache* cache,
                        const uint16_t* q, uint16_t* out, int32_t* sel_out,
                        void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * lowram_decode_step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace: its kernels use a fixed device array of
+ * LOWRAM_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library, one per GPU,
+ * whose address is looked up (hipGetSymbolAddress) at the first call on each
+ * device.  It calls no hipMalloc, hipFree or allocating library routine; the
+ * caller still passes q, out, sel_out and the cache, as for
+ * lowram_decode_step, and gets the same results.
+ *   Limit: shapes whose lowram_workspace_bytes exceeds the scratch size are
+ *   refused with LOWRAM_ERR_SCRATCH before any HIP call (e.g. at 262144
+ *   tokens and rank 512, about 3.3 MB per sequence: up to 20 sequences).
+ *   Every call on a GPU shares that GPU's scratch, which keeps the last
+ *   call's contents (nothing in it needs to start at zero): calls that
+ *   overlap on one GPU (different streams, or threads without ordering) race
+ *   and must be serialised by the caller.
+ * Other errors as lowram_decode_step; LOWRAM_ERR_HIP also when the scratch's
+ * address cannot be looked up, LOWRAM_ERR_UNSUPPORTED on a device ordinal
+ * of 64 or more.
+ */
+int lowram_decode_step_noalloc(const lowram_shape* shape, const lowram_layer_cache* cache,
+                               const uint16_t* q, uint16_t* out, int32_t* sel_out, void* stream);
 
 /*
  * How lowram_decode_step schedules the selected chunks for `shape` on a

@@ -2,10 +2,12 @@
 // call), workspace carving, and the launch sequence
 //   score (landmark GEMV) -> select (exact top-k) -> attend (fused rebuild +
 //   split-K attention, window included) -> merge (log-sum-exp of the splits).
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/lowram.h"
 #include "common.h"
@@ -143,13 +145,12 @@ AttendPlan attend_plan(const lowram_shape* s, const Plan& p, bool stage_outputs,
   return a;
 }
 
-int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t* q, uint16_t* out,
-             int32_t* sel_out, float* scores_out, float* kpre_out, float* kpost_out,
-             float* vhat_out, void* ws, size_t ws_bytes, void* stream,
-             void* const* events = nullptr, bool shared = false) {
+// Every argument check of a decode step except the workspace's (no HIP call).
+int check_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t* q, uint16_t* out,
+               int32_t* sel_out, float* scores_out, float* kpre_out, float* kpost_out, float* vhat_out) {
   int st = check_shape(s);
   if (st) return st;
-  if (!c || !q || !out || !ws) return LOWRAM_ERR_NULL;
+  if (!c || !q || !out) return LOWRAM_ERR_NULL;
   const Plan p = make_plan(s);
   const bool has_prefix = s->prefix_len > 0 && p.n_cand > 0;
   const bool ci4 = s->coeff_fmt == LOWRAM_FMT_INT4_G32, ri4 = s->resid_fmt == LOWRAM_FMT_INT4_G32;
@@ -164,7 +165,7 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
     if (c->cand_ids && (s->prefix_cap || s->window_cap)) return LOWRAM_ERR_SHAPE;  // eviction: dense only
   }
   if (s->window > 0 && (!c->win_k || !c->win_v)) return LOWRAM_ERR_NULL;
-  const void* bulk[] = {q, out, ws, c->coeff, c->basis, c->landmark, c->w1, c->w2, c->res_val,
+  const void* bulk[] = {q, out, c->coeff, c->basis, c->landmark, c->w1, c->w2, c->res_val,
                         c->win_k, c->win_v};
   for (const void* ptr : bulk)
     if (ptr && misaligned(ptr, 16)) return LOWRAM_ERR_ALIGN;
@@ -175,8 +176,17 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   if (kpre_out && misaligned(kpre_out, 16)) return LOWRAM_ERR_ALIGN;
   if (kpost_out && misaligned(kpost_out, 16)) return LOWRAM_ERR_ALIGN;
   if (p.n_split > kMergeMaxSplits) return LOWRAM_ERR_UNSUPPORTED;
-  if (ws_bytes < p.total) return LOWRAM_ERR_WORKSPACE;
+  return LOWRAM_OK;
+}
 
+// The launches of a decode step whose arguments check_step accepted, with a
+// workspace of at least make_plan(s).total bytes.
+int launch_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t* q, uint16_t* out,
+                int32_t* sel_out, float* scores_out, float* kpre_out, float* kpost_out,
+                float* vhat_out, void* ws, void* stream, void* const* events, bool shared) {
+  const Plan p = make_plan(s);
+  const bool has_prefix = s->prefix_len > 0 && p.n_cand > 0;
+  const bool ci4 = s->coeff_fmt == LOWRAM_FMT_INT4_G32, ri4 = s->resid_fmt == LOWRAM_FMT_INT4_G32;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   unsigned char* w = static_cast<unsigned char*>(ws);
   uint32_t* keys = reinterpret_cast<uint32_t*>(w + p.off_keys);
@@ -249,6 +259,51 @@ int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t*
   if (launch_merge(part, out, s->batch, s->n_heads_kv, p.g, n_split, hs) != hipSuccess)
     return LOWRAM_ERR_HIP;
   if (!mark(4)) return LOWRAM_ERR_HIP;
+  return LOWRAM_OK;
+}
+
+int run_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t* q, uint16_t* out,
+             int32_t* sel_out, float* scores_out, float* kpre_out, float* kpost_out,
+             float* vhat_out, void* ws, size_t ws_bytes, void* stream,
+             void* const* events = nullptr, bool shared = false) {
+  const int st = check_step(s, c, q, out, sel_out, scores_out, kpre_out, kpost_out, vhat_out);
+  if (st) return st;
+  if (!ws) return LOWRAM_ERR_NULL;
+  if (misaligned(ws, 16)) return LOWRAM_ERR_ALIGN;
+  if (ws_bytes < make_plan(s).total) return LOWRAM_ERR_WORKSPACE;
+  return launch_step(s, c, q, out, sel_out, scores_out, kpre_out, kpost_out, vhat_out, ws, stream, events,
+                     shared);
+}
+
+// ---------------------------------------------------------------------------
+// Fixed scratch of the no-allocation decode step.  Each GPU the library runs
+// on holds its own copy of this array from the library's load until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[LOWRAM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (looked up at the first call on
+// that device).
+int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LOWRAM_ERR_HIP;
+  if (dev < 0 || dev >= kScratchDevices) return LOWRAM_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LOWRAM_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
   return LOWRAM_OK;
 }
 
@@ -342,6 +397,9 @@ const char* lowram_strerror(int status) {
     case LOWRAM_ERR_WORKSPACE: return "workspace too small";
     case LOWRAM_ERR_ALIGN: return "misaligned pointer";
     case LOWRAM_ERR_HIP: return "HIP launch failed";
+    case LOWRAM_ERR_SCRATCH:
+      return "the shape needs more workspace than the fixed no-allocation scratch holds "
+             "(LOWRAM_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -376,6 +434,18 @@ int lowram_decode_step(const lowram_shape* shape, const lowram_layer_cache* cach
                        size_t ws_bytes, void* stream) {
   return run_step(shape, cache, q, out, sel_out, nullptr, nullptr, nullptr, nullptr, workspace,
                   ws_bytes, stream);
+}
+
+int lowram_decode_step_noalloc(const lowram_shape* shape, const lowram_layer_cache* cache,
+                               const uint16_t* q, uint16_t* out, int32_t* sel_out, void* stream) {
+  const int st = check_step(shape, cache, q, out, sel_out, nullptr, nullptr, nullptr, nullptr);
+  if (st) return st;
+  if (make_plan(shape).total > (size_t)LOWRAM_NOALLOC_SCRATCH_BYTES) return LOWRAM_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int sp = scratch_ptr(&ws);
+  if (sp) return sp;
+  return launch_step(shape, cache, q, out, sel_out, nullptr, nullptr, nullptr, nullptr, ws, stream, nullptr,
+                     false);
 }
 
 int lowram_decode_step_events(const lowram_shape* shape, const lowram_layer_cache* cache,

@@ -23,6 +23,7 @@ SYMBOLS = (
     "lowram_workspace_bytes",
     "lowram_decode_plan",
     "lowram_decode_step",
+    "lowram_decode_step_noalloc",
     "lowram_decode_stages",
     "lowram_decode_step_events",
     "lowram_decode_shared",
@@ -39,7 +40,11 @@ SYMBOLS = (
     "lowram_fit_basis",
 )
 
-ERRORS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "UNSUPPORTED", -4: "WORKSPACE", -5: "ALIGN", -6: "HIP"}
+ERRORS = {0: "OK", -1: "NULL", -2: "SHAPE", -3: "UNSUPPORTED", -4: "WORKSPACE", -5: "ALIGN", -6: "HIP",
+          -7: "SCRATCH"}
+
+# LOWRAM_NOALLOC_SCRATCH_BYTES of include/lowram.h
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class LowramAttendPlan(ctypes.Structure):
@@ -126,6 +131,8 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(LowramAttendPlan)]
         L.lowram_decode_step.argtypes = [ctypes.POINTER(LowramShape), ctypes.POINTER(LowramLayerCache),
                                          vp, vp, vp, vp, sz, vp]
+        L.lowram_decode_step_noalloc.argtypes = [ctypes.POINTER(LowramShape), ctypes.POINTER(LowramLayerCache),
+                                                 vp, vp, vp, vp]
         L.lowram_decode_stages.argtypes = [ctypes.POINTER(LowramShape), ctypes.POINTER(LowramLayerCache),
                                            vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.lowram_decode_step_events.argtypes = [ctypes.POINTER(LowramShape), ctypes.POINTER(LowramLayerCache),
@@ -230,6 +237,13 @@ def decode_step(shape, cache, q, out, workspace, sel_out=None, stream=None) -> N
     _check(lib().lowram_decode_step(ctypes.byref(shape), ctypes.byref(c), _ptr(q), _ptr(out),
                                     _ptr(sel_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)), "lowram_decode_step")
+
+
+def decode_step_noalloc(shape, cache, q, out, sel_out=None, stream=None) -> None:
+    """lowram_decode_step_noalloc: the decode step on the library's fixed scratch (no workspace)."""
+    c = cache if isinstance(cache, LowramLayerCache) else make_cache(cache)
+    _check(lib().lowram_decode_step_noalloc(ctypes.byref(shape), ctypes.byref(c), _ptr(q), _ptr(out),
+                                            _ptr(sel_out), _stream(stream)), "lowram_decode_step_noalloc")
 
 
 def decode_step_events(shape, cache, q, out, workspace, events, sel_out=None, stream=None) -> None:

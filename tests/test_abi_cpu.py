@@ -156,6 +156,33 @@ def test_shapes_at_the_grid_limits_are_accepted():
     assert native.dense_workspace_bytes(native.dense_shape(1023, 1025 * 2048, 32, 16)) > 0
 
 
+def call_noalloc(s, cache, q=FakeTensor(0x7000000000), out=FakeTensor(0x7100000000)):
+    with pytest.raises(native.LowramError) as e:
+        native.decode_step_noalloc(s, cache, q, out, stream=0)
+    return e.value.status
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    m = re.search(r"#define\s+LOWRAM_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == native.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_refuses_shapes_past_its_scratch_before_any_hip_call():
+    import synth
+    big = native.make_shape(synth.C3, batch=28)            # ~93 MB of workspace
+    assert native.workspace_bytes(big) > native.NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(big, fake_cache()) == -7
+    assert "no-allocation scratch" in native.strerror(-7)
+    fits = native.make_shape(synth.C3, batch=16)
+    assert native.workspace_bytes(fits) <= native.NOALLOC_SCRATCH_BYTES
+    # argument errors come first, as for lowram_decode_step
+    c = fake_cache()
+    c["coeff"] = None
+    assert call_noalloc(big, c) == -1
+    assert call_noalloc(shape(n_heads_q=7), fake_cache()) == -2
+    assert call_noalloc(shape(), fake_cache(), q=FakeTensor(0x7000000008)) == -5
+
+
 def test_step_requires_int4_scales_and_candidates():
     s = shape(rank=128, coeff_fmt=1)
     assert call_step(s, fake_cache()) == -1          # coeff_scale missing
