@@ -172,7 +172,8 @@ int lowram_decode_step(const lowram_shape* shape, const lowram_layer_cache* cach
  * lowram_decode_step, and gets the same results.
  *   Limit: shapes whose lowram_workspace_bytes exceeds the scratch size are
  *   refused with LOWRAM_ERR_SCRATCH before any HIP call (e.g. at 262144
- *   tokens and rank 512, about 3.3 MB per sequence: up to 20 sequences).
+ *   tokens, top-1024 chunks and rank 512, about 7.7 MB per sequence: up
+ *   to 8 sequences).
  *   Every call on a GPU shares that GPU's scratch, which keeps the last
  *   call's contents (nothing in it needs to start at zero): calls that
  *   overlap on one GPU (different streams, or threads without ordering) race

@@ -30,9 +30,10 @@ constexpr int64_t kMaxGrid1D = ((int64_t)0xFFFFFFFF / 256) & ~(int64_t)7;
 
 struct Plan {
   // n_split: partial slots per head of the 4-wave kernel (one per tile);
-  // n_part: slots reserved per head, enough for either attention kernel
-  int g, n_chunks, n_cand, k_eff, n_sel_tiles, n_win_tiles, n_split, n_part;
-  size_t off_keys, off_sel, off_part, total;
+  // n_part: slots reserved per head, enough for either attention kernel;
+  // n_ph: PH rows reserved per head (the producer/consumer kernel's slots)
+  int g, n_chunks, n_cand, k_eff, n_sel_tiles, n_win_tiles, n_split, n_part, n_ph;
+  size_t off_keys, off_sel, off_part, off_ph, total;
 };
 
 int check_shape(const lowram_shape* s) {
@@ -108,12 +109,14 @@ Plan make_plan(const lowram_shape* s) {
   p.n_split = p.n_sel_tiles + p.n_win_tiles;
   // The producer/consumer kernel writes 4 slots per group of tiles, and its
   // groups hold at least 2 tiles where a head has 2: 2 n + 6 slots cover it.
-  p.n_part = (p.n_sel_tiles > 0 ? 2 * p.n_sel_tiles + 6 : 0) + p.n_win_tiles;
+  p.n_ph = p.n_sel_tiles > 0 ? 2 * p.n_sel_tiles + 6 : 0;
+  p.n_part = p.n_ph + p.n_win_tiles;
   const size_t heads = (size_t)s->batch * s->n_heads_kv;
   p.off_keys = 0;
   p.off_sel = align_up(heads * (size_t)p.n_cand * 4);
   p.off_part = p.off_sel + align_up(heads * (size_t)p.k_eff * 4);
-  p.total = p.off_part + align_up(heads * (size_t)p.n_part * p.g * kPartStride * 4);
+  p.off_ph = p.off_part + align_up(heads * (size_t)p.n_part * p.g * kPartStride * 4);
+  p.total = p.off_ph + align_up(heads * (size_t)p.n_ph * p.g * kHidden * 4);
   return p;
 }
 
@@ -192,6 +195,7 @@ int launch_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16
   uint32_t* keys = reinterpret_cast<uint32_t*>(w + p.off_keys);
   int32_t* sel = reinterpret_cast<int32_t*>(w + p.off_sel);
   float* part = reinterpret_cast<float*>(w + p.off_part);
+  float* ph = reinterpret_cast<float*>(w + p.off_ph);
   auto mark = [&](int i) {
     return !events || hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) == hipSuccess;
   };
@@ -215,7 +219,7 @@ int launch_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16
   a.w1 = c->w1; a.b1 = c->b1; a.w2 = c->w2; a.b2 = c->b2;
   a.res_idx = c->res_idx; a.res_val = c->res_val; a.res_scale = c->res_scale;
   a.res_desc = c->res_chunk_desc; a.win_k = c->win_k; a.win_v = c->win_v;
-  a.q = q; a.sel = sel; a.part = part;
+  a.q = q; a.sel = sel; a.part = part; a.ph = ph; a.n_ph = p.n_ph;
   a.kpre_out = kpre_out; a.kpost_out = kpost_out; a.vhat_out = vhat_out;
   a.nb = s->batch; a.hq = s->n_heads_q; a.hkv = s->n_heads_kv; a.g = p.g;
   a.prefix = s->prefix_len; a.window = s->window; a.n_chunks = p.n_chunks; a.k_eff = p.k_eff;
@@ -256,7 +260,15 @@ int launch_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16
   if (launch_attend(a, s->rank, ci4, ri4, hs) != hipSuccess) return LOWRAM_ERR_HIP;
   if (launch_attend_pipe(a, s->rank, ci4, ri4, hs) != hipSuccess) return LOWRAM_ERR_HIP;
   if (!mark(3)) return LOWRAM_ERR_HIP;
-  if (launch_merge(part, out, s->batch, s->n_heads_kv, p.g, n_split, hs) != hipSuccess)
+  MergePH phm;
+  if (ap.pipe) {  // the producer/consumer kernel's slots leave W2 to the merge
+    phm.ph = ph;
+    phm.n_ph_used = ap.sel_slots;
+    phm.ph_stride = p.n_ph;
+    phm.cache_bmul = a.cache_bmul;
+    phm.w2 = c->w2;
+  }
+  if (launch_merge(part, out, s->batch, s->n_heads_kv, p.g, n_split, hs, phm) != hipSuccess)
     return LOWRAM_ERR_HIP;
   if (!mark(4)) return LOWRAM_ERR_HIP;
   return LOWRAM_OK;

@@ -723,15 +723,22 @@ hipError_t launch_attend(const AttendArgs& a, int rank, bool ci4, bool ri4, hipS
 // wave 0 forms the weights w_s = exp2(m_s - M) / L in LDS (M = max_s m_s,
 // L = sum_s exp2(m_s - M) l_s) while those loads are in flight; the 4 split
 // groups' sums meet in LDS.
+// Splits of the producer/consumer kernel carry, beside o (the residual share
+// and b2 l), the PH row sum_t p_t gelu(W1 K_pre + b1) of their tokens, and
+// the value MLP's second layer is applied here, once:
+//   out = (sum_s w_s o_s + W2 (sum_s w_s PH_s)) / L.
+// The 512 threads first form sum_s w_s PH_s (256 units x 2 halves of the
+// splits), then thread (d, sg) adds W2[d][64 sg .. 64 sg + 63] . that sum.
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 512;
 constexpr int kMergeBatch = 16;
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part,
                                                               uint16_t* __restrict__ out, int hkv,
-                                                              int g, int n_split) {
+                                                              int g, int n_split, MergePH phm) {
   __shared__ float wgt[kMergeMaxSplits];
   __shared__ float red[3][kHeadDim];
+  __shared__ float phc[2][kHidden];
   __shared__ float inv_l;
   const int tid = threadIdx.x, d = tid & (kHeadDim - 1), sg = tid >> 7;
   const int j = blockIdx.x;
@@ -739,12 +746,21 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   const size_t st = (size_t)g * kPartStride;  // between splits
   const float* pj = part + head * (size_t)n_split * st + (size_t)j * kPartStride;
   const int ns = n_split;
+  const int nph = phm.n_ph_used;
   // this thread's first batch of o values (indices clamped into the list,
   // so that the loads are unconditional and all in flight together; the
   // extra ones are not summed)
   float ov[kMergeBatch];
 #pragma unroll
   for (int k = 0; k < kMergeBatch; ++k) ov[k] = pj[min(sg + 4 * k, ns - 1) * st + 2 + d];
+  // W2 row d, units [64 sg, 64 sg + 64), of this head (issued with the o loads)
+  bf16x8 w2v[8];
+  if (nph > 0) {
+    const size_t chead = (size_t)blockIdx.z * phm.cache_bmul * hkv + blockIdx.y;
+    const uint16_t* w2row = phm.w2 + (chead * kHeadDim + d) * kHidden + 64 * sg;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w2v[k] = load_bf16x8(w2row + 8 * k);
+  }
   if (tid < 64) {
     float m = -__builtin_huge_valf();
     for (int sp = tid; sp < ns; sp += 64) m = fmaxf(m, pj[sp * st]);
@@ -775,6 +791,34 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
       acc += sp < ns ? ov[k] * wgt[min(sp, ns - 1)] : 0.f;
     }
   }
+  if (nph > 0) {
+    // sum_s w_s PH_s: unit u = tid % 256, splits of parity tid / 256
+    const int u = tid & (kHidden - 1), half = tid >> 8;
+    const size_t phs = (size_t)g * kHidden;  // between splits
+    const float* pp = phm.ph + head * (size_t)phm.ph_stride * phs + (size_t)j * kHidden + u;
+    float hs = 0.f;
+    for (int base = half; base < nph; base += 2 * kMergeBatch) {
+      float hv[kMergeBatch];
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) hv[k] = pp[min(base + 2 * k, nph - 1) * phs];
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const int sp = base + 2 * k;
+        hs += sp < nph ? hv[k] * wgt[min(sp, nph - 1)] : 0.f;
+      }
+    }
+    phc[half][u] = hs;
+    __syncthreads();
+    float w2acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int uu = 64 * sg + 8 * k + e;
+        w2acc = fmaf((float)w2v[k][e], phc[0][uu] + phc[1][uu], w2acc);
+      }
+    acc += w2acc;
+  }
   if (sg > 0) red[sg - 1][d] = acc;
   __syncthreads();
   if (sg == 0) {
@@ -784,9 +828,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
 }
 
 hipError_t launch_merge(const float* part, uint16_t* out, int nb, int hkv, int g, int n_split,
-                        hipStream_t st) {
+                        hipStream_t st, const MergePH& phm) {
   if (n_split > kMergeMaxSplits || n_split < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_kernel, dim3(g, hkv, nb), dim3(kMergeThreads), 0, st, part, out, hkv, g, n_split);
+  if (phm.n_ph_used > 0 && (!phm.ph || !phm.w2 || phm.n_ph_used > n_split || phm.ph_stride < phm.n_ph_used))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_kernel, dim3(g, hkv, nb), dim3(kMergeThreads), 0, st, part, out, hkv, g, n_split, phm);
   return hipGetLastError();
 }
 

@@ -5,7 +5,11 @@
 // paragraphs; explainer "How the method works"):
 //   K_pre = C[t] . B_blk, K_post = RoPE(K_pre, t), z = q . K_post,
 //   sum_t p_t V_t = W2 (sum_t p_t gelu(W1 K_pre + b1)) + b2 sum_t p_t + sum_t p_t R_t.
-// What changes is which wave does what, and when.
+// What changes is which wave does what, and when, and where W2 is applied:
+// W2 is linear, so this kernel stops at PH = sum_t p_t gelu(W1 K_pre + b1)
+// (per slot and group of tiles, beside the output-space record of the
+// residuals and b2), and the merge kernel applies W2 once per (sequence, KV
+// head) to the softmax-weighted sum of the groups' PH.
 //
 // In the 4-wave kernel every wave runs the MFMA-only reconstruction and then
 // the VALU-heavy value section of its own tokens, so the two co-resident
@@ -26,9 +30,9 @@
 //                              slice hand K_pre to the consumer through LDS,
 //                              then RoPE, QK and the running softmax, and
 //                              hand over the weights p
-//   consumer, tile-step i + 1  the value MLP of tile i from the W1/W2 stream
-//                              (32 hidden units per step), then the tile's
-//                              residual rows
+//   consumer, tile-step i + 1  the first MLP layer, GELU and PH of tile i
+//                              from the W1 stream (32 hidden units per step),
+//                              then the tile's residual rows
 // so on every SIMD the reconstruction of one tile runs beside the value
 // section of the one before.  Producer and consumer run separate loops with
 // the same number of barriers; the role is a scalar (wave-uniform) branch.
@@ -41,11 +45,12 @@
 // m' = max(m, max_t z_t), sends the consumer p_t = exp2(z_t - m') and
 // alpha = exp2(m - m'), and sets l = l alpha + sum_t p_t; a group starts from
 // m = -inf, so its first alpha is 0 and clears the consumer's accumulator.
-// The consumer scales its output accumulator by alpha before adding the
-// tile.  When a group ends, each consumer writes its slot's partial
-// (m, l, o + b2 l) per query head to partial slot 4 gx + slot of the head
-// (gx = the group's index in the head); the merge kernel combines them with
-// the window's.
+// The consumer scales its accumulators (PH, and the residual share R) by
+// alpha before adding the tile.  When a group ends, each consumer writes its
+// slot's partials per query head to slot 4 gx + slot of the head (gx = the
+// group's index in the head): (m, l, R + b2 l) among the output-space
+// partials, and PH (256 hidden units) in the PH area; the merge kernel
+// combines them with the window's.
 #include "attend_ops.h"
 #include "common.h"
 #include "internal.h"
@@ -61,7 +66,7 @@ static_assert(kAttSelNT == 2 && kAttChunksWG == 16, "tiles of 128 tokens, 32 per
 
 struct PipeLds {
   alignas(16) unsigned char bring[2][kStage];                   // basis stages (producers)
-  alignas(16) unsigned char mring[2][kStage];                   // W1/W2 stages (consumers)
+  alignas(16) unsigned char mring[2][kStage / 2];               // W1 stages (consumers)
   alignas(16) unsigned char hand[2][kPipeSlots][kHandSlot];     // by tile parity; consumer residual rows too
   // RoPE rotations as fp16 (cos, sin) tables, frequency-contiguous: by the
   // offset 0..7 inside a chunk, and to each chunk start (per producer, its 4 chunks)
@@ -512,95 +517,81 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     for (int s = 0; s < NS; ++s) __syncthreads();  // the consumers' last tile
   } else {
     // ===================================================================== consumer
-    // Software-pipelined by one value stage: step c runs GELU, PH and OUT of
+    // Software-pipelined by one value stage: step c runs GELU and PH of
     // stage c - 1 (VALU work that overlaps the producer's reconstruction
     // MFMAs and this wave's own next products) and then MLP1 of stage c.
     // The last stage of a tile finishes at step 0 of the next tile-step (or
-    // after the loop).  Accordingly the W1 half of stage c is stored at the
-    // end of step c - 1 and read at step c, the W2 half stored at the end of
-    // step c and read at step c + 1, each half in a ring of two buffers.
-    // W1 and W2 of one cache head through descriptors carried across tiles,
-    // moved to the next tile's head at the steps whose loads start reading it
-    // (W1: step NS - 2, W2: step NS - 1)
+    // after the loop).  Accordingly W1 of stage c is stored at the end of
+    // step c - 1 and read at step c, in a ring of two buffers.
+    // W1 of one cache head through a descriptor carried across tiles, moved
+    // to the next tile's head at the step whose loads start reading it (NS - 2)
     auto w1_of = [&](int chead) { return buffer_rsrc(a.w1 + (size_t)chead * kHidden * kHeadDim, kHidden * kHeadDim * 2); };
-    auto w2_of = [&](int chead) { return buffer_rsrc(a.w2 + (size_t)chead * kHeadDim * kHidden, kHeadDim * kHidden * 2); };
-    // stage c: W1 rows [32 c, 32 c + 32) in pi order (8 KiB at offset 0 of a
-    // ring buffer), W2 columns [32 c, 32 c + 32) (natural, four rows per
-    // 256-byte line, 8 KiB at offset 8192)
+    // stage c: W1 rows [32 c, 32 c + 32) in pi order (8 KiB of a ring buffer)
     const int w1row = rt >> 4, w1p = rt & 15;
     const uint32_t w1_goff = (uint32_t)(((8 * ((w1row >> 2) & 3) + (w1row & 3)) * kHeadDim + 8 * w1p) * 2);
     const int w1_loff = w1row * 256 + (w1p ^ (w1row & 15)) * 16;
-    const uint32_t w2_goff = (uint32_t)(((rt >> 2) * kHidden + 8 * (rt & 3)) * 2);
-    const int w2_loff = 8192 + (rt >> 4) * 256 + ((rt & 15) ^ ((rt >> 4) & 15)) * 16;
     auto w1_load = [&](__amdgpu_buffer_rsrc_t w1r, int c, u32x4 (&r)[2]) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) r[u] = buffer_ld16(w1r, w1_goff, (32 * c + 4 * u) * kHeadDim * 2);
-    };
-    auto w2_load = [&](__amdgpu_buffer_rsrc_t w2r, int c, u32x4 (&r)[2]) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) r[u] = buffer_ld16(w2r, w2_goff, (u * 64 * kHidden + 32 * c) * 2);
     };
     auto w1_store = [&](int buf, const u32x4 (&r)[2]) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(L.mring[buf] + w1_loff + 4096 * u) = r[u];
     };
-    auto w2_store = [&](int buf, const u32x4 (&r)[2]) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(L.mring[buf] + w2_loff + 4096 * u) = r[u];
-    };
-    // W1 position row 16 hn + col, piece 4 ks + grp; W2 row 16 nd + col, piece grp
-    int rw1[4], rw2[4];
+    // W1 position row 16 hn + col, piece 4 ks + grp
+    int rw1[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) rw1[s] = col * 256 + ((4 * s + grp) ^ col) * 16;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      rw2[q] = 8192 + (col >> 2) * 256 + ((((col & 3) ^ q) << 2) | (grp ^ (col >> 2))) * 16;
 
-    u32x4 w1reg[NS][2], w2reg[NS][2];
-    __amdgpu_buffer_rsrc_t w1r, w2r;
+    u32x4 w1reg[NS][2];
+    __amdgpu_buffer_rsrc_t w1r;
     {
       const int chead0 = pipe_first(a, wg).chead;
       w1r = w1_of(chead0);
-      w2r = w2_of(chead0);
       w1_load(w1r, 0, w1reg[0]);
       w1_load(w1r, 1, w1reg[1]);
-      w2_load(w2r, 0, w2reg[0]);
     }
     w1_store(0, w1reg[0]);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < NS; ++s) __syncthreads();  // the producers' first tile
 
-    f32x4 oacc[8];
+    // The value section without W2: over a group, this slot accumulates
+    //   PH[h][j] = sum_t p_t[j] gelu(W1 K_pre[t] + b1)[h]
+    // (rescaled by alpha per tile, like any running-softmax accumulator);
+    // the merge kernel applies W2 once per (sequence, KV head) to the
+    // weighted sum of the groups' PH.  racc holds the residual rows' share,
+    // sum_t p_t R_t, in the output space.
+    f32x4 racc[8];
 #pragma unroll
-    for (int nd = 0; nd < 8; ++nd) oacc[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nd = 0; nd < 8; ++nd) racc[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // PH of stage cs (hidden positions 16 hn + 4 grp + e of the stage) in phacc[cs][hn]
+    f32x4 phacc[NS][2];
+#pragma unroll
+    for (int cs = 0; cs < NS; ++cs)
+#pragma unroll
+      for (int hn = 0; hn < 2; ++hn) phacc[cs][hn] = f32x4{0.f, 0.f, 0.f, 0.f};
     f32x4 hacc[2][NT][2];  // MLP1 of stage c in hacc[c & 1] (before GELU)
     f16x8 pa;              // softmax weights of the current tile (fp16: the PH product)
-    // GELU, PH and OUT of stage cs (MLP1 result in hacc[cs & 1], W2 operands
-    // already read), softmax weights pw:
-    //   PH  D[h][j] = gelu(hid)^T[h][t] x p^T[t][j];  OUT D[d][j] += W2[d][h] x PH[h][j]
-    auto finish_stage = [&](int cs, const bf16x8 (&w2op)[8], const f16x8& pw) {
+    // GELU and PH of stage cs (MLP1 result in hacc[cs & 1]), softmax weights pw:
+    //   PH  D[h][j] += gelu(hid)^T[h][t] x p^T[t][j]
+    auto finish_stage = [&](int cs, const f16x8& pw) {
       const f32x4 lo[2] = {hacc[cs & 1][0][0], hacc[cs & 1][0][1]};
       const f32x4 hi[2] = {hacc[cs & 1][1][0], hacc[cs & 1][1][1]};
       f16x8 gl[2];
       gelu16_h(lo, hi, gl);
-      f32x4 pht[2];
 #pragma unroll
-      for (int hn = 0; hn < 2; ++hn) pht[hn] = mfma16h(gl[hn], pw, f32x4{0.f, 0.f, 0.f, 0.f});
-      const bf16x8 hbv = pack8(pht[0], pht[1]);
-#pragma unroll
-      for (int nd = 0; nd < 8; ++nd) oacc[nd] = mfma16(w2op[nd], hbv, oacc[nd]);
+      for (int hn = 0; hn < 2; ++hn) phacc[cs][hn] = mfma16h(gl[hn], pw, phacc[cs][hn]);
     };
-    auto read_w2 = [&](int cs, bf16x8 (&w2op)[8]) {
-      const unsigned char* sb = L.mring[cs & 1];
-#pragma unroll
-      for (int nd = 0; nd < 8; ++nd) w2op[nd] = lds16(sb, rw2[nd & 3] + 1024 * nd);
-    };
-    // group grp_id's partial: slot 4 gx + slot of its head bh; (m, l) from the
-    // producer, b2 of the head from LDS (parity par)
+    // group t's partials: slot 4 gx + slot of its head bh.  The output-space
+    // record (m, l, R share + b2 l) with (m, l) from the producer and b2 of
+    // the head from LDS (parity par), and the slot's PH row of each query
+    // head in hidden-unit order: position 16 hn + 4 grp + e of stage cs is
+    // unit 32 cs + 8 grp + 4 hn + e (the pi order of the W1 rows).
     auto write_part = [&](const PipeCur& t, float m, float l, int par) {
       if (col >= g) return;
-      float* pp = a.part + (((size_t)t.bh * a.n_split + kPipeSlots * t.gx + slot) * g + col) * kPartStride;
+      const size_t sl = (size_t)t.bh * a.n_split + kPipeSlots * t.gx + slot;
+      float* pp = a.part + (sl * g + col) * kPartStride;
       if (grp == 0) {
         pp[0] = m;
         pp[1] = l;
@@ -610,8 +601,13 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int d = 16 * nd + 4 * grp + e;
-          pp[2 + d] = fmaf(L.b2f[par][d], l, oacc[nd][e]);
+          pp[2 + d] = fmaf(L.b2f[par][d], l, racc[nd][e]);
         }
+      float* ph = a.ph + (((size_t)t.bh * a.n_ph + kPipeSlots * t.gx + slot) * g + col) * kHidden;
+#pragma unroll
+      for (int cs = 0; cs < NS; ++cs)
+#pragma unroll
+        for (int hn = 0; hn < 2; ++hn) *reinterpret_cast<f32x4*>(ph + 32 * cs + 8 * grp + 4 * hn) = phacc[cs][hn];
     };
     constexpr int RL = RI4 ? 2 : 8;  // 16-byte residual pieces per lane
     float m_cur = 0.f, l_cur = 0.f;    // the producer's (m, l) after the tile being consumed
@@ -628,8 +624,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
       u32x2 rsc = {0u, 0u};
 #pragma unroll
       for (int c = 0; c < NS; ++c) {
-        // ---- LDS operands first: MLP1 of stage c, OUT of stage c - 1, and at a
-        //      tile start the handoff (at the very first step the W2 read is unused)
+        // ---- LDS operands first: MLP1 of stage c, and at a tile start the handoff
         bf16x8 w1op[4][2];
         f32x4 b1v[2];
         {
@@ -641,8 +636,6 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 #pragma unroll
           for (int hn = 0; hn < 2; ++hn) b1v[hn] = L.b1q[i & 1][32 * c + 16 * hn + col];
         }
-        bf16x8 w2op[8];  // W2 operands of the previous stage
-        read_w2((c + NS - 1) % NS, w2op);
         f16x8 pnew;
         float alpha = 1.f;
         float m_prev = 0.f, l_prev = 0.f;
@@ -670,27 +663,27 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
               hacc[c & 1][tt][hn] = mfma16(kpre_b[tt][ks], w1op[ks][hn], ks == 0 ? b1v[hn] : hacc[c & 1][tt][hn]);
-        // ---- the previous stage: GELU, PH, OUT (at a tile start: the previous
+        // ---- the previous stage: GELU, PH (at a tile start: the previous
         //      tile's last stage with that tile's weights, then the rescale)
-        if (c > 0 || i > 0) finish_stage((c + NS - 1) % NS, w2op, pa);
+        if (c > 0 || i > 0) finish_stage((c + NS - 1) % NS, pa);
         if (c == 0) {
           if (prev_end) write_part(tp, m_prev, l_prev, (i - 1) & 1);
           pa = pnew;
 #pragma unroll
           for (int e = 0; e < 8; ++e) pab[e] = (__bf16)(float)pa[e];
 #pragma unroll
-          for (int nd = 0; nd < 8; ++nd) oacc[nd] *= alpha;
+          for (int nd = 0; nd < 8; ++nd) racc[nd] *= alpha;
+#pragma unroll
+          for (int cs = 0; cs < NS; ++cs)
+#pragma unroll
+            for (int hn = 0; hn < 2; ++hn) phacc[cs][hn] *= alpha;
         }
 
         if (c == NS - 1) {
-          // ---- residuals: rows -> this slot's handoff region (read at step 0,
-          //      not written again before the tile after next), then
-          //      OUT += R^T[d][t] x p^T[t][j]
+          // ---- residuals: the rows are in this slot's handoff region (stored
+          //      at steps 3-6); R share += R^T[d][t] x p^T[t][j]
           if constexpr (!RI4) {
-#pragma unroll
-            for (int u = 0; u < RL; ++u)
-              *reinterpret_cast<u32x4*>(hb + (4 * u + (lane >> 4)) * kResRow + (lane & 15) * 16) = rres[u];
-            // the reads below take the bytes just written under another type
+            // the reads below take bytes written under another type
             asm volatile("" ::: "memory");
 #pragma unroll
             for (int nd = 0; nd < 8; ++nd) {
@@ -700,14 +693,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
                 const int t = e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4;
                 rop[e] = *reinterpret_cast<const __bf16*>(hb + t * kResRow + (16 * nd + col) * 2);
               }
-              oacc[nd] = mfma16(rop, pab, oacc[nd]);
+              racc[nd] = mfma16(rop, pab, racc[nd]);
             }
           } else {
-#pragma unroll
-            for (int u = 0; u < RL; ++u)
-              *reinterpret_cast<u32x4*>(hb + (16 * u + (lane >> 2)) * kResRow4 + (lane & 3) * 16) = rres[u];
-            if (lane < 32) *reinterpret_cast<u32x2*>(hb + lane * kResRow4 + 64) = rsc;
-            asm volatile("" ::: "memory");  // the reads below take these bytes under other types
+            asm volatile("" ::: "memory");  // the reads below take bytes written under other types
             auto resid_at = [&](int t, int d) -> float {
               const uint32_t byte = hb[t * kResRow4 + (d >> 1)];
               const int code = static_cast<int>(((byte >> (4 * (d & 1))) & 0xFu) ^ 8u) - 8;
@@ -722,18 +711,16 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
                 lo[e] = resid_at(4 * grp + e, 16 * nd + col);
                 hi[e] = resid_at(16 + 4 * grp + e, 16 * nd + col);
               }
-              oacc[nd] = mfma16(pack8(lo, hi), pab, oacc[nd]);
+              racc[nd] = mfma16(pack8(lo, hi), pab, racc[nd]);
             }
           }
         }
         // Loads for later steps after this step's work (see the producer):
-        // the same weights every tile, W1 two stages ahead and W2 one, and
-        // the tile's residual rows for step NS - 1
+        // the same weights every tile, W1 two stages ahead, and the tile's
+        // residual rows for step NS - 1
         __builtin_amdgcn_sched_barrier(0);
         if (c == NS - 2) w1r = w1_of(tn.chead);  // from here on the loads are the next tile's
-        if (c == NS - 1) w2r = w2_of(tn.chead);
         w1_load(w1r, (c + 2) % NS, w1reg[(c + 2) % NS]);
-        w2_load(w2r, (c + 1) % NS, w2reg[(c + 1) % NS]);
         if (c >= 2 && c <= 5) {
           // this slot's residual rows, spread over steps 2-5 (zeros where a
           // token has none: reads past the end of the buffer return 0);
@@ -772,24 +759,31 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
             }
           }
         }
-        // W1 of stage c + 1 into the buffer step c - 1 read; W2 of stage c
-        // into the buffer step c - 1 read (stage c - 2)
+        // W1 of stage c + 1 into the buffer step c - 1 read
         w1_store((c + 1) & 1, w1reg[(c + 1) % NS]);
-        w2_store(c & 1, w2reg[c]);
+        // the residual rows loaded a step ago -> this slot's handoff region
+        // (read at step 0, free until the tile after next), so that no row
+        // is held in registers for longer than a step
+        if constexpr (!RI4) {
+          if (c >= 3 && c <= 6) {
+#pragma unroll
+            for (int u = 2 * (c - 3); u < 2 * (c - 2); ++u)
+              *reinterpret_cast<u32x4*>(hb + (4 * u + (lane >> 4)) * kResRow + (lane & 15) * 16) = rres[u];
+          }
+        } else {
+          if (c >= 3 && c - 3 < RL)
+            *reinterpret_cast<u32x4*>(hb + (16 * (c - 3) + (lane >> 2)) * kResRow4 + (lane & 3) * 16) = rres[c - 3];
+          if (c == RL + 3 && lane < 32) *reinterpret_cast<u32x2*>(hb + lane * kResRow4 + 64) = rsc;
+        }
         __syncthreads();
       }
       tp = tc;
       tc = tn;
       tn = pipe_next(a, tn);
     }
-    {
-      // the last tile's last stage (its W2 buffer is not written again), and
-      // the partial of the last group
-      bf16x8 w2op[8];
-      read_w2(NS - 1, w2op);
-      finish_stage(NS - 1, w2op, pa);
-      write_part(tp, m_cur, l_cur, (ntiles - 1) & 1);
-    }
+    // the last tile's last stage, and the partials of the last group
+    finish_stage(NS - 1, pa);
+    write_part(tp, m_cur, l_cur, (ntiles - 1) & 1);
   }
 }
 

@@ -55,6 +55,10 @@ struct AttendArgs {
   const uint16_t* q;
   const int32_t* sel;
   float* part;
+  // producer/consumer kernel: PH rows [head][n_ph][g][kHidden] beside the
+  // output-space partials of its slots (slot s of a head at row s)
+  float* ph;
+  int n_ph;
   float* kpre_out;
   float* kpost_out;
   float* vhat_out;
@@ -101,8 +105,17 @@ hipError_t launch_attend(const AttendArgs& a, int rank, bool coeff_int4, bool re
 size_t split_select_ws_bytes(int n_lists, int n);
 hipError_t launch_select_split(const uint32_t* keys, int32_t* sel, int n_lists, int n, int k, void* ws,
                                hipStream_t st, int sel_stride = -1, float* thresh = nullptr);
+// Merge of the split partials of every (sequence, KV head, query head).  With
+// ph: its first n_ph_used slots also have PH rows (ph [head][ph_stride][g][kHidden]),
+// to which W2 of the head (w2 [cache head][d][kHidden], cache head =
+// sequence * cache_bmul * hkv + KV head) is applied.
+struct MergePH {
+  const float* ph = nullptr;
+  int n_ph_used = 0, ph_stride = 0, cache_bmul = 1;
+  const uint16_t* w2 = nullptr;
+};
 hipError_t launch_merge(const float* part, uint16_t* out, int nb, int hkv, int g, int n_split,
-                        hipStream_t st);
+                        hipStream_t st, const MergePH& phm = MergePH{});
 hipError_t launch_dense(const uint16_t* k, const uint16_t* v, const uint16_t* q, float* part,
                         int nb, int ctx, int hq, int hkv, int n_split, int tok_per_split,
                         float scale_log2, hipStream_t st);

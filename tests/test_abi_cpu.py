@@ -75,10 +75,14 @@ def test_workspace_bytes_formula():
     # selection tiles of 16 chunks (4 waves x 32 tokens), window tiles of 128
     # tokens; partial slots reserved per head: 2 per selection tile + 6 (the
     # producer/consumer kernel's 4 per group of >= 2 tiles) and 1 per window tile
+    # and, for those producer/consumer slots, one PH row of 256 hidden units
+    # per query head
     n_sel = -(-keff // 16)
-    n_part = 2 * n_sel + 6 + -(-cfg.window // 128)
+    n_ph = 2 * n_sel + 6
+    n_part = n_ph + -(-cfg.window // 128)
     al = lambda x: (x + 255) // 256 * 256
-    want = al(heads * cfg.n_cand * 4) + al(heads * keff * 4) + al(heads * n_part * 4 * 130 * 4)
+    want = (al(heads * cfg.n_cand * 4) + al(heads * keff * 4) + al(heads * n_part * 4 * 130 * 4)
+            + al(heads * n_ph * 4 * 256 * 4))
     assert native.workspace_bytes(s) == want
 
 
@@ -169,11 +173,11 @@ def test_noalloc_scratch_size_matches_the_header():
 
 def test_noalloc_refuses_shapes_past_its_scratch_before_any_hip_call():
     import synth
-    big = native.make_shape(synth.C3, batch=28)            # ~93 MB of workspace
+    big = native.make_shape(synth.C3, batch=9)             # ~70 MB of workspace
     assert native.workspace_bytes(big) > native.NOALLOC_SCRATCH_BYTES
     assert call_noalloc(big, fake_cache()) == -7
     assert "no-allocation scratch" in native.strerror(-7)
-    fits = native.make_shape(synth.C3, batch=16)
+    fits = native.make_shape(synth.C3, batch=8)
     assert native.workspace_bytes(fits) <= native.NOALLOC_SCRATCH_BYTES
     # argument errors come first, as for lowram_decode_step
     c = fake_cache()
