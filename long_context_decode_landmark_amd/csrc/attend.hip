@@ -723,12 +723,15 @@ hipError_t launch_attend(const AttendArgs& a, int rank, bool ci4, bool ri4, hipS
 // wave 0 forms the weights w_s = exp2(m_s - M) / L in LDS (M = max_s m_s,
 // L = sum_s exp2(m_s - M) l_s) while those loads are in flight; the 4 split
 // groups' sums meet in LDS.
-// Splits of the producer/consumer kernel carry, beside o (the residual share
-// and b2 l), the PH row sum_t p_t gelu(W1 K_pre + b1) of their tokens, and
-// the value MLP's second layer is applied here, once:
-//   out = (sum_s w_s o_s + W2 (sum_s w_s PH_s)) / L.
-// The 512 threads first form sum_s w_s PH_s (256 units x 2 halves of the
-// splits), then thread (d, sg) adds W2[d][64 sg .. 64 sg + 63] . that sum.
+// The producer/consumer kernel's slots come in groups of 4 (one group of
+// tiles, slot w = consumer w); beside each slot's o (its residual share and
+// b2 l), a group has one PH row, sum_t p_t gelu(W1 K_pre + b1) over its
+// tokens, relative to the largest of its slots' maxima, and the value MLP's
+// second layer is applied here, once:
+//   out = (sum_s w_s o_s + W2 (sum_groups W_g PH_g)) / L,  W_g = max of the group's w_s.
+// The 512 threads first form the weighted sum of the PH rows (256 units x 2
+// halves of the groups), then thread (d, sg) adds W2[d][64 sg .. 64 sg + 63]
+// . that sum.
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 512;
 constexpr int kMergeBatch = 16;
@@ -792,19 +795,22 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
     }
   }
   if (nph > 0) {
-    // sum_s w_s PH_s: unit u = tid % 256, splits of parity tid / 256
+    // sum_g W_g PH_g: unit u = tid % 256, groups of parity tid / 256 (PH row
+    // of group gx = slot 4 gx)
     const int u = tid & (kHidden - 1), half = tid >> 8;
-    const size_t phs = (size_t)g * kHidden;  // between splits
+    const int ngrp = nph / 4;
+    const size_t phs = (size_t)g * kHidden;  // between slots
     const float* pp = phm.ph + head * (size_t)phm.ph_stride * phs + (size_t)j * kHidden + u;
     float hs = 0.f;
-    for (int base = half; base < nph; base += 2 * kMergeBatch) {
+    for (int base = half; base < ngrp; base += 2 * kMergeBatch) {
       float hv[kMergeBatch];
 #pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) hv[k] = pp[min(base + 2 * k, nph - 1) * phs];
+      for (int k = 0; k < kMergeBatch; ++k) hv[k] = pp[4 * min(base + 2 * k, ngrp - 1) * phs];
 #pragma unroll
       for (int k = 0; k < kMergeBatch; ++k) {
-        const int sp = base + 2 * k;
-        hs += sp < nph ? hv[k] * wgt[min(sp, nph - 1)] : 0.f;
+        const int gx = min(base + 2 * k, ngrp - 1);
+        const float wg = fmaxf(fmaxf(wgt[4 * gx], wgt[4 * gx + 1]), fmaxf(wgt[4 * gx + 2], wgt[4 * gx + 3]));
+        hs += base + 2 * k < ngrp ? hv[k] * wg : 0.f;
       }
     }
     phc[half][u] = hs;
@@ -830,7 +836,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
 hipError_t launch_merge(const float* part, uint16_t* out, int nb, int hkv, int g, int n_split,
                         hipStream_t st, const MergePH& phm) {
   if (n_split > kMergeMaxSplits || n_split < 1) return hipErrorInvalidValue;
-  if (phm.n_ph_used > 0 && (!phm.ph || !phm.w2 || phm.n_ph_used > n_split || phm.ph_stride < phm.n_ph_used))
+  if (phm.n_ph_used > 0 && (!phm.ph || !phm.w2 || phm.n_ph_used > n_split || phm.ph_stride < phm.n_ph_used ||
+                            phm.n_ph_used % 4))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(merge_kernel, dim3(g, hkv, nb), dim3(kMergeThreads), 0, st, part, out, hkv, g, n_split, phm);
   return hipGetLastError();

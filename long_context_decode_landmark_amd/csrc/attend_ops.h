@@ -65,18 +65,11 @@ __device__ __forceinline__ f16x8 gelu8_h(f32x4 lo, f32x4 hi) {
                                  0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// GELU of two 8-value operands at once, evaluated level by level across the
-// eight fp16 pairs so that the dependent Horner chains interleave (one chain
-// alone stalls on every step).  Operand hn is (lo[hn], hi[hn]) as for gelu8_h.
-__device__ __forceinline__ void gelu16_h(const f32x4 (&lo)[2], const f32x4 (&hi)[2], f16x8 (&out)[2]) {
-  h2 x[8], s[8], q[8];
-#pragma unroll
-  for (int hn = 0; hn < 2; ++hn) {
-    x[4 * hn + 0] = __builtin_convertvector(f32x2{lo[hn][0], lo[hn][1]}, h2);
-    x[4 * hn + 1] = __builtin_convertvector(f32x2{lo[hn][2], lo[hn][3]}, h2);
-    x[4 * hn + 2] = __builtin_convertvector(f32x2{hi[hn][0], hi[hn][1]}, h2);
-    x[4 * hn + 3] = __builtin_convertvector(f32x2{hi[hn][2], hi[hn][3]}, h2);
-  }
+// GELU (gelu_h2) of eight fp16 pairs in place, evaluated level by level
+// across the pairs so that the dependent Horner chains interleave (one chain
+// alone stalls on every step).
+__device__ __forceinline__ void gelu_h2x8(h2 (&x)[8]) {
+  h2 s[8], q[8];
 #pragma unroll
   for (int p = 0; p < 8; ++p) s[p] = x[p] * x[p];
 #pragma unroll
@@ -99,6 +92,20 @@ __device__ __forceinline__ void gelu16_h(const f32x4 (&lo)[2], const f32x4 (&hi)
                                   h2{(_Float16)1.f, (_Float16)1.f});
     x[p] = x[p] * t;
   }
+}
+
+// GELU of two 8-value operands at once.  Operand hn is (lo[hn], hi[hn]) as
+// for gelu8_h.
+__device__ __forceinline__ void gelu16_h(const f32x4 (&lo)[2], const f32x4 (&hi)[2], f16x8 (&out)[2]) {
+  h2 x[8];
+#pragma unroll
+  for (int hn = 0; hn < 2; ++hn) {
+    x[4 * hn + 0] = __builtin_convertvector(f32x2{lo[hn][0], lo[hn][1]}, h2);
+    x[4 * hn + 1] = __builtin_convertvector(f32x2{lo[hn][2], lo[hn][3]}, h2);
+    x[4 * hn + 2] = __builtin_convertvector(f32x2{hi[hn][0], hi[hn][1]}, h2);
+    x[4 * hn + 3] = __builtin_convertvector(f32x2{hi[hn][2], hi[hn][3]}, h2);
+  }
+  gelu_h2x8(x);
 #pragma unroll
   for (int hn = 0; hn < 2; ++hn)
     out[hn] = __builtin_shufflevector(__builtin_shufflevector(x[4 * hn], x[4 * hn + 1], 0, 1, 2, 3),

@@ -30,13 +30,15 @@
 //                              slice hand K_pre to the consumer through LDS,
 //                              then RoPE, QK and the running softmax, and
 //                              hand over the weights p
-//   consumer, tile-step i + 1  the first MLP layer, GELU and PH of tile i
-//                              from the W1 stream (32 hidden units per step),
-//                              then the tile's residual rows
+//   consumer, tile-step i + 1  the first MLP layer, GELU and PH of tile i:
+//                              consumer w owns hidden units 64 w .. 64 w + 63
+//                              (its W1 rows in registers) and takes one
+//                              16-token piece of the tile per step; then
+//                              slot w's residual rows
 // so on every SIMD the reconstruction of one tile runs beside the value
 // section of the one before.  Producer and consumer run separate loops with
 // the same number of barriers; the role is a scalar (wave-uniform) branch.
-// Everything that depends on the head (basis, W1/W2, biases, queries,
+// Everything that depends on the head (basis, W1, biases, queries,
 // selection list, descriptors) is looked up per tile, and the loads issued
 // for the next tile use the next tile's head.
 //
@@ -45,12 +47,13 @@
 // m' = max(m, max_t z_t), sends the consumer p_t = exp2(z_t - m') and
 // alpha = exp2(m - m'), and sets l = l alpha + sum_t p_t; a group starts from
 // m = -inf, so its first alpha is 0 and clears the consumer's accumulator.
-// The consumer scales its accumulators (PH, and the residual share R) by
-// alpha before adding the tile.  When a group ends, each consumer writes its
-// slot's partials per query head to slot 4 gx + slot of the head (gx = the
-// group's index in the head): (m, l, R + b2 l) among the output-space
-// partials, and PH (256 hidden units) in the PH area; the merge kernel
-// combines them with the window's.
+// The consumers put the four slots' weights on one scale per tile (the
+// largest slot maximum) for PH, and keep slot w's own scale for its residual
+// share R.  When a group ends, consumer w writes slot w's output-space
+// partial (m, l, R + b2 l) per query head to slot 4 gx + w of the head (gx =
+// the group's index in the head) and its quarter of the group's PH (256
+// hidden units, relative to the largest slot maximum) to PH row 4 gx; the
+// merge kernel combines them with the window's.
 #include "attend_ops.h"
 #include "common.h"
 #include "internal.h"
@@ -66,8 +69,8 @@ static_assert(kAttSelNT == 2 && kAttChunksWG == 16, "tiles of 128 tokens, 32 per
 
 struct PipeLds {
   alignas(16) unsigned char bring[2][kStage];                   // basis stages (producers)
-  alignas(16) unsigned char mring[2][kStage / 2];               // W1 stages (consumers)
-  alignas(16) unsigned char hand[2][kPipeSlots][kHandSlot];     // by tile parity; consumer residual rows too
+  alignas(16) unsigned char hand[2][kPipeSlots][kHandSlot];     // K_pre operands and weights, by tile parity
+  alignas(16) unsigned char rrow[kPipeSlots][32 * kResRow];     // each slot's residual rows (consumer w: slot w)
   // RoPE rotations as fp16 (cos, sin) tables, frequency-contiguous: by the
   // offset 0..7 inside a chunk, and to each chunk start (per producer, its 4 chunks)
   alignas(16) _Float16 rope_oc[kChunk][64];
@@ -77,9 +80,7 @@ struct PipeLds {
   // the queries of the current tile's head as fp16: row j < g (zeros above),
   // 16-byte piece p of the row at piece p ^ j
   alignas(16) _Float16 qh[16][kHeadDim];
-  // per tile parity: b1 of unit 32 c + row_perm32(p) at 32 c + p, x4 (an MFMA
-  // C operand), and b2 (read when a group's partial is written)
-  f32x4 b1q[2][kHidden];
+  // b2 of each tile's head, by tile parity (read when a group's partial is written)
   float b2f[2][kHeadDim];
   double invf[64];                       // RoPE frequencies (read where needed: no registers held)
   // per query head after each tile, by tile parity: the accumulator rescale
@@ -289,7 +290,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     load_next_ids(tn);
     // The queries of a tile's head go to LDS as fp16 before its tail (step 0
     // of its tile-step; rank 64: the last step of the tile-step before), from
-    // 16 bytes per thread loaded at the previous tail.
+    // 16 bytes per thread loaded a whole tile-step earlier (step 0 of the tile
+    // before; rank 64: at the previous tail).
     constexpr int kQStep = NR >= 2 ? 0 : NS - 1;
     bf16x8 qld;
     auto load_q = [&](int bh) {
@@ -343,17 +345,15 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
       const bool grp_end = tc.lt + 1 == tc.gend;  // the group ends with this tile
       int rc_next = 0;   // the next tile's rotation-table chunk (clamped)
       uint32_t rdv = 0;
-      uint16_t b1raw = 0, b2raw = 0;  // this tile's biases, to LDS at the last step
+      uint16_t b2raw = 0;  // this tile's b2, to LDS at the last step
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         if (s == kQStep) store_q();  // rank >= 128: this tile's; rank 64: the next tile's
         if (s == NS - 1) {
-          // this tile's biases for its consumer tile-step (b2: for its
-          // partial), ahead of the tail so that they are not held through it
+          // this tile's b2 for its consumer tile-step (for the group's
+          // partial), ahead of the tail so that it is not held through it
           // (indexed as slot base + lane, the lane offsets the other writes use)
-          const float v = bf16_to_f32(b1raw);
           const int ln = fresh(lane);
-          (&L.b1q[i & 1][slot * 64])[ln] = f32x4{v, v, v, v};
           if (slot < kHeadDim / 64) (&L.b2f[i & 1][slot * 64])[ln] = bf16_to_f32(b2raw);
         }
         if (s < NR) {
@@ -364,7 +364,6 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
             const int c0 = __shfl(tokA[0], 8 * (lane & 1)), c1 = __shfl(tokA[1], 8 * (lane & 1));
             if (lane < 4) rdv = a.res_desc[(size_t)chead_c * desc_rows + ((lane & 2) ? c1 : c0) / kChunk];
             const int r = fresh(rt);
-            b1raw = a.b1[(size_t)chead_c * kHidden + (r & ~31) + row_perm32(r & 31)];
             b2raw = a.b2[(size_t)chead_c * kHeadDim + (r & (kHeadDim - 1))];
           }
           if (s == (NR > 1 ? 1 : 0)) {
@@ -375,12 +374,6 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
           if constexpr (LG == 0) gather(s, tokA, cseq_c);  // rank 64: the stage's own rows
           __builtin_amdgcn_sched_barrier(0);
 
-          if (s == 0) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-              for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
           // all 16 basis operands of the stage are read first, so that the
           // matrix core is not left waiting on one LDS round trip per pair
           const unsigned char* sb = L.bring[(i * NR + s) & 1];
@@ -401,7 +394,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-              for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mfma16(aop[ks][mt], bop[nt], acc[nt][mt]);
+              for (int nt = 0; nt < NT; ++nt)
+                // a tile's first products start from zero (no accumulator to clear)
+                acc[nt][mt] = mfma16(aop[ks][mt], bop[nt], s == 0 && ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nt][mt]);
           }
           // fp64 angle reductions for the next tile, one per step from step 1 on,
           // off the tail of the last stage
@@ -491,13 +486,14 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) tokA[nt] = tokB[nt];
             load_next_ids(tnn);
-            load_q(bh_n);
+            if constexpr (NR == 1) load_q(bh_n);
           }
           // Loads for later stages, issued after this step's products so that
           // a full memory pipeline stalls nothing the step needs.  (Past the
           // last tile they repeat the last tile: harmless, and they keep the
           // code branch-free.)
           __builtin_amdgcn_sched_barrier(0);
+          if (NR >= 2 && s == 0) load_q(bh_n);  // the next tile's queries, stored at its step 0
           if (s == NR - SL) bas = bas_of(tn.chead);  // from here on the loads are the next tile's
           if constexpr (SL > 0) stage_load(bas, (s + SL) % NR, sreg[(s + SL) % NR]);
           if constexpr (LG > 0) {
@@ -517,77 +513,90 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     for (int s = 0; s < NS; ++s) __syncthreads();  // the consumers' last tile
   } else {
     // ===================================================================== consumer
-    // Software-pipelined by one value stage: step c runs GELU and PH of
-    // stage c - 1 (VALU work that overlaps the producer's reconstruction
-    // MFMAs and this wave's own next products) and then MLP1 of stage c.
-    // The last stage of a tile finishes at step 0 of the next tile-step (or
-    // after the loop).  Accordingly W1 of stage c is stored at the end of
-    // step c - 1 and read at step c, in a ring of two buffers.
-    // W1 of one cache head through a descriptor carried across tiles, moved
-    // to the next tile's head at the step whose loads start reading it (NS - 2)
-    auto w1_of = [&](int chead) { return buffer_rsrc(a.w1 + (size_t)chead * kHidden * kHeadDim, kHidden * kHeadDim * 2); };
-    // stage c: W1 rows [32 c, 32 c + 32) in pi order (8 KiB of a ring buffer)
-    const int w1row = rt >> 4, w1p = rt & 15;
-    const uint32_t w1_goff = (uint32_t)(((8 * ((w1row >> 2) & 3) + (w1row & 3)) * kHeadDim + 8 * w1p) * 2);
-    const int w1_loff = w1row * 256 + (w1p ^ (w1row & 15)) * 16;
-    auto w1_load = [&](__amdgpu_buffer_rsrc_t w1r, int c, u32x4 (&r)[2]) {
+    // Consumer w owns hidden units [64 w, 64 w + 64) of every token of the
+    // tile (all four slots), with its W1 rows and b1 in registers, reloaded
+    // when the head changes.  Step c of a tile-step runs the first MLP layer
+    // of the tile's 16-token piece c (slot c / 2, half c % 2, from the K_pre
+    // operands the producers handed over) and the GELU of piece c - 1; each
+    // pair of pieces (one slot's 32 tokens) then meets that slot's softmax
+    // weights in the PH product.  The last piece of a tile finishes at step 0
+    // of the next tile-step (or after the loop).
+    //
+    // The slots' weights are relative to each slot's running maximum m_s
+    // (its producer's).  A consumer puts them on one scale per tile,
+    // M = max_s m_s, by multiplying slot s's weights by exp2(m_s - M), and
+    // rescales its PH accumulator by exp2(M_old - M) (or clears it when a
+    // group starts).  A group's PH is thus relative to the largest of its
+    // slots' final maxima, and the merge weights it by the largest of the
+    // slots' weights.
+    //
+    // Consumer w also takes slot w's residual rows (with slot w's weights and
+    // running maximum, as the producer keeps them): loaded over steps 1-4,
+    // stored a step later into slot w's residual region of LDS, then
+    // R share += R^T x p^T at step 7.
+    const int hq0 = 64 * slot;  // this wave's first hidden unit
+    // W1 rows hq0 + 16 hn + col as MLP1 B operands (k = d = 32 ks + 8 grp .. + 7), and b1 of those units
+    bf16x8 w1op[4][4];
+    float b1v[4];
+    auto load_w1 = [&](int chead) {
+      const uint16_t* w = a.w1 + ((size_t)chead * kHidden + hq0 + col) * kHeadDim + 8 * grp;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) r[u] = buffer_ld16(w1r, w1_goff, (32 * c + 4 * u) * kHeadDim * 2);
+      for (int hn = 0; hn < 4; ++hn)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) w1op[ks][hn] = load_bf16x8(w + 16 * hn * kHeadDim + 32 * ks);
+      const uint16_t* bb = a.b1 + (size_t)chead * kHidden + hq0 + col;
+#pragma unroll
+      for (int hn = 0; hn < 4; ++hn) b1v[hn] = bf16_to_f32(bb[16 * hn]);
     };
-    auto w1_store = [&](int buf, const u32x4 (&r)[2]) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(L.mring[buf] + w1_loff + 4096 * u) = r[u];
-    };
-    // W1 position row 16 hn + col, piece 4 ks + grp
-    int rw1[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) rw1[s] = col * 256 + ((4 * s + grp) ^ col) * 16;
-
-    u32x4 w1reg[NS][2];
-    __amdgpu_buffer_rsrc_t w1r;
-    {
-      const int chead0 = pipe_first(a, wg).chead;
-      w1r = w1_of(chead0);
-      w1_load(w1r, 0, w1reg[0]);
-      w1_load(w1r, 1, w1reg[1]);
-    }
-    w1_store(0, w1reg[0]);
+    PipeCur tc = pipe_first(a, wg), tp = tc;  // this tile and the one before
+    PipeCur tn = pipe_next(a, tc);
+    load_w1(tc.chead);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < NS; ++s) __syncthreads();  // the producers' first tile
 
-    // The value section without W2: over a group, this slot accumulates
-    //   PH[h][j] = sum_t p_t[j] gelu(W1 K_pre[t] + b1)[h]
-    // (rescaled by alpha per tile, like any running-softmax accumulator);
-    // the merge kernel applies W2 once per (sequence, KV head) to the
-    // weighted sum of the groups' PH.  racc holds the residual rows' share,
-    // sum_t p_t R_t, in the output space.
-    f32x4 racc[8];
+    f32x4 racc[8];   // slot w's residual share (+ nothing else), output space, scale m_w
+    f32x4 phacc[4];  // PH of units hq0 + 16 hn + 4 grp + e, query col, scale M
 #pragma unroll
     for (int nd = 0; nd < 8; ++nd) racc[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // PH of stage cs (hidden positions 16 hn + 4 grp + e of the stage) in phacc[cs][hn]
-    f32x4 phacc[NS][2];
 #pragma unroll
-    for (int cs = 0; cs < NS; ++cs)
+    for (int hn = 0; hn < 4; ++hn) phacc[hn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 hacc[2][4];  // MLP1 of piece c in hacc[c & 1]
+    h2 glo[4][2];      // GELU of the first piece of a pair
+    f16x8 pq[4];       // each slot's weights of the tile being finished, on the scale M
+    bf16x8 pab;        // slot w's weights, own scale (the residual product)
+    float m_run = -__builtin_huge_valf();  // M after the current tile (query col)
+    float m_w = 0.f, l_w = 0.f;            // slot w's running (m, l) after the current tile
+
+    // GELU of piece pc (MLP1 result in hacc[pc & 1]); the second piece of a
+    // pair completes PH of slot pc / 2:  D[h][j] += gelu^T[h][t] x p^T[t][j]
+    auto finish_piece = [&](int pc) {
+      h2 x[8];
 #pragma unroll
-      for (int hn = 0; hn < 2; ++hn) phacc[cs][hn] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 hacc[2][NT][2];  // MLP1 of stage c in hacc[c & 1] (before GELU)
-    f16x8 pa;              // softmax weights of the current tile (fp16: the PH product)
-    // GELU and PH of stage cs (MLP1 result in hacc[cs & 1]), softmax weights pw:
-    //   PH  D[h][j] += gelu(hid)^T[h][t] x p^T[t][j]
-    auto finish_stage = [&](int cs, const f16x8& pw) {
-      const f32x4 lo[2] = {hacc[cs & 1][0][0], hacc[cs & 1][0][1]};
-      const f32x4 hi[2] = {hacc[cs & 1][1][0], hacc[cs & 1][1][1]};
-      f16x8 gl[2];
-      gelu16_h(lo, hi, gl);
+      for (int hn = 0; hn < 4; ++hn) {
+        x[2 * hn] = __builtin_convertvector(f32x2{hacc[pc & 1][hn][0], hacc[pc & 1][hn][1]}, h2);
+        x[2 * hn + 1] = __builtin_convertvector(f32x2{hacc[pc & 1][hn][2], hacc[pc & 1][hn][3]}, h2);
+      }
+      gelu_h2x8(x);
+      if ((pc & 1) == 0) {
 #pragma unroll
-      for (int hn = 0; hn < 2; ++hn) phacc[cs][hn] = mfma16h(gl[hn], pw, phacc[cs][hn]);
+        for (int hn = 0; hn < 4; ++hn) {
+          glo[hn][0] = x[2 * hn];
+          glo[hn][1] = x[2 * hn + 1];
+        }
+      } else {
+#pragma unroll
+        for (int hn = 0; hn < 4; ++hn) {
+          const f16x8 a8 = __builtin_shufflevector(__builtin_shufflevector(glo[hn][0], glo[hn][1], 0, 1, 2, 3),
+                                                   __builtin_shufflevector(x[2 * hn], x[2 * hn + 1], 0, 1, 2, 3),
+                                                   0, 1, 2, 3, 4, 5, 6, 7);
+          phacc[hn] = mfma16h(a8, pq[pc >> 1], phacc[hn]);
+        }
+      }
     };
-    // group t's partials: slot 4 gx + slot of its head bh.  The output-space
-    // record (m, l, R share + b2 l) with (m, l) from the producer and b2 of
-    // the head from LDS (parity par), and the slot's PH row of each query
-    // head in hidden-unit order: position 16 hn + 4 grp + e of stage cs is
-    // unit 32 cs + 8 grp + 4 hn + e (the pi order of the W1 rows).
+    // group t's partials: slot w's output-space record (m_w, l_w, R share +
+    // b2 l_w; b2 of the head from LDS, parity par) at slot 4 gx + w, and this
+    // wave's quarter of the group's PH (units hq0 ..) in PH row 4 gx
     auto write_part = [&](const PipeCur& t, float m, float l, int par) {
       if (col >= g) return;
       const size_t sl = (size_t)t.bh * a.n_split + kPipeSlots * t.gx + slot;
@@ -603,104 +612,99 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
           const int d = 16 * nd + 4 * grp + e;
           pp[2 + d] = fmaf(L.b2f[par][d], l, racc[nd][e]);
         }
-      float* ph = a.ph + (((size_t)t.bh * a.n_ph + kPipeSlots * t.gx + slot) * g + col) * kHidden;
+      float* ph = a.ph + (((size_t)t.bh * a.n_ph + kPipeSlots * t.gx) * g + col) * kHidden + hq0 + 4 * grp;
 #pragma unroll
-      for (int cs = 0; cs < NS; ++cs)
-#pragma unroll
-        for (int hn = 0; hn < 2; ++hn) *reinterpret_cast<f32x4*>(ph + 32 * cs + 8 * grp + 4 * hn) = phacc[cs][hn];
+      for (int hn = 0; hn < 4; ++hn) *reinterpret_cast<f32x4*>(ph + 16 * hn) = phacc[hn];
     };
+    // slot w's value among four wave-uniform ones (no indexed register array)
+    auto of_slot = [&](auto v0, auto v1, auto v2, auto v3) { return slot == 0 ? v0 : slot == 1 ? v1 : slot == 2 ? v2 : v3; };
     constexpr int RL = RI4 ? 2 : 8;  // 16-byte residual pieces per lane
-    float m_cur = 0.f, l_cur = 0.f;    // the producer's (m, l) after the tile being consumed
-    PipeCur tc = pipe_first(a, wg), tp = tc;  // this tile and the one before
-    PipeCur tn = pipe_next(a, tc);
     for (int i = 0; i < ntiles; ++i) {
       const int chead_c = tc.chead;
-      // the previous tile ended its group
-      const bool prev_end = i > 0 && tp.lt + 1 == tp.gend;
-      unsigned char* hb = L.hand[i & 1][slot];
-      bf16x8 kpre_b[NT][4];
-      bf16x8 pab;  // the softmax weights in bf16 (the residual product)
+      const bool prev_end = i > 0 && tp.lt + 1 == tp.gend;   // the previous tile ended its group
+      const bool new_grp = tc.lt == tc.gx * a.pipe_tpw;      // this tile starts one
+      const unsigned char* hk = L.hand[i & 1][0];            // this tile's hand-off
+      unsigned char* hr = L.rrow[slot];                      // slot w's residual rows
       u32x4 rres[RL];
       u32x2 rsc = {0u, 0u};
 #pragma unroll
       for (int c = 0; c < NS; ++c) {
-        // ---- LDS operands first: MLP1 of stage c, and at a tile start the handoff
-        bf16x8 w1op[4][2];
-        f32x4 b1v[2];
+        // ---- LDS operands first: K_pre of piece c, and at a tile start the
+        //      slots' running softmax state and weights
+        bf16x8 ka[4];
         {
-          const unsigned char* sb = L.mring[c & 1];
+          const unsigned char* hp = hk + (c >> 1) * kHandSlot + (c & 1) * 4096;
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int hn = 0; hn < 2; ++hn) w1op[ks][hn] = lds16(sb, rw1[ks] + 4096 * hn);
-#pragma unroll
-          for (int hn = 0; hn < 2; ++hn) b1v[hn] = L.b1q[i & 1][32 * c + 16 * hn + col];
+          for (int ks = 0; ks < 4; ++ks) ka[ks] = lds16(hp, ks * 1024 + lane * 16);
         }
-        f16x8 pnew;
-        float alpha = 1.f;
-        float m_prev = 0.f, l_prev = 0.f;
+        f32x4 sm[4];
+        f16x8 praw[4];
         if (c == 0) {
-          m_prev = m_cur;
-          l_prev = l_cur;
-          const f32x4 sm = L.sm[i & 1][slot][col];
-          m_cur = sm[1];
-          l_cur = sm[2];
-          alpha = sm[0];
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-              kpre_b[nt][ks] = lds16(hb, (nt * 4 + ks) * 1024 + lane * 16);
-          pnew = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(hb + kHandP + lane * 16));
+          for (int s2 = 0; s2 < 4; ++s2) {
+            sm[s2] = L.sm[i & 1][s2][col];
+            praw[s2] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(hk + s2 * kHandSlot + kHandP + lane * 16));
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
-        // ---- MLP1 of stage c: D[t][h] = K_pre[t][d] x W1^T[d][h] (b1 initial value),
-        //      hidden units [32 c, 32 c + 32); its matrix work runs under the GELU below
+        // ---- the previous piece (its products finished during the previous
+        //      step; at a tile start: the previous tile's last piece with that
+        //      tile's weights), under the K_pre reads; then at a tile start
+        //      the rescale
+        if (c > 0 || i > 0) finish_piece((c + NS - 1) % NS);
+        if (c == 0) {
+          if (prev_end) write_part(tp, m_w, l_w, (i - 1) & 1);
+          float mnew = -__builtin_huge_valf();
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) mnew = fmaxf(mnew, sm[s2][1]);
+          const float fac = new_grp || m_run == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
+#pragma unroll
+          for (int hn = 0; hn < 4; ++hn) phacc[hn] *= fac;
+          m_run = mnew;
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) {
+            const float f = sm[s2][1] == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(sm[s2][1] - mnew);
+            const _Float16 fh = (_Float16)f;
+            pq[s2] = praw[s2] * f16x8{fh, fh, fh, fh, fh, fh, fh, fh};
+          }
+          const f32x4 smw = of_slot(sm[0], sm[1], sm[2], sm[3]);
+          const f16x8 pw = of_slot(praw[0], praw[1], praw[2], praw[3]);
+          m_w = smw[1];
+          l_w = smw[2];
+#pragma unroll
+          for (int nd = 0; nd < 8; ++nd) racc[nd] *= smw[0];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pab[e] = (__bf16)(float)pw[e];
+        }
+        // ---- MLP1 of piece c: D[t][h] = K_pre[t][d] x W1^T[d][h] (b1 initial value)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int hn = 0; hn < 2; ++hn)
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-              hacc[c & 1][tt][hn] = mfma16(kpre_b[tt][ks], w1op[ks][hn], ks == 0 ? b1v[hn] : hacc[c & 1][tt][hn]);
-        // ---- the previous stage: GELU, PH (at a tile start: the previous
-        //      tile's last stage with that tile's weights, then the rescale)
-        if (c > 0 || i > 0) finish_stage((c + NS - 1) % NS, pa);
-        if (c == 0) {
-          if (prev_end) write_part(tp, m_prev, l_prev, (i - 1) & 1);
-          pa = pnew;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pab[e] = (__bf16)(float)pa[e];
-#pragma unroll
-          for (int nd = 0; nd < 8; ++nd) racc[nd] *= alpha;
-#pragma unroll
-          for (int cs = 0; cs < NS; ++cs)
-#pragma unroll
-            for (int hn = 0; hn < 2; ++hn) phacc[cs][hn] *= alpha;
-        }
+          for (int hn = 0; hn < 4; ++hn)
+            hacc[c & 1][hn] = mfma16(ka[ks], w1op[ks][hn],
+                                     ks == 0 ? f32x4{b1v[hn], b1v[hn], b1v[hn], b1v[hn]} : hacc[c & 1][hn]);
 
         if (c == NS - 1) {
-          // ---- residuals: the rows are in this slot's handoff region (stored
-          //      at steps 3-6); R share += R^T[d][t] x p^T[t][j]
+          // ---- residuals (at the last step, where the producers' tail is the
+          //      longer part): the rows are in slot w's region (stored at steps
+          //      2-5); R share += R^T[d][t] x p^T[t][j]
+          asm volatile("" ::: "memory");  // the reads below take bytes written under other types
           if constexpr (!RI4) {
-            // the reads below take bytes written under another type
-            asm volatile("" ::: "memory");
 #pragma unroll
             for (int nd = 0; nd < 8; ++nd) {
               bf16x8 rop;
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
                 const int t = e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4;
-                rop[e] = *reinterpret_cast<const __bf16*>(hb + t * kResRow + (16 * nd + col) * 2);
+                rop[e] = *reinterpret_cast<const __bf16*>(hr + t * kResRow + (16 * nd + col) * 2);
               }
               racc[nd] = mfma16(rop, pab, racc[nd]);
             }
           } else {
-            asm volatile("" ::: "memory");  // the reads below take bytes written under other types
             auto resid_at = [&](int t, int d) -> float {
-              const uint32_t byte = hb[t * kResRow4 + (d >> 1)];
+              const uint32_t byte = hr[t * kResRow4 + (d >> 1)];
               const int code = static_cast<int>(((byte >> (4 * (d & 1))) & 0xFu) ^ 8u) - 8;
-              const uint16_t sc = *reinterpret_cast<const uint16_t*>(hb + t * kResRow4 + 64 + (d >> 5) * 2);
+              const uint16_t sc = *reinterpret_cast<const uint16_t*>(hr + t * kResRow4 + 64 + (d >> 5) * 2);
               return static_cast<float>(code) * f16_to_f32(sc);
             };
 #pragma unroll
@@ -715,16 +719,13 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
             }
           }
         }
-        // Loads for later steps after this step's work (see the producer):
-        // the same weights every tile, W1 two stages ahead, and the tile's
-        // residual rows for step NS - 1
+        // ---- loads for later steps, after this step's work: at the last
+        //      piece of a head's last tile the next head's W1 (used from the
+        //      next step on); slot w's residual rows over steps 1-4
         __builtin_amdgcn_sched_barrier(0);
-        if (c == NS - 2) w1r = w1_of(tn.chead);  // from here on the loads are the next tile's
-        w1_load(w1r, (c + 2) % NS, w1reg[(c + 2) % NS]);
-        if (c >= 2 && c <= 5) {
-          // this slot's residual rows, spread over steps 2-5 (zeros where a
-          // token has none: reads past the end of the buffer return 0);
-          // descriptors from the producer
+        if (c == NS - 1 && tn.chead != chead_c) load_w1(tn.chead);
+        if (c >= 1 && c <= 4) {
+          // zeros where a token has none: reads past the end of the buffer return 0
           auto row_of = [&](uint32_t dsc, int t) -> int {
             const int bit = t & 7;
             if (!((dsc >> bit) & 1u)) return -1;
@@ -735,7 +736,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
             const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(
                 static_cast<const uint16_t*>(a.res_val) + (size_t)chead_c * a.n_resid * kHeadDim, nbytes);
 #pragma unroll
-            for (int u = 2 * (c - 2); u < 2 * (c - 1); ++u) {
+            for (int u = 2 * (c - 1); u < 2 * c; ++u) {
               const int t = 4 * u + (lane >> 4);
               const int rn = row_of(L.rdesc[i & 1][slot][u >> 1], t);
               rres[u] = buffer_ld16(rv, rn >= 0 ? (uint32_t)rn * 256 + (lane & 15) * 16 : nbytes, 0);
@@ -747,33 +748,30 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
                 static_cast<const uint8_t*>(a.res_val) + (size_t)chead_c * a.n_resid * (kHeadDim / 2), nbytes);
             const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
                 a.res_scale + (size_t)chead_c * a.n_resid * (kHeadDim / 32), sbytes);
-            if (c - 1 <= RL) {
-              const int u = c - 2;
+            if (c <= RL) {
+              const int u = c - 1;
               const int t = 16 * u + (lane >> 2);
               const int rn = row_of(L.rdesc[i & 1][slot][2 * u + (lane >> 5)], t);
               rres[u] = buffer_ld16(rv, rn >= 0 ? (uint32_t)rn * 64 + (lane & 3) * 16 : nbytes, 0);
-            } else if (c == RL + 2) {
+            } else if (c == RL + 1) {
               const int t = lane & 31;
               const int rn = row_of(L.rdesc[i & 1][slot][t >> 3], t);
               rsc = __builtin_amdgcn_raw_buffer_load_b64(rs, rn >= 0 ? (uint32_t)rn * 8 : sbytes, 0, 0);
             }
           }
         }
-        // W1 of stage c + 1 into the buffer step c - 1 read
-        w1_store((c + 1) & 1, w1reg[(c + 1) % NS]);
-        // the residual rows loaded a step ago -> this slot's handoff region
-        // (read at step 0, free until the tile after next), so that no row
-        // is held in registers for longer than a step
+        // the residual rows loaded a step ago -> slot w's region, so that no
+        // row is held in registers for longer than a step
         if constexpr (!RI4) {
-          if (c >= 3 && c <= 6) {
+          if (c >= 2 && c <= 5) {
 #pragma unroll
-            for (int u = 2 * (c - 3); u < 2 * (c - 2); ++u)
-              *reinterpret_cast<u32x4*>(hb + (4 * u + (lane >> 4)) * kResRow + (lane & 15) * 16) = rres[u];
+            for (int u = 2 * (c - 2); u < 2 * (c - 1); ++u)
+              *reinterpret_cast<u32x4*>(hr + (4 * u + (lane >> 4)) * kResRow + (lane & 15) * 16) = rres[u];
           }
         } else {
-          if (c >= 3 && c - 3 < RL)
-            *reinterpret_cast<u32x4*>(hb + (16 * (c - 3) + (lane >> 2)) * kResRow4 + (lane & 3) * 16) = rres[c - 3];
-          if (c == RL + 3 && lane < 32) *reinterpret_cast<u32x2*>(hb + lane * kResRow4 + 64) = rsc;
+          if (c >= 2 && c - 2 < RL)
+            *reinterpret_cast<u32x4*>(hr + (16 * (c - 2) + (lane >> 2)) * kResRow4 + (lane & 3) * 16) = rres[c - 2];
+          if (c == RL + 2 && lane < 32) *reinterpret_cast<u32x2*>(hr + lane * kResRow4 + 64) = rsc;
         }
         __syncthreads();
       }
@@ -781,9 +779,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
       tc = tn;
       tn = pipe_next(a, tn);
     }
-    // the last tile's last stage, and the partials of the last group
-    finish_stage(NS - 1, pa);
-    write_part(tp, m_cur, l_cur, (ntiles - 1) & 1);
+    // the last tile's last piece, and the partials of the last group
+    finish_piece(NS - 1);
+    write_part(tp, m_w, l_w, (ntiles - 1) & 1);
   }
 }
 

@@ -56,7 +56,7 @@ struct AttendArgs {
   const int32_t* sel;
   float* part;
   // producer/consumer kernel: PH rows [head][n_ph][g][kHidden] beside the
-  // output-space partials of its slots (slot s of a head at row s)
+  // output-space partials of its slots (group gx of a head at row 4 gx)
   float* ph;
   int n_ph;
   float* kpre_out;
@@ -106,9 +106,10 @@ size_t split_select_ws_bytes(int n_lists, int n);
 hipError_t launch_select_split(const uint32_t* keys, int32_t* sel, int n_lists, int n, int k, void* ws,
                                hipStream_t st, int sel_stride = -1, float* thresh = nullptr);
 // Merge of the split partials of every (sequence, KV head, query head).  With
-// ph: its first n_ph_used slots also have PH rows (ph [head][ph_stride][g][kHidden]),
-// to which W2 of the head (w2 [cache head][d][kHidden], cache head =
-// sequence * cache_bmul * hkv + KV head) is applied.
+// ph: its first n_ph_used slots form groups of 4, each with one PH row (row
+// 4 gx of ph [head][ph_stride][g][kHidden], relative to the largest of the
+// group's slot maxima), to which W2 of the head (w2 [cache head][d][kHidden],
+// cache head = sequence * cache_bmul * hkv + KV head) is applied.
 struct MergePH {
   const float* ph = nullptr;
   int n_ph_used = 0, ph_stride = 0, cache_bmul = 1;

@@ -110,6 +110,9 @@ VARIANTS = {
     # chunks), biases on
     "multitile_b8": synth.C0.with_(name="multitile_b8", batch=8, n_heads_q=32, n_heads_kv=8, rank=128,
                                    topk=250, bias_std=0.1),
+    # the same at rank 512, where the kernel keeps three basis stages in LDS
+    "multitile_r512": synth.C0.with_(name="multitile_r512", batch=8, n_heads_q=32, n_heads_kv=8, rank=512,
+                                     topk=250, bias_std=0.1),
     # the same with int4 coefficients and residuals and eviction (13 tiles per
     # head: groups of unequal length)
     "multitile_int4_evict": synth.C4.with_(name="multitile_int4_evict", batch=8, ctx=4096, window=64, n_layers=4,
@@ -117,7 +120,7 @@ VARIANTS = {
 }
 
 
-@pytest.mark.parametrize("name", ["multitile_b8", "multitile_int4_evict"])
+@pytest.mark.parametrize("name", ["multitile_b8", "multitile_r512", "multitile_int4_evict"])
 def test_multitile_cases_plan_several_tiles(name):
     cfg = VARIANTS[name]
     n_tiles = -(-min(cfg.topk, cfg.n_cand) // 16)
@@ -133,7 +136,7 @@ def test_multitile_cases_plan_several_tiles(name):
 PIPE_CUS = (1, 7, 100)
 
 
-@pytest.mark.parametrize("name", ["multitile_b8", "multitile_int4_evict"])
+@pytest.mark.parametrize("name", ["multitile_b8", "multitile_r512", "multitile_int4_evict"])
 def test_pipe_long_ranges(name):
     """The producer/consumer kernel planned for few CUs: each workgroup runs
     many groups of different heads in one pipeline (head changes at group
