@@ -383,20 +383,37 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) aop[ks][mt] = lds16(sb, ra[ks][mt & 1] + 2048 * mt);
           __builtin_amdgcn_sched_barrier(0);
+          if (s < NR - 1) {
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 bop[NT];
+            for (int ks = 0; ks < 2; ++ks) {
+              bf16x8 bop[NT];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-              if constexpr (!CI4) bop[nt] = cv[s][ks][nt];
-              else bop[nt] = dequant8(cq[s][nt][ks], csc[s][nt]);
+              for (int nt = 0; nt < NT; ++nt) {
+                if constexpr (!CI4) bop[nt] = cv[s][ks][nt];
+                else bop[nt] = dequant8(cq[s][nt][ks], csc[s][nt]);
+              }
+#pragma unroll
+              for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                  // a tile's first products start from zero (no accumulator to clear)
+                  acc[nt][mt] = mfma16(aop[ks][mt], bop[nt], s == 0 && ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nt][mt]);
             }
+          } else {
+            // the last stage one 16-token half at a time, so that the first
+            // half's RoPE can run on the vector ALUs under the second half's
+            // products
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-              for (int nt = 0; nt < NT; ++nt)
-                // a tile's first products start from zero (no accumulator to clear)
-                acc[nt][mt] = mfma16(aop[ks][mt], bop[nt], s == 0 && ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nt][mt]);
+              for (int ks = 0; ks < 2; ++ks) {
+                bf16x8 bop;
+                if constexpr (!CI4) bop = cv[s][ks][nt];
+                else bop = dequant8(cq[s][nt][ks], csc[s][nt]);
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt)
+                  acc[nt][mt] = mfma16(aop[ks][mt], bop, s == 0 && ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nt][mt]);
+              }
           }
           // fp64 angle reductions for the next tile, one per step from step 1 on,
           // off the tail of the last stage
