@@ -62,6 +62,12 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
+// 16-byte load with the non-temporal (streaming) cache policy: for data read
+// once, whose 128-byte lines are consumed whole by neighbouring loads.
+__device__ __forceinline__ u32x4 load_nt16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 }

@@ -29,7 +29,7 @@ namespace lowram {
 // Each wave keeps 4 groups of 16 landmarks (16 KiB) in flight per iteration.
 // ---------------------------------------------------------------------------
 #ifndef LOWRAM_SCORE_WG_PER_CU
-#define LOWRAM_SCORE_WG_PER_CU 1
+#define LOWRAM_SCORE_WG_PER_CU 2
 #endif
 __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ landmark,
