@@ -724,10 +724,41 @@ def bench_shared(args, cfg, nq, n_layers):
 
 def bench_peaks(args):
     """What the chip reaches on plain work, beside the published peaks: a
-    device-to-device copy of 4 GiB (HBM read + write bytes / time) and an
-    8192^3 bf16 matrix product through torch (hipBLASLt; 2 n^3 flops / time)."""
+    device-to-device copy of 4 GiB (HBM read + write bytes / time), a
+    streaming read of 8 GiB and a register-only MFMA loop (libpeaks.so), and
+    an 8192^3 bf16 matrix product through torch (hipBLASLt; 2 n^3 flops / time)."""
+    import ctypes
+
     import torch
+    from long_context_decode_landmark_amd import build as lbuild
     dev = torch.device("cuda:0")
+    if not os.path.exists(lbuild.PEAKS_LIB):
+        raise RuntimeError(f"{lbuild.PEAKS_LIB} is not built: run __graft_entry__.build()")
+    P = ctypes.CDLL(lbuild.PEAKS_LIB)
+    P.peaks_read_gbs.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.POINTER(ctypes.c_double)]
+    P.peaks_mfma_tfs.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
+    rd_bytes = 8 << 30
+    rbuf = torch.ones(rd_bytes, dtype=torch.uint8, device=dev)
+    scratch = torch.empty(65536 * 256, dtype=torch.float32, device=dev)
+    read = {}
+    for n_wg in (2048, 8192):
+        v = ctypes.c_double(0.0)
+        rc = P.peaks_read_gbs(ctypes.c_void_p(rbuf.data_ptr()), rd_bytes, n_wg,
+                              ctypes.c_void_p(scratch.data_ptr()), ctypes.byref(v))
+        if rc != 0:
+            raise RuntimeError(f"peaks_read_gbs failed ({rc})")
+        read[n_wg] = v.value
+    del rbuf
+    torch.cuda.empty_cache()
+    mf = {}
+    for n_wg in (1024, 4096):
+        v = ctypes.c_double(0.0)
+        rc = P.peaks_mfma_tfs(n_wg, 20000, ctypes.c_void_p(scratch.data_ptr()), ctypes.byref(v))
+        if rc != 0:
+            raise RuntimeError(f"peaks_mfma_tfs failed ({rc})")
+        mf[n_wg] = v.value
+    del scratch
     n = 4 << 30
     src = torch.ones(n, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -763,6 +794,12 @@ def bench_peaks(args):
         "metric": "achievable peaks on this MI355X", "n_gpus": 1, "steps": reps,
         "copy": {"GB/s": round(copy_gbs, 1), "frac_of_8TB/s": round(copy_gbs / HBM_PEAK_GBS, 4),
                  "what": "device-to-device copy of 4 GiB, read + write bytes"},
+        "read": {"GB/s": round(max(read.values()), 1), "frac_of_8TB/s": round(max(read.values()) / HBM_PEAK_GBS, 4),
+                 "by_workgroups": {str(k): round(v, 1) for k, v in read.items()},
+                 "what": "8 GiB streamed once with 16-byte non-temporal loads, contiguous per workgroup"},
+        "mfma_loop": {"TFLOP/s": round(max(mf.values()), 1), "frac_of_2.5PF": round(max(mf.values()) / MFMA_BF16_PEAK_TFS, 4),
+                      "by_workgroups": {str(k): round(v, 1) for k, v in mf.items()},
+                      "what": "v_mfma_f32_16x16x32_bf16 on registers, 8 independent chains per wave, 4 waves per workgroup"},
         "bf16_gemm": {"TFLOP/s": round(mm_tfs, 1), "frac_of_2.5PF": round(mm_tfs / MFMA_BF16_PEAK_TFS, 4),
                       "what": "torch.mm bf16 8192 x 8192 x 8192 (hipBLASLt)"},
     }))

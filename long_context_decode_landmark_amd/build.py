@@ -16,6 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblowram.so")
 BUILD = os.path.join(HERE, "_build")
+PEAKS_SRC = os.path.join(HERE, "peaks")
+PEAKS_LIB = os.path.join(HERE, "libpeaks.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -33,7 +35,22 @@ def _compile(src: str) -> str:
     return obj
 
 
+def build_peaks(verbose: bool = False) -> str:
+    """libpeaks.so: the benchmark's achievable-peak probes (streaming read,
+    MFMA loop), kept out of the decode library."""
+    src = os.path.join(PEAKS_SRC, "peaks.hip")
+    tmp = PEAKS_LIB + ".tmp"
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", "-o", tmp, src], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    os.replace(tmp, PEAKS_LIB)
+    if verbose:
+        print("built", PEAKS_LIB)
+    return PEAKS_LIB
+
+
 def build(verbose: bool = False) -> str:
+    build_peaks(verbose)
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:

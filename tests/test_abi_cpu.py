@@ -30,6 +30,21 @@ def test_library_loads_and_exports_every_symbol():
     assert native.strerror(-4) == "workspace too small"
 
 
+def test_peaks_library_loads_and_checks_its_arguments():
+    """The benchmark's peak probes live in their own library; argument errors
+    return before any HIP call."""
+    from long_context_decode_landmark_amd import build as lbuild
+    P = ctypes.CDLL(lbuild.PEAKS_LIB)
+    P.peaks_read_gbs.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.POINTER(ctypes.c_double)]
+    P.peaks_mfma_tfs.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
+    v = ctypes.c_double(1.0)
+    assert P.peaks_read_gbs(None, 1000, 4, None, ctypes.byref(v)) == -2  # not a multiple of n_wg * 32 KiB
+    assert P.peaks_read_gbs(None, 1 << 20, 0, None, ctypes.byref(v)) == -2
+    assert P.peaks_mfma_tfs(0, 10, None, ctypes.byref(v)) == -2
+    assert P.peaks_mfma_tfs(4, 0, None, ctypes.byref(v)) == -2
+
+
 def shape(**kw):
     import synth
     return native.make_shape(synth.C0, **kw)
