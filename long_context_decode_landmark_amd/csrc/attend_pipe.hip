@@ -548,9 +548,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     // slots' weights.
     //
     // Consumer w also takes slot w's residual rows (with slot w's weights and
-    // running maximum, as the producer keeps them): loaded over steps 1-4,
-    // stored a step later into slot w's residual region of LDS, then
-    // R share += R^T x p^T at step 7.
+    // running maximum, as the producer keeps them): loaded over steps 1-4
+    // (int4: steps 1-2, with each lane's group scale), stored a step later
+    // into slot w's residual region of LDS as bf16 rows (int4 rows dequantised
+    // on the way), then R share += R^T x p^T at step 7.
     const int hq0 = 64 * slot;  // this wave's first hidden unit
     // W1 rows hq0 + 16 hn + col as MLP1 B operands (k = d = 32 ks + 8 grp .. + 7), and b1 of those units
     bf16x8 w1op[4][4];
@@ -643,7 +644,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
       const unsigned char* hk = L.hand[i & 1][0];            // this tile's hand-off
       unsigned char* hr = L.rrow[slot];                      // slot w's residual rows
       u32x4 rres[RL];
-      u32x2 rsc = {0u, 0u};
+      uint16_t rsc[RI4 ? RL : 1];
 #pragma unroll
       for (int c = 0; c < NS; ++c) {
         // ---- LDS operands first: K_pre of piece c, and at a tile start the
@@ -703,37 +704,16 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 
         if (c == NS - 1) {
           // ---- residuals (at the last step, where the producers' tail is the
-          //      longer part): the rows are in slot w's region (stored at steps
-          //      2-5); R share += R^T[d][t] x p^T[t][j]
+          //      longer part): bf16 rows t of slot w's region (stored at steps
+          //      2-5); R share += R^T[d][t] x p^T[t][j].  The B operand (tokens
+          //      4 grp + 0..3 and 16 + 4 grp + 0..3 of column d = 16 nd + col)
+          //      comes from two transpose reads of the row-major rows.
           asm volatile("" ::: "memory");  // the reads below take bytes written under other types
-          if constexpr (!RI4) {
+          const int rb = (4 * grp + (col >> 2)) * kResRow + 8 * (col & 3);
 #pragma unroll
-            for (int nd = 0; nd < 8; ++nd) {
-              bf16x8 rop;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const int t = e < 4 ? 4 * grp + e : 16 + 4 * grp + e - 4;
-                rop[e] = *reinterpret_cast<const __bf16*>(hr + t * kResRow + (16 * nd + col) * 2);
-              }
-              racc[nd] = mfma16(rop, pab, racc[nd]);
-            }
-          } else {
-            auto resid_at = [&](int t, int d) -> float {
-              const uint32_t byte = hr[t * kResRow4 + (d >> 1)];
-              const int code = static_cast<int>(((byte >> (4 * (d & 1))) & 0xFu) ^ 8u) - 8;
-              const uint16_t sc = *reinterpret_cast<const uint16_t*>(hr + t * kResRow4 + 64 + (d >> 5) * 2);
-              return static_cast<float>(code) * f16_to_f32(sc);
-            };
-#pragma unroll
-            for (int nd = 0; nd < 8; ++nd) {
-              f32x4 lo, hi;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                lo[e] = resid_at(4 * grp + e, 16 * nd + col);
-                hi[e] = resid_at(16 + 4 * grp + e, 16 * nd + col);
-              }
-              racc[nd] = mfma16(pack8(lo, hi), pab, racc[nd]);
-            }
+          for (int nd = 0; nd < 8; ++nd) {
+            const bf16x8 rop = bf16x8_of(lds_tr16(hr, rb + 32 * nd), lds_tr16(hr, rb + 16 * kResRow + 32 * nd));
+            racc[nd] = mfma16(rop, pab, racc[nd]);
           }
         }
         // ---- loads for later steps, after this step's work: at the last
@@ -766,14 +746,12 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
             const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
                 a.res_scale + (size_t)chead_c * a.n_resid * (kHeadDim / 32), sbytes);
             if (c <= RL) {
+              // token 16 u + lane / 4: its 32 codes of group lane % 4, and that group's scale
               const int u = c - 1;
               const int t = 16 * u + (lane >> 2);
               const int rn = row_of(L.rdesc[i & 1][slot][2 * u + (lane >> 5)], t);
               rres[u] = buffer_ld16(rv, rn >= 0 ? (uint32_t)rn * 64 + (lane & 3) * 16 : nbytes, 0);
-            } else if (c == RL + 1) {
-              const int t = lane & 31;
-              const int rn = row_of(L.rdesc[i & 1][slot][t >> 3], t);
-              rsc = __builtin_amdgcn_raw_buffer_load_b64(rs, rn >= 0 ? (uint32_t)rn * 8 : sbytes, 0, 0);
+              rsc[u] = __builtin_amdgcn_raw_buffer_load_b16(rs, rn >= 0 ? (uint32_t)rn * 8 + (lane & 3) * 2 : sbytes, 0, 0);
             }
           }
         }
@@ -786,9 +764,15 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
               *reinterpret_cast<u32x4*>(hr + (4 * u + (lane >> 4)) * kResRow + (lane & 15) * 16) = rres[u];
           }
         } else {
-          if (c >= 2 && c - 2 < RL)
-            *reinterpret_cast<u32x4*>(hr + (16 * (c - 2) + (lane >> 2)) * kResRow4 + (lane & 3) * 16) = rres[c - 2];
-          if (c == RL + 2 && lane < 32) *reinterpret_cast<u32x2*>(hr + lane * kResRow4 + 64) = rsc;
+          // int4 rows are dequantised on the way: 32 bf16 values (64 bytes) of
+          // group lane % 4 of token 16 u + lane / 4, in the bf16 row layout
+          if (c >= 2 && c - 2 < RL) {
+            const int u = c - 2;
+            const float sc = f16_to_f32(rsc[u]);
+            unsigned char* dst = hr + (16 * u + (lane >> 2)) * kResRow + (lane & 3) * 64;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(dst + 16 * k) = __builtin_bit_cast(u32x4, dequant8(rres[u][k], sc));
+          }
         }
         __syncthreads();
       }

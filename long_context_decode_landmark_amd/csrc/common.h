@@ -68,6 +68,19 @@ __device__ __forceinline__ u32x4 load_nt16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// ds_read_b64_tr_b16 (gfx950): in each block of 16 lanes, lane i receives
+// element i % 4 of the 4-element (8-byte) row addressed by lane 4 j + i / 4 of
+// its block, as its element j (j = 0..3).  Two of them give a lane the eight
+// k values of an MFMA B operand from rows stored k-major (one row per k).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ s16x4 lds_tr16(const unsigned char* base, int off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + off));
+}
+__device__ __forceinline__ bf16x8 bf16x8_of(s16x4 lo, s16x4 hi) {
+  return __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 }

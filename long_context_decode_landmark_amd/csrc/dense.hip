@@ -16,9 +16,6 @@
 
 namespace lowram {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-
 constexpr int kDenseVBlock = kAttTokWave * kHeadDim * 2;  // bytes of one wave's V block in LDS
 
 // Byte offset in a wave's V block of byte `byte` of token row r: rows of
@@ -26,14 +23,6 @@ constexpr int kDenseVBlock = kAttTokWave * kHeadDim * 2;  // bytes of one wave's
 // one transpose read touches spread over all banks.
 __device__ __forceinline__ int dense_voff(int r, int byte) {
   return r * 256 + ((((byte >> 5) ^ (r & 7)) << 5) | (byte & 31));
-}
-
-// ds_read_b64_tr_b16: in each block of 16 lanes, lane i receives element i % 4
-// of the 4-element row addressed by lane 4 j + i / 4 of its block, as its
-// element j (j = 0..3).
-__device__ __forceinline__ s16x4 lds_tr16(const unsigned char* base, int off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(base + off));
 }
 
 __global__ __launch_bounds__(kAttWaves * 64) void dense_kernel(
@@ -150,7 +139,7 @@ __global__ __launch_bounds__(kAttWaves * 64) void dense_kernel(
       // from the transpose reads hh = 0, 1 (the same token order as pa)
       const s16x4 lo = lds_tr16(vb_lds, roff[0] ^ (nt << 5));
       const s16x4 hi = lds_tr16(vb_lds, roff[1] ^ (nt << 5));
-      const bf16x8 vbn = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      const bf16x8 vbn = bf16x8_of(lo, hi);
 #pragma unroll
       for (int e = 0; e < 4; ++e) oacc[nt][e] *= al[e];
       oacc[nt] = mfma16(pa, vbn, oacc[nt]);
