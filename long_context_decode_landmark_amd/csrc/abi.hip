@@ -129,7 +129,9 @@ struct AttendPlan {
 AttendPlan attend_plan(const lowram_shape* s, const Plan& p, bool stage_outputs, int n_cu, int mode) {
   // The producer/consumer kernel: one workgroup per CU working through
   // groups of tiles, 4 partial slots per group.  It pays off once every CU
-  // gets several tiles (its pipeline fills and drains once per workgroup);
+  // gets more than 2 tiles (its pipeline fills and drains once per workgroup,
+  // and its merge applies W2; at 2 tiles per CU the 4-wave kernel measured
+  // faster);
   // small problems, every call that asks for stage outputs, and shapes whose
   // partial slots would not fit the reserve or the merge run the 4-wave
   // kernel (one slot per tile).  A forced mode overrides the size rule only.
@@ -142,7 +144,7 @@ AttendPlan attend_plan(const lowram_shape* s, const Plan& p, bool stage_outputs,
   const long long all_tiles = (long long)heads * p.n_sel_tiles;
   const int pipe_split = kPipeSplitsPerGroup * a.n_grp + p.n_win_tiles;
   const bool fits = a.n_wg > 0 && pipe_split <= p.n_part && pipe_split <= kMergeMaxSplits;
-  a.pipe = has_prefix && !stage_outputs && fits && (mode == 0 ? all_tiles >= 2LL * n_cu : mode == 1);
+  a.pipe = has_prefix && !stage_outputs && fits && (mode == 0 ? all_tiles > 2LL * n_cu : mode == 1);
   a.sel_slots = !has_prefix ? 0 : a.pipe ? kPipeSplitsPerGroup * a.n_grp : p.n_sel_tiles;
   a.n_split = a.sel_slots + p.n_win_tiles;
   return a;

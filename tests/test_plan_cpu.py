@@ -49,8 +49,8 @@ def test_plan_matches_restatement(name, cfg, nb, n_cu):
     assert auto["reserved_slots"] == 2 * n + 6 + n_win
     for pl in (auto, pipe, wave):
         assert pl["partial_slots"] <= pl["reserved_slots"]
-    # automatic choice: the producer/consumer kernel once every CU gets two tiles
-    assert auto["kernel"] == (1 if heads * n >= 2 * n_cu else 2)
+    # automatic choice: the producer/consumer kernel once every CU gets more than two tiles
+    assert auto["kernel"] == (1 if heads * n > 2 * n_cu else 2)
     assert auto == (pipe if auto["kernel"] == 1 else wave)
 
 
