@@ -177,22 +177,32 @@ __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_multi_kerne
 // keys equal to T are still needed; an ordered compaction then keeps every
 // key > T and the first `need` keys == T in candidate order.  Candidates are
 // in ascending chunk order, so the output is ascending.  One workgroup of
-// 1024 threads per (sequence, KV head).  The keys of the head are staged in
-// LDS once (up to kSelLdsKeys of them; longer lists are re-read from L2 in
-// every pass).  12-bit first digits spread the fp32 exponent over 4096 bins
-// so few lanes of an LDS atomic hit the same bin; the digit search and the
-// compaction offsets use wave-shuffle scans with one LDS exchange.
+// 1024 threads per (sequence, KV head).
+//
+// Thread t owns the `per` consecutive candidates [per t, per t + per), per the
+// smallest power of two with 1024 per >= n_cand.  The keys of the head are
+// staged in LDS once (up to kSelLdsKeys of them; longer lists are re-read from
+// L2 in every pass), transposed: candidate per t + j at word j (1024 + 1) + t,
+// so that the 1024 threads reading their j-th keys touch consecutive words
+// (the extra word per row keeps the staging writes of one wave on different
+// banks).  12-bit first digits spread the fp32 exponent over 4096 bins so few
+// lanes of an LDS atomic hit the same bin; the digit search uses wave-shuffle
+// scans with one LDS exchange.  The compaction counts each thread's keys > T
+// and == T, takes one block-wide exclusive scan of the two counts, and has
+// every thread write its own selected candidates in order: no per-key ballot.
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelBins = 4096;
 constexpr int kSelLdsKeys = 32768;
+constexpr int kSelRow = kSelThreads + 1;          // LDS words per transposed key row
+constexpr int kSelLdsWords = (kSelLdsKeys / kSelThreads) * kSelRow;
 
 struct SelLds {  // the key array comes last: the L2-reading variant omits it
   uint32_t hist[kSelBins];
   uint32_t wsum[2][kSelWaves];
   uint32_t found[2];
-  alignas(16) uint32_t keys[kSelLdsKeys];
+  alignas(16) uint32_t keys[kSelLdsWords];
 };
 constexpr int kSelBatch = 8;  // loads a thread has in flight at once
 
@@ -202,6 +212,16 @@ __device__ __forceinline__ uint32_t wave_scan_down(uint32_t x, int lane) {
   for (int o = 1; o < 64; o <<= 1) {
     const uint32_t y = __shfl_down(x, o);
     if (lane + o < 64) x += y;
+  }
+  return x;
+}
+
+// inclusive scan of x over the 64 lanes of a wave, from lane 0 up
+__device__ __forceinline__ uint32_t wave_scan_up(uint32_t x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
   return x;
 }
@@ -232,35 +252,51 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
     return;
   }
+  int lp = 0;  // per = 2^lp candidates per thread
+  while (((long long)kSelThreads << lp) < n_cand) ++lp;
+  const int per = 1 << lp;
+  const int i_begin = tid << lp;                                  // this thread's first candidate
+  const int cnt = max(0, min(per, n_cand - i_begin));             // and how many it owns
   if constexpr (kLds) {
-    // Every load of a batch goes out before the first store waits on one
-    // (a plain copy loop kept one load per thread in flight): 16-byte pieces
-    // when the list is 16-byte aligned, single keys otherwise.  Indices past
-    // the end are clamped to the last element, which is then stored again
-    // with its own value: no branch for the compiler to sink a load into.
+    // Every load of a batch goes out before the first store waits on one:
+    // 16-byte pieces when the list is 16-byte aligned, single keys otherwise.
+    // Indices past the end are clamped to the last element, which is then
+    // stored again with its own value: no branch for the compiler to sink a
+    // load into.
+    auto put = [&](int i, uint32_t v) { S.keys[(i & (per - 1)) * kSelRow + (i >> lp)] = v; };
     if ((reinterpret_cast<uintptr_t>(kg) & 15) == 0 && n_cand >= 4) {
       const int n4 = n_cand >> 2;
       const uint4* kg4 = reinterpret_cast<const uint4*>(kg);
-      uint4* ks4 = reinterpret_cast<uint4*>(S.keys);
       for (int i0 = tid; i0 < n4; i0 += kSelThreads * kSelBatch) {
         uint4 v[kSelBatch];
 #pragma unroll
         for (int u = 0; u < kSelBatch; ++u) v[u] = kg4[min(i0 + u * kSelThreads, n4 - 1)];
 #pragma unroll
-        for (int u = 0; u < kSelBatch; ++u) ks4[min(i0 + u * kSelThreads, n4 - 1)] = v[u];
+        for (int u = 0; u < kSelBatch; ++u) {
+          const int i = 4 * min(i0 + u * kSelThreads, n4 - 1);
+          put(i, v[u].x);
+          put(i + 1, v[u].y);
+          put(i + 2, v[u].z);
+          put(i + 3, v[u].w);
+        }
       }
-      for (int i = 4 * n4 + tid; i < n_cand; i += kSelThreads) S.keys[i] = kg[i];
+      for (int i = 4 * n4 + tid; i < n_cand; i += kSelThreads) put(i, kg[i]);
     } else {
       for (int i0 = tid; i0 < n_cand; i0 += kSelThreads * kSelBatch) {
         uint32_t v[kSelBatch];
 #pragma unroll
         for (int u = 0; u < kSelBatch; ++u) v[u] = kg[min(i0 + u * kSelThreads, n_cand - 1)];
 #pragma unroll
-        for (int u = 0; u < kSelBatch; ++u) S.keys[min(i0 + u * kSelThreads, n_cand - 1)] = v[u];
+        for (int u = 0; u < kSelBatch; ++u) put(min(i0 + u * kSelThreads, n_cand - 1), v[u]);
       }
     }
+    __syncthreads();
   }
-  const uint32_t* kv = kLds ? S.keys : kg;
+  // key j of this thread (j < cnt)
+  auto key_of = [&](int j) -> uint32_t {
+    if constexpr (kLds) return S.keys[j * kSelRow + tid];
+    else return kg[i_begin + j];
+  };
 
   uint32_t prefix = 0, pmask = 0, kk = (uint32_t)k;
   constexpr int kShift[3] = {20, 8, 0};
@@ -271,14 +307,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint32_t dmask = (uint32_t)nbins - 1;
     for (int i = tid; i < nbins; i += kSelThreads) S.hist[i] = 0;
     __syncthreads();
-    for (int i0 = tid; i0 < n_cand; i0 += kSelThreads * kSelBatch) {
+    for (int j0 = 0; j0 < cnt; j0 += kSelBatch) {
       uint32_t kx[kSelBatch];  // a batch of reads before its atomics
 #pragma unroll
-      for (int u = 0; u < kSelBatch; ++u) kx[u] = kv[min(i0 + u * kSelThreads, n_cand - 1)];
+      for (int u = 0; u < kSelBatch; ++u) kx[u] = key_of(min(j0 + u, cnt - 1));
 #pragma unroll
       for (int u = 0; u < kSelBatch; ++u)
-        if (i0 + u * kSelThreads < n_cand && (kx[u] & pmask) == prefix)
-          atomicAdd(&S.hist[(kx[u] >> shift) & dmask], 1u);
+        if (j0 + u < cnt && (kx[u] & pmask) == prefix) atomicAdd(&S.hist[(kx[u] >> shift) & dmask], 1u);
     }
     __syncthreads();
     // thread t owns bins [bpt*t, bpt*t + bpt); the digit D is the bin where
@@ -308,62 +343,57 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     kk -= S.found[1];
     prefix |= digit << shift;
     pmask |= dmask << shift;
-    __syncthreads();  // hist is cleared by the next pass
+    __syncthreads();  // hist and wsum are reused next
   }
   const uint32_t T = prefix, need = kk;
 
-  // ordered compaction: wave w owns candidates [w*per, w*per + per) and walks
-  // them 64 at a time (lane-strided, conflict-free LDS reads); ballots give
-  // each key its rank among the wave's earlier > T / == T keys.
-  const int per = (n_cand + kSelWaves - 1) / kSelWaves;
-  const int w0 = min(n_cand, wave * per), w1 = min(n_cand, w0 + per);
-  const uint64_t below = (1ull << lane) - 1;  // lanes under this one
+  // ordered compaction: this thread's counts of keys > T and == T, their
+  // exclusive scans over the block in thread order, then this thread's
+  // selected candidates in order
   uint32_t ngt = 0, neq = 0;
-  // batches of kSelBatch x 64 keys, read before they are counted (the batch
-  // loop is uniform over the wave, so every ballot sees all 64 lanes)
-  for (int b0 = w0; b0 < w1; b0 += 64 * kSelBatch) {
+  for (int j0 = 0; j0 < cnt; j0 += kSelBatch) {
     uint32_t kx[kSelBatch];
 #pragma unroll
-    for (int u = 0; u < kSelBatch; ++u) kx[u] = kv[min(b0 + 64 * u + lane, n_cand - 1)];
+    for (int u = 0; u < kSelBatch; ++u) kx[u] = key_of(min(j0 + u, cnt - 1));
 #pragma unroll
     for (int u = 0; u < kSelBatch; ++u) {
-      const bool in = b0 + 64 * u + lane < w1;
-      ngt += __popcll(__ballot(in && kx[u] > T));
-      neq += __popcll(__ballot(in && kx[u] == T));
+      const bool in = j0 + u < cnt;
+      ngt += (in && kx[u] > T) ? 1u : 0u;
+      neq += (in && kx[u] == T) ? 1u : 0u;
     }
   }
-  if (lane == 0) {
-    S.wsum[0][wave] = ngt;
-    S.wsum[1][wave] = neq;
+  const uint32_t gt_incl = wave_scan_up(ngt, lane), eq_incl = wave_scan_up(neq, lane);
+  if (lane == 63) {
+    S.wsum[0][wave] = gt_incl;
+    S.wsum[1][wave] = eq_incl;
   }
   __syncthreads();
-  uint32_t gt_run = 0, eq_run = 0;
+  uint32_t gt_run = gt_incl - ngt, eq_run = eq_incl - neq;  // counts of the threads before this one
   for (int w = 0; w < wave; ++w) {
     gt_run += S.wsum[0][w];
     eq_run += S.wsum[1][w];
   }
-  for (int b0 = w0; b0 < w1; b0 += 64 * kSelBatch) {
+  if (gt_run + min(eq_run, need) >= (uint32_t)k_eff || (ngt == 0 && (neq == 0 || eq_run >= need))) return;
+  for (int j0 = 0; j0 < cnt; j0 += kSelBatch) {
     uint32_t kx[kSelBatch];
 #pragma unroll
-    for (int u = 0; u < kSelBatch; ++u) kx[u] = kv[min(b0 + 64 * u + lane, n_cand - 1)];
+    for (int u = 0; u < kSelBatch; ++u) kx[u] = key_of(min(j0 + u, cnt - 1));
 #pragma unroll
     for (int u = 0; u < kSelBatch; ++u) {
-      const int i = b0 + 64 * u + lane;
-      const bool in = i < w1;
+      const int j = j0 + u;
+      const bool in = j < cnt;
       const bool gt = in && kx[u] > T, eq = in && kx[u] == T;
-      const uint64_t mg = __ballot(gt), me = __ballot(eq);
-      const uint32_t gt_before = gt_run + __popcll(mg & below);
-      const uint32_t eq_before = eq_run + __popcll(me & below);
-      if (gt || (eq && eq_before < need)) {
-        const uint32_t pos = gt_before + min(eq_before, need);
+      if (gt || (eq && eq_run < need)) {
+        const uint32_t pos = gt_run + min(eq_run, need);
         if (pos < (uint32_t)k_eff) {
+          const int i = i_begin + j;
           const int32_t c = ids ? ids[i] : i;
           so[pos] = c;
           if (so2) so2[pos] = c;
         }
       }
-      gt_run += __popcll(mg);
-      eq_run += __popcll(me);
+      gt_run += gt ? 1u : 0u;
+      eq_run += eq ? 1u : 0u;
     }
   }
 }
@@ -651,7 +681,7 @@ hipError_t launch_select(const uint32_t* keys, const int32_t* cand_ids, int32_t*
     hipLaunchKernelGGL(select_kernel<true>, grid, block, sizeof(SelLds), st, keys, cand_ids, sel, sel_out,
                        n_cand, k, hkv, cache_bmul);
   } else {
-    hipLaunchKernelGGL(select_kernel<false>, grid, block, sizeof(SelLds) - kSelLdsKeys * 4, st, keys,
+    hipLaunchKernelGGL(select_kernel<false>, grid, block, sizeof(SelLds) - kSelLdsWords * 4, st, keys,
                        cand_ids, sel, sel_out, n_cand, k, hkv, cache_bmul);
   }
   return hipGetLastError();
