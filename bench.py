@@ -57,7 +57,10 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c3_262k_b28_hbm_traffic.txt")
+TRAFFIC_FILES = {
+    ("c3_llama8b_262k", 28): os.path.join(ROOT, "profiles", "decode_c3_262k_b28_hbm_traffic.txt"),
+    ("c4_eq_int4_evict_262k", 16): os.path.join(ROOT, "profiles", "decode_c4_int4_evict_262k_b16_hbm_traffic.txt"),
+}
 KERNEL_SOURCES = {
     "attend": ("attend.hip", "attend_pipe.hip", "attend_ops.h", "common.h", "internal.h"),
     "score": ("score_select.hip", "common.h", "internal.h"),
@@ -78,10 +81,13 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, workload, nb, path=TRAFFIC_FILE):
+def measured_traffic(kernel, workload, nb, path=None):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size), or None when
-    the summary is for another workload or the kernel's sources changed since."""
+    there is none for the workload or the kernel's sources changed since."""
+    path = path or TRAFFIC_FILES.get((workload, nb))
+    if path is None:
+        return None
     try:
         lines = open(path).read().splitlines()
     except OSError:
