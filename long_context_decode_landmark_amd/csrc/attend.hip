@@ -718,11 +718,13 @@ hipError_t launch_attend(const AttendArgs& a, int rank, bool ci4, bool ri4, hipS
 
 // ---------------------------------------------------------------------------
 // Split merge: one workgroup per (sequence, KV head, query head j), 512
-// threads = 128 output dims d x 4 split groups.  Every thread first issues the
-// loads of its o values (splits sg, sg + 4, ... in batches of kMergeBatch), then
-// wave 0 forms the weights w_s = exp2(m_s - M) / L in LDS (M = max_s m_s,
-// L = sum_s exp2(m_s - M) l_s) while those loads are in flight; the 4 split
-// groups' sums meet in LDS.
+// threads = 128 output dims d x 4 split groups.  Every load that does not
+// depend on the weights goes out first, together: each thread's o values
+// (splits sg, sg + 4, ... in batches of kMergeBatch), its W2 row piece, its PH
+// values, and for wave 0 the (m, l) of the first 128 splits.  Wave 0 then
+// forms the weights w_s = exp2(m_s - M) / L in LDS (M = max_s m_s,
+// L = sum_s exp2(m_s - M) l_s) from registers; the 4 split groups' sums meet
+// in LDS.
 // The producer/consumer kernel's slots come in groups of 4 (one group of
 // tiles, slot w = consumer w); beside each slot's o (its residual share and
 // b2 l), a group has one PH row, sum_t p_t gelu(W1 K_pre + b1) over its
@@ -735,6 +737,7 @@ hipError_t launch_attend(const AttendArgs& a, int rank, bool ci4, bool ri4, hipS
 // ---------------------------------------------------------------------------
 constexpr int kMergeThreads = 512;
 constexpr int kMergeBatch = 16;
+constexpr int kMergePhBatch = 8;  // PH groups a thread has in flight (per half)
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part,
                                                               uint16_t* __restrict__ out, int hkv,
@@ -756,20 +759,48 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   float ov[kMergeBatch];
 #pragma unroll
   for (int k = 0; k < kMergeBatch; ++k) ov[k] = pj[min(sg + 4 * k, ns - 1) * st + 2 + d];
-  // W2 row d, units [64 sg, 64 sg + 64), of this head (issued with the o loads)
+  // W2 row d, units [64 sg, 64 sg + 64), of this head, and this thread's PH
+  // values: unit u = tid % 256 of the groups of parity tid / 256 (PH row of
+  // group gx = slot 4 gx)
   bf16x8 w2v[8];
+  const int u = tid & (kHidden - 1), half = tid >> 8;
+  const int ngrp = nph / 4;
+  const size_t phs = (size_t)g * kHidden;  // between slots
+  const float* pp = phm.ph + head * (size_t)phm.ph_stride * phs + (size_t)j * kHidden + u;
+  float hv[kMergePhBatch];
   if (nph > 0) {
     const size_t chead = (size_t)blockIdx.z * phm.cache_bmul * hkv + blockIdx.y;
     const uint16_t* w2row = phm.w2 + (chead * kHeadDim + d) * kHidden + 64 * sg;
 #pragma unroll
     for (int k = 0; k < 8; ++k) w2v[k] = load_bf16x8(w2row + 8 * k);
+#pragma unroll
+    for (int k = 0; k < kMergePhBatch; ++k) hv[k] = pp[4 * min(half + 2 * k, ngrp - 1) * phs];
   }
   if (tid < 64) {
+    // (m, l) of splits tid and tid + 64 in registers; any beyond 128 are read in a loop
+    float mv[2], lv[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int sp = min(tid + 64 * r, ns - 1);
+      mv[r] = pj[sp * st];
+      lv[r] = pj[sp * st + 1];
+    }
     float m = -__builtin_huge_valf();
-    for (int sp = tid; sp < ns; sp += 64) m = fmaxf(m, pj[sp * st]);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) m = tid + 64 * r < ns ? fmaxf(m, mv[r]) : m;
+    for (int sp = tid + 128; sp < ns; sp += 64) m = fmaxf(m, pj[sp * st]);
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     float l = 0.f;
-    for (int sp = tid; sp < ns; sp += 64) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int sp = tid + 64 * r;
+      if (sp < ns) {
+        const float w = mv[r] == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(mv[r] - m);
+        wgt[sp] = w;
+        l += w * lv[r];
+      }
+    }
+    for (int sp = tid + 128; sp < ns; sp += 64) {
       const float ms = pj[sp * st];
       const float w = ms == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(ms - m);
       wgt[sp] = w;
@@ -795,22 +826,23 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
     }
   }
   if (nph > 0) {
-    // sum_g W_g PH_g: unit u = tid % 256, groups of parity tid / 256 (PH row
-    // of group gx = slot 4 gx)
-    const int u = tid & (kHidden - 1), half = tid >> 8;
-    const int ngrp = nph / 4;
-    const size_t phs = (size_t)g * kHidden;  // between slots
-    const float* pp = phm.ph + head * (size_t)phm.ph_stride * phs + (size_t)j * kHidden + u;
+    // sum_g W_g PH_g over this thread's groups (the first batch already loaded)
+    auto group_weight = [&](int gx) {
+      return fmaxf(fmaxf(wgt[4 * gx], wgt[4 * gx + 1]), fmaxf(wgt[4 * gx + 2], wgt[4 * gx + 3]));
+    };
     float hs = 0.f;
-    for (int base = half; base < ngrp; base += 2 * kMergeBatch) {
-      float hv[kMergeBatch];
 #pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) hv[k] = pp[4 * min(base + 2 * k, ngrp - 1) * phs];
+    for (int k = 0; k < kMergePhBatch; ++k) {
+      const int gx = half + 2 * k;
+      hs += gx < ngrp ? hv[k] * group_weight(min(gx, ngrp - 1)) : 0.f;
+    }
+    for (int base = half + 2 * kMergePhBatch; base < ngrp; base += 2 * kMergePhBatch) {
 #pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) {
-        const int gx = min(base + 2 * k, ngrp - 1);
-        const float wg = fmaxf(fmaxf(wgt[4 * gx], wgt[4 * gx + 1]), fmaxf(wgt[4 * gx + 2], wgt[4 * gx + 3]));
-        hs += base + 2 * k < ngrp ? hv[k] * wg : 0.f;
+      for (int k = 0; k < kMergePhBatch; ++k) hv[k] = pp[4 * min(base + 2 * k, ngrp - 1) * phs];
+#pragma unroll
+      for (int k = 0; k < kMergePhBatch; ++k) {
+        const int gx = base + 2 * k;
+        hs += gx < ngrp ? hv[k] * group_weight(min(gx, ngrp - 1)) : 0.f;
       }
     }
     phc[half][u] = hs;
