@@ -23,10 +23,10 @@ namespace lowram {
 // On the VALU it would cost one bf16->fp32 convert plus g FMAs per element
 // and a 16-lane reduction per chunk, close to the whole VALU issue budget at
 // full HBM rate; one v_mfma_f32_16x16x32_bf16 instead takes 16 landmarks x
-// 32 dims straight from the load registers.  A = the KV head's queries (rows
-// j < g, zero rows above), B = 16 landmarks (columns), so lane l (< 16 per
-// 16-lane group) ends up owning chunk c0 + l%16 with rows j = 4*(l/16) + e.
-// Each wave keeps 4 groups of 16 landmarks (16 KiB) in flight per iteration.
+// 32 dims per instruction.  A = the KV head's queries (rows j < g, zero rows
+// above), B = 16 landmarks (columns), so lane l (< 16 per 16-lane group) ends
+// up owning chunk c0 + l%16 with rows j = 4*(l/16) + e.  Each wave keeps 64
+// landmarks (16 KiB) in flight while it multiplies the previous 64 out of LDS.
 // ---------------------------------------------------------------------------
 #ifndef LOWRAM_SCORE_WG_PER_CU
 #define LOWRAM_SCORE_WG_PER_CU 2
@@ -53,27 +53,40 @@ __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
   const int c_begin = blockIdx.x * chunks_per_wg;
   const int c_end = min(n_cand, c_begin + chunks_per_wg);
 
-  // software pipeline: the next 64 landmarks of this wave are in flight
-  // while the current 64 are multiplied
-  auto load_group = [&](int c0, bf16x8 (&lv)[4][4]) {
+  // Landmark rows reach the MFMA through a per-wave LDS tile.  Each load
+  // instruction takes 4 whole rows (1 KiB contiguous) with the non-temporal
+  // policy (every 128-byte line is consumed whole by the instruction that
+  // reads it); piece p of row r is stored at piece p ^ (r & 15), so that both
+  // the stores and the B-operand reads (16 rows, one 16-byte piece each) are
+  // conflict-free.  The next 64 rows of the wave are in flight in registers
+  // while the current 64 are multiplied.
+  __shared__ __attribute__((aligned(16))) unsigned char tile[4][64 * 256];
+  unsigned char* my = tile[wave];
+  auto load_rows = [&](int c0, u32x4 (&v)[16]) {
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      const int cc = min(c0 + 16 * gi + col, n_cand - 1);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        lv[gi][ks] = load_bf16x8(lm + (size_t)cc * kHeadDim + 32 * ks + 8 * grp);
+    for (int i = 0; i < 16; ++i) {
+      const int cc = min(c0 + 4 * i + grp, n_cand - 1);
+      v[i] = load_nt16(lm + (size_t)cc * kHeadDim + 8 * col);
     }
   };
-  bf16x8 cur[4][4], nxt[4][4];
+  u32x4 nxt[16];
   int c0 = c_begin + wave * 64;
-  if (c0 < c_end) load_group(c0, cur);
+  if (c0 < c_end) load_rows(c0, nxt);
   for (; c0 < c_end; c0 += 256) {
-    if (c0 + 256 < c_end) load_group(c0 + 256, nxt);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 4 * i + grp;
+      *reinterpret_cast<u32x4*>(my + r * 256 + 16 * (col ^ (r & 15))) = nxt[i];
+    }
+    if (c0 + 256 < c_end) load_rows(c0 + 256, nxt);
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * gi + col;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma16(qa[ks], cur[gi][ks], acc);
+      for (int ks = 0; ks < 4; ++ks)
+        acc = mfma16(qa[ks], __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                 my + r * 256 + 16 * ((4 * ks + grp) ^ (r & 15)))), acc);
       float s = -__builtin_huge_valf();
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -86,10 +99,6 @@ __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
         if (sout) sout[c] = s;
       }
     }
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) cur[gi][ks] = nxt[gi][ks];
   }
 }
 
