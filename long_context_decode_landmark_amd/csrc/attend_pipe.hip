@@ -87,6 +87,9 @@ struct PipeLds {
   // alpha and the running (m, l)
   f32x4 sm[2][kPipeSlots][16];
   uint32_t rdesc[2][kPipeSlots][4];     // residual descriptors of each slot's 4 chunks, by tile parity
+  // role synchronisation (counts only grow): producer step barrier, tiles
+  // handed to the consumers, tiles the consumers have released
+  unsigned sync_step, sync_handed, sync_released;
 };
 static_assert(sizeof(PipeLds) <= 160 * 1024, "one workgroup per CU");
 
@@ -163,6 +166,22 @@ __device__ __forceinline__ PipeCur pipe_next(const AttendArgs& a, PipeCur c) {
   return c.g + a.pipe_wgs < a.pipe_groups ? pipe_first(a, c.g + a.pipe_wgs) : c;
 }
 
+// The two roles meet through counters in LDS instead of workgroup barriers.
+// pipe_post: lane 0 adds 1 after every earlier LDS access of the wave has
+// completed (release).  pipe_wait: the wave spins until the count reaches
+// target (acquire); the spin is bounded (about 4 ms, several hundred times a
+// tile-step), so a count that never arrived would end the wait, not hang the
+// kernel.
+__device__ __forceinline__ void pipe_post(unsigned* c, int lane) {
+  if (lane == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void pipe_wait(unsigned* c, unsigned target) {
+  for (int it = 0; it < (1 << 16); ++it) {
+    if (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 template <int RANK, bool CI4, bool RI4>
 __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const AttendArgs a) {
   __shared__ PipeLds L;
@@ -198,6 +217,11 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
   };
 
   // tables
+  if (tid == 0) {
+    L.sync_step = 0;
+    L.sync_handed = 0;
+    L.sync_released = 0;
+  }
   if (tid < 64) L.invf[tid] = a.inv_freq[tid];
   if (tid < 256) {
     // offset tables: two consecutive frequencies per thread, as fp16 pairs
@@ -340,6 +364,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 
     f32x4 acc[NT][8];
     const size_t desc_rows = (size_t)(a.prefix_cap / kChunk);
+    unsigned step_count = 0;
     for (int i = 0; i < ntiles; ++i) {
       const int bh_n = tn.bh, chead_c = tc.chead, cseq_c = tc.cseq, cseq_n = tn.cseq;
       const bool grp_end = tc.lt + 1 == tc.gend;  // the group ends with this tile
@@ -348,6 +373,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
       uint16_t b2raw = 0;  // this tile's b2, to LDS at the last step
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
+        // this tile's hand-off structures (parity i & 1) are written from here
+        // on: the consumers must have released tile i - 2
+        if (s == NR - 1 && i >= 2) pipe_wait(&L.sync_released, 4u * (unsigned)(i - 1));
         if (s == kQStep) store_q();  // rank >= 128: this tile's; rank 64: the next tile's
         if (s == NS - 1) {
           // this tile's b2 for its consumer tile-step (for the group's
@@ -520,14 +548,17 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
           // next basis stage into the buffer the previous step read
           stage_store((i * NR + s + 1) & 1, sreg[(s + 1) % NR]);
         }
-        __syncthreads();
+        // the four producers meet after every step (the basis ring, the queries)
+        pipe_post(&L.sync_step, lane);
+        ++step_count;
+        pipe_wait(&L.sync_step, 4u * step_count);
       }
+      // tile i is handed to the consumers
+      pipe_post(&L.sync_handed, lane);
       tc = tn;
       tn = tnn;
       tnn = pipe_next(a, tnn);
     }
-#pragma unroll
-    for (int s = 0; s < NS; ++s) __syncthreads();  // the consumers' last tile
   } else {
     // ===================================================================== consumer
     // Consumer w owns hidden units [64 w, 64 w + 64) of every token of the
@@ -570,8 +601,6 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     PipeCur tn = pipe_next(a, tc);
     load_w1(tc.chead);
     __syncthreads();
-#pragma unroll
-    for (int s = 0; s < NS; ++s) __syncthreads();  // the producers' first tile
 
     f32x4 racc[8];   // slot w's residual share (+ nothing else), output space, scale m_w
     f32x4 phacc[4];  // PH of units hq0 + 16 hn + 4 grp + e, query col, scale M
@@ -647,6 +676,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
       uint16_t rsc[RI4 ? RL : 1];
 #pragma unroll
       for (int c = 0; c < NS; ++c) {
+        if (c == 0) pipe_wait(&L.sync_handed, 4u * (unsigned)(i + 1));  // tile i handed
         // ---- LDS operands first: K_pre of piece c, and at a tile start the
         //      slots' running softmax state and weights
         bf16x8 ka[4];
@@ -672,6 +702,8 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
         if (c > 0 || i > 0) finish_piece((c + NS - 1) % NS);
         if (c == 0) {
           if (prev_end) write_part(tp, m_w, l_w, (i - 1) & 1);
+          // the previous tile's LDS (hand-off, weights, descriptors, b2) is read
+          if (i > 0) pipe_post(&L.sync_released, lane);
           float mnew = -__builtin_huge_valf();
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2) mnew = fmaxf(mnew, sm[s2][1]);
@@ -774,7 +806,6 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
             for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(dst + 16 * k) = __builtin_bit_cast(u32x4, dequant8(rres[u][k], sc));
           }
         }
-        __syncthreads();
       }
       tp = tc;
       tc = tn;
