@@ -73,11 +73,18 @@ BUILD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "build_c3_262k_hbm_traffic.t
 
 
 def source_hash(kernel):
+    """sha256[:16] of the kernel's source files with comments and blank space
+    removed: a counter summary stays valid across comment edits, and goes
+    stale with any change to the code itself."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "long_context_decode_landmark_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "long_context_decode_landmark_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

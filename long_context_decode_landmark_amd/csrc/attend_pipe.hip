@@ -15,29 +15,32 @@
 // the VALU-heavy value section of its own tokens, so the two co-resident
 // workgroups of a CU keep the matrix cores and the vector ALUs busy in turn
 // rather than together.  Here one workgroup of 8 waves holds a CU (about
-// 158 KiB of LDS) for the whole launch.  The 128-token tiles of every
+// 152 KiB of LDS) for the whole launch.  The 128-token tiles of every
 // (sequence, KV head) are cut into groups of tpw consecutive tiles; the grid
 // has one workgroup per CU (W of them), and workgroup w takes groups
 // w, w + W, w + 2 W, ... one after another inside one pipeline, so the
 // pipeline fills and drains once per CU, and at any time the neighbouring
 // workgroups of an XCD work on the groups of the same few heads (their
-// basis and W1/W2 stay in that XCD's L2).  Waves 0-3 are producers and
-// waves 4-7 consumers; producer w and consumer w + 4 own the same 32 tokens
-// (slot w) of every tile.  Time runs in tile-steps of 8 steps with a
-// workgroup barrier after each step:
-//   producer, tile-step i      rebuild K_pre of tile i from the basis stream
-//                              (one r-slice of 64 per step); after the last
-//                              slice hand K_pre to the consumer through LDS,
-//                              then RoPE, QK and the running softmax, and
-//                              hand over the weights p
-//   consumer, tile-step i + 1  the first MLP layer, GELU and PH of tile i:
-//                              consumer w owns hidden units 64 w .. 64 w + 63
-//                              (its W1 rows in registers) and takes one
-//                              16-token piece of the tile per step; then
-//                              slot w's residual rows
+// basis and W1 stay in that XCD's L2).  Waves 0-3 are producers and waves
+// 4-7 consumers; producer w owns the 32 tokens of slot w of every tile, and
+// consumer w hidden units 64 w .. 64 w + 63 of all of them plus slot w's
+// residual rows.  A tile takes 8 steps in each role:
+//   producer, tile i       rebuild K_pre of tile i from the basis stream (one
+//                          r-slice of 64 per step); after the last slice hand
+//                          K_pre to the consumers through LDS, then RoPE, QK
+//                          and the running softmax, and hand over the weights p
+//   consumer, tile i - 1   the first MLP layer, GELU and PH of the tile the
+//                          producers handed over last, one 16-token piece per
+//                          step (its W1 rows in registers); then slot w's
+//                          residual rows
 // so on every SIMD the reconstruction of one tile runs beside the value
-// section of the one before.  Producer and consumer run separate loops with
-// the same number of barriers; the role is a scalar (wave-uniform) branch.
+// section of the one before.  The role is a scalar (wave-uniform) branch, and
+// the roles meet through counters in LDS (pipe_post / pipe_wait): the four
+// producers after every step (they share the basis ring and the queries),
+// the consumers when a tile has been handed over, and the producers, before
+// they overwrite a hand-off buffer, when the consumers have released the
+// tile that used it two tiles earlier.  Each role thus runs at its own pace,
+// at most two tiles apart.
 // Everything that depends on the head (basis, W1, biases, queries,
 // selection list, descriptors) is looked up per tile, and the loads issued
 // for the next tile use the next tile's head.
@@ -62,7 +65,7 @@ namespace lowram {
 
 constexpr int kPipeSlots = kPipeSplitsPerGroup;  // producer/consumer pairs (one partial slot each)
 constexpr int kPipeThreads = 2 * kPipeSlots * 64;
-constexpr int kPipeSteps = kHidden / 32;      // value stages = steps per tile-step
+constexpr int kPipeSteps = kHidden / 32;      // value stages = steps per tile
 constexpr int kHandSlot = 9216;               // per slot: K_pre operands (8 KiB), then p (1 KiB)
 constexpr int kHandP = 8192;
 static_assert(kAttSelNT == 2 && kAttChunksWG == 16, "tiles of 128 tokens, 32 per slot");
@@ -170,7 +173,7 @@ __device__ __forceinline__ PipeCur pipe_next(const AttendArgs& a, PipeCur c) {
 // pipe_post: lane 0 adds 1 after every earlier LDS access of the wave has
 // completed (release).  pipe_wait: the wave spins until the count reaches
 // target (acquire); the spin is bounded (about 4 ms, several hundred times a
-// tile-step), so a count that never arrived would end the wait, not hang the
+// tile's time), so a count that never arrived would end the wait, not hang the
 // kernel.
 __device__ __forceinline__ void pipe_post(unsigned* c, int lane) {
   if (lane == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -186,7 +189,7 @@ template <int RANK, bool CI4, bool RI4>
 __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const AttendArgs a) {
   __shared__ PipeLds L;
   constexpr int NR = RANK / 64;                 // basis stages per tile
-  constexpr int NS = kPipeSteps;                // steps per tile-step
+  constexpr int NS = kPipeSteps;                // steps per tile
   static_assert(NR >= 1 && NR <= NS, "rank 64 .. 512");
   constexpr int SL = NR < 2 ? NR : 2;           // basis stage registers run SL stages ahead
   constexpr int LG = NR - 1 < 2 ? NR - 1 : 2;   // coefficient gathers run LG stages ahead (0: same step)
@@ -313,9 +316,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     };
     load_next_ids(tn);
     // The queries of a tile's head go to LDS as fp16 before its tail (step 0
-    // of its tile-step; rank 64: the last step of the tile-step before), from
-    // 16 bytes per thread loaded a whole tile-step earlier (step 0 of the tile
-    // before; rank 64: at the previous tail).
+    // of its tile; rank 64: the last step of the tile before), from 16 bytes
+    // per thread loaded a whole tile earlier (step 0 of the tile before; rank
+    // 64: at the previous tail).
     constexpr int kQStep = NR >= 2 ? 0 : NS - 1;
     bf16x8 qld;
     auto load_q = [&](int bh) {
@@ -378,7 +381,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
         if (s == NR - 1 && i >= 2) pipe_wait(&L.sync_released, 4u * (unsigned)(i - 1));
         if (s == kQStep) store_q();  // rank >= 128: this tile's; rank 64: the next tile's
         if (s == NS - 1) {
-          // this tile's b2 for its consumer tile-step (for the group's
+          // this tile's b2 for the consumers (for the group's
           // partial), ahead of the tail so that it is not held through it
           // (indexed as slot base + lane, the lane offsets the other writes use)
           const int ln = fresh(lane);
@@ -563,12 +566,12 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     // ===================================================================== consumer
     // Consumer w owns hidden units [64 w, 64 w + 64) of every token of the
     // tile (all four slots), with its W1 rows and b1 in registers, reloaded
-    // when the head changes.  Step c of a tile-step runs the first MLP layer
+    // when the head changes.  Step c of a tile runs the first MLP layer
     // of the tile's 16-token piece c (slot c / 2, half c % 2, from the K_pre
     // operands the producers handed over) and the GELU of piece c - 1; each
     // pair of pieces (one slot's 32 tokens) then meets that slot's softmax
     // weights in the PH product.  The last piece of a tile finishes at step 0
-    // of the next tile-step (or after the loop).
+    // of the next tile (or after the loop).
     //
     // The slots' weights are relative to each slot's running maximum m_s
     // (its producer's).  A consumer puts them on one scale per tile,
