@@ -15,7 +15,7 @@
 // the VALU-heavy value section of its own tokens, so the two co-resident
 // workgroups of a CU keep the matrix cores and the vector ALUs busy in turn
 // rather than together.  Here one workgroup of 8 waves holds a CU (about
-// 152 KiB of LDS) for the whole launch.  The 128-token tiles of every
+// 160 KiB of LDS) for the whole launch.  The 128-token tiles of every
 // (sequence, KV head) are cut into groups of tpw consecutive tiles; the grid
 // has one workgroup per CU (W of them), and workgroup w takes groups
 // w, w + W, w + 2 W, ... one after another inside one pipeline, so the
@@ -24,23 +24,30 @@
 // basis and W1 stay in that XCD's L2).  Waves 0-3 are producers and waves
 // 4-7 consumers; producer w owns the 32 tokens of slot w of every tile, and
 // consumer w hidden units 64 w .. 64 w + 63 of all of them plus slot w's
-// residual rows.  A tile takes 8 steps in each role:
+// residual rows.  Per tile:
 //   producer, tile i       rebuild K_pre of tile i from the basis stream (one
-//                          r-slice of 64 per step); after the last slice hand
-//                          K_pre to the consumers through LDS, then RoPE, QK
-//                          and the running softmax, and hand over the weights p
+//                          r-slice of 64 per step, rank / 64 steps); after the
+//                          last slice hand K_pre to the consumers through LDS,
+//                          then RoPE, QK and the running softmax, and hand over
+//                          the weights p
 //   consumer, tile i - 1   the first MLP layer, GELU and PH of the tile the
 //                          producers handed over last, one 16-token piece per
-//                          step (its W1 rows in registers); then slot w's
-//                          residual rows
+//                          step (8 steps, its W1 rows in registers); then slot
+//                          w's residual rows
 // so on every SIMD the reconstruction of one tile runs beside the value
 // section of the one before.  The role is a scalar (wave-uniform) branch, and
-// the roles meet through counters in LDS (pipe_post / pipe_wait): the four
-// producers after every step (they share the basis ring and the queries),
-// the consumers when a tile has been handed over, and the producers, before
-// they overwrite a hand-off buffer, when the consumers have released the
-// tile that used it two tiles earlier.  Each role thus runs at its own pace,
-// at most two tiles apart.
+// the waves meet through counters in LDS (pipe_post / pipe_wait), never at a
+// workgroup barrier: the producers among themselves over the basis ring (a
+// stage is read once all four have stored their quarter of it), the
+// consumers when a tile has been handed over, and the producers, before they
+// overwrite a hand-off buffer, when the consumers have released the tile
+// that used it two tiles earlier.  The producers thus run up to about half a
+// step apart, and the two roles at most two tiles apart.  Every count is
+// exact: no wave can post ahead of the count another wave is waiting for (a
+// producer cannot store stage G + 2 before all have stored G + 1, nor hand
+// over tile i + 2 before all have handed over tile i, hence the per-parity
+// hand-off counts; a consumer cannot release tile i + 1 before all have
+// released tile i).
 // Everything that depends on the head (basis, W1, biases, queries,
 // selection list, descriptors) is looked up per tile, and the loads issued
 // for the next tile use the next tile's head.
@@ -80,9 +87,10 @@ struct PipeLds {
   alignas(16) _Float16 rope_os[kChunk][64];
   alignas(16) _Float16 rope_bc[kPipeSlots][4][64];
   alignas(16) _Float16 rope_bs[kPipeSlots][4][64];
-  // the queries of the current tile's head as fp16: row j < g (zeros above),
-  // 16-byte piece p of the row at piece p ^ j
-  alignas(16) _Float16 qh[16][kHeadDim];
+  // the queries of each tile's head as fp16, three tiles in turn (tile i in
+  // buffer i % 3): row j < g (zeros above), 16-byte piece p of the row at
+  // piece p ^ j
+  alignas(16) _Float16 qh[3][16][kHeadDim];
   // b2 of each tile's head, by tile parity (read when a group's partial is written)
   float b2f[2][kHeadDim];
   double invf[64];                       // RoPE frequencies (read where needed: no registers held)
@@ -90,9 +98,10 @@ struct PipeLds {
   // alpha and the running (m, l)
   f32x4 sm[2][kPipeSlots][16];
   uint32_t rdesc[2][kPipeSlots][4];     // residual descriptors of each slot's 4 chunks, by tile parity
-  // role synchronisation (counts only grow): producer step barrier, tiles
-  // handed to the consumers, tiles the consumers have released
-  unsigned sync_step, sync_handed, sync_released;
+  // role synchronisation (counts only grow): basis stage quarters stored to
+  // the ring, tiles handed to the consumers (by tile parity), tiles the
+  // consumers have released
+  unsigned sync_stored, sync_handed[2], sync_released;
 };
 static_assert(sizeof(PipeLds) <= 160 * 1024, "one workgroup per CU");
 
@@ -179,6 +188,7 @@ __device__ __forceinline__ void pipe_post(unsigned* c, int lane) {
   if (lane == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 __device__ __forceinline__ void pipe_wait(unsigned* c, unsigned target) {
+#pragma nounroll
   for (int it = 0; it < (1 << 16); ++it) {
     if (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
     __builtin_amdgcn_s_sleep(2);
@@ -191,7 +201,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
   constexpr int NR = RANK / 64;                 // basis stages per tile
   constexpr int NS = kPipeSteps;                // steps per tile
   static_assert(NR >= 1 && NR <= NS, "rank 64 .. 512");
-  constexpr int SL = NR < 2 ? NR : 2;           // basis stage registers run SL stages ahead
+  constexpr int SL = NR + 1 < 3 ? NR + 1 : 3;   // basis stage registers run SL stages ahead
   constexpr int LG = NR - 1 < 2 ? NR - 1 : 2;   // coefficient gathers run LG stages ahead (0: same step)
   constexpr int NT = 2;
 
@@ -221,8 +231,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 
   // tables
   if (tid == 0) {
-    L.sync_step = 0;
-    L.sync_handed = 0;
+    L.sync_stored = 0;
+    L.sync_handed[0] = 0;
+    L.sync_handed[1] = 0;
     L.sync_released = 0;
   }
   if (tid < 64) L.invf[tid] = a.inv_freq[tid];
@@ -238,20 +249,19 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     // ===================================================================== producer
     // basis stage s = columns [64 s, 64 s + 64), 128 rows in pi order, two rows per
     // 256-byte line, 16-byte pieces XOR-swizzled by the line index
-    // The basis of one cache head through a descriptor carried across tiles:
-    // it moves to the next tile's head at the step whose stage loads start
-    // reading the next tile (step NR - SL), so every load keeps constant offsets.
     auto bas_of = [&](int chead) {
       return buffer_rsrc(a.basis + (size_t)chead * kHeadDim * RANK, kHeadDim * RANK * 2);
     };
     const int r0 = rt >> 3, pb = rt & 7;
     const uint32_t bas_goff = (uint32_t)((row_perm32(r0) * RANK + 8 * pb) * 2);
-    const int bas_loff = (r0 >> 1) * 256 + ((((r0 & 1) << 3) | pb) ^ ((r0 >> 1) & 15)) * 16;
     auto stage_load = [&](__amdgpu_buffer_rsrc_t bas, int s, u32x4 (&r)[kStageLd]) {
 #pragma unroll
       for (int u = 0; u < kStageLd; ++u) r[u] = buffer_ld16(bas, bas_goff, (32 * u * RANK + 64 * s) * 2);
     };
     auto stage_store = [&](int buf, const u32x4 (&r)[kStageLd]) {
+      // (the offset is formed here from an opaque thread id, not held across the loop)
+      const int t = fresh(rt), q0 = t >> 3, q = t & 7;
+      const int bas_loff = (q0 >> 1) * 256 + ((((q0 & 1) << 3) | q) ^ ((q0 >> 1) & 15)) * 16;
       unsigned char* dst = L.bring[buf];
 #pragma unroll
       for (int u = 0; u < kStageLd; ++u) *reinterpret_cast<u32x4*>(dst + bas_loff + 4096 * u) = r[u];
@@ -265,8 +275,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     bf16x8 cv[CI4 ? 1 : NR][2][NT];
     u32x2 cq[CI4 ? NR : 1][NT];
     float csc[CI4 ? NR : 1][NT];
-    // coefficient rows tk of cache sequence cseq, stage s
+    // coefficient rows tk of cache sequence cseq, stage s (lane offsets formed
+    // here from an opaque lane id, not held across the tile loop)
     auto gather = [&](int s, const int (&tk)[NT], int cseq) {
+      const int grp = fresh(lane) >> 4;
       if constexpr (!CI4) {
         const uint16_t* cb = static_cast<const uint16_t*>(a.coeff) + (size_t)cseq * a.prefix_cap * RANK;
 #pragma unroll
@@ -295,6 +307,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
       }
 
     // ---- prologue
+    // stage registers: stage s of a tile in sreg[s]; the stage of global index
+    // G (= tile x NR + s) is loaded at step G - SL and stored to the ring in
+    // the middle of step G - 1
     u32x4 sreg[NR][kStageLd];
     int tokA[NT], tokB[NT];
     // this tile, the next and the one after (look-ahead loads)
@@ -315,26 +330,23 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
       rcN = sel_at(bh, t.lt, 4 * slot + (ln >> 4));
     };
     load_next_ids(tn);
-    // The queries of a tile's head go to LDS as fp16 before its tail (step 0
-    // of its tile; rank 64: the last step of the tile before), from 16 bytes
-    // per thread loaded a whole tile earlier (step 0 of the tile before; rank
-    // 64: at the previous tail).
-    constexpr int kQStep = NR >= 2 ? 0 : NS - 1;
+    // The queries of tile i + 1 go to LDS as fp16 at step 0 of tile i, from
+    // 16 bytes per thread loaded at the last step of the tile before.  Three
+    // buffers: at step 0 of tile i every producer has passed the middle of
+    // the last step of tile i - 1, so none still reads the buffer of tile i - 2.
     bf16x8 qld;
     auto load_q = [&](int bh) {
       const int r = fresh(rt), j = r >> 4;
       const bf16x8 v = load_bf16x8(a.q + ((size_t)bh * g + min(j, g - 1)) * kHeadDim + 8 * (r & 15));
       qld = j < g ? v : zero_bf16x8();
     };
-    auto store_q = [&]() {
+    auto store_q = [&](int buf) {
       const int r = fresh(rt), j = r >> 4;
       f16x8 h;
 #pragma unroll
       for (int e = 0; e < 8; ++e) h[e] = (_Float16)(float)qld[e];
-      *reinterpret_cast<f16x8*>(&L.qh[j][8 * ((r & 15) ^ j)]) = h;
+      *reinterpret_cast<f16x8*>(&L.qh[buf][j][8 * ((r & 15) ^ j)]) = h;
     };
-    load_q(bh0);
-    if constexpr (NR == 1) store_q();  // the first tail is at step 0
     // this wave's rotation table row: chunk lane / 16, frequencies 4 (lane % 16) + k,
     // written as fp16 pairs, the access type the RoPE reads use
     auto store_rot = [&](float2 r0, float2 r1, float2 r2, float2 r3) {
@@ -350,9 +362,11 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
       ps[1] = s23;
     };
     float2 rot_next[4];  // rotations to the chunk starts: tile 0 here, later the next tile's
-    __amdgpu_buffer_rsrc_t bas = bas_of(tc.chead);
+    // stages 0 .. SL - 1; those of the next tile (SL > NR) after stage 0 has
+    // left its registers
 #pragma unroll
-    for (int s = 0; s < SL; ++s) stage_load(bas, s, sreg[s]);
+    for (int s = 0; s < SL; ++s)
+      if (s < NR) stage_load(bas_of(tc.chead), s, sreg[s]);
 #pragma unroll
     for (int s = 0; s < LG; ++s) gather(s, tokA, tc.cseq);
     {
@@ -362,202 +376,233 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
       store_rot(rot_next[0], rot_next[1], rot_next[2], rot_next[3]);
     }
     stage_store(0, sreg[0]);
+#pragma unroll
+    for (int s = NR; s < SL; ++s) stage_load(bas_of(tn.chead), s - NR, sreg[s - NR]);
+    load_q(bh0);
+    store_q(0);
+    load_q(tn.bh);
     float mrun = -__builtin_huge_valf(), lrun = 0.f;
     __syncthreads();
 
+    // The ring of two basis stages: stage G is read from buffer G & 1 at
+    // step G, once all four producers have stored their quarter of it (the
+    // count of stored quarters reaches 4 G).  Each producer posted that store
+    // after its reads of stage G - 1 had completed (the post is a release),
+    // so at that point the other buffer is free as well: right after reading
+    // stage G a producer stores its quarter of stage G + 1 there, and posts it
+    // once the first half of the step's products is issued.  A producer can
+    // thus run up to about half a step ahead of the slowest one.
+
     f32x4 acc[NT][8];
     const size_t desc_rows = (size_t)(a.prefix_cap / kChunk);
-    unsigned step_count = 0;
+    int qb = 0;  // i % 3: this tile's query buffer
     for (int i = 0; i < ntiles; ++i) {
-      const int bh_n = tn.bh, chead_c = tc.chead, cseq_c = tc.cseq, cseq_n = tn.cseq;
+      const int chead_c = tc.chead, cseq_c = tc.cseq, cseq_n = tn.cseq;
       const bool grp_end = tc.lt + 1 == tc.gend;  // the group ends with this tile
       int rc_next = 0;   // the next tile's rotation-table chunk (clamped)
       uint32_t rdv = 0;
-      uint16_t b2raw = 0;  // this tile's b2, to LDS at the last step
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
+      uint16_t b2raw = 0;  // this tile's b2, to LDS at the tail
+      bf16x8 aop[2][8];
+      // ---- the start of step s (stage G = i NR + s): per-tile loads and
+      //      hand-offs, then the stage's 16 basis operands from the ring
+      auto step_begin = [&](int s) {
+        const unsigned G = (unsigned)(i * NR + s);
         // this tile's hand-off structures (parity i & 1) are written from here
         // on: the consumers must have released tile i - 2
         if (s == NR - 1 && i >= 2) pipe_wait(&L.sync_released, 4u * (unsigned)(i - 1));
-        if (s == kQStep) store_q();  // rank >= 128: this tile's; rank 64: the next tile's
-        if (s == NS - 1) {
-          // this tile's b2 for the consumers (for the group's
-          // partial), ahead of the tail so that it is not held through it
-          // (indexed as slot base + lane, the lane offsets the other writes use)
+        if (s == 0) {
+          // residual descriptors of this tile's 4 chunks (lane k < 4: chunk k),
+          // handed to the consumer with K_pre; token 0 of chunk k sits in
+          // tokA[k / 2] of lane 8 (k % 2)
+          const int c0 = __shfl(tokA[0], 8 * (lane & 1)), c1 = __shfl(tokA[1], 8 * (lane & 1));
+          if (lane < 4) rdv = a.res_desc[(size_t)chead_c * desc_rows + ((lane & 2) ? c1 : c0) / kChunk];
+          const int r = fresh(rt);
+          b2raw = a.b2[(size_t)chead_c * kHeadDim + (r & (kHeadDim - 1))];
+        }
+        if (s == (NR > 1 ? 1 : 0)) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) tokB[nt] = clamp_chunk(selN[nt]) * kChunk + (fresh(lane) & 7);
+          rc_next = clamp_chunk(rcN);
+        }
+        if constexpr (LG == 0) gather(s, tokA, cseq_c);  // rank 64: the stage's own rows
+        // stage G is in the ring once all four producers have stored their quarter
+        if (G > 0) pipe_wait(&L.sync_stored, 4u * G);
+        if (s == 0) store_q(qb == 2 ? 0 : qb + 1);  // the next tile's queries
+        __builtin_amdgcn_sched_barrier(0);
+        // all 16 basis operands of the stage are read first, so that the
+        // matrix core is not left waiting on one LDS round trip per pair
+        const unsigned char* sb = L.bring[G & 1];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int mt = 0; mt < 8; ++mt) aop[ks][mt] = lds16(sb, ra[ks][mt & 1] + 2048 * mt);
+        // this producer's quarter of stage G + 1 into the other buffer
+        stage_store((int)((G + 1) & 1), sreg[(s + 1) % NR]);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // the coefficient operand of stage s, k-step ks, token half nt
+      auto coeff_op = [&](int s, int ks, int nt) -> bf16x8 {
+        if constexpr (!CI4) return cv[s][ks][nt];
+        else return dequant8(cq[s][nt][ks], csc[s][nt]);
+      };
+      // ---- the end of step s: the fp64 angle reduction of the step (the next
+      //      tile's rotations, one per step from step 1 on, off the tail)
+      //      and the loads for later stages
+      auto step_end = [&](int s) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (s == (NR > 1 ? (1 + k < NR - 1 ? 1 + k : NR - 1) : 0)) {
+            rot_next[k] = rot_of((double)rc_next * kChunk * L.invf[(lane & 15) * 4 + k]);
+            // keep the work in this step (the compiler would otherwise sink it into the tail)
+            asm volatile("" : "+v"(rot_next[k].x), "+v"(rot_next[k].y));
+          }
+        }
+      };
+      // Loads for later stages, issued after the step's products so that a
+      // full memory pipeline stalls nothing the step needs.  (Past the last
+      // tile they repeat the last tile: harmless, and they keep the code
+      // branch-free.)
+      auto step_loads = [&](int s) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (s == NR - 1) load_q(tnn.bh);  // stored at step 0 of the next tile
+        // stage G + SL: stage (s + SL) % NR of the tile (s + SL) / NR tiles on
+        const int ahead = (s + SL) / NR;
+        const int chead_l = ahead == 0 ? tc.chead : ahead == 1 ? tn.chead : tnn.chead;
+        stage_load(bas_of(chead_l), (s + SL) % NR, sreg[(s + SL) % NR]);
+        if constexpr (LG > 0) {
+          if (s + LG < NR) gather(s + LG, tokA, cseq_c);
+          else gather(s + LG - NR, tokB, cseq_n);
+        }
+      };
+
+      // ---- reconstruction stages before the last: k-step major
+#pragma unroll
+      for (int s = 0; s < NR - 1; ++s) {
+        step_begin(s);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 bop[NT];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) bop[nt] = coeff_op(s, ks, nt);
+#pragma unroll
+          for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              // a tile's first products start from zero (no accumulator to clear)
+              acc[nt][mt] = mfma16(aop[ks][mt], bop[nt], s == 0 && ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nt][mt]);
+          if (ks == 0) pipe_post(&L.sync_stored, lane);  // stage G + 1 stored
+        }
+        step_end(s);
+        step_loads(s);
+      }
+
+      // ---- the last stage, one 16-token half at a time, so that the first
+      //      half's RoPE can run on the vector ALUs under the second half's
+      //      products; then the tail
+      {
+        constexpr int s = NR - 1;
+        step_begin(s);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 bop = coeff_op(s, ks, nt);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+              acc[nt][mt] = mfma16(aop[ks][mt], bop, s == 0 && ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nt][mt]);
+          }
+          if (nt == 0) pipe_post(&L.sync_stored, lane);  // stage G + 1 stored
+        }
+        step_end(s);
+
+        // this tile's b2 for the consumers (for the group's partial), indexed
+        // as slot base + lane, the lane offsets the other writes use
+        {
           const int ln = fresh(lane);
           if (slot < kHeadDim / 64) (&L.b2f[i & 1][slot * 64])[ln] = bf16_to_f32(b2raw);
         }
-        if (s < NR) {
-          if (s == 0) {
-            // residual descriptors of this tile's 4 chunks (lane k < 4: chunk k),
-            // handed to the consumer with K_pre; token 0 of chunk k sits in
-            // tokA[k / 2] of lane 8 (k % 2)
-            const int c0 = __shfl(tokA[0], 8 * (lane & 1)), c1 = __shfl(tokA[1], 8 * (lane & 1));
-            if (lane < 4) rdv = a.res_desc[(size_t)chead_c * desc_rows + ((lane & 2) ? c1 : c0) / kChunk];
-            const int r = fresh(rt);
-            b2raw = a.b2[(size_t)chead_c * kHeadDim + (r & (kHeadDim - 1))];
-          }
-          if (s == (NR > 1 ? 1 : 0)) {
+        // ---- K_pre done: acc[nt][mt][e] = K_pre[t][d], t = 16 nt + col,
+        //      d = 32 (mt / 2) + 8 grp + 4 (mt % 2) + e.  Hand the bf16
+        //      operands to the consumer in its register layout.
+        unsigned char* hb = L.hand[i & 1][slot];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) tokB[nt] = clamp_chunk(selN[nt]) * kChunk + (col & 7);
-            rc_next = clamp_chunk(rcN);
-          }
-          if constexpr (LG == 0) gather(s, tokA, cseq_c);  // rank 64: the stage's own rows
-          __builtin_amdgcn_sched_barrier(0);
-
-          // all 16 basis operands of the stage are read first, so that the
-          // matrix core is not left waiting on one LDS round trip per pair
-          const unsigned char* sb = L.bring[(i * NR + s) & 1];
-          bf16x8 aop[2][8];
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
+          for (int ks = 0; ks < 4; ++ks)
+            *reinterpret_cast<u32x4*>(hb + (nt * 4 + ks) * 1024 + lane * 16) =
+                __builtin_bit_cast(u32x4, pack8(acc[nt][2 * ks], acc[nt][2 * ks + 1]));
+        // RoPE on packed fp16 pairs of consecutive frequencies: pair (d, d + 64)
+        // = m-tiles (mt, mt + 4) of the same lane; the rotation is the chunk
+        // start's composed with the offset's.  K_post stays fp16 (relative
+        // error ~3 2^-11, below the 2^-9 of a bf16 operand) and feeds an fp16
+        // QK.  One 16-token half at a time, so that only half of K_post is
+        // held at once.  (Lane-derived offsets come from an opaque lane id:
+        // formed here, not held across the tile loop.)
+        const int lq = fresh(lane), cl = lq & 15;
+        f16x8 qp[4];
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) aop[ks][mt] = lds16(sb, ra[ks][mt & 1] + 2048 * mt);
-          __builtin_amdgcn_sched_barrier(0);
-          if (s < NR - 1) {
+        for (int ks = 0; ks < 4; ++ks)
+          qp[ks] = *reinterpret_cast<const f16x8*>(&L.qh[qb][cl][8 * ((4 * ks + (lq >> 4)) ^ cl)]);
+        f32x4 zacc[NT];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-              bf16x8 bop[NT];
+        for (int nt = 0; nt < NT; ++nt) {
+          const int cs = 2 * nt + (cl >> 3);
+          h2 kp[8][2];  // K_post of this half, [mt][e pair]
 #pragma unroll
-              for (int nt = 0; nt < NT; ++nt) {
-                if constexpr (!CI4) bop[nt] = cv[s][ks][nt];
-                else bop[nt] = dequant8(cq[s][nt][ks], csc[s][nt]);
-              }
+          for (int mt = 0; mt < 4; ++mt) {
+            const int p0 = 32 * (mt >> 1) + 8 * (lq >> 4) + 4 * (mt & 1);
+            const h2* oc = reinterpret_cast<const h2*>(&L.rope_oc[cl & 7][p0]);
+            const h2* os = reinterpret_cast<const h2*>(&L.rope_os[cl & 7][p0]);
+            const h2* bc = reinterpret_cast<const h2*>(&L.rope_bc[slot][cs][p0]);
+            const h2* bs = reinterpret_cast<const h2*>(&L.rope_bs[slot][cs][p0]);
 #pragma unroll
-              for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                  // a tile's first products start from zero (no accumulator to clear)
-                  acc[nt][mt] = mfma16(aop[ks][mt], bop[nt], s == 0 && ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nt][mt]);
-            }
-          } else {
-            // the last stage one 16-token half at a time, so that the first
-            // half's RoPE can run on the vector ALUs under the second half's
-            // products
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-              for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 bop;
-                if constexpr (!CI4) bop = cv[s][ks][nt];
-                else bop = dequant8(cq[s][nt][ks], csc[s][nt]);
-#pragma unroll
-                for (int mt = 0; mt < 8; ++mt)
-                  acc[nt][mt] = mfma16(aop[ks][mt], bop, s == 0 && ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nt][mt]);
-              }
-          }
-          // fp64 angle reductions for the next tile, one per step from step 1 on,
-          // off the tail of the last stage
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            if (s == (NR > 1 ? (1 + k < NR - 1 ? 1 + k : NR - 1) : 0)) {
-              rot_next[k] = rot_of((double)rc_next * kChunk * L.invf[(lane & 15) * 4 + k]);
-              // keep the work in this step (the compiler would otherwise sink it into the tail)
-              asm volatile("" : "+v"(rot_next[k].x), "+v"(rot_next[k].y));
+            for (int q = 0; q < 2; ++q) {
+              const h2 o_c = oc[q], o_s = os[q], b_c = bc[q], b_s = bs[q];
+              const h2 c = __builtin_elementwise_fma(b_c, o_c, -(b_s * o_s));
+              const h2 sn = __builtin_elementwise_fma(b_s, o_c, b_c * o_s);
+              const h2 x1 = __builtin_convertvector(f32x2{acc[nt][mt][2 * q], acc[nt][mt][2 * q + 1]}, h2);
+              const h2 x2 = __builtin_convertvector(f32x2{acc[nt][mt + 4][2 * q], acc[nt][mt + 4][2 * q + 1]}, h2);
+              kp[mt][q] = __builtin_elementwise_fma(x1, c, -(x2 * sn));
+              kp[mt + 4][q] = __builtin_elementwise_fma(x2, c, x1 * sn);
             }
           }
-
-          if (s == NR - 1) {
-            // ---- K_pre done: acc[nt][mt][e] = K_pre[t][d], t = 16 nt + col,
-            //      d = 32 (mt / 2) + 8 grp + 4 (mt % 2) + e.  Hand the bf16
-            //      operands to the consumer in its register layout.
-            unsigned char* hb = L.hand[i & 1][slot];
+          // QK of this half (fp16 operands)
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-              for (int ks = 0; ks < 4; ++ks)
-                *reinterpret_cast<u32x4*>(hb + (nt * 4 + ks) * 1024 + lane * 16) =
-                    __builtin_bit_cast(u32x4, pack8(acc[nt][2 * ks], acc[nt][2 * ks + 1]));
-            // RoPE on packed fp16 pairs of consecutive frequencies: pair (d, d + 64)
-            // = m-tiles (mt, mt + 4) of the same lane; the rotation is the chunk
-            // start's composed with the offset's.  K_post stays fp16 (relative
-            // error ~3 2^-11, below the 2^-9 of a bf16 operand) and feeds an fp16
-            // QK.  One 16-token half at a time, so that only half of K_post is
-            // held at once.
-            const int cl = fresh(lane) & 15;
-            f16x8 qp[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-              qp[ks] = *reinterpret_cast<const f16x8*>(&L.qh[cl][8 * ((4 * ks + grp) ^ cl)]);
-            f32x4 zacc[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-              const int cs = 2 * nt + (cl >> 3);
-              h2 kp[8][2];  // K_post of this half, [mt][e pair]
-#pragma unroll
-              for (int mt = 0; mt < 4; ++mt) {
-                const int p0 = 32 * (mt >> 1) + 8 * grp + 4 * (mt & 1);
-                const h2* oc = reinterpret_cast<const h2*>(&L.rope_oc[cl & 7][p0]);
-                const h2* os = reinterpret_cast<const h2*>(&L.rope_os[cl & 7][p0]);
-                const h2* bc = reinterpret_cast<const h2*>(&L.rope_bc[slot][cs][p0]);
-                const h2* bs = reinterpret_cast<const h2*>(&L.rope_bs[slot][cs][p0]);
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                  const h2 o_c = oc[q], o_s = os[q], b_c = bc[q], b_s = bs[q];
-                  const h2 c = __builtin_elementwise_fma(b_c, o_c, -(b_s * o_s));
-                  const h2 sn = __builtin_elementwise_fma(b_s, o_c, b_c * o_s);
-                  const h2 x1 = __builtin_convertvector(f32x2{acc[nt][mt][2 * q], acc[nt][mt][2 * q + 1]}, h2);
-                  const h2 x2 = __builtin_convertvector(f32x2{acc[nt][mt + 4][2 * q], acc[nt][mt + 4][2 * q + 1]}, h2);
-                  kp[mt][q] = __builtin_elementwise_fma(x1, c, -(x2 * sn));
-                  kp[mt + 4][q] = __builtin_elementwise_fma(x2, c, x1 * sn);
-                }
-              }
-              // QK of this half (fp16 operands)
-              f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int ks = 0; ks < 4; ++ks) {
-                const f16x8 kop = __builtin_shufflevector(
-                    __builtin_shufflevector(kp[2 * ks][0], kp[2 * ks][1], 0, 1, 2, 3),
-                    __builtin_shufflevector(kp[2 * ks + 1][0], kp[2 * ks + 1][1], 0, 1, 2, 3),
-                    0, 1, 2, 3, 4, 5, 6, 7);
-                z = mfma16h(kop, qp[ks], z);
-              }
-              zacc[nt] = z;
-            }
-            // the running softmax
-            float alpha;
-            f16x8 pa;
-            pipe_softmax(zacc, slot_valid(tc.lt), a.scale_log2, grp, mrun, lrun, alpha, pa);
-            *reinterpret_cast<u32x4*>(hb + kHandP + lane * 16) = __builtin_bit_cast(u32x4, pa);
-            {
-              const int ln = fresh(lane);
-              if (lane < 16) (&L.sm[i & 1][slot][0])[ln] = f32x4{alpha, mrun, lrun, 0.f};
-              if (lane < 4) (&L.rdesc[i & 1][slot][0])[ln] = rdv;
-            }
-            // a new group starts from nothing (its first alpha is 0)
-            if (grp_end) {
-              mrun = -__builtin_huge_valf();
-              lrun = 0.f;
-            }
-            // this wave's rotation table for the next tile
-            store_rot(rot_next[0], rot_next[1], rot_next[2], rot_next[3]);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) tokA[nt] = tokB[nt];
-            load_next_ids(tnn);
-            if constexpr (NR == 1) load_q(bh_n);
+          for (int ks = 0; ks < 4; ++ks) {
+            const f16x8 kop = __builtin_shufflevector(
+                __builtin_shufflevector(kp[2 * ks][0], kp[2 * ks][1], 0, 1, 2, 3),
+                __builtin_shufflevector(kp[2 * ks + 1][0], kp[2 * ks + 1][1], 0, 1, 2, 3),
+                0, 1, 2, 3, 4, 5, 6, 7);
+            z = mfma16h(kop, qp[ks], z);
           }
-          // Loads for later stages, issued after this step's products so that
-          // a full memory pipeline stalls nothing the step needs.  (Past the
-          // last tile they repeat the last tile: harmless, and they keep the
-          // code branch-free.)
-          __builtin_amdgcn_sched_barrier(0);
-          if (NR >= 2 && s == 0) load_q(bh_n);  // the next tile's queries, stored at its step 0
-          if (s == NR - SL) bas = bas_of(tn.chead);  // from here on the loads are the next tile's
-          if constexpr (SL > 0) stage_load(bas, (s + SL) % NR, sreg[(s + SL) % NR]);
-          if constexpr (LG > 0) {
-            if (s + LG < NR) gather(s + LG, tokA, cseq_c);
-            else gather(s + LG - NR, tokB, cseq_n);
-          }
-          // next basis stage into the buffer the previous step read
-          stage_store((i * NR + s + 1) & 1, sreg[(s + 1) % NR]);
+          zacc[nt] = z;
         }
-        // the four producers meet after every step (the basis ring, the queries)
-        pipe_post(&L.sync_step, lane);
-        ++step_count;
-        pipe_wait(&L.sync_step, 4u * step_count);
+        // the running softmax
+        float alpha;
+        f16x8 pa;
+        pipe_softmax(zacc, slot_valid(tc.lt), a.scale_log2, lq >> 4, mrun, lrun, alpha, pa);
+        *reinterpret_cast<u32x4*>(hb + kHandP + lane * 16) = __builtin_bit_cast(u32x4, pa);
+        {
+          const int ln = fresh(lane);
+          if (lane < 16) (&L.sm[i & 1][slot][0])[ln] = f32x4{alpha, mrun, lrun, 0.f};
+          if (lane < 4) (&L.rdesc[i & 1][slot][0])[ln] = rdv;
+        }
+        // a new group starts from nothing (its first alpha is 0)
+        if (grp_end) {
+          mrun = -__builtin_huge_valf();
+          lrun = 0.f;
+        }
+        // this wave's rotation table for the next tile
+        store_rot(rot_next[0], rot_next[1], rot_next[2], rot_next[3]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) tokA[nt] = tokB[nt];
+        load_next_ids(tnn);
+        step_loads(s);
       }
       // tile i is handed to the consumers
-      pipe_post(&L.sync_handed, lane);
+      pipe_post(&L.sync_handed[i & 1], lane);
+      qb = qb == 2 ? 0 : qb + 1;
       tc = tn;
       tn = tnn;
       tnn = pipe_next(a, tnn);
@@ -679,7 +724,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
       uint16_t rsc[RI4 ? RL : 1];
 #pragma unroll
       for (int c = 0; c < NS; ++c) {
-        if (c == 0) pipe_wait(&L.sync_handed, 4u * (unsigned)(i + 1));  // tile i handed
+        if (c == 0) pipe_wait(&L.sync_handed[i & 1], 4u * (unsigned)(i / 2 + 1));  // tile i handed
         // ---- LDS operands first: K_pre of piece c, and at a tile start the
         //      slots' running softmax state and weights
         bf16x8 ka[4];
