@@ -17,6 +17,28 @@ constexpr float kGeluClamp = 4.0f;
 constexpr float kGeluQ[7] = {3.978703618e-01f, -6.455454975e-02f, 8.763747290e-03f, -8.121979772e-04f,
                              4.776486458e-05f, -1.588871555e-06f, 2.258899912e-08f};
 
+// Reductions over the lane pairs {l, l ^ 16} and {l, l ^ 32} of a wave on
+// the vector ALUs instead of the LDS crossbar: v_permlane16_swap with both
+// operands the same register gives, at lane l, the values of lanes l & ~16
+// and l | 16 (v_permlane32_swap: l & ~32 and l | 32).  Both lanes of a pair
+// get the same result (the sum adds the lower lane's value first).
+__device__ __forceinline__ float pair_max16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_add16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_add32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float gelu_fast(float x) {
   const float xc = __builtin_amdgcn_fmed3f(x, -kGeluClamp, kGeluClamp);
   const float u = xc * xc;

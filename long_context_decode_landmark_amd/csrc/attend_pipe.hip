@@ -120,8 +120,7 @@ __device__ __forceinline__ void pipe_softmax(const f32x4 (&zacc)[2], int nvalid,
       p[nt][e] = t < nvalid ? zacc[nt][e] * scale_log2 : -__builtin_huge_valf();
       m = fmaxf(m, p[nt][e]);
     }
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
+  m = pair_max32(pair_max16(m));
   const float mnew = fmaxf(mrun, m);
   const float msafe = mnew == -__builtin_huge_valf() ? 0.f : mnew;
   float lsum = 0.f;
@@ -132,8 +131,7 @@ __device__ __forceinline__ void pipe_softmax(const f32x4 (&zacc)[2], int nvalid,
       p[nt][e] = __builtin_amdgcn_exp2f(p[nt][e] - msafe);
       lsum += p[nt][e];
     }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = pair_add32(pair_add16(lsum));
   alpha = mrun == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(mrun - mnew);
   lrun = lrun * alpha + lsum;
   mrun = mnew;
@@ -332,8 +330,9 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
     load_next_ids(tn);
     // The queries of tile i + 1 go to LDS as fp16 at step 0 of tile i, from
     // 16 bytes per thread loaded at the last step of the tile before.  Three
-    // buffers: at step 0 of tile i every producer has passed the middle of
-    // the last step of tile i - 1, so none still reads the buffer of tile i - 2.
+    // buffers: at step 0 of tile i every producer has passed the wait for that
+    // stage, which needs the posts made at the ends of all four tails of tile
+    // i - 1, so none still reads the buffer of tile i - 2.
     bf16x8 qld;
     auto load_q = [&](int bh) {
       const int r = fresh(rt), j = r >> 4;
@@ -496,14 +495,25 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
         step_loads(s);
       }
 
-      // ---- the last stage, one 16-token half at a time, so that the first
-      //      half's RoPE can run on the vector ALUs under the second half's
-      //      products; then the tail
+      // ---- the last stage, then the tail.  Its "stored" post goes at the end
+      //      of the tail: the other producers need stage G + 1 only for the
+      //      next tile, after their own tails, and so no branch separates the
+      //      products from the work on their results (the first half's RoPE
+      //      and QK can be scheduled under the second half's products).
       {
         constexpr int s = NR - 1;
         step_begin(s);
+        step_end(s);
+        // this tile's b2 for the consumers (for the group's partial): producer
+        // w writes entries 64 (w % 2) + lane, producers 2 and 3 the values 0
+        // and 1 write (indexed as slot base + lane, the lane offsets the other
+        // writes use; not a branch)
+        {
+          const int ln = fresh(lane);
+          (&L.b2f[i & 1][(slot & 1) * 64])[ln] = bf16_to_f32(b2raw);
+        }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             const bf16x8 bop = coeff_op(s, ks, nt);
@@ -511,26 +521,11 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
             for (int mt = 0; mt < 8; ++mt)
               acc[nt][mt] = mfma16(aop[ks][mt], bop, s == 0 && ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[nt][mt]);
           }
-          if (nt == 0) pipe_post(&L.sync_stored, lane);  // stage G + 1 stored
-        }
-        step_end(s);
-
-        // this tile's b2 for the consumers (for the group's partial), indexed
-        // as slot base + lane, the lane offsets the other writes use
-        {
-          const int ln = fresh(lane);
-          if (slot < kHeadDim / 64) (&L.b2f[i & 1][slot * 64])[ln] = bf16_to_f32(b2raw);
-        }
         // ---- K_pre done: acc[nt][mt][e] = K_pre[t][d], t = 16 nt + col,
         //      d = 32 (mt / 2) + 8 grp + 4 (mt % 2) + e.  Hand the bf16
-        //      operands to the consumer in its register layout.
+        //      operands to the consumer in its register layout, one 16-token
+        //      half at a time (the first half's results come first).
         unsigned char* hb = L.hand[i & 1][slot];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            *reinterpret_cast<u32x4*>(hb + (nt * 4 + ks) * 1024 + lane * 16) =
-                __builtin_bit_cast(u32x4, pack8(acc[nt][2 * ks], acc[nt][2 * ks + 1]));
         // RoPE on packed fp16 pairs of consecutive frequencies: pair (d, d + 64)
         // = m-tiles (mt, mt + 4) of the same lane; the rotation is the chunk
         // start's composed with the offset's.  K_post stays fp16 (relative
@@ -546,6 +541,10 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
         f32x4 zacc[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            *reinterpret_cast<u32x4*>(hb + (nt * 4 + ks) * 1024 + lane * 16) =
+                __builtin_bit_cast(u32x4, pack8(acc[nt][2 * ks], acc[nt][2 * ks + 1]));
           const int cs = 2 * nt + (cl >> 3);
           h2 kp[8][2];  // K_post of this half, [mt][e pair]
 #pragma unroll
@@ -598,6 +597,7 @@ __global__ __launch_bounds__(kPipeThreads, 1) void attend_pipe_kernel(const Atte
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) tokA[nt] = tokB[nt];
         load_next_ids(tnn);
+        pipe_post(&L.sync_stored, lane);  // stage G + 1 stored
         step_loads(s);
       }
       // tile i is handed to the consumers
