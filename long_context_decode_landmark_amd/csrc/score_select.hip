@@ -5,8 +5,6 @@
 // current query and rebuilds only the top-k.  The score of chunk c for KV
 // head h is the maximum over h's query heads j of q_j . L[c]; the k largest
 // are kept, exact ties to the lower chunk id, output in ascending chunk id.
-#include <atomic>
-
 #include "common.h"
 #include "internal.h"
 
@@ -189,130 +187,289 @@ __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_multi_kerne
 // 1024 threads per (sequence, KV head).
 //
 // Thread t owns the `per` consecutive candidates [per t, per t + per), per the
-// smallest power of two with 1024 per >= n_cand.  The keys of the head are
-// staged in LDS once (up to kSelLdsKeys of them; longer lists are re-read from
-// L2 in every pass), transposed: candidate per t + j at word j (1024 + 1) + t,
-// so that the 1024 threads reading their j-th keys touch consecutive words
-// (the extra word per row keeps the staging writes of one wave on different
-// banks).  12-bit first digits spread the fp32 exponent over 4096 bins so few
-// lanes of an LDS atomic hit the same bin; the digit search uses wave-shuffle
-// scans with one LDS exchange.  The compaction counts each thread's keys > T
-// and == T, takes one block-wide exclusive scan of the two counts, and has
-// every thread write its own selected candidates in order: no per-key ballot.
+// smallest power of two with 1024 per >= n_cand.  Lists of up to 32768
+// candidates keep each thread's keys in registers for the whole selection
+// (select_reg_kernel, per a template parameter, so every loop over a
+// thread's keys is unrolled); longer lists re-read them from L2 in every pass
+// (select_l2_kernel).  12-bit first digits spread the fp32 exponent over 4096
+// bins so few lanes of an LDS atomic hit the same bin; the digit search uses
+// DPP wave scans with one LDS exchange.  The compaction counts each
+// thread's keys > T and == T, takes one block-wide exclusive scan of the two
+// counts, and has every thread write its own selected candidates in order:
+// no per-key ballot.
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelBins = 4096;
-constexpr int kSelLdsKeys = 32768;
-constexpr int kSelRow = kSelThreads + 1;          // LDS words per transposed key row
-constexpr int kSelLdsWords = (kSelLdsKeys / kSelThreads) * kSelRow;
+constexpr int kSelRegKeys = 32 * kSelThreads;  // longest list kept in registers
+constexpr int kSelBatch = 8;                   // L2 variant: loads a thread has in flight at once
+constexpr int kSelShift[3] = {20, 8, 0};
+constexpr int kSelBits[3] = {12, 12, 8};
 
-struct SelLds {  // the key array comes last: the L2-reading variant omits it
+struct SelLds {
   uint32_t hist[kSelBins];
   uint32_t wsum[2][kSelWaves];
   uint32_t found[2];
-  alignas(16) uint32_t keys[kSelLdsWords];
 };
-constexpr int kSelBatch = 8;  // loads a thread has in flight at once
+
+// inclusive scan of x over the 64 lanes of a wave, from lane 0 up, on DPP
+// moves: row shifts by 1, 2, 4 and 8 scan each row of 16 lanes (lanes
+// shifted in from outside the row add 0), then the last lane of row 0 is
+// added to row 1 and of row 2 to row 3 (row_bcast:15 on rows 1 and 3), and
+// the last lane of row 1 to rows 2 and 3 (row_bcast:31); six vector adds,
+// no LDS crossbar round trip
+__device__ __forceinline__ uint32_t wave_scan_up(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
 
 // inclusive scan of x over the 64 lanes of a wave, from the highest lane down
-__device__ __forceinline__ uint32_t wave_scan_down(uint32_t x, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_down(x, o);
-    if (lane + o < 64) x += y;
-  }
-  return x;
+__device__ __forceinline__ uint32_t wave_scan_down(uint32_t x) {
+  const uint32_t up = wave_scan_up(x);
+  return __builtin_amdgcn_readlane(up, 63) - up + x;
 }
 
-// inclusive scan of x over the 64 lanes of a wave, from lane 0 up
-__device__ __forceinline__ uint32_t wave_scan_up(uint32_t x, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
+// The digit of one radix pass: the bin D of hist (nbins bins, kSelThreads
+// threads) where the count of keys in higher bins first reaches kk.  Thread t
+// owns bins [bpt t, bpt t + bpt).  Leaves found[0] = D and found[1] = the
+// count in the bins above D, read after the barrier at the end; wsum (one word
+// per wave) is scratch.  hist may be LDS or global memory.
+template <class H>
+__device__ __forceinline__ void pick_digit(H hist, int nbins, uint32_t kk, uint32_t* wsum, uint32_t* found) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bpt = nbins >= kSelThreads ? nbins / kSelThreads : 1;
+  const bool owner = tid * bpt < nbins;
+  uint32_t mine = 0;
+  if (owner)
+    for (int j = 0; j < bpt; ++j) mine += hist[tid * bpt + j];
+  const uint32_t incl = wave_scan_down(mine);  // this lane and above, in the wave
+  if (lane == 0) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t above = incl - mine;
+  for (int w = wave + 1; w < kSelWaves; ++w) above += wsum[w];
+  if (owner) {
+    for (int j = bpt - 1; j >= 0; --j) {
+      const uint32_t c = hist[tid * bpt + j];
+      if (above < kk && kk <= above + c) {
+        found[0] = tid * bpt + j;
+        found[1] = above;
+      }
+      above += c;
+    }
   }
-  return x;
+  __syncthreads();
 }
 
-template <bool kLds>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
+// Exclusive scans over the block, in thread order, of two per-thread counts.
+__device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t (*wsum)[kSelWaves], uint32_t& a_before,
+                                            uint32_t& b_before) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t a_incl = wave_scan_up(a), b_incl = wave_scan_up(b);
+  if (lane == 63) {
+    wsum[0][wave] = a_incl;
+    wsum[1][wave] = b_incl;
+  }
+  __syncthreads();
+  a_before = a_incl - a;
+  b_before = b_incl - b;
+  for (int w = 0; w < wave; ++w) {
+    a_before += wsum[0][w];
+    b_before += wsum[1][w];
+  }
+}
+
+// The selection's common start: pads sel_out past k_eff with -1 and takes
+// every candidate when there are no more than k.  Returns true when done.
+__device__ __forceinline__ bool select_trivial(const int32_t* ids, int32_t* so, int32_t* so2, int n_cand, int k,
+                                               int k_eff) {
+  const int tid = threadIdx.x;
+  if (so2)
+    for (int i = k_eff + tid; i < k; i += kSelThreads) so2[i] = -1;
+  if (n_cand > k) return false;
+  for (int i = tid; i < n_cand; i += kSelThreads) {
+    const int32_t c = ids ? ids[i] : i;
+    so[i] = c;
+    if (so2) so2[i] = c;
+  }
+  return true;
+}
+
+template <int LP>
+__global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
     const uint32_t* __restrict__ keys, const int32_t* __restrict__ cand_ids,
     int32_t* __restrict__ sel, int32_t* __restrict__ sel_out, int n_cand, int k, int n_heads_kv,
     int cache_bmul) {
-  extern __shared__ unsigned char sel_smem[];
-  SelLds& S = *reinterpret_cast<SelLds*>(sel_smem);
+  constexpr int PER = 1 << LP;
+  __shared__ SelLds S;
   const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const size_t head = (size_t)b * n_heads_kv + h;
   const uint32_t* kg = keys + head * (size_t)n_cand;
   const int32_t* ids = cand_ids ? cand_ids + ((size_t)b * cache_bmul * n_heads_kv + h) * (size_t)n_cand : nullptr;
   const int k_eff = min(k, n_cand);
   int32_t* so = sel + head * (size_t)k_eff;
   int32_t* so2 = sel_out ? sel_out + head * (size_t)k : nullptr;
+  if (select_trivial(ids, so, so2, n_cand, k, k_eff)) return;
 
-  if (so2)
-    for (int i = k_eff + tid; i < k; i += kSelThreads) so2[i] = -1;
-  if (n_cand <= k) {  // every candidate is selected
-    for (int i = tid; i < n_cand; i += kSelThreads) {
-      const int32_t c = ids ? ids[i] : i;
-      so[i] = c;
-      if (so2) so2[i] = c;
+  const int i_begin = tid * PER;                         // this thread's first candidate
+  const int cnt = max(0, min(PER, n_cand - i_begin));    // and how many it owns
+  // key j of this thread is in the list when bit j of vmask is set; a wave
+  // whose threads all own PER keys (every wave but the list's last) takes
+  // the loops below without that test (the first pass then has no branch).
+  // (A bit mask, not j < cnt: the compiler would turn that into a run-time
+  // trip count and index the key registers dynamically.)
+  const uint32_t vmask = cnt >= 32 ? 0xffffffffu : (1u << cnt) - 1u;
+  const bool wave_full = __all(cnt == PER);
+  // This thread's keys.  With 16-byte-aligned lists: at most 4 keys per
+  // thread, one 16-byte load each (consecutive lanes, consecutive pieces);
+  // more, through LDS, so that every load instruction of a wave reads
+  // consecutive 16-byte pieces: piece g of the list (owner g / P4, piece
+  // g % P4 of it) goes to slot owner P4 + (piece ^ ((owner >> SW) & (P4 - 1))),
+  // which keeps both the stores and each thread's reads of its own pieces off
+  // shared banks.  Otherwise one key at a time with indices clamped into the
+  // list.  (Keys past the list's end hold anything: vmask excludes them.)
+  uint32_t kx[PER];
+  const bool aligned = (reinterpret_cast<uintptr_t>(kg) & 15) == 0;
+  if constexpr (PER >= 8) {
+    constexpr int P4 = PER / 4;                    // 16-byte pieces per thread
+    constexpr int SW = P4 == 2 ? 3 : P4 == 4 ? 2 : 1;
+    __shared__ u32x4 stage[PER * kSelThreads / 4];
+    if (aligned) {
+      const int n4 = n_cand >> 2, rem = n_cand & 3;
+      const u32x4* kg4 = reinterpret_cast<const u32x4*>(kg);
+      u32x4 v[P4];
+#pragma unroll
+      for (int q = 0; q < P4; ++q) {
+        const int g = tid + kSelThreads * q;
+        if (g < n4) {
+          v[q] = kg4[g];
+        } else {  // the list's last, partial piece (indices clamped), or past the end
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[q][e] = kg[min(4 * g + e, n_cand - 1)];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < P4; ++q) {
+        const int g = tid + kSelThreads * q, o = g / P4, pc = g % P4;
+        if (g < n4 + (rem ? 1 : 0)) stage[o * P4 + (pc ^ ((o >> SW) & (P4 - 1)))] = v[q];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int pc = 0; pc < P4; ++pc) {
+        const u32x4 w = stage[tid * P4 + (pc ^ ((tid >> SW) & (P4 - 1)))];
+        kx[4 * pc] = w[0];
+        kx[4 * pc + 1] = w[1];
+        kx[4 * pc + 2] = w[2];
+        kx[4 * pc + 3] = w[3];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) kx[j] = kg[min(i_begin + j, n_cand - 1)];
     }
-    return;
+  } else if (PER == 4 && cnt == PER && aligned) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(kg + i_begin);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) kx[e] = w[e];
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) kx[j] = kg[min(i_begin + j, n_cand - 1)];
   }
+
+  uint32_t prefix = 0, pmask = 0, kk = (uint32_t)k;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = kSelShift[pass], nbins = 1 << kSelBits[pass];
+    const uint32_t dmask = (uint32_t)nbins - 1;
+    for (int i = tid; i < nbins; i += kSelThreads) S.hist[i] = 0;
+    __syncthreads();
+    if (wave_full) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if ((kx[j] & pmask) == prefix) atomicAdd(&S.hist[(kx[j] >> shift) & dmask], 1u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (((vmask >> j) & 1u) && (kx[j] & pmask) == prefix) atomicAdd(&S.hist[(kx[j] >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    pick_digit(S.hist, nbins, kk, S.wsum[0], S.found);
+    const uint32_t digit = S.found[0];
+    kk -= S.found[1];
+    prefix |= digit << shift;
+    pmask |= dmask << shift;
+    __syncthreads();  // hist, wsum and found are reused next
+  }
+  const uint32_t T = prefix, need = kk;
+
+  // ordered compaction: this thread's counts of keys > T and == T, their
+  // exclusive scans over the block, then this thread's selected candidates
+  uint32_t ngt = 0, neq = 0;
+  if (wave_full) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      ngt += kx[j] > T ? 1u : 0u;
+      neq += kx[j] == T ? 1u : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const bool in = (vmask >> j) & 1u;
+      ngt += (in && kx[j] > T) ? 1u : 0u;
+      neq += (in && kx[j] == T) ? 1u : 0u;
+    }
+  }
+  uint32_t gt_run, eq_run;
+  block_scan2(ngt, neq, S.wsum, gt_run, eq_run);
+  if (gt_run + min(eq_run, need) >= (uint32_t)k_eff || (ngt == 0 && (neq == 0 || eq_run >= need))) return;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool in = (vmask >> j) & 1u;
+    const bool gt = in && kx[j] > T, eq = in && kx[j] == T;
+    if (gt || (eq && eq_run < need)) {
+      const uint32_t pos = gt_run + min(eq_run, need);
+      if (pos < (uint32_t)k_eff) {
+        const int i = i_begin + j;
+        const int32_t c = ids ? ids[i] : i;
+        so[pos] = c;
+        if (so2) so2[pos] = c;
+      }
+    }
+    gt_run += gt ? 1u : 0u;
+    eq_run += eq ? 1u : 0u;
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_l2_kernel(
+    const uint32_t* __restrict__ keys, const int32_t* __restrict__ cand_ids,
+    int32_t* __restrict__ sel, int32_t* __restrict__ sel_out, int n_cand, int k, int n_heads_kv,
+    int cache_bmul) {
+  __shared__ SelLds S;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const size_t head = (size_t)b * n_heads_kv + h;
+  const uint32_t* kg = keys + head * (size_t)n_cand;
+  const int32_t* ids = cand_ids ? cand_ids + ((size_t)b * cache_bmul * n_heads_kv + h) * (size_t)n_cand : nullptr;
+  const int k_eff = min(k, n_cand);
+  int32_t* so = sel + head * (size_t)k_eff;
+  int32_t* so2 = sel_out ? sel_out + head * (size_t)k : nullptr;
+  if (select_trivial(ids, so, so2, n_cand, k, k_eff)) return;
+
   int lp = 0;  // per = 2^lp candidates per thread
   while (((long long)kSelThreads << lp) < n_cand) ++lp;
   const int per = 1 << lp;
   const int i_begin = tid << lp;                                  // this thread's first candidate
   const int cnt = max(0, min(per, n_cand - i_begin));             // and how many it owns
-  if constexpr (kLds) {
-    // Every load of a batch goes out before the first store waits on one:
-    // 16-byte pieces when the list is 16-byte aligned, single keys otherwise.
-    // Indices past the end are clamped to the last element, which is then
-    // stored again with its own value: no branch for the compiler to sink a
-    // load into.
-    auto put = [&](int i, uint32_t v) { S.keys[(i & (per - 1)) * kSelRow + (i >> lp)] = v; };
-    if ((reinterpret_cast<uintptr_t>(kg) & 15) == 0 && n_cand >= 4) {
-      const int n4 = n_cand >> 2;
-      const uint4* kg4 = reinterpret_cast<const uint4*>(kg);
-      for (int i0 = tid; i0 < n4; i0 += kSelThreads * kSelBatch) {
-        uint4 v[kSelBatch];
-#pragma unroll
-        for (int u = 0; u < kSelBatch; ++u) v[u] = kg4[min(i0 + u * kSelThreads, n4 - 1)];
-#pragma unroll
-        for (int u = 0; u < kSelBatch; ++u) {
-          const int i = 4 * min(i0 + u * kSelThreads, n4 - 1);
-          put(i, v[u].x);
-          put(i + 1, v[u].y);
-          put(i + 2, v[u].z);
-          put(i + 3, v[u].w);
-        }
-      }
-      for (int i = 4 * n4 + tid; i < n_cand; i += kSelThreads) put(i, kg[i]);
-    } else {
-      for (int i0 = tid; i0 < n_cand; i0 += kSelThreads * kSelBatch) {
-        uint32_t v[kSelBatch];
-#pragma unroll
-        for (int u = 0; u < kSelBatch; ++u) v[u] = kg[min(i0 + u * kSelThreads, n_cand - 1)];
-#pragma unroll
-        for (int u = 0; u < kSelBatch; ++u) put(min(i0 + u * kSelThreads, n_cand - 1), v[u]);
-      }
-    }
-    __syncthreads();
-  }
-  // key j of this thread (j < cnt)
-  auto key_of = [&](int j) -> uint32_t {
-    if constexpr (kLds) return S.keys[j * kSelRow + tid];
-    else return kg[i_begin + j];
-  };
+  auto key_of = [&](int j) -> uint32_t { return kg[i_begin + j]; };  // key j of this thread (j < cnt)
 
   uint32_t prefix = 0, pmask = 0, kk = (uint32_t)k;
-  constexpr int kShift[3] = {20, 8, 0};
-  constexpr int kBits[3] = {12, 12, 8};
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
-    const int shift = kShift[pass], nbins = 1 << kBits[pass];
+    const int shift = kSelShift[pass], nbins = 1 << kSelBits[pass];
     const uint32_t dmask = (uint32_t)nbins - 1;
     for (int i = tid; i < nbins; i += kSelThreads) S.hist[i] = 0;
     __syncthreads();
@@ -325,40 +482,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         if (j0 + u < cnt && (kx[u] & pmask) == prefix) atomicAdd(&S.hist[(kx[u] >> shift) & dmask], 1u);
     }
     __syncthreads();
-    // thread t owns bins [bpt*t, bpt*t + bpt); the digit D is the bin where
-    // the count of keys in higher bins first reaches kk
-    const int bpt = nbins >= kSelThreads ? nbins / kSelThreads : 1;
-    const bool owner = tid * bpt < nbins;
-    uint32_t mine = 0;
-    if (owner)
-      for (int j = 0; j < bpt; ++j) mine += S.hist[tid * bpt + j];
-    const uint32_t incl = wave_scan_down(mine, lane);  // this lane and above, in the wave
-    if (lane == 0) S.wsum[0][wave] = incl;
-    __syncthreads();
-    uint32_t above = incl - mine;
-    for (int w = wave + 1; w < kSelWaves; ++w) above += S.wsum[0][w];
-    if (owner) {
-      for (int j = bpt - 1; j >= 0; --j) {
-        const uint32_t c = S.hist[tid * bpt + j];
-        if (above < kk && kk <= above + c) {
-          S.found[0] = tid * bpt + j;
-          S.found[1] = above;
-        }
-        above += c;
-      }
-    }
-    __syncthreads();
+    pick_digit(S.hist, nbins, kk, S.wsum[0], S.found);
     const uint32_t digit = S.found[0];
     kk -= S.found[1];
     prefix |= digit << shift;
     pmask |= dmask << shift;
-    __syncthreads();  // hist and wsum are reused next
+    __syncthreads();  // hist, wsum and found are reused next
   }
   const uint32_t T = prefix, need = kk;
 
-  // ordered compaction: this thread's counts of keys > T and == T, their
-  // exclusive scans over the block in thread order, then this thread's
-  // selected candidates in order
   uint32_t ngt = 0, neq = 0;
   for (int j0 = 0; j0 < cnt; j0 += kSelBatch) {
     uint32_t kx[kSelBatch];
@@ -371,17 +503,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       neq += (in && kx[u] == T) ? 1u : 0u;
     }
   }
-  const uint32_t gt_incl = wave_scan_up(ngt, lane), eq_incl = wave_scan_up(neq, lane);
-  if (lane == 63) {
-    S.wsum[0][wave] = gt_incl;
-    S.wsum[1][wave] = eq_incl;
-  }
-  __syncthreads();
-  uint32_t gt_run = gt_incl - ngt, eq_run = eq_incl - neq;  // counts of the threads before this one
-  for (int w = 0; w < wave; ++w) {
-    gt_run += S.wsum[0][w];
-    eq_run += S.wsum[1][w];
-  }
+  uint32_t gt_run, eq_run;
+  block_scan2(ngt, neq, S.wsum, gt_run, eq_run);
   if (gt_run + min(eq_run, need) >= (uint32_t)k_eff || (ngt == 0 && (neq == 0 || eq_run >= need))) return;
   for (int j0 = 0; j0 < cnt; j0 += kSelBatch) {
     uint32_t kx[kSelBatch];
@@ -461,32 +584,13 @@ __global__ __launch_bounds__(kSplitThreads) void split_hist_kernel(const uint32_
 __global__ __launch_bounds__(kSelThreads) void split_digit_kernel(SplitWs w, int shift, uint32_t dmask) {
   __shared__ uint32_t wsum[kSelWaves];
   __shared__ uint32_t found[2];
-  const int l = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l = blockIdx.x, tid = threadIdx.x;
   uint32_t* gh = w.hist + (size_t)l * kSelBins;
   const int nbins = (int)dmask + 1;
   const uint32_t kk = w.state[4 * l + 2];
+  pick_digit(gh, nbins, kk, wsum, found);
   const int bpt = nbins >= kSelThreads ? nbins / kSelThreads : 1;
-  const bool owner = tid * bpt < nbins;
-  uint32_t mine = 0;
-  if (owner)
-    for (int j = 0; j < bpt; ++j) mine += gh[tid * bpt + j];
-  const uint32_t incl = wave_scan_down(mine, lane);
-  if (lane == 0) wsum[wave] = incl;
-  __syncthreads();
-  uint32_t above = incl - mine;
-  for (int v = wave + 1; v < kSelWaves; ++v) above += wsum[v];
-  if (owner) {
-    for (int j = bpt - 1; j >= 0; --j) {
-      const uint32_t c = gh[tid * bpt + j];
-      if (above < kk && kk <= above + c) {
-        found[0] = tid * bpt + j;
-        found[1] = above;
-      }
-      above += c;
-    }
-  }
-  __syncthreads();
-  if (owner)
+  if (tid * bpt < nbins)
     for (int j = 0; j < bpt; ++j) gh[tid * bpt + j] = 0u;
   if (tid == 0) {
     w.state[4 * l + 0] |= found[0] << shift;
@@ -674,25 +778,24 @@ hipError_t launch_select(const uint32_t* keys, const int32_t* cand_ids, int32_t*
                          int cache_bmul) {
   if (n_cand <= 0 && !sel_out) return hipSuccess;
   const dim3 grid(hkv, nb), block(kSelThreads);
-  // dynamic LDS above 64 KiB must be allowed once per device (the attribute
-  // belongs to the function on the current device); bit d: done on device d
-  static std::atomic<uint64_t> attr_set{0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-  const uint64_t bit = dev >= 0 && dev < 64 ? 1ull << dev : 0;  // devices past 63: set on every call
-  if (!bit || !(attr_set.load(std::memory_order_acquire) & bit)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(select_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SelLds)) != hipSuccess)
-      return hipErrorInvalidValue;
-    attr_set.fetch_or(bit, std::memory_order_release);
+  if (n_cand > kSelRegKeys) {
+    hipLaunchKernelGGL(select_l2_kernel, grid, block, 0, st, keys, cand_ids, sel, sel_out, n_cand, k, hkv, cache_bmul);
+    return hipGetLastError();
   }
-  if (n_cand <= kSelLdsKeys) {
-    hipLaunchKernelGGL(select_kernel<true>, grid, block, sizeof(SelLds), st, keys, cand_ids, sel, sel_out,
-                       n_cand, k, hkv, cache_bmul);
-  } else {
-    hipLaunchKernelGGL(select_kernel<false>, grid, block, sizeof(SelLds) - kSelLdsWords * 4, st, keys,
-                       cand_ids, sel, sel_out, n_cand, k, hkv, cache_bmul);
+  int lp = 0;  // 2^lp candidates per thread
+  while ((kSelThreads << lp) < n_cand) ++lp;
+#define LOWRAM_SEL(LP)                                                                                  \
+  hipLaunchKernelGGL(select_reg_kernel<LP>, grid, block, 0, st, keys, cand_ids, sel, sel_out, n_cand, k, \
+                     hkv, cache_bmul)
+  switch (lp) {
+    case 0: LOWRAM_SEL(0); break;
+    case 1: LOWRAM_SEL(1); break;
+    case 2: LOWRAM_SEL(2); break;
+    case 3: LOWRAM_SEL(3); break;
+    case 4: LOWRAM_SEL(4); break;
+    default: LOWRAM_SEL(5); break;
   }
+#undef LOWRAM_SEL
   return hipGetLastError();
 }
 

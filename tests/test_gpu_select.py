@@ -6,11 +6,13 @@ scores next to the k-th stay far apart (checked: well beyond fp32 rounding).  Th
 with ties to the lower chunk id are then unique and the GPU's fp32 scores
 order them as the oracle's fp64 ones do: the selection must equal
 steps.select_topk exactly, with no tie band.  The list lengths cover the
-variant that stages the keys in LDS at 32, 8 and 1 keys per thread (32736,
-5000 and 1000 candidates; 5000 is not a multiple of its ranges), the variant
-that re-reads them from L2 (40960 candidates, 64 per thread), k above the
-candidate count, and a selection that ends inside a group of up to ~5800
-equal scores (7 distinct rows).
+variant that keeps each thread's keys in registers at 32, 8 and 1 keys per
+thread (32736, 5000 and 1000 candidates; 5000 is not a multiple of its
+ranges), 8191 candidates at 8 per thread (the first list's last 16-byte piece
+is partial, and the other lists start off 16-byte alignment, so their keys are
+loaded one at a time), the variant that re-reads them from L2 (40960
+candidates, 64 per thread), k above the candidate count, and a selection that
+ends inside a group of up to ~5800 equal scores (7 distinct rows).
 """
 import numpy as np
 import pytest
@@ -31,10 +33,11 @@ from test_gpu_fullsize import draw_batch, host  # noqa: E402
 
 
 @pytest.mark.parametrize("name,n_cand,window,topk,n_rows", [
-    ("lds_32_per_thread", 32736, 256, 1024, 7),
-    ("lds_32_per_thread_60_rows", 32736, 256, 1024, 60),
-    ("lds_8_per_thread_ragged", 5000, 64, 45, 11),
-    ("lds_1_per_thread", 1000, 64, 32, 5),
+    ("regs_32_per_thread", 32736, 256, 1024, 7),
+    ("regs_32_per_thread_60_rows", 32736, 256, 1024, 60),
+    ("regs_8_per_thread_ragged", 5000, 64, 45, 11),
+    ("regs_8_per_thread_unaligned", 8191, 64, 300, 13),
+    ("regs_1_per_thread", 1000, 64, 32, 5),
     ("l2_64_per_thread", 40960, 256, 1024, 7),
     ("k_above_candidates", 300, 64, 512, 3),
 ])
