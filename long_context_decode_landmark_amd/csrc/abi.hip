@@ -27,6 +27,9 @@ bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p
 // a multiple of 8 workgroups, so the limit is the largest multiple of 8 below
 // (2^32 - 1) / 256.
 constexpr int64_t kMaxGrid1D = ((int64_t)0xFFFFFFFF / 256) & ~(int64_t)7;
+// The merge: one 512-thread workgroup per (sequence, query head), also a
+// 1-D grid padded to a multiple of 8.
+constexpr int64_t kMaxMergeGrid = ((int64_t)0xFFFFFFFF / 512) & ~(int64_t)7;
 
 struct Plan {
   // n_split: partial slots per head of the 4-wave kernel (one per tile);
@@ -71,6 +74,7 @@ int check_shape(const lowram_shape* s) {
   const int64_t k_eff = s->n_cand < s->topk ? s->n_cand : s->topk;
   const int64_t tiles = (k_eff + kAttChunksWG - 1) / kAttChunksWG + (s->window + kAttTokWG - 1) / kAttTokWG;
   if ((int64_t)s->batch * s->n_heads_kv * tiles > kMaxGrid1D) return LOWRAM_ERR_UNSUPPORTED;
+  if ((int64_t)s->batch * s->n_heads_q > kMaxMergeGrid) return LOWRAM_ERR_UNSUPPORTED;
   // nothing to attend: no candidate chunk and no window token gives no split
   if (s->n_cand == 0 && s->window == 0) return LOWRAM_ERR_SHAPE;
   return LOWRAM_OK;
@@ -334,6 +338,7 @@ int check_dense(const dense_shape* s) {
   if ((int64_t)s->batch * s->n_heads_kv * ((s->ctx_len + kDenseTokPerSplit - 1) / kDenseTokPerSplit) >
       kMaxGrid1D)
     return LOWRAM_ERR_UNSUPPORTED;
+  if ((int64_t)s->batch * s->n_heads_q > kMaxMergeGrid) return LOWRAM_ERR_UNSUPPORTED;
   return LOWRAM_OK;
 }
 

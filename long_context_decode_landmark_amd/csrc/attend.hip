@@ -741,14 +741,20 @@ constexpr int kMergePhBatch = 8;  // PH groups a thread has in flight (per half)
 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __restrict__ part,
                                                               uint16_t* __restrict__ out, int hkv,
-                                                              int g, int n_split, MergePH phm) {
+                                                              int g, int n_split, MergePH phm, int n_blocks) {
   __shared__ float wgt[kMergeMaxSplits];
   __shared__ float red[3][kHeadDim];
   __shared__ float phc[2][kHidden];
   __shared__ float inv_l;
   const int tid = threadIdx.x, d = tid & (kHeadDim - 1), sg = tid >> 7;
-  const int j = blockIdx.x;
-  const size_t head = (size_t)blockIdx.z * hkv + blockIdx.y;
+  // one workgroup per (sequence, KV head, query head j), j fastest; the
+  // workgroups of one (sequence, KV head) go to one XCD, so that the head's
+  // W2 rows are fetched into that XCD's L2 once and shared
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  if (lb >= n_blocks) return;
+  const int j = lb % g, hb = lb / g;
+  const int bq = hb / hkv, hq = hb - bq * hkv;
+  const size_t head = (size_t)hb;
   const size_t st = (size_t)g * kPartStride;  // between splits
   const float* pj = part + head * (size_t)n_split * st + (size_t)j * kPartStride;
   const int ns = n_split;
@@ -769,7 +775,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float* __res
   const float* pp = phm.ph + head * (size_t)phm.ph_stride * phs + (size_t)j * kHidden + u;
   float hv[kMergePhBatch];
   if (nph > 0) {
-    const size_t chead = (size_t)blockIdx.z * phm.cache_bmul * hkv + blockIdx.y;
+    const size_t chead = (size_t)bq * phm.cache_bmul * hkv + hq;
     const uint16_t* w2row = phm.w2 + (chead * kHeadDim + d) * kHidden + 64 * sg;
 #pragma unroll
     for (int k = 0; k < 8; ++k) w2v[k] = load_bf16x8(w2row + 8 * k);
@@ -871,7 +877,12 @@ hipError_t launch_merge(const float* part, uint16_t* out, int nb, int hkv, int g
   if (phm.n_ph_used > 0 && (!phm.ph || !phm.w2 || phm.n_ph_used > n_split || phm.ph_stride < phm.n_ph_used ||
                             phm.n_ph_used % 4))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_kernel, dim3(g, hkv, nb), dim3(kMergeThreads), 0, st, part, out, hkv, g, n_split, phm);
+  const long long n_blocks = (long long)g * hkv * nb;
+  if (n_blocks <= 0) return hipSuccess;
+  if (n_blocks > ((long long)0xFFFFFFFF / kMergeThreads & ~7LL)) return hipErrorInvalidValue;  // work-items in 32 bits
+  const int padded = (int)((n_blocks + 7) & ~7LL);  // a multiple of the 8 XCDs
+  hipLaunchKernelGGL(merge_kernel, dim3(padded), dim3(kMergeThreads), 0, st, part, out, hkv, g, n_split, phm,
+                     (int)n_blocks);
   return hipGetLastError();
 }
 

@@ -73,6 +73,8 @@ def ws_bytes(**kw):
     (dict(n_heads_q=65536, n_heads_kv=65536), -3),
     # (sequence, KV head, tile) workgroups of 256 work-items: at most (2^32 - 1) / 256, padded to 8
     (dict(batch=1024, n_heads_q=32, n_heads_kv=16, prefix_len=0, n_cand=0, n_resid=0, window=1025 * 128), -3),
+    # the merge: (sequence, query head) workgroups of 512 work-items, at most (2^32 - 1) / 512, padded to 8
+    (dict(batch=32769, n_heads_q=256, n_heads_kv=16), -3),
     (dict(n_cand=0, window=0), -2),     # a prefix but no candidate and no window: nothing to attend
 ])
 def test_workspace_bytes_rejects_shapes(kw, code):
@@ -171,8 +173,10 @@ def test_shapes_at_the_grid_limits_are_accepted():
     assert ws_bytes(batch=1023, n_heads_q=32, n_heads_kv=16, prefix_len=0, n_cand=0, n_resid=0,
                     window=1025 * 128) > 0
     assert ws_bytes(n_cand=0, window=1) > 0
+    assert ws_bytes(batch=32767, n_heads_q=256, n_heads_kv=16) > 0
     assert native.dense_workspace_bytes(native.dense_shape(65535, 100, 8, 2)) > 0
     assert native.dense_workspace_bytes(native.dense_shape(1023, 1025 * 2048, 32, 16)) > 0
+    assert native.dense_workspace_bytes(native.dense_shape(32767, 100, 256, 16)) > 0
 
 
 def call_noalloc(s, cache, q=FakeTensor(0x7000000000), out=FakeTensor(0x7100000000)):
@@ -214,7 +218,8 @@ def test_dense_rejects():
         native.dense_workspace_bytes(native.dense_shape(1, 100, 7, 2))
     assert e.value.status == -2
     for bad in (native.dense_shape(65536, 100, 8, 2),          # grid dimension limit
-                native.dense_shape(1024, 1025 * 2048, 32, 16)):  # over (2^32 - 1) / 256 workgroups
+                native.dense_shape(1024, 1025 * 2048, 32, 16),   # over (2^32 - 1) / 256 workgroups
+                native.dense_shape(32769, 100, 256, 16)):        # merge: over (2^32 - 1) / 512 workgroups
         with pytest.raises(native.LowramError) as e:
             native.dense_workspace_bytes(bad)
         assert e.value.status == -3
