@@ -29,20 +29,26 @@ namespace lowram {
 #ifndef LOWRAM_SCORE_WG_PER_CU
 #define LOWRAM_SCORE_WG_PER_CU 2
 #endif
+// NBW: batches of 64 landmark rows per wave (a workgroup scores 256 NBW
+// chunks), a template parameter so that the batch loop is straight-line code
+template <int NBW>
 __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ landmark,
     uint32_t* __restrict__ keys, float* __restrict__ scores_out, int n_cand, int n_heads_q,
-    int n_heads_kv, int chunks_per_wg, int cache_bmul, int lm_rows) {
+    int n_heads_kv, int cache_bmul, int lm_rows) {
+  constexpr int chunks_per_wg = 256 * NBW;
   const int b = blockIdx.z, h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, col = lane & 15;
   const int g = n_heads_q / n_heads_kv;
 
+  // the KV head's queries as the A operand (rows j < g; the loads are
+  // unconditional, row clamped, and the rows from g on zeroed after them, so
+  // that no wait on them precedes the landmark loads)
   bf16x8 qa[4];
   const uint16_t* qb = q + ((size_t)b * n_heads_q + (size_t)h * g) * kHeadDim;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    qa[ks] = col < g ? load_bf16x8(qb + col * kHeadDim + 32 * ks + 8 * grp) : zero_bf16x8();
+  for (int ks = 0; ks < 4; ++ks) qa[ks] = load_bf16x8(qb + min(col, g - 1) * kHeadDim + 32 * ks + 8 * grp);
 
   const size_t head = (size_t)b * n_heads_kv + h;
   const uint16_t* lm = landmark + ((size_t)b * cache_bmul * n_heads_kv + h) * (size_t)lm_rows * kHeadDim;
@@ -50,14 +56,24 @@ __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
   float* sout = scores_out ? scores_out + head * (size_t)n_cand : nullptr;
   const int c_begin = blockIdx.x * chunks_per_wg;
   const int c_end = min(n_cand, c_begin + chunks_per_wg);
+  // this workgroup's chunks of the outputs as buffer resources: writes past
+  // c_end are dropped by the range check, so the writes need no branch (no
+  // score output: a zero-length range, every write dropped)
+  const uint32_t out_bytes = (uint32_t)max(0, c_end - c_begin) * 4u;
+  const __amdgpu_buffer_rsrc_t kbuf = buffer_rsrc(kout + c_begin, out_bytes);
+  const __amdgpu_buffer_rsrc_t sbuf = sout ? buffer_rsrc(sout + c_begin, out_bytes) : buffer_rsrc(kout + c_begin, 0u);
 
   // Landmark rows reach the MFMA through a per-wave LDS tile.  Each load
   // instruction takes 4 whole rows (1 KiB contiguous) with the non-temporal
   // policy (every 128-byte line is consumed whole by the instruction that
   // reads it); piece p of row r is stored at piece p ^ (r & 15), so that both
   // the stores and the B-operand reads (16 rows, one 16-byte piece each) are
-  // conflict-free.  The next 64 rows of the wave are in flight in registers
-  // while the current 64 are multiplied.
+  // conflict-free.  Two batches of 64 rows are in flight per wave, in two
+  // register buffers that take turns: a batch goes to LDS, its buffer is
+  // refilled with the batch two ahead, and the batch is multiplied while the
+  // other buffer's loads fly.  Loads and writes are unconditional (rows past
+  // the list are clamped to its last one, writes past c_end are dropped), so
+  // the in-order wait before a batch's stores covers that batch's loads only.
   __shared__ __attribute__((aligned(16))) unsigned char tile[4][64 * 256];
   unsigned char* my = tile[wave];
   auto load_rows = [&](int c0, u32x4 (&v)[16]) {
@@ -67,16 +83,22 @@ __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
       v[i] = load_nt16(lm + (size_t)cc * kHeadDim + 8 * col);
     }
   };
-  u32x4 nxt[16];
-  int c0 = c_begin + wave * 64;
-  if (c0 < c_end) load_rows(c0, nxt);
-  for (; c0 < c_end; c0 += 256) {
+  u32x4 rbuf[2][16];
+  const int cw = c_begin + wave * 64;  // this wave's first row
+  load_rows(cw, rbuf[0]);
+  if constexpr (NBW > 1) load_rows(cw + 256, rbuf[1]);
+  if (col >= g)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qa[ks] = zero_bf16x8();
+#pragma unroll
+  for (int bi = 0; bi < NBW; ++bi) {
+    const int c0 = cw + 256 * bi;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 4 * i + grp;
-      *reinterpret_cast<u32x4*>(my + r * 256 + 16 * (col ^ (r & 15))) = nxt[i];
+      *reinterpret_cast<u32x4*>(my + r * 256 + 16 * (col ^ (r & 15))) = rbuf[bi & 1][i];
     }
-    if (c0 + 256 < c_end) load_rows(c0 + 256, nxt);
+    if (bi + 2 < NBW) load_rows(c0 + 512, rbuf[bi & 1]);
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -91,11 +113,10 @@ __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
         if (4 * grp + e < g) s = fmaxf(s, acc[e]);
       s = fmaxf(s, __shfl_xor(s, 16));
       s = fmaxf(s, __shfl_xor(s, 32));
-      const int c = c0 + 16 * gi + col;
-      if (grp == 0 && c < c_end) {
-        kout[c] = score_key(s);
-        if (sout) sout[c] = s;
-      }
+      // (the four lanes of a chunk hold the same maximum and write it alike)
+      const uint32_t off = (uint32_t)(c0 + 16 * gi + col - c_begin) * 4u;
+      __builtin_amdgcn_raw_buffer_store_b32(score_key(s), kbuf, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), sbuf, off, 0, 0);
     }
   }
 }
@@ -759,8 +780,17 @@ hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* k
   while ((long long)((n_cand + cpw - 1) / cpw) * heads > LOWRAM_SCORE_MAX_WG && cpw < 4096) cpw *= 2;
   dim3 grid((n_cand + cpw - 1) / cpw, hkv, qblocks);
   if (!multi) {
-    hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, st, q, landmark, keys, scores_out,
-                       n_cand, hq, hkv, cpw, cache_bmul, lm_rows);
+#define LOWRAM_SCORE(NBW)                                                                              \
+  hipLaunchKernelGGL(score_kernel<NBW>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, \
+                     hkv, cache_bmul, lm_rows)
+    switch (cpw / 256) {
+      case 1: LOWRAM_SCORE(1); break;
+      case 2: LOWRAM_SCORE(2); break;
+      case 4: LOWRAM_SCORE(4); break;
+      case 8: LOWRAM_SCORE(8); break;
+      default: LOWRAM_SCORE(16); break;
+    }
+#undef LOWRAM_SCORE
   } else {
     switch (g) {
       case 1: hipLaunchKernelGGL(score_multi_kernel<1>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, hkv, cpw, nb, lm_rows); break;
