@@ -272,7 +272,8 @@ __device__ __forceinline__ void pick_digit(H hist, int nbins, uint32_t kk, uint3
   if (lane == 0) wsum[wave] = incl;
   __syncthreads();
   uint32_t above = incl - mine;
-  for (int w = wave + 1; w < kSelWaves; ++w) above += wsum[w];
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) above += w > wave ? wsum[w] : 0u;  // (independent reads, not a loop of round trips)
   if (owner) {
     for (int j = bpt - 1; j >= 0; --j) {
       const uint32_t c = hist[tid * bpt + j];
@@ -298,10 +299,24 @@ __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t (*w
   __syncthreads();
   a_before = a_incl - a;
   b_before = b_incl - b;
-  for (int w = 0; w < wave; ++w) {
-    a_before += wsum[0][w];
-    b_before += wsum[1][w];
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    a_before += w < wave ? wsum[0][w] : 0u;
+    b_before += w < wave ? wsum[1][w] : 0u;
   }
+}
+
+// minimum of x over the 64 lanes of a wave (wave-uniform result): DPP row
+// shifts take each row of 16 lanes to its minimum in lane 15 of the row
+// (a lane with no source keeps its own value), then the four rows meet in
+// scalar registers
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  return min(min(__builtin_amdgcn_readlane(x, 15), __builtin_amdgcn_readlane(x, 31)),
+             min(__builtin_amdgcn_readlane(x, 47), __builtin_amdgcn_readlane(x, 63)));
 }
 
 // The selection's common start: pads sel_out past k_eff with -1 and takes
@@ -401,6 +416,34 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
     for (int j = 0; j < PER; ++j) kx[j] = kg[min(i_begin + j, n_cand - 1)];
   }
 
+  // A lower bound lb on the k-th largest key, so that the histograms skip
+  // keys that cannot be selected (the first pass's 12 bits are mostly the
+  // fp32 exponent, and its atomics crowd into few bins).  Take each thread's
+  // r-th largest key (r = 1 or 2), minimised over the m threads that own at
+  // least r keys: those threads hold m r keys at or above the minimum, so
+  // for k <= m r the k-th largest is at or above it too.  A key below lb
+  // lies below the threshold T, in a bin no higher than T's: leaving it out
+  // changes neither the counts above T's bin nor which bin reaches k first,
+  // in any pass.  (lb = 0 when k exceeds both products.)
+  uint32_t lb = 0;
+  const int m1 = min(kSelThreads, (n_cand + PER - 1) / PER);
+  const int m2 = min(kSelThreads, n_cand / PER + (n_cand % PER >= 2 ? 1 : 0));
+  const int r = k <= m1 ? 1 : k <= 2 * m2 ? 2 : 0;  // uniform over the workgroup
+  {
+    if (r > 0) {
+      uint32_t t1 = 0, t2 = 0;  // this thread's largest and second largest key
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const uint32_t x = ((vmask >> j) & 1u) ? kx[j] : 0u;
+        t2 = max(t2, min(t1, x));
+        t1 = max(t1, x);
+      }
+      const uint32_t v = cnt < r ? 0xffffffffu : r == 1 ? t1 : t2;
+      const uint32_t wm = wave_min(v);
+      if ((tid & 63) == 0) S.wsum[1][tid >> 6] = wm;  // read after the first pass's barrier
+    }
+  }
+
   uint32_t prefix = 0, pmask = 0, kk = (uint32_t)k;
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
@@ -408,14 +451,20 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
     const uint32_t dmask = (uint32_t)nbins - 1;
     for (int i = tid; i < nbins; i += kSelThreads) S.hist[i] = 0;
     __syncthreads();
+    if (pass == 0 && r > 0) {
+      lb = 0xffffffffu;
+#pragma unroll
+      for (int w = 0; w < kSelWaves; ++w) lb = min(lb, S.wsum[1][w]);
+    }
     if (wave_full) {
 #pragma unroll
       for (int j = 0; j < PER; ++j)
-        if ((kx[j] & pmask) == prefix) atomicAdd(&S.hist[(kx[j] >> shift) & dmask], 1u);
+        if ((kx[j] & pmask) == prefix && kx[j] >= lb) atomicAdd(&S.hist[(kx[j] >> shift) & dmask], 1u);
     } else {
 #pragma unroll
       for (int j = 0; j < PER; ++j)
-        if (((vmask >> j) & 1u) && (kx[j] & pmask) == prefix) atomicAdd(&S.hist[(kx[j] >> shift) & dmask], 1u);
+        if (((vmask >> j) & 1u) && (kx[j] & pmask) == prefix && kx[j] >= lb)
+          atomicAdd(&S.hist[(kx[j] >> shift) & dmask], 1u);
     }
     __syncthreads();
     pick_digit(S.hist, nbins, kk, S.wsum[0], S.found);
@@ -446,22 +495,42 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
   }
   uint32_t gt_run, eq_run;
   block_scan2(ngt, neq, S.wsum, gt_run, eq_run);
-  if (gt_run + min(eq_run, need) >= (uint32_t)k_eff || (ngt == 0 && (neq == 0 || eq_run >= need))) return;
+  // Each thread puts its selected candidates' list indices at their output
+  // positions; up to kSelBins of them go to LDS (the histogram's space, free
+  // after the last pass) and then out in one coalesced pass, with the id
+  // lookup done there; longer outputs are written directly.
+  const bool staged = k_eff <= kSelBins;
+  const bool mine = !(gt_run + min(eq_run, need) >= (uint32_t)k_eff || (ngt == 0 && (neq == 0 || eq_run >= need)));
+  if (mine) {
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const bool in = (vmask >> j) & 1u;
-    const bool gt = in && kx[j] > T, eq = in && kx[j] == T;
-    if (gt || (eq && eq_run < need)) {
-      const uint32_t pos = gt_run + min(eq_run, need);
-      if (pos < (uint32_t)k_eff) {
-        const int i = i_begin + j;
-        const int32_t c = ids ? ids[i] : i;
-        so[pos] = c;
-        if (so2) so2[pos] = c;
+    for (int j = 0; j < PER; ++j) {
+      const bool in = (vmask >> j) & 1u;
+      const bool gt = in && kx[j] > T, eq = in && kx[j] == T;
+      if (gt || (eq && eq_run < need)) {
+        const uint32_t pos = gt_run + min(eq_run, need);
+        if (pos < (uint32_t)k_eff) {
+          const int i = i_begin + j;
+          if (staged) {
+            S.hist[pos] = (uint32_t)i;
+          } else {
+            const int32_t c = ids ? ids[i] : i;
+            so[pos] = c;
+            if (so2) so2[pos] = c;
+          }
+        }
       }
+      gt_run += gt ? 1u : 0u;
+      eq_run += eq ? 1u : 0u;
     }
-    gt_run += gt ? 1u : 0u;
-    eq_run += eq ? 1u : 0u;
+  }
+  if (staged) {
+    __syncthreads();
+    for (int p = tid; p < k_eff; p += kSelThreads) {
+      const int i = (int)S.hist[p];
+      const int32_t c = ids ? ids[i] : i;
+      so[p] = c;
+      if (so2) so2[p] = c;
+    }
   }
 }
 
