@@ -62,10 +62,10 @@ TRAFFIC_FILES = {
     ("c4_eq_int4_evict_262k", 16): os.path.join(ROOT, "profiles", "decode_c4_int4_evict_262k_b16_hbm_traffic.txt"),
 }
 KERNEL_SOURCES = {
-    "attend": ("attend.hip", "attend_pipe.hip", "attend_ops.h", "common.h", "internal.h"),
-    "score": ("score_select.hip", "common.h", "internal.h"),
-    "select": ("score_select.hip", "common.h", "internal.h"),
-    "merge": ("attend.hip", "common.h", "internal.h"),
+    "attend": ("attend.hip", "attend_pipe.hip", "attend_ops.h", "window.h", "common.h", "internal.h"),
+    "score": ("score_select.hip", "window.h", "common.h", "internal.h"),
+    "select": ("score_select.hip", "window.h", "common.h", "internal.h"),
+    "merge": ("attend.hip", "window.h", "common.h", "internal.h"),
     "predict": ("build.hip", "common.h", "internal.h"),
     "proj": ("build.hip", "common.h", "internal.h"),
 }
@@ -161,14 +161,16 @@ def copy_probe(mib):
     print(f"copy probe: 3 copies of {n} bytes", file=sys.stderr)
 
 
-def algorithmic(cfg, nb):
+def algorithmic(cfg, nb, window_stage="attend"):
     """Algorithmic HBM bytes and MFMA flops of one layer for `nb` sequences.
 
     Per (sequence, layer): landmarks read once; coefficients of the k*S
     selected tokens per KV head; this layer's basis blocks and MLP weights;
     residual rows (and indices, chunk offsets) of the selected tokens at the
     stored density; the exact window; q in, out.  Flops: landmark scores,
-    reconstruction, the two MLP layers, attention.
+    reconstruction, the two MLP layers, attention.  The window's bytes and
+    flops are counted in the stage whose launch runs its tiles
+    (window_stage: "attend", or "score" when they ride in the score grid).
     """
     Hkv, Hq, d, H, r, S = cfg.n_heads_kv, cfg.n_heads_q, cfg.head_dim, cfg.mlp_hidden, cfg.rank, cfg.chunk
     k = min(cfg.topk, cfg.n_cand)
@@ -179,15 +181,33 @@ def algorithmic(cfg, nb):
     b = {}
     b["score"] = cfg.n_cand * Hkv * d * 2 + (cfg.n_cand * Hkv * 4 if cfg.evict else 0) + Hq * d * 2
     b["attend"] = (Hkv * kS * r * s_c + Hkv * r * d * 2 + Hkv * (2 * d * H + H + d) * 2
-                   + Hkv * kS * rho * (s_r + 4) + Hkv * k * 8 + 2 * Hkv * cfg.window * d * 2 + Hq * d * 2)
+                   + Hkv * kS * rho * (s_r + 4) + Hkv * k * 8 + Hq * d * 2)
     b["merge"] = Hq * d * 2
     b["select"] = 0.0
     f = {
         "score": 2.0 * Hq * cfg.n_cand * d,
-        "attend": 2.0 * Hkv * kS * r * d + 4.0 * Hkv * kS * d * H + 4.0 * Hq * (kS + cfg.window) * d,
+        "attend": 2.0 * Hkv * kS * r * d + 4.0 * Hkv * kS * d * H + 4.0 * Hq * kS * d,
         "select": 0.0, "merge": 0.0,
     }
+    b[window_stage] += 2 * Hkv * cfg.window * d * 2
+    f[window_stage] += 4.0 * Hq * cfg.window * d
     return {kk: v * nb for kk, v in b.items()}, {kk: v * nb for kk, v in f.items()}
+
+
+def window_stage(cfg, nb):
+    """The stage whose launch runs the exact window's tiles in this process's
+    decode step (the library's plan for this device, with the same
+    LOWRAM_PIPE_CUS / LOWRAM_ATTEND overrides the library reads)."""
+    import torch
+
+    from long_context_decode_landmark_amd import native
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    env_cu = os.environ.get("LOWRAM_PIPE_CUS", "")
+    if env_cu.isdigit() and 1 <= int(env_cu) <= 65536:
+        n_cu = int(env_cu)
+    mode = {"pipe": 1, "wave": 2}.get(os.environ.get("LOWRAM_ATTEND", ""), 0)
+    plan = native.decode_plan(native.make_shape(cfg, batch=nb), n_cu, mode)
+    return "score" if plan["window_kernel"] == 1 else "attend"
 
 
 def build_device_cache(cfg, nb, n_layers, seed, dev, q_nb=None):
@@ -854,7 +874,7 @@ def main():
     # (the same launches; the eager pass, with HIP events between kernels,
     # gives the per-kernel times)
     step_ms = graph_ms if graph_ms is not None else eager_ms
-    byts, flops = algorithmic(cfg, nb)
+    byts, flops = algorithmic(cfg, nb, window_stage(cfg, nb))
     dom = max(KERNELS, key=lambda k: kern[k])
     t_dom = kern[dom] * 1e-3
     inten = flops[dom] / max(byts[dom], 1.0)

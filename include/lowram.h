@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LOWRAM_ABI_VERSION 2
+#define LOWRAM_ABI_VERSION 3
 
 enum {
   LOWRAM_OK = 0,
@@ -199,11 +199,16 @@ int lowram_decode_step_noalloc(const lowram_shape* shape, const lowram_layer_cac
  *                    combines, window tiles included
  *   reserved_slots   partial slots per (sequence, KV head) in the workspace
  *                    (lowram_workspace_bytes), >= partial_slots
+ *   window_kernel    where the exact window's tiles run: 0 no window, 1 as
+ *                    extra workgroups of the landmark-score launch (with the
+ *                    producer/consumer kernel), 2 in a 4-wave kernel launch
+ *                    (field added in ABI version 3)
  * Returns LOWRAM_ERR_NULL, the shape errors of lowram_workspace_bytes, or
  * LOWRAM_ERR_SHAPE for n_cu < 1 or a mode outside 0..2.
  */
 typedef struct lowram_attend_plan {
   int32_t kernel, workgroups, tiles_per_group, groups_per_head, partial_slots, reserved_slots;
+  int32_t window_kernel;
 } lowram_attend_plan;
 int lowram_decode_plan(const lowram_shape* shape, int n_cu, int mode, lowram_attend_plan* plan);
 

@@ -154,6 +154,29 @@ AttendPlan attend_plan(const lowram_shape* s, const Plan& p, bool stage_outputs,
   return a;
 }
 
+// Where the exact window's tiles run: as extra workgroups of the score
+// launch when the selected chunks go to the producer/consumer kernel and the
+// caches are per sequence (it would otherwise take a launch of its own;
+// the 4-wave kernel takes the window tiles into its own grid).
+bool window_in_score(const lowram_shape* s, const Plan& p, const AttendPlan& ap, bool shared) {
+  const bool has_prefix = s->prefix_len > 0 && p.n_cand > 0;
+  return has_prefix && ap.pipe && !shared && p.n_win_tiles > 0;
+}
+
+// CUs the producer/consumer kernel is planned for: LOWRAM_PIPE_CUS, else the
+// current device's count (256 if it cannot be read).
+int plan_cus() {
+  int n_cu = pipe_cus_override();
+  if (n_cu <= 0) {
+    n_cu = 256;
+    int dev = 0, cu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0)
+      n_cu = cu;
+  }
+  return n_cu;
+}
+
 // Every argument check of a decode step except the workspace's (no HIP call).
 int check_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16_t* q, uint16_t* out,
                int32_t* sel_out, float* scores_out, float* kpre_out, float* kpost_out, float* vhat_out) {
@@ -206,11 +229,24 @@ int launch_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16
     return !events || hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) == hipSuccess;
   };
 
+  const int heads = s->batch * s->n_heads_kv;
+  const AttendPlan ap = attend_plan(s, p, kpre_out || kpost_out || vhat_out, plan_cus(), attend_mode());
+  const bool wave4 = !ap.pipe;
+  const int n_split = ap.n_split;
+  const float scale_log2 = s->softmax_scale * 1.4426950408889634f;
+  const bool win_score = window_in_score(s, p, ap, shared);
+
   if (!mark(0)) return LOWRAM_ERR_HIP;
   if (has_prefix) {
+    ScoreWindow sw;
+    if (win_score) {
+      sw.win_k = c->win_k; sw.win_v = c->win_v; sw.part = part;
+      sw.n_tiles = p.n_win_tiles; sw.window = s->window; sw.window_cap = window_rows(s);
+      sw.n_split = n_split; sw.slot0 = ap.sel_slots; sw.scale_log2 = scale_log2;
+    }
     if (launch_score(q, c->landmark, keys, scores_out, s->batch, p.n_cand, s->n_heads_q,
-                     s->n_heads_kv, hs, shared ? 0 : 1, c->cand_ids ? p.n_cand : prefix_rows(s) / s->chunk) !=
-        hipSuccess)
+                     s->n_heads_kv, hs, shared ? 0 : 1, c->cand_ids ? p.n_cand : prefix_rows(s) / s->chunk,
+                     sw) != hipSuccess)
       return LOWRAM_ERR_HIP;
   }
   if (!mark(1)) return LOWRAM_ERR_HIP;
@@ -233,24 +269,13 @@ int launch_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16
   a.cache_bmul = shared ? 0 : 1;
   a.prefix_cap = prefix_rows(s);
   a.window_cap = window_rows(s);
-  const int heads = s->batch * s->n_heads_kv;
-  int n_cu = pipe_cus_override();
-  if (n_cu <= 0) {
-    n_cu = 256;
-    int dev = 0, cu = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0)
-      n_cu = cu;
-  }
-  const AttendPlan ap = attend_plan(s, p, kpre_out || kpost_out || vhat_out, n_cu, attend_mode());
-  const bool wave4 = !ap.pipe;
-  const int n_split = ap.n_split;
   a.n_sel_tiles = ap.sel_slots;
   a.n_win_tiles = p.n_win_tiles;
   a.n_split = n_split;
   a.split_base = wave4 ? 0 : ap.sel_slots;
   a.n_split_launch = wave4 ? n_split : p.n_win_tiles;
-  a.total = heads * a.n_split_launch;
+  // (no launch of its own for the window when the score grid ran it)
+  a.total = win_score ? 0 : heads * a.n_split_launch;
   a.padded_total = (a.total + 7) & ~7;
   a.pipe_tiles = p.n_sel_tiles;
   a.pipe_grp = ap.n_grp;
@@ -260,7 +285,7 @@ int launch_step(const lowram_shape* s, const lowram_layer_cache* c, const uint16
   a.pipe_padded = (a.pipe_wgs + 7) & ~7;
   a.grp_div = make_fastdiv(ap.n_grp);
   a.hkv_div = make_fastdiv(s->n_heads_kv);
-  a.scale_log2 = s->softmax_scale * 1.4426950408889634f;
+  a.scale_log2 = scale_log2;
   for (int i = 0; i < 64; ++i)
     a.inv_freq[i] = std::pow((double)s->rope_theta, -2.0 * i / (double)kHeadDim);
   if (launch_attend(a, s->rank, ci4, ri4, hs) != hipSuccess) return LOWRAM_ERR_HIP;
@@ -445,6 +470,7 @@ int lowram_decode_plan(const lowram_shape* shape, int n_cu, int mode, lowram_att
   plan->groups_per_head = a.pipe ? a.n_grp : 0;
   plan->partial_slots = a.n_split;
   plan->reserved_slots = p.n_part;
+  plan->window_kernel = p.n_win_tiles == 0 ? 0 : window_in_score(shape, p, a, false) ? 1 : 2;
   return LOWRAM_OK;
 }
 

@@ -43,6 +43,7 @@
 #include "attend_ops.h"
 #include "common.h"
 #include "internal.h"
+#include "window.h"
 
 namespace lowram {
 
@@ -57,43 +58,6 @@ struct AttLds {
   uint32_t rdesc[kAttChunksWG];
   alignas(16) uint16_t qs[16][kHeadDim];  // this KV head's query rows
 };
-
-// Softmax state of one wave's 16 NT tokens for query head j = col: the logits
-// z[t][j] sit in rows t = 16 nt + 4 grp + e of zacc[nt].  Returns the wave's
-// max and sum and the unnormalised weights as NT / 2 MFMA operands; in
-// operand q, k slot 8 grp + e' is token 32 q + 4 grp + e' (e' < 4) or
-// 32 q + 16 + 4 grp + e' - 4.
-template <int NT>
-__device__ __forceinline__ void wave_softmax(const f32x4 (&zacc)[NT], int nvalid, float scale_log2, int grp,
-                                             float& m, float& lsum, bf16x8 (&pa)[NT / 2]) {
-  float p[NT][4];
-  m = -__builtin_huge_valf();
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = 16 * nt + 4 * grp + e;
-      p[nt][e] = t < nvalid ? zacc[nt][e] * scale_log2 : -__builtin_huge_valf();
-      m = fmaxf(m, p[nt][e]);
-    }
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  const float msafe = m == -__builtin_huge_valf() ? 0.f : m;
-  lsum = 0.f;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      p[nt][e] = __builtin_amdgcn_exp2f(p[nt][e] - msafe);
-      lsum += p[nt][e];
-    }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-#pragma unroll
-  for (int q = 0; q < NT / 2; ++q)
-    pa[q] = pack8(f32x4{p[2 * q][0], p[2 * q][1], p[2 * q][2], p[2 * q][3]},
-                  f32x4{p[2 * q + 1][0], p[2 * q + 1][1], p[2 * q + 1][2], p[2 * q + 1][3]});
-}
 
 // Workgroups per CU the register budget is sized for, and how many stages
 // ahead each wave's coefficient gather runs (compile-time tunables).
@@ -618,70 +582,14 @@ __global__ __launch_bounds__(kAttWaves * 64, LOWRAM_ATT_WG_PER_CU) void attend_k
   } else {
     // ========================================================= exact window
     const int w0 = (split - a.n_sel_tiles) * kAttTokWG + wave * kAttTokWave;
-    const int nvalid = max(0, min(kAttTokWave, a.window - w0));
-    const uint16_t* kw = a.win_k + chead * (size_t)a.window_cap * kHeadDim;
-    const uint16_t* vw = a.win_v + chead * (size_t)a.window_cap * kHeadDim;
-    bf16x8 qn[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      qn[s] = col < g ? load_bf16x8(qh + col * kHeadDim + 32 * s + 8 * grp) : zero_bf16x8();
-    f32x4 zacc[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int t = min(w0 + 16 * nt + col, a.window - 1);
-      f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) z = mfma16(load_bf16x8(kw + (size_t)t * kHeadDim + 32 * s + 8 * grp), qn[s], z);
-      zacc[nt] = z;
-    }
-    // V^T[d][t] as the A operand: dimension d = 16 nd + col, token slots
-    bf16x8 vt[8];
-#pragma unroll
-    for (int nd = 0; nd < 8; ++nd) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int t = min(w0 + 16 * (e >> 2) + 4 * grp + (e & 3), a.window - 1);
-        vt[nd][e] = __builtin_bit_cast(__bf16, vw[(size_t)t * kHeadDim + 16 * nd + col]);
-      }
-    }
-    bf16x8 pa[1];
-    wave_softmax<2>(zacc, nvalid, a.scale_log2, grp, wm, wl, pa);
-#pragma unroll
-    for (int nd = 0; nd < 8; ++nd) oacc[nd] = mfma16(vt[nd], pa[0], f32x4{0.f, 0.f, 0.f, 0.f});
+    window_wave(qh, a.win_k + chead * (size_t)a.window_cap * kHeadDim,
+                a.win_v + chead * (size_t)a.window_cap * kHeadDim, w0, a.window, g, a.scale_log2, grp, col, oacc,
+                wm, wl);
   }
 
   // ======================================== merge the 4 waves, write partial
-  __syncthreads();
-  float* mo = reinterpret_cast<float*>(buf);  // 32 KiB: 4 waves x 16 heads x 128
-  float* ml = L.ml;
-#pragma unroll
-  for (int nd = 0; nd < 8; ++nd)
-    *reinterpret_cast<f32x4*>(&mo[(wave * 16 + col) * kHeadDim + 16 * nd + 4 * grp]) = oacc[nd];
-  if (grp == 0) {
-    ml[wave * 16 + col] = wm;
-    ml[kAttWaves * 16 + wave * 16 + col] = wl;
-  }
-  __syncthreads();
-  float* part = a.part + (head * (size_t)a.n_split + split) * g * kPartStride;
-  for (int idx = tid; idx < g * kHeadDim; idx += kAttWaves * 64) {
-    const int j = idx / kHeadDim, d = idx % kHeadDim;
-    float M = -__builtin_huge_valf();
-#pragma unroll
-    for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, ml[w * 16 + j]);
-    float lt = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < kAttWaves; ++w) {
-      const float mw = ml[w * 16 + j];
-      const float sc = mw == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      lt += ml[kAttWaves * 16 + w * 16 + j] * sc;
-      o += mo[(w * 16 + j) * kHeadDim + d] * sc;
-    }
-    if (d == 0) {
-      part[j * kPartStride] = M;
-      part[j * kPartStride + 1] = lt;
-    }
-    part[j * kPartStride + 2 + d] = o;
-  }
+  write_partial4(reinterpret_cast<float*>(buf), L.ml, oacc, wm, wl,
+                 a.part + (head * (size_t)a.n_split + split) * g * kPartStride, g, tid, wave, grp, col);
 }
 
 template <int RANK, bool STAGES>

@@ -89,11 +89,23 @@ void plan_pipe(int heads, int n_tiles, int n_cu, int* n_wg, int* tpw, int* n_grp
 hipError_t launch_attend_pipe(const AttendArgs& a, int rank, bool coeff_int4, bool resid_int4,
                               hipStream_t st);
 
+// The exact window's tiles when they run as extra workgroups of the score
+// grid: n_tiles 128-token tiles per (sequence, KV head), tile i written to
+// partial slot slot0 + i of part [head][n_split][g][kPartStride]; window
+// rows [cache head][window_cap][d] (cache head as for the landmarks).
+struct ScoreWindow {
+  const uint16_t* win_k = nullptr;
+  const uint16_t* win_v = nullptr;
+  float* part = nullptr;
+  int n_tiles = 0, window = 0, window_cap = 0, n_split = 0, slot0 = 0;
+  float scale_log2 = 0.f;
+};
 // cache_bmul: 1 = landmarks / candidate ids per sequence, 0 = one shared context
 // lm_rows: landmark rows per (sequence, KV head) (>= n_cand)
+// win: window tiles to run in the same grid (per-sequence caches only), or none
 hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* keys,
                         float* scores_out, int nb, int n_cand, int hq, int hkv, hipStream_t st,
-                        int cache_bmul = 1, int lm_rows = -1);
+                        int cache_bmul = 1, int lm_rows = -1, const ScoreWindow& win = ScoreWindow{});
 hipError_t launch_select(const uint32_t* keys, const int32_t* cand_ids, int32_t* sel,
                          int32_t* sel_out, int nb, int n_cand, int k, int hkv, hipStream_t st,
                          int cache_bmul = 1);

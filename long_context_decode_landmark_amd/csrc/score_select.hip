@@ -7,6 +7,7 @@
 // are kept, exact ties to the lower chunk id, output in ascending chunk id.
 #include "common.h"
 #include "internal.h"
+#include "window.h"
 
 // Grid cap of the score kernel (measured at 262K context, batch 28: 16384,
 // i.e. 512 chunks per workgroup, beat 2048-8192 by 3-5% and 32768 by 1-2%)
@@ -30,17 +31,38 @@ namespace lowram {
 #define LOWRAM_SCORE_WG_PER_CU 2
 #endif
 // NBW: batches of 64 landmark rows per wave (a workgroup scores 256 NBW
-// chunks), a template parameter so that the batch loop is straight-line code
+// chunks), a template parameter so that the batch loop is straight-line code.
+// The last win.n_tiles workgroups along x of each (sequence, KV head) run
+// that head's exact-window tiles instead: the window needs neither the
+// scores nor the selection, and its few rows ride along with the landmark
+// stream instead of taking a launch of their own.
 template <int NBW>
 __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ landmark,
     uint32_t* __restrict__ keys, float* __restrict__ scores_out, int n_cand, int n_heads_q,
-    int n_heads_kv, int cache_bmul, int lm_rows) {
+    int n_heads_kv, int cache_bmul, int lm_rows, const ScoreWindow win) {
   constexpr int chunks_per_wg = 256 * NBW;
   const int b = blockIdx.z, h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, col = lane & 15;
   const int g = n_heads_q / n_heads_kv;
+  __shared__ __attribute__((aligned(16))) unsigned char tile[4][64 * 256];
+
+  const int wt = (int)blockIdx.x - ((int)gridDim.x - win.n_tiles);  // window tile, if >= 0
+  if (wt >= 0) {
+    const size_t head = (size_t)b * n_heads_kv + h;
+    const size_t chead = (size_t)b * cache_bmul * n_heads_kv + h;
+    f32x4 oacc[8];
+    float wm, wl;
+    window_wave(q + ((size_t)b * n_heads_q + (size_t)h * g) * kHeadDim,
+                win.win_k + chead * (size_t)win.window_cap * kHeadDim,
+                win.win_v + chead * (size_t)win.window_cap * kHeadDim, wt * kAttTokWG + wave * kAttTokWave,
+                win.window, g, win.scale_log2, grp, col, oacc, wm, wl);
+    write_partial4(reinterpret_cast<float*>(&tile[0][0]), reinterpret_cast<float*>(&tile[2][0]), oacc, wm, wl,
+                   win.part + (head * (size_t)win.n_split + win.slot0 + wt) * g * kPartStride, g,
+                   (int)threadIdx.x, wave, grp, col);
+    return;
+  }
 
   // the KV head's queries as the A operand (rows j < g; the loads are
   // unconditional, row clamped, and the rows from g on zeroed after them, so
@@ -74,7 +96,6 @@ __global__ __launch_bounds__(256, LOWRAM_SCORE_WG_PER_CU) void score_kernel(
   // other buffer's loads fly.  Loads and writes are unconditional (rows past
   // the list are clamped to its last one, writes past c_end are dropped), so
   // the in-order wait before a batch's stores covers that batch's loads only.
-  __shared__ __attribute__((aligned(16))) unsigned char tile[4][64 * 256];
   unsigned char* my = tile[wave];
   auto load_rows = [&](int c0, u32x4 (&v)[16]) {
 #pragma unroll
@@ -836,7 +857,7 @@ hipError_t launch_select_split(const uint32_t* keys, int32_t* sel, int n_lists, 
 
 hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* keys,
                         float* scores_out, int nb, int n_cand, int hq, int hkv, hipStream_t st,
-                        int cache_bmul, int lm_rows) {
+                        int cache_bmul, int lm_rows, const ScoreWindow& win) {
   if (lm_rows < 0) lm_rows = n_cand;
   if (n_cand <= 0) return hipSuccess;
   // chunks per workgroup: the smallest power of two >= 256 that keeps the
@@ -848,10 +869,13 @@ hipError_t launch_score(const uint16_t* q, const uint16_t* landmark, uint32_t* k
   int cpw = 256;
   while ((long long)((n_cand + cpw - 1) / cpw) * heads > LOWRAM_SCORE_MAX_WG && cpw < 4096) cpw *= 2;
   dim3 grid((n_cand + cpw - 1) / cpw, hkv, qblocks);
+  // window tiles: only in the one-query-per-context grid
+  if (win.n_tiles > 0 && (multi || cache_bmul != 1)) return hipErrorInvalidValue;
   if (!multi) {
+    grid.x += win.n_tiles;
 #define LOWRAM_SCORE(NBW)                                                                              \
   hipLaunchKernelGGL(score_kernel<NBW>, grid, dim3(256), 0, st, q, landmark, keys, scores_out, n_cand, hq, \
-                     hkv, cache_bmul, lm_rows)
+                     hkv, cache_bmul, lm_rows, win)
     switch (cpw / 256) {
       case 1: LOWRAM_SCORE(1); break;
       case 2: LOWRAM_SCORE(2); break;

@@ -49,7 +49,8 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 
 class LowramAttendPlan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "kernel", "workgroups", "tiles_per_group", "groups_per_head", "partial_slots", "reserved_slots")]
+        "kernel", "workgroups", "tiles_per_group", "groups_per_head", "partial_slots", "reserved_slots",
+        "window_kernel")]
 
 
 class LowramShape(ctypes.Structure):

@@ -26,7 +26,7 @@ def test_library_loads_and_exports_every_symbol():
     L = native.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert native.abi_version() == 2
+    assert native.abi_version() == 3
     assert native.strerror(-4) == "workspace too small"
 
 

@@ -52,14 +52,25 @@ def test_plan_matches_restatement(name, cfg, nb, n_cu):
     # automatic choice: the producer/consumer kernel once every CU gets more than two tiles
     assert auto["kernel"] == (1 if heads * n > 2 * n_cu else 2)
     assert auto == (pipe if auto["kernel"] == 1 else wave)
+    # the window's tiles ride in the score launch beside the producer/consumer
+    # kernel, in the 4-wave kernel's own grid otherwise
+    assert pipe["window_kernel"] == (1 if n_win else 0)
+    assert wave["window_kernel"] == (2 if n_win else 0)
 
 
 def test_plan_of_the_benchmark_workload():
     # 262K context, batch 28 on 256 CUs: groups of 8 tiles, 8 per head, 7 per workgroup
     p = native.decode_plan(native.make_shape(synth.C3, batch=28), 256)
     assert p == {"kernel": 1, "workgroups": 256, "tiles_per_group": 8, "groups_per_head": 8,
-                 "partial_slots": 4 * 8 + 2, "reserved_slots": 2 * 64 + 6 + 2}
+                 "partial_slots": 4 * 8 + 2, "reserved_slots": 2 * 64 + 6 + 2, "window_kernel": 1}
     assert pipe_plan(28 * 8, 64)[3] == 56  # tiles per workgroup
+
+
+def test_plan_window_without_prefix():
+    # no compressed prefix yet: nothing is scored, the window runs in the 4-wave kernel's grid
+    cfg = synth.C0.with_(name="window_only", ctx=64, window=64)
+    p = native.decode_plan(native.make_shape(cfg, prefix_len=0, n_cand=0, n_resid=0), 256, 1)
+    assert p["kernel"] == 0 and p["window_kernel"] == 2
 
 
 def test_plan_rejects_bad_arguments():
