@@ -466,6 +466,7 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
   }
 
   uint32_t prefix = 0, pmask = 0, kk = (uint32_t)k;
+  bool whole_bin = false;
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = kSelShift[pass], nbins = 1 << kSelBits[pass];
@@ -490,12 +491,20 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
     __syncthreads();
     pick_digit(S.hist, nbins, kk, S.wsum[0], S.found);
     const uint32_t digit = S.found[0];
+    const uint32_t in_bin = S.hist[digit];
     kk -= S.found[1];
     prefix |= digit << shift;
     pmask |= dmask << shift;
+    // The chosen bin holds exactly the kk keys still needed, and it lies
+    // wholly at or above lb, so the counts left none of its keys out: the k
+    // largest are then exactly the keys >= the bin's lowest value (prefix),
+    // and the later passes are skipped with the same result.
+    whole_bin = pass < 2 && kk == in_bin && prefix > 0 && prefix >= lb;
     __syncthreads();  // hist, wsum and found are reused next
+    if (whole_bin) break;
   }
-  const uint32_t T = prefix, need = kk;
+  // select the keys > T and the first `need` keys == T
+  const uint32_t T = whole_bin ? prefix - 1 : prefix, need = whole_bin ? 0u : kk;
 
   // ordered compaction: this thread's counts of keys > T and == T, their
   // exclusive scans over the block, then this thread's selected candidates
@@ -578,6 +587,7 @@ __global__ __launch_bounds__(kSelThreads) void select_l2_kernel(
   auto key_of = [&](int j) -> uint32_t { return kg[i_begin + j]; };  // key j of this thread (j < cnt)
 
   uint32_t prefix = 0, pmask = 0, kk = (uint32_t)k;
+  bool whole_bin = false;
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = kSelShift[pass], nbins = 1 << kSelBits[pass];
@@ -595,12 +605,17 @@ __global__ __launch_bounds__(kSelThreads) void select_l2_kernel(
     __syncthreads();
     pick_digit(S.hist, nbins, kk, S.wsum[0], S.found);
     const uint32_t digit = S.found[0];
+    const uint32_t in_bin = S.hist[digit];
     kk -= S.found[1];
     prefix |= digit << shift;
     pmask |= dmask << shift;
+    // as in select_reg_kernel (every key is counted here): a bin holding
+    // exactly the keys still needed ends the passes
+    whole_bin = pass < 2 && kk == in_bin && prefix > 0;
     __syncthreads();  // hist, wsum and found are reused next
+    if (whole_bin) break;
   }
-  const uint32_t T = prefix, need = kk;
+  const uint32_t T = whole_bin ? prefix - 1 : prefix, need = whole_bin ? 0u : kk;
 
   uint32_t ngt = 0, neq = 0;
   for (int j0 = 0; j0 < cnt; j0 += kSelBatch) {
