@@ -77,3 +77,50 @@ def test_select_equals_oracle_topk_on_exact_ties(name, n_cand, window, topk, n_r
             assert np.array_equal(sel_h[b, h, :keff], want), f"{name} b{b} h{h}"
             assert np.all(sel_h[b, h, keff:] == -1)
     print(f"{name}: {nb * cfg.n_heads_kv} lists equal to the oracle's top-{topk}", flush=True)
+
+
+@pytest.mark.parametrize("name,n_cand,m_top", [
+    ("exit_after_first_pass", 32736, 3),
+    ("bin_at_the_lower_bound", 8192, 1),
+    ("l2_exit_after_first_pass", 40960, 5),
+])
+def test_select_whole_bin(name, n_cand, m_top):
+    """Landmark row c of a head is one base row times 2^(c mod 8) (exact in
+    bf16, and every score is then exactly 2^(c mod 8) times one value in fp32
+    too), so the 8 distinct scores differ in their exponent and each fills a
+    first-pass bin of its own, with n_cand / 8 copies.  k is the number of
+    chunks whose score is among the m_top highest: the bin of the k-th key
+    holds exactly the keys still needed after the first pass.  At 32736 and
+    40960 candidates (the register and L2 variants) the passes stop there; at
+    8192 with m_top = 1 the lower bound on the k-th key equals that key, the
+    bin starts below it, and all three passes run.  Either way the selection
+    is every chunk of the m_top highest rows, equal to the oracle's top-k."""
+    nb, n_rows = 2, 8
+    cfg0 = synth.C3.with_(name=f"select_{name}", batch=nb, n_heads_q=8, n_heads_kv=2, rank=64,
+                          ctx=n_cand * synth.C3.chunk + 64, window=64, topk=1024)
+    assert cfg0.n_cand == n_cand and n_cand % n_rows == 0
+    print(f"\n{name}: drawing", flush=True)
+    cache = draw_batch(cfg0, nb, seed=717)
+    scale = torch.pow(2.0, (torch.arange(n_cand, device=DEV) % n_rows).float()).to(torch.bfloat16)
+    cache["landmark"] = (cache["landmark"][:, :, :1] * scale[None, None, :, None]).contiguous()
+    q = sd.draw_queries(cfg0, nb, 818, DEV)
+    topk = m_top * (n_cand // n_rows)
+    cfg = cfg0.with_(topk=topk)
+    out = torch.empty_like(q)
+    shape = native.make_shape(cfg, batch=nb)
+    ws = torch.empty(native.workspace_bytes(shape), dtype=torch.uint8, device=DEV)
+    sel = torch.full((nb, cfg.n_heads_kv, topk), -7, dtype=torch.int32, device=DEV)
+    native.decode_step(shape, native.make_cache(cache), q, out, ws, sel_out=sel)
+    torch.cuda.synchronize()
+    sel_h = sel.cpu().numpy()
+    q_h, lm_h = host(q), host(cache["landmark"])
+    g = cfg.gqa
+    for b in range(nb):
+        for h in range(cfg.n_heads_kv):
+            sc = steps.landmark_scores(decode.widen(q_h[b, h * g:(h + 1) * g]), decode.widen(lm_h[b, h]))
+            distinct = np.unique(sc)
+            assert len(distinct) == n_rows and sc[0] != 0.0
+            want = steps.select_topk(sc, topk)
+            assert np.array_equal(np.sort(sc[want]), np.sort(sc[sc >= distinct[-m_top]]))  # whole groups
+            assert np.array_equal(sel_h[b, h], want), f"{name} b{b} h{h}"
+    print(f"{name}: {nb * cfg.n_heads_kv} lists equal to the oracle's top-{topk}", flush=True)
