@@ -12,6 +12,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblowram.so")
+ABI_VERSION = 3  # LOWRAM_ABI_VERSION of the header these structs follow
 
 FMT_BF16 = 0
 FMT_INT4_G32 = 1
@@ -160,6 +161,10 @@ def lib() -> ctypes.CDLL:
         for name in SYMBOLS:
             getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
         L.lowram_strerror.restype = ctypes.c_char_p
+        # the structs above follow one version of include/lowram.h
+        if L.lowram_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.lowram_abi_version()}, this binding "
+                               f"expects {ABI_VERSION}: rebuild it (__graft_entry__.build())")
         _lib = L
     return _lib
 
