@@ -252,6 +252,7 @@ struct SelLds {
   uint32_t hist[kSelBins];
   uint32_t wsum[2][kSelWaves];
   uint32_t found[2];
+  uint32_t spare[64];  // one word per lane: the ordered compaction's stores of unselected keys
 };
 
 // inclusive scan of x over the 64 lanes of a wave, from lane 0 up, on DPP
@@ -531,7 +532,23 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
   // lookup done there; longer outputs are written directly.
   const bool staged = k_eff <= kSelBins;
   const bool mine = !(gt_run + min(eq_run, need) >= (uint32_t)k_eff || (ngt == 0 && (neq == 0 || eq_run >= need)));
-  if (mine) {
+  if (staged) {
+    // one store per key and no branch in the loop: an unselected key's
+    // index goes to this lane's spare word
+    if (mine) {
+      uint32_t* const spare = &S.spare[tid & 63];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const bool in = (vmask >> j) & 1u;
+        const bool gt = in && kx[j] > T, eq = in && kx[j] == T;
+        const uint32_t pos = gt_run + min(eq_run, need);
+        const bool put = (gt || (eq && eq_run < need)) && pos < (uint32_t)k_eff;
+        *(put ? &S.hist[min(pos, (uint32_t)kSelBins - 1)] : spare) = (uint32_t)(i_begin + j);
+        gt_run += gt ? 1u : 0u;
+        eq_run += eq ? 1u : 0u;
+      }
+    }
+  } else if (mine) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const bool in = (vmask >> j) & 1u;
@@ -540,13 +557,9 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
         const uint32_t pos = gt_run + min(eq_run, need);
         if (pos < (uint32_t)k_eff) {
           const int i = i_begin + j;
-          if (staged) {
-            S.hist[pos] = (uint32_t)i;
-          } else {
-            const int32_t c = ids ? ids[i] : i;
-            so[pos] = c;
-            if (so2) so2[pos] = c;
-          }
+          const int32_t c = ids ? ids[i] : i;
+          so[pos] = c;
+          if (so2) so2[pos] = c;
         }
       }
       gt_run += gt ? 1u : 0u;
