@@ -252,7 +252,7 @@ struct SelLds {
   uint32_t hist[kSelBins];
   uint32_t wsum[2][kSelWaves];
   uint32_t found[2];
-  uint32_t spare[64];  // one word per lane: the ordered compaction's stores of unselected keys
+  uint32_t spare[64];  // one word per lane: the passes' and the compaction's writes for keys they skip
 };
 
 // inclusive scan of x over the 64 lanes of a wave, from lane 0 up, on DPP
@@ -479,15 +479,15 @@ __global__ __launch_bounds__(kSelThreads) void select_reg_kernel(
 #pragma unroll
       for (int w = 0; w < kSelWaves; ++w) lb = min(lb, S.wsum[1][w]);
     }
-    if (wave_full) {
+    {
+      // one LDS atomic per key and no branch in the loop: a key outside the
+      // prefix or below lb counts in its lane's spare word (never read)
+      uint32_t* const spare = &S.spare[tid & 63];
 #pragma unroll
-      for (int j = 0; j < PER; ++j)
-        if ((kx[j] & pmask) == prefix && kx[j] >= lb) atomicAdd(&S.hist[(kx[j] >> shift) & dmask], 1u);
-    } else {
-#pragma unroll
-      for (int j = 0; j < PER; ++j)
-        if (((vmask >> j) & 1u) && (kx[j] & pmask) == prefix && kx[j] >= lb)
-          atomicAdd(&S.hist[(kx[j] >> shift) & dmask], 1u);
+      for (int j = 0; j < PER; ++j) {
+        const bool in = (wave_full || ((vmask >> j) & 1u)) && (kx[j] & pmask) == prefix && kx[j] >= lb;
+        atomicAdd(in ? &S.hist[(kx[j] >> shift) & dmask] : spare, 1u);
+      }
     }
     __syncthreads();
     pick_digit(S.hist, nbins, kk, S.wsum[0], S.found);
